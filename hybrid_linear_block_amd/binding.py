@@ -1,0 +1,126 @@
+"""ctypes binding of libhf.so (the C ABI declared in include/hf.h).
+
+Argument marshalling only: every step of the hybrid attention runs in the HIP
+kernels of libhf. PyTorch provides device memory and the stream. If the library
+has not been built, importing this module raises; there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, Structure, c_float, c_int, c_int32, c_int64, c_size_t, c_void_p
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhf.so")
+
+HF_OK = 0
+HF_ERR_INVALID_ARG = 1
+HF_ERR_UNSUPPORTED = 2
+HF_ERR_STATE = 3
+HF_ERR_HIP = 4
+HF_BF16 = 0
+HF_F32 = 1
+
+
+class hf_config(Structure):
+    _fields_ = [
+        ("num_heads", c_int32),
+        ("head_dim", c_int32),
+        ("block_size", c_int32),
+        ("dtype", c_int32),
+        ("eps", c_float),
+        ("softmax_scale", c_float),
+        ("max_n_q", c_int64),
+        ("max_n_kv", c_int64),
+        ("max_n_ev", c_int64),
+        ("max_top_k", c_int32),
+    ]
+
+
+class HfError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {hf_status_string(status)}")
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(
+            f"{_LIB_PATH} is missing: build the HIP library first "
+            "(python -m hybrid_linear_block_amd.build, or __graft_entry__.build())")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = c_void_p
+    sig = {
+        "hf_workspace_bytes": (c_size_t, [POINTER(hf_config)]),
+        "hf_state_init": (c_int, [POINTER(hf_config), P, P, P, c_size_t, c_int, c_int64, P,
+                                  POINTER(c_void_p)]),
+        "hf_absorb_evicted": (c_int, [P, P, P, c_int64, c_int64, c_int64, P]),
+        "hf_attend_chunk": (c_int, [P, P, c_int64, c_int64, P, P, c_int64, c_int64, c_int32, P,
+                                    c_int64, P, P]),
+        "hf_block_scores": (c_int, [P, P, c_int64, c_int64, P, c_int64, c_int64, P, P]),
+        "hf_next_ev_index": (c_int64, [P]),
+        "hf_state_destroy": (None, [P]),
+        "hf_status_string": (ctypes.c_char_p, [c_int]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+EXPORTED = ("hf_workspace_bytes", "hf_state_init", "hf_absorb_evicted", "hf_attend_chunk",
+            "hf_block_scores", "hf_next_ev_index", "hf_state_destroy", "hf_status_string")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+# ---------------------------------------------------------------- raw C calls
+# Same names and argument order as include/hf.h; pointers and streams are ints.
+
+
+def hf_status_string(status: int) -> str:
+    return _lib.hf_status_string(int(status)).decode()
+
+
+def hf_workspace_bytes(cfg: hf_config) -> int:
+    return int(_lib.hf_workspace_bytes(ctypes.byref(cfg)))
+
+
+def hf_state_init(cfg: hf_config, S: int, z: int, workspace: int, ws_bytes: int, zero_fill: int,
+                  next_ev_index: int, stream: int):
+    """Returns (status, handle or None)."""
+    h = c_void_p()
+    st = _lib.hf_state_init(ctypes.byref(cfg), S, z, workspace, ws_bytes, int(zero_fill),
+                            int(next_ev_index), stream, ctypes.byref(h))
+    return st, (h.value if st == HF_OK else None)
+
+
+def hf_absorb_evicted(state: int, k_ev: int, v_ev: int, n_ev: int, ev_head_stride: int,
+                      ev_index: int, stream: int) -> int:
+    return _lib.hf_absorb_evicted(state, k_ev, v_ev, n_ev, ev_head_stride, ev_index, stream)
+
+
+def hf_attend_chunk(state: int, q: int, n_q: int, q_head_stride: int, k_win: int, v_win: int,
+                    n_kv: int, kv_head_stride: int, top_k: int, out: int, out_head_stride: int,
+                    sel_out: int, stream: int) -> int:
+    return _lib.hf_attend_chunk(state, q, n_q, q_head_stride, k_win, v_win, n_kv,
+                                kv_head_stride, top_k, out, out_head_stride, sel_out, stream)
+
+
+def hf_block_scores(state: int, q: int, n_q: int, q_head_stride: int, k_win: int, n_kv: int,
+                    kv_head_stride: int, scores_out: int, stream: int) -> int:
+    return _lib.hf_block_scores(state, q, n_q, q_head_stride, k_win, n_kv, kv_head_stride,
+                                scores_out, stream)
+
+
+def hf_next_ev_index(state) -> int:
+    return int(_lib.hf_next_ev_index(state))
+
+
+def hf_state_destroy(state) -> None:
+    _lib.hf_state_destroy(state)

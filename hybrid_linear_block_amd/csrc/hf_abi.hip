@@ -1,0 +1,269 @@
+// hf_abi.hip -- the extern "C" entry points of libhf (declared in include/hf.h).
+//
+// Host side only: argument validation (always before any HIP call, so that an
+// invalid call enqueues nothing), the workspace layout, the eviction-sequence
+// check and the kernel launches on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <new>
+
+#include "../../include/hf.h"
+#include "hf_launch.h"
+
+struct hf_state {
+  hf_config cfg;
+  float* S;
+  float* z;
+  char* ws;
+  size_t ws_bytes;
+  int64_t next_ev;
+  int device;
+  float scale;
+  int nqb_cap, nkb_cap;
+  float* pooled_q;
+  float* pooled_k;
+  int32_t* sel;
+  float* partials;
+  unsigned* tickets;
+  size_t tickets_bytes;
+};
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t elem_size(int dtype) { return dtype == HF_BF16 ? 2 : 4; }
+
+// Configuration check: HF_ERR_INVALID_ARG for values that are meaningless,
+// HF_ERR_UNSUPPORTED for meaningful values outside the instantiated kernels.
+hf_status check_config(const hf_config* c) {
+  if (!c) return HF_ERR_INVALID_ARG;
+  if (c->num_heads < 1 || c->head_dim < 1 || c->block_size < 1) return HF_ERR_INVALID_ARG;
+  if (c->dtype != HF_BF16 && c->dtype != HF_F32) return HF_ERR_UNSUPPORTED;
+  if (!(c->eps >= 0.f) || !std::isfinite(c->eps)) return HF_ERR_INVALID_ARG;
+  if (!(c->softmax_scale >= 0.f) || !std::isfinite(c->softmax_scale)) return HF_ERR_INVALID_ARG;
+  if (c->max_n_q < 1 || c->max_n_kv < 1 || c->max_n_ev < 0 || c->max_top_k < 1)
+    return HF_ERR_INVALID_ARG;
+  if (c->head_dim != 64 && c->head_dim != 128) return HF_ERR_UNSUPPORTED;
+  if (c->dtype == HF_BF16 && c->block_size != 64) return HF_ERR_UNSUPPORTED;
+  if (c->dtype == HF_F32 && c->block_size != 16 && c->block_size != 64) return HF_ERR_UNSUPPORTED;
+  if (ceil_div(c->max_n_kv, c->block_size) > hf::kMaxKeyBlocks) return HF_ERR_UNSUPPORTED;
+  if (ceil_div(c->max_n_q, c->block_size) > (int64_t)1 << 24) return HF_ERR_UNSUPPORTED;
+  if (c->max_top_k > ceil_div(c->max_n_kv, c->block_size)) return HF_ERR_INVALID_ARG;
+  return HF_OK;
+}
+
+struct Layout {
+  size_t pooled_q, pooled_k, sel, partials, tickets, total, tickets_bytes;
+};
+
+Layout layout(const hf_config* c) {
+  const size_t H = (size_t)c->num_heads, d = (size_t)c->head_dim;
+  const size_t nqb = (size_t)ceil_div(c->max_n_q, c->block_size);
+  const size_t nkb = (size_t)ceil_div(c->max_n_kv, c->block_size);
+  Layout L;
+  size_t off = 0;
+  L.pooled_q = off;
+  off += round_up(H * nqb * d * 4);
+  L.pooled_k = off;
+  off += round_up(H * nkb * d * 4);
+  L.sel = off;
+  off += round_up(H * nqb * (size_t)c->max_top_k * 4);
+  L.partials = off;
+  off += round_up(hf::absorb_partial_floats((int)H, (int)d) * 4);
+  L.tickets = off;
+  L.tickets_bytes = hf::absorb_ticket_count((int)H, (int)d) * 4;
+  off += round_up(L.tickets_bytes);
+  L.total = off;
+  return L;
+}
+
+// Runs `fn` with the state's device current, restoring the caller's device.
+template <typename F>
+hf_status on_device(int device, F fn) {
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return HF_ERR_HIP;
+  if (cur != device && hipSetDevice(device) != hipSuccess) return HF_ERR_HIP;
+  const hipError_t e = fn();
+  if (cur != device) (void)hipSetDevice(cur);
+  return e == hipSuccess ? HF_OK : HF_ERR_HIP;
+}
+
+hf_status check_tensor(const void* p, int64_t n, int64_t head_stride, const hf_config& c) {
+  if (!p || !aligned16(p)) return HF_ERR_INVALID_ARG;
+  if (head_stride < n * c.head_dim) return HF_ERR_INVALID_ARG;
+  if ((head_stride * (int64_t)elem_size(c.dtype)) % 16 != 0) return HF_ERR_INVALID_ARG;
+  return HF_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t hf_workspace_bytes(const hf_config* cfg) {
+  if (check_config(cfg) != HF_OK) return 0;
+  return layout(cfg).total;
+}
+
+hf_status hf_state_init(const hf_config* cfg, float* S, float* z, void* workspace,
+                        size_t ws_bytes, int zero_fill, int64_t next_ev_index, void* stream,
+                        hf_state** out) {
+  if (!out) return HF_ERR_INVALID_ARG;
+  *out = nullptr;
+  const hf_status cs = check_config(cfg);
+  if (cs != HF_OK) return cs;
+  if (!S || !z || !workspace || !aligned16(S) || !aligned16(z) || !aligned16(workspace))
+    return HF_ERR_INVALID_ARG;
+  if (next_ev_index < 0) return HF_ERR_INVALID_ARG;
+  const Layout L = layout(cfg);
+  if (ws_bytes < L.total) return HF_ERR_INVALID_ARG;
+
+  hf_state* st = new (std::nothrow) hf_state();
+  if (!st) return HF_ERR_HIP;
+  st->cfg = *cfg;
+  st->S = S;
+  st->z = z;
+  st->ws = static_cast<char*>(workspace);
+  st->ws_bytes = ws_bytes;
+  st->next_ev = next_ev_index;
+  st->scale = cfg->softmax_scale > 0.f ? cfg->softmax_scale
+                                       : 1.0f / std::sqrt((float)cfg->head_dim);
+  st->nqb_cap = (int)ceil_div(cfg->max_n_q, cfg->block_size);
+  st->nkb_cap = (int)ceil_div(cfg->max_n_kv, cfg->block_size);
+  st->pooled_q = reinterpret_cast<float*>(st->ws + L.pooled_q);
+  st->pooled_k = reinterpret_cast<float*>(st->ws + L.pooled_k);
+  st->sel = reinterpret_cast<int32_t*>(st->ws + L.sel);
+  st->partials = reinterpret_cast<float*>(st->ws + L.partials);
+  st->tickets = reinterpret_cast<unsigned*>(st->ws + L.tickets);
+  st->tickets_bytes = L.tickets_bytes;
+  if (hipGetDevice(&st->device) != hipSuccess) {
+    delete st;
+    return HF_ERR_HIP;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t H = (size_t)cfg->num_heads, d = (size_t)cfg->head_dim;
+  const hf_status r = on_device(st->device, [&]() -> hipError_t {
+    hipError_t e = hf::launch_fill_zero(st->tickets, st->tickets_bytes, s);
+    if (e == hipSuccess && zero_fill) e = hf::launch_fill_zero(S, H * d * d * 4, s);
+    if (e == hipSuccess && zero_fill) e = hf::launch_fill_zero(z, H * d * 4, s);
+    return e;
+  });
+  if (r != HF_OK) {
+    delete st;
+    return r;
+  }
+  *out = st;
+  return HF_OK;
+}
+
+hf_status hf_absorb_evicted(hf_state* st, const void* k_ev, const void* v_ev, int64_t n_ev,
+                            int64_t ev_head_stride, int64_t ev_index, void* stream) {
+  if (!st || n_ev < 0) return HF_ERR_INVALID_ARG;
+  const hf_config& c = st->cfg;
+  if (n_ev > c.max_n_ev) return HF_ERR_INVALID_ARG;
+  if (n_ev > 0) {
+    hf_status e = check_tensor(k_ev, n_ev, ev_head_stride, c);
+    if (e == HF_OK) e = check_tensor(v_ev, n_ev, ev_head_stride, c);
+    if (e != HF_OK) return e;
+  }
+  if (ev_index != st->next_ev) return HF_ERR_STATE;
+  if (n_ev == 0) return HF_OK;
+  const hf_status r = on_device(st->device, [&]() {
+    return hf::launch_absorb(c.dtype, c.num_heads, c.head_dim, k_ev, v_ev, n_ev, ev_head_stride,
+                             st->S, st->z, st->partials, st->tickets,
+                             static_cast<hipStream_t>(stream));
+  });
+  if (r == HF_OK) st->next_ev += n_ev;
+  return r;
+}
+
+static hf_status check_attend(const hf_state* st, const void* q, int64_t n_q, int64_t q_hs,
+                              const void* k_win, int64_t n_kv, int64_t kv_hs) {
+  const hf_config& c = st->cfg;
+  if (n_q < 0 || n_kv < 1) return HF_ERR_INVALID_ARG;
+  if (n_q > c.max_n_q || n_kv > c.max_n_kv) return HF_ERR_INVALID_ARG;
+  hf_status e = n_q > 0 ? check_tensor(q, n_q, q_hs, c) : HF_OK;
+  if (e == HF_OK) e = check_tensor(k_win, n_kv, kv_hs, c);
+  return e;
+}
+
+hf_status hf_attend_chunk(hf_state* st, const void* q, int64_t n_q, int64_t q_head_stride,
+                          const void* k_win, const void* v_win, int64_t n_kv,
+                          int64_t kv_head_stride, int32_t top_k, void* out,
+                          int64_t out_head_stride, int32_t* sel_out, void* stream) {
+  if (!st) return HF_ERR_INVALID_ARG;
+  const hf_config& c = st->cfg;
+  hf_status e = check_attend(st, q, n_q, q_head_stride, k_win, n_kv, kv_head_stride);
+  if (e == HF_OK) e = check_tensor(v_win, n_kv, kv_head_stride, c);
+  if (e == HF_OK && n_q > 0) e = check_tensor(out, n_q, out_head_stride, c);
+  if (e != HF_OK) return e;
+  const int64_t nkb = ceil_div(n_kv, c.block_size);
+  if (top_k < 1 || top_k > nkb || top_k > c.max_top_k) return HF_ERR_INVALID_ARG;
+  if (sel_out && (reinterpret_cast<uintptr_t>(sel_out) & 3u)) return HF_ERR_INVALID_ARG;
+  if (n_q == 0) return HF_OK;
+  const int nqb = (int)ceil_div(n_q, c.block_size);
+  int32_t* sel = sel_out ? sel_out : st->sel;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return on_device(st->device, [&]() {
+    hipError_t r = hf::launch_block_pool(c.dtype, c.num_heads, c.head_dim, c.block_size, q, n_q,
+                                         q_head_stride, k_win, n_kv, kv_head_stride,
+                                         st->pooled_q, st->pooled_k, st->nqb_cap, st->nkb_cap, s);
+    if (r == hipSuccess)
+      r = hf::launch_score_select(c.num_heads, c.head_dim, nqb, (int)nkb, st->nqb_cap,
+                                  st->nkb_cap, st->pooled_q, st->pooled_k, st->scale, top_k, sel,
+                                  nullptr, s);
+    if (r == hipSuccess)
+      r = hf::launch_sparse_swa(c.dtype, c.num_heads, c.head_dim, c.block_size, q, n_q,
+                                q_head_stride, k_win, v_win, n_kv, kv_head_stride, sel, top_k,
+                                st->S, st->z, c.eps, st->scale, out, out_head_stride, s);
+    return r;
+  });
+}
+
+hf_status hf_block_scores(hf_state* st, const void* q, int64_t n_q, int64_t q_head_stride,
+                          const void* k_win, int64_t n_kv, int64_t kv_head_stride,
+                          float* scores_out, void* stream) {
+  if (!st) return HF_ERR_INVALID_ARG;
+  const hf_config& c = st->cfg;
+  hf_status e = check_attend(st, q, n_q, q_head_stride, k_win, n_kv, kv_head_stride);
+  if (e != HF_OK) return e;
+  if (!scores_out || (reinterpret_cast<uintptr_t>(scores_out) & 3u)) return HF_ERR_INVALID_ARG;
+  if (n_q == 0) return HF_OK;
+  const int nqb = (int)ceil_div(n_q, c.block_size);
+  const int nkb = (int)ceil_div(n_kv, c.block_size);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return on_device(st->device, [&]() {
+    hipError_t r = hf::launch_block_pool(c.dtype, c.num_heads, c.head_dim, c.block_size, q, n_q,
+                                         q_head_stride, k_win, n_kv, kv_head_stride,
+                                         st->pooled_q, st->pooled_k, st->nqb_cap, st->nkb_cap, s);
+    if (r == hipSuccess)
+      r = hf::launch_score_select(c.num_heads, c.head_dim, nqb, nkb, st->nqb_cap, st->nkb_cap,
+                                  st->pooled_q, st->pooled_k, st->scale, 1, nullptr, scores_out,
+                                  s);
+    return r;
+  });
+}
+
+int64_t hf_next_ev_index(const hf_state* st) { return st ? st->next_ev : -1; }
+
+void hf_state_destroy(hf_state* st) { delete st; }
+
+const char* hf_status_string(hf_status s) {
+  switch (s) {
+    case HF_OK: return "HF_OK";
+    case HF_ERR_INVALID_ARG: return "HF_ERR_INVALID_ARG: invalid argument";
+    case HF_ERR_UNSUPPORTED: return "HF_ERR_UNSUPPORTED: head_dim, block_size or dtype not instantiated";
+    case HF_ERR_STATE: return "HF_ERR_STATE: eviction index out of sequence";
+    case HF_ERR_HIP: return "HF_ERR_HIP: HIP runtime or launch error";
+  }
+  return "unknown hf_status";
+}
+
+}  // extern "C"

@@ -1,0 +1,99 @@
+// hf_device.h -- device helpers shared by the gfx950 kernels of libhf.
+//
+// MFMA operand layout used throughout (v_mfma_f32_16x16x32_bf16 and
+// v_mfma_f32_16x16x4_f32, wave64): with lane l, g = l / 16 and c = l % 16,
+//   A operand (16 x KSTEP, row-major M x K): lane holds A[c][g*KP .. g*KP+KP)
+//   B operand (KSTEP x 16, K x N):          lane holds B[g*KP .. g*KP+KP)[c]
+//   C/D (16 x 16 fp32):                     lane holds D[4g + r][c], r = 0..3
+// with KSTEP = 32, KP = 8 for bf16 and KSTEP = 4, KP = 1 for fp32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hf {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t bf16_t;  // bf16 is carried as its 16-bit pattern
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// phi(x) = elu(x) + 1
+__device__ __forceinline__ float phi(float x) { return x > 0.f ? x + 1.f : __expf(x); }
+
+template <typename T> struct Mfma;
+
+template <> struct Mfma<bf16_t> {
+  static constexpr int KSTEP = 32;
+  static constexpr int KP = 8;
+  typedef bf16x8 op_t;
+  __device__ __forceinline__ static f32x4 mma(op_t a, op_t b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <> struct Mfma<float> {
+  static constexpr int KSTEP = 4;
+  static constexpr int KP = 1;
+  typedef float op_t;
+  __device__ __forceinline__ static f32x4 mma(op_t a, op_t b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+};
+
+// Pack 8 bf16 patterns (as 4 uint32 words, low half first) into an MFMA operand.
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 w) { return __builtin_bit_cast(bf16x8, w); }
+
+// Split 8 fp32 values into bf16 hi + lo operands (x ~= hi + lo to ~2^-17 relative).
+__device__ __forceinline__ void split_bf16x8(const float* x, bf16x8& hi, bf16x8& lo) {
+  uint32_t h[8], l[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    h[e] = f32_to_bf16_bits(x[e]);
+    l[e] = f32_to_bf16_bits(x[e] - bf16_to_f32(h[e]));
+  }
+  uint4 hw = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                        h[6] | (h[7] << 16));
+  uint4 lw = make_uint4(l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16),
+                        l[6] | (l[7] << 16));
+  hi = as_bf16x8(hw);
+  lo = as_bf16x8(lw);
+}
+
+// Word k / 16-bit half e of a 16-byte register value (indices are compile-time
+// constants after unrolling, so these fold to register selects).
+__device__ __forceinline__ uint32_t word(const uint4& v, int k) {
+  return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
+}
+__device__ __forceinline__ uint32_t half16(const uint4& v, int e) {
+  return (word(v, e >> 1) >> ((e & 1) * 16)) & 0xFFFFu;
+}
+
+__device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
+
+// 16-byte global load with an in-bounds predicate (out of bounds reads nothing and
+// yields zeros).
+__device__ __forceinline__ uint4 ld16(const void* p, bool ok) {
+  return ok ? *reinterpret_cast<const uint4*>(p) : zero4();
+}
+
+// Map a launch-order workgroup id to a logical work index so that each XCD (the
+// hardware hands consecutive workgroups to the 8 XCDs in turn) processes one
+// contiguous range of the logical order. Returns -1 for padding workgroups.
+__device__ __forceinline__ int xcd_remap(int wg, int n_wg_padded, int n_logical) {
+  const int per = n_wg_padded >> 3;
+  const int logical = (wg & 7) * per + (wg >> 3);
+  return logical < n_logical ? logical : -1;
+}
+
+}  // namespace hf

@@ -1,0 +1,43 @@
+// hf_launch.h -- internal launchers of libhf's gfx950 kernels (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace hf {
+
+// ---- absorb: S += V^T phi(K), z += sum phi(K) ------------------------------------
+constexpr int kAbsorbMaxSplits = 8;
+struct AbsorbPlan {
+  int tokens_per_split;
+  int n_split;
+};
+AbsorbPlan absorb_plan(int64_t n_ev);
+size_t absorb_partial_floats(int heads, int d);
+size_t absorb_ticket_count(int heads, int d);
+hipError_t launch_absorb(int dtype, int heads, int d, const void* k, const void* v, int64_t n_ev,
+                         int64_t head_stride, float* S, float* z, float* partials,
+                         unsigned* tickets, hipStream_t stream);
+
+// ---- block pooling, scoring and top-K selection ----------------------------------
+constexpr int kMaxKeyBlocks = 8192;
+hipError_t launch_block_pool(int dtype, int heads, int d, int block, const void* q, int64_t n_q,
+                             int64_t q_hs, const void* k, int64_t n_kv, int64_t kv_hs,
+                             float* pooled_q, float* pooled_k, int nqb_cap, int nkb_cap,
+                             hipStream_t stream);
+hipError_t launch_score_select(int heads, int d, int nqb, int nkb, int nqb_cap, int nkb_cap,
+                               const float* pooled_q, const float* pooled_k, float scale,
+                               int top_k, int32_t* sel, float* scores_out, hipStream_t stream);
+
+// ---- block-sparse softmax attention + linear read ---------------------------------
+hipError_t launch_sparse_swa(int dtype, int heads, int d, int block, const void* q, int64_t n_q,
+                             int64_t q_hs, const void* k, const void* v, int64_t n_kv,
+                             int64_t kv_hs, const int32_t* sel, int top_k, const float* S,
+                             const float* z, float eps, float scale, void* out, int64_t out_hs,
+                             hipStream_t stream);
+
+// ---- utilities -------------------------------------------------------------------
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
+
+}  // namespace hf

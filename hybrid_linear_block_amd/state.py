@@ -1,0 +1,168 @@
+"""PyTorch-facing handle over libhf: one hybrid-attention layer's streaming state.
+
+The linear state (S, z) and the workspace are torch tensors on the GPU; every call
+passes raw pointers and the current HIP stream to the C ABI and returns without
+synchronising. Nothing here computes any part of the attention.
+"""
+
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import torch
+
+from . import binding as B
+
+_DTYPES = {torch.bfloat16: B.HF_BF16, torch.float32: B.HF_F32}
+
+
+def _check(status: int, what: str) -> None:
+    if status != B.HF_OK:
+        raise B.HfError(status, what)
+
+
+def _rows(t: torch.Tensor, name: str, d: int) -> Tuple[int, int]:
+    """(n, head stride in elements) of a [H][n][d] tensor with contiguous rows."""
+    if t.dim() != 3 or t.shape[2] != d:
+        raise ValueError(f"{name} must be [H][n][{d}], got {tuple(t.shape)}")
+    if t.shape[1] > 1 and t.stride(1) != d or t.stride(2) != 1:
+        raise ValueError(f"{name} must have contiguous rows of {d} elements")
+    hs = t.stride(0) if t.shape[0] > 1 else max(t.shape[1] * d, 1)
+    return t.shape[1], hs
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+class HybridAttentionState:
+    """Per-layer state of the per-chunk hybrid attention (see include/hf.h)."""
+
+    def __init__(self, num_heads: int, head_dim: int, block_size: int, dtype: torch.dtype,
+                 max_n_q: int, max_n_kv: int, max_n_ev: int, max_top_k: int,
+                 eps: float = 1e-6, softmax_scale: float = 0.0,
+                 device: Optional[torch.device] = None, S: Optional[torch.Tensor] = None,
+                 z: Optional[torch.Tensor] = None, next_ev_index: int = 0):
+        if dtype not in _DTYPES:
+            raise ValueError(f"unsupported dtype {dtype}")
+        self.device = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+        self.dtype = dtype
+        self.cfg = B.hf_config(num_heads, head_dim, block_size, _DTYPES[dtype], eps,
+                               softmax_scale, max_n_q, max_n_kv, max_n_ev, max_top_k)
+        ws = B.hf_workspace_bytes(self.cfg)
+        if ws == 0:
+            raise B.HfError(B.HF_ERR_UNSUPPORTED, "hf_workspace_bytes")
+        adopt = S is not None
+        if adopt != (z is not None):
+            raise ValueError("pass both S and z to adopt a saved state, or neither")
+        if adopt:
+            if S.shape != (num_heads, head_dim, head_dim) or z.shape != (num_heads, head_dim):
+                raise ValueError("S must be [H][d][d] and z [H][d]")
+            self.S = S.to(device=self.device, dtype=torch.float32).contiguous().clone()
+            self.z = z.to(device=self.device, dtype=torch.float32).contiguous().clone()
+        else:
+            self.S = torch.empty((num_heads, head_dim, head_dim), dtype=torch.float32,
+                                 device=self.device)
+            self.z = torch.empty((num_heads, head_dim), dtype=torch.float32, device=self.device)
+        self.workspace = torch.empty(ws, dtype=torch.uint8, device=self.device)
+        st, h = B.hf_state_init(self.cfg, self.S.data_ptr(), self.z.data_ptr(),
+                                self.workspace.data_ptr(), ws, 0 if adopt else 1,
+                                next_ev_index, _stream(self.device))
+        _check(st, "hf_state_init")
+        self._h = h
+
+    # ------------------------------------------------------------------ calls
+
+    @property
+    def handle(self) -> int:
+        if self._h is None:
+            raise RuntimeError("state is closed")
+        return self._h
+
+    @property
+    def next_ev_index(self) -> int:
+        return B.hf_next_ev_index(self.handle)
+
+    def _check_input(self, t: torch.Tensor, name: str) -> Tuple[int, int]:
+        if t.dtype != self.dtype or t.device != self.device:
+            raise ValueError(f"{name} must be {self.dtype} on {self.device}")
+        if t.shape[0] != self.cfg.num_heads:
+            raise ValueError(f"{name} must have {self.cfg.num_heads} heads")
+        return _rows(t, name, self.cfg.head_dim)
+
+    def absorb_evicted(self, k_ev: torch.Tensor, v_ev: torch.Tensor,
+                       ev_index: Optional[int] = None) -> None:
+        """S += V^T phi(K), z += sum phi(K) over the evicted tokens (enqueued)."""
+        n, hs = self._check_input(k_ev, "k_ev")
+        n2, hs2 = self._check_input(v_ev, "v_ev")
+        if n2 != n or hs2 != hs:
+            raise ValueError("k_ev and v_ev must have the same length and head stride")
+        idx = self.next_ev_index if ev_index is None else ev_index
+        _check(B.hf_absorb_evicted(self.handle, k_ev.data_ptr(), v_ev.data_ptr(), n, hs, idx,
+                                   _stream(self.device)), "hf_absorb_evicted")
+
+    def attend_chunk(self, q: torch.Tensor, k_win: torch.Tensor, v_win: torch.Tensor,
+                     top_k: int, out: Optional[torch.Tensor] = None,
+                     sel_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """Hybrid attention of the chunk q over the window (and the state); enqueued."""
+        n_q, q_hs = self._check_input(q, "q")
+        n_kv, kv_hs = self._check_input(k_win, "k_win")
+        n_kv2, kv_hs2 = self._check_input(v_win, "v_win")
+        if n_kv2 != n_kv or kv_hs2 != kv_hs:
+            raise ValueError("k_win and v_win must have the same length and head stride")
+        if out is None:
+            out = torch.empty((self.cfg.num_heads, n_q, self.cfg.head_dim), dtype=self.dtype,
+                              device=self.device)
+        n_o, o_hs = self._check_input(out, "out")
+        if n_o != n_q:
+            raise ValueError("out must have as many rows as q")
+        sel_ptr = 0
+        if sel_out is not None:
+            nqb = -(-n_q // self.cfg.block_size)
+            if (sel_out.dtype != torch.int32 or sel_out.device != self.device
+                    or tuple(sel_out.shape) != (self.cfg.num_heads, nqb, top_k)
+                    or not sel_out.is_contiguous()):
+                raise ValueError(f"sel_out must be contiguous int32 [H][{nqb}][{top_k}]")
+            sel_ptr = sel_out.data_ptr()
+        _check(B.hf_attend_chunk(self.handle, q.data_ptr(), n_q, q_hs, k_win.data_ptr(),
+                                 v_win.data_ptr(), n_kv, kv_hs, int(top_k), out.data_ptr(), o_hs,
+                                 sel_ptr, _stream(self.device)), "hf_attend_chunk")
+        return out
+
+    def block_scores(self, q: torch.Tensor, k_win: torch.Tensor) -> torch.Tensor:
+        """fp32 pooled block scores [H][ceil(n_q/B)][ceil(n_kv/B)] (enqueued)."""
+        n_q, q_hs = self._check_input(q, "q")
+        n_kv, kv_hs = self._check_input(k_win, "k_win")
+        bs = self.cfg.block_size
+        scores = torch.empty((self.cfg.num_heads, -(-n_q // bs), -(-n_kv // bs)),
+                             dtype=torch.float32, device=self.device)
+        _check(B.hf_block_scores(self.handle, q.data_ptr(), n_q, q_hs, k_win.data_ptr(), n_kv,
+                                 kv_hs, scores.data_ptr(), _stream(self.device)),
+               "hf_block_scores")
+        return scores
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None:
+            B.hf_state_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def window_frames(step: int, chunk_frames: int, window_frames: int):
+    """Caller-side window bookkeeping of a chunked stream.
+
+    Chunk `step` holds frames [c*step, c*step + c). Before attending it, the frames
+    that left the last-W-frames window since the previous step are evicted (and
+    must be absorbed); the window is the last W frames up to and including the
+    chunk. Returns ((evict_lo, evict_hi), (win_lo, win_hi)) in frames.
+    """
+    end = chunk_frames * (step + 1)
+    lo = end - window_frames if end > window_frames else 0
+    prev_end = chunk_frames * step
+    prev_lo = prev_end - window_frames if prev_end > window_frames else 0
+    return (prev_lo if step > 0 else 0, lo), (lo, end)

@@ -1,0 +1,152 @@
+/*
+ * hf.h -- C ABI of the MI355X (gfx950) hybrid-attention library (libhf.so).
+ *
+ * The library computes the per-chunk hybrid attention of Hybrid Forcing, a
+ * streaming video generation method (arXiv 2604.10103). Sources:
+ *   [EN]  gist.science English summary, "Long-Horizon Streaming Video Generation
+ *         via Hybrid Attention with Decoupled Distillation".
+ *   [ES]  gist.science Spanish summary, "Resumen Tecnico: Hybrid Forcing".
+ *   [ABS] the authors' abstract on the fugumt.com listing of arXiv 2604.10103v1.
+ *
+ * Two paths are summed into one output ([ES] 2.A.2, last bullet):
+ *   - a linear temporal path: a compact per-head state that incrementally absorbs
+ *     the tokens evicted from the sliding window and is read at a cost independent
+ *     of the stream length ([ABS]; [EN] 2.A.1 "Linear Temporal Attention");
+ *   - a block-sparse sliding-window softmax path that scores key blocks by block
+ *     importance and keeps only the top-K blocks per query block ([EN] 2.A.2
+ *     "Block-Sparse Sliding Window Attention").
+ * The pages do not fix the formulas. This library implements (per head, tau =
+ * softmax_scale, phi(x) = x + 1 for x > 0 and exp(x) otherwise):
+ *   state   S = sum_n v_n phi(k_n)^T  (d x d, value-major: S[j][i]),
+ *           z = sum_n phi(k_n)        (d)
+ *   scores  s[i][j] = tau * mean(Q rows of query block i) . mean(K rows of window
+ *           block j), fp32; blocks tile the chunk and the window from row 0 with a
+ *           ragged last block;
+ *   select  per query block, the top_k key blocks by (score desc, index asc),
+ *           listed in ascending index order;
+ *   output  out_r = sum_{t in selected rows} softmax_t(tau q_r . k_t) v_t
+ *                 + S phi(q_r) / (z . phi(q_r) + eps).
+ *
+ * Layouts. Q, K, V and out are [H][N][d] row-major with d fastest; consecutive
+ * heads are `*_head_stride` ELEMENTS apart (so a window can be a pointer offset
+ * into a longer sequence buffer). Element type: bf16 (HF_BF16) or fp32 (HF_F32),
+ * fixed per state. S is [H][d][d] fp32 and z is [H][d] fp32, dense.
+ *
+ * Ownership. The caller allocates and owns all device memory (Q, K, V, out, S, z,
+ * sel_out and the workspace) and keeps it alive until the enqueued work is done.
+ * The library allocates only the small host-side handle, freed by
+ * hf_state_destroy. It never allocates device memory.
+ *
+ * Asynchrony. Calls validate on the host, enqueue on `stream` (a hipStream_t;
+ * NULL = the default stream) and return without synchronising. Device faults
+ * surface at the caller's next synchronisation.
+ *
+ * Errors. Status codes only: no abort, no exception across the ABI, no logging.
+ * On any error nothing is enqueued and the state is unchanged.
+ *   HF_ERR_INVALID_ARG  null pointer; negative size; top_k outside [1, ceil(n_kv/B)]
+ *                       or above max_top_k; a head stride below n*d or not a multiple
+ *                       of 16 bytes; a pointer not 16-byte aligned; a size above the
+ *                       max_* limits of the state.
+ *   HF_ERR_UNSUPPORTED  head_dim, block_size or dtype outside the instantiated set:
+ *                       head_dim in {64, 128}; bf16 with block_size 64; fp32 with
+ *                       block_size 16 or 64.
+ *   HF_ERR_STATE        ev_index differs from the next expected eviction index
+ *                       (a gap or a duplicate in the eviction sequence).
+ *   HF_ERR_HIP          a HIP runtime call or kernel launch failed.
+ *
+ * Threading. One handle must not be used from two host threads at once. Handles
+ * are independent of each other (one per attention layer). Two calls that use
+ * the same workspace must be ordered on one stream.
+ */
+#ifndef HF_H_
+#define HF_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HF_OK = 0,
+  HF_ERR_INVALID_ARG = 1,
+  HF_ERR_UNSUPPORTED = 2,
+  HF_ERR_STATE = 3,
+  HF_ERR_HIP = 4
+} hf_status;
+
+typedef enum { HF_BF16 = 0, HF_F32 = 1 } hf_dtype;
+
+typedef struct {
+  int32_t num_heads;   /* H >= 1 */
+  int32_t head_dim;    /* d: 64 or 128 */
+  int32_t block_size;  /* B: rows per query/key block (bf16: 64; fp32: 16 or 64) */
+  int32_t dtype;       /* hf_dtype of Q, K, V and out; S and z are always fp32 */
+  float eps;           /* added once to the linear normaliser; >= 0 (1e-6 typical) */
+  float softmax_scale; /* tau; 0 selects 1/sqrt(head_dim) */
+  int64_t max_n_q;     /* capacity limits used to size the workspace */
+  int64_t max_n_kv;    /* ceil(max_n_kv / B) must be <= 8192 */
+  int64_t max_n_ev;
+  int32_t max_top_k;
+} hf_config;
+
+typedef struct hf_state hf_state; /* opaque host-side handle */
+
+/* Bytes of device workspace a state with this configuration needs (0 on an
+ * invalid or unsupported configuration). */
+size_t hf_workspace_bytes(const hf_config* cfg);
+
+/* Create a handle over caller-owned S [H][d][d] fp32, z [H][d] fp32 and a
+ * workspace of ws_bytes >= hf_workspace_bytes(cfg) bytes (all device memory,
+ * 16-byte aligned). zero_fill != 0 enqueues S = 0, z = 0 (an empty state, [EN]
+ * 2.A.1); zero_fill == 0 adopts the current contents of S and z (resume from a
+ * checkpoint). next_ev_index is the absolute index of the next token to be
+ * evicted (0 for a new stream). The workspace's internal counters are always
+ * reset. *out receives the handle. */
+hf_status hf_state_init(const hf_config* cfg, float* S, float* z, void* workspace,
+                        size_t ws_bytes, int zero_fill, int64_t next_ev_index,
+                        void* stream, hf_state** out);
+
+/* Absorb n_ev evicted tokens into the state ([ABS]; [EN] 2.A.1; [ES] 2.A.1):
+ * S[h] += V_ev[h]^T phi(K_ev[h]), z[h] += sum_n phi(K_ev[h][n]). k_ev and v_ev are
+ * [H][n_ev][d] with head stride ev_head_stride elements. ev_index is the absolute
+ * index of the first evicted token and must equal the state's next eviction
+ * index (HF_ERR_STATE otherwise); on success the next index advances by n_ev.
+ * n_ev == 0 is a valid no-op. The reduction order is fixed, so results are
+ * bitwise reproducible. */
+hf_status hf_absorb_evicted(hf_state* st, const void* k_ev, const void* v_ev, int64_t n_ev,
+                            int64_t ev_head_stride, int64_t ev_index, void* stream);
+
+/* Hybrid attention of one chunk ([EN] 2.A.1 and 2.A.2; [ES] 2.A.2): q is
+ * [H][n_q][d] (head stride q_head_stride), k_win and v_win are the window
+ * [H][n_kv][d] (head stride kv_head_stride, shared by K and V), which includes
+ * the current chunk; out is [H][n_q][d] (head stride out_head_stride) in the
+ * state's element type. top_k key blocks are kept per query block. If sel_out
+ * is not NULL it receives the selection, int32 [H][ceil(n_q/B)][top_k], each
+ * row ascending. n_q == 0 is a valid no-op. */
+hf_status hf_attend_chunk(hf_state* st, const void* q, int64_t n_q, int64_t q_head_stride,
+                          const void* k_win, const void* v_win, int64_t n_kv,
+                          int64_t kv_head_stride, int32_t top_k, void* out,
+                          int64_t out_head_stride, int32_t* sel_out, void* stream);
+
+/* The pooled block importance scores alone ([EN] 2.A.2), the first stage of
+ * hf_attend_chunk: scores_out is fp32 [H][ceil(n_q/B)][ceil(n_kv/B)], dense. The
+ * same kernels and arithmetic as hf_attend_chunk produce it. */
+hf_status hf_block_scores(hf_state* st, const void* q, int64_t n_q, int64_t q_head_stride,
+                          const void* k_win, int64_t n_kv, int64_t kv_head_stride,
+                          float* scores_out, void* stream);
+
+/* Absolute index of the next token the state expects to absorb (-1 if st is NULL). */
+int64_t hf_next_ev_index(const hf_state* st);
+
+/* Free the handle (not the caller's device memory). NULL is allowed. */
+void hf_state_destroy(hf_state* st);
+
+/* Static description of a status code. */
+const char* hf_status_string(hf_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HF_H_ */

@@ -1,0 +1,296 @@
+"""Parity of the HIP path (through the C ABI) with the float64 oracle, on the GPU.
+
+Inputs are the seeded synthetic workloads of `synth`; the oracle sees the exact
+same values (bf16 or fp32) widened to float64. Tolerances and the near-tie rule
+for the selection are in tests/hfutil.py.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from synth.inputs import frame_block
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import hybrid_linear_block_amd as hla  # the HIP library must load: no fallback path
+else:
+    hla = None
+from hfutil import (compare_out, compare_sel, dev_bf16, dev_f32, host_f64,  # noqa: E402
+                    row_mask, state_close)
+
+TORCH_DT = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+def _draw(seed, stream, H, n, d, std, dtype):
+    x = frame_block(seed, stream, 0, H, n, d, std)
+    if dtype == "bf16":
+        bits = synth.bf16_bits(x)
+        return dev_bf16(bits), oracle.as_f64(bits, "bf16")
+    return dev_f32(x), x.astype(np.float64)
+
+
+def _run_random_case(H, d, B, dtype, n_q, n_kv, n_ev, top_k, seed):
+    std = 1.0 / np.sqrt(d) if dtype == "bf16" else 1.0
+    qd, q = _draw(seed, 11, H, n_q, d, std, dtype)
+    kd, k = _draw(seed, 12, H, n_kv, d, std, dtype)
+    vd, v = _draw(seed, 13, H, n_kv, d, std, dtype)
+    kevd, kev = _draw(seed, 14, H, max(n_ev, 1), d, std, dtype)
+    vevd, vev = _draw(seed, 15, H, max(n_ev, 1), d, std, dtype)
+    st = hla.HybridAttentionState(H, d, B, TORCH_DT[dtype], max_n_q=max(n_q, 1), max_n_kv=n_kv,
+                                  max_n_ev=max(n_ev, 1), max_top_k=top_k)
+    if n_ev:
+        st.absorb_evicted(kevd[:, :n_ev], vevd[:, :n_ev])
+    nqb = -(-n_q // B)
+    sel = torch.empty((H, nqb, top_k), dtype=torch.int32, device="cuda")
+    out = st.attend_chunk(qd, kd, vd, top_k, sel_out=sel)
+    torch.cuda.synchronize()
+    S, z = oracle.state_init(H, d)
+    if n_ev:
+        oracle.absorb(S, z, kev[:, :n_ev], vev[:, :n_ev])
+    state_close(host_f64(st.S), host_f64(st.z), S, z, dtype)
+    sel_ref, s32 = oracle.select(q, k, B, top_k)
+    differ = compare_sel(sel.cpu().numpy(), sel_ref, s32, top_k)
+    ref = oracle.attend_with_sel(q, k, v, sel_ref, S, z, B)
+    stats = compare_out(host_f64(out), ref, dtype, row_mask(ref.shape, differ, B))
+    st.close()
+    return stats
+
+
+# ------------------------------------------------------------ small full cases
+
+
+@pytest.mark.parametrize("H,d,B,dtype,n_q,n_kv,n_ev,top_k", [
+    (2, 128, 64, "bf16", 200, 600, 300, 3),   # 3 full query blocks + 8-row tail; 24-row key tail
+    (2, 64, 64, "bf16", 130, 333, 65, 2),
+    (1, 128, 64, "bf16", 4680 // 3, 1560 * 3, 1560, 19),
+    (1, 64, 16, "f32", 100, 150, 77, 4),      # 4-row query tail, 6-row key tail
+    (2, 128, 16, "f32", 48, 80, 33, 5),
+    (2, 64, 64, "f32", 150, 260, 70, 2),
+    (1, 128, 64, "f32", 64, 256, 64, 4),
+])
+def test_random_case_full_compare(H, d, B, dtype, n_q, n_kv, n_ev, top_k):
+    print(f"case H={H} d={d} B={B} {dtype} n_q={n_q} n_kv={n_kv} n_ev={n_ev} K={top_k}", flush=True)
+    _run_random_case(H, d, B, dtype, n_q, n_kv, n_ev, top_k, seed=100 + n_q)
+
+
+@pytest.mark.parametrize("dtype,d,B", [("bf16", 128, 64), ("f32", 64, 16)])
+@pytest.mark.parametrize("n_q,n_kv,top_k,n_ev", [
+    (1, 1, 1, 0),      # one query row, one key row, empty state
+    (1, 70, 2, 1),     # single query row against a ragged window
+    (65, 64, 1, 5),    # a single key block, two query blocks (1-row tail)
+    (64, 200, "all", 3),  # top-K = all key blocks: dense sliding-window attention
+])
+def test_edge_cases(dtype, d, B, n_q, n_kv, top_k, n_ev):
+    nkb = -(-n_kv // B)
+    K = nkb if top_k == "all" else min(top_k, nkb)
+    print(f"edge {dtype} n_q={n_q} n_kv={n_kv} K={K} n_ev={n_ev}", flush=True)
+    _run_random_case(1, d, B, dtype, n_q, n_kv, n_ev, K, seed=7)
+
+
+# --------------------------------------------------------------- tiny fp32 stream
+
+
+def test_tiny_f32_stream():
+    wl = synth.WORKLOADS["tiny_f32"]
+    T, c, W, B, K = wl.frame_tokens, wl.chunk_frames, wl.window_frames, wl.block, wl.top_k
+    q, k, v = synth.tiny_f32_frames(1)
+    qd, kd, vd = dev_f32(q), dev_f32(k), dev_f32(v)
+    q64, k64, v64 = (x.astype(np.float64) for x in (q, k, v))
+    st = hla.HybridAttentionState(1, 64, B, torch.float32, max_n_q=c * T, max_n_kv=W * T,
+                                  max_n_ev=c * T, max_top_k=K, eps=wl.eps)
+    S, z = oracle.state_init(1, 64)
+    for t in range(3):
+        (e0, e1), (w0, w1) = hla.window_frames(t, c, W)
+        assert ((e0, e1), (w0, w1)) == oracle.stream_step_frames(t, c, W)
+        if e1 > e0:
+            st.absorb_evicted(kd[:, e0 * T:e1 * T], vd[:, e0 * T:e1 * T])
+            oracle.absorb(S, z, k64[:, e0 * T:e1 * T], v64[:, e0 * T:e1 * T])
+        qs = slice((w1 - c) * T, w1 * T)
+        ws = slice(w0 * T, w1 * T)
+        sel = torch.empty((1, c * T // B, K), dtype=torch.int32, device="cuda")
+        out = st.attend_chunk(qd[:, qs], kd[:, ws], vd[:, ws], K, sel_out=sel)
+        torch.cuda.synchronize()
+        out_ref, sel_ref, s32 = oracle.attend(q64[:, qs], k64[:, ws], v64[:, ws], S, z, B, K,
+                                              eps=wl.eps)
+        assert np.array_equal(sel.cpu().numpy(), sel_ref)
+        compare_out(host_f64(out), out_ref, "f32")
+        state_close(host_f64(st.S), host_f64(st.z), S, z, "f32")
+    assert st.next_ev_index == 4 * T
+
+
+# ------------------------------------------------------------ Wan-like bf16 layer
+
+
+def _sample_blocks(H, nqb, rng, extra=24):
+    blocks = {(0, i) for i in range(nqb)} | {(h, nqb - 1) for h in range(H)}
+    while len(blocks) < nqb + H + extra:
+        blocks.add((int(rng.integers(H)), int(rng.integers(nqb))))
+    return sorted(blocks)
+
+
+def _check_layer(inp, top_k, seed, st=None, sel_expect=None):
+    """Absorb the evicted span, attend the chunk; compare with the oracle on samples."""
+    wl = synth.WORKLOADS["wan_layer_bf16"]
+    H, d, B = wl.heads, wl.head_dim, wl.block
+    qd, kd, vd = dev_bf16(inp["q"]), dev_bf16(inp["k"]), dev_bf16(inp["v"])
+    e0, e1, w0, w1 = inp["ev_lo"], inp["ev_hi"], inp["win_lo"], inp["win_hi"]
+    n_q, n_kv = qd.shape[1], w1 - w0
+    if st is None:
+        st = hla.HybridAttentionState(H, d, B, torch.bfloat16, max_n_q=n_q, max_n_kv=n_kv,
+                                      max_n_ev=e1 - e0, max_top_k=top_k)
+    st.absorb_evicted(kd[:, e0:e1], vd[:, e0:e1])
+    nqb = -(-n_q // B)
+    sel = torch.empty((H, nqb, top_k), dtype=torch.int32, device="cuda")
+    out = st.attend_chunk(qd, kd[:, w0:w1], vd[:, w0:w1], top_k, sel_out=sel)
+    torch.cuda.synchronize()
+    q64 = oracle.as_f64(inp["q"], "bf16")
+    k64 = oracle.as_f64(inp["k"], "bf16")
+    v64 = oracle.as_f64(inp["v"], "bf16")
+    S, z = oracle.state_init(H, d)
+    oracle.absorb(S, z, k64[:, e0:e1], v64[:, e0:e1])
+    state_close(host_f64(st.S), host_f64(st.z), S, z, "bf16")
+    sel_ref, s32 = oracle.select(q64, k64[:, w0:w1], B, top_k)
+    sel_dev = sel.cpu().numpy()
+    if sel_expect is not None:
+        assert np.array_equal(sel_dev, sel_expect)
+    differ = compare_sel(sel_dev, sel_ref, s32, top_k)
+    blocks = _sample_blocks(H, nqb, np.random.default_rng(seed))
+    ref = oracle.attend_with_sel(q64, k64[:, w0:w1], v64[:, w0:w1], sel_ref, S, z, B,
+                                 blocks=blocks)
+    stats = compare_out(host_f64(out), ref, "bf16", row_mask(ref.shape, differ, B))
+    return st, stats, int(differ.sum())
+
+
+def test_wan_layer_bf16():
+    wl = synth.WORKLOADS["wan_layer_bf16"]
+    inp = synth.wan_layer_inputs(2024)
+    K = synth.top_k_count(wl.top_k_frac, 220)
+    st, stats, n_diff = _check_layer(inp, K, seed=1)
+    print("wan layer", stats, "rows with near-tie differences:", n_diff, flush=True)
+
+
+def test_block_scores_match_oracle():
+    inp = synth.wan_layer_inputs(7)
+    H, B = 12, 64
+    st = hla.HybridAttentionState(H, 128, B, torch.bfloat16, max_n_q=4680, max_n_kv=14040,
+                                  max_n_ev=4680, max_top_k=55)
+    qd, kd = dev_bf16(inp["q"]), dev_bf16(inp["k"])
+    sc = st.block_scores(qd, kd[:, 4680:])
+    torch.cuda.synchronize()
+    ref = oracle.block_scores(oracle.as_f64(inp["q"], "bf16"),
+                              oracle.as_f64(inp["k"][:, 4680:], "bf16"), B)
+    err = np.abs(host_f64(sc) - ref).max() / np.abs(ref).max()
+    assert err < 1e-5, err
+
+
+def test_determinism_bitwise():
+    inp = synth.wan_layer_inputs(5)
+    outs = []
+    for rep in range(2):
+        qd, kd, vd = dev_bf16(inp["q"]), dev_bf16(inp["k"]), dev_bf16(inp["v"])
+        st = hla.HybridAttentionState(12, 128, 64, torch.bfloat16, max_n_q=4680, max_n_kv=14040,
+                                      max_n_ev=4680, max_top_k=55)
+        st.absorb_evicted(kd[:, :4680], vd[:, :4680])
+        out = st.attend_chunk(qd, kd[:, 4680:], vd[:, 4680:], 55)
+        torch.cuda.synchronize()
+        outs.append((out.view(torch.int16).cpu().numpy(), st.S.cpu().numpy(), st.z.cpu().numpy()))
+    for a, b in zip(outs[0], outs[1]):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+def test_resume_from_saved_state_bitwise():
+    T, H = 1560, 12
+    ls = synth.LongStream(9)
+    k = dev_bf16(ls.frames("k", 0, 9))
+    v = dev_bf16(ls.frames("v", 0, 9))
+    q = dev_bf16(ls.frames("q", 6, 9))
+    mk = dict(max_n_q=3 * T, max_n_kv=9 * T, max_n_ev=3 * T, max_top_k=55)
+    a = hla.HybridAttentionState(H, 128, 64, torch.bfloat16, **mk)
+    a.absorb_evicted(k[:, :3 * T], v[:, :3 * T])
+    torch.cuda.synchronize()
+    b = hla.HybridAttentionState(H, 128, 64, torch.bfloat16, S=a.S.cpu(), z=a.z.cpu(),
+                                 next_ev_index=a.next_ev_index, **mk)
+    for s in (a, b):
+        s.absorb_evicted(k[:, 3 * T:6 * T], v[:, 3 * T:6 * T])
+    oa = a.attend_chunk(q, k[:, 3 * T:], v[:, 3 * T:], 55)
+    ob = b.attend_chunk(q, k[:, 3 * T:], v[:, 3 * T:], 55)
+    torch.cuda.synchronize()
+    assert torch.equal(a.S, b.S) and torch.equal(a.z, b.z)
+    assert torch.equal(oa.view(torch.int16), ob.view(torch.int16))
+
+
+def test_eviction_sequence_errors_leave_state_unchanged():
+    H, d, T = 2, 128, 128
+    st = hla.HybridAttentionState(H, d, 64, torch.bfloat16, max_n_q=T, max_n_kv=T, max_n_ev=T,
+                                  max_top_k=2)
+    k = torch.randn(H, T, d, device="cuda").to(torch.bfloat16)
+    st.absorb_evicted(k, k)
+    torch.cuda.synchronize()
+    S0 = st.S.clone()
+    for bad in (0, T - 1, T + 1):
+        with pytest.raises(hla.HfError) as ei:
+            st.absorb_evicted(k, k, ev_index=bad)
+        assert ei.value.status == hla.HF_ERR_STATE
+    with pytest.raises(hla.HfError) as ei:
+        st.attend_chunk(k, k, k, 3)  # top_k > number of key blocks
+    assert ei.value.status == hla.HF_ERR_INVALID_ARG
+    torch.cuda.synchronize()
+    assert torch.equal(st.S, S0) and st.next_ev_index == T
+
+
+def test_duplicate_key_block_tie_goes_to_lower_index():
+    inp = synth.wan_layer_inputs(31)
+    w0 = inp["win_lo"]
+    kbits = inp["k"].copy()
+    kbits[:, w0 + 2 * 64:w0 + 3 * 64] = kbits[:, w0 + 7 * 64:w0 + 8 * 64]  # block 2 := block 7
+    q64 = oracle.as_f64(inp["q"], "bf16")
+    k64 = oracle.as_f64(kbits[:, w0:], "bf16")
+    s32 = oracle.select(q64, k64, 64, 1)[1]
+    st = hla.HybridAttentionState(12, 128, 64, torch.bfloat16, max_n_q=4680, max_n_kv=14040,
+                                  max_n_ev=1, max_top_k=220)
+    qd, kd = dev_bf16(inp["q"]), dev_bf16(kbits)
+    checked = 0
+    for h in range(12):
+        for i in range(0, 74, 7):
+            row = s32[h, i].astype(np.float64)
+            sp = row[2]
+            others = np.delete(row, [2, 7])
+            if np.abs(others - sp).min() < 1e-3 * np.abs(row).max():
+                continue  # the pair is near another block's score: not a clean tie test
+            K = int((row > sp).sum()) + 1
+            sel = torch.empty((12, 74, K), dtype=torch.int32, device="cuda")
+            st.attend_chunk(qd, kd[:, w0:], kd[:, w0:], K, sel_out=sel)
+            torch.cuda.synchronize()
+            r = sel[h, i].cpu().numpy()
+            assert 2 in r and 7 not in r, (h, i, K, r)
+            checked += 1
+            break
+    assert checked >= 6
+
+
+# ---------------------------------------------------------- planted structure
+
+
+@pytest.mark.parametrize("frac", synth.inputs.PLANTED_FRACTIONS)
+def test_planted_sparsity_sweep(frac):
+    inp = synth.planted_inputs(77, frac)
+    st, stats, n_diff = _check_layer(inp, inp["top_k"], seed=3, sel_expect=inp["planted"])
+    assert n_diff == 0
+    print("planted", frac, stats, flush=True)
+
+
+# ---------------------------------------------------------------- full depth
+
+
+def test_full_depth_layers_sampled():
+    """Several of the 30 independent layers, each with its own seed, run back-to-back."""
+    wl = synth.WORKLOADS["full_depth_bf16"]
+    K = synth.top_k_count(wl.top_k_frac, 220)
+    for layer in (0, 13, 29):
+        inp = synth.wan_layer_inputs(5000 + layer)
+        _, stats, _ = _check_layer(inp, K, seed=layer)
+        print("layer", layer, stats, flush=True)

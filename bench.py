@@ -1,0 +1,320 @@
+#!/usr/bin/env python3
+"""Benchmark: one step of the per-chunk hybrid attention on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input: the
+absorb of the evicted tokens into the linear state (hf_absorb_evicted) and the
+hybrid attention of the chunk (hf_attend_chunk: block pooling, block scores and
+top-K selection, block-sparse attention with the fused linear read). The default
+workload is one Wan-1.3B-like layer: 12 heads, d = 128, a 3-frame chunk (4680
+query tokens) over a 9-frame window (14040 key/value tokens), 64-token blocks,
+top-K = 55 of 220 key blocks, 4680 evicted tokens. Inputs are resident in HBM
+before timing starts; `--sets` independent input sets (each with its own state)
+are rotated so that consecutive steps do not hit a warm cache.
+
+Prints one JSON line on stdout. The effective throughput counts the algorithmic
+FLOPs of the step (absorb 2*n_ev*d^2*H; scores 2*Nqb*Nkb*d*H; sparse attention
+4*|Q_i|*|K_j|*d over the executed (query block, selected key block) pairs with
+actual row counts; linear read 2*n_q*d*(d+1)*H).
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "hybrid-attention ms/chunk/layer and effective TFLOP/s (% of MFMA peak), 1 GPU"
+PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # MI355X dense MFMA peaks
+PEAK_HBM_GBS = 8000.0
+SWA_SOURCES = ("hybrid_linear_block_amd/csrc/hf_sparse_swa.hip",
+               "hybrid_linear_block_amd/csrc/hf_device.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_sparse_swa_wan_layer.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=40)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--sets", type=int, default=4, help="rotated input sets (cache-cold timing)")
+    p.add_argument("--workload", default="wan_layer_bf16",
+                   choices=["wan_layer_bf16", "full_depth_bf16"])
+    p.add_argument("--seed", type=int, default=1234)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-reps", type=int, default=3)
+    p.add_argument("--calibrate-copy-mib", type=int, default=0,
+                   help="also run device copies of this size (HBM counter calibration)")
+    return p.parse_args()
+
+
+def swa_source_sha():
+    h = hashlib.sha256()
+    for rel in SWA_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+class LayerSet:
+    """One input set of the Wan-like layer resident on the GPU, with its own state."""
+
+    def __init__(self, hla, torch, synth, seed, top_k):
+        inp = synth.wan_layer_inputs(seed)
+        dev = torch.device("cuda:0")
+        to = lambda b: torch.from_numpy(b.view("int16")).view(torch.bfloat16).to(dev)  # noqa
+        self.q = to(inp["q"])
+        self.k = to(inp["k"])
+        self.v = to(inp["v"])
+        e0, e1, w0, w1 = inp["ev_lo"], inp["ev_hi"], inp["win_lo"], inp["win_hi"]
+        self.kev, self.vev = self.k[:, e0:e1], self.v[:, e0:e1]
+        self.kw, self.vw = self.k[:, w0:w1], self.v[:, w0:w1]
+        self.H, self.n_q, self.d = self.q.shape
+        self.n_kv, self.n_ev = w1 - w0, e1 - e0
+        self.top_k = top_k
+        self.out = torch.empty_like(self.q)
+        self.st = hla.HybridAttentionState(self.H, self.d, 64, torch.bfloat16,
+                                           max_n_q=self.n_q, max_n_kv=self.n_kv,
+                                           max_n_ev=self.n_ev, max_top_k=top_k, device=dev)
+        self.inp = inp
+
+    def step(self):
+        self.st.absorb_evicted(self.kev, self.vev)
+        self.st.attend_chunk(self.q, self.kw, self.vw, self.top_k, out=self.out)
+
+    def flops(self, torch, sel):
+        """Algorithmic FLOPs per kernel for this set's selection (numpy int math)."""
+        import numpy as np
+        H, n_q, d, B = self.H, self.n_q, self.d, 64
+        nqb, nkb = -(-n_q // B), -(-self.n_kv // B)
+        qrows = np.minimum(B, n_q - B * np.arange(nqb))
+        krows = np.minimum(B, self.n_kv - B * np.arange(nkb))
+        swa = 4 * d * int((qrows[None, :, None] * krows[sel]).sum())
+        lin = 2 * n_q * d * (d + 1) * H
+        return dict(absorb=2 * self.n_ev * d * d * H, block_pool=(n_q + self.n_kv) * d * H,
+                    score_select=2 * nqb * nkb * d * H, sparse_swa=swa + lin,
+                    sparse_swa_softmax_part=swa)
+
+    def bytes(self):
+        H, n_q, d, B = self.H, self.n_q, self.d, 64
+        nqb, nkb = -(-n_q // B), -(-self.n_kv // B)
+        return dict(
+            absorb=2 * self.n_ev * d * 2 * H + 2 * (d * d + d) * 4 * H,
+            block_pool=(n_q + self.n_kv) * d * 2 * H + (nqb + nkb) * d * 4 * H,
+            score_select=(nqb + nkb) * d * 4 * H + nqb * self.top_k * 4 * H,
+            sparse_swa=(n_q + 2 * self.n_kv) * d * 2 * H + n_q * d * 2 * H + (d * d + d) * 4 * H)
+
+
+def cpu_baseline(layer: LayerSet, reps: int):
+    """The float64 oracle on the host cores: the same layer step, median of `reps`."""
+    import numpy as np
+    import oracle
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        cores = max((i.get("num_threads") or 1) for i in info) if info else 1
+        blas = ",".join(sorted({i.get("internal_api", "?") for i in info}))
+    except Exception:  # pragma: no cover
+        cores, blas = os.cpu_count(), "unknown"
+    inp = layer.inp
+    q = oracle.as_f64(inp["q"], "bf16")
+    k = oracle.as_f64(inp["k"], "bf16")
+    v = oracle.as_f64(inp["v"], "bf16")
+    e0, e1, w0, w1 = inp["ev_lo"], inp["ev_hi"], inp["win_lo"], inp["win_hi"]
+    times, sel = [], None
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        S, z = oracle.state_init(layer.H, layer.d)
+        oracle.absorb(S, z, k[:, e0:e1], v[:, e0:e1])
+        _, sel, _ = oracle.attend(q, k[:, w0:w1], v[:, w0:w1], S, z, 64, layer.top_k)
+        times.append(time.perf_counter() - t0)
+    t = statistics.median(times)
+    fl = layer.flops(None, sel)
+    total = fl["absorb"] + fl["score_select"] + fl["sparse_swa"]
+    return dict(value=total / t / 1e12, unit="TFLOP/s", cores=int(cores), kind="oracle",
+                sample=f"one full Wan-like layer step (absorb {layer.n_ev} tokens + attend "
+                       f"{layer.n_q} query tokens, all {layer.H} heads), float64 NumPy "
+                       f"({blas} BLAS), median of {reps}",
+                ms_per_step=t * 1e3)
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on exactly one GPU: the hybrid attention path is built and "
+              "measured per GPU (heads shard across GPUs with no exchange inside the path); "
+              f"--gpus {args.gpus} is not supported.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import hybrid_linear_block_amd as hla
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    wl = synth.WORKLOADS[args.workload]
+    top_k = synth.top_k_count(wl.top_k_frac, -(-wl.window_tokens // wl.block))
+    n_sets = wl.layers if args.workload == "full_depth_bf16" else max(1, args.sets)
+    t0 = time.time()
+    sets = [LayerSet(hla, torch, synth, args.seed + i, top_k) for i in range(n_sets)]
+    log(f"[bench] {n_sets} input sets resident ({time.time() - t0:.1f}s)")
+
+    # Selection of every set (for the executed-FLOP count); not timed.
+    flops = []
+    for s in sets:
+        sel = torch.empty((s.H, -(-s.n_q // 64), top_k), dtype=torch.int32, device="cuda")
+        s.st.attend_chunk(s.q, s.kw, s.vw, top_k, out=s.out, sel_out=sel)
+        torch.cuda.synchronize()
+        flops.append(s.flops(torch, sel.cpu().numpy()))
+
+    per_step_layers = n_sets if args.workload == "full_depth_bf16" else 1
+
+    def run(k):
+        if args.workload == "full_depth_bf16":
+            for s in sets:
+                s.step()
+        else:
+            sets[k % n_sets].step()
+
+    def step_flops(k):
+        idx = range(n_sets) if args.workload == "full_depth_bf16" else [k % n_sets]
+        return sum(flops[i]["absorb"] + flops[i]["score_select"] + flops[i]["sparse_swa"]
+                   for i in idx)
+
+    for k in range(args.warmup):
+        run(k)
+    torch.cuda.synchronize()
+    log("[bench] warmup done")
+
+    # Timed region: K steps, bracketed by device synchronisation.
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    ev0.record()
+    for k in range(args.steps):
+        run(k)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    total_flop = sum(step_flops(k) for k in range(args.steps))
+    value = total_flop / (ms_step * args.steps / 1e3) / 1e12
+    log(f"[bench] {ms_step:.4f} ms/step (wall {wall * 1e3 / args.steps:.4f})")
+
+    # Same K steps again with HIP events around every kernel (on the launch stream).
+    for s in sets:
+        s.st.profile_start(args.steps + 2)
+    ev0.record()
+    for k in range(args.steps):
+        run(k)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms_step_ev = ev0.elapsed_time(ev1) / args.steps
+    tot = {}
+    for s in sets:
+        for name, (ms, n) in s.st.profile_stop().items():
+            a = tot.setdefault(name, [0.0, 0])
+            a[0] += ms
+            a[1] += n
+    kern_us = {k: (v[0] / v[1] * 1e3 if v[1] else None) for k, v in tot.items()}
+    log(f"[bench] per-kernel us: {kern_us}")
+
+    # Cache-warm variant: one input set repeated.
+    ms_warm = None
+    if args.workload == "wan_layer_bf16":
+        torch.cuda.synchronize()
+        ev0.record()
+        for k in range(args.steps):
+            sets[0].step()
+        ev1.record()
+        torch.cuda.synchronize()
+        ms_warm = ev0.elapsed_time(ev1) / args.steps
+
+    # Roofline of the dominant kernel (sparse_swa): executed algorithmic FLOPs per launch
+    # over its average event-timed duration.
+    swa_flop = statistics.mean(f["sparse_swa"] for f in flops)
+    swa_us = kern_us["sparse_swa"]
+    achieved = swa_flop / (swa_us * 1e-6) / 1e12
+    peak = PEAK_MFMA_TFLOPS[wl.dtype]
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE) and args.workload == "wan_layer_bf16":
+        tr = json.load(open(TRAFFIC_FILE))
+        if tr.get("source_sha256") == swa_source_sha():
+            traffic = tr.get("hbm_bytes_per_launch")
+    roofline = dict(bound="mfma", achieved=round(achieved, 2), peak=peak, unit="TFLOP/s",
+                    frac=round(achieved / peak, 4), traffic=traffic, kernel="sparse_swa",
+                    flop_per_launch=int(swa_flop), avg_launch_us=round(swa_us, 2))
+
+    kernels = {}
+    for name in ("absorb", "block_pool", "score_select", "sparse_swa"):
+        us = kern_us.get(name)
+        b = sets[0].bytes()[name]
+        f = statistics.mean(fl[name] for fl in flops)
+        kernels[name] = dict(avg_us=None if us is None else round(us, 2),
+                             algo_bytes=int(b), algo_flop=int(f),
+                             gbs=None if not us else round(b / (us * 1e-6) / 1e9, 1),
+                             tflops=None if not us else round(f / (us * 1e-6) / 1e12, 2))
+
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copies of {args.calibrate_copy_mib} MiB done")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the float64 oracle on the host ...")
+        cpu = cpu_baseline(sets[0], args.cpu_reps)
+        if args.workload == "full_depth_bf16":
+            cpu["value_note"] = "per-layer oracle time; 30 layers are 30x this time"
+
+    s0 = sets[0]
+    res = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "ms_per_chunk_per_layer": round(ms_step / per_step_layers, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded N(0,1)/sqrt(d) bf16 Q/K/V; no weights or dataset)",
+        "config": {
+            "workload": (f"{args.workload}: {per_step_layers} layer(s) per step, {s0.H} heads, "
+                         f"d={s0.d}, chunk {s0.n_q} query tokens (3 latent frames of 1560), "
+                         f"window {s0.n_kv} tokens (9 frames), block 64, top-K {top_k} of "
+                         f"{-(-s0.n_kv // 64)}, {s0.n_ev} evicted tokens absorbed per step"),
+            "heads": s0.H, "head_dim": s0.d, "n_q": s0.n_q, "n_kv": s0.n_kv, "n_ev": s0.n_ev,
+            "block": 64, "top_k": top_k, "input_sets": n_sets, "layers_per_step": per_step_layers,
+        },
+        "pct_of_mfma_peak": round(100 * value / peak, 3),
+        "ms_per_step_with_kernel_events": round(ms_step_ev, 5),
+        "ms_per_step_cache_warm": None if ms_warm is None else round(ms_warm, 5),
+        "kernels": kernels,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -47,7 +47,7 @@ def _load():
     if not os.path.exists(_LIB_PATH):
         raise ImportError(
             f"{_LIB_PATH} is missing: build the HIP library first "
-            "(python -m hybrid_linear_block_amd.build, or __graft_entry__.build())")
+            "(python hybrid_linear_block_amd/build.py, or __graft_entry__.build())")
     lib = ctypes.CDLL(_LIB_PATH)
     P = c_void_p
     sig = {
@@ -58,6 +58,8 @@ def _load():
         "hf_attend_chunk": (c_int, [P, P, c_int64, c_int64, P, P, c_int64, c_int64, c_int32, P,
                                     c_int64, P, P]),
         "hf_block_scores": (c_int, [P, P, c_int64, c_int64, P, c_int64, c_int64, P, P]),
+        "hf_profile_start": (c_int, [P, c_int32]),
+        "hf_profile_stop": (c_int, [P, POINTER(ctypes.c_double), POINTER(c_int32)]),
         "hf_next_ev_index": (c_int64, [P]),
         "hf_state_destroy": (None, [P]),
         "hf_status_string": (ctypes.c_char_p, [c_int]),
@@ -72,7 +74,9 @@ def _load():
 _lib = _load()
 
 EXPORTED = ("hf_workspace_bytes", "hf_state_init", "hf_absorb_evicted", "hf_attend_chunk",
-            "hf_block_scores", "hf_next_ev_index", "hf_state_destroy", "hf_status_string")
+            "hf_block_scores", "hf_profile_start", "hf_profile_stop", "hf_next_ev_index",
+            "hf_state_destroy", "hf_status_string")
+HF_KERNEL_NAMES = ("absorb", "block_pool", "score_select", "sparse_swa")
 
 
 def library_path() -> str:
@@ -116,6 +120,18 @@ def hf_block_scores(state: int, q: int, n_q: int, q_head_stride: int, k_win: int
                     kv_head_stride: int, scores_out: int, stream: int) -> int:
     return _lib.hf_block_scores(state, q, n_q, q_head_stride, k_win, n_kv, kv_head_stride,
                                 scores_out, stream)
+
+
+def hf_profile_start(state: int, max_launches: int) -> int:
+    return _lib.hf_profile_start(state, int(max_launches))
+
+
+def hf_profile_stop(state: int):
+    """Returns (status, {kernel name: (total ms, launches)})."""
+    ms = (ctypes.c_double * len(HF_KERNEL_NAMES))()
+    n = (c_int32 * len(HF_KERNEL_NAMES))()
+    st = _lib.hf_profile_stop(state, ms, n)
+    return st, {k: (ms[i], n[i]) for i, k in enumerate(HF_KERNEL_NAMES)}
 
 
 def hf_next_ev_index(state) -> int:

@@ -7,6 +7,7 @@
 
 #include <cmath>
 #include <new>
+#include <vector>
 
 #include "../../include/hf.h"
 #include "hf_launch.h"
@@ -25,8 +26,11 @@ struct hf_state {
   float* pooled_k;
   int32_t* sel;
   float* partials;
-  unsigned* tickets;
-  size_t tickets_bytes;
+  // Per-kernel timing (hf_profile_start / hf_profile_stop).
+  bool prof_on = false;
+  int prof_cap = 0;
+  std::vector<hipEvent_t> prof_ev[HF_KERNEL_COUNT];  // start/end pairs
+  int prof_n[HF_KERNEL_COUNT] = {0, 0, 0, 0};
 };
 
 namespace {
@@ -61,7 +65,7 @@ hf_status check_config(const hf_config* c) {
 }
 
 struct Layout {
-  size_t pooled_q, pooled_k, sel, partials, tickets, total, tickets_bytes;
+  size_t pooled_q, pooled_k, sel, partials, total;
 };
 
 Layout layout(const hf_config* c) {
@@ -78,9 +82,6 @@ Layout layout(const hf_config* c) {
   off += round_up(H * nqb * (size_t)c->max_top_k * 4);
   L.partials = off;
   off += round_up(hf::absorb_partial_floats((int)H, (int)d) * 4);
-  L.tickets = off;
-  L.tickets_bytes = hf::absorb_ticket_count((int)H, (int)d) * 4;
-  off += round_up(L.tickets_bytes);
   L.total = off;
   return L;
 }
@@ -94,6 +95,34 @@ hf_status on_device(int device, F fn) {
   const hipError_t e = fn();
   if (cur != device) (void)hipSetDevice(cur);
   return e == hipSuccess ? HF_OK : HF_ERR_HIP;
+}
+
+void prof_release(hf_state* st) {
+  for (int k = 0; k < HF_KERNEL_COUNT; ++k) {
+    for (hipEvent_t e : st->prof_ev[k]) (void)hipEventDestroy(e);
+    st->prof_ev[k].clear();
+    st->prof_n[k] = 0;
+  }
+  st->prof_on = false;
+  st->prof_cap = 0;
+}
+
+// Launch `fn` (one kernel) on stream s, bracketed by profiling events if enabled.
+template <typename F>
+hipError_t timed(hf_state* st, int kernel, hipStream_t s, F fn) {
+  const bool rec = st->prof_on && st->prof_n[kernel] < st->prof_cap;
+  const int i = st->prof_n[kernel];
+  if (rec) {
+    const hipError_t e = hipEventRecord(st->prof_ev[kernel][2 * i], s);
+    if (e != hipSuccess) return e;
+  }
+  const hipError_t r = fn();
+  if (rec && r == hipSuccess) {
+    const hipError_t e = hipEventRecord(st->prof_ev[kernel][2 * i + 1], s);
+    if (e != hipSuccess) return e;
+    st->prof_n[kernel] = i + 1;
+  }
+  return r;
 }
 
 hf_status check_tensor(const void* p, int64_t n, int64_t head_stride, const hf_config& c) {
@@ -141,8 +170,6 @@ hf_status hf_state_init(const hf_config* cfg, float* S, float* z, void* workspac
   st->pooled_k = reinterpret_cast<float*>(st->ws + L.pooled_k);
   st->sel = reinterpret_cast<int32_t*>(st->ws + L.sel);
   st->partials = reinterpret_cast<float*>(st->ws + L.partials);
-  st->tickets = reinterpret_cast<unsigned*>(st->ws + L.tickets);
-  st->tickets_bytes = L.tickets_bytes;
   if (hipGetDevice(&st->device) != hipSuccess) {
     delete st;
     return HF_ERR_HIP;
@@ -150,8 +177,8 @@ hf_status hf_state_init(const hf_config* cfg, float* S, float* z, void* workspac
   hipStream_t s = static_cast<hipStream_t>(stream);
   const size_t H = (size_t)cfg->num_heads, d = (size_t)cfg->head_dim;
   const hf_status r = on_device(st->device, [&]() -> hipError_t {
-    hipError_t e = hf::launch_fill_zero(st->tickets, st->tickets_bytes, s);
-    if (e == hipSuccess && zero_fill) e = hf::launch_fill_zero(S, H * d * d * 4, s);
+    hipError_t e = hipSuccess;
+    if (zero_fill) e = hf::launch_fill_zero(S, H * d * d * 4, s);
     if (e == hipSuccess && zero_fill) e = hf::launch_fill_zero(z, H * d * 4, s);
     return e;
   });
@@ -175,10 +202,12 @@ hf_status hf_absorb_evicted(hf_state* st, const void* k_ev, const void* v_ev, in
   }
   if (ev_index != st->next_ev) return HF_ERR_STATE;
   if (n_ev == 0) return HF_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
   const hf_status r = on_device(st->device, [&]() {
-    return hf::launch_absorb(c.dtype, c.num_heads, c.head_dim, k_ev, v_ev, n_ev, ev_head_stride,
-                             st->S, st->z, st->partials, st->tickets,
-                             static_cast<hipStream_t>(stream));
+    return timed(st, HF_KERNEL_ABSORB, s, [&]() {
+      return hf::launch_absorb(c.dtype, c.num_heads, c.head_dim, k_ev, v_ev, n_ev,
+                               ev_head_stride, st->S, st->z, st->partials, s);
+    });
   });
   if (r == HF_OK) st->next_ev += n_ev;
   return r;
@@ -212,17 +241,24 @@ hf_status hf_attend_chunk(hf_state* st, const void* q, int64_t n_q, int64_t q_he
   int32_t* sel = sel_out ? sel_out : st->sel;
   hipStream_t s = static_cast<hipStream_t>(stream);
   return on_device(st->device, [&]() {
-    hipError_t r = hf::launch_block_pool(c.dtype, c.num_heads, c.head_dim, c.block_size, q, n_q,
-                                         q_head_stride, k_win, n_kv, kv_head_stride,
-                                         st->pooled_q, st->pooled_k, st->nqb_cap, st->nkb_cap, s);
+    hipError_t r = timed(st, HF_KERNEL_BLOCK_POOL, s, [&]() {
+      return hf::launch_block_pool(c.dtype, c.num_heads, c.head_dim, c.block_size, q, n_q,
+                                   q_head_stride, k_win, n_kv, kv_head_stride, st->pooled_q,
+                                   st->pooled_k, st->nqb_cap, st->nkb_cap, s);
+    });
     if (r == hipSuccess)
-      r = hf::launch_score_select(c.num_heads, c.head_dim, nqb, (int)nkb, st->nqb_cap,
-                                  st->nkb_cap, st->pooled_q, st->pooled_k, st->scale, top_k, sel,
-                                  nullptr, s);
+      r = timed(st, HF_KERNEL_SCORE_SELECT, s, [&]() {
+        return hf::launch_score_select(c.num_heads, c.head_dim, nqb, (int)nkb, st->nqb_cap,
+                                       st->nkb_cap, st->pooled_q, st->pooled_k, st->scale, top_k,
+                                       sel, nullptr, s);
+      });
     if (r == hipSuccess)
-      r = hf::launch_sparse_swa(c.dtype, c.num_heads, c.head_dim, c.block_size, q, n_q,
-                                q_head_stride, k_win, v_win, n_kv, kv_head_stride, sel, top_k,
-                                st->S, st->z, c.eps, st->scale, out, out_head_stride, s);
+      r = timed(st, HF_KERNEL_SPARSE_SWA, s, [&]() {
+        return hf::launch_sparse_swa(c.dtype, c.num_heads, c.head_dim, c.block_size, q, n_q,
+                                     q_head_stride, k_win, v_win, n_kv, kv_head_stride, sel,
+                                     top_k, st->S, st->z, c.eps, st->scale, out, out_head_stride,
+                                     s);
+      });
     return r;
   });
 }
@@ -251,9 +287,63 @@ hf_status hf_block_scores(hf_state* st, const void* q, int64_t n_q, int64_t q_he
   });
 }
 
+hf_status hf_profile_start(hf_state* st, int32_t max_launches) {
+  if (!st || max_launches < 1 || max_launches > (1 << 20)) return HF_ERR_INVALID_ARG;
+  prof_release(st);
+  const hf_status r = on_device(st->device, [&]() -> hipError_t {
+    for (int k = 0; k < HF_KERNEL_COUNT; ++k) {
+      st->prof_ev[k].resize(2 * (size_t)max_launches, nullptr);
+      for (hipEvent_t& e : st->prof_ev[k]) {
+        const hipError_t err = hipEventCreate(&e);
+        if (err != hipSuccess) {
+          e = nullptr;
+          return err;
+        }
+      }
+    }
+    return hipSuccess;
+  });
+  if (r != HF_OK) {
+    for (int k = 0; k < HF_KERNEL_COUNT; ++k)
+      for (hipEvent_t& e : st->prof_ev[k])
+        if (e) (void)hipEventDestroy(e);
+    for (int k = 0; k < HF_KERNEL_COUNT; ++k) st->prof_ev[k].clear();
+    return r;
+  }
+  st->prof_cap = max_launches;
+  st->prof_on = true;
+  return HF_OK;
+}
+
+hf_status hf_profile_stop(hf_state* st, double* total_ms, int32_t* launches) {
+  if (!st || !total_ms || !launches) return HF_ERR_INVALID_ARG;
+  const hf_status r = on_device(st->device, [&]() -> hipError_t {
+    for (int k = 0; k < HF_KERNEL_COUNT; ++k) {
+      double sum = 0.0;
+      for (int i = 0; i < st->prof_n[k]; ++i) {
+        hipError_t e = hipEventSynchronize(st->prof_ev[k][2 * i + 1]);
+        float ms = 0.f;
+        if (e == hipSuccess)
+          e = hipEventElapsedTime(&ms, st->prof_ev[k][2 * i], st->prof_ev[k][2 * i + 1]);
+        if (e != hipSuccess) return e;
+        sum += ms;
+      }
+      total_ms[k] = sum;
+      launches[k] = st->prof_n[k];
+    }
+    return hipSuccess;
+  });
+  prof_release(st);
+  return r;
+}
+
 int64_t hf_next_ev_index(const hf_state* st) { return st ? st->next_ev : -1; }
 
-void hf_state_destroy(hf_state* st) { delete st; }
+void hf_state_destroy(hf_state* st) {
+  if (!st) return;
+  prof_release(st);
+  delete st;
+}
 
 const char* hf_status_string(hf_status s) {
   switch (s) {

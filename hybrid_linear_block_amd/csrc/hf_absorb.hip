@@ -11,9 +11,10 @@
 // index, are contiguous per MFMA lane), forms phi(K) in fp32 and, for bf16
 // inputs, splits it into bf16 hi + lo so that the bf16 MFMA keeps ~fp32
 // accuracy (V is exact in bf16). Each workgroup writes a partial 64x64 tile (and
-// a partial z) to the workspace; the last workgroup of a (head, tile) -- found
-// with an atomic ticket -- adds the partials in split order to S and z. The
-// order of every sum is fixed, so the result is bitwise reproducible.
+// a partial z) to the workspace; a second kernel adds the partials in split
+// order to S and z. No atomics or device-wide fences are involved (on a chip
+// whose XCDs have separate L2 caches those would have to write the L2 back),
+// and the order of every sum is fixed, so the result is bitwise reproducible.
 #include "hf_device.h"
 #include "hf_launch.h"
 
@@ -40,7 +41,6 @@ struct AbsorbSmem<bf16_t> {
   bf16_t fhi[AT][BPITCH];
   bf16_t flo[AT][BPITCH];
   float zred[16][AT];
-  int flag;
 };
 
 template <>
@@ -48,43 +48,35 @@ struct AbsorbSmem<float> {
   float vs[TS][FPITCH];
   float fs[TS][FPITCH];
   float zred[8][AT];
-  int flag;
 };
 
-__device__ __forceinline__ void finish(float* part, float* S, float* z, unsigned* ticket,
-                                       int n_split, int split, int D, int jt, int it,
-                                       int* flag) {
-  // Publish this workgroup's partial, then take a ticket; the last one reduces.
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) *flag = (atomicAdd(ticket, 1u) == (unsigned)(n_split - 1));
-  __syncthreads();
-  if (!*flag) return;
-  __threadfence();
-  float* base = part - (size_t)split * PART;  // partial of split 0
-  for (int e = threadIdx.x; e < PART; e += NTHR) {
-    float acc = 0.f;
-    for (int s = 0; s < n_split; ++s) acc += __builtin_nontemporal_load(base + (size_t)s * PART + e);
-    if (e < AT * AT) {
-      const int j = e / AT, i = e % AT;
-      float* dst = S + (size_t)(jt * AT + j) * D + it * AT + i;
-      *dst = *dst + acc;
-    } else if (jt == 0) {
-      float* dst = z + it * AT + (e - AT * AT);
-      *dst = *dst + acc;
-    }
+// Second pass: S[h][tile] += sum_s partial[s] (and z), splits added in order.
+template <int D>
+__global__ __launch_bounds__(NTHR) void absorb_reduce(const float* __restrict__ partials,
+                                                      int n_split, float* __restrict__ S,
+                                                      float* __restrict__ z) {
+  constexpr int NT = D / AT;
+  const int e = blockIdx.x * NTHR + threadIdx.x;
+  const int tile = blockIdx.y, h = blockIdx.z;
+  const int jt = tile / NT, it = tile % NT;
+  if (e >= PART || (e >= AT * AT && jt != 0)) return;
+  const float* p = partials + ((size_t)h * NT * NT + tile) * n_split * PART + e;
+  float acc = 0.f;
+  for (int s = 0; s < n_split; ++s) acc += p[(size_t)s * PART];
+  if (e < AT * AT) {
+    float* dst = S + (size_t)h * D * D + (size_t)(jt * AT + e / AT) * D + it * AT + e % AT;
+    *dst += acc;
+  } else {
+    z[(size_t)h * D + it * AT + (e - AT * AT)] += acc;
   }
-  if (threadIdx.x == 0) *ticket = 0u;  // ready for the next call (kernel boundary orders it)
 }
 
 template <int D>
 __global__ __launch_bounds__(NTHR) void absorb_bf16(const bf16_t* __restrict__ kev,
                                                     const bf16_t* __restrict__ vev,
                                                     int64_t n_ev, int64_t hs, int tps,
-                                                    int n_split, float* __restrict__ S,
-                                                    float* __restrict__ z,
-                                                    float* __restrict__ partials,
-                                                    unsigned* __restrict__ tickets) {
+                                                    int n_split,
+                                                    float* __restrict__ partials) {
   constexpr int NT = D / AT;  // tiles per edge
   __shared__ AbsorbSmem<bf16_t> sm;
   const int split = blockIdx.x, tile = blockIdx.y, h = blockIdx.z;
@@ -188,17 +180,13 @@ __global__ __launch_bounds__(NTHR) void absorb_bf16(const bf16_t* __restrict__ k
     for (int q = 0; q < 16; ++q) s += sm.zred[q][tid];
     part[AT * AT + tid] = s;
   }
-  finish(part, S + (size_t)h * D * D, z + (size_t)h * D, tickets + (size_t)h * NT * NT + tile,
-         n_split, split, D, jt, it, &sm.flag);
 }
 
 template <int D>
 __global__ __launch_bounds__(NTHR) void absorb_f32(const float* __restrict__ kev,
                                                    const float* __restrict__ vev, int64_t n_ev,
                                                    int64_t hs, int tps, int n_split,
-                                                   float* __restrict__ S, float* __restrict__ z,
-                                                   float* __restrict__ partials,
-                                                   unsigned* __restrict__ tickets) {
+                                                   float* __restrict__ partials) {
   constexpr int NT = D / AT;
   __shared__ AbsorbSmem<float> sm;
   const int split = blockIdx.x, tile = blockIdx.y, h = blockIdx.z;
@@ -284,8 +272,6 @@ __global__ __launch_bounds__(NTHR) void absorb_f32(const float* __restrict__ kev
     for (int q = 0; q < 8; ++q) s += sm.zred[q][tid];
     part[AT * AT + tid] = s;
   }
-  finish(part, S + (size_t)h * D * D, z + (size_t)h * D, tickets + (size_t)h * NT * NT + tile,
-         n_split, split, D, jt, it, &sm.flag);
 }
 
 }  // namespace
@@ -306,36 +292,28 @@ size_t absorb_partial_floats(int heads, int d) {
   return (size_t)heads * nt * nt * kAbsorbMaxSplits * PART;
 }
 
-size_t absorb_ticket_count(int heads, int d) {
-  const int nt = d / AT;
-  return (size_t)heads * nt * nt;
-}
-
 hipError_t launch_absorb(int dtype, int heads, int d, const void* k, const void* v, int64_t n_ev,
                          int64_t head_stride, float* S, float* z, float* partials,
-                         unsigned* tickets, hipStream_t stream) {
+                         hipStream_t stream) {
   const AbsorbPlan p = absorb_plan(n_ev);
   const int nt = d / AT;
   dim3 grid(p.n_split, nt * nt, heads);
+#define HF_ABS(KER, T, D)                                                                     \
+  KER<D><<<grid, NTHR, 0, stream>>>(static_cast<const T*>(k), static_cast<const T*>(v), n_ev, \
+                                    head_stride, p.tokens_per_split, p.n_split, partials)
   if (dtype == 0) {
-    const bf16_t* kk = static_cast<const bf16_t*>(k);
-    const bf16_t* vv = static_cast<const bf16_t*>(v);
-    if (d == 128)
-      absorb_bf16<128><<<grid, NTHR, 0, stream>>>(kk, vv, n_ev, head_stride, p.tokens_per_split,
-                                                  p.n_split, S, z, partials, tickets);
-    else
-      absorb_bf16<64><<<grid, NTHR, 0, stream>>>(kk, vv, n_ev, head_stride, p.tokens_per_split,
-                                                 p.n_split, S, z, partials, tickets);
+    if (d == 128) HF_ABS(absorb_bf16, bf16_t, 128); else HF_ABS(absorb_bf16, bf16_t, 64);
   } else {
-    const float* kk = static_cast<const float*>(k);
-    const float* vv = static_cast<const float*>(v);
-    if (d == 128)
-      absorb_f32<128><<<grid, NTHR, 0, stream>>>(kk, vv, n_ev, head_stride, p.tokens_per_split,
-                                                 p.n_split, S, z, partials, tickets);
-    else
-      absorb_f32<64><<<grid, NTHR, 0, stream>>>(kk, vv, n_ev, head_stride, p.tokens_per_split,
-                                                p.n_split, S, z, partials, tickets);
+    if (d == 128) HF_ABS(absorb_f32, float, 128); else HF_ABS(absorb_f32, float, 64);
   }
+#undef HF_ABS
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dim3 rgrid((PART + NTHR - 1) / NTHR, nt * nt, heads);
+  if (d == 128)
+    absorb_reduce<128><<<rgrid, NTHR, 0, stream>>>(partials, p.n_split, S, z);
+  else
+    absorb_reduce<64><<<rgrid, NTHR, 0, stream>>>(partials, p.n_split, S, z);
   return hipGetLastError();
 }
 

@@ -15,10 +15,10 @@ struct AbsorbPlan {
 };
 AbsorbPlan absorb_plan(int64_t n_ev);
 size_t absorb_partial_floats(int heads, int d);
-size_t absorb_ticket_count(int heads, int d);
+// Two kernels: per-split partial tiles into `partials`, then an in-order reduction.
 hipError_t launch_absorb(int dtype, int heads, int d, const void* k, const void* v, int64_t n_ev,
                          int64_t head_stride, float* S, float* z, float* partials,
-                         unsigned* tickets, hipStream_t stream);
+                         hipStream_t stream);
 
 // ---- block pooling, scoring and top-K selection ----------------------------------
 constexpr int kMaxKeyBlocks = 8192;

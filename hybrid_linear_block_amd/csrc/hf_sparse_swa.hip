@@ -38,10 +38,14 @@ constexpr float kLog2e = 1.4426950408889634f;
 template <typename T, int D, int BLK>
 struct SwaSmem;
 
+// bf16: K and V blocks row-major in 16-byte chunks; chunk cc of row r is stored
+// in slot cc ^ (r mod CPR), which spreads both the 16-byte K operand reads (16
+// rows, one chunk) and the transposing V reads (16 rows, two chunks) over all
+// LDS banks.
 template <int D, int BLK>
 struct SwaSmem<bf16_t, D, BLK> {
-  bf16_t k[BLK][D + 8];   // row-major K block (+16 B pad per row)
-  bf16_t vt[D][BLK + 8];  // V^T, keys permuted per 32-key chunk
+  uint4 k[BLK * D / 8];
+  uint4 v[BLK * D / 8];
 };
 
 template <int D, int BLK>
@@ -50,11 +54,14 @@ struct SwaSmem<float, D, BLK> {
   float v[BLK][D + 4];
 };
 
-// Position of key `k` in a transposed V row: key = 32c + 16hh + 4gg + r is stored
-// at 32c + 8gg + 4hh + r, so that lane group gg finds its 8 keys (4 from each of
-// the two 16-key score tiles of the 32-key chunk) in one 16-byte read.
-__device__ __forceinline__ int vt_pos(int key) {
-  return (key & ~31) + ((key & 15) >> 2) * 8 + ((key >> 4) & 1) * 4 + (key & 3);
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, if lane
+// 4j + p supplies the address of 4 consecutive elements M[j][4p .. 4p+3], lane i
+// receives M[0..3][i].
+__device__ __forceinline__ v4i16 lds_read_tr(const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p));
 }
 
 template <typename T, int D, int BLK, int QW>
@@ -67,13 +74,12 @@ struct SwaCfg {
   static constexpr int VEC = 16 / sizeof(T);
   static constexpr int CPR = D / VEC;      // 16-byte chunks per row
   static constexpr int KCH = BLK * CPR / NT;  // K chunks per thread
-  // V chunks per thread: bf16 stages groups of 4 keys x 8 features (4 chunks).
-  static constexpr int VCH = sizeof(T) == 2 ? (BLK / 4) * CPR / NT * 4 : BLK * CPR / NT;
+  static constexpr int VCH = BLK * CPR / NT;  // V chunks per thread
   static_assert(BLK * CPR % NT == 0, "staging split");
 };
 
 template <typename T, int D, int BLK, int QW>
-__global__ __launch_bounds__((BLK / QW) * 64) void sparse_swa(
+__global__ __launch_bounds__((BLK / QW) * 64) __attribute__((amdgpu_waves_per_eu(2))) void sparse_swa(
     const T* __restrict__ q, int64_t n_q, int64_t q_hs, const T* __restrict__ kg,
     const T* __restrict__ vg, int64_t n_kv, int64_t kv_hs, const int32_t* __restrict__ sel,
     int top_k, int nqb, int n_logical, const float* __restrict__ S,
@@ -123,48 +129,34 @@ __global__ __launch_bounds__((BLK / QW) * 64) void sparse_swa(
       const int row = ch / C::CPR, cc = ch % C::CPR;
       kreg[u] = ld16(kh + (base + row) * D + cc * C::VEC, base + row < n_kv);
     }
+#pragma unroll
+    for (int u = 0; u < C::VCH; ++u) {
+      const int ch = tid + u * C::NT;
+      const int row = ch / C::CPR, cc = ch % C::CPR;
+      vreg[u] = ld16(vh + (base + row) * D + cc * C::VEC, base + row < n_kv);
+    }
+  };
+  auto store_block = [&]() {
     if constexpr (KP == 8) {
 #pragma unroll
-      for (int u = 0; u < C::VCH / 4; ++u) {
-        const int gq = tid + u * C::NT;
-        const int kgp = gq / C::CPR, cc = gq % C::CPR;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int64_t row = base + kgp * 4 + r;
-          vreg[u * 4 + r] = ld16(vh + row * D + cc * C::VEC, row < n_kv);
-        }
+      for (int u = 0; u < C::KCH; ++u) {
+        const int ch = tid + u * C::NT;
+        const int row = ch / C::CPR, cc = ch % C::CPR;
+        sm.k[row * C::CPR + (cc ^ (row & (C::CPR - 1)))] = kreg[u];
       }
-    } else {
 #pragma unroll
       for (int u = 0; u < C::VCH; ++u) {
         const int ch = tid + u * C::NT;
         const int row = ch / C::CPR, cc = ch % C::CPR;
-        vreg[u] = ld16(vh + (base + row) * D + cc * C::VEC, base + row < n_kv);
-      }
-    }
-  };
-  auto store_block = [&]() {
-#pragma unroll
-    for (int u = 0; u < C::KCH; ++u) {
-      const int ch = tid + u * C::NT;
-      const int row = ch / C::CPR, cc = ch % C::CPR;
-      *reinterpret_cast<uint4*>(&sm.k[row][cc * C::VEC]) = kreg[u];
-    }
-    if constexpr (KP == 8) {
-#pragma unroll
-      for (int u = 0; u < C::VCH / 4; ++u) {
-        const int gq = tid + u * C::NT;
-        const int kgp = gq / C::CPR, cc = gq % C::CPR;
-        const int pos = vt_pos(kgp * 4);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t a = half16(vreg[u * 4 + 0], e), b = half16(vreg[u * 4 + 1], e);
-          const uint32_t cc2 = half16(vreg[u * 4 + 2], e), d2 = half16(vreg[u * 4 + 3], e);
-          *reinterpret_cast<uint2*>(&sm.vt[cc * 8 + e][pos]) =
-              make_uint2(a | (b << 16), cc2 | (d2 << 16));
-        }
+        sm.v[row * C::CPR + (cc ^ (row & (C::CPR - 1)))] = vreg[u];
       }
     } else {
+#pragma unroll
+      for (int u = 0; u < C::KCH; ++u) {
+        const int ch = tid + u * C::NT;
+        const int row = ch / C::CPR, cc = ch % C::CPR;
+        *reinterpret_cast<uint4*>(&sm.k[row][cc * C::VEC]) = kreg[u];
+      }
 #pragma unroll
       for (int u = 0; u < C::VCH; ++u) {
         const int ch = tid + u * C::NT;
@@ -211,7 +203,8 @@ __global__ __launch_bounds__((BLK / QW) * 64) void sparse_swa(
       for (int mt = 0; mt < C::NMT; ++mt) {
         op_t kop;
         if constexpr (KP == 8) {
-          kop = as_bf16x8(*reinterpret_cast<const uint4*>(&sm.k[mt * 16 + c][s * KSTEP + g * 8]));
+          const int row = mt * 16 + c;
+          kop = as_bf16x8(sm.k[row * C::CPR + ((s * 4 + g) ^ (row & (C::CPR - 1)))]);
         } else {
           kop = sm.k[mt * 16 + c][s * KSTEP + g];
         }
@@ -274,10 +267,21 @@ __global__ __launch_bounds__((BLK / QW) * 64) void sparse_swa(
           pop[n] = as_bf16x8(make_uint4(b[0] | (b[1] << 16), b[2] | (b[3] << 16),
                                         b[4] | (b[5] << 16), b[6] | (b[7] << 16)));
         }
+        // A = V^T of this 32-key chunk, keys in the order of pop: lane group g takes
+        // keys 32c2 + 4g + 0..3 (score tile 2c2) then 32c2 + 16 + 4g + 0..3 (tile
+        // 2c2 + 1); source lane 4j + p of the group points at V[row j][16et + 4p ..].
+        const int jr = (lane & 15) >> 2, pp = lane & 3;
 #pragma unroll
         for (int et = 0; et < C::NET; ++et) {
-          const op_t vop =
-              as_bf16x8(*reinterpret_cast<const uint4*>(&sm.vt[et * 16 + c][c2 * 32 + g * 8]));
+          const int chunk = 2 * et + (pp >> 1);
+          const int r0 = c2 * 32 + 4 * g + jr, r1 = r0 + 16;
+          const char* vb = reinterpret_cast<const char*>(sm.v);
+          const v4i16 lo = lds_read_tr(vb + (r0 * C::CPR + (chunk ^ (r0 & (C::CPR - 1)))) * 16 +
+                                       (pp & 1) * 8);
+          const v4i16 hi = lds_read_tr(vb + (r1 * C::CPR + (chunk ^ (r1 & (C::CPR - 1)))) * 16 +
+                                       (pp & 1) * 8);
+          const op_t vop = __builtin_bit_cast(op_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3,
+                                                                            4, 5, 6, 7));
 #pragma unroll
           for (int n = 0; n < C::NQT; ++n) acc[et][n] = M::mma(vop, pop[n], acc[et][n]);
         }
@@ -384,6 +388,344 @@ __global__ __launch_bounds__((BLK / QW) * 64) void sparse_swa(
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16, 64-row blocks: 2 waves x 32 query rows per workgroup.
+//
+// K and V blocks go from global memory straight into LDS (16-byte
+// global_load_lds, no staging registers) in the swizzled row-major layout above.
+// The two tiles are single-buffered and their loads are staggered so each one
+// overlaps compute: K(t+1) streams in during the softmax and O^T += V^T P^T of
+// block t, V(t+1) during S^T = K Q^T and the softmax of block t+1. The V operand
+// is read with the transposing LDS read, so V needs no transposed copy. After the
+// loop the tile buffers hold the normalised sparse output, the linear read is
+// added in place and the rows leave in coalesced 16-byte stores.
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// This wave's LDS reads are complete, then a plain s_barrier (no memory fence, so
+// in-flight global->LDS loads are not waited for).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// 16-byte global -> LDS load of every lane: lane l's 16 bytes land at LDS byte
+// offset lds_off + 16 l (lds_off wave-uniform). Issued from inline asm so that the
+// compiler does not track it: the kernel orders these loads itself (wait_vmem and
+// the barriers), and the compiler's own tracking would make every LDS read wait
+// for all of them. Vector-memory operations complete in issue order, so loads the
+// compiler does not know about can only make its own waits stricter. m0 is used
+// by nothing else in these kernels.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_dma16(const void* gp, uint32_t lds_off) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(lds_off), "v"(gp)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>((lds_void*)p);
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(N | (0x7 << 4) | (0xF << 8));
+}
+
+template <int D>
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void sparse_swa_bf16(
+    const bf16_t* __restrict__ q, int64_t n_q, int64_t q_hs, const bf16_t* __restrict__ kg,
+    const bf16_t* __restrict__ vg, int64_t n_kv, int64_t kv_hs, const int32_t* __restrict__ sel,
+    int top_k, int nqb, int n_logical, const float* __restrict__ S,
+    const float* __restrict__ z, float eps, float scale, bf16_t* __restrict__ out,
+    int64_t out_hs) {
+  constexpr int BLK = 64, NW = 2, NQT = 2, NMT = 4, NET = D / 16, NKS = D / 32;
+  constexpr int CPR = D / 8;            // 16-byte chunks per K/V row
+  constexpr int TCH = BLK * CPR;        // chunks per tile
+  constexpr int LPT = TCH / (NW * 64);  // global->LDS loads per lane per tile
+  constexpr int OCPR = D / 4;           // 16-byte fp32 chunks per staged output row
+  // Separate objects, so that the compiler can tell an in-flight load into one
+  // tile from reads of the other; after the loop each holds one wave's output rows.
+  __shared__ uint4 lds_k[TCH];
+  __shared__ uint4 lds_v[TCH];
+
+  const int logical = xcd_remap(blockIdx.x, gridDim.x, n_logical);
+  if (logical < 0) return;
+  const int h = logical / nqb, i = logical % nqb;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4, c = lane & 15;
+  const bf16_t* qh = q + (size_t)h * q_hs;
+  const bf16_t* kh = kg + (size_t)h * kv_hs;
+  const bf16_t* vh = vg + (size_t)h * kv_hs;
+  const int32_t* my_sel = sel + ((size_t)h * nqb + i) * top_k;
+  const int64_t qrow0 = (int64_t)i * BLK + w * 32;
+
+  // Load u of this wave fills LDS chunks (u*NW + w)*64 + lane of a tile with global
+  // chunk (row, (slot ^ row) mod CPR) of the block. The per-lane element offsets
+  // inside a block are fixed, so they are computed once; the block base is
+  // wave-uniform. Rows past the window (ragged last block only) repeat the last
+  // row: their scores are masked, so the values only need to be finite.
+  int loff[LPT];
+#pragma unroll
+  for (int u = 0; u < LPT; ++u) {
+    const int P = (u * NW + w) * 64 + lane;
+    const int row = P / CPR, cc = (P % CPR) ^ (row % CPR);
+    loff[u] = row * D + cc * 8;
+  }
+  auto issue_tile = [&](const bf16_t* src, int jb, const uint4* tile) {
+    const bf16_t* tb = src + (size_t)jb * BLK * D;
+    const int64_t left = n_kv - (int64_t)jb * BLK;
+    const int last = (int)(left < BLK ? left : BLK) - 1;  // last row inside the window
+    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_offset(tile) + w * 64 * 16);
+#pragma unroll
+    for (int u = 0; u < LPT; ++u) {
+      const int row = loff[u] / D;
+      const int off = row <= last ? loff[u] : last * D + loff[u] % D;
+      lds_dma16(tb + off, base + u * NW * 64 * 16);
+    }
+  };
+
+  // Q operands (B of S^T = K Q^T): lane holds Q[16n + c][32s + 8g .. +8].
+  bf16x8 qop[NQT][NKS];
+#pragma unroll
+  for (int n = 0; n < NQT; ++n) {
+    const int64_t r = qrow0 + n * 16 + c;
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) qop[n][s] = as_bf16x8(ld16(qh + r * D + s * 32 + g * 8, r < n_q));
+  }
+
+  f32x4 acc[NET][NQT];
+#pragma unroll
+  for (int e = 0; e < NET; ++e)
+#pragma unroll
+    for (int n = 0; n < NQT; ++n) acc[e][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[NQT], l_run[NQT];
+#pragma unroll
+  for (int n = 0; n < NQT; ++n) {
+    m_run[n] = -INFINITY;
+    l_run[n] = 0.f;
+  }
+  const float sl2 = scale * kLog2e;
+  const int jr = (lane & 15) >> 2, pp = lane & 3;  // transposing-read source role
+
+  issue_tile(kh, my_sel[0], lds_k);
+  issue_tile(vh, my_sel[0], lds_v);
+  for (int t = 0; t < top_k; ++t) {
+    const int jb = my_sel[t];
+    const bool more = t + 1 < top_k;
+    wait_vmem<LPT>();  // K(t) has landed (V(t) may still be in flight)
+    lds_barrier();
+
+    // ---- S^T = K Q^T: st[mt][n][r] = score(key 16mt + 4g + r, query 16n + c) ----
+    f32x4 st[NMT][NQT];
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+      for (int n = 0; n < NQT; ++n) st[mt][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt) {
+        const int row = mt * 16 + c;
+        const bf16x8 kop = as_bf16x8(lds_k[row * CPR + ((s * 4 + g) ^ (row % CPR))]);
+#pragma unroll
+        for (int n = 0; n < NQT; ++n)
+          st[mt][n] = Mfma<bf16_t>::mma(kop, qop[n][s], st[mt][n]);
+      }
+    }
+    lds_barrier();  // every wave is done with K(t)
+    if (more) issue_tile(kh, my_sel[t + 1], lds_k);
+
+    // ---- online softmax (base 2); p holds the bf16-rounded weights PV uses ----
+    const int64_t key0 = (int64_t)jb * BLK;
+    const bool tail = key0 + BLK > n_kv;
+#pragma unroll
+    for (int n = 0; n < NQT; ++n) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float x = st[mt][n][r] * sl2;
+          if (tail && key0 + mt * 16 + g * 4 + r >= n_kv) x = -INFINITY;
+          st[mt][n][r] = x;
+          mx = fmaxf(mx, x);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run[n], mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run[n] - m_new);
+      float rs = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float e = bf16_to_f32(f32_to_bf16_bits(__builtin_amdgcn_exp2f(st[mt][n][r] - m_new)));
+          st[mt][n][r] = e;
+          rs += e;
+        }
+      rs += __shfl_xor(rs, 16);
+      rs += __shfl_xor(rs, 32);
+      l_run[n] = l_run[n] * alpha + rs;
+      m_run[n] = m_new;
+#pragma unroll
+      for (int e = 0; e < NET; ++e) acc[e][n] *= alpha;
+    }
+
+    if (more) wait_vmem<LPT>(); else wait_vmem<0>();  // V(t) has landed
+    lds_barrier();
+
+    // ---- O^T += V^T P^T ----
+    const char* vb = reinterpret_cast<const char*>(lds_v);
+#pragma unroll
+    for (int c2 = 0; c2 < BLK / 32; ++c2) {
+      bf16x8 pop[NQT];
+#pragma unroll
+      for (int n = 0; n < NQT; ++n) {
+        uint32_t b[8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          b[r] = f32_to_bf16_bits(st[2 * c2][n][r]);
+          b[4 + r] = f32_to_bf16_bits(st[2 * c2 + 1][n][r]);
+        }
+        pop[n] = as_bf16x8(make_uint4(b[0] | (b[1] << 16), b[2] | (b[3] << 16),
+                                      b[4] | (b[5] << 16), b[6] | (b[7] << 16)));
+      }
+      // Lane group g takes keys 32c2 + 4g + 0..3 then 32c2 + 16 + 4g + 0..3 (the key
+      // order of pop); source lane 4j + p points at V[row j][16et + 4p ..].
+      const int r0 = c2 * 32 + 4 * g + jr;
+#pragma unroll
+      for (int et = 0; et < NET; ++et) {
+        const int chunk = 2 * et + (pp >> 1);
+        const v4i16 lo = lds_read_tr(vb + (r0 * CPR + (chunk ^ (r0 % CPR))) * 16 + (pp & 1) * 8);
+        const v4i16 hi =
+            lds_read_tr(vb + ((r0 + 16) * CPR + (chunk ^ (r0 % CPR))) * 16 + (pp & 1) * 8);
+        const bf16x8 vop =
+            __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int n = 0; n < NQT; ++n) acc[et][n] = Mfma<bf16_t>::mma(vop, pop[n], acc[et][n]);
+      }
+    }
+    lds_barrier();  // every wave is done with V(t)
+    if (more) issue_tile(vh, my_sel[t + 1], lds_v);
+  }
+
+  // ---- epilogue ----
+  // Normalised sparse output -> this wave's tile buffer (K for wave 0, V for wave 1),
+  // fp32 rows of OCPR chunks, chunk ch of row r in slot ch ^ (r mod OCPR).
+  static_assert(32 * OCPR == TCH, "one wave's output rows fill one tile buffer");
+  float4* ob = reinterpret_cast<float4*>(w == 0 ? lds_k : lds_v);
+#pragma unroll
+  for (int n = 0; n < NQT; ++n) {
+    const float inv_l = 1.f / l_run[n];
+    const int row = n * 16 + c;
+#pragma unroll
+    for (int et = 0; et < NET; ++et)
+      ob[row * OCPR + ((et * 4 + g) ^ (row % OCPR))] =
+          make_float4(acc[et][n][0] * inv_l, acc[et][n][1] * inv_l, acc[et][n][2] * inv_l,
+                      acc[et][n][3] * inv_l);
+  }
+
+  // Linear read: num^T = S phi(Q)^T on MFMA with S and phi(q) split into bf16 hi + lo
+  // (three products), normaliser z . phi(q) in fp32.
+  const float* Sh = S + (size_t)h * D * D;
+  const float* zh = z + (size_t)h * D;
+  f32x4 num[NET][NQT];
+#pragma unroll
+  for (int e = 0; e < NET; ++e)
+#pragma unroll
+    for (int n = 0; n < NQT; ++n) num[e][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float den[NQT] = {0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < NKS; ++s) {
+    const int i0 = s * 32 + g * 8;
+    const float4 z0 = *reinterpret_cast<const float4*>(zh + i0);
+    const float4 z1 = *reinterpret_cast<const float4*>(zh + i0 + 4);
+    const float zz[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
+    bf16x8 fhi[NQT], flo[NQT];
+#pragma unroll
+    for (int n = 0; n < NQT; ++n) {
+      const uint4 qb = __builtin_bit_cast(uint4, qop[n][s]);
+      float f[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        f[e] = phi(bf16_to_f32(half16(qb, e)));
+        den[n] += zz[e] * f[e];
+      }
+      split_bf16x8(f, fhi[n], flo[n]);
+    }
+#pragma unroll
+    for (int et = 0; et < NET; ++et) {
+      const float* sp = Sh + (size_t)(et * 16 + c) * D + i0;
+      const float4 a0 = *reinterpret_cast<const float4*>(sp);
+      const float4 a1 = *reinterpret_cast<const float4*>(sp + 4);
+      const float sv[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+      bf16x8 shi, slo;
+      split_bf16x8(sv, shi, slo);
+#pragma unroll
+      for (int n = 0; n < NQT; ++n) {
+        num[et][n] = Mfma<bf16_t>::mma(shi, fhi[n], num[et][n]);
+        num[et][n] = Mfma<bf16_t>::mma(slo, fhi[n], num[et][n]);
+        num[et][n] = Mfma<bf16_t>::mma(shi, flo[n], num[et][n]);
+      }
+    }
+  }
+#pragma unroll
+  for (int n = 0; n < NQT; ++n) {
+    float dn = den[n];
+    dn += __shfl_xor(dn, 16);
+    dn += __shfl_xor(dn, 32);
+    const float inv_den = 1.f / (dn + eps);
+    const int row = n * 16 + c;
+#pragma unroll
+    for (int et = 0; et < NET; ++et) {
+      float4& o = ob[row * OCPR + ((et * 4 + g) ^ (row % OCPR))];
+      float4 v = o;
+      v.x += num[et][n][0] * inv_den;
+      v.y += num[et][n][1] * inv_den;
+      v.z += num[et][n][2] * inv_den;
+      v.w += num[et][n][3] * inv_den;
+      o = v;
+    }
+  }
+  // Coalesced bf16 stores: lane handles 8 consecutive features of a row per step.
+  bf16_t* oh = out + (size_t)h * out_hs;
+  constexpr int C8 = D / 8;
+#pragma unroll
+  for (int u = 0; u < 32 * C8 / 64; ++u) {
+    const int idx = u * 64 + lane;
+    const int row = idx / C8, c8 = idx % C8;
+    const int64_t r = qrow0 + row;
+    const float4 a = ob[row * OCPR + ((2 * c8) ^ (row % OCPR))];
+    const float4 b = ob[row * OCPR + ((2 * c8 + 1) ^ (row % OCPR))];
+    const uint4 pk = make_uint4(f32_to_bf16_bits(a.x) | (f32_to_bf16_bits(a.y) << 16),
+                                f32_to_bf16_bits(a.z) | (f32_to_bf16_bits(a.w) << 16),
+                                f32_to_bf16_bits(b.x) | (f32_to_bf16_bits(b.y) << 16),
+                                f32_to_bf16_bits(b.z) | (f32_to_bf16_bits(b.w) << 16));
+    if (r < n_q) *reinterpret_cast<uint4*>(oh + r * D + c8 * 8) = pk;
+  }
+}
+
+template <int D>
+hipError_t launch_bf16(const void* q, int64_t n_q, int64_t q_hs, const void* k, const void* v,
+                       int64_t n_kv, int64_t kv_hs, const int32_t* sel, int top_k, int heads,
+                       const float* S, const float* z, float eps, float scale, void* out,
+                       int64_t out_hs, hipStream_t stream) {
+  const int nqb = (int)((n_q + 63) / 64);
+  const int n_logical = nqb * heads;
+  const int n_wg = (n_logical + 7) / 8 * 8;
+  sparse_swa_bf16<D><<<n_wg, 128, 0, stream>>>(
+      static_cast<const bf16_t*>(q), n_q, q_hs, static_cast<const bf16_t*>(k),
+      static_cast<const bf16_t*>(v), n_kv, kv_hs, sel, top_k, nqb, n_logical, S, z, eps, scale,
+      static_cast<bf16_t*>(out), out_hs);
+  return hipGetLastError();
+}
+
 template <typename T, int D, int BLK, int QW>
 hipError_t launch(const void* q, int64_t n_q, int64_t q_hs, const void* k, const void* v,
                   int64_t n_kv, int64_t kv_hs, const int32_t* sel, int top_k, int heads,
@@ -410,8 +752,12 @@ hipError_t launch_sparse_swa(int dtype, int heads, int d, int block, const void*
   return launch<T, D, BLK, QW>(q, n_q, q_hs, k, v, n_kv, kv_hs, sel, top_k, heads, S, z, eps, \
                                scale, out, out_hs, stream)
   if (dtype == 0) {
-    if (block == 64 && d == 128) HF_SWA(bf16_t, 128, 64, 32);
-    if (block == 64 && d == 64) HF_SWA(bf16_t, 64, 64, 32);
+    if (block == 64 && d == 128)
+      return launch_bf16<128>(q, n_q, q_hs, k, v, n_kv, kv_hs, sel, top_k, heads, S, z, eps,
+                              scale, out, out_hs, stream);
+    if (block == 64 && d == 64)
+      return launch_bf16<64>(q, n_q, q_hs, k, v, n_kv, kv_hs, sel, top_k, heads, S, z, eps,
+                             scale, out, out_hs, stream);
   } else {
     if (block == 16 && d == 64) HF_SWA(float, 64, 16, 16);
     if (block == 16 && d == 128) HF_SWA(float, 128, 16, 16);

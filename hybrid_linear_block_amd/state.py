@@ -141,6 +141,16 @@ class HybridAttentionState:
                "hf_block_scores")
         return scores
 
+    def profile_start(self, max_launches: int) -> None:
+        """Record HIP events around each kernel this state launches (profiling aid)."""
+        _check(B.hf_profile_start(self.handle, max_launches), "hf_profile_start")
+
+    def profile_stop(self):
+        """{kernel: (total ms, launches)} since profile_start; waits for the events."""
+        st, res = B.hf_profile_stop(self.handle)
+        _check(st, "hf_profile_stop")
+        return res
+
     def close(self) -> None:
         if getattr(self, "_h", None) is not None:
             B.hf_state_destroy(self._h)

@@ -102,8 +102,7 @@ size_t hf_workspace_bytes(const hf_config* cfg);
  * 16-byte aligned). zero_fill != 0 enqueues S = 0, z = 0 (an empty state, [EN]
  * 2.A.1); zero_fill == 0 adopts the current contents of S and z (resume from a
  * checkpoint). next_ev_index is the absolute index of the next token to be
- * evicted (0 for a new stream). The workspace's internal counters are always
- * reset. *out receives the handle. */
+ * evicted (0 for a new stream). *out receives the handle. */
 hf_status hf_state_init(const hf_config* cfg, float* S, float* z, void* workspace,
                         size_t ws_bytes, int zero_fill, int64_t next_ev_index,
                         void* stream, hf_state** out);
@@ -136,6 +135,26 @@ hf_status hf_attend_chunk(hf_state* st, const void* q, int64_t n_q, int64_t q_he
 hf_status hf_block_scores(hf_state* st, const void* q, int64_t n_q, int64_t q_head_stride,
                           const void* k_win, int64_t n_kv, int64_t kv_head_stride,
                           float* scores_out, void* stream);
+
+/* Kernels a state launches, for per-kernel timing. */
+typedef enum {
+  HF_KERNEL_ABSORB = 0,       /* hf_absorb_evicted */
+  HF_KERNEL_BLOCK_POOL = 1,   /* block means of Q and K (first kernel of an attend call) */
+  HF_KERNEL_SCORE_SELECT = 2, /* block scores + top-K selection */
+  HF_KERNEL_SPARSE_SWA = 3,   /* block-sparse attention + linear read + sum */
+  HF_KERNEL_COUNT = 4
+} hf_kernel;
+
+/* Profiling aid (not needed for results). From this call on, every kernel the
+ * state launches is bracketed by two HIP events recorded on the same stream,
+ * for at most max_launches launches per kernel. The events are created here (no
+ * device memory is allocated). Restarting discards earlier records. */
+hf_status hf_profile_start(hf_state* st, int32_t max_launches);
+
+/* Wait for the recorded events and write, per hf_kernel, the summed kernel time
+ * in milliseconds (total_ms[HF_KERNEL_COUNT]) and the number of timed launches
+ * (launches[HF_KERNEL_COUNT]); then stop recording and release the events. */
+hf_status hf_profile_stop(hf_state* st, double* total_ms, int32_t* launches);
 
 /* Absolute index of the next token the state expects to absorb (-1 if st is NULL). */
 int64_t hf_next_ev_index(const hf_state* st);

@@ -417,10 +417,14 @@ __device__ __forceinline__ void lds_barrier() {
 // by nothing else in these kernels.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void lds_dma16(const void* gp, uint32_t lds_off) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+// Address = wave-uniform base (SGPR pair) + per-lane 32-bit byte offset. The
+// compiler cannot see hazards inside the asm, so two wait states separate the m0
+// write (and any VALU write of the offset register) from the load, as the
+// compiler itself does for this instruction.
+__device__ __forceinline__ void lds_dma16(const void* base, uint32_t voff, uint32_t lds_off) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 1\n\tglobal_load_lds_dwordx4 %1, %2"
                :
-               : "s"(lds_off), "v"(gp)
+               : "s"(lds_off), "v"(voff), "s"(base)
                : "memory", "m0");
 }
 #pragma clang diagnostic pop
@@ -428,6 +432,38 @@ __device__ __forceinline__ void lds_dma16(const void* gp, uint32_t lds_off) {
 __device__ __forceinline__ uint32_t lds_offset(const void* p) {
   return (uint32_t)reinterpret_cast<uintptr_t>((lds_void*)p);
 }
+
+// Cross-lane reductions over the 4 lane groups (l, l^16, l^32, l^48) that hold the
+// same query: the gfx950 permlane swaps exchange lane halves / 16-lane rows.
+__device__ __forceinline__ float max_over_groups(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_over_groups(float x) {
+  // Both partners form the same two-term sums, so every lane ends with the same total.
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+// Two fp32 -> packed bf16 (round to nearest even; v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
+}
+
+// The running reference max of a query moves only when a block's max exceeds it by
+// more than this (log2 units), so weights stay <= 2^8 and the output rescale is
+// skipped whenever no query of the wave moved (softmax is shift-invariant).
+constexpr float kLazyMaxSlack = 8.f;
 
 // Wait until at most N vector-memory operations of this wave are in flight.
 template <int N>
@@ -470,23 +506,28 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void s
   // inside a block are fixed, so they are computed once; the block base is
   // wave-uniform. Rows past the window (ragged last block only) repeat the last
   // row: their scores are masked, so the values only need to be finite.
-  int loff[LPT];
+  uint32_t loff[LPT];  // byte offsets inside a block
 #pragma unroll
   for (int u = 0; u < LPT; ++u) {
     const int P = (u * NW + w) * 64 + lane;
     const int row = P / CPR, cc = (P % CPR) ^ (row % CPR);
-    loff[u] = row * D + cc * 8;
+    loff[u] = (uint32_t)(row * D + cc * 8) * 2u;
   }
   auto issue_tile = [&](const bf16_t* src, int jb, const uint4* tile) {
     const bf16_t* tb = src + (size_t)jb * BLK * D;
-    const int64_t left = n_kv - (int64_t)jb * BLK;
-    const int last = (int)(left < BLK ? left : BLK) - 1;  // last row inside the window
     const uint32_t base = __builtin_amdgcn_readfirstlane(lds_offset(tile) + w * 64 * 16);
+    const int64_t left = n_kv - (int64_t)jb * BLK;
+    if (left >= BLK) {
 #pragma unroll
-    for (int u = 0; u < LPT; ++u) {
-      const int row = loff[u] / D;
-      const int off = row <= last ? loff[u] : last * D + loff[u] % D;
-      lds_dma16(tb + off, base + u * NW * 64 * 16);
+      for (int u = 0; u < LPT; ++u) lds_dma16(tb, loff[u], base + u * NW * 64 * 16);
+    } else {  // ragged last block: rows past the window repeat the last row
+      const uint32_t row_bytes = D * 2, last = (uint32_t)left - 1;
+#pragma unroll
+      for (int u = 0; u < LPT; ++u) {
+        const uint32_t row = loff[u] / row_bytes;
+        const uint32_t off = row <= last ? loff[u] : last * row_bytes + loff[u] % row_bytes;
+        lds_dma16(tb, off, base + u * NW * 64 * 16);
+      }
     }
   };
 
@@ -541,40 +582,56 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void s
     lds_barrier();  // every wave is done with K(t)
     if (more) issue_tile(kh, my_sel[t + 1], lds_k);
 
-    // ---- online softmax (base 2); p holds the bf16-rounded weights PV uses ----
+    // ---- online softmax (base 2) with a lazily moved reference max ----
     const int64_t key0 = (int64_t)jb * BLK;
-    const bool tail = key0 + BLK > n_kv;
+    if (key0 + BLK > n_kv) {  // ragged last block: keys past the window get -inf
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (key0 + mt * 16 + g * 4 + r >= n_kv)
+#pragma unroll
+            for (int n = 0; n < NQT; ++n) st[mt][n][r] = -INFINITY;
+    }
+    float m_blk[NQT];
+    bool move_any = false;
 #pragma unroll
     for (int n = 0; n < NQT; ++n) {
-      float mx = -INFINITY;
+      float mx = st[0][n][0];
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float x = st[mt][n][r] * sl2;
-          if (tail && key0 + mt * 16 + g * 4 + r >= n_kv) x = -INFINITY;
-          st[mt][n][r] = x;
-          mx = fmaxf(mx, x);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run[n], mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_run[n] - m_new);
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, st[mt][n][r]);
+      m_blk[n] = max_over_groups(mx) * sl2;
+      move_any |= m_blk[n] > m_run[n] + kLazyMaxSlack;
+    }
+    if (__builtin_amdgcn_ballot_w64(move_any)) {  // wave-uniform, rare after block 0
+#pragma unroll
+      for (int n = 0; n < NQT; ++n) {
+        const float m_new = m_blk[n] > m_run[n] + kLazyMaxSlack ? m_blk[n] : m_run[n];
+        const float alpha = __builtin_amdgcn_exp2f(m_run[n] - m_new);
+        m_run[n] = m_new;
+        l_run[n] *= alpha;
+#pragma unroll
+        for (int e = 0; e < NET; ++e) acc[e][n] *= alpha;
+      }
+    }
+    uint32_t pk[NMT][NQT][2];  // bf16 weights, packed in pairs (the B operand of PV)
+#pragma unroll
+    for (int n = 0; n < NQT; ++n) {
       float rs = 0.f;
 #pragma unroll
-      for (int mt = 0; mt < NMT; ++mt)
+      for (int mt = 0; mt < NMT; ++mt) {
+        float e4[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float e = bf16_to_f32(f32_to_bf16_bits(__builtin_amdgcn_exp2f(st[mt][n][r] - m_new)));
-          st[mt][n][r] = e;
-          rs += e;
+          e4[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[mt][n][r], sl2, -m_run[n]));
+          rs += e4[r];
         }
-      rs += __shfl_xor(rs, 16);
-      rs += __shfl_xor(rs, 32);
-      l_run[n] = l_run[n] * alpha + rs;
-      m_run[n] = m_new;
-#pragma unroll
-      for (int e = 0; e < NET; ++e) acc[e][n] *= alpha;
+        pk[mt][n][0] = pack_bf16x2(e4[0], e4[1]);
+        pk[mt][n][1] = pack_bf16x2(e4[2], e4[3]);
+      }
+      l_run[n] += sum_over_groups(rs);
     }
 
     if (more) wait_vmem<LPT>(); else wait_vmem<0>();  // V(t) has landed
@@ -586,16 +643,9 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void s
     for (int c2 = 0; c2 < BLK / 32; ++c2) {
       bf16x8 pop[NQT];
 #pragma unroll
-      for (int n = 0; n < NQT; ++n) {
-        uint32_t b[8];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          b[r] = f32_to_bf16_bits(st[2 * c2][n][r]);
-          b[4 + r] = f32_to_bf16_bits(st[2 * c2 + 1][n][r]);
-        }
-        pop[n] = as_bf16x8(make_uint4(b[0] | (b[1] << 16), b[2] | (b[3] << 16),
-                                      b[4] | (b[5] << 16), b[6] | (b[7] << 16)));
-      }
+      for (int n = 0; n < NQT; ++n)
+        pop[n] = as_bf16x8(make_uint4(pk[2 * c2][n][0], pk[2 * c2][n][1], pk[2 * c2 + 1][n][0],
+                                      pk[2 * c2 + 1][n][1]));
       // Lane group g takes keys 32c2 + 4g + 0..3 then 32c2 + 16 + 4g + 0..3 (the key
       // order of pop); source lane 4j + p points at V[row j][16et + 4p ..].
       const int r0 = c2 * 32 + 4 * g + jr;

@@ -71,115 +71,145 @@ __global__ __launch_bounds__(NTHR) void absorb_reduce(const float* __restrict__ 
   }
 }
 
+// bf16: K and V token tiles (64 tokens x 64 features, 128-byte rows) go straight
+// from global memory into a 4-stage LDS ring (16-byte global->LDS loads); chunk
+// cc of row r sits in slot cc ^ (r mod 8) ^ 4((r / 8) mod 2), so the transposing
+// reads of the four lane groups (rows 8 apart) fall on different banks. Both MFMA
+// operands are read with the transposing LDS read (tokens, the contraction index,
+// end up contiguous per lane); phi, the tail mask and the hi/lo split are applied
+// to the K operand in registers.
+__device__ __forceinline__ int abs_slot(int row, int cc) {
+  return cc ^ (row & 7) ^ (((row >> 3) & 1) << 2);
+}
+
 template <int D>
 __global__ __launch_bounds__(NTHR) void absorb_bf16(const bf16_t* __restrict__ kev,
                                                     const bf16_t* __restrict__ vev,
                                                     int64_t n_ev, int64_t hs, int tps,
                                                     int n_split,
                                                     float* __restrict__ partials) {
-  constexpr int NT = D / AT;  // tiles per edge
-  __shared__ AbsorbSmem<bf16_t> sm;
+  constexpr int NT = D / AT;       // tiles per edge
+  constexpr int NST = 4;           // pipeline stages
+  constexpr int TCH = TS * AT / 8; // 16-byte chunks per tile (512)
+  constexpr int LPT = TCH / NTHR;  // loads per lane per tile (2)
+  __shared__ uint4 lds_k[NST][TCH];
+  __shared__ uint4 lds_v[NST][TCH];
   const int split = blockIdx.x, tile = blockIdx.y, h = blockIdx.z;
   const int jt = tile / NT, it = tile % NT;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, c = lane & 15;
-  const int wj = w >> 1, wi = w & 1;
   const int64_t n0 = (int64_t)split * tps;
   const int64_t n1 = n0 + tps < n_ev ? n0 + tps : n_ev;
+  const int niter = (int)((n1 - n0 + TS - 1) / TS);
+  const bf16_t* kb = kev + (size_t)h * hs + it * AT;
+  const bf16_t* vb = vev + (size_t)h * hs + jt * AT;
 
-  // Staging role: threads 0..127 stage V columns jt*64.., threads 128..255 stage
-  // K columns it*64..; each handles 4 consecutive tokens x 8 features.
-  const bool is_v = tid < 128;
-  const int sid = tid & 127;
-  const int tg = sid >> 3, cg = sid & 7;
-  const bf16_t* src = (is_v ? vev + (size_t)jt * AT : kev + (size_t)it * AT) + (size_t)h * hs +
-                      cg * 8;
-  float zsum[8];
+  // Load u of wave w fills chunks (u*4 + w)*64 + lane of a tile.
+  uint32_t loff[LPT];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) zsum[e] = 0.f;
-
-  f32x4 acc[2][2];
+  for (int u = 0; u < LPT; ++u) {
+    const int P = (u * 4 + w) * 64 + lane;
+    const int row = P / 8, slot = P % 8;
+    const int cc = slot ^ (row & 7) ^ (((row >> 3) & 1) << 2);  // inverse of abs_slot
+    loff[u] = (uint32_t)(row * D + cc * 8) * 2u;
+  }
+  auto issue = [&](int t) {
+    const int st = t % NST;
+    const bf16_t* kt = kb + (size_t)(n0 + (int64_t)t * TS) * D;
+    const bf16_t* vt = vb + (size_t)(n0 + (int64_t)t * TS) * D;
+    const uint32_t kbase = __builtin_amdgcn_readfirstlane(lds_offset(&lds_k[st][0]) + w * 1024);
+    const uint32_t vbase = __builtin_amdgcn_readfirstlane(lds_offset(&lds_v[st][0]) + w * 1024);
+    const int64_t left = n1 - (n0 + (int64_t)t * TS);
+    if (left >= TS) {
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int b = 0; b < 2; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int64_t t0 = n0; t0 < n1; t0 += TS) {
-    uint4 rows[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t n = t0 + tg * 4 + r;
-      rows[r] = ld16(src + n * D, n < n1);
-    }
-    __syncthreads();  // previous iteration's MFMAs are done with the tiles
-    if (is_v) {
-      // Transpose 4 tokens x 8 features into 8 rows of 4 tokens.
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        uint32_t v4[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v4[r] = half16(rows[r], e);
-        uint2 pk = make_uint2(v4[0] | (v4[1] << 16), v4[2] | (v4[3] << 16));
-        *reinterpret_cast<uint2*>(&sm.vt[cg * 8 + e][tg * 4]) = pk;
+      for (int u = 0; u < LPT; ++u) {
+        lds_dma16(kt, loff[u], kbase + u * 4096);
+        lds_dma16(vt, loff[u], vbase + u * 4096);
       }
-    } else {
+    } else {  // partial last tile: rows past the end repeat the last row (masked below)
+      const uint32_t rb = D * 2, last = (uint32_t)left - 1;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        uint32_t hi4[4], lo4[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const bool ok = t0 + tg * 4 + r < n1;
-          const float x = bf16_to_f32(half16(rows[r], e));
-          const float f = ok ? phi(x) : 0.f;
-          zsum[e] += f;
-          hi4[r] = f32_to_bf16_bits(f);
-          lo4[r] = f32_to_bf16_bits(f - bf16_to_f32(hi4[r]));
-        }
-        *reinterpret_cast<uint2*>(&sm.fhi[cg * 8 + e][tg * 4]) =
-            make_uint2(hi4[0] | (hi4[1] << 16), hi4[2] | (hi4[3] << 16));
-        *reinterpret_cast<uint2*>(&sm.flo[cg * 8 + e][tg * 4]) =
-            make_uint2(lo4[0] | (lo4[1] << 16), lo4[2] | (lo4[3] << 16));
+      for (int u = 0; u < LPT; ++u) {
+        const uint32_t row = loff[u] / rb;
+        const uint32_t off = row <= last ? loff[u] : last * rb + loff[u] % rb;
+        lds_dma16(kt, off, kbase + u * 4096);
+        lds_dma16(vt, off, vbase + u * 4096);
       }
     }
-    __syncthreads();
+  };
+
+  // Wave w owns key-feature columns 16w .. 16w+15 of the tile and all 64 value
+  // rows, so phi of every K element is formed exactly once.
+  f32x4 acc[4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a) acc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float zacc = 0.f;
+  const int jr = (lane & 15) >> 2, pp = lane & 3;  // transposing-read source role
+
+  // Byte address of the 8 bytes (row, 4 features at col) of a tile.
+  auto tr_addr = [&](const uint4* base, int row, int col) {
+    return reinterpret_cast<const char*>(base) + (row * 8 + abs_slot(row, col >> 3)) * 16 +
+           ((col >> 2) & 1) * 8;
+  };
+
+  for (int t = 0; t < NST - 1 && t < niter; ++t) issue(t);
+  for (int t = 0; t < niter; ++t) {
+    // Stage t has landed once at most (#later stages issued) * 2 * LPT loads remain.
+    const int later = (niter - 1 - t) < (NST - 2) ? (niter - 1 - t) : (NST - 2);
+    if (later >= 2) wait_vmem<2 * 2 * LPT>();
+    else if (later == 1) wait_vmem<2 * LPT>();
+    else wait_vmem<0>();
+    lds_barrier();
+    if (t + NST - 1 < niter) issue(t + NST - 1);  // its stage was consumed at t - 1
+    const int st = t % NST;
+    const int valid = (int)(n1 - (n0 + (int64_t)t * TS));  // tokens of this tile in range
 #pragma unroll
     for (int ks = 0; ks < TS / 32; ++ks) {
-      bf16x8 a[2], bh[2], bl[2];
+      const int r0 = ks * 32 + g * 8 + jr;  // rows of the first transposing read
+      // B: phi(K) for this wave's 16 columns, tokens ks*32 + 8g + 0..7, split hi + lo.
+      const int ck = w * 16 + pp * 4;
+      const v4i16 k0 = lds_read_tr(tr_addr(lds_k[st], r0, ck));
+      const v4i16 k1 = lds_read_tr(tr_addr(lds_k[st], r0 + 4, ck));
+      float f[8];
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        a[q] = as_bf16x8(*reinterpret_cast<const uint4*>(&sm.vt[wj * 32 + q * 16 + c][ks * 32 + g * 8]));
-        bh[q] = as_bf16x8(*reinterpret_cast<const uint4*>(&sm.fhi[wi * 32 + q * 16 + c][ks * 32 + g * 8]));
-        bl[q] = as_bf16x8(*reinterpret_cast<const uint4*>(&sm.flo[wi * 32 + q * 16 + c][ks * 32 + g * 8]));
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t bits = (uint32_t)(uint16_t)(e < 4 ? k0[e] : k1[e - 4]);
+        const int tok = ks * 32 + g * 8 + e;  // token of element e in this lane
+        f[e] = tok < valid ? phi(bf16_to_f32(bits)) : 0.f;
+        zacc += f[e];
       }
+      uint32_t hw[4], lw[4];
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj)
+      for (int e = 0; e < 4; ++e) {
+        hw[e] = pack_bf16x2(f[2 * e], f[2 * e + 1]);
+        lw[e] = pack_bf16x2(f[2 * e] - __uint_as_float(hw[e] << 16),
+                            f[2 * e + 1] - __uint_as_float(hw[e] & 0xFFFF0000u));
+      }
+      const bf16x8 bh = as_bf16x8(make_uint4(hw[0], hw[1], hw[2], hw[3]));
+      const bf16x8 bl = as_bf16x8(make_uint4(lw[0], lw[1], lw[2], lw[3]));
+      // A: V^T for the 4 value-row tiles.
 #pragma unroll
-        for (int ii = 0; ii < 2; ++ii) {
-          acc[jj][ii] = Mfma<bf16_t>::mma(a[jj], bh[ii], acc[jj][ii]);
-          acc[jj][ii] = Mfma<bf16_t>::mma(a[jj], bl[ii], acc[jj][ii]);
-        }
+      for (int q = 0; q < 4; ++q) {
+        const int cv = q * 16 + pp * 4;
+        const v4i16 v0 = lds_read_tr(tr_addr(lds_v[st], r0, cv));
+        const v4i16 v1 = lds_read_tr(tr_addr(lds_v[st], r0 + 4, cv));
+        const bf16x8 a =
+            __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[q] = Mfma<bf16_t>::mma(a, bh, acc[q]);
+        acc[q] = Mfma<bf16_t>::mma(a, bl, acc[q]);
+      }
     }
   }
 
-  // Partial tile -> workspace.
+  // Partial tile and partial z.
   float* part = partials + (((size_t)h * NT * NT + tile) * n_split + split) * PART;
 #pragma unroll
-  for (int jj = 0; jj < 2; ++jj)
+  for (int q = 0; q < 4; ++q)
 #pragma unroll
-    for (int ii = 0; ii < 2; ++ii)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        part[(wj * 32 + jj * 16 + g * 4 + r) * AT + wi * 32 + ii * 16 + c] = acc[jj][ii][r];
-  if (!is_v) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) sm.zred[tg][cg * 8 + e] = zsum[e];
-  }
-  __syncthreads();
-  if (tid < AT) {
-    float s = 0.f;
-    for (int q = 0; q < 16; ++q) s += sm.zred[q][tid];
-    part[AT * AT + tid] = s;
-  }
+    for (int r = 0; r < 4; ++r) part[(q * 16 + g * 4 + r) * AT + w * 16 + c] = acc[q][r];
+  const float zs = sum_over_groups(zacc);
+  if (g == 0) part[AT * AT + w * 16 + c] = zs;
 }
 
 template <int D>

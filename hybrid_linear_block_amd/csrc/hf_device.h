@@ -28,6 +28,13 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return u >> 16;
 }
 
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+// Two fp32 -> packed bf16 (round to nearest even; v_cvt_pk_bf16_f32), lo in bits 0..15.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
+}
+
 // phi(x) = elu(x) + 1
 __device__ __forceinline__ float phi(float x) { return x > 0.f ? x + 1.f : __expf(x); }
 
@@ -94,6 +101,82 @@ __device__ __forceinline__ int xcd_remap(int wg, int n_wg_padded, int n_logical)
   const int per = n_wg_padded >> 3;
   const int logical = (wg & 7) * per + (wg >> 3);
   return logical < n_logical ? logical : -1;
+}
+
+
+// ---------------------------------------------------------------------------
+// LDS staging helpers shared by the MFMA kernels.
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, if lane
+// 4j + p supplies the address of 4 consecutive elements M[j][4p .. 4p+3], lane i
+// receives M[0..3][i].
+__device__ __forceinline__ v4i16 lds_read_tr(const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p));
+}
+
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// This wave's LDS reads are complete, then a plain s_barrier (no memory fence, so
+// in-flight global->LDS loads are not waited for).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// 16-byte global -> LDS load of every lane: lane l's 16 bytes land at LDS byte
+// offset lds_off + 16 l (lds_off wave-uniform). Issued from inline asm so that the
+// compiler does not track it: the kernel orders these loads itself (wait_vmem and
+// the barriers), and the compiler's own tracking would make every LDS read wait
+// for all of them. Vector-memory operations complete in issue order, so loads the
+// compiler does not know about can only make its own waits stricter. m0 is used
+// by nothing else in these kernels.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// Address = wave-uniform base (SGPR pair) + per-lane 32-bit byte offset. The
+// compiler cannot see hazards inside the asm, so two wait states separate the m0
+// write (and any VALU write of the offset register) from the load, as the
+// compiler itself does for this instruction.
+__device__ __forceinline__ void lds_dma16(const void* base, uint32_t voff, uint32_t lds_off) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 1\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds_off), "v"(voff), "s"(base)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>((lds_void*)p);
+}
+
+
+// Wait until at most N vector-memory operations of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(N | (0x7 << 4) | (0xF << 8));
+}
+
+// Cross-lane reductions over the 4 lane groups (l, l^16, l^32, l^48) that hold the
+// same MFMA column: the gfx950 permlane swaps exchange lane halves / 16-lane rows.
+__device__ __forceinline__ float max_over_groups(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_over_groups(float x) {
+  // Both partners form the same two-term sums, so every lane ends with the same total.
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 }  // namespace hf

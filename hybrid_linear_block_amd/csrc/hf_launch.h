@@ -21,7 +21,7 @@ hipError_t launch_absorb(int dtype, int heads, int d, const void* k, const void*
                          hipStream_t stream);
 
 // ---- block pooling, scoring and top-K selection ----------------------------------
-constexpr int kMaxKeyBlocks = 8192;
+constexpr int kMaxKeyBlocks = 2048;  // key blocks per window (selection LDS budget)
 hipError_t launch_block_pool(int dtype, int heads, int d, int block, const void* q, int64_t n_q,
                              int64_t q_hs, const void* k, int64_t n_kv, int64_t kv_hs,
                              float* pooled_q, float* pooled_k, int nqb_cap, int nkb_cap,

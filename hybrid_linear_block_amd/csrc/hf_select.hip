@@ -6,14 +6,15 @@
 // 2.A.2 "Block-Sparse Sliding Window Attention"). The importance of key block j
 // for query block i is tau * mean(Q rows of i) . mean(K rows of j), in fp32.
 //
-// block_pool  (HBM-bound): one workgroup per (block, head) streams the block's
-//             rows once with 16-byte coalesced loads and writes the fp32 row mean.
-// score_select (latency-bound): one workgroup per (query block, head) forms the
-//             block's scores against all key blocks, then selects the top_k by
-//             exact rank counting on a unique order-preserving key (score bits,
-//             then lower index first) and compacts the kept indices in ascending
-//             order with wave ballots. Ties therefore go to the lower index, and
-//             -0.0 counts as +0.0.
+// block_pool  (HBM-bound): one wave per (head, block) streams the block's rows
+//             once with 16-byte coalesced loads (all in flight together) and
+//             writes the fp32 row mean.
+// score_select (latency-bound): one workgroup per (4 query blocks, head) forms
+//             their scores against all key blocks (one thread per key block),
+//             then one wave per query block selects the top_k exactly on an
+//             order-preserving uint32 key of the fp32 score (-0.0 counts as
+//             +0.0), ties going to the lower index, and writes the kept indices
+//             in ascending order.
 #include "hf_device.h"
 #include "hf_launch.h"
 
@@ -21,48 +22,62 @@ namespace hf {
 
 namespace {
 
-constexpr int POOL_THREADS = 256;
+constexpr int POOL_THREADS = 256;  // 4 waves, one (head, block) per wave
 
+// Row mean of one block per wave: lane (rg, cc) accumulates 16-byte column chunk
+// cc over rows rg, rg + RPI, ... (all loads independent), then the row groups are
+// added with lane exchanges in a fixed order.
 template <typename T, int D>
 __global__ __launch_bounds__(POOL_THREADS) void block_pool(
     const T* __restrict__ q, int64_t n_q, int64_t q_hs, const T* __restrict__ k, int64_t n_kv,
-    int64_t kv_hs, int block, int nqb, float* __restrict__ pooled_q,
+    int64_t kv_hs, int block, int nqb, int nkb, int heads, float* __restrict__ pooled_q,
     float* __restrict__ pooled_k, int nqb_cap, int nkb_cap) {
-  constexpr int VEC = 16 / sizeof(T);    // elements per 16-byte chunk
-  constexpr int CPR = D / VEC;           // chunks per row
-  constexpr int RPP = POOL_THREADS / CPR;  // rows per pass
-  __shared__ float red[RPP][D];
-  const int b = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  constexpr int VEC = 16 / sizeof(T);  // elements per 16-byte chunk
+  constexpr int CPR = D / VEC;         // chunks per row
+  constexpr int RPI = 64 / CPR;        // rows per wave-wide load
+  const int lane = threadIdx.x & 63;
+  const int wid = blockIdx.x * (POOL_THREADS / 64) + (threadIdx.x >> 6);
+  if (wid >= heads * (nqb + nkb)) return;
+  const int h = wid / (nqb + nkb), b = wid % (nqb + nkb);
   const bool is_q = b < nqb;
   const int blk = is_q ? b : b - nqb;
   const int64_t n = is_q ? n_q : n_kv;
-  const T* base = (is_q ? q + (size_t)h * q_hs : k + (size_t)h * kv_hs);
+  const T* base = is_q ? q + (size_t)h * q_hs : k + (size_t)h * kv_hs;
   const int64_t r0 = (int64_t)blk * block;
   const int64_t r1 = r0 + block < n ? r0 + block : n;
-  const int cc = tid % CPR, rg = tid / CPR;
+  const int cc = lane % CPR, rg = lane / CPR;
   float acc[VEC];
 #pragma unroll
   for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
-  for (int64_t r = r0 + rg; r < r1; r += RPP) {
-    const uint4 x = *reinterpret_cast<const uint4*>(base + r * D + cc * VEC);
+  constexpr int MAXIT = 64 / RPI;  // blocks have at most 64 rows
+  uint4 x[MAXIT];
+#pragma unroll
+  for (int u = 0; u < MAXIT; ++u) {
+    const int64_t r = r0 + rg + u * RPI;
+    x[u] = ld16(base + r * D + cc * VEC, r < r1);  // rows past the block read nothing
+  }
+#pragma unroll
+  for (int u = 0; u < MAXIT; ++u) {
     if constexpr (sizeof(T) == 2) {
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) acc[e] += bf16_to_f32(half16(x, e));
+      for (int e = 0; e < VEC; ++e) acc[e] += bf16_to_f32(half16(x[u], e));
     } else {
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) acc[e] += __uint_as_float(word(x, e));
+      for (int e = 0; e < VEC; ++e) acc[e] += __uint_as_float(word(x[u], e));
     }
   }
 #pragma unroll
-  for (int e = 0; e < VEC; ++e) red[rg][cc * VEC + e] = acc[e];
-  __syncthreads();
-  if (tid < D) {
-    float s = 0.f;
-    for (int p = 0; p < RPP; ++p) s += red[p][tid];
-    const float mean = s / (float)(r1 - r0);
+  for (int off = CPR; off < 64; off <<= 1)
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[e] += __shfl_xor(acc[e], off);
+  if (rg == 0) {
+    const float inv = 1.f / (float)(r1 - r0);
     float* dst = is_q ? pooled_q + ((size_t)h * nqb_cap + blk) * D
                       : pooled_k + ((size_t)h * nkb_cap + blk) * D;
-    dst[tid] = mean;
+#pragma unroll
+    for (int e = 0; e < VEC; e += 4)
+      *reinterpret_cast<float4*>(dst + cc * VEC + e) =
+          make_float4(acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv);
   }
 }
 
@@ -75,65 +90,88 @@ __device__ __forceinline__ uint32_t score_key(float s) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-template <int D>
+constexpr int SEL_QB = SEL_THREADS / 64;  // query blocks per workgroup, one wave each
+
+// Scores of SEL_QB query blocks against all key blocks (one thread per key block,
+// fixed-order dot products), then one wave per query block selects exactly:
+// T = the top_k-th largest key is found bit by bit (count of keys >= candidate by
+// ballots), every key above T is kept, and keys equal to T are kept in ascending
+// index order until top_k are kept; the kept indices are written in ascending
+// order. Keys are unique up to exact score ties, which therefore go to the lower
+// index.
+template <int D, int NE>
 __global__ __launch_bounds__(SEL_THREADS) void score_select(
     const float* __restrict__ pooled_q, const float* __restrict__ pooled_k, int nqb, int nkb,
     int nqb_cap, int nkb_cap, float scale, int top_k, int32_t* __restrict__ sel,
     float* __restrict__ scores_out) {
-  __shared__ uint32_t key[kMaxKeyBlocks];
-  __shared__ int wave_cnt[SEL_THREADS / 64];
-  const int i = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
-  // 16 lanes per key block, D/16 consecutive features per lane.
-  constexpr int PER = D / 16;
-  const int sub = lane & 15, slot = tid >> 4;  // 16 key blocks per pass
-  const float* qm = pooled_q + ((size_t)h * nqb_cap + i) * D + sub * PER;
-  float qv[PER];
+  __shared__ uint32_t key[SEL_QB][kMaxKeyBlocks];
+  __shared__ float4 qs[SEL_QB][D / 4];
+  const int i0 = blockIdx.x * SEL_QB, h = blockIdx.y, tid = threadIdx.x;
+  const int nq = nqb - i0 < SEL_QB ? nqb - i0 : SEL_QB;
+  for (int x = tid; x < SEL_QB * (D / 4); x += SEL_THREADS) {
+    const int r = x / (D / 4), e = x % (D / 4);
+    qs[r][e] = r < nq ? reinterpret_cast<const float4*>(
+                            pooled_q + ((size_t)h * nqb_cap + i0 + r) * D)[e]
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  __syncthreads();
+  for (int j = tid; j < nkb; j += SEL_THREADS) {
+    const float4* km = reinterpret_cast<const float4*>(pooled_k + ((size_t)h * nkb_cap + j) * D);
+    float4 kv[D / 4];
 #pragma unroll
-  for (int e = 0; e < PER; ++e) qv[e] = qm[e];
-  for (int j0 = 0; j0 < nkb; j0 += SEL_THREADS / 16) {
-    const int j = j0 + slot;
-    float s = 0.f;
-    if (j < nkb) {
-      const float* km = pooled_k + ((size_t)h * nkb_cap + j) * D + sub * PER;
+    for (int e = 0; e < D / 4; ++e) kv[e] = km[e];
 #pragma unroll
-      for (int e = 0; e < PER; ++e) s += qv[e] * km[e];
-    }
-    // Fixed-order butterfly over the 16 lanes of this key block.
-    s += __shfl_xor(s, 8, 16);
-    s += __shfl_xor(s, 4, 16);
-    s += __shfl_xor(s, 2, 16);
-    s += __shfl_xor(s, 1, 16);
-    if (j < nkb && sub == 0) {
+    for (int r = 0; r < SEL_QB; ++r) {
+      float s = 0.f;
+#pragma unroll
+      for (int e = 0; e < D / 4; ++e) {
+        const float4 qv = qs[r][e];
+        s += qv.x * kv[e].x;
+        s += qv.y * kv[e].y;
+        s += qv.z * kv[e].z;
+        s += qv.w * kv[e].w;
+      }
       const float sc = s * scale;
-      key[j] = score_key(sc);
-      if (scores_out) scores_out[((size_t)h * nqb + i) * nkb + j] = sc;
+      key[r][j] = score_key(sc);
+      if (scores_out && r < nq) scores_out[((size_t)h * nqb + i0 + r) * nkb + j] = sc;
     }
   }
   __syncthreads();
-  if (!sel) return;
-  int32_t* out = sel + ((size_t)h * nqb + i) * top_k;
-  int base = 0;  // kept blocks with a lower index than this pass
-  for (int j0 = 0; j0 < nkb; j0 += SEL_THREADS) {
-    const int j = j0 + tid;
-    bool keep = false;
-    if (j < nkb) {
-      const uint32_t kj = key[j];
-      int rank = 0;  // blocks ranked strictly before j
-      for (int m = 0; m < nkb; ++m) {
-        const uint32_t km = key[m];
-        rank += (km > kj) | ((km == kj) & (m < j));
-      }
-      keep = rank < top_k;
-    }
-    const uint64_t bal = __ballot(keep);
-    if (lane == 0) wave_cnt[w] = __popcll(bal);
-    __syncthreads();
-    int off = base;
-    for (int q = 0; q < w; ++q) off += wave_cnt[q];
-    if (keep) out[off + __popcll(bal & ((1ull << lane) - 1ull))] = j;
-    for (int q = 0; q < SEL_THREADS / 64; ++q) base += wave_cnt[q];
-    __syncthreads();
+  const int r = tid >> 6, lane = tid & 63;
+  if (!sel || r >= nq) return;
+  // Keys of this query block in registers, key j = 64e + lane; past the window the
+  // key is 0, which never counts (every candidate below is >= 1, and a finite
+  // score's key is >= 1).
+  uint32_t kr[NE];
+#pragma unroll
+  for (int e = 0; e < NE; ++e) {
+    const int j = e * 64 + lane;
+    kr[e] = j < nkb ? key[r][j] : 0u;
+  }
+  auto count_at_least = [&](uint32_t cand) {
+    int cnt = 0;
+#pragma unroll
+    for (int e = 0; e < NE; ++e) cnt += __popcll(__ballot(kr[e] >= cand));
+    return cnt;
+  };
+  uint32_t T = 0u;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = T | (1u << bit);
+    if (count_at_least(cand) >= top_k) T = cand;
+  }
+  const int need = top_k - count_at_least(T + 1u);  // keys equal to T to keep
+  const uint64_t lt = (1ull << lane) - 1ull;
+  int32_t* out = sel + ((size_t)h * nqb + i0 + r) * top_k;
+  int pos = 0, eq_before = 0;
+#pragma unroll
+  for (int e = 0; e < NE; ++e) {
+    const bool eq = kr[e] == T;  // T >= 1, so padding never matches
+    const uint64_t beq = __ballot(eq);
+    const bool keep = kr[e] > T || (eq && eq_before + __popcll(beq & lt) < need);
+    eq_before += __popcll(beq);
+    const uint64_t bk = __ballot(keep);
+    if (keep) out[pos + __popcll(bk & lt)] = e * 64 + lane;
+    pos += __popcll(bk);
   }
 }
 
@@ -145,11 +183,12 @@ hipError_t launch_block_pool(int dtype, int heads, int d, int block, const void*
                              hipStream_t stream) {
   const int nqb = (int)((n_q + block - 1) / block);
   const int nkb = (int)((n_kv + block - 1) / block);
-  dim3 grid(nqb + nkb, heads);
+  const int waves = heads * (nqb + nkb);
+  const int grid = (waves + POOL_THREADS / 64 - 1) / (POOL_THREADS / 64);
 #define HF_POOL(T, D)                                                                        \
   block_pool<T, D><<<grid, POOL_THREADS, 0, stream>>>(                                       \
       static_cast<const T*>(q), n_q, q_hs, static_cast<const T*>(k), n_kv, kv_hs, block, nqb, \
-      pooled_q, pooled_k, nqb_cap, nkb_cap)
+      nkb, heads, pooled_q, pooled_k, nqb_cap, nkb_cap)
   if (dtype == 0) {
     if (d == 128) HF_POOL(bf16_t, 128); else HF_POOL(bf16_t, 64);
   } else {
@@ -162,13 +201,17 @@ hipError_t launch_block_pool(int dtype, int heads, int d, int block, const void*
 hipError_t launch_score_select(int heads, int d, int nqb, int nkb, int nqb_cap, int nkb_cap,
                                const float* pooled_q, const float* pooled_k, float scale,
                                int top_k, int32_t* sel, float* scores_out, hipStream_t stream) {
-  dim3 grid(nqb, heads);
-  if (d == 128)
-    score_select<128><<<grid, SEL_THREADS, 0, stream>>>(pooled_q, pooled_k, nqb, nkb, nqb_cap,
-                                                        nkb_cap, scale, top_k, sel, scores_out);
-  else
-    score_select<64><<<grid, SEL_THREADS, 0, stream>>>(pooled_q, pooled_k, nqb, nkb, nqb_cap,
-                                                       nkb_cap, scale, top_k, sel, scores_out);
+  dim3 grid((nqb + SEL_QB - 1) / SEL_QB, heads);
+#define HF_SEL(D, NE)                                                                      \
+  score_select<D, NE><<<grid, SEL_THREADS, 0, stream>>>(pooled_q, pooled_k, nqb, nkb, nqb_cap, \
+                                                         nkb_cap, scale, top_k, sel, scores_out)
+  // NE = 64-key chunks held per lane in the selection (the smallest that covers nkb).
+  if (d == 128) {
+    if (nkb <= 256) HF_SEL(128, 4); else if (nkb <= 512) HF_SEL(128, 8); else HF_SEL(128, 32);
+  } else {
+    if (nkb <= 256) HF_SEL(64, 4); else if (nkb <= 512) HF_SEL(64, 8); else HF_SEL(64, 32);
+  }
+#undef HF_SEL
   return hipGetLastError();
 }
 

@@ -54,16 +54,6 @@ struct SwaSmem<float, D, BLK> {
   float v[BLK][D + 4];
 };
 
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-
-// Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, if lane
-// 4j + p supplies the address of 4 consecutive elements M[j][4p .. 4p+3], lane i
-// receives M[0..3][i].
-__device__ __forceinline__ v4i16 lds_read_tr(const void* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p));
-}
-
 template <typename T, int D, int BLK, int QW>
 struct SwaCfg {
   static constexpr int NW = BLK / QW;      // waves per workgroup
@@ -79,7 +69,7 @@ struct SwaCfg {
 };
 
 template <typename T, int D, int BLK, int QW>
-__global__ __launch_bounds__((BLK / QW) * 64) __attribute__((amdgpu_waves_per_eu(2))) void sparse_swa(
+__global__ __launch_bounds__((BLK / QW) * 64) void sparse_swa(
     const T* __restrict__ q, int64_t n_q, int64_t q_hs, const T* __restrict__ kg,
     const T* __restrict__ vg, int64_t n_kv, int64_t kv_hs, const int32_t* __restrict__ sel,
     int top_k, int nqb, int n_logical, const float* __restrict__ S,
@@ -400,77 +390,10 @@ __global__ __launch_bounds__((BLK / QW) * 64) __attribute__((amdgpu_waves_per_eu
 // loop the tile buffers hold the normalised sparse output, the linear read is
 // added in place and the rows leave in coalesced 16-byte stores.
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-// This wave's LDS reads are complete, then a plain s_barrier (no memory fence, so
-// in-flight global->LDS loads are not waited for).
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// 16-byte global -> LDS load of every lane: lane l's 16 bytes land at LDS byte
-// offset lds_off + 16 l (lds_off wave-uniform). Issued from inline asm so that the
-// compiler does not track it: the kernel orders these loads itself (wait_vmem and
-// the barriers), and the compiler's own tracking would make every LDS read wait
-// for all of them. Vector-memory operations complete in issue order, so loads the
-// compiler does not know about can only make its own waits stricter. m0 is used
-// by nothing else in these kernels.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-// Address = wave-uniform base (SGPR pair) + per-lane 32-bit byte offset. The
-// compiler cannot see hazards inside the asm, so two wait states separate the m0
-// write (and any VALU write of the offset register) from the load, as the
-// compiler itself does for this instruction.
-__device__ __forceinline__ void lds_dma16(const void* base, uint32_t voff, uint32_t lds_off) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 1\n\tglobal_load_lds_dwordx4 %1, %2"
-               :
-               : "s"(lds_off), "v"(voff), "s"(base)
-               : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-__device__ __forceinline__ uint32_t lds_offset(const void* p) {
-  return (uint32_t)reinterpret_cast<uintptr_t>((lds_void*)p);
-}
-
-// Cross-lane reductions over the 4 lane groups (l, l^16, l^32, l^48) that hold the
-// same query: the gfx950 permlane swaps exchange lane halves / 16-lane rows.
-__device__ __forceinline__ float max_over_groups(float x) {
-  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                  false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                  false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float sum_over_groups(float x) {
-  // Both partners form the same two-term sums, so every lane ends with the same total.
-  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                  false);
-  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                  false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-// Two fp32 -> packed bf16 (round to nearest even; v_cvt_pk_bf16_f32).
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
-}
-
 // The running reference max of a query moves only when a block's max exceeds it by
 // more than this (log2 units), so weights stay <= 2^8 and the output rescale is
 // skipped whenever no query of the wave moved (softmax is shift-invariant).
 constexpr float kLazyMaxSlack = 8.f;
-
-// Wait until at most N vector-memory operations of this wave are in flight.
-template <int N>
-__device__ __forceinline__ void wait_vmem() {
-  static_assert(N >= 0 && N < 16, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt(N | (0x7 << 4) | (0xF << 8));
-}
 
 template <int D>
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void sparse_swa_bf16(

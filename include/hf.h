@@ -86,7 +86,7 @@ typedef struct {
   float eps;           /* added once to the linear normaliser; >= 0 (1e-6 typical) */
   float softmax_scale; /* tau; 0 selects 1/sqrt(head_dim) */
   int64_t max_n_q;     /* capacity limits used to size the workspace */
-  int64_t max_n_kv;    /* ceil(max_n_kv / B) must be <= 8192 */
+  int64_t max_n_kv;    /* ceil(max_n_kv / B) must be <= 2048 */
   int64_t max_n_ev;
   int32_t max_top_k;
 } hf_config;

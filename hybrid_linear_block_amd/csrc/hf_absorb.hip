@@ -6,15 +6,17 @@
 // and in the gist.science English summary "Long-Horizon Streaming Video
 // Generation via Hybrid Attention with Decoupled Distillation", 2.A.1.
 //
-// Work split: grid (token split, 64x64 output tile, head). A workgroup stages 64
-// evicted tokens at a time in LDS (transposed so that tokens, the contraction
-// index, are contiguous per MFMA lane), forms phi(K) in fp32 and, for bf16
-// inputs, splits it into bf16 hi + lo so that the bf16 MFMA keeps ~fp32
-// accuracy (V is exact in bf16). Each workgroup writes a partial 64x64 tile (and
-// a partial z) to the workspace; a second kernel adds the partials in split
-// order to S and z. No atomics or device-wide fences are involved (on a chip
-// whose XCDs have separate L2 caches those would have to write the L2 back),
-// and the order of every sum is fixed, so the result is bitwise reproducible.
+// Work split: one workgroup per (head, token split) forms the partial state of
+// its tokens for the whole head and writes it to the workspace; a second kernel
+// adds the partials to S and z in split order. No atomics or device-wide fences
+// are involved (on a chip whose XCDs have separate L2 caches those would have to
+// write the L2 back), and the order of every sum is fixed, so the result is
+// bitwise reproducible.
+//
+// bf16: wave w owns the key features (state columns) 16w .. 16w+15 and every value
+// feature (state row), so each K element is read once and phi(K) is formed once
+// per workgroup; phi is split into bf16 hi + lo so that the bf16 MFMA keeps ~fp32
+// accuracy (V is exact in bf16).
 #include "hf_device.h"
 #include "hf_launch.h"
 
@@ -22,194 +24,205 @@ namespace hf {
 
 namespace {
 
-constexpr int AT = 64;       // output tile edge
+constexpr float kLog2eAbs = 1.4426950408889634f;
+
+// fp32 path: grid (token split, 64x64 state tile, head).
+constexpr int AT = 64;       // state tile edge
 constexpr int TS = 64;       // tokens staged per iteration
 constexpr int NTHR = 256;    // 4 waves, each owns a 32x32 quarter of the tile
-constexpr int PART = AT * AT + AT;  // floats per partial: tile + z slice
 
-// bf16: transposed tiles [64 features][TS tokens (+8 pad)] of V, phi_hi, phi_lo.
-constexpr int BPITCH = TS + 8;
+// Floats per partial: the head's full state (D x D, value-major) and z (D).
+template <int D>
+constexpr int part_floats() { return D * D + D; }
+
 // fp32: row-major tiles [TS tokens][64 features (+4 pad)] of V and phi.
 constexpr int FPITCH = AT + 4;
 
-template <typename T>
-struct AbsorbSmem;
-
-template <>
-struct AbsorbSmem<bf16_t> {
-  bf16_t vt[AT][BPITCH];
-  bf16_t fhi[AT][BPITCH];
-  bf16_t flo[AT][BPITCH];
-  float zred[16][AT];
-};
-
-template <>
-struct AbsorbSmem<float> {
+struct AbsorbSmemF32 {
   float vs[TS][FPITCH];
   float fs[TS][FPITCH];
   float zred[8][AT];
 };
 
-// Second pass: S[h][tile] += sum_s partial[s] (and z), splits added in order.
+// Second pass: S[h] += sum_s partial[h][s] (and z), splits added in order. Each
+// thread owns 4 consecutive floats; the loads of all splits are independent.
+constexpr int RED_THREADS = 256;
 template <int D>
-__global__ __launch_bounds__(NTHR) void absorb_reduce(const float* __restrict__ partials,
-                                                      int n_split, float* __restrict__ S,
-                                                      float* __restrict__ z) {
-  constexpr int NT = D / AT;
-  const int e = blockIdx.x * NTHR + threadIdx.x;
-  const int tile = blockIdx.y, h = blockIdx.z;
-  const int jt = tile / NT, it = tile % NT;
-  if (e >= PART || (e >= AT * AT && jt != 0)) return;
-  const float* p = partials + ((size_t)h * NT * NT + tile) * n_split * PART + e;
-  float acc = 0.f;
-  for (int s = 0; s < n_split; ++s) acc += p[(size_t)s * PART];
-  if (e < AT * AT) {
-    float* dst = S + (size_t)h * D * D + (size_t)(jt * AT + e / AT) * D + it * AT + e % AT;
-    *dst += acc;
-  } else {
-    z[(size_t)h * D + it * AT + (e - AT * AT)] += acc;
+__global__ __launch_bounds__(RED_THREADS) void absorb_reduce(const float* __restrict__ partials,
+                                                             int n_split, float* __restrict__ S,
+                                                             float* __restrict__ z) {
+  constexpr int P = part_floats<D>();
+  const int e4 = (blockIdx.x * RED_THREADS + threadIdx.x) * 4, h = blockIdx.y;
+  if (e4 >= P) return;
+  const float* p = partials + (size_t)h * n_split * P + e4;
+  // Groups of 4 splits: the loads of a group are issued together, then added in order.
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  int s = 0;
+  for (; s + 4 <= n_split; s += 4) {
+    float4 x[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) x[u] = *reinterpret_cast<const float4*>(p + (size_t)(s + u) * P);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      acc.x += x[u].x;
+      acc.y += x[u].y;
+      acc.z += x[u].z;
+      acc.w += x[u].w;
+    }
   }
+  for (; s < n_split; ++s) {
+    const float4 x = *reinterpret_cast<const float4*>(p + (size_t)s * P);
+    acc.x += x.x;
+    acc.y += x.y;
+    acc.z += x.z;
+    acc.w += x.w;
+  }
+  float* dst = e4 < D * D ? S + (size_t)h * D * D + e4 : z + (size_t)h * D + (e4 - D * D);
+  float4 o = *reinterpret_cast<float4*>(dst);
+  o.x += acc.x;
+  o.y += acc.y;
+  o.z += acc.z;
+  o.w += acc.w;
+  *reinterpret_cast<float4*>(dst) = o;
 }
 
-// bf16: K and V token tiles (64 tokens x 64 features, 128-byte rows) go straight
-// from global memory into a 4-stage LDS ring (16-byte global->LDS loads); chunk
-// cc of row r sits in slot cc ^ (r mod 8) ^ 4((r / 8) mod 2), so the transposing
-// reads of the four lane groups (rows 8 apart) fall on different banks. Both MFMA
-// operands are read with the transposing LDS read (tokens, the contraction index,
-// end up contiguous per lane); phi, the tail mask and the hi/lo split are applied
-// to the K operand in registers.
-__device__ __forceinline__ int abs_slot(int row, int cc) {
-  return cc ^ (row & 7) ^ (((row >> 3) & 1) << 2);
+// bf16: K and V token tiles (BT tokens x D features, rows of D*2 bytes) go straight
+// from global memory into an NST-stage LDS ring (16-byte global->LDS loads, one per
+// thread per tile). Both MFMA operands come from the transposing LDS read (tokens,
+// the contraction index, end up contiguous per lane); phi, the tail mask and the
+// hi/lo split are applied to the K operand in registers. A transposing read covers
+// 32 bytes of rows 8g + e (+4), g, e = 0..3; chunk cc of row r sits in slot
+// cc ^ 2 swz(r), which gives the rows that one half-wave reads (g = 0, 1 or 2, 3)
+// distinct 32-byte bank groups.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) return (r & 3) | ((r >> 1) & 4);  // rows of 256 B: 8 groups
+  else return ((r >> 1) & 1) | ((r >> 2) & 2);            // rows of 128 B: 2 rows per 256 B
 }
+constexpr int BT = 32;   // tokens per stage
+constexpr int BNST = 6;  // stages in the ring (BNST - 1 in flight ahead of the one in use)
 
 template <int D>
-__global__ __launch_bounds__(NTHR) void absorb_bf16(const bf16_t* __restrict__ kev,
-                                                    const bf16_t* __restrict__ vev,
-                                                    int64_t n_ev, int64_t hs, int tps,
-                                                    int n_split,
-                                                    float* __restrict__ partials) {
-  constexpr int NT = D / AT;       // tiles per edge
-  constexpr int NST = 4;           // pipeline stages
-  constexpr int TCH = TS * AT / 8; // 16-byte chunks per tile (512)
-  constexpr int LPT = TCH / NTHR;  // loads per lane per tile (2)
-  __shared__ uint4 lds_k[NST][TCH];
-  __shared__ uint4 lds_v[NST][TCH];
-  const int split = blockIdx.x, tile = blockIdx.y, h = blockIdx.z;
-  const int jt = tile / NT, it = tile % NT;
-  const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+__global__ __launch_bounds__(D * 4) void absorb_bf16(const bf16_t* __restrict__ kev,
+                                                     const bf16_t* __restrict__ vev,
+                                                     int64_t n_ev, int64_t hs, int tps,
+                                                     int n_split,
+                                                     float* __restrict__ partials) {
+  constexpr int NW = D / 16;       // waves: one per 16 key features
+  constexpr int NTH = NW * 64;
+  constexpr int CPR = D / 8;       // 16-byte chunks per row
+  constexpr int TCH = BT * CPR;    // chunks per tile (== NTH: one load per thread)
+  constexpr int NJT = D / 16;      // value-feature tiles
+  static_assert(TCH == NTH, "one 16-byte load per thread and tile");
+  __shared__ uint4 lds_k[BNST][TCH];
+  __shared__ uint4 lds_v[BNST][TCH];
+  const int split = blockIdx.x, h = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, c = lane & 15;
   const int64_t n0 = (int64_t)split * tps;
   const int64_t n1 = n0 + tps < n_ev ? n0 + tps : n_ev;
-  const int niter = (int)((n1 - n0 + TS - 1) / TS);
-  const bf16_t* kb = kev + (size_t)h * hs + it * AT;
-  const bf16_t* vb = vev + (size_t)h * hs + jt * AT;
+  const int niter = (int)((n1 - n0 + BT - 1) / BT);
+  const bf16_t* kb = kev + (size_t)h * hs;
+  const bf16_t* vb = vev + (size_t)h * hs;
 
-  // Load u of wave w fills chunks (u*4 + w)*64 + lane of a tile.
-  uint32_t loff[LPT];
-#pragma unroll
-  for (int u = 0; u < LPT; ++u) {
-    const int P = (u * 4 + w) * 64 + lane;
-    const int row = P / 8, slot = P % 8;
-    const int cc = slot ^ (row & 7) ^ (((row >> 3) & 1) << 2);  // inverse of abs_slot
-    loff[u] = (uint32_t)(row * D + cc * 8) * 2u;
-  }
+  // Thread tid fills LDS chunk tid of a tile (row tid / CPR, slot tid % CPR) with
+  // global chunk slot ^ 2 swz(row) of that row.
+  const int lrow = tid / CPR;
+  const uint32_t loff = (uint32_t)(lrow * D + (((tid % CPR) ^ (2 * swz<D>(lrow))) * 8)) * 2u;
   auto issue = [&](int t) {
-    const int st = t % NST;
-    const bf16_t* kt = kb + (size_t)(n0 + (int64_t)t * TS) * D;
-    const bf16_t* vt = vb + (size_t)(n0 + (int64_t)t * TS) * D;
+    const int st = t % BNST;
+    const int64_t r0 = n0 + (int64_t)t * BT;
+    const bf16_t* kt = kb + (size_t)r0 * D;
+    const bf16_t* vt = vb + (size_t)r0 * D;
     const uint32_t kbase = __builtin_amdgcn_readfirstlane(lds_offset(&lds_k[st][0]) + w * 1024);
     const uint32_t vbase = __builtin_amdgcn_readfirstlane(lds_offset(&lds_v[st][0]) + w * 1024);
-    const int64_t left = n1 - (n0 + (int64_t)t * TS);
-    if (left >= TS) {
-#pragma unroll
-      for (int u = 0; u < LPT; ++u) {
-        lds_dma16(kt, loff[u], kbase + u * 4096);
-        lds_dma16(vt, loff[u], vbase + u * 4096);
-      }
-    } else {  // partial last tile: rows past the end repeat the last row (masked below)
-      const uint32_t rb = D * 2, last = (uint32_t)left - 1;
-#pragma unroll
-      for (int u = 0; u < LPT; ++u) {
-        const uint32_t row = loff[u] / rb;
-        const uint32_t off = row <= last ? loff[u] : last * rb + loff[u] % rb;
-        lds_dma16(kt, off, kbase + u * 4096);
-        lds_dma16(vt, off, vbase + u * 4096);
-      }
+    const int64_t left = n1 - r0;
+    uint32_t off = loff;
+    if (left < BT) {  // partial last tile: rows past the end repeat the last row (masked)
+      const uint32_t last = (uint32_t)left - 1;
+      if ((uint32_t)lrow > last) off = last * (D * 2) + loff % (D * 2);
     }
+    lds_dma16(kt, off, kbase);
+    lds_dma16(vt, off, vbase);
   };
 
-  // Wave w owns key-feature columns 16w .. 16w+15 of the tile and all 64 value
-  // rows, so phi of every K element is formed exactly once.
-  f32x4 acc[4];
+  // Transposing-read source role: lane 4e + q of group g points at row 8g + e (+4),
+  // columns col0 + 4q .. +3 (chunk col0/8 + q/2, half q & 1).
+  const int e_row = (lane & 15) >> 2, q = lane & 3;
+  auto tr_off = [&](int row, int col0) {  // byte offset inside a tile
+    const int cc = (col0 >> 3) + (q >> 1);
+    return (uint32_t)((row * CPR + (cc ^ (2 * swz<D>(row)))) * 16 + (q & 1) * 8);
+  };
+  const int ra = 8 * g + e_row, rb = ra + 4;
+  const uint32_t koff_a = tr_off(ra, w * 16), koff_b = tr_off(rb, w * 16);
+
+  f32x4 acc[NJT];
 #pragma unroll
-  for (int a = 0; a < 4; ++a) acc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < NJT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   float zacc = 0.f;
-  const int jr = (lane & 15) >> 2, pp = lane & 3;  // transposing-read source role
 
-  // Byte address of the 8 bytes (row, 4 features at col) of a tile.
-  auto tr_addr = [&](const uint4* base, int row, int col) {
-    return reinterpret_cast<const char*>(base) + (row * 8 + abs_slot(row, col >> 3)) * 16 +
-           ((col >> 2) & 1) * 8;
-  };
-
-  for (int t = 0; t < NST - 1 && t < niter; ++t) issue(t);
+  for (int t = 0; t < BNST - 1 && t < niter; ++t) issue(t);
   for (int t = 0; t < niter; ++t) {
-    // Stage t has landed once at most (#later stages issued) * 2 * LPT loads remain.
-    const int later = (niter - 1 - t) < (NST - 2) ? (niter - 1 - t) : (NST - 2);
-    if (later >= 2) wait_vmem<2 * 2 * LPT>();
-    else if (later == 1) wait_vmem<2 * LPT>();
-    else wait_vmem<0>();
-    lds_barrier();
-    if (t + NST - 1 < niter) issue(t + NST - 1);  // its stage was consumed at t - 1
-    const int st = t % NST;
-    const int valid = (int)(n1 - (n0 + (int64_t)t * TS));  // tokens of this tile in range
-#pragma unroll
-    for (int ks = 0; ks < TS / 32; ++ks) {
-      const int r0 = ks * 32 + g * 8 + jr;  // rows of the first transposing read
-      // B: phi(K) for this wave's 16 columns, tokens ks*32 + 8g + 0..7, split hi + lo.
-      const int ck = w * 16 + pp * 4;
-      const v4i16 k0 = lds_read_tr(tr_addr(lds_k[st], r0, ck));
-      const v4i16 k1 = lds_read_tr(tr_addr(lds_k[st], r0 + 4, ck));
-      float f[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t bits = (uint32_t)(uint16_t)(e < 4 ? k0[e] : k1[e - 4]);
-        const int tok = ks * 32 + g * 8 + e;  // token of element e in this lane
-        f[e] = tok < valid ? phi(bf16_to_f32(bits)) : 0.f;
-        zacc += f[e];
-      }
-      uint32_t hw[4], lw[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        hw[e] = pack_bf16x2(f[2 * e], f[2 * e + 1]);
-        lw[e] = pack_bf16x2(f[2 * e] - __uint_as_float(hw[e] << 16),
-                            f[2 * e + 1] - __uint_as_float(hw[e] & 0xFFFF0000u));
-      }
-      const bf16x8 bh = as_bf16x8(make_uint4(hw[0], hw[1], hw[2], hw[3]));
-      const bf16x8 bl = as_bf16x8(make_uint4(lw[0], lw[1], lw[2], lw[3]));
-      // A: V^T for the 4 value-row tiles.
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int cv = q * 16 + pp * 4;
-        const v4i16 v0 = lds_read_tr(tr_addr(lds_v[st], r0, cv));
-        const v4i16 v1 = lds_read_tr(tr_addr(lds_v[st], r0 + 4, cv));
-        const bf16x8 a =
-            __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-        acc[q] = Mfma<bf16_t>::mma(a, bh, acc[q]);
-        acc[q] = Mfma<bf16_t>::mma(a, bl, acc[q]);
-      }
+    // Stage t has landed once at most (#later stages issued) * 2 loads remain.
+    const int later = niter - 1 - t < BNST - 2 ? niter - 1 - t : BNST - 2;
+    switch (later) {
+      case 0: wait_vmem<0>(); break;
+      case 1: wait_vmem<2>(); break;
+      case 2: wait_vmem<4>(); break;
+      case 3: wait_vmem<6>(); break;
+      default: wait_vmem<8>(); break;
     }
+    static_assert(BNST - 2 <= 4, "wait cases");
+    lds_barrier();  // ... for every wave; every wave is also done with stage t-1
+    if (t + BNST - 1 < niter) issue(t + BNST - 1);  // into the stage consumed at t - 1
+    const int st = t % BNST;
+    const int valid = (int)(n1 - (n0 + (int64_t)t * BT));  // tokens of this stage in range
+    const uint32_t kt = lds_offset(&lds_k[st][0]), vt = lds_offset(&lds_v[st][0]);
+    // A: V^T for every value-feature tile, tokens in the same order as B. The reads
+    // are issued before the phi work so that their latency is hidden behind it; the
+    // hi products of all tiles go before the lo products, so no MFMA waits for the
+    // one just before it.
+    bf16x8 a[NJT];
+#pragma unroll
+    for (int j = 0; j < NJT; ++j) {
+      const v4i16 v0 = lds_tr8(vt + tr_off(ra, j * 16)), v1 = lds_tr8(vt + tr_off(rb, j * 16));
+      a[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the phi work
+    // B: phi(K) for this wave's 16 key features, tokens 8g + 0..7, split hi + lo.
+    const v4i16 k0 = lds_tr8(kt + koff_a), k1 = lds_tr8(kt + koff_b);
+    float f[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = bf16_to_f32((uint32_t)(uint16_t)(e < 4 ? k0[e] : k1[e - 4]));
+      const float ph = x > 0.f ? x + 1.f : __builtin_amdgcn_exp2f(x * kLog2eAbs);
+      f[e] = 8 * g + e < valid ? ph : 0.f;
+      zacc += f[e];
+    }
+    uint32_t hw[4], lw[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      hw[e] = pack_bf16x2(f[2 * e], f[2 * e + 1]);
+      lw[e] = pack_bf16x2(f[2 * e] - __uint_as_float(hw[e] << 16),
+                          f[2 * e + 1] - __uint_as_float(hw[e] & 0xFFFF0000u));
+    }
+    const bf16x8 bh = as_bf16x8(make_uint4(hw[0], hw[1], hw[2], hw[3]));
+    const bf16x8 bl = as_bf16x8(make_uint4(lw[0], lw[1], lw[2], lw[3]));
+#pragma unroll
+    for (int j = 0; j < NJT; ++j) acc[j] = Mfma<bf16_t>::mma(a[j], bh, acc[j]);
+#pragma unroll
+    for (int j = 0; j < NJT; ++j) acc[j] = Mfma<bf16_t>::mma(a[j], bl, acc[j]);
   }
 
-  // Partial tile and partial z.
-  float* part = partials + (((size_t)h * NT * NT + tile) * n_split + split) * PART;
+  // Partial state: acc[j][r] = S[16j + 4g + r][16w + c].
+  float* part = partials + ((size_t)h * n_split + split) * part_floats<D>();
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
+  for (int j = 0; j < NJT; ++j)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) part[(q * 16 + g * 4 + r) * AT + w * 16 + c] = acc[q][r];
+    for (int r = 0; r < 4; ++r) part[(j * 16 + g * 4 + r) * D + w * 16 + c] = acc[j][r];
   const float zs = sum_over_groups(zacc);
-  if (g == 0) part[AT * AT + w * 16 + c] = zs;
+  if (g == 0) part[D * D + w * 16 + c] = zs;
 }
 
 template <int D>
@@ -218,7 +231,7 @@ __global__ __launch_bounds__(NTHR) void absorb_f32(const float* __restrict__ kev
                                                    int64_t hs, int tps, int n_split,
                                                    float* __restrict__ partials) {
   constexpr int NT = D / AT;
-  __shared__ AbsorbSmem<float> sm;
+  __shared__ AbsorbSmemF32 sm;
   const int split = blockIdx.x, tile = blockIdx.y, h = blockIdx.z;
   const int jt = tile / NT, it = tile % NT;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -284,23 +297,25 @@ __global__ __launch_bounds__(NTHR) void absorb_f32(const float* __restrict__ kev
     }
   }
 
-  float* part = partials + (((size_t)h * NT * NT + tile) * n_split + split) * PART;
+  // This workgroup's 64x64 tile of the head's partial state (z from the jt == 0 tiles).
+  float* part = partials + ((size_t)h * n_split + split) * part_floats<D>();
 #pragma unroll
   for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        part[(wj * 32 + jj * 16 + g * 4 + r) * AT + wi * 32 + ii * 16 + c] = acc[jj][ii][r];
+        part[(size_t)(jt * AT + wj * 32 + jj * 16 + g * 4 + r) * D + it * AT + wi * 32 + ii * 16 +
+             c] = acc[jj][ii][r];
   if (!is_v) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) sm.zred[row0][col4 * 4 + e] = zsum[e];
   }
   __syncthreads();
-  if (tid < AT) {
+  if (tid < AT && jt == 0) {
     float s = 0.f;
     for (int q = 0; q < 8; ++q) s += sm.zred[q][tid];
-    part[AT * AT + tid] = s;
+    part[D * D + it * AT + tid] = s;
   }
 }
 
@@ -309,8 +324,8 @@ __global__ __launch_bounds__(NTHR) void absorb_f32(const float* __restrict__ kev
 AbsorbPlan absorb_plan(int64_t n_ev) {
   AbsorbPlan p;
   int64_t per = (n_ev + kAbsorbMaxSplits - 1) / kAbsorbMaxSplits;
-  if (per < 256) per = 256;
-  per = (per + TS - 1) / TS * TS;
+  if (per < 128) per = 128;
+  per = (per + TS - 1) / TS * TS;  // a multiple of both token tilings (64 and 32)
   p.tokens_per_split = (int)per;
   p.n_split = (int)((n_ev + per - 1) / per);
   if (p.n_split < 1) p.n_split = 1;
@@ -318,32 +333,38 @@ AbsorbPlan absorb_plan(int64_t n_ev) {
 }
 
 size_t absorb_partial_floats(int heads, int d) {
-  const int nt = d / AT;
-  return (size_t)heads * nt * nt * kAbsorbMaxSplits * PART;
+  return (size_t)heads * kAbsorbMaxSplits * (size_t)(d * d + d);
 }
 
 hipError_t launch_absorb(int dtype, int heads, int d, const void* k, const void* v, int64_t n_ev,
                          int64_t head_stride, float* S, float* z, float* partials,
                          hipStream_t stream) {
   const AbsorbPlan p = absorb_plan(n_ev);
-  const int nt = d / AT;
-  dim3 grid(p.n_split, nt * nt, heads);
-#define HF_ABS(KER, T, D)                                                                     \
-  KER<D><<<grid, NTHR, 0, stream>>>(static_cast<const T*>(k), static_cast<const T*>(v), n_ev, \
-                                    head_stride, p.tokens_per_split, p.n_split, partials)
   if (dtype == 0) {
-    if (d == 128) HF_ABS(absorb_bf16, bf16_t, 128); else HF_ABS(absorb_bf16, bf16_t, 64);
-  } else {
-    if (d == 128) HF_ABS(absorb_f32, float, 128); else HF_ABS(absorb_f32, float, 64);
-  }
+    dim3 grid(p.n_split, heads);
+#define HF_ABS(D)                                                                             \
+  absorb_bf16<D><<<grid, D * 4, 0, stream>>>(static_cast<const bf16_t*>(k),                 \
+                                             static_cast<const bf16_t*>(v), n_ev, head_stride, \
+                                             p.tokens_per_split, p.n_split, partials)
+    if (d == 128) HF_ABS(128); else HF_ABS(64);
 #undef HF_ABS
+  } else {
+    const int nt = d / AT;
+    dim3 grid(p.n_split, nt * nt, heads);
+#define HF_ABS(D)                                                                             \
+  absorb_f32<D><<<grid, NTHR, 0, stream>>>(static_cast<const float*>(k),                    \
+                                           static_cast<const float*>(v), n_ev, head_stride,  \
+                                           p.tokens_per_split, p.n_split, partials)
+    if (d == 128) HF_ABS(128); else HF_ABS(64);
+#undef HF_ABS
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dim3 rgrid((PART + NTHR - 1) / NTHR, nt * nt, heads);
-  if (d == 128)
-    absorb_reduce<128><<<rgrid, NTHR, 0, stream>>>(partials, p.n_split, S, z);
-  else
-    absorb_reduce<64><<<rgrid, NTHR, 0, stream>>>(partials, p.n_split, S, z);
+#define HF_RED(D)                                                                   \
+  absorb_reduce<D><<<dim3((part_floats<D>() / 4 + RED_THREADS - 1) / RED_THREADS, heads), \
+                     RED_THREADS, 0, stream>>>(partials, p.n_split, S, z)
+  if (d == 128) HF_RED(128); else HF_RED(64);
+#undef HF_RED
   return hipGetLastError();
 }
 

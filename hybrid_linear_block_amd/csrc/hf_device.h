@@ -151,12 +151,24 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p) {
   return (uint32_t)reinterpret_cast<uintptr_t>((lds_void*)p);
 }
 
+// LDS accesses by byte offset: a lane-varying offset plus a compile-time constant
+// lets the constant go into the instruction's offset field.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 lds_ld16(uint32_t byte_off) {
+  const u32x4_t v =
+      *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>((size_t)byte_off);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ v4i16 lds_tr8(uint32_t byte_off) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)((size_t)byte_off));
+}
+
 
 // Wait until at most N vector-memory operations of this wave are in flight.
 template <int N>
 __device__ __forceinline__ void wait_vmem() {
-  static_assert(N >= 0 && N < 16, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt(N | (0x7 << 4) | (0xF << 8));
+  static_assert(N >= 0 && N < 64, "vmcnt field");  // 6 bits: [3:0] and [15:14]
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
 // Cross-lane reductions over the 4 lane groups (l, l^16, l^32, l^48) that hold the

@@ -8,7 +8,7 @@
 namespace hf {
 
 // ---- absorb: S += V^T phi(K), z += sum phi(K) ------------------------------------
-constexpr int kAbsorbMaxSplits = 8;
+constexpr int kAbsorbMaxSplits = 16;
 struct AbsorbPlan {
   int tokens_per_split;
   int n_split;

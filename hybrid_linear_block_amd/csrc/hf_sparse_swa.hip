@@ -39,9 +39,18 @@ template <typename T, int D, int BLK>
 struct SwaSmem;
 
 // bf16: K and V blocks row-major in 16-byte chunks; chunk cc of row r is stored
-// in slot cc ^ (r mod CPR), which spreads both the 16-byte K operand reads (16
-// rows, one chunk) and the transposing V reads (16 rows, two chunks) over all
-// LDS banks.
+// in slot cc ^ swz(r). A K operand read touches one chunk of 16 consecutive rows,
+// a transposing V read an aligned pair of chunks of 16 consecutive rows (8 per
+// half-wave). With 256-byte rows (CPR = 16) every row starts on the same bank, so
+// swz must give 16 rows distinct slots and 8 consecutive rows distinct slot pairs:
+// swz(r) = 2 (r mod 8) + bit 3 of r. With 128-byte rows (CPR = 8) even and odd
+// rows sit on different bank halves, so the same holds per parity class:
+// swz(r) = 2 ((r / 2) mod 4) + bit 3 of r.
+template <int CPR>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (CPR == 16) return ((r & 7) << 1) | ((r >> 3) & 1);
+  else return (((r >> 1) & 3) << 1) | ((r >> 3) & 1);
+}
 template <int D, int BLK>
 struct SwaSmem<bf16_t, D, BLK> {
   uint4 k[BLK * D / 8];
@@ -425,7 +434,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void s
   const int64_t qrow0 = (int64_t)i * BLK + w * 32;
 
   // Load u of this wave fills LDS chunks (u*NW + w)*64 + lane of a tile with global
-  // chunk (row, (slot ^ row) mod CPR) of the block. The per-lane element offsets
+  // chunk (row, slot ^ swz(row)) of the block. The per-lane element offsets
   // inside a block are fixed, so they are computed once; the block base is
   // wave-uniform. Rows past the window (ragged last block only) repeat the last
   // row: their scores are masked, so the values only need to be finite.
@@ -433,7 +442,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void s
 #pragma unroll
   for (int u = 0; u < LPT; ++u) {
     const int P = (u * NW + w) * 64 + lane;
-    const int row = P / CPR, cc = (P % CPR) ^ (row % CPR);
+    const int row = P / CPR, cc = (P % CPR) ^ swz<CPR>(row);
     loff[u] = (uint32_t)(row * D + cc * 8) * 2u;
   }
   auto issue_tile = [&](const bf16_t* src, int jb, const uint4* tile) {
@@ -496,7 +505,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void s
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt) {
         const int row = mt * 16 + c;
-        const bf16x8 kop = as_bf16x8(lds_k[row * CPR + ((s * 4 + g) ^ (row % CPR))]);
+        const bf16x8 kop = as_bf16x8(lds_k[row * CPR + ((s * 4 + g) ^ swz<CPR>(row))]);
 #pragma unroll
         for (int n = 0; n < NQT; ++n)
           st[mt][n] = Mfma<bf16_t>::mma(kop, qop[n][s], st[mt][n]);
@@ -575,9 +584,9 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void s
 #pragma unroll
       for (int et = 0; et < NET; ++et) {
         const int chunk = 2 * et + (pp >> 1);
-        const v4i16 lo = lds_read_tr(vb + (r0 * CPR + (chunk ^ (r0 % CPR))) * 16 + (pp & 1) * 8);
+        const v4i16 lo = lds_read_tr(vb + (r0 * CPR + (chunk ^ swz<CPR>(r0))) * 16 + (pp & 1) * 8);
         const v4i16 hi =
-            lds_read_tr(vb + ((r0 + 16) * CPR + (chunk ^ (r0 % CPR))) * 16 + (pp & 1) * 8);
+            lds_read_tr(vb + ((r0 + 16) * CPR + (chunk ^ swz<CPR>(r0 + 16))) * 16 + (pp & 1) * 8);
         const bf16x8 vop =
             __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll

@@ -26,6 +26,7 @@ struct hf_state {
   float* pooled_k;
   int32_t* sel;
   float* partials;
+  uint16_t* s_split;  // bf16 hi/lo split of S (bf16 states), kept in step with S
   // Per-kernel timing (hf_profile_start / hf_profile_stop).
   bool prof_on = false;
   int prof_cap = 0;
@@ -65,7 +66,7 @@ hf_status check_config(const hf_config* c) {
 }
 
 struct Layout {
-  size_t pooled_q, pooled_k, sel, partials, total;
+  size_t pooled_q, pooled_k, sel, partials, s_split, total;
 };
 
 Layout layout(const hf_config* c) {
@@ -82,6 +83,8 @@ Layout layout(const hf_config* c) {
   off += round_up(H * nqb * (size_t)c->max_top_k * 4);
   L.partials = off;
   off += round_up(hf::absorb_partial_floats((int)H, (int)d) * 4);
+  L.s_split = off;
+  if (c->dtype == HF_BF16) off += round_up(H * 2 * d * d * 2);
   L.total = off;
   return L;
 }
@@ -170,6 +173,7 @@ hf_status hf_state_init(const hf_config* cfg, float* S, float* z, void* workspac
   st->pooled_k = reinterpret_cast<float*>(st->ws + L.pooled_k);
   st->sel = reinterpret_cast<int32_t*>(st->ws + L.sel);
   st->partials = reinterpret_cast<float*>(st->ws + L.partials);
+  st->s_split = cfg->dtype == HF_BF16 ? reinterpret_cast<uint16_t*>(st->ws + L.s_split) : nullptr;
   if (hipGetDevice(&st->device) != hipSuccess) {
     delete st;
     return HF_ERR_HIP;
@@ -180,6 +184,9 @@ hf_status hf_state_init(const hf_config* cfg, float* S, float* z, void* workspac
     hipError_t e = hipSuccess;
     if (zero_fill) e = hf::launch_fill_zero(S, H * d * d * 4, s);
     if (e == hipSuccess && zero_fill) e = hf::launch_fill_zero(z, H * d * 4, s);
+    if (e == hipSuccess && st->s_split)
+      e = zero_fill ? hf::launch_fill_zero(st->s_split, H * 2 * d * d * 2, s)
+                    : hf::launch_split_state((int)H, (int)d, S, st->s_split, s);
     return e;
   });
   if (r != HF_OK) {
@@ -206,7 +213,7 @@ hf_status hf_absorb_evicted(hf_state* st, const void* k_ev, const void* v_ev, in
   const hf_status r = on_device(st->device, [&]() {
     return timed(st, HF_KERNEL_ABSORB, s, [&]() {
       return hf::launch_absorb(c.dtype, c.num_heads, c.head_dim, k_ev, v_ev, n_ev,
-                               ev_head_stride, st->S, st->z, st->partials, s);
+                               ev_head_stride, st->S, st->z, st->partials, st->s_split, s);
     });
   });
   if (r == HF_OK) st->next_ev += n_ev;
@@ -256,8 +263,8 @@ hf_status hf_attend_chunk(hf_state* st, const void* q, int64_t n_q, int64_t q_he
       r = timed(st, HF_KERNEL_SPARSE_SWA, s, [&]() {
         return hf::launch_sparse_swa(c.dtype, c.num_heads, c.head_dim, c.block_size, q, n_q,
                                      q_head_stride, k_win, v_win, n_kv, kv_head_stride, sel,
-                                     top_k, st->S, st->z, c.eps, st->scale, out, out_head_stride,
-                                     s);
+                                     top_k, st->S, st->s_split, st->z, c.eps, st->scale, out,
+                                     out_head_stride, s);
       });
     return r;
   });

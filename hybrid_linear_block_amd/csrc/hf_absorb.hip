@@ -47,10 +47,33 @@ struct AbsorbSmemF32 {
 // Second pass: S[h] += sum_s partial[h][s] (and z), splits added in order. Each
 // thread owns 4 consecutive floats; the loads of all splits are independent.
 constexpr int RED_THREADS = 256;
+// hi = bf16(x), lo = bf16(x - hi) for 4 values, packed little-endian.
+__device__ __forceinline__ void split4(const float4 x, uint2& hi, uint2& lo) {
+  const float v[4] = {x.x, x.y, x.z, x.w};
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    h[e] = f32_to_bf16_bits(v[e]);
+    l[e] = f32_to_bf16_bits(v[e] - bf16_to_f32(h[e]));
+  }
+  hi = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+  lo = make_uint2(l[0] | (l[1] << 16), l[2] | (l[3] << 16));
+}
+
+template <int D>
+__device__ __forceinline__ void store_split(uint16_t* s_split, int h, int e4, float4 x) {
+  uint2 hi, lo;
+  split4(x, hi, lo);
+  uint16_t* dst = s_split + (size_t)h * 2 * D * D + e4;
+  *reinterpret_cast<uint2*>(dst) = hi;
+  *reinterpret_cast<uint2*>(dst + D * D) = lo;
+}
+
 template <int D>
 __global__ __launch_bounds__(RED_THREADS) void absorb_reduce(const float* __restrict__ partials,
                                                              int n_split, float* __restrict__ S,
-                                                             float* __restrict__ z) {
+                                                             float* __restrict__ z,
+                                                             uint16_t* __restrict__ s_split) {
   constexpr int P = part_floats<D>();
   const int e4 = (blockIdx.x * RED_THREADS + threadIdx.x) * 4, h = blockIdx.y;
   if (e4 >= P) return;
@@ -84,6 +107,15 @@ __global__ __launch_bounds__(RED_THREADS) void absorb_reduce(const float* __rest
   o.z += acc.z;
   o.w += acc.w;
   *reinterpret_cast<float4*>(dst) = o;
+  if (s_split && e4 < D * D) store_split<D>(s_split, h, e4, o);
+}
+
+template <int D>
+__global__ __launch_bounds__(RED_THREADS) void split_state(const float* __restrict__ S,
+                                                           uint16_t* __restrict__ s_split) {
+  const int e4 = (blockIdx.x * RED_THREADS + threadIdx.x) * 4, h = blockIdx.y;
+  if (e4 >= D * D) return;
+  store_split<D>(s_split, h, e4, *reinterpret_cast<const float4*>(S + (size_t)h * D * D + e4));
 }
 
 // bf16: K and V token tiles (BT tokens x D features, rows of D*2 bytes) go straight
@@ -338,7 +370,7 @@ size_t absorb_partial_floats(int heads, int d) {
 
 hipError_t launch_absorb(int dtype, int heads, int d, const void* k, const void* v, int64_t n_ev,
                          int64_t head_stride, float* S, float* z, float* partials,
-                         hipStream_t stream) {
+                         uint16_t* s_split, hipStream_t stream) {
   const AbsorbPlan p = absorb_plan(n_ev);
   if (dtype == 0) {
     dim3 grid(p.n_split, heads);
@@ -362,9 +394,19 @@ hipError_t launch_absorb(int dtype, int heads, int d, const void* k, const void*
   if (e != hipSuccess) return e;
 #define HF_RED(D)                                                                   \
   absorb_reduce<D><<<dim3((part_floats<D>() / 4 + RED_THREADS - 1) / RED_THREADS, heads), \
-                     RED_THREADS, 0, stream>>>(partials, p.n_split, S, z)
+                     RED_THREADS, 0, stream>>>(partials, p.n_split, S, z, s_split)
   if (d == 128) HF_RED(128); else HF_RED(64);
 #undef HF_RED
+  return hipGetLastError();
+}
+
+hipError_t launch_split_state(int heads, int d, const float* S, uint16_t* s_split,
+                              hipStream_t stream) {
+  const int blocks = (d * d / 4 + RED_THREADS - 1) / RED_THREADS;
+  if (d == 128)
+    split_state<128><<<dim3(blocks, heads), RED_THREADS, 0, stream>>>(S, s_split);
+  else
+    split_state<64><<<dim3(blocks, heads), RED_THREADS, 0, stream>>>(S, s_split);
   return hipGetLastError();
 }
 

@@ -15,10 +15,16 @@ struct AbsorbPlan {
 };
 AbsorbPlan absorb_plan(int64_t n_ev);
 size_t absorb_partial_floats(int heads, int d);
-// Two kernels: per-split partial tiles into `partials`, then an in-order reduction.
+// Two kernels: per-split partial states into `partials`, then an in-order reduction,
+// which also refreshes s_split (if not null) from the new S.
 hipError_t launch_absorb(int dtype, int heads, int d, const void* k, const void* v, int64_t n_ev,
                          int64_t head_stride, float* S, float* z, float* partials,
-                         hipStream_t stream);
+                         uint16_t* s_split, hipStream_t stream);
+// s_split[h] = the bf16 hi and lo parts of S[h] ([H][2][d][d]): x ~= hi + lo, hi =
+// bf16(x), lo = bf16(x - hi), both rounded to nearest even. The bf16 attention
+// epilogue reads S in this form.
+hipError_t launch_split_state(int heads, int d, const float* S, uint16_t* s_split,
+                              hipStream_t stream);
 
 // ---- block pooling, scoring and top-K selection ----------------------------------
 constexpr int kMaxKeyBlocks = 2048;  // key blocks per window (selection LDS budget)
@@ -34,8 +40,8 @@ hipError_t launch_score_select(int heads, int d, int nqb, int nkb, int nqb_cap, 
 hipError_t launch_sparse_swa(int dtype, int heads, int d, int block, const void* q, int64_t n_q,
                              int64_t q_hs, const void* k, const void* v, int64_t n_kv,
                              int64_t kv_hs, const int32_t* sel, int top_k, const float* S,
-                             const float* z, float eps, float scale, void* out, int64_t out_hs,
-                             hipStream_t stream);
+                             const uint16_t* s_split, const float* z, float eps, float scale,
+                             void* out, int64_t out_hs, hipStream_t stream);
 
 // ---- utilities -------------------------------------------------------------------
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream);

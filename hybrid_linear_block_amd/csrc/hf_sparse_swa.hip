@@ -395,27 +395,26 @@ __global__ __launch_bounds__((BLK / QW) * 64) void sparse_swa(
 // The two tiles are single-buffered and their loads are staggered so each one
 // overlaps compute: K(t+1) streams in during the softmax and O^T += V^T P^T of
 // block t, V(t+1) during S^T = K Q^T and the softmax of block t+1. The V operand
-// is read with the transposing LDS read, so V needs no transposed copy. After the
-// loop the tile buffers hold the normalised sparse output, the linear read is
-// added in place and the rows leave in coalesced 16-byte stores.
+// is read with the transposing LDS read, so V needs no transposed copy. The
+// epilogue normalises the accumulators in place, adds the linear read on MFMA
+// into them and stores the rows from registers.
 
 // The running reference max of a query moves only when a block's max exceeds it by
 // more than this (log2 units), so weights stay <= 2^8 and the output rescale is
 // skipped whenever no query of the wave moved (softmax is shift-invariant).
 constexpr float kLazyMaxSlack = 8.f;
 
-template <int D>
+template <int D, bool SHORT>
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void sparse_swa_bf16(
     const bf16_t* __restrict__ q, int64_t n_q, int64_t q_hs, const bf16_t* __restrict__ kg,
     const bf16_t* __restrict__ vg, int64_t n_kv, int64_t kv_hs, const int32_t* __restrict__ sel,
-    int top_k, int nqb, int n_logical, const float* __restrict__ S,
+    int top_k, int nqb, int n_logical, const uint16_t* __restrict__ s_split,
     const float* __restrict__ z, float eps, float scale, bf16_t* __restrict__ out,
     int64_t out_hs) {
   constexpr int BLK = 64, NW = 2, NQT = 2, NMT = 4, NET = D / 16, NKS = D / 32;
   constexpr int CPR = D / 8;            // 16-byte chunks per K/V row
   constexpr int TCH = BLK * CPR;        // chunks per tile
   constexpr int LPT = TCH / (NW * 64);  // global->LDS loads per lane per tile
-  constexpr int OCPR = D / 4;           // 16-byte fp32 chunks per staged output row
   // Separate objects, so that the compiler can tell an in-flight load into one
   // tile from reads of the other; after the loop each holds one wave's output rows.
   __shared__ uint4 lds_k[TCH];
@@ -445,15 +444,22 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void s
     const int row = P / CPR, cc = (P % CPR) ^ swz<CPR>(row);
     loff[u] = (uint32_t)(row * D + cc * 8) * 2u;
   }
+  // The ragged last block of the window is loaded as the window's last BLK rows
+  // (all in bounds; its valid keys are then the tile's last rows and the rows
+  // before them are masked), so every load of every tile takes the same address
+  // path. A window shorter than one block (SHORT) repeats its last row instead.
+  auto tile_row0 = [&](int jb) {
+    const int64_t r0 = (int64_t)jb * BLK;
+    return (!SHORT && r0 + BLK > n_kv) ? n_kv - BLK : r0;
+  };
   auto issue_tile = [&](const bf16_t* src, int jb, const uint4* tile) {
-    const bf16_t* tb = src + (size_t)jb * BLK * D;
+    const bf16_t* tb = src + (size_t)tile_row0(jb) * D;
     const uint32_t base = __builtin_amdgcn_readfirstlane(lds_offset(tile) + w * 64 * 16);
-    const int64_t left = n_kv - (int64_t)jb * BLK;
-    if (left >= BLK) {
+    if constexpr (!SHORT) {
 #pragma unroll
       for (int u = 0; u < LPT; ++u) lds_dma16(tb, loff[u], base + u * NW * 64 * 16);
-    } else {  // ragged last block: rows past the window repeat the last row
-      const uint32_t row_bytes = D * 2, last = (uint32_t)left - 1;
+    } else {
+      const uint32_t row_bytes = D * 2, last = (uint32_t)n_kv - 1;
 #pragma unroll
       for (int u = 0; u < LPT; ++u) {
         const uint32_t row = loff[u] / row_bytes;
@@ -470,6 +476,29 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void s
     const int64_t r = qrow0 + n * 16 + c;
 #pragma unroll
     for (int s = 0; s < NKS; ++s) qop[n][s] = as_bf16x8(ld16(qh + r * D + s * 32 + g * 8, r < n_q));
+  }
+
+  // Normaliser of the linear read, 1 / (z . phi(q) + eps), formed here (fp32) so that
+  // it is ready when the epilogue folds the linear read into the accumulators.
+  float inv_den[NQT];
+  {
+    const float* zh = z + (size_t)h * D;
+    float den[NQT] = {};
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+      const int i0 = s * 32 + g * 8;
+      const float4 z0 = *reinterpret_cast<const float4*>(zh + i0);
+      const float4 z1 = *reinterpret_cast<const float4*>(zh + i0 + 4);
+      const float zz[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
+#pragma unroll
+      for (int n = 0; n < NQT; ++n) {
+        const uint4 qb = __builtin_bit_cast(uint4, qop[n][s]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) den[n] += zz[e] * phi(bf16_to_f32(half16(qb, e)));
+      }
+    }
+#pragma unroll
+    for (int n = 0; n < NQT; ++n) inv_den[n] = 1.f / (sum_over_groups(den[n]) + eps);
   }
 
   f32x4 acc[NET][NQT];
@@ -516,14 +545,17 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void s
 
     // ---- online softmax (base 2) with a lazily moved reference max ----
     const int64_t key0 = (int64_t)jb * BLK;
-    if (key0 + BLK > n_kv) {  // ragged last block: keys past the window get -inf
+    if (key0 + BLK > n_kv) {  // ragged last block: tile rows outside the block get -inf
+      const int valid = (int)(n_kv - key0);
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (key0 + mt * 16 + g * 4 + r >= n_kv)
+        for (int r = 0; r < 4; ++r) {
+          const int tr = mt * 16 + g * 4 + r;  // tile row of this key
+          const bool out = SHORT ? tr >= valid : tr < BLK - valid;
 #pragma unroll
-            for (int n = 0; n < NQT; ++n) st[mt][n][r] = -INFINITY;
+          for (int n = 0; n < NQT; ++n) st[mt][n][r] = out ? -INFINITY : st[mt][n][r];
+        }
     }
     float m_blk[NQT];
     bool move_any = false;
@@ -598,113 +630,79 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void s
   }
 
   // ---- epilogue ----
-  // Normalised sparse output -> this wave's tile buffer (K for wave 0, V for wave 1),
-  // fp32 rows of OCPR chunks, chunk ch of row r in slot ch ^ (r mod OCPR).
-  static_assert(32 * OCPR == TCH, "one wave's output rows fill one tile buffer");
-  float4* ob = reinterpret_cast<float4*>(w == 0 ? lds_k : lds_v);
+  // out = O / l + S phi(q) / (z . phi(q) + eps): the accumulators are normalised in
+  // place, then the linear read accumulates S (phi(q) / den) into them on MFMA, with
+  // S and the scaled phi(q) split into bf16 hi + lo (three products; the split of S
+  // is kept up to date with S by the absorb). The 16 S operand loads of a k-step are
+  // issued together.
 #pragma unroll
   for (int n = 0; n < NQT; ++n) {
     const float inv_l = 1.f / l_run[n];
-    const int row = n * 16 + c;
 #pragma unroll
-    for (int et = 0; et < NET; ++et)
-      ob[row * OCPR + ((et * 4 + g) ^ (row % OCPR))] =
-          make_float4(acc[et][n][0] * inv_l, acc[et][n][1] * inv_l, acc[et][n][2] * inv_l,
-                      acc[et][n][3] * inv_l);
+    for (int et = 0; et < NET; ++et) acc[et][n] *= inv_l;
   }
-
-  // Linear read: num^T = S phi(Q)^T on MFMA with S and phi(q) split into bf16 hi + lo
-  // (three products), normaliser z . phi(q) in fp32.
-  const float* Sh = S + (size_t)h * D * D;
-  const float* zh = z + (size_t)h * D;
-  f32x4 num[NET][NQT];
-#pragma unroll
-  for (int e = 0; e < NET; ++e)
-#pragma unroll
-    for (int n = 0; n < NQT; ++n) num[e][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float den[NQT] = {0.f, 0.f};
+  const uint16_t* Ssh = s_split + (size_t)h * 2 * D * D;
 #pragma unroll
   for (int s = 0; s < NKS; ++s) {
     const int i0 = s * 32 + g * 8;
-    const float4 z0 = *reinterpret_cast<const float4*>(zh + i0);
-    const float4 z1 = *reinterpret_cast<const float4*>(zh + i0 + 4);
-    const float zz[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
+    bf16x8 shi[NET], slo[NET];
+#pragma unroll
+    for (int et = 0; et < NET; ++et) {
+      const uint16_t* sp = Ssh + (size_t)(et * 16 + c) * D + i0;
+      shi[et] = as_bf16x8(*reinterpret_cast<const uint4*>(sp));
+      slo[et] = as_bf16x8(*reinterpret_cast<const uint4*>(sp + D * D));
+    }
     bf16x8 fhi[NQT], flo[NQT];
 #pragma unroll
     for (int n = 0; n < NQT; ++n) {
       const uint4 qb = __builtin_bit_cast(uint4, qop[n][s]);
       float f[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        f[e] = phi(bf16_to_f32(half16(qb, e)));
-        den[n] += zz[e] * f[e];
-      }
+      for (int e = 0; e < 8; ++e) f[e] = phi(bf16_to_f32(half16(qb, e))) * inv_den[n];
       split_bf16x8(f, fhi[n], flo[n]);
     }
 #pragma unroll
-    for (int et = 0; et < NET; ++et) {
-      const float* sp = Sh + (size_t)(et * 16 + c) * D + i0;
-      const float4 a0 = *reinterpret_cast<const float4*>(sp);
-      const float4 a1 = *reinterpret_cast<const float4*>(sp + 4);
-      const float sv[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-      bf16x8 shi, slo;
-      split_bf16x8(sv, shi, slo);
+    for (int et = 0; et < NET; ++et)
 #pragma unroll
       for (int n = 0; n < NQT; ++n) {
-        num[et][n] = Mfma<bf16_t>::mma(shi, fhi[n], num[et][n]);
-        num[et][n] = Mfma<bf16_t>::mma(slo, fhi[n], num[et][n]);
-        num[et][n] = Mfma<bf16_t>::mma(shi, flo[n], num[et][n]);
+        acc[et][n] = Mfma<bf16_t>::mma(shi[et], fhi[n], acc[et][n]);
+        acc[et][n] = Mfma<bf16_t>::mma(slo[et], fhi[n], acc[et][n]);
+        acc[et][n] = Mfma<bf16_t>::mma(shi[et], flo[n], acc[et][n]);
       }
-    }
   }
+  // Stores straight from the MFMA layout: lane (c, g) holds features 16et + 4g .. +3
+  // of query row 16n + c (8 bytes); a wave's 8 stores per row complete it in L2.
+  bf16_t* oh = out + (size_t)h * out_hs;
+  const bool full = qrow0 + 32 <= n_q;  // wave-uniform
 #pragma unroll
   for (int n = 0; n < NQT; ++n) {
-    float dn = den[n];
-    dn += __shfl_xor(dn, 16);
-    dn += __shfl_xor(dn, 32);
-    const float inv_den = 1.f / (dn + eps);
-    const int row = n * 16 + c;
+    const int64_t r = qrow0 + n * 16 + c;
+    if (full || r < n_q) {
 #pragma unroll
-    for (int et = 0; et < NET; ++et) {
-      float4& o = ob[row * OCPR + ((et * 4 + g) ^ (row % OCPR))];
-      float4 v = o;
-      v.x += num[et][n][0] * inv_den;
-      v.y += num[et][n][1] * inv_den;
-      v.z += num[et][n][2] * inv_den;
-      v.w += num[et][n][3] * inv_den;
-      o = v;
+      for (int et = 0; et < NET; ++et)
+        *reinterpret_cast<uint2*>(oh + r * D + et * 16 + g * 4) =
+            make_uint2(pack_bf16x2(acc[et][n][0], acc[et][n][1]),
+                       pack_bf16x2(acc[et][n][2], acc[et][n][3]));
     }
-  }
-  // Coalesced bf16 stores: lane handles 8 consecutive features of a row per step.
-  bf16_t* oh = out + (size_t)h * out_hs;
-  constexpr int C8 = D / 8;
-#pragma unroll
-  for (int u = 0; u < 32 * C8 / 64; ++u) {
-    const int idx = u * 64 + lane;
-    const int row = idx / C8, c8 = idx % C8;
-    const int64_t r = qrow0 + row;
-    const float4 a = ob[row * OCPR + ((2 * c8) ^ (row % OCPR))];
-    const float4 b = ob[row * OCPR + ((2 * c8 + 1) ^ (row % OCPR))];
-    const uint4 pk = make_uint4(f32_to_bf16_bits(a.x) | (f32_to_bf16_bits(a.y) << 16),
-                                f32_to_bf16_bits(a.z) | (f32_to_bf16_bits(a.w) << 16),
-                                f32_to_bf16_bits(b.x) | (f32_to_bf16_bits(b.y) << 16),
-                                f32_to_bf16_bits(b.z) | (f32_to_bf16_bits(b.w) << 16));
-    if (r < n_q) *reinterpret_cast<uint4*>(oh + r * D + c8 * 8) = pk;
   }
 }
 
 template <int D>
 hipError_t launch_bf16(const void* q, int64_t n_q, int64_t q_hs, const void* k, const void* v,
                        int64_t n_kv, int64_t kv_hs, const int32_t* sel, int top_k, int heads,
-                       const float* S, const float* z, float eps, float scale, void* out,
-                       int64_t out_hs, hipStream_t stream) {
+                       const uint16_t* s_split, const float* z, float eps, float scale,
+                       void* out, int64_t out_hs, hipStream_t stream) {
   const int nqb = (int)((n_q + 63) / 64);
   const int n_logical = nqb * heads;
   const int n_wg = (n_logical + 7) / 8 * 8;
-  sparse_swa_bf16<D><<<n_wg, 128, 0, stream>>>(
-      static_cast<const bf16_t*>(q), n_q, q_hs, static_cast<const bf16_t*>(k),
-      static_cast<const bf16_t*>(v), n_kv, kv_hs, sel, top_k, nqb, n_logical, S, z, eps, scale,
-      static_cast<bf16_t*>(out), out_hs);
+#define HF_SWA_BF16(SHORT)                                                                   \
+  sparse_swa_bf16<D, SHORT><<<n_wg, 128, 0, stream>>>(                                       \
+      static_cast<const bf16_t*>(q), n_q, q_hs, static_cast<const bf16_t*>(k),                \
+      static_cast<const bf16_t*>(v), n_kv, kv_hs, sel, top_k, nqb, n_logical, s_split, z, eps,  \
+      scale,                                                                                  \
+      static_cast<bf16_t*>(out), out_hs)
+  if (n_kv < 64) HF_SWA_BF16(true); else HF_SWA_BF16(false);
+#undef HF_SWA_BF16
   return hipGetLastError();
 }
 
@@ -728,18 +726,18 @@ hipError_t launch(const void* q, int64_t n_q, int64_t q_hs, const void* k, const
 hipError_t launch_sparse_swa(int dtype, int heads, int d, int block, const void* q, int64_t n_q,
                              int64_t q_hs, const void* k, const void* v, int64_t n_kv,
                              int64_t kv_hs, const int32_t* sel, int top_k, const float* S,
-                             const float* z, float eps, float scale, void* out, int64_t out_hs,
-                             hipStream_t stream) {
+                             const uint16_t* s_split, const float* z, float eps, float scale,
+                             void* out, int64_t out_hs, hipStream_t stream) {
 #define HF_SWA(T, D, BLK, QW)                                                                 \
   return launch<T, D, BLK, QW>(q, n_q, q_hs, k, v, n_kv, kv_hs, sel, top_k, heads, S, z, eps, \
                                scale, out, out_hs, stream)
   if (dtype == 0) {
     if (block == 64 && d == 128)
-      return launch_bf16<128>(q, n_q, q_hs, k, v, n_kv, kv_hs, sel, top_k, heads, S, z, eps,
-                              scale, out, out_hs, stream);
+      return launch_bf16<128>(q, n_q, q_hs, k, v, n_kv, kv_hs, sel, top_k, heads, s_split, z,
+                              eps, scale, out, out_hs, stream);
     if (block == 64 && d == 64)
-      return launch_bf16<64>(q, n_q, q_hs, k, v, n_kv, kv_hs, sel, top_k, heads, S, z, eps,
-                             scale, out, out_hs, stream);
+      return launch_bf16<64>(q, n_q, q_hs, k, v, n_kv, kv_hs, sel, top_k, heads, s_split, z,
+                             eps, scale, out, out_hs, stream);
   } else {
     if (block == 16 && d == 64) HF_SWA(float, 64, 16, 16);
     if (block == 16 && d == 128) HF_SWA(float, 128, 16, 16);

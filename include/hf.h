@@ -35,7 +35,10 @@
  * Ownership. The caller allocates and owns all device memory (Q, K, V, out, S, z,
  * sel_out and the workspace) and keeps it alive until the enqueued work is done.
  * The library allocates only the small host-side handle, freed by
- * hf_state_destroy. It never allocates device memory.
+ * hf_state_destroy. It never allocates device memory. For bf16 states the
+ * workspace also holds a derived copy of S (its bf16 hi/lo split) that the
+ * library refreshes whenever it updates S, so after hf_state_init S and z must be
+ * changed only through the library (to load other values, create a new handle).
  *
  * Asynchrony. Calls validate on the host, enqueue on `stream` (a hipStream_t;
  * NULL = the default stream) and return without synchronising. Device faults

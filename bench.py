@@ -2,9 +2,11 @@
 """Benchmark: one step of the per-chunk hybrid attention on one MI355X.
 
 A step is one pass of the whole hot path over one batch of synthetic input: the
-absorb of the evicted tokens into the linear state (hf_absorb_evicted) and the
-hybrid attention of the chunk (hf_attend_chunk: block pooling, block scores and
-top-K selection, block-sparse attention with the fused linear read). The default
+absorb of the evicted tokens into the linear state and the hybrid attention of
+the chunk (block pooling, block scores and top-K selection, block-sparse
+attention with the fused linear read), issued as one hf_absorb_and_attend call
+on one stream (`--side-stream`: its absorb on a second stream next to the block
+selection; `--serial`: hf_absorb_evicted then hf_attend_chunk). The default
 workload is one Wan-1.3B-like layer: 12 heads, d = 128, a 3-frame chunk (4680
 query tokens) over a 9-frame window (14040 key/value tokens), 64-token blocks,
 top-K = 55 of 220 key blocks, 4680 evicted tokens. Inputs are resident in HBM
@@ -51,6 +53,10 @@ def parse():
                    choices=["wan_layer_bf16", "full_depth_bf16"])
     p.add_argument("--seed", type=int, default=1234)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--serial", action="store_true",
+                   help="hf_absorb_evicted then hf_attend_chunk (two calls)")
+    p.add_argument("--side-stream", action="store_true",
+                   help="hf_absorb_and_attend with the absorb on a side stream")
     p.add_argument("--cpu-reps", type=int, default=3)
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="also run device copies of this size (HBM counter calibration)")
@@ -87,9 +93,13 @@ class LayerSet:
                                            max_n_ev=self.n_ev, max_top_k=top_k, device=dev)
         self.inp = inp
 
-    def step(self):
-        self.st.absorb_evicted(self.kev, self.vev)
-        self.st.attend_chunk(self.q, self.kw, self.vw, self.top_k, out=self.out)
+    def step(self, side=None, serial=False):
+        if serial:
+            self.st.absorb_evicted(self.kev, self.vev)
+            self.st.attend_chunk(self.q, self.kw, self.vw, self.top_k, out=self.out)
+        else:  # one call; with a side stream the absorb overlaps the block selection
+            self.st.absorb_and_attend(self.kev, self.vev, self.q, self.kw, self.vw, self.top_k,
+                                      out=self.out, side_stream=side)
 
     def flops(self, torch, sel):
         """Algorithmic FLOPs per kernel for this set's selection (numpy int math)."""
@@ -180,13 +190,14 @@ def main():
         flops.append(s.flops(torch, sel.cpu().numpy()))
 
     per_step_layers = n_sets if args.workload == "full_depth_bf16" else 1
+    side = torch.cuda.Stream() if args.side_stream else None  # default priority
 
     def run(k):
         if args.workload == "full_depth_bf16":
             for s in sets:
-                s.step()
+                s.step(side, args.serial)
         else:
-            sets[k % n_sets].step()
+            sets[k % n_sets].step(side, args.serial)
 
     def step_flops(k):
         idx = range(n_sets) if args.workload == "full_depth_bf16" else [k % n_sets]
@@ -237,7 +248,7 @@ def main():
         torch.cuda.synchronize()
         ev0.record()
         for k in range(args.steps):
-            sets[0].step()
+            sets[0].step(side, args.serial)
         ev1.record()
         torch.cuda.synchronize()
         ms_warm = ev0.elapsed_time(ev1) / args.steps
@@ -305,6 +316,9 @@ def main():
                          f"{-(-s0.n_kv // 64)}, {s0.n_ev} evicted tokens absorbed per step"),
             "heads": s0.H, "head_dim": s0.d, "n_q": s0.n_q, "n_kv": s0.n_kv, "n_ev": s0.n_ev,
             "block": 64, "top_k": top_k, "input_sets": n_sets, "layers_per_step": per_step_layers,
+            "issue": ("hf_absorb_evicted, then hf_attend_chunk" if args.serial else
+                      "hf_absorb_and_attend, absorb on a side stream" if args.side_stream else
+                      "hf_absorb_and_attend, one stream"),
         },
         "pct_of_mfma_peak": round(100 * value / peak, 3),
         "ms_per_step_with_kernel_events": round(ms_step_ev, 5),

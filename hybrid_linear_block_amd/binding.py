@@ -57,6 +57,8 @@ def _load():
         "hf_absorb_evicted": (c_int, [P, P, P, c_int64, c_int64, c_int64, P]),
         "hf_attend_chunk": (c_int, [P, P, c_int64, c_int64, P, P, c_int64, c_int64, c_int32, P,
                                     c_int64, P, P]),
+        "hf_absorb_and_attend": (c_int, [P, P, P, c_int64, c_int64, c_int64, P, c_int64, c_int64,
+                                         P, P, c_int64, c_int64, c_int32, P, c_int64, P, P, P]),
         "hf_block_scores": (c_int, [P, P, c_int64, c_int64, P, c_int64, c_int64, P, P]),
         "hf_profile_start": (c_int, [P, c_int32]),
         "hf_profile_stop": (c_int, [P, POINTER(ctypes.c_double), POINTER(c_int32)]),
@@ -74,7 +76,7 @@ def _load():
 _lib = _load()
 
 EXPORTED = ("hf_workspace_bytes", "hf_state_init", "hf_absorb_evicted", "hf_attend_chunk",
-            "hf_block_scores", "hf_profile_start", "hf_profile_stop", "hf_next_ev_index",
+            "hf_absorb_and_attend", "hf_block_scores", "hf_profile_start", "hf_profile_stop", "hf_next_ev_index",
             "hf_state_destroy", "hf_status_string")
 HF_KERNEL_NAMES = ("absorb", "block_pool", "score_select", "sparse_swa")
 
@@ -114,6 +116,15 @@ def hf_attend_chunk(state: int, q: int, n_q: int, q_head_stride: int, k_win: int
                     sel_out: int, stream: int) -> int:
     return _lib.hf_attend_chunk(state, q, n_q, q_head_stride, k_win, v_win, n_kv,
                                 kv_head_stride, top_k, out, out_head_stride, sel_out, stream)
+
+
+def hf_absorb_and_attend(state: int, k_ev: int, v_ev: int, n_ev: int, ev_head_stride: int,
+                         ev_index: int, q: int, n_q: int, q_head_stride: int, k_win: int,
+                         v_win: int, n_kv: int, kv_head_stride: int, top_k: int, out: int,
+                         out_head_stride: int, sel_out: int, stream: int, side_stream: int) -> int:
+    return _lib.hf_absorb_and_attend(state, k_ev, v_ev, n_ev, ev_head_stride, ev_index, q, n_q,
+                                     q_head_stride, k_win, v_win, n_kv, kv_head_stride, top_k,
+                                     out, out_head_stride, sel_out, stream, side_stream)
 
 
 def hf_block_scores(state: int, q: int, n_q: int, q_head_stride: int, k_win: int, n_kv: int,

@@ -27,6 +27,7 @@ struct hf_state {
   int32_t* sel;
   float* partials;
   uint16_t* s_split;  // bf16 hi/lo split of S (bf16 states), kept in step with S
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;  // hf_absorb_and_attend's fork / join
   // Per-kernel timing (hf_profile_start / hf_profile_stop).
   bool prof_on = false;
   int prof_cap = 0;
@@ -110,6 +111,12 @@ void prof_release(hf_state* st) {
   st->prof_cap = 0;
 }
 
+void release_events(hf_state* st) {
+  if (st->ev_fork) (void)hipEventDestroy(st->ev_fork);
+  if (st->ev_join) (void)hipEventDestroy(st->ev_join);
+  st->ev_fork = st->ev_join = nullptr;
+}
+
 // Launch `fn` (one kernel) on stream s, bracketed by profiling events if enabled.
 template <typename F>
 hipError_t timed(hf_state* st, int kernel, hipStream_t s, F fn) {
@@ -189,33 +196,50 @@ hf_status hf_state_init(const hf_config* cfg, float* S, float* z, void* workspac
                     : hf::launch_split_state((int)H, (int)d, S, st->s_split, s);
     return e;
   });
-  if (r != HF_OK) {
+  const hf_status re = r != HF_OK ? r : on_device(st->device, [&]() -> hipError_t {
+    hipError_t e = hipEventCreateWithFlags(&st->ev_fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&st->ev_join, hipEventDisableTiming);
+    return e;
+  });
+  if (re != HF_OK) {
+    release_events(st);
     delete st;
-    return r;
+    return re;
   }
   *out = st;
   return HF_OK;
 }
 
-hf_status hf_absorb_evicted(hf_state* st, const void* k_ev, const void* v_ev, int64_t n_ev,
-                            int64_t ev_head_stride, int64_t ev_index, void* stream) {
-  if (!st || n_ev < 0) return HF_ERR_INVALID_ARG;
+static hf_status check_absorb(const hf_state* st, const void* k_ev, const void* v_ev, int64_t n_ev,
+                              int64_t ev_head_stride, int64_t ev_index) {
   const hf_config& c = st->cfg;
-  if (n_ev > c.max_n_ev) return HF_ERR_INVALID_ARG;
+  if (n_ev < 0 || n_ev > c.max_n_ev) return HF_ERR_INVALID_ARG;
   if (n_ev > 0) {
     hf_status e = check_tensor(k_ev, n_ev, ev_head_stride, c);
     if (e == HF_OK) e = check_tensor(v_ev, n_ev, ev_head_stride, c);
     if (e != HF_OK) return e;
   }
-  if (ev_index != st->next_ev) return HF_ERR_STATE;
-  if (n_ev == 0) return HF_OK;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const hf_status r = on_device(st->device, [&]() {
-    return timed(st, HF_KERNEL_ABSORB, s, [&]() {
-      return hf::launch_absorb(c.dtype, c.num_heads, c.head_dim, k_ev, v_ev, n_ev,
-                               ev_head_stride, st->S, st->z, st->partials, st->s_split, s);
-    });
+  return ev_index != st->next_ev ? HF_ERR_STATE : HF_OK;
+}
+
+// The absorb kernels on stream s (n_ev > 0); the caller has validated everything.
+static hipError_t enqueue_absorb(hf_state* st, const void* k_ev, const void* v_ev, int64_t n_ev,
+                                 int64_t ev_head_stride, hipStream_t s) {
+  const hf_config& c = st->cfg;
+  return timed(st, HF_KERNEL_ABSORB, s, [&]() {
+    return hf::launch_absorb(c.dtype, c.num_heads, c.head_dim, k_ev, v_ev, n_ev, ev_head_stride,
+                             st->S, st->z, st->partials, st->s_split, s);
   });
+}
+
+hf_status hf_absorb_evicted(hf_state* st, const void* k_ev, const void* v_ev, int64_t n_ev,
+                            int64_t ev_head_stride, int64_t ev_index, void* stream) {
+  if (!st) return HF_ERR_INVALID_ARG;
+  const hf_status e = check_absorb(st, k_ev, v_ev, n_ev, ev_head_stride, ev_index);
+  if (e != HF_OK || n_ev == 0) return e;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hf_status r =
+      on_device(st->device, [&]() { return enqueue_absorb(st, k_ev, v_ev, n_ev, ev_head_stride, s); });
   if (r == HF_OK) st->next_ev += n_ev;
   return r;
 }
@@ -230,44 +254,107 @@ static hf_status check_attend(const hf_state* st, const void* q, int64_t n_q, in
   return e;
 }
 
+static hf_status check_attend_all(const hf_state* st, const void* q, int64_t n_q, int64_t q_hs,
+                                  const void* k_win, const void* v_win, int64_t n_kv,
+                                  int64_t kv_hs, int32_t top_k, const void* out, int64_t out_hs,
+                                  const int32_t* sel_out) {
+  const hf_config& c = st->cfg;
+  hf_status e = check_attend(st, q, n_q, q_hs, k_win, n_kv, kv_hs);
+  if (e == HF_OK) e = check_tensor(v_win, n_kv, kv_hs, c);
+  if (e == HF_OK && n_q > 0) e = check_tensor(out, n_q, out_hs, c);
+  if (e != HF_OK) return e;
+  const int64_t nkb = ceil_div(n_kv, c.block_size);
+  if (top_k < 1 || top_k > nkb || top_k > c.max_top_k) return HF_ERR_INVALID_ARG;
+  if (sel_out && (reinterpret_cast<uintptr_t>(sel_out) & 3u)) return HF_ERR_INVALID_ARG;
+  return HF_OK;
+}
+
+// The attention kernels on stream s (n_q > 0); if join is not null, the sparse
+// kernel (the only one that reads S and z) waits for it first.
+static hipError_t enqueue_attend(hf_state* st, const void* q, int64_t n_q, int64_t q_hs,
+                                 const void* k_win, const void* v_win, int64_t n_kv,
+                                 int64_t kv_hs, int32_t top_k, void* out, int64_t out_hs,
+                                 int32_t* sel_out, hipStream_t s, hipEvent_t join) {
+  const hf_config& c = st->cfg;
+  const int nqb = (int)ceil_div(n_q, c.block_size);
+  const int nkb = (int)ceil_div(n_kv, c.block_size);
+  int32_t* sel = sel_out ? sel_out : st->sel;
+  hipError_t r = timed(st, HF_KERNEL_BLOCK_POOL, s, [&]() {
+    return hf::launch_block_pool(c.dtype, c.num_heads, c.head_dim, c.block_size, q, n_q, q_hs,
+                                 k_win, n_kv, kv_hs, st->pooled_q, st->pooled_k, st->nqb_cap,
+                                 st->nkb_cap, s);
+  });
+  if (r == hipSuccess)
+    r = timed(st, HF_KERNEL_SCORE_SELECT, s, [&]() {
+      return hf::launch_score_select(c.num_heads, c.head_dim, nqb, nkb, st->nqb_cap, st->nkb_cap,
+                                     st->pooled_q, st->pooled_k, st->scale, top_k, sel, nullptr,
+                                     s);
+    });
+  if (r == hipSuccess && join) r = hipStreamWaitEvent(s, join, 0);
+  if (r == hipSuccess)
+    r = timed(st, HF_KERNEL_SPARSE_SWA, s, [&]() {
+      return hf::launch_sparse_swa(c.dtype, c.num_heads, c.head_dim, c.block_size, q, n_q, q_hs,
+                                   k_win, v_win, n_kv, kv_hs, sel, top_k, st->S, st->s_split,
+                                   st->z, c.eps, st->scale, out, out_hs, s);
+    });
+  return r;
+}
+
 hf_status hf_attend_chunk(hf_state* st, const void* q, int64_t n_q, int64_t q_head_stride,
                           const void* k_win, const void* v_win, int64_t n_kv,
                           int64_t kv_head_stride, int32_t top_k, void* out,
                           int64_t out_head_stride, int32_t* sel_out, void* stream) {
   if (!st) return HF_ERR_INVALID_ARG;
-  const hf_config& c = st->cfg;
-  hf_status e = check_attend(st, q, n_q, q_head_stride, k_win, n_kv, kv_head_stride);
-  if (e == HF_OK) e = check_tensor(v_win, n_kv, kv_head_stride, c);
-  if (e == HF_OK && n_q > 0) e = check_tensor(out, n_q, out_head_stride, c);
-  if (e != HF_OK) return e;
-  const int64_t nkb = ceil_div(n_kv, c.block_size);
-  if (top_k < 1 || top_k > nkb || top_k > c.max_top_k) return HF_ERR_INVALID_ARG;
-  if (sel_out && (reinterpret_cast<uintptr_t>(sel_out) & 3u)) return HF_ERR_INVALID_ARG;
-  if (n_q == 0) return HF_OK;
-  const int nqb = (int)ceil_div(n_q, c.block_size);
-  int32_t* sel = sel_out ? sel_out : st->sel;
+  const hf_status e = check_attend_all(st, q, n_q, q_head_stride, k_win, v_win, n_kv,
+                                       kv_head_stride, top_k, out, out_head_stride, sel_out);
+  if (e != HF_OK || n_q == 0) return e;
   hipStream_t s = static_cast<hipStream_t>(stream);
   return on_device(st->device, [&]() {
-    hipError_t r = timed(st, HF_KERNEL_BLOCK_POOL, s, [&]() {
-      return hf::launch_block_pool(c.dtype, c.num_heads, c.head_dim, c.block_size, q, n_q,
-                                   q_head_stride, k_win, n_kv, kv_head_stride, st->pooled_q,
-                                   st->pooled_k, st->nqb_cap, st->nkb_cap, s);
-    });
-    if (r == hipSuccess)
-      r = timed(st, HF_KERNEL_SCORE_SELECT, s, [&]() {
-        return hf::launch_score_select(c.num_heads, c.head_dim, nqb, (int)nkb, st->nqb_cap,
-                                       st->nkb_cap, st->pooled_q, st->pooled_k, st->scale, top_k,
-                                       sel, nullptr, s);
-      });
-    if (r == hipSuccess)
-      r = timed(st, HF_KERNEL_SPARSE_SWA, s, [&]() {
-        return hf::launch_sparse_swa(c.dtype, c.num_heads, c.head_dim, c.block_size, q, n_q,
-                                     q_head_stride, k_win, v_win, n_kv, kv_head_stride, sel,
-                                     top_k, st->S, st->s_split, st->z, c.eps, st->scale, out,
-                                     out_head_stride, s);
-      });
-    return r;
+    return enqueue_attend(st, q, n_q, q_head_stride, k_win, v_win, n_kv, kv_head_stride, top_k,
+                          out, out_head_stride, sel_out, s, nullptr);
   });
+}
+
+hf_status hf_absorb_and_attend(hf_state* st, const void* k_ev, const void* v_ev, int64_t n_ev,
+                               int64_t ev_head_stride, int64_t ev_index, const void* q,
+                               int64_t n_q, int64_t q_head_stride, const void* k_win,
+                               const void* v_win, int64_t n_kv, int64_t kv_head_stride,
+                               int32_t top_k, void* out, int64_t out_head_stride,
+                               int32_t* sel_out, void* stream, void* side_stream) {
+  if (!st) return HF_ERR_INVALID_ARG;
+  hf_status e = check_absorb(st, k_ev, v_ev, n_ev, ev_head_stride, ev_index);
+  if (e == HF_OK)
+    e = check_attend_all(st, q, n_q, q_head_stride, k_win, v_win, n_kv, kv_head_stride, top_k,
+                         out, out_head_stride, sel_out);
+  if (e != HF_OK) return e;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipStream_t side = static_cast<hipStream_t>(side_stream);
+  const bool fork = n_ev > 0 && n_q > 0 && side != nullptr && side != s;
+  bool absorbed = false;
+  const hf_status r = on_device(st->device, [&]() -> hipError_t {
+    hipError_t err = hipSuccess;
+    if (fork) {
+      err = hipEventRecord(st->ev_fork, s);
+      if (err == hipSuccess) err = hipStreamWaitEvent(side, st->ev_fork, 0);
+      if (err == hipSuccess) err = enqueue_absorb(st, k_ev, v_ev, n_ev, ev_head_stride, side);
+      absorbed = err == hipSuccess;
+      if (err == hipSuccess) err = hipEventRecord(st->ev_join, side);
+      if (err == hipSuccess)
+        err = enqueue_attend(st, q, n_q, q_head_stride, k_win, v_win, n_kv, kv_head_stride,
+                             top_k, out, out_head_stride, sel_out, s, st->ev_join);
+      return err;
+    }
+    if (n_ev > 0) {
+      err = enqueue_absorb(st, k_ev, v_ev, n_ev, ev_head_stride, s);
+      absorbed = err == hipSuccess;
+    }
+    if (err == hipSuccess && n_q > 0)
+      err = enqueue_attend(st, q, n_q, q_head_stride, k_win, v_win, n_kv, kv_head_stride, top_k,
+                           out, out_head_stride, sel_out, s, nullptr);
+    return err;
+  });
+  if (absorbed) st->next_ev += n_ev;  // the absorb is enqueued and will run
+  return r;
 }
 
 hf_status hf_block_scores(hf_state* st, const void* q, int64_t n_q, int64_t q_head_stride,
@@ -349,6 +436,11 @@ int64_t hf_next_ev_index(const hf_state* st) { return st ? st->next_ev : -1; }
 void hf_state_destroy(hf_state* st) {
   if (!st) return;
   prof_release(st);
+  int cur = -1;
+  const bool switched = hipGetDevice(&cur) == hipSuccess && cur != st->device &&
+                        hipSetDevice(st->device) == hipSuccess;
+  release_events(st);
+  if (switched) (void)hipSetDevice(cur);
   delete st;
 }
 

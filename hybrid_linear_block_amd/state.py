@@ -93,18 +93,19 @@ class HybridAttentionState:
     def absorb_evicted(self, k_ev: torch.Tensor, v_ev: torch.Tensor,
                        ev_index: Optional[int] = None) -> None:
         """S += V^T phi(K), z += sum phi(K) over the evicted tokens (enqueued)."""
-        n, hs = self._check_input(k_ev, "k_ev")
-        n2, hs2 = self._check_input(v_ev, "v_ev")
-        if n2 != n or hs2 != hs:
-            raise ValueError("k_ev and v_ev must have the same length and head stride")
+        n, hs = self._evicted_args(k_ev, v_ev)
         idx = self.next_ev_index if ev_index is None else ev_index
         _check(B.hf_absorb_evicted(self.handle, k_ev.data_ptr(), v_ev.data_ptr(), n, hs, idx,
                                    _stream(self.device)), "hf_absorb_evicted")
 
-    def attend_chunk(self, q: torch.Tensor, k_win: torch.Tensor, v_win: torch.Tensor,
-                     top_k: int, out: Optional[torch.Tensor] = None,
-                     sel_out: Optional[torch.Tensor] = None) -> torch.Tensor:
-        """Hybrid attention of the chunk q over the window (and the state); enqueued."""
+    def _evicted_args(self, k_ev: torch.Tensor, v_ev: torch.Tensor):
+        n, hs = self._check_input(k_ev, "k_ev")
+        n2, hs2 = self._check_input(v_ev, "v_ev")
+        if n2 != n or hs2 != hs:
+            raise ValueError("k_ev and v_ev must have the same length and head stride")
+        return n, hs
+
+    def _attend_args(self, q, k_win, v_win, top_k, out, sel_out):
         n_q, q_hs = self._check_input(q, "q")
         n_kv, kv_hs = self._check_input(k_win, "k_win")
         n_kv2, kv_hs2 = self._check_input(v_win, "v_win")
@@ -124,9 +125,32 @@ class HybridAttentionState:
                     or not sel_out.is_contiguous()):
                 raise ValueError(f"sel_out must be contiguous int32 [H][{nqb}][{top_k}]")
             sel_ptr = sel_out.data_ptr()
-        _check(B.hf_attend_chunk(self.handle, q.data_ptr(), n_q, q_hs, k_win.data_ptr(),
-                                 v_win.data_ptr(), n_kv, kv_hs, int(top_k), out.data_ptr(), o_hs,
-                                 sel_ptr, _stream(self.device)), "hf_attend_chunk")
+        return out, (q.data_ptr(), n_q, q_hs, k_win.data_ptr(), v_win.data_ptr(), n_kv, kv_hs,
+                     int(top_k), out.data_ptr(), o_hs, sel_ptr)
+
+    def attend_chunk(self, q: torch.Tensor, k_win: torch.Tensor, v_win: torch.Tensor,
+                     top_k: int, out: Optional[torch.Tensor] = None,
+                     sel_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """Hybrid attention of the chunk q over the window (and the state); enqueued."""
+        out, args = self._attend_args(q, k_win, v_win, top_k, out, sel_out)
+        _check(B.hf_attend_chunk(self.handle, *args, _stream(self.device)), "hf_attend_chunk")
+        return out
+
+    def absorb_and_attend(self, k_ev: torch.Tensor, v_ev: torch.Tensor, q: torch.Tensor,
+                          k_win: torch.Tensor, v_win: torch.Tensor, top_k: int,
+                          out: Optional[torch.Tensor] = None,
+                          sel_out: Optional[torch.Tensor] = None,
+                          ev_index: Optional[int] = None,
+                          side_stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+        """absorb_evicted then attend_chunk in one call (same results); with a side
+        stream the absorb overlaps the block scoring and selection."""
+        n_ev, ev_hs = self._evicted_args(k_ev, v_ev)
+        out, args = self._attend_args(q, k_win, v_win, top_k, out, sel_out)
+        idx = self.next_ev_index if ev_index is None else ev_index
+        side = side_stream.cuda_stream if side_stream is not None else 0
+        _check(B.hf_absorb_and_attend(self.handle, k_ev.data_ptr(), v_ev.data_ptr(), n_ev, ev_hs,
+                                      idx, *args, _stream(self.device), side),
+               "hf_absorb_and_attend")
         return out
 
     def block_scores(self, q: torch.Tensor, k_win: torch.Tensor) -> torch.Tensor:

@@ -34,8 +34,8 @@
  *
  * Ownership. The caller allocates and owns all device memory (Q, K, V, out, S, z,
  * sel_out and the workspace) and keeps it alive until the enqueued work is done.
- * The library allocates only the small host-side handle, freed by
- * hf_state_destroy. It never allocates device memory. For bf16 states the
+ * The library allocates only the small host-side handle (and two HIP events),
+ * freed by hf_state_destroy. It never allocates device memory. For bf16 states the
  * workspace also holds a derived copy of S (its bf16 hi/lo split) that the
  * library refreshes whenever it updates S, so after hf_state_init S and z must be
  * changed only through the library (to load other values, create a new handle).
@@ -131,6 +131,22 @@ hf_status hf_attend_chunk(hf_state* st, const void* q, int64_t n_q, int64_t q_he
                           const void* k_win, const void* v_win, int64_t n_kv,
                           int64_t kv_head_stride, int32_t top_k, void* out,
                           int64_t out_head_stride, int32_t* sel_out, void* stream);
+
+/* hf_absorb_evicted followed by hf_attend_chunk in one call, with the same
+ * results bit for bit. Of the chunk's attention only the sparse attention kernel
+ * reads S and z, so when side_stream is not NULL and differs from stream, the
+ * absorb runs on side_stream, overlapping the block scoring and selection: it
+ * starts after the work already enqueued on stream, and the sparse attention
+ * kernel waits for it (two events of the handle). side_stream belongs to the
+ * caller and must not carry other work of this handle meanwhile. Either part may
+ * be empty (n_ev == 0, n_q == 0). Both parts are validated before anything is
+ * enqueued; the eviction index advances once the absorb is enqueued. */
+hf_status hf_absorb_and_attend(hf_state* st, const void* k_ev, const void* v_ev, int64_t n_ev,
+                               int64_t ev_head_stride, int64_t ev_index, const void* q,
+                               int64_t n_q, int64_t q_head_stride, const void* k_win,
+                               const void* v_win, int64_t n_kv, int64_t kv_head_stride,
+                               int32_t top_k, void* out, int64_t out_head_stride,
+                               int32_t* sel_out, void* stream, void* side_stream);
 
 /* The pooled block importance scores alone ([EN] 2.A.2), the first stage of
  * hf_attend_chunk: scores_out is fp32 [H][ceil(n_q/B)][ceil(n_kv/B)], dense. The

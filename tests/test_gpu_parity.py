@@ -225,6 +225,52 @@ def test_resume_from_saved_state_bitwise():
     assert torch.equal(oa.view(torch.int16), ob.view(torch.int16))
 
 
+def test_absorb_and_attend_matches_separate_calls_bitwise():
+    """The combined call (on one stream, and with the absorb forked onto a side
+    stream) gives bit for bit the state and outputs of absorb_evicted followed by
+    attend_chunk, over consecutive stream steps (window bookkeeping as in the
+    oracle's stream order)."""
+    H, d, T, c, W, K = 4, 128, 320, 3, 9, 12
+    std = 1.0 / np.sqrt(d)
+    nf = c * 6 + c
+    kd, _ = _draw(41, 21, H, nf * T, d, std, "bf16")
+    vd, _ = _draw(41, 22, H, nf * T, d, std, "bf16")
+    qd, _ = _draw(41, 23, H, nf * T, d, std, "bf16")
+    mk = dict(max_n_q=c * T, max_n_kv=W * T, max_n_ev=c * T, max_top_k=K)
+    ref, one, two = (hla.HybridAttentionState(H, d, 64, torch.bfloat16, **mk) for _ in range(3))
+    side = torch.cuda.Stream()
+    for t in range(6):
+        (e0, e1), (w0, w1) = oracle.stream_step_frames(t, c, W)
+        kev, vev = kd[:, e0 * T:e1 * T], vd[:, e0 * T:e1 * T]
+        q = qd[:, c * t * T:(c * t + c) * T]
+        kw, vw = kd[:, w0 * T:w1 * T], vd[:, w0 * T:w1 * T]
+        nkb = -(-(w1 - w0) * T // 64)
+        k_t = min(K, nkb)
+        sels = [torch.empty((H, -(-c * T // 64), k_t), dtype=torch.int32, device="cuda")
+                for _ in range(3)]
+        ref.absorb_evicted(kev, vev)
+        o_ref = ref.attend_chunk(q, kw, vw, k_t, sel_out=sels[0])
+        o_one = one.absorb_and_attend(kev, vev, q, kw, vw, k_t, sel_out=sels[1])
+        o_two = two.absorb_and_attend(kev, vev, q, kw, vw, k_t, sel_out=sels[2], side_stream=side)
+        torch.cuda.synchronize()
+        print(f"step {t}: evicted frames [{e0}, {e1}), window [{w0}, {w1}), K={k_t}", flush=True)
+        for st, o, sel in ((one, o_one, sels[1]), (two, o_two, sels[2])):
+            assert torch.equal(st.S, ref.S) and torch.equal(st.z, ref.z)
+            assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16))
+            assert torch.equal(sel, sels[0])
+            assert st.next_ev_index == ref.next_ev_index
+    # validation covers both parts: nothing is enqueued on an error of either
+    S0 = two.S.clone()
+    with pytest.raises(hla.HfError) as ei:
+        two.absorb_and_attend(kev, vev, q, kw, vw, k_t, ev_index=0, side_stream=side)
+    assert ei.value.status == hla.HF_ERR_STATE
+    with pytest.raises(hla.HfError) as ei:
+        two.absorb_and_attend(kev, vev, q, kw, vw, 10 ** 6, side_stream=side)
+    assert ei.value.status == hla.HF_ERR_INVALID_ARG
+    torch.cuda.synchronize()
+    assert torch.equal(two.S, S0) and two.next_ev_index == ref.next_ev_index
+
+
 def test_eviction_sequence_errors_leave_state_unchanged():
     H, d, T = 2, 128, 128
     st = hla.HybridAttentionState(H, d, 64, torch.bfloat16, max_n_q=T, max_n_kv=T, max_n_ev=T,

@@ -506,12 +506,17 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void s
   for (int e = 0; e < NET; ++e)
 #pragma unroll
     for (int n = 0; n < NQT; ++n) acc[e][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run[NQT], l_run[NQT];
+  // Row sums of the weights on the MFMA (P times a ones operand; every row of the
+  // result holds the sum of the query's column), so the sums are those of exactly
+  // the bf16 weights that go into O.
+  f32x4 acc_l[NQT];
+  float m_run[NQT];  // reference max of each query (log2 units), set by the first block
 #pragma unroll
   for (int n = 0; n < NQT; ++n) {
-    m_run[n] = -INFINITY;
-    l_run[n] = 0.f;
+    m_run[n] = 0.f;
+    acc_l[n] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  const bf16x8 ones = as_bf16x8(make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
   const float sl2 = scale * kLog2e;
   const int jr = (lane & 15) >> 2, pp = lane & 3;  // transposing-read source role
 
@@ -557,46 +562,63 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void s
           for (int n = 0; n < NQT; ++n) st[mt][n][r] = out ? -INFINITY : st[mt][n][r];
         }
     }
-    float m_blk[NQT];
+    // Exponent of every weight relative to the query's reference max, t = s tau log2 e
+    // - m (the FMA output needs no canonicalisation for the max below). The
+    // reference moves only when some key of the block exceeds it by more than the
+    // slack: each lane checks its own 16 keys of the query, and only if any lane of
+    // the wave sees that (rare after the first block) is the block max formed
+    // across the lane groups, t shifted and the output rescaled.
+    if (t == 0) {  // the reference starts at the first block's max (finite: every
+                   // block has a key in the window)
+#pragma unroll
+      for (int n = 0; n < NQT; ++n) {
+        float m4[NMT];
+#pragma unroll
+        for (int mt = 0; mt < NMT; ++mt)
+          m4[mt] = fmaxf(fmaxf(st[mt][n][0], st[mt][n][1]), fmaxf(st[mt][n][2], st[mt][n][3]));
+        m_run[n] = max_over_groups(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]))) * sl2;
+      }
+    }
+    f32x4 tx[NMT][NQT];
+    float mx[NQT];
     bool move_any = false;
 #pragma unroll
     for (int n = 0; n < NQT; ++n) {
-      float mx = st[0][n][0];
+      float m4[NMT];
 #pragma unroll
-      for (int mt = 0; mt < NMT; ++mt)
+      for (int mt = 0; mt < NMT; ++mt) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, st[mt][n][r]);
-      m_blk[n] = max_over_groups(mx) * sl2;
-      move_any |= m_blk[n] > m_run[n] + kLazyMaxSlack;
+        for (int r = 0; r < 4; ++r) tx[mt][n][r] = __builtin_fmaf(st[mt][n][r], sl2, -m_run[n]);
+        m4[mt] = fmaxf(fmaxf(tx[mt][n][0], tx[mt][n][1]), fmaxf(tx[mt][n][2], tx[mt][n][3]));
+      }
+      mx[n] = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+      move_any |= mx[n] > kLazyMaxSlack;
     }
-    if (__builtin_amdgcn_ballot_w64(move_any)) {  // wave-uniform, rare after block 0
+    if (__builtin_amdgcn_ballot_w64(move_any)) {  // wave-uniform
 #pragma unroll
       for (int n = 0; n < NQT; ++n) {
-        const float m_new = m_blk[n] > m_run[n] + kLazyMaxSlack ? m_blk[n] : m_run[n];
-        const float alpha = __builtin_amdgcn_exp2f(m_run[n] - m_new);
-        m_run[n] = m_new;
-        l_run[n] *= alpha;
+        const float d_blk = max_over_groups(mx[n]);  // block max - reference
+        const float shift = d_blk > kLazyMaxSlack ? d_blk : 0.f;
+        const float alpha = __builtin_amdgcn_exp2f(-shift);
+        m_run[n] += shift;
+        acc_l[n] *= alpha;
 #pragma unroll
         for (int e = 0; e < NET; ++e) acc[e][n] *= alpha;
+#pragma unroll
+        for (int mt = 0; mt < NMT; ++mt) tx[mt][n] -= shift;
       }
     }
     uint32_t pk[NMT][NQT][2];  // bf16 weights, packed in pairs (the B operand of PV)
 #pragma unroll
-    for (int n = 0; n < NQT; ++n) {
-      float rs = 0.f;
+    for (int n = 0; n < NQT; ++n)
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt) {
         float e4[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          e4[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[mt][n][r], sl2, -m_run[n]));
-          rs += e4[r];
-        }
+        for (int r = 0; r < 4; ++r) e4[r] = __builtin_amdgcn_exp2f(tx[mt][n][r]);
         pk[mt][n][0] = pack_bf16x2(e4[0], e4[1]);
         pk[mt][n][1] = pack_bf16x2(e4[2], e4[3]);
       }
-      l_run[n] += sum_over_groups(rs);
-    }
 
     if (more) wait_vmem<LPT>(); else wait_vmem<0>();  // V(t) has landed
     lds_barrier();
@@ -607,9 +629,11 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void s
     for (int c2 = 0; c2 < BLK / 32; ++c2) {
       bf16x8 pop[NQT];
 #pragma unroll
-      for (int n = 0; n < NQT; ++n)
+      for (int n = 0; n < NQT; ++n) {
         pop[n] = as_bf16x8(make_uint4(pk[2 * c2][n][0], pk[2 * c2][n][1], pk[2 * c2 + 1][n][0],
                                       pk[2 * c2 + 1][n][1]));
+        acc_l[n] = Mfma<bf16_t>::mma(ones, pop[n], acc_l[n]);
+      }
       // Lane group g takes keys 32c2 + 4g + 0..3 then 32c2 + 16 + 4g + 0..3 (the key
       // order of pop); source lane 4j + p points at V[row j][16et + 4p ..].
       const int r0 = c2 * 32 + 4 * g + jr;
@@ -637,7 +661,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void s
   // issued together.
 #pragma unroll
   for (int n = 0; n < NQT; ++n) {
-    const float inv_l = 1.f / l_run[n];
+    const float inv_l = 1.f / acc_l[n][0];
 #pragma unroll
     for (int et = 0; et < NET; ++et) acc[et][n] *= inv_l;
   }

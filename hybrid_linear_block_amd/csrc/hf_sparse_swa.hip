@@ -39,17 +39,20 @@ template <typename T, int D, int BLK>
 struct SwaSmem;
 
 // bf16: K and V blocks row-major in 16-byte chunks; chunk cc of row r is stored
-// in slot cc ^ swz(r). A K operand read touches one chunk of 16 consecutive rows,
-// a transposing V read an aligned pair of chunks of 16 consecutive rows (8 per
-// half-wave). With 256-byte rows (CPR = 16) every row starts on the same bank, so
-// swz must give 16 rows distinct slots and 8 consecutive rows distinct slot pairs:
-// swz(r) = 2 (r mod 8) + bit 3 of r. With 128-byte rows (CPR = 8) even and odd
-// rows sit on different bank halves, so the same holds per parity class:
-// swz(r) = 2 ((r / 2) mod 4) + bit 3 of r.
+// in slot cc ^ swz(r). Two reads use the tiles: the K operand (ds_read_b128; lane
+// (g, c) reads chunk 4s + g of row c) and the transposing V read
+// (ds_read_b64_tr_b16; 8 rows x one aligned chunk pair per half-wave). gfx950 LDS
+// has 64 four-byte banks; the transposing read serves each half-wave in one pass,
+// so 8 consecutive rows need distinct slot pairs, but ds_read_b128 does not serve
+// the 16 lanes of one lane group together, and a swizzle that only keeps those 16
+// slots distinct (e.g. 2 (r mod 8) + bit 3 of r) still conflicts 2-way. The linear
+// (over GF(2)) swizzles below were chosen so that both reads are conflict-free, as
+// measured with the LDS bank-conflict counter on patterns of exactly these reads.
+// With 128-byte rows (CPR = 8) two rows share the 64 banks, so swz has 3 bits.
 template <int CPR>
 __device__ __forceinline__ int swz(int r) {
-  if constexpr (CPR == 16) return ((r & 7) << 1) | ((r >> 3) & 1);
-  else return (((r >> 1) & 3) << 1) | ((r >> 3) & 1);
+  if constexpr (CPR == 16) return ((r & 1) << 3) ^ (r & 6) ^ (((r >> 3) & 1) * 5);
+  else return (r & 6) ^ (((r >> 3) & 1) * 5);
 }
 template <int D, int BLK>
 struct SwaSmem<bf16_t, D, BLK> {
@@ -433,16 +436,21 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void s
   const int64_t qrow0 = (int64_t)i * BLK + w * 32;
 
   // Load u of this wave fills LDS chunks (u*NW + w)*64 + lane of a tile with global
-  // chunk (row, slot ^ swz(row)) of the block. The per-lane element offsets
-  // inside a block are fixed, so they are computed once; the block base is
-  // wave-uniform. Rows past the window (ragged last block only) repeat the last
-  // row: their scores are masked, so the values only need to be finite.
-  uint32_t loff[LPT];  // byte offsets inside a block
+  // chunk (row, slot ^ swz(row)) of the block: rows RPU u + (w*64 + lane) / CPR. The
+  // swizzle reads row bits 0..3 only, so the lane's offset inside its row group
+  // repeats every 2 loads (RPU = 8) or every load (RPU a multiple of 16); the row
+  // group goes into the wave-uniform base. Rows past the window (ragged last block
+  // only) repeat the last row: their scores are masked, so the values only need to
+  // be finite.
+  constexpr int RPU = NW * 64 / CPR;  // tile rows per load of the workgroup
+  constexpr int NPAT = RPU % 16 == 0 ? 1 : 2;
+  static_assert(RPU % 8 == 0, "offset period");
+  uint32_t lpat[NPAT];  // byte offsets inside the row group
 #pragma unroll
-  for (int u = 0; u < LPT; ++u) {
+  for (int u = 0; u < NPAT; ++u) {
     const int P = (u * NW + w) * 64 + lane;
     const int row = P / CPR, cc = (P % CPR) ^ swz<CPR>(row);
-    loff[u] = (uint32_t)(row * D + cc * 8) * 2u;
+    lpat[u] = (uint32_t)((row - u * RPU) * D + cc * 8) * 2u;
   }
   // The ragged last block of the window is loaded as the window's last BLK rows
   // (all in bounds; its valid keys are then the tile's last rows and the rows
@@ -455,19 +463,36 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void s
   auto issue_tile = [&](const bf16_t* src, int jb, const uint4* tile) {
     const bf16_t* tb = src + (size_t)tile_row0(jb) * D;
     const uint32_t base = __builtin_amdgcn_readfirstlane(lds_offset(tile) + w * 64 * 16);
-    if constexpr (!SHORT) {
 #pragma unroll
-      for (int u = 0; u < LPT; ++u) lds_dma16(tb, loff[u], base + u * NW * 64 * 16);
-    } else {
-      const uint32_t row_bytes = D * 2, last = (uint32_t)n_kv - 1;
-#pragma unroll
-      for (int u = 0; u < LPT; ++u) {
-        const uint32_t row = loff[u] / row_bytes;
-        const uint32_t off = row <= last ? loff[u] : last * row_bytes + loff[u] % row_bytes;
-        lds_dma16(tb, off, base + u * NW * 64 * 16);
+    for (int u = 0; u < LPT; ++u) {
+      const uint32_t off = lpat[u % NPAT];
+      if constexpr (!SHORT) {
+        lds_dma16(tb + u * RPU * D, off, base + u * NW * 64 * 16);
+      } else {  // rows of the group past the window read the last row
+        const uint32_t row_bytes = D * 2, row = u * RPU + off / row_bytes;
+        const uint32_t last = (uint32_t)n_kv - 1;
+        lds_dma16(tb, (row <= last ? row : last) * row_bytes + off % row_bytes,
+                  base + u * NW * 64 * 16);
       }
     }
   };
+
+  // The linear read's S operands are staged through the same two buffers, one k-step
+  // at a time: slice s holds, for each output feature tile et and each part (hi,
+  // lo) of the split S, the 64 lanes' A operands (S[16et + c][32s + 8g .. +8]) as
+  // 1 KB in lane order, so that both waves read them back linearly. A slice is
+  // NET * 2 KB = one tile, LPT loads per lane, to the same LDS offsets as a tile.
+  const uint16_t* Ssh = s_split + (size_t)h * 2 * D * D;
+  const uint32_t soff = (uint32_t)(c * D + g * 8) * 2u;  // lane part of the S address
+  auto issue_s = [&](int ks, const uint4* tile) {
+    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_offset(tile) + w * 64 * 16);
+#pragma unroll
+    for (int u = 0; u < LPT; ++u) {
+      const int pr = u * NW + w, et = pr >> 1, part = pr & 1;  // operand (et, part)
+      lds_dma16(Ssh + (size_t)part * D * D + et * 16 * D + ks * 32, soff, base + u * NW * 64 * 16);
+    }
+  };
+  static_assert(NET * 2 == LPT * NW, "an S slice is one tile");
 
   // Q operands (B of S^T = K Q^T): lane holds Q[16n + c][32s + 8g .. +8].
   bf16x8 qop[NQT][NKS];
@@ -518,15 +543,38 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void s
   }
   const bf16x8 ones = as_bf16x8(make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
   const float sl2 = scale * kLog2e;
-  const int jr = (lane & 15) >> 2, pp = lane & 3;  // transposing-read source role
+  // LDS byte addresses of this lane's operand reads. The swizzle reads row bits 0..3
+  // only, so the key tile (16 rows), the 32-key chunk and the second half of a chunk
+  // (16 rows) are constant offsets from these.
+  //   K operand (k-step s, key tile mt): row 16mt + c, chunk 4s + g.
+  //   V^T operand (feature tile et, chunk c2): source lane 4j + p of group g points at
+  //   features 16et + 4p .. +3 of row 32c2 + 4g + j (and of that row + 16).
+  uint32_t kaddr[NKS], vaddr[NET];
+#pragma unroll
+  for (int s = 0; s < NKS; ++s)
+    kaddr[s] = lds_offset(lds_k) + (uint32_t)(c * CPR + ((s * 4 + g) ^ swz<CPR>(c))) * 16u;
+  {
+    const int rv = 4 * g + ((lane & 15) >> 2), pp = lane & 3;
+#pragma unroll
+    for (int et = 0; et < NET; ++et)
+      vaddr[et] = lds_offset(lds_v) +
+                  (uint32_t)(rv * CPR + ((2 * et + (pp >> 1)) ^ swz<CPR>(rv))) * 16u + (pp & 1) * 8u;
+  }
+  constexpr uint32_t kRow16 = 16 * CPR * 16;  // bytes of 16 tile rows
 
-  issue_tile(kh, my_sel[0], lds_k);
-  issue_tile(vh, my_sel[0], lds_v);
+  int jb = my_sel[0];
+  issue_tile(kh, jb, lds_k);
+  issue_tile(vh, jb, lds_v);
+#pragma clang loop unroll(disable)  // no peeled first step (register pressure)
   for (int t = 0; t < top_k; ++t) {
-    const int jb = my_sel[t];
     const bool more = t + 1 < top_k;
+    const int jb_next = more ? my_sel[t + 1] : 0;
     wait_vmem<LPT>();  // K(t) has landed (V(t) may still be in flight)
     lds_barrier();
+    // The next block index is taken here, where the barrier has already waited for
+    // the scalar load, so no scalar load is pending once the operand reads start
+    // (it would make every wait for them a full wait).
+    asm volatile("" ::"s"(jb_next));
 
     // ---- S^T = K Q^T: st[mt][n][r] = score(key 16mt + 4g + r, query 16n + c) ----
     f32x4 st[NMT][NQT];
@@ -534,19 +582,36 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void s
     for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
       for (int n = 0; n < NQT; ++n) st[mt][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // The operands of k-steps 0 and 1 are read up front, those of step s + 2 while the
+    // products of step s run.
+    bf16x8 kop[NKS][NMT];
+    auto read_k = [&](int s) {
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt) kop[s][mt] = as_bf16x8(lds_ld16(kaddr[s] + mt * kRow16));
+    };
+    read_k(0);
+    if (NKS > 1) read_k(1);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
+      if (s + 2 < NKS) read_k(s + 2);
 #pragma unroll
-      for (int mt = 0; mt < NMT; ++mt) {
-        const int row = mt * 16 + c;
-        const bf16x8 kop = as_bf16x8(lds_k[row * CPR + ((s * 4 + g) ^ swz<CPR>(row))]);
+      for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
         for (int n = 0; n < NQT; ++n)
-          st[mt][n] = Mfma<bf16_t>::mma(kop, qop[n][s], st[mt][n]);
+          st[mt][n] = Mfma<bf16_t>::mma(kop[s][mt], qop[n][s], st[mt][n]);
+      if (s + 2 < NKS) {
+#pragma unroll
+        for (int mt = 0; mt < NMT; ++mt) {  // one read of step s + 2 after every 2 products
+          __builtin_amdgcn_sched_group_barrier(0x008, NQT, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
     lds_barrier();  // every wave is done with K(t)
-    if (more) issue_tile(kh, my_sel[t + 1], lds_k);
+    if (more) issue_tile(kh, jb_next, lds_k);
+    else issue_s(0, lds_k);  // last block: the first S slice takes the K buffer
 
     // ---- online softmax (base 2) with a lazily moved reference max ----
     const int64_t key0 = (int64_t)jb * BLK;
@@ -620,13 +685,24 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void s
         pk[mt][n][1] = pack_bf16x2(e4[2], e4[3]);
       }
 
-    if (more) wait_vmem<LPT>(); else wait_vmem<0>();  // V(t) has landed
+    wait_vmem<LPT>();  // V(t) has landed (K(t+1) or S slice 0 may be in flight)
     lds_barrier();
 
     // ---- O^T += V^T P^T ----
-    const char* vb = reinterpret_cast<const char*>(lds_v);
+    // Lane group g takes keys 32c2 + 4g + 0..3 then 32c2 + 16 + 4g + 0..3 (the key
+    // order of the weights in pop). The V^T operands of the first 32-key chunk are
+    // read up front, those of the second while the first chunk's products run.
+    bf16x8 vop[2][NET];
+    auto read_v = [&](int c2) {
 #pragma unroll
-    for (int c2 = 0; c2 < BLK / 32; ++c2) {
+      for (int et = 0; et < NET; ++et) {
+        const v4i16 lo = lds_tr8(vaddr[et] + 2 * c2 * kRow16);
+        const v4i16 hi = lds_tr8(vaddr[et] + (2 * c2 + 1) * kRow16);
+        vop[c2][et] =
+            __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    };
+    auto mma_v = [&](int c2) {
       bf16x8 pop[NQT];
 #pragma unroll
       for (int n = 0; n < NQT; ++n) {
@@ -634,48 +710,43 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void s
                                       pk[2 * c2 + 1][n][1]));
         acc_l[n] = Mfma<bf16_t>::mma(ones, pop[n], acc_l[n]);
       }
-      // Lane group g takes keys 32c2 + 4g + 0..3 then 32c2 + 16 + 4g + 0..3 (the key
-      // order of pop); source lane 4j + p points at V[row j][16et + 4p ..].
-      const int r0 = c2 * 32 + 4 * g + jr;
 #pragma unroll
-      for (int et = 0; et < NET; ++et) {
-        const int chunk = 2 * et + (pp >> 1);
-        const v4i16 lo = lds_read_tr(vb + (r0 * CPR + (chunk ^ swz<CPR>(r0))) * 16 + (pp & 1) * 8);
-        const v4i16 hi =
-            lds_read_tr(vb + ((r0 + 16) * CPR + (chunk ^ swz<CPR>(r0 + 16))) * 16 + (pp & 1) * 8);
-        const bf16x8 vop =
-            __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      for (int et = 0; et < NET; ++et)
 #pragma unroll
-        for (int n = 0; n < NQT; ++n) acc[et][n] = Mfma<bf16_t>::mma(vop, pop[n], acc[et][n]);
-      }
+        for (int n = 0; n < NQT; ++n)
+          acc[et][n] = Mfma<bf16_t>::mma(vop[c2][et], pop[n], acc[et][n]);
+    };
+    read_v(0);
+    __builtin_amdgcn_sched_barrier(0);
+    read_v(1);
+    mma_v(0);
+#pragma unroll
+    for (int k = 0; k < 2 * NET; ++k) {  // one read of chunk 1 after each product of chunk 0
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    mma_v(1);
     lds_barrier();  // every wave is done with V(t)
-    if (more) issue_tile(vh, my_sel[t + 1], lds_v);
+    if (more) issue_tile(vh, jb_next, lds_v);
+    else if (NKS > 1) issue_s(1, lds_v);
+    jb = jb_next;
   }
 
   // ---- epilogue ----
   // out = O / l + S phi(q) / (z . phi(q) + eps): the accumulators are normalised in
   // place, then the linear read accumulates S (phi(q) / den) into them on MFMA, with
   // S and the scaled phi(q) split into bf16 hi + lo (three products; the split of S
-  // is kept up to date with S by the absorb). The 16 S operand loads of a k-step are
-  // issued together.
+  // is kept up to date with S by the absorb). Slice s of S is in buffer s % 2; slice
+  // s + 2 is loaded into it once both waves have read slice s.
 #pragma unroll
   for (int n = 0; n < NQT; ++n) {
     const float inv_l = 1.f / acc_l[n][0];
 #pragma unroll
     for (int et = 0; et < NET; ++et) acc[et][n] *= inv_l;
   }
-  const uint16_t* Ssh = s_split + (size_t)h * 2 * D * D;
 #pragma unroll
   for (int s = 0; s < NKS; ++s) {
-    const int i0 = s * 32 + g * 8;
-    bf16x8 shi[NET], slo[NET];
-#pragma unroll
-    for (int et = 0; et < NET; ++et) {
-      const uint16_t* sp = Ssh + (size_t)(et * 16 + c) * D + i0;
-      shi[et] = as_bf16x8(*reinterpret_cast<const uint4*>(sp));
-      slo[et] = as_bf16x8(*reinterpret_cast<const uint4*>(sp + D * D));
-    }
     bf16x8 fhi[NQT], flo[NQT];
 #pragma unroll
     for (int n = 0; n < NQT; ++n) {
@@ -684,6 +755,19 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void s
 #pragma unroll
       for (int e = 0; e < 8; ++e) f[e] = phi(bf16_to_f32(half16(qb, e))) * inv_den[n];
       split_bf16x8(f, fhi[n], flo[n]);
+    }
+    if (s + 1 < NKS) wait_vmem<LPT>(); else wait_vmem<0>();  // slice s has landed
+    lds_barrier();
+    const uint32_t sb = lds_offset(s % 2 == 0 ? lds_k : lds_v) + lane * 16u;
+    bf16x8 shi[NET], slo[NET];
+#pragma unroll
+    for (int et = 0; et < NET; ++et) {
+      shi[et] = as_bf16x8(lds_ld16(sb + (2 * et) * 1024u));
+      slo[et] = as_bf16x8(lds_ld16(sb + (2 * et + 1) * 1024u));
+    }
+    if (s + 2 < NKS) {
+      lds_barrier();  // every wave has read slice s
+      issue_s(s + 2, s % 2 == 0 ? lds_k : lds_v);
     }
 #pragma unroll
     for (int et = 0; et < NET; ++et)

@@ -36,6 +36,7 @@ PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # MI355X dense MFMA peaks
 PEAK_HBM_GBS = 8000.0
 SWA_SOURCES = ("hybrid_linear_block_amd/csrc/hf_sparse_swa.hip",
                "hybrid_linear_block_amd/csrc/hf_device.h")
+PEAK_HBM_BPS = 8.0e12  # MI355X HBM3E, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_sparse_swa_wan_layer.json")
 
 
@@ -276,7 +277,9 @@ def main():
         kernels[name] = dict(avg_us=None if us is None else round(us, 2),
                              algo_bytes=int(b), algo_flop=int(f),
                              gbs=None if not us else round(b / (us * 1e-6) / 1e9, 1),
-                             tflops=None if not us else round(f / (us * 1e-6) / 1e12, 2))
+                             tflops=None if not us else round(f / (us * 1e-6) / 1e12, 2),
+                             pct_hbm=None if not us else round(100 * b / (us * 1e-6) / PEAK_HBM_BPS, 1),
+                             pct_mfma=None if not us else round(100 * f / (us * 1e-6) / 1e12 / peak, 1))
 
     if args.calibrate_copy_mib:
         n = args.calibrate_copy_mib * (1 << 20) // 4

@@ -8,7 +8,7 @@
 namespace hf {
 
 // ---- absorb: S += V^T phi(K), z += sum phi(K) ------------------------------------
-constexpr int kAbsorbMaxSplits = 16;
+constexpr int kAbsorbMaxSplits = 24;
 struct AbsorbPlan {
   int tokens_per_split;
   int n_split;

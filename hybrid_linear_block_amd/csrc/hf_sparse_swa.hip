@@ -419,7 +419,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void s
   constexpr int TCH = BLK * CPR;        // chunks per tile
   constexpr int LPT = TCH / (NW * 64);  // global->LDS loads per lane per tile
   // Separate objects, so that the compiler can tell an in-flight load into one
-  // tile from reads of the other; after the loop each holds one wave's output rows.
+  // tile from reads of the other; after the loop they stage the slices of S.
   __shared__ uint4 lds_k[TCH];
   __shared__ uint4 lds_v[TCH];
 

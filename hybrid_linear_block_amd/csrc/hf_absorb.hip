@@ -19,6 +19,7 @@
 // accuracy (V is exact in bf16).
 #include "hf_device.h"
 #include "hf_launch.h"
+#include "hf_reduce.h"
 
 namespace hf {
 
@@ -31,10 +32,6 @@ constexpr int AT = 64;       // state tile edge
 constexpr int TS = 64;       // tokens staged per iteration
 constexpr int NTHR = 256;    // 4 waves, each owns a 32x32 quarter of the tile
 
-// Floats per partial: the head's full state (D x D, value-major) and z (D).
-template <int D>
-constexpr int part_floats() { return D * D + D; }
-
 // fp32: row-major tiles [TS tokens][64 features (+4 pad)] of V and phi.
 constexpr int FPITCH = AT + 4;
 
@@ -44,70 +41,13 @@ struct AbsorbSmemF32 {
   float zred[8][AT];
 };
 
-// Second pass: S[h] += sum_s partial[h][s] (and z), splits added in order. Each
-// thread owns 4 consecutive floats; the loads of all splits are independent.
-constexpr int RED_THREADS = 256;
-// hi = bf16(x), lo = bf16(x - hi) for 4 values, packed little-endian.
-__device__ __forceinline__ void split4(const float4 x, uint2& hi, uint2& lo) {
-  const float v[4] = {x.x, x.y, x.z, x.w};
-  uint32_t h[4], l[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    h[e] = f32_to_bf16_bits(v[e]);
-    l[e] = f32_to_bf16_bits(v[e] - bf16_to_f32(h[e]));
-  }
-  hi = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-  lo = make_uint2(l[0] | (l[1] << 16), l[2] | (l[3] << 16));
-}
-
-template <int D>
-__device__ __forceinline__ void store_split(uint16_t* s_split, int h, int e4, float4 x) {
-  uint2 hi, lo;
-  split4(x, hi, lo);
-  uint16_t* dst = s_split + (size_t)h * 2 * D * D + e4;
-  *reinterpret_cast<uint2*>(dst) = hi;
-  *reinterpret_cast<uint2*>(dst + D * D) = lo;
-}
-
+// Second pass (absorb_reduce_group, shared with the pooling launch).
 template <int D>
 __global__ __launch_bounds__(RED_THREADS) void absorb_reduce(const float* __restrict__ partials,
                                                              int n_split, float* __restrict__ S,
                                                              float* __restrict__ z,
                                                              uint16_t* __restrict__ s_split) {
-  constexpr int P = part_floats<D>();
-  const int e4 = (blockIdx.x * RED_THREADS + threadIdx.x) * 4, h = blockIdx.y;
-  if (e4 >= P) return;
-  const float* p = partials + (size_t)h * n_split * P + e4;
-  // Groups of 4 splits: the loads of a group are issued together, then added in order.
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  int s = 0;
-  for (; s + 4 <= n_split; s += 4) {
-    float4 x[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) x[u] = *reinterpret_cast<const float4*>(p + (size_t)(s + u) * P);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      acc.x += x[u].x;
-      acc.y += x[u].y;
-      acc.z += x[u].z;
-      acc.w += x[u].w;
-    }
-  }
-  for (; s < n_split; ++s) {
-    const float4 x = *reinterpret_cast<const float4*>(p + (size_t)s * P);
-    acc.x += x.x;
-    acc.y += x.y;
-    acc.z += x.z;
-    acc.w += x.w;
-  }
-  float* dst = e4 < D * D ? S + (size_t)h * D * D + e4 : z + (size_t)h * D + (e4 - D * D);
-  float4 o = *reinterpret_cast<float4*>(dst);
-  o.x += acc.x;
-  o.y += acc.y;
-  o.z += acc.z;
-  o.w += acc.w;
-  *reinterpret_cast<float4*>(dst) = o;
-  if (s_split && e4 < D * D) store_split<D>(s_split, h, e4, o);
+  absorb_reduce_group<D>(blockIdx.x, blockIdx.y, partials, n_split, S, z, s_split);
 }
 
 template <int D>
@@ -370,7 +310,7 @@ size_t absorb_partial_floats(int heads, int d) {
 
 hipError_t launch_absorb(int dtype, int heads, int d, const void* k, const void* v, int64_t n_ev,
                          int64_t head_stride, float* S, float* z, float* partials,
-                         uint16_t* s_split, hipStream_t stream) {
+                         uint16_t* s_split, hipStream_t stream, bool reduce) {
   const AbsorbPlan p = absorb_plan(n_ev);
   if (dtype == 0) {
     dim3 grid(p.n_split, heads);
@@ -391,7 +331,7 @@ hipError_t launch_absorb(int dtype, int heads, int d, const void* k, const void*
 #undef HF_ABS
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || !reduce) return e;
 #define HF_RED(D)                                                                   \
   absorb_reduce<D><<<dim3((part_floats<D>() / 4 + RED_THREADS - 1) / RED_THREADS, heads), \
                      RED_THREADS, 0, stream>>>(partials, p.n_split, S, z, s_split)

@@ -16,10 +16,11 @@ struct AbsorbPlan {
 AbsorbPlan absorb_plan(int64_t n_ev);
 size_t absorb_partial_floats(int heads, int d);
 // Two kernels: per-split partial states into `partials`, then an in-order reduction,
-// which also refreshes s_split (if not null) from the new S.
+// which also refreshes s_split (if not null) from the new S. With reduce = false
+// only the first is launched; launch_pool_and_reduce runs the second.
 hipError_t launch_absorb(int dtype, int heads, int d, const void* k, const void* v, int64_t n_ev,
                          int64_t head_stride, float* S, float* z, float* partials,
-                         uint16_t* s_split, hipStream_t stream);
+                         uint16_t* s_split, hipStream_t stream, bool reduce = true);
 // s_split[h] = the bf16 hi and lo parts of S[h] ([H][2][d][d]): x ~= hi + lo, hi =
 // bf16(x), lo = bf16(x - hi), both rounded to nearest even. The bf16 attention
 // epilogue reads S in this form.
@@ -32,6 +33,13 @@ hipError_t launch_block_pool(int dtype, int heads, int d, int block, const void*
                              int64_t q_hs, const void* k, int64_t n_kv, int64_t kv_hs,
                              float* pooled_q, float* pooled_k, int nqb_cap, int nkb_cap,
                              hipStream_t stream);
+// launch_block_pool and, in the same launch, the reduce of an absorb of n_ev tokens
+// whose partial states launch_absorb(..., reduce = false) has written.
+hipError_t launch_pool_and_reduce(int dtype, int heads, int d, int block, const void* q,
+                                  int64_t n_q, int64_t q_hs, const void* k, int64_t n_kv,
+                                  int64_t kv_hs, float* pooled_q, float* pooled_k, int nqb_cap,
+                                  int nkb_cap, const float* partials, int64_t n_ev, float* S,
+                                  float* z, uint16_t* s_split, hipStream_t stream);
 hipError_t launch_score_select(int heads, int d, int nqb, int nkb, int nqb_cap, int nkb_cap,
                                const float* pooled_q, const float* pooled_k, float scale,
                                int top_k, int32_t* sel, float* scores_out, hipStream_t stream);

@@ -17,6 +17,7 @@
 //             in ascending order.
 #include "hf_device.h"
 #include "hf_launch.h"
+#include "hf_reduce.h"
 
 namespace hf {
 
@@ -28,15 +29,15 @@ constexpr int POOL_THREADS = 256;  // 4 waves, one (head, block) per wave
 // cc over rows rg, rg + RPI, ... (all loads independent), then the row groups are
 // added with lane exchanges in a fixed order.
 template <typename T, int D>
-__global__ __launch_bounds__(POOL_THREADS) void block_pool(
-    const T* __restrict__ q, int64_t n_q, int64_t q_hs, const T* __restrict__ k, int64_t n_kv,
-    int64_t kv_hs, int block, int nqb, int nkb, int heads, float* __restrict__ pooled_q,
-    float* __restrict__ pooled_k, int nqb_cap, int nkb_cap) {
+__device__ __forceinline__ void pool_group(
+    int wg, const T* __restrict__ q, int64_t n_q, int64_t q_hs, const T* __restrict__ k,
+    int64_t n_kv, int64_t kv_hs, int block, int nqb, int nkb, int heads,
+    float* __restrict__ pooled_q, float* __restrict__ pooled_k, int nqb_cap, int nkb_cap) {
   constexpr int VEC = 16 / sizeof(T);  // elements per 16-byte chunk
   constexpr int CPR = D / VEC;         // chunks per row
   constexpr int RPI = 64 / CPR;        // rows per wave-wide load
   const int lane = threadIdx.x & 63;
-  const int wid = blockIdx.x * (POOL_THREADS / 64) + (threadIdx.x >> 6);
+  const int wid = wg * (POOL_THREADS / 64) + (threadIdx.x >> 6);
   if (wid >= heads * (nqb + nkb)) return;
   const int h = wid / (nqb + nkb), b = wid % (nqb + nkb);
   const bool is_q = b < nqb;
@@ -78,6 +79,37 @@ __global__ __launch_bounds__(POOL_THREADS) void block_pool(
     for (int e = 0; e < VEC; e += 4)
       *reinterpret_cast<float4*>(dst + cc * VEC + e) =
           make_float4(acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv);
+  }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(POOL_THREADS) void block_pool(
+    const T* __restrict__ q, int64_t n_q, int64_t q_hs, const T* __restrict__ k, int64_t n_kv,
+    int64_t kv_hs, int block, int nqb, int nkb, int heads, float* __restrict__ pooled_q,
+    float* __restrict__ pooled_k, int nqb_cap, int nkb_cap) {
+  pool_group<T, D>(blockIdx.x, q, n_q, q_hs, k, n_kv, kv_hs, block, nqb, nkb, heads, pooled_q,
+                   pooled_k, nqb_cap, nkb_cap);
+}
+
+// The block pooling and the absorb's reduce in one launch: workgroups below
+// n_pool pool, the others reduce (red_groups per head). The two read different
+// buffers and write different buffers, and both are bound by memory, so running
+// them side by side saves the second launch and its ramp.
+static_assert(POOL_THREADS == RED_THREADS, "one workgroup size for both parts");
+template <typename T, int D>
+__global__ __launch_bounds__(POOL_THREADS) void pool_and_reduce(
+    const T* __restrict__ q, int64_t n_q, int64_t q_hs, const T* __restrict__ k, int64_t n_kv,
+    int64_t kv_hs, int block, int nqb, int nkb, int heads, float* __restrict__ pooled_q,
+    float* __restrict__ pooled_k, int nqb_cap, int nkb_cap, int n_pool,
+    const float* __restrict__ partials, int n_split, float* __restrict__ S,
+    float* __restrict__ z, uint16_t* __restrict__ s_split) {
+  if ((int)blockIdx.x < n_pool) {
+    pool_group<T, D>(blockIdx.x, q, n_q, q_hs, k, n_kv, kv_hs, block, nqb, nkb, heads, pooled_q,
+                     pooled_k, nqb_cap, nkb_cap);
+  } else {
+    const int r = blockIdx.x - n_pool;
+    absorb_reduce_group<D>(r % red_groups<D>(), r / red_groups<D>(), partials, n_split, S, z,
+                           s_split);
   }
 }
 
@@ -195,6 +227,28 @@ hipError_t launch_block_pool(int dtype, int heads, int d, int block, const void*
     if (d == 128) HF_POOL(float, 128); else HF_POOL(float, 64);
   }
 #undef HF_POOL
+  return hipGetLastError();
+}
+
+hipError_t launch_pool_and_reduce(int dtype, int heads, int d, int block, const void* q,
+                                  int64_t n_q, int64_t q_hs, const void* k, int64_t n_kv,
+                                  int64_t kv_hs, float* pooled_q, float* pooled_k, int nqb_cap,
+                                  int nkb_cap, const float* partials, int64_t n_ev, float* S,
+                                  float* z, uint16_t* s_split, hipStream_t stream) {
+  const int nqb = (int)((n_q + block - 1) / block);
+  const int nkb = (int)((n_kv + block - 1) / block);
+  const int n_pool = (heads * (nqb + nkb) + POOL_THREADS / 64 - 1) / (POOL_THREADS / 64);
+  const int n_split = absorb_plan(n_ev).n_split;
+#define HF_POOLRED(T, D)                                                                       \
+  pool_and_reduce<T, D><<<n_pool + red_groups<D>() * heads, POOL_THREADS, 0, stream>>>(         \
+      static_cast<const T*>(q), n_q, q_hs, static_cast<const T*>(k), n_kv, kv_hs, block, nqb,   \
+      nkb, heads, pooled_q, pooled_k, nqb_cap, nkb_cap, n_pool, partials, n_split, S, z, s_split)
+  if (dtype == 0) {
+    if (d == 128) HF_POOLRED(bf16_t, 128); else HF_POOLRED(bf16_t, 64);
+  } else {
+    if (d == 128) HF_POOLRED(float, 128); else HF_POOLRED(float, 64);
+  }
+#undef HF_POOLRED
   return hipGetLastError();
 }
 

@@ -225,28 +225,30 @@ def test_resume_from_saved_state_bitwise():
     assert torch.equal(oa.view(torch.int16), ob.view(torch.int16))
 
 
-def test_absorb_and_attend_matches_separate_calls_bitwise():
-    """The combined call (on one stream, and with the absorb forked onto a side
-    stream) gives bit for bit the state and outputs of absorb_evicted followed by
-    attend_chunk, over consecutive stream steps (window bookkeeping as in the
-    oracle's stream order)."""
-    H, d, T, c, W, K = 4, 128, 320, 3, 9, 12
+@pytest.mark.parametrize("dt,d,B", [("bf16", 128, 64), ("bf16", 64, 64), ("f32", 64, 16)])
+def test_absorb_and_attend_matches_separate_calls_bitwise(dt, d, B):
+    """The combined call (on one stream, where the absorb's reduce shares the
+    pooling launch, and with the absorb forked onto a side stream) gives bit for
+    bit the state and outputs of absorb_evicted followed by attend_chunk, over
+    consecutive stream steps (window bookkeeping as in the oracle's stream order)."""
+    H, T, c, W, K = 4, 320, 3, 9, 12
     std = 1.0 / np.sqrt(d)
     nf = c * 6 + c
-    kd, _ = _draw(41, 21, H, nf * T, d, std, "bf16")
-    vd, _ = _draw(41, 22, H, nf * T, d, std, "bf16")
-    qd, _ = _draw(41, 23, H, nf * T, d, std, "bf16")
+    kd, _ = _draw(41, 21, H, nf * T, d, std, dt)
+    vd, _ = _draw(41, 22, H, nf * T, d, std, dt)
+    qd, _ = _draw(41, 23, H, nf * T, d, std, dt)
     mk = dict(max_n_q=c * T, max_n_kv=W * T, max_n_ev=c * T, max_top_k=K)
-    ref, one, two = (hla.HybridAttentionState(H, d, 64, torch.bfloat16, **mk) for _ in range(3))
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    ref, one, two = (hla.HybridAttentionState(H, d, B, tdt, **mk) for _ in range(3))
     side = torch.cuda.Stream()
     for t in range(6):
         (e0, e1), (w0, w1) = oracle.stream_step_frames(t, c, W)
         kev, vev = kd[:, e0 * T:e1 * T], vd[:, e0 * T:e1 * T]
         q = qd[:, c * t * T:(c * t + c) * T]
         kw, vw = kd[:, w0 * T:w1 * T], vd[:, w0 * T:w1 * T]
-        nkb = -(-(w1 - w0) * T // 64)
+        nkb = -(-(w1 - w0) * T // B)
         k_t = min(K, nkb)
-        sels = [torch.empty((H, -(-c * T // 64), k_t), dtype=torch.int32, device="cuda")
+        sels = [torch.empty((H, -(-c * T // B), k_t), dtype=torch.int32, device="cuda")
                 for _ in range(3)]
         ref.absorb_evicted(kev, vev)
         o_ref = ref.attend_chunk(q, kw, vw, k_t, sel_out=sels[0])
@@ -256,7 +258,7 @@ def test_absorb_and_attend_matches_separate_calls_bitwise():
         print(f"step {t}: evicted frames [{e0}, {e1}), window [{w0}, {w1}), K={k_t}", flush=True)
         for st, o, sel in ((one, o_one, sels[1]), (two, o_two, sels[2])):
             assert torch.equal(st.S, ref.S) and torch.equal(st.z, ref.z)
-            assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16))
+            assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16))  # bit patterns
             assert torch.equal(sel, sels[0])
             assert st.next_ev_index == ref.next_ev_index
     # validation covers both parts: nothing is enqueued on an error of either

@@ -115,11 +115,15 @@ class LayerSet:
                     score_select=2 * nqb * nkb * d * H, sparse_swa=swa + lin,
                     sparse_swa_softmax_part=swa)
 
+    def state_bytes(self):
+        """Bytes of the state S (d x d) and normaliser z (d) the absorb writes, per head."""
+        return 2 * (self.d * self.d + self.d) * 4 * self.H
+
     def bytes(self):
         H, n_q, d, B = self.H, self.n_q, self.d, 64
         nqb, nkb = -(-n_q // B), -(-self.n_kv // B)
         return dict(
-            absorb=2 * self.n_ev * d * 2 * H + 2 * (d * d + d) * 4 * H,
+            absorb=2 * self.n_ev * d * 2 * H + self.state_bytes(),
             block_pool=(n_q + self.n_kv) * d * 2 * H + (nqb + nkb) * d * 4 * H,
             score_select=(nqb + nkb) * d * 4 * H + nqb * self.top_k * 4 * H,
             sparse_swa=(n_q + 2 * self.n_kv) * d * 2 * H + n_q * d * 2 * H + (d * d + d) * 4 * H)
@@ -269,10 +273,18 @@ def main():
                     frac=round(achieved / peak, 4), traffic=traffic, kernel="sparse_swa",
                     flop_per_launch=int(swa_flop), avg_launch_us=round(swa_us, 2))
 
+    # On one stream (the default) the absorb's reduce, which writes S and z, runs inside
+    # the pooling launch, so its bytes are counted there.
+    fused = not args.side_stream and not args.serial
+    kbytes = dict(sets[0].bytes())
+    if fused:
+        sz = sets[0].state_bytes()
+        kbytes["absorb"] -= sz
+        kbytes["block_pool"] += sz
     kernels = {}
     for name in ("absorb", "block_pool", "score_select", "sparse_swa"):
         us = kern_us.get(name)
-        b = sets[0].bytes()[name]
+        b = kbytes[name]
         f = statistics.mean(fl[name] for fl in flops)
         kernels[name] = dict(avg_us=None if us is None else round(us, 2),
                              algo_bytes=int(b), algo_flop=int(f),
@@ -280,6 +292,8 @@ def main():
                              tflops=None if not us else round(f / (us * 1e-6) / 1e12, 2),
                              pct_hbm=None if not us else round(100 * b / (us * 1e-6) / PEAK_HBM_BPS, 1),
                              pct_mfma=None if not us else round(100 * f / (us * 1e-6) / 1e12 / peak, 1))
+    if fused:
+        kernels["block_pool"]["includes"] = "absorb reduce (S and z written)"
 
     if args.calibrate_copy_mib:
         n = args.calibrate_copy_mib * (1 << 20) // 4

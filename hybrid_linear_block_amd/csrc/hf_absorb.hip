@@ -17,6 +17,8 @@
 // feature (state row), so each K element is read once and phi(K) is formed once
 // per workgroup; phi is split into bf16 hi + lo so that the bf16 MFMA keeps ~fp32
 // accuracy (V is exact in bf16).
+#include <atomic>
+
 #include "hf_device.h"
 #include "hf_launch.h"
 #include "hf_reduce.h"
@@ -72,7 +74,13 @@ __device__ __forceinline__ int swz(int r) {
   else return ((r >> 1) & 1) | ((r >> 2) & 2);            // rows of 128 B: 2 rows per 256 B
 }
 constexpr int BT = 32;   // tokens per stage
-constexpr int BNST = 6;  // stages in the ring (BNST - 1 in flight ahead of the one in use)
+constexpr int BNST = 4;  // stages in the ring (BNST - 1 in flight ahead of the one in use)
+
+template <int D>
+struct AbsorbStage {  // one ring stage: the K tile, then the V tile
+  uint4 k[BT * D / 8];
+  uint4 v[BT * D / 8];
+};
 
 template <int D>
 __global__ __launch_bounds__(D * 4) void absorb_bf16(const bf16_t* __restrict__ kev,
@@ -86,8 +94,10 @@ __global__ __launch_bounds__(D * 4) void absorb_bf16(const bf16_t* __restrict__ 
   constexpr int TCH = BT * CPR;    // chunks per tile (== NTH: one load per thread)
   constexpr int NJT = D / 16;      // value-feature tiles
   static_assert(TCH == NTH, "one 16-byte load per thread and tile");
-  __shared__ uint4 lds_k[BNST][TCH];
-  __shared__ uint4 lds_v[BNST][TCH];
+  // The whole ring spans less than 64 KB, so a stage's tile base is an immediate
+  // offset of the LDS reads once the stage index is a compile-time constant.
+  static_assert(sizeof(AbsorbStage<D>) * BNST <= 65536, "ring offsets fit the immediate");
+  __shared__ AbsorbStage<D> ring[BNST];
   const int split = blockIdx.x, h = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -102,13 +112,12 @@ __global__ __launch_bounds__(D * 4) void absorb_bf16(const bf16_t* __restrict__ 
   // global chunk slot ^ 2 swz(row) of that row.
   const int lrow = tid / CPR;
   const uint32_t loff = (uint32_t)(lrow * D + (((tid % CPR) ^ (2 * swz<D>(lrow))) * 8)) * 2u;
-  auto issue = [&](int t) {
-    const int st = t % BNST;
+  auto issue = [&](int t, int st) {
     const int64_t r0 = n0 + (int64_t)t * BT;
     const bf16_t* kt = kb + (size_t)r0 * D;
     const bf16_t* vt = vb + (size_t)r0 * D;
-    const uint32_t kbase = __builtin_amdgcn_readfirstlane(lds_offset(&lds_k[st][0]) + w * 1024);
-    const uint32_t vbase = __builtin_amdgcn_readfirstlane(lds_offset(&lds_v[st][0]) + w * 1024);
+    const uint32_t kbase = __builtin_amdgcn_readfirstlane(lds_offset(&ring[st].k[0]) + w * 1024);
+    const uint32_t vbase = __builtin_amdgcn_readfirstlane(lds_offset(&ring[st].v[0]) + w * 1024);
     const int64_t left = n1 - r0;
     uint32_t off = loff;
     if (left < BT) {  // partial last tile: rows past the end repeat the last row (masked)
@@ -127,64 +136,78 @@ __global__ __launch_bounds__(D * 4) void absorb_bf16(const bf16_t* __restrict__ 
     return (uint32_t)((row * CPR + (cc ^ (2 * swz<D>(row)))) * 16 + (q & 1) * 8);
   };
   const int ra = 8 * g + e_row, rb = ra + 4;
-  const uint32_t koff_a = tr_off(ra, w * 16), koff_b = tr_off(rb, w * 16);
+  // Per-lane read addresses in stage 0; stage st adds st * sizeof(stage) as an immediate.
+  const uint32_t ring0 = lds_offset(&ring[0]);
+  const uint32_t koff_a = ring0 + tr_off(ra, w * 16), koff_b = ring0 + tr_off(rb, w * 16);
+  uint32_t voff_a[NJT], voff_b[NJT];
+#pragma unroll
+  for (int j = 0; j < NJT; ++j) {
+    voff_a[j] = ring0 + (uint32_t)sizeof(ring[0].k) + tr_off(ra, j * 16);
+    voff_b[j] = ring0 + (uint32_t)sizeof(ring[0].k) + tr_off(rb, j * 16);
+  }
 
   f32x4 acc[NJT];
 #pragma unroll
   for (int j = 0; j < NJT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   float zacc = 0.f;
 
-  for (int t = 0; t < BNST - 1 && t < niter; ++t) issue(t);
-  for (int t = 0; t < niter; ++t) {
-    // Stage t has landed once at most (#later stages issued) * 2 loads remain.
-    const int later = niter - 1 - t < BNST - 2 ? niter - 1 - t : BNST - 2;
-    switch (later) {
-      case 0: wait_vmem<0>(); break;
-      case 1: wait_vmem<2>(); break;
-      case 2: wait_vmem<4>(); break;
-      case 3: wait_vmem<6>(); break;
-      default: wait_vmem<8>(); break;
+  for (int t = 0; t < BNST - 1 && t < niter; ++t) issue(t, t);
+  for (int t0 = 0; t0 < niter; t0 += BNST) {
+#pragma unroll
+    for (int st = 0; st < BNST; ++st) {  // stage st of the ring holds tile t0 + st
+      const int t = t0 + st;
+      if (t >= niter) break;
+      // Tile t has landed once at most (#later tiles issued) * 2 loads remain.
+      const int later = niter - 1 - t < BNST - 2 ? niter - 1 - t : BNST - 2;
+      static_assert(BNST - 2 == 2, "wait cases");
+      if (later >= 2) wait_vmem<4>();
+      else if (later == 1) wait_vmem<2>();
+      else wait_vmem<0>();
+      lds_barrier();  // ... for every wave; every wave is also done with tile t-1
+      if (t + BNST - 1 < niter) issue(t + BNST - 1, (st + BNST - 1) % BNST);  // stage of t-1
+      const int valid = (int)(n1 - (n0 + (int64_t)t * BT));  // tokens of this tile in range
+      constexpr uint32_t kStage = sizeof(AbsorbStage<D>);
+      // A: V^T for every value-feature tile, tokens in the same order as B. The reads
+      // are issued before the phi work so that their latency is hidden behind it; the
+      // hi products of all tiles go before the lo products, so no MFMA waits for the
+      // one just before it.
+      bf16x8 a[NJT];
+#pragma unroll
+      for (int j = 0; j < NJT; ++j) {
+        const v4i16 v0 = lds_tr8(voff_a[j] + st * kStage), v1 = lds_tr8(voff_b[j] + st * kStage);
+        a[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+      __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the phi work
+      // B: phi(K) for this wave's 16 key features, tokens 8g + 0..7, split hi + lo.
+      // phi(x) = exp(min(x, 0)) + max(x, 0): x + 1 for x > 0 (exp(0) = 1 exactly), e^x
+      // otherwise (plus zero).
+      const v4i16 k0 = lds_tr8(koff_a + st * kStage), k1 = lds_tr8(koff_b + st * kStage);
+      float f[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = bf16_to_f32((uint32_t)(uint16_t)(e < 4 ? k0[e] : k1[e - 4]));
+        f[e] = __builtin_amdgcn_exp2f(fminf(x * kLog2eAbs, 0.f)) + fmaxf(x, 0.f);
+      }
+      if (valid < BT) {  // partial last tile (wave-uniform): tokens past the end weigh 0
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = 8 * g + e < valid ? f[e] : 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) zacc += f[e];
+      uint32_t hw[4], lw[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        hw[e] = pack_bf16x2(f[2 * e], f[2 * e + 1]);
+        lw[e] = pack_bf16x2(f[2 * e] - __uint_as_float(hw[e] << 16),
+                            f[2 * e + 1] - __uint_as_float(hw[e] & 0xFFFF0000u));
+      }
+      const bf16x8 bh = as_bf16x8(make_uint4(hw[0], hw[1], hw[2], hw[3]));
+      const bf16x8 bl = as_bf16x8(make_uint4(lw[0], lw[1], lw[2], lw[3]));
+#pragma unroll
+      for (int j = 0; j < NJT; ++j) acc[j] = Mfma<bf16_t>::mma(a[j], bh, acc[j]);
+#pragma unroll
+      for (int j = 0; j < NJT; ++j) acc[j] = Mfma<bf16_t>::mma(a[j], bl, acc[j]);
     }
-    static_assert(BNST - 2 <= 4, "wait cases");
-    lds_barrier();  // ... for every wave; every wave is also done with stage t-1
-    if (t + BNST - 1 < niter) issue(t + BNST - 1);  // into the stage consumed at t - 1
-    const int st = t % BNST;
-    const int valid = (int)(n1 - (n0 + (int64_t)t * BT));  // tokens of this stage in range
-    const uint32_t kt = lds_offset(&lds_k[st][0]), vt = lds_offset(&lds_v[st][0]);
-    // A: V^T for every value-feature tile, tokens in the same order as B. The reads
-    // are issued before the phi work so that their latency is hidden behind it; the
-    // hi products of all tiles go before the lo products, so no MFMA waits for the
-    // one just before it.
-    bf16x8 a[NJT];
-#pragma unroll
-    for (int j = 0; j < NJT; ++j) {
-      const v4i16 v0 = lds_tr8(vt + tr_off(ra, j * 16)), v1 = lds_tr8(vt + tr_off(rb, j * 16));
-      a[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-    }
-    __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the phi work
-    // B: phi(K) for this wave's 16 key features, tokens 8g + 0..7, split hi + lo.
-    const v4i16 k0 = lds_tr8(kt + koff_a), k1 = lds_tr8(kt + koff_b);
-    float f[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float x = bf16_to_f32((uint32_t)(uint16_t)(e < 4 ? k0[e] : k1[e - 4]));
-      const float ph = x > 0.f ? x + 1.f : __builtin_amdgcn_exp2f(x * kLog2eAbs);
-      f[e] = 8 * g + e < valid ? ph : 0.f;
-      zacc += f[e];
-    }
-    uint32_t hw[4], lw[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      hw[e] = pack_bf16x2(f[2 * e], f[2 * e + 1]);
-      lw[e] = pack_bf16x2(f[2 * e] - __uint_as_float(hw[e] << 16),
-                          f[2 * e + 1] - __uint_as_float(hw[e] & 0xFFFF0000u));
-    }
-    const bf16x8 bh = as_bf16x8(make_uint4(hw[0], hw[1], hw[2], hw[3]));
-    const bf16x8 bl = as_bf16x8(make_uint4(lw[0], lw[1], lw[2], lw[3]));
-#pragma unroll
-    for (int j = 0; j < NJT; ++j) acc[j] = Mfma<bf16_t>::mma(a[j], bh, acc[j]);
-#pragma unroll
-    for (int j = 0; j < NJT; ++j) acc[j] = Mfma<bf16_t>::mma(a[j], bl, acc[j]);
   }
 
   // Partial state: acc[j][r] = S[16j + 4g + r][16w + c].
@@ -293,11 +316,39 @@ __global__ __launch_bounds__(NTHR) void absorb_f32(const float* __restrict__ kev
 
 }  // namespace
 
-AbsorbPlan absorb_plan(int64_t n_ev) {
+// Compute units of the current device, cached per device (the split plan aims at one
+// resident workgroup per compute unit).
+static int device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+AbsorbPlan absorb_plan(int dtype, int heads, int d, int64_t n_ev) {
   AbsorbPlan p;
-  int64_t per = (n_ev + kAbsorbMaxSplits - 1) / kAbsorbMaxSplits;
-  if (per < 128) per = 128;
-  per = (per + TS - 1) / TS * TS;  // a multiple of both token tilings (64 and 32)
+  int64_t per;
+  if (dtype == 0) {
+    // bf16: as many splits as fill every compute unit once (the kernel's LDS ring
+    // admits one workgroup per unit at d = 128, three at d = 64), at most the maximum,
+    // in whole 32-token tiles.
+    const int per_cu = d == 128 ? 1 : 3;
+    int target = per_cu * device_cu_count() / (heads > 0 ? heads : 1);
+    if (target > kAbsorbMaxSplits) target = kAbsorbMaxSplits;
+    if (target < 1) target = 1;
+    per = (n_ev + target - 1) / target;
+    if (per < 128) per = 128;
+    per = (per + BT - 1) / BT * BT;
+  } else {
+    per = (n_ev + kAbsorbMaxSplits - 1) / kAbsorbMaxSplits;
+    if (per < 128) per = 128;
+    per = (per + TS - 1) / TS * TS;  // whole fp32 token tiles
+  }
   p.tokens_per_split = (int)per;
   p.n_split = (int)((n_ev + per - 1) / per);
   if (p.n_split < 1) p.n_split = 1;
@@ -311,7 +362,7 @@ size_t absorb_partial_floats(int heads, int d) {
 hipError_t launch_absorb(int dtype, int heads, int d, const void* k, const void* v, int64_t n_ev,
                          int64_t head_stride, float* S, float* z, float* partials,
                          uint16_t* s_split, hipStream_t stream, bool reduce) {
-  const AbsorbPlan p = absorb_plan(n_ev);
+  const AbsorbPlan p = absorb_plan(dtype, heads, d, n_ev);
   if (dtype == 0) {
     dim3 grid(p.n_split, heads);
 #define HF_ABS(D)                                                                             \

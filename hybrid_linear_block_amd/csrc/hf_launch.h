@@ -13,7 +13,9 @@ struct AbsorbPlan {
   int tokens_per_split;
   int n_split;
 };
-AbsorbPlan absorb_plan(int64_t n_ev);
+// Token split of an absorb of n_ev tokens (dtype 0 = bf16, 1 = fp32); the same for
+// every call with the same arguments on the same device.
+AbsorbPlan absorb_plan(int dtype, int heads, int d, int64_t n_ev);
 size_t absorb_partial_floats(int heads, int d);
 // Two kernels: per-split partial states into `partials`, then an in-order reduction,
 // which also refreshes s_split (if not null) from the new S. With reduce = false

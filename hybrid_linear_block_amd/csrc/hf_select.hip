@@ -238,7 +238,7 @@ hipError_t launch_pool_and_reduce(int dtype, int heads, int d, int block, const 
   const int nqb = (int)((n_q + block - 1) / block);
   const int nkb = (int)((n_kv + block - 1) / block);
   const int n_pool = (heads * (nqb + nkb) + POOL_THREADS / 64 - 1) / (POOL_THREADS / 64);
-  const int n_split = absorb_plan(n_ev).n_split;
+  const int n_split = absorb_plan(dtype, heads, d, n_ev).n_split;
 #define HF_POOLRED(T, D)                                                                       \
   pool_and_reduce<T, D><<<n_pool + red_groups<D>() * heads, POOL_THREADS, 0, stream>>>(         \
       static_cast<const T*>(q), n_q, q_hs, static_cast<const T*>(k), n_kv, kv_hs, block, nqb,   \

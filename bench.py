@@ -222,12 +222,14 @@ def main():
     for k in range(args.steps):
         run(k)
     ev1.record()
+    host = time.perf_counter() - w0  # host time to enqueue the K steps
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     ms_step = ev0.elapsed_time(ev1) / args.steps
     total_flop = sum(step_flops(k) for k in range(args.steps))
     value = total_flop / (ms_step * args.steps / 1e3) / 1e12
-    log(f"[bench] {ms_step:.4f} ms/step (wall {wall * 1e3 / args.steps:.4f})")
+    log(f"[bench] {ms_step:.4f} ms/step (wall {wall * 1e3 / args.steps:.4f}, "
+        f"host enqueue {host * 1e3 / args.steps:.4f})")
 
     # Same K steps again with HIP events around every kernel (on the launch stream).
     for s in sets:
@@ -273,27 +275,36 @@ def main():
                     frac=round(achieved / peak, 4), traffic=traffic, kernel="sparse_swa",
                     flop_per_launch=int(swa_flop), avg_launch_us=round(swa_us, 2))
 
-    # On one stream (the default) the absorb's reduce, which writes S and z, runs inside
-    # the pooling launch, so its bytes are counted there.
+    # On one stream (the default) the absorb shares the attend call's launches: its
+    # partial states are formed in the pooling launch and its reduce (which writes S
+    # and z) runs in the selection launch, so its bytes and FLOPs are counted there.
     fused = not args.side_stream and not args.serial
     kbytes = dict(sets[0].bytes())
+    kflops = {name: statistics.mean(fl[name] for fl in flops)
+              for name in ("absorb", "block_pool", "score_select", "sparse_swa")}
+    names = ("absorb", "block_pool", "score_select", "sparse_swa")
     if fused:
         sz = sets[0].state_bytes()
-        kbytes["absorb"] -= sz
-        kbytes["block_pool"] += sz
+        kbytes = dict(absorb_and_pool=kbytes["absorb"] - sz + kbytes["block_pool"],
+                      select_and_reduce=kbytes["score_select"] + sz,
+                      sparse_swa=kbytes["sparse_swa"])
+        kflops = dict(absorb_and_pool=kflops["absorb"] + kflops["block_pool"],
+                      select_and_reduce=kflops["score_select"], sparse_swa=kflops["sparse_swa"])
+        kern_us = dict(absorb_and_pool=kern_us.get("block_pool"),
+                       select_and_reduce=kern_us.get("score_select"),
+                       sparse_swa=kern_us.get("sparse_swa"))
+        names = ("absorb_and_pool", "select_and_reduce", "sparse_swa")
     kernels = {}
-    for name in ("absorb", "block_pool", "score_select", "sparse_swa"):
+    for name in names:
         us = kern_us.get(name)
         b = kbytes[name]
-        f = statistics.mean(fl[name] for fl in flops)
+        f = kflops[name]
         kernels[name] = dict(avg_us=None if us is None else round(us, 2),
                              algo_bytes=int(b), algo_flop=int(f),
                              gbs=None if not us else round(b / (us * 1e-6) / 1e9, 1),
                              tflops=None if not us else round(f / (us * 1e-6) / 1e12, 2),
                              pct_hbm=None if not us else round(100 * b / (us * 1e-6) / PEAK_HBM_BPS, 1),
                              pct_mfma=None if not us else round(100 * f / (us * 1e-6) / 1e12 / peak, 1))
-    if fused:
-        kernels["block_pool"]["includes"] = "absorb reduce (S and z written)"
 
     if args.calibrate_copy_mib:
         n = args.calibrate_copy_mib * (1 << 20) // 4

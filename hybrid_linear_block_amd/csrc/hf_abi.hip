@@ -223,14 +223,12 @@ static hf_status check_absorb(const hf_state* st, const void* k_ev, const void* 
 }
 
 // The absorb kernels on stream s (n_ev > 0); the caller has validated everything.
-// With reduce = false only the partial states are formed: the reduce then has to
-// run before anything reads S or z (enqueue_attend does it in the pooling launch).
 static hipError_t enqueue_absorb(hf_state* st, const void* k_ev, const void* v_ev, int64_t n_ev,
-                                 int64_t ev_head_stride, hipStream_t s, bool reduce = true) {
+                                 int64_t ev_head_stride, hipStream_t s) {
   const hf_config& c = st->cfg;
   return timed(st, HF_KERNEL_ABSORB, s, [&]() {
     return hf::launch_absorb(c.dtype, c.num_heads, c.head_dim, k_ev, v_ev, n_ev, ev_head_stride,
-                             st->S, st->z, st->partials, st->s_split, s, reduce);
+                             st->S, st->z, st->partials, st->s_split, s);
   });
 }
 
@@ -271,37 +269,50 @@ static hf_status check_attend_all(const hf_state* st, const void* q, int64_t n_q
   return HF_OK;
 }
 
-// The attention kernels on stream s (n_q > 0); if join is not null, the sparse
-// kernel (the only one that reads S and z) waits for it first. reduce_n_ev > 0: an
-// absorb of that many tokens has formed its partial states without the reduce, and
-// the reduce runs in the same launch as the block pooling (*reduced tells whether
-// that launch was enqueued).
+// Evicted tokens that an attend call absorbs in its own launches.
+struct FusedAbsorb {
+  const void* k_ev;
+  const void* v_ev;
+  int64_t n_ev;  // > 0
+  int64_t head_stride;
+};
+
+// Block pooling, selection and attention on stream s (n_q > 0), validated by the
+// caller; with `join`, the attention waits for that event. With `fa`, the absorb of
+// its tokens runs inside the first two launches: the partial states next to the
+// pooling, the reduce next to the selection, so S and z hold the new tokens before
+// the attention reads them; *absorbed tells whether the reduce was enqueued.
 static hipError_t enqueue_attend(hf_state* st, const void* q, int64_t n_q, int64_t q_hs,
                                  const void* k_win, const void* v_win, int64_t n_kv,
                                  int64_t kv_hs, int32_t top_k, void* out, int64_t out_hs,
                                  int32_t* sel_out, hipStream_t s, hipEvent_t join,
-                                 int64_t reduce_n_ev = 0, bool* reduced = nullptr) {
+                                 const FusedAbsorb* fa = nullptr, bool* absorbed = nullptr) {
   const hf_config& c = st->cfg;
   const int nqb = (int)ceil_div(n_q, c.block_size);
   const int nkb = (int)ceil_div(n_kv, c.block_size);
   int32_t* sel = sel_out ? sel_out : st->sel;
   hipError_t r = timed(st, HF_KERNEL_BLOCK_POOL, s, [&]() {
-    if (reduce_n_ev > 0)
-      return hf::launch_pool_and_reduce(c.dtype, c.num_heads, c.head_dim, c.block_size, q, n_q,
+    if (fa)
+      return hf::launch_absorb_and_pool(c.dtype, c.num_heads, c.head_dim, c.block_size, fa->k_ev,
+                                        fa->v_ev, fa->n_ev, fa->head_stride, st->partials, q, n_q,
                                         q_hs, k_win, n_kv, kv_hs, st->pooled_q, st->pooled_k,
-                                        st->nqb_cap, st->nkb_cap, st->partials, reduce_n_ev, st->S,
-                                        st->z, st->s_split, s);
+                                        st->nqb_cap, st->nkb_cap, s);
     return hf::launch_block_pool(c.dtype, c.num_heads, c.head_dim, c.block_size, q, n_q, q_hs,
                                  k_win, n_kv, kv_hs, st->pooled_q, st->pooled_k, st->nqb_cap,
                                  st->nkb_cap, s);
   });
-  if (reduced) *reduced = r == hipSuccess;
   if (r == hipSuccess)
     r = timed(st, HF_KERNEL_SCORE_SELECT, s, [&]() {
+      if (fa)
+        return hf::launch_select_and_reduce(c.dtype, c.num_heads, c.head_dim, nqb, nkb,
+                                            st->nqb_cap, st->nkb_cap, st->pooled_q, st->pooled_k,
+                                            st->scale, top_k, sel, st->partials, fa->n_ev, st->S,
+                                            st->z, st->s_split, s);
       return hf::launch_score_select(c.num_heads, c.head_dim, nqb, nkb, st->nqb_cap, st->nkb_cap,
                                      st->pooled_q, st->pooled_k, st->scale, top_k, sel, nullptr,
                                      s);
     });
+  if (absorbed) *absorbed = fa && r == hipSuccess;
   if (r == hipSuccess && join) r = hipStreamWaitEvent(s, join, 0);
   if (r == hipSuccess)
     r = timed(st, HF_KERNEL_SPARSE_SWA, s, [&]() {
@@ -356,19 +367,19 @@ hf_status hf_absorb_and_attend(hf_state* st, const void* k_ev, const void* v_ev,
                              top_k, out, out_head_stride, sel_out, s, st->ev_join);
       return err;
     }
-    // One stream: the absorb's reduce runs in the pooling launch of the attention;
-    // the absorb counts as enqueued once its reduce is.
-    if (n_ev > 0) {
-      err = enqueue_absorb(st, k_ev, v_ev, n_ev, ev_head_stride, s, /*reduce=*/n_q == 0);
-      absorbed = err == hipSuccess && n_q == 0;
+    // One stream: the absorb runs inside the attend call's pooling and selection
+    // launches; it counts as enqueued once its reduce is.
+    if (n_q == 0) {
+      if (n_ev > 0) {
+        err = enqueue_absorb(st, k_ev, v_ev, n_ev, ev_head_stride, s);
+        absorbed = err == hipSuccess;
+      }
+      return err;
     }
-    if (err == hipSuccess && n_q > 0) {
-      bool reduced = false;
-      err = enqueue_attend(st, q, n_q, q_head_stride, k_win, v_win, n_kv, kv_head_stride, top_k,
-                           out, out_head_stride, sel_out, s, nullptr, n_ev, &reduced);
-      absorbed = n_ev > 0 && reduced;
-    }
-    return err;
+    const FusedAbsorb fa{k_ev, v_ev, n_ev, ev_head_stride};
+    return enqueue_attend(st, q, n_q, q_head_stride, k_win, v_win, n_kv, kv_head_stride, top_k,
+                          out, out_head_stride, sel_out, s, nullptr, n_ev > 0 ? &fa : nullptr,
+                          &absorbed);
   });
   if (absorbed) st->next_ev += n_ev;  // the absorb is enqueued and will run
   return r;

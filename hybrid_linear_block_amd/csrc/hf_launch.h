@@ -16,13 +16,14 @@ struct AbsorbPlan {
 // Token split of an absorb of n_ev tokens (dtype 0 = bf16, 1 = fp32); the same for
 // every call with the same arguments on the same device.
 AbsorbPlan absorb_plan(int dtype, int heads, int d, int64_t n_ev);
+// Workgroups of the partial-state pass of that plan.
+int absorb_items(int dtype, int heads, int d, const AbsorbPlan& p);
 size_t absorb_partial_floats(int heads, int d);
 // Two kernels: per-split partial states into `partials`, then an in-order reduction,
-// which also refreshes s_split (if not null) from the new S. With reduce = false
-// only the first is launched; launch_pool_and_reduce runs the second.
+// which also refreshes s_split (if not null) from the new S.
 hipError_t launch_absorb(int dtype, int heads, int d, const void* k, const void* v, int64_t n_ev,
                          int64_t head_stride, float* S, float* z, float* partials,
-                         uint16_t* s_split, hipStream_t stream, bool reduce = true);
+                         uint16_t* s_split, hipStream_t stream);
 // s_split[h] = the bf16 hi and lo parts of S[h] ([H][2][d][d]): x ~= hi + lo, hi =
 // bf16(x), lo = bf16(x - hi), both rounded to nearest even. The bf16 attention
 // epilogue reads S in this form.
@@ -35,16 +36,25 @@ hipError_t launch_block_pool(int dtype, int heads, int d, int block, const void*
                              int64_t q_hs, const void* k, int64_t n_kv, int64_t kv_hs,
                              float* pooled_q, float* pooled_k, int nqb_cap, int nkb_cap,
                              hipStream_t stream);
-// launch_block_pool and, in the same launch, the reduce of an absorb of n_ev tokens
-// whose partial states launch_absorb(..., reduce = false) has written.
-hipError_t launch_pool_and_reduce(int dtype, int heads, int d, int block, const void* q,
-                                  int64_t n_q, int64_t q_hs, const void* k, int64_t n_kv,
-                                  int64_t kv_hs, float* pooled_q, float* pooled_k, int nqb_cap,
-                                  int nkb_cap, const float* partials, int64_t n_ev, float* S,
-                                  float* z, uint16_t* s_split, hipStream_t stream);
+// The partial-state pass of an absorb of n_ev evicted tokens (as in launch_absorb)
+// and launch_block_pool in one launch: the two read and write different buffers
+// and are both bound by memory. The absorb is complete once
+// launch_select_and_reduce has run its reduce.
+hipError_t launch_absorb_and_pool(int dtype, int heads, int d, int block, const void* k_ev,
+                                  const void* v_ev, int64_t n_ev, int64_t ev_hs, float* partials,
+                                  const void* q, int64_t n_q, int64_t q_hs, const void* k,
+                                  int64_t n_kv, int64_t kv_hs, float* pooled_q, float* pooled_k,
+                                  int nqb_cap, int nkb_cap, hipStream_t stream);
 hipError_t launch_score_select(int heads, int d, int nqb, int nkb, int nqb_cap, int nkb_cap,
                                const float* pooled_q, const float* pooled_k, float scale,
                                int top_k, int32_t* sel, float* scores_out, hipStream_t stream);
+// launch_score_select and, in the same launch, the reduce of the absorb whose
+// partial states launch_absorb_and_pool has written (dtype and n_ev as given there).
+hipError_t launch_select_and_reduce(int dtype, int heads, int d, int nqb, int nkb, int nqb_cap,
+                                    int nkb_cap, const float* pooled_q, const float* pooled_k,
+                                    float scale, int top_k, int32_t* sel, const float* partials,
+                                    int64_t n_ev, float* S, float* z, uint16_t* s_split,
+                                    hipStream_t stream);
 
 // ---- block-sparse softmax attention + linear read ---------------------------------
 hipError_t launch_sparse_swa(int dtype, int heads, int d, int block, const void* q, int64_t n_q,

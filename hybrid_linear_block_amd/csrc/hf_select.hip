@@ -15,6 +15,7 @@
 //             order-preserving uint32 key of the fp32 score (-0.0 counts as
 //             +0.0), ties going to the lower index, and writes the kept indices
 //             in ascending order.
+#include "hf_absorb_parts.h"
 #include "hf_device.h"
 #include "hf_launch.h"
 #include "hf_reduce.h"
@@ -28,16 +29,17 @@ constexpr int POOL_THREADS = 256;  // 4 waves, one (head, block) per wave
 // Row mean of one block per wave: lane (rg, cc) accumulates 16-byte column chunk
 // cc over rows rg, rg + RPI, ... (all loads independent), then the row groups are
 // added with lane exchanges in a fixed order.
+// Wave `wid` pools (head wid / (nqb + nkb), block wid % (nqb + nkb)); the Q blocks of
+// a head come first, then its key blocks.
 template <typename T, int D>
-__device__ __forceinline__ void pool_group(
-    int wg, const T* __restrict__ q, int64_t n_q, int64_t q_hs, const T* __restrict__ k,
+__device__ __forceinline__ void pool_wave(
+    int wid, const T* __restrict__ q, int64_t n_q, int64_t q_hs, const T* __restrict__ k,
     int64_t n_kv, int64_t kv_hs, int block, int nqb, int nkb, int heads,
     float* __restrict__ pooled_q, float* __restrict__ pooled_k, int nqb_cap, int nkb_cap) {
   constexpr int VEC = 16 / sizeof(T);  // elements per 16-byte chunk
   constexpr int CPR = D / VEC;         // chunks per row
   constexpr int RPI = 64 / CPR;        // rows per wave-wide load
   const int lane = threadIdx.x & 63;
-  const int wid = wg * (POOL_THREADS / 64) + (threadIdx.x >> 6);
   if (wid >= heads * (nqb + nkb)) return;
   const int h = wid / (nqb + nkb), b = wid % (nqb + nkb);
   const bool is_q = b < nqb;
@@ -87,29 +89,29 @@ __global__ __launch_bounds__(POOL_THREADS) void block_pool(
     const T* __restrict__ q, int64_t n_q, int64_t q_hs, const T* __restrict__ k, int64_t n_kv,
     int64_t kv_hs, int block, int nqb, int nkb, int heads, float* __restrict__ pooled_q,
     float* __restrict__ pooled_k, int nqb_cap, int nkb_cap) {
-  pool_group<T, D>(blockIdx.x, q, n_q, q_hs, k, n_kv, kv_hs, block, nqb, nkb, heads, pooled_q,
-                   pooled_k, nqb_cap, nkb_cap);
+  pool_wave<T, D>(blockIdx.x * (POOL_THREADS / 64) + (threadIdx.x >> 6), q, n_q, q_hs, k, n_kv,
+                  kv_hs, block, nqb, nkb, heads, pooled_q, pooled_k, nqb_cap, nkb_cap);
 }
 
-// The block pooling and the absorb's reduce in one launch: workgroups below
-// n_pool pool, the others reduce (red_groups per head). The two read different
-// buffers and write different buffers, and both are bound by memory, so running
-// them side by side saves the second launch and its ramp.
-static_assert(POOL_THREADS == RED_THREADS, "one workgroup size for both parts");
+// The absorb's partial states and the block pooling in one launch: workgroups
+// below n_abs are absorb workgroups (absorb::item), the others pool one (head,
+// block) per wave. The two read and write different buffers and both are bound by
+// memory, so they share the launch (and its ramp) instead of running one after
+// the other. The absorb workgroups come first, so that they are spread over the
+// compute units before the pooling fills the rest.
 template <typename T, int D>
-__global__ __launch_bounds__(POOL_THREADS) void pool_and_reduce(
-    const T* __restrict__ q, int64_t n_q, int64_t q_hs, const T* __restrict__ k, int64_t n_kv,
-    int64_t kv_hs, int block, int nqb, int nkb, int heads, float* __restrict__ pooled_q,
-    float* __restrict__ pooled_k, int nqb_cap, int nkb_cap, int n_pool,
-    const float* __restrict__ partials, int n_split, float* __restrict__ S,
-    float* __restrict__ z, uint16_t* __restrict__ s_split) {
-  if ((int)blockIdx.x < n_pool) {
-    pool_group<T, D>(blockIdx.x, q, n_q, q_hs, k, n_kv, kv_hs, block, nqb, nkb, heads, pooled_q,
-                     pooled_k, nqb_cap, nkb_cap);
+__global__ __launch_bounds__((absorb::threads<T, D>())) void absorb_and_pool(
+    const T* __restrict__ kev, const T* __restrict__ vev, int64_t n_ev, int64_t ev_hs, int tps,
+    int n_split, float* __restrict__ partials, int n_abs, const T* __restrict__ q, int64_t n_q,
+    int64_t q_hs, const T* __restrict__ k, int64_t n_kv, int64_t kv_hs, int block, int nqb,
+    int nkb, int heads, float* __restrict__ pooled_q, float* __restrict__ pooled_k, int nqb_cap,
+    int nkb_cap) {
+  if ((int)blockIdx.x < n_abs) {
+    absorb::item<T, D>(blockIdx.x, n_split, kev, vev, n_ev, ev_hs, tps, partials);
   } else {
-    const int r = blockIdx.x - n_pool;
-    absorb_reduce_group<D>(r % red_groups<D>(), r / red_groups<D>(), partials, n_split, S, z,
-                           s_split);
+    constexpr int WPG = absorb::threads<T, D>() / 64;  // pooling waves per workgroup
+    pool_wave<T, D>(((int)blockIdx.x - n_abs) * WPG + (threadIdx.x >> 6), q, n_q, q_hs, k, n_kv,
+                    kv_hs, block, nqb, nkb, heads, pooled_q, pooled_k, nqb_cap, nkb_cap);
   }
 }
 
@@ -132,13 +134,13 @@ constexpr int SEL_QB = SEL_THREADS / 64;  // query blocks per workgroup, one wav
 // order. Keys are unique up to exact score ties, which therefore go to the lower
 // index.
 template <int D, int NE>
-__global__ __launch_bounds__(SEL_THREADS) void score_select(
-    const float* __restrict__ pooled_q, const float* __restrict__ pooled_k, int nqb, int nkb,
-    int nqb_cap, int nkb_cap, float scale, int top_k, int32_t* __restrict__ sel,
-    float* __restrict__ scores_out) {
+__device__ __forceinline__ void select_group(
+    int qg, int h, const float* __restrict__ pooled_q, const float* __restrict__ pooled_k,
+    int nqb, int nkb, int nqb_cap, int nkb_cap, float scale, int top_k,
+    int32_t* __restrict__ sel, float* __restrict__ scores_out) {
   __shared__ uint32_t key[SEL_QB][kMaxKeyBlocks];
   __shared__ float4 qs[SEL_QB][D / 4];
-  const int i0 = blockIdx.x * SEL_QB, h = blockIdx.y, tid = threadIdx.x;
+  const int i0 = qg * SEL_QB, tid = threadIdx.x;
   const int nq = nqb - i0 < SEL_QB ? nqb - i0 : SEL_QB;
   for (int x = tid; x < SEL_QB * (D / 4); x += SEL_THREADS) {
     const int r = x / (D / 4), e = x % (D / 4);
@@ -147,25 +149,41 @@ __global__ __launch_bounds__(SEL_THREADS) void score_select(
                       : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   __syncthreads();
-  for (int j = tid; j < nkb; j += SEL_THREADS) {
-    const float4* km = reinterpret_cast<const float4*>(pooled_k + ((size_t)h * nkb_cap + j) * D);
-    float4 kv[D / 4];
+  // Four adjacent lanes per key block, each over a quarter of the features (the
+  // block's row is read as four contiguous segments); the quarters are added with
+  // two lane exchanges, which give every lane of the four the same sum.
+  constexpr int PARTS = 4, EV = D / 4 / PARTS;  // float4s per quarter
+  static_assert(SEL_THREADS % PARTS == 0, "a key block's lanes stay in one pass");
+  const int part = tid % PARTS;
+  for (int x = tid; x < nkb * PARTS; x += SEL_THREADS) {
+    const int j = x / PARTS;
+    const float4* km =
+        reinterpret_cast<const float4*>(pooled_k + ((size_t)h * nkb_cap + j) * D) + part * EV;
+    float4 kv[EV];
 #pragma unroll
-    for (int e = 0; e < D / 4; ++e) kv[e] = km[e];
+    for (int e = 0; e < EV; ++e) kv[e] = km[e];
+    float sq[SEL_QB];
 #pragma unroll
     for (int r = 0; r < SEL_QB; ++r) {
       float s = 0.f;
 #pragma unroll
-      for (int e = 0; e < D / 4; ++e) {
-        const float4 qv = qs[r][e];
+      for (int e = 0; e < EV; ++e) {
+        const float4 qv = qs[r][part * EV + e];
         s += qv.x * kv[e].x;
         s += qv.y * kv[e].y;
         s += qv.z * kv[e].z;
         s += qv.w * kv[e].w;
       }
-      const float sc = s * scale;
-      key[r][j] = score_key(sc);
-      if (scores_out && r < nq) scores_out[((size_t)h * nqb + i0 + r) * nkb + j] = sc;
+      s += __shfl_xor(s, 1);
+      s += __shfl_xor(s, 2);
+      sq[r] = s * scale;
+    }
+    if (part == 0) {
+#pragma unroll
+      for (int r = 0; r < SEL_QB; ++r) {
+        key[r][j] = score_key(sq[r]);
+        if (scores_out && r < nq) scores_out[((size_t)h * nqb + i0 + r) * nkb + j] = sq[r];
+      }
     }
   }
   __syncthreads();
@@ -207,6 +225,35 @@ __global__ __launch_bounds__(SEL_THREADS) void score_select(
   }
 }
 
+template <int D, int NE>
+__global__ __launch_bounds__(SEL_THREADS) void score_select(
+    const float* __restrict__ pooled_q, const float* __restrict__ pooled_k, int nqb, int nkb,
+    int nqb_cap, int nkb_cap, float scale, int top_k, int32_t* __restrict__ sel,
+    float* __restrict__ scores_out) {
+  select_group<D, NE>(blockIdx.x, blockIdx.y, pooled_q, pooled_k, nqb, nkb, nqb_cap, nkb_cap,
+                      scale, top_k, sel, scores_out);
+}
+
+// The selection and the absorb's reduce in one launch: workgroups below n_sel
+// select (n_qg groups of query blocks per head), the others reduce (red_groups per
+// head). They read and write different buffers.
+static_assert(SEL_THREADS == RED_THREADS, "one workgroup size for both parts");
+template <int D, int NE>
+__global__ __launch_bounds__(SEL_THREADS) void select_and_reduce(
+    const float* __restrict__ pooled_q, const float* __restrict__ pooled_k, int nqb, int nkb,
+    int nqb_cap, int nkb_cap, float scale, int top_k, int32_t* __restrict__ sel, int n_qg,
+    int n_sel, const float* __restrict__ partials, int n_split, float* __restrict__ S,
+    float* __restrict__ z, uint16_t* __restrict__ s_split) {
+  if ((int)blockIdx.x < n_sel) {
+    select_group<D, NE>((int)blockIdx.x % n_qg, (int)blockIdx.x / n_qg, pooled_q, pooled_k, nqb,
+                        nkb, nqb_cap, nkb_cap, scale, top_k, sel, nullptr);
+  } else {
+    const int r = (int)blockIdx.x - n_sel;
+    absorb_reduce_group<D>(r % red_groups<D>(), r / red_groups<D>(), partials, n_split, S, z,
+                           s_split);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_block_pool(int dtype, int heads, int d, int block, const void* q, int64_t n_q,
@@ -230,25 +277,31 @@ hipError_t launch_block_pool(int dtype, int heads, int d, int block, const void*
   return hipGetLastError();
 }
 
-hipError_t launch_pool_and_reduce(int dtype, int heads, int d, int block, const void* q,
-                                  int64_t n_q, int64_t q_hs, const void* k, int64_t n_kv,
-                                  int64_t kv_hs, float* pooled_q, float* pooled_k, int nqb_cap,
-                                  int nkb_cap, const float* partials, int64_t n_ev, float* S,
-                                  float* z, uint16_t* s_split, hipStream_t stream) {
+hipError_t launch_absorb_and_pool(int dtype, int heads, int d, int block, const void* k_ev,
+                                  const void* v_ev, int64_t n_ev, int64_t ev_hs, float* partials,
+                                  const void* q, int64_t n_q, int64_t q_hs, const void* k,
+                                  int64_t n_kv, int64_t kv_hs, float* pooled_q, float* pooled_k,
+                                  int nqb_cap, int nkb_cap, hipStream_t stream) {
   const int nqb = (int)((n_q + block - 1) / block);
   const int nkb = (int)((n_kv + block - 1) / block);
-  const int n_pool = (heads * (nqb + nkb) + POOL_THREADS / 64 - 1) / (POOL_THREADS / 64);
-  const int n_split = absorb_plan(dtype, heads, d, n_ev).n_split;
-#define HF_POOLRED(T, D)                                                                       \
-  pool_and_reduce<T, D><<<n_pool + red_groups<D>() * heads, POOL_THREADS, 0, stream>>>(         \
-      static_cast<const T*>(q), n_q, q_hs, static_cast<const T*>(k), n_kv, kv_hs, block, nqb,   \
-      nkb, heads, pooled_q, pooled_k, nqb_cap, nkb_cap, n_pool, partials, n_split, S, z, s_split)
-  if (dtype == 0) {
-    if (d == 128) HF_POOLRED(bf16_t, 128); else HF_POOLRED(bf16_t, 64);
-  } else {
-    if (d == 128) HF_POOLRED(float, 128); else HF_POOLRED(float, 64);
+  const AbsorbPlan p = absorb_plan(dtype, heads, d, n_ev);
+  const int n_abs = absorb_items(dtype, heads, d, p);
+#define HF_ABSPOOL(T, D)                                                                       \
+  {                                                                                            \
+    constexpr int wpg = absorb::threads<T, D>() / 64;                                          \
+    const int n_pool = (heads * (nqb + nkb) + wpg - 1) / wpg;                                  \
+    absorb_and_pool<T, D><<<n_abs + n_pool, absorb::threads<T, D>(), 0, stream>>>(             \
+        static_cast<const T*>(k_ev), static_cast<const T*>(v_ev), n_ev, ev_hs,                 \
+        p.tokens_per_split, p.n_split, partials, n_abs, static_cast<const T*>(q), n_q, q_hs,   \
+        static_cast<const T*>(k), n_kv, kv_hs, block, nqb, nkb, heads, pooled_q, pooled_k,     \
+        nqb_cap, nkb_cap);                                                                     \
   }
-#undef HF_POOLRED
+  if (dtype == 0) {
+    if (d == 128) HF_ABSPOOL(bf16_t, 128) else HF_ABSPOOL(bf16_t, 64)
+  } else {
+    if (d == 128) HF_ABSPOOL(float, 128) else HF_ABSPOOL(float, 64)
+  }
+#undef HF_ABSPOOL
   return hipGetLastError();
 }
 
@@ -266,6 +319,27 @@ hipError_t launch_score_select(int heads, int d, int nqb, int nkb, int nqb_cap, 
     if (nkb <= 256) HF_SEL(64, 4); else if (nkb <= 512) HF_SEL(64, 8); else HF_SEL(64, 32);
   }
 #undef HF_SEL
+  return hipGetLastError();
+}
+
+hipError_t launch_select_and_reduce(int dtype, int heads, int d, int nqb, int nkb, int nqb_cap,
+                                    int nkb_cap, const float* pooled_q, const float* pooled_k,
+                                    float scale, int top_k, int32_t* sel, const float* partials,
+                                    int64_t n_ev, float* S, float* z, uint16_t* s_split,
+                                    hipStream_t stream) {
+  const int n_qg = (nqb + SEL_QB - 1) / SEL_QB;
+  const int n_sel = n_qg * heads;
+  const int n_split = absorb_plan(dtype, heads, d, n_ev).n_split;
+#define HF_SELRED(D, NE)                                                                    \
+  select_and_reduce<D, NE><<<n_sel + red_groups<D>() * heads, SEL_THREADS, 0, stream>>>(    \
+      pooled_q, pooled_k, nqb, nkb, nqb_cap, nkb_cap, scale, top_k, sel, n_qg, n_sel,       \
+      partials, n_split, S, z, s_split)
+  if (d == 128) {
+    if (nkb <= 256) HF_SELRED(128, 4); else if (nkb <= 512) HF_SELRED(128, 8); else HF_SELRED(128, 32);
+  } else {
+    if (nkb <= 256) HF_SELRED(64, 4); else if (nkb <= 512) HF_SELRED(64, 8); else HF_SELRED(64, 32);
+  }
+#undef HF_SELRED
   return hipGetLastError();
 }
 

@@ -134,9 +134,12 @@ hf_status hf_attend_chunk(hf_state* st, const void* q, int64_t n_q, int64_t q_he
 
 /* hf_absorb_evicted followed by hf_attend_chunk in one call, with the same
  * results bit for bit. Of the chunk's attention only the sparse attention kernel
- * reads S and z, so when side_stream is not NULL and differs from stream, the
- * absorb runs on side_stream, overlapping the block scoring and selection: it
- * starts after the work already enqueued on stream, and the sparse attention
+ * reads S and z. On one stream (side_stream NULL or equal to stream) the absorb
+ * shares the chunk's launches: its partial states are formed in the block pooling
+ * launch and reduced in the selection launch, so the call takes three launches
+ * instead of five. When side_stream is not NULL and differs from stream, the
+ * absorb runs on side_stream instead, overlapping the block scoring and selection:
+ * it starts after the work already enqueued on stream, and the sparse attention
  * kernel waits for it (two events of the handle). side_stream belongs to the
  * caller and must not carry other work of this handle meanwhile. Either part may
  * be empty (n_ev == 0, n_q == 0). Both parts are validated before anything is
@@ -157,9 +160,12 @@ hf_status hf_block_scores(hf_state* st, const void* q, int64_t n_q, int64_t q_he
 
 /* Kernels a state launches, for per-kernel timing. */
 typedef enum {
-  HF_KERNEL_ABSORB = 0,       /* hf_absorb_evicted */
-  HF_KERNEL_BLOCK_POOL = 1,   /* block means of Q and K (first kernel of an attend call) */
-  HF_KERNEL_SCORE_SELECT = 2, /* block scores + top-K selection */
+  HF_KERNEL_ABSORB = 0,       /* hf_absorb_evicted (both of its launches) */
+  HF_KERNEL_BLOCK_POOL = 1,   /* block means of Q and K (first kernel of an attend call;
+                                 in a one-stream hf_absorb_and_attend also the absorb's
+                                 partial states) */
+  HF_KERNEL_SCORE_SELECT = 2, /* block scores + top-K selection (in a one-stream
+                                 hf_absorb_and_attend also the absorb's reduce) */
   HF_KERNEL_SPARSE_SWA = 3,   /* block-sparse attention + linear read + sum */
   HF_KERNEL_COUNT = 4
 } hf_kernel;

@@ -227,8 +227,9 @@ def test_resume_from_saved_state_bitwise():
 
 @pytest.mark.parametrize("dt,d,B", [("bf16", 128, 64), ("bf16", 64, 64), ("f32", 64, 16)])
 def test_absorb_and_attend_matches_separate_calls_bitwise(dt, d, B):
-    """The combined call (on one stream, where the absorb's reduce shares the
-    pooling launch, and with the absorb forked onto a side stream) gives bit for
+    """The combined call (on one stream, where the absorb's partial states share the
+    pooling launch and its reduce the selection launch, and with the absorb forked
+    onto a side stream) gives bit for
     bit the state and outputs of absorb_evicted followed by attend_chunk, over
     consecutive stream steps (window bookkeeping as in the oracle's stream order)."""
     H, T, c, W, K = 4, 320, 3, 9, 12

@@ -13,6 +13,10 @@ top-K = 55 of 220 key blocks, 4680 evicted tokens. Inputs are resident in HBM
 before timing starts; `--sets` independent input sets (each with its own state)
 are rotated so that consecutive steps do not hit a warm cache.
 
+Before the warmup steps, untimed steps run for --settle-ms (default 100 ms): the
+GPU needs tens of milliseconds of sustained load before its clocks reach their
+steady state, and a stream of chunks runs at that state.
+
 Prints one JSON line on stdout. The effective throughput counts the algorithmic
 FLOPs of the step (absorb 2*n_ev*d^2*H; scores 2*Nqb*Nkb*d*H; sparse attention
 4*|Q_i|*|K_j|*d over the executed (query block, selected key block) pairs with
@@ -47,8 +51,12 @@ def log(*a):
 def parse():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=40)
+    p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--settle-ms", type=float, default=100.0,
+                   help="untimed steps for at least this long before the warmup steps: the "
+                        "GPU's clocks take tens of ms of sustained load to reach their "
+                        "steady state")
     p.add_argument("--sets", type=int, default=4, help="rotated input sets (cache-cold timing)")
     p.add_argument("--workload", default="wan_layer_bf16",
                    choices=["wan_layer_bf16", "full_depth_bf16"])
@@ -209,6 +217,15 @@ def main():
         return sum(flops[i]["absorb"] + flops[i]["score_select"] + flops[i]["sparse_swa"]
                    for i in idx)
 
+    settled = 0
+    if args.settle_ms > 0:
+        t0 = time.perf_counter()
+        while (time.perf_counter() - t0) * 1e3 < args.settle_ms:
+            for _ in range(10):
+                run(settled)
+                settled += 1
+            torch.cuda.synchronize()
+        log(f"[bench] settled: {settled} untimed steps in {(time.perf_counter() - t0) * 1e3:.0f} ms")
     for k in range(args.warmup):
         run(k)
     torch.cuda.synchronize()
@@ -330,6 +347,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_steps": settled,
         "ms_per_step": round(ms_step, 5),
         "ms_per_chunk_per_layer": round(ms_step / per_step_layers, 5),
         "higher_is_better": True,

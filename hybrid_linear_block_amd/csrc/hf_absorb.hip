@@ -31,7 +31,7 @@ __global__ __launch_bounds__(RED_THREADS) void absorb_reduce(const float* __rest
                                                              int n_split, float* __restrict__ S,
                                                              float* __restrict__ z,
                                                              uint16_t* __restrict__ s_split) {
-  absorb_reduce_group<D>(blockIdx.x, blockIdx.y, partials, n_split, S, z, s_split);
+  absorb_reduce_group<D>(blockIdx.x, blockIdx.y, partials, n_split, S, z, s_split, threadIdx.x);
 }
 
 template <int D>
@@ -51,9 +51,7 @@ __global__ __launch_bounds__((absorb::threads<T, D>())) void absorb_parts(
 
 }  // namespace
 
-// Compute units of the current device, cached per device (the split plan aims at one
-// resident workgroup per compute unit).
-static int device_cu_count() {
+int device_cu_count() {
   static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;

@@ -7,6 +7,9 @@
 
 namespace hf {
 
+// Compute units of the current device (cached per device).
+int device_cu_count();
+
 // ---- absorb: S += V^T phi(K), z += sum phi(K) ------------------------------------
 constexpr int kAbsorbMaxSplits = 24;
 struct AbsorbPlan {

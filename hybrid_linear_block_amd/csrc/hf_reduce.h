@@ -44,7 +44,7 @@ __device__ __forceinline__ void store_split(uint16_t* s_split, int h, int e4, fl
   *reinterpret_cast<uint2*>(dst + D * D) = lo;
 }
 
-// Workgroup `grp` of head h (RED_THREADS threads): each thread owns 4 consecutive
+// Group `grp` of head h (RED_THREADS threads, thread tid): each thread owns 4 consecutive
 // floats of the partial layout; the loads of a group of 4 splits are issued
 // together, then added in split order.
 template <int D>
@@ -52,9 +52,10 @@ __device__ __forceinline__ void absorb_reduce_group(int grp, int h,
                                                     const float* __restrict__ partials,
                                                     int n_split, float* __restrict__ S,
                                                     float* __restrict__ z,
-                                                    uint16_t* __restrict__ s_split) {
+                                                    uint16_t* __restrict__ s_split,
+                                                    int tid) {
   constexpr int P = part_floats<D>();
-  const int e4 = (grp * RED_THREADS + (int)threadIdx.x) * 4;
+  const int e4 = (grp * RED_THREADS + tid) * 4;
   if (e4 >= P) return;
   const float* p = partials + (size_t)h * n_split * P + e4;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);

@@ -9,8 +9,8 @@
 // block_pool  (HBM-bound): one wave per (head, block) streams the block's rows
 //             once with 16-byte coalesced loads (all in flight together) and
 //             writes the fp32 row mean.
-// score_select (latency-bound): one workgroup per (4 query blocks, head) forms
-//             their scores against all key blocks (one thread per key block),
+// score_select (latency-bound): one workgroup per (5 query blocks, head) forms
+//             their scores against all key blocks (four lanes per key block),
 //             then one wave per query block selects the top_k exactly on an
 //             order-preserving uint32 key of the fp32 score (-0.0 counts as
 //             +0.0), ties going to the lower index, and writes the kept indices
@@ -109,13 +109,20 @@ __global__ __launch_bounds__((absorb::threads<T, D>())) void absorb_and_pool(
   if ((int)blockIdx.x < n_abs) {
     absorb::item<T, D>(blockIdx.x, n_split, kev, vev, n_ev, ev_hs, tps, partials);
   } else {
+    // The pooling workgroups are as many as fit next to the absorb's (the launcher
+    // sizes them), and each wave pools every n_waves-th block, so that all of the
+    // pooling streams from the start instead of waiting for free slots.
     constexpr int WPG = absorb::threads<T, D>() / 64;  // pooling waves per workgroup
-    pool_wave<T, D>(((int)blockIdx.x - n_abs) * WPG + (threadIdx.x >> 6), q, n_q, q_hs, k, n_kv,
-                    kv_hs, block, nqb, nkb, heads, pooled_q, pooled_k, nqb_cap, nkb_cap);
+    const int n_waves = ((int)gridDim.x - n_abs) * WPG;
+    const int total = heads * (nqb + nkb);
+    for (int wid = ((int)blockIdx.x - n_abs) * WPG + (int)(threadIdx.x >> 6); wid < total;
+         wid += n_waves)
+      pool_wave<T, D>(wid, q, n_q, q_hs, k, n_kv, kv_hs, block, nqb, nkb, heads, pooled_q,
+                      pooled_k, nqb_cap, nkb_cap);
   }
 }
 
-constexpr int SEL_THREADS = 256;
+constexpr int SEL_THREADS = 1024;  // 16 waves: the score phase, then 4 of them select
 
 // Order-preserving map of an fp32 score to uint32 (larger score -> larger key).
 __device__ __forceinline__ uint32_t score_key(float s) {
@@ -124,9 +131,9 @@ __device__ __forceinline__ uint32_t score_key(float s) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-constexpr int SEL_QB = SEL_THREADS / 64;  // query blocks per workgroup, one wave each
+constexpr int SEL_QB = 5;  // query blocks per workgroup, one selecting wave each
 
-// Scores of SEL_QB query blocks against all key blocks (one thread per key block,
+// Scores of SEL_QB query blocks against all key blocks (four lanes per key block,
 // fixed-order dot products), then one wave per query block selects exactly:
 // T = the top_k-th largest key is found bit by bit (count of keys >= candidate by
 // ballots), every key above T is kept, and keys equal to T are kept in ascending
@@ -151,12 +158,13 @@ __device__ __forceinline__ void select_group(
   __syncthreads();
   // Four adjacent lanes per key block, each over a quarter of the features (the
   // block's row is read as four contiguous segments); the quarters are added with
-  // two lane exchanges, which give every lane of the four the same sum.
+  // two lane exchanges, which give every lane of the four the same sum. One pass
+  // covers SEL_THREADS / 4 key blocks (256), so the pooled key rows' load latency is
+  // paid once.
   constexpr int PARTS = 4, EV = D / 4 / PARTS;  // float4s per quarter
   static_assert(SEL_THREADS % PARTS == 0, "a key block's lanes stay in one pass");
-  const int part = tid % PARTS;
   for (int x = tid; x < nkb * PARTS; x += SEL_THREADS) {
-    const int j = x / PARTS;
+    const int j = x / PARTS, part = x % PARTS;
     const float4* km =
         reinterpret_cast<const float4*>(pooled_k + ((size_t)h * nkb_cap + j) * D) + part * EV;
     float4 kv[EV];
@@ -165,6 +173,9 @@ __device__ __forceinline__ void select_group(
     float sq[SEL_QB];
 #pragma unroll
     for (int r = 0; r < SEL_QB; ++r) {
+      // Query row r's reads stay here (all rows hoisted at once would not fit the
+      // registers of a 1024-thread workgroup and would serialise the loads above).
+      asm volatile("" ::: "memory");
       float s = 0.f;
 #pragma unroll
       for (int e = 0; e < EV; ++e) {
@@ -235,9 +246,13 @@ __global__ __launch_bounds__(SEL_THREADS) void score_select(
 }
 
 // The selection and the absorb's reduce in one launch: workgroups below n_sel
-// select (n_qg groups of query blocks per head), the others reduce (red_groups per
-// head). They read and write different buffers.
-static_assert(SEL_THREADS == RED_THREADS, "one workgroup size for both parts");
+// select (n_qg groups of query blocks per head), the others reduce (red_wgs per
+// head, RED_PER_WG reduce groups each). They read and write different buffers.
+// A workgroup of the reduce part runs SEL_THREADS / RED_THREADS reduce groups.
+constexpr int RED_PER_WG = SEL_THREADS / RED_THREADS;
+static_assert(SEL_THREADS % RED_THREADS == 0, "whole reduce groups per workgroup");
+template <int D>
+constexpr int red_wgs() { return (red_groups<D>() + RED_PER_WG - 1) / RED_PER_WG; }
 template <int D, int NE>
 __global__ __launch_bounds__(SEL_THREADS) void select_and_reduce(
     const float* __restrict__ pooled_q, const float* __restrict__ pooled_k, int nqb, int nkb,
@@ -249,8 +264,10 @@ __global__ __launch_bounds__(SEL_THREADS) void select_and_reduce(
                         nkb, nqb_cap, nkb_cap, scale, top_k, sel, nullptr);
   } else {
     const int r = (int)blockIdx.x - n_sel;
-    absorb_reduce_group<D>(r % red_groups<D>(), r / red_groups<D>(), partials, n_split, S, z,
-                           s_split);
+    const int grp = (r % red_wgs<D>()) * RED_PER_WG + (int)threadIdx.x / RED_THREADS;
+    if (grp < red_groups<D>())
+      absorb_reduce_group<D>(grp, r / red_wgs<D>(), partials, n_split, S, z, s_split,
+                             (int)threadIdx.x % RED_THREADS);
   }
 }
 
@@ -277,6 +294,21 @@ hipError_t launch_block_pool(int dtype, int heads, int d, int block, const void*
   return hipGetLastError();
 }
 
+// Pooling workgroups of an absorb_and_pool launch: the resident slots the absorb's
+// n_abs workgroups leave free (at least one per compute unit), at most `needed`.
+template <typename K>
+int pool_workgroups(K kernel, int threads, int n_abs, int needed) {
+  int dev = 0, occ = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, threads, 0) != hipSuccess ||
+      occ < 1)
+    occ = 1;
+  const int n_cu = device_cu_count();
+  int n = occ * n_cu - n_abs;
+  if (n < n_cu) n = n_cu;
+  return n < needed ? n : needed;
+}
+
 hipError_t launch_absorb_and_pool(int dtype, int heads, int d, int block, const void* k_ev,
                                   const void* v_ev, int64_t n_ev, int64_t ev_hs, float* partials,
                                   const void* q, int64_t n_q, int64_t q_hs, const void* k,
@@ -289,7 +321,8 @@ hipError_t launch_absorb_and_pool(int dtype, int heads, int d, int block, const 
 #define HF_ABSPOOL(T, D)                                                                       \
   {                                                                                            \
     constexpr int wpg = absorb::threads<T, D>() / 64;                                          \
-    const int n_pool = (heads * (nqb + nkb) + wpg - 1) / wpg;                                  \
+    const int n_pool = pool_workgroups(absorb_and_pool<T, D>, absorb::threads<T, D>(), n_abs, \
+                                       (heads * (nqb + nkb) + wpg - 1) / wpg);                 \
     absorb_and_pool<T, D><<<n_abs + n_pool, absorb::threads<T, D>(), 0, stream>>>(             \
         static_cast<const T*>(k_ev), static_cast<const T*>(v_ev), n_ev, ev_hs,                 \
         p.tokens_per_split, p.n_split, partials, n_abs, static_cast<const T*>(q), n_q, q_hs,   \
@@ -331,7 +364,7 @@ hipError_t launch_select_and_reduce(int dtype, int heads, int d, int nqb, int nk
   const int n_sel = n_qg * heads;
   const int n_split = absorb_plan(dtype, heads, d, n_ev).n_split;
 #define HF_SELRED(D, NE)                                                                    \
-  select_and_reduce<D, NE><<<n_sel + red_groups<D>() * heads, SEL_THREADS, 0, stream>>>(    \
+  select_and_reduce<D, NE><<<n_sel + red_wgs<D>() * heads, SEL_THREADS, 0, stream>>>(        \
       pooled_q, pooled_k, nqb, nkb, nqb_cap, nkb_cap, scale, top_k, sel, n_qg, n_sel,       \
       partials, n_split, S, z, s_split)
   if (d == 128) {

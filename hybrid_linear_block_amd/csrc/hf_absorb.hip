@@ -25,7 +25,7 @@ namespace hf {
 
 namespace {
 
-// Second pass (absorb_reduce_group, shared with the pooling launch).
+// Second pass (absorb_reduce_group, shared with the selection launch).
 template <int D>
 __global__ __launch_bounds__(RED_THREADS) void absorb_reduce(const float* __restrict__ partials,
                                                              int n_split, float* __restrict__ S,

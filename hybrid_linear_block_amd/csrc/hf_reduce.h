@@ -2,7 +2,7 @@
 // splits added in order, and the bf16 hi/lo split of the new S (gfx950).
 //
 // Shared by the absorb_reduce kernel and by the kernel that runs it next to the
-// block pooling in one launch (the two are independent and both bound by memory).
+// top-K selection in one launch (the two read and write different buffers).
 // The sums are those of the absorb of evicted tokens into the linear state (the
 // gist.science English summary "Long-Horizon Streaming Video Generation via
 // Hybrid Attention with Decoupled Distillation", 2.A.1).
@@ -18,7 +18,7 @@ constexpr int RED_THREADS = 256;
 template <int D>
 constexpr int part_floats() { return D * D + D; }
 
-// Workgroups per head of the reduce.
+// Groups of RED_THREADS threads per head of the reduce.
 template <int D>
 constexpr int red_groups() { return (part_floats<D>() / 4 + RED_THREADS - 1) / RED_THREADS; }
 

@@ -15,6 +15,9 @@
 //             order-preserving uint32 key of the fp32 score (-0.0 counts as
 //             +0.0), ties going to the lower index, and writes the kept indices
 //             in ascending order.
+// absorb_and_pool / select_and_reduce: the same pooling and selection with the
+//             absorb's partial states (first) and its reduce (second) as extra
+//             workgroups of the launch, for the one-stream combined call.
 #include "hf_absorb_parts.h"
 #include "hf_device.h"
 #include "hf_launch.h"

@@ -18,6 +18,8 @@
 // absorb_and_pool / select_and_reduce: the same pooling and selection with the
 //             absorb's partial states (first) and its reduce (second) as extra
 //             workgroups of the launch, for the one-stream combined call.
+#include <atomic>
+
 #include "hf_absorb_parts.h"
 #include "hf_device.h"
 #include "hf_launch.h"
@@ -299,13 +301,19 @@ hipError_t launch_block_pool(int dtype, int heads, int d, int block, const void*
 
 // Pooling workgroups of an absorb_and_pool launch: the resident slots the absorb's
 // n_abs workgroups leave free (at least one per compute unit), at most `needed`.
+// `occ_cache` (one per kernel instance) keeps the occupancy per device.
 template <typename K>
-int pool_workgroups(K kernel, int threads, int n_abs, int needed) {
+int pool_workgroups(K kernel, int threads, int n_abs, int needed,
+                    std::atomic<int> (&occ_cache)[64]) {
   int dev = 0, occ = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, threads, 0) != hipSuccess ||
-      occ < 1)
-    occ = 1;
+  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64)
+    occ = occ_cache[dev].load(std::memory_order_relaxed);
+  if (occ < 1) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, threads, 0) != hipSuccess ||
+        occ < 1)
+      occ = 1;
+    if (dev >= 0 && dev < 64) occ_cache[dev].store(occ, std::memory_order_relaxed);
+  }
   const int n_cu = device_cu_count();
   int n = occ * n_cu - n_abs;
   if (n < n_cu) n = n_cu;
@@ -324,8 +332,9 @@ hipError_t launch_absorb_and_pool(int dtype, int heads, int d, int block, const 
 #define HF_ABSPOOL(T, D)                                                                       \
   {                                                                                            \
     constexpr int wpg = absorb::threads<T, D>() / 64;                                          \
+    static std::atomic<int> occ_cache[64];                                                     \
     const int n_pool = pool_workgroups(absorb_and_pool<T, D>, absorb::threads<T, D>(), n_abs, \
-                                       (heads * (nqb + nkb) + wpg - 1) / wpg);                 \
+                                       (heads * (nqb + nkb) + wpg - 1) / wpg, occ_cache);      \
     absorb_and_pool<T, D><<<n_abs + n_pool, absorb::threads<T, D>(), 0, stream>>>(             \
         static_cast<const T*>(k_ev), static_cast<const T*>(v_ev), n_ev, ev_hs,                 \
         p.tokens_per_split, p.n_split, partials, n_abs, static_cast<const T*>(q), n_q, q_hs,   \

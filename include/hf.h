@@ -116,7 +116,8 @@ hf_status hf_state_init(const hf_config* cfg, float* S, float* z, void* workspac
  * index of the first evicted token and must equal the state's next eviction
  * index (HF_ERR_STATE otherwise); on success the next index advances by n_ev.
  * n_ev == 0 is a valid no-op. The reduction order is fixed, so results are
- * bitwise reproducible. */
+ * bitwise reproducible on a given device type (the bf16 token split follows the
+ * device's compute-unit count). */
 hf_status hf_absorb_evicted(hf_state* st, const void* k_ev, const void* v_ev, int64_t n_ev,
                             int64_t ev_head_stride, int64_t ev_index, void* stream);
 

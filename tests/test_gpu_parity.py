@@ -134,8 +134,10 @@ def _sample_blocks(H, nqb, rng, extra=24):
     return sorted(blocks)
 
 
-def _check_layer(inp, top_k, seed, st=None, sel_expect=None):
-    """Absorb the evicted span, attend the chunk; compare with the oracle on samples."""
+def _check_layer(inp, top_k, seed, st=None, sel_expect=None, combined=False):
+    """Absorb the evicted span, attend the chunk; compare with the oracle on samples.
+    With `combined`, both go through one absorb_and_attend call on one stream (the
+    launch configuration bench.py times), else absorb_evicted then attend_chunk."""
     wl = synth.WORKLOADS["wan_layer_bf16"]
     H, d, B = wl.heads, wl.head_dim, wl.block
     qd, kd, vd = dev_bf16(inp["q"]), dev_bf16(inp["k"]), dev_bf16(inp["v"])
@@ -144,10 +146,14 @@ def _check_layer(inp, top_k, seed, st=None, sel_expect=None):
     if st is None:
         st = hla.HybridAttentionState(H, d, B, torch.bfloat16, max_n_q=n_q, max_n_kv=n_kv,
                                       max_n_ev=e1 - e0, max_top_k=top_k)
-    st.absorb_evicted(kd[:, e0:e1], vd[:, e0:e1])
     nqb = -(-n_q // B)
     sel = torch.empty((H, nqb, top_k), dtype=torch.int32, device="cuda")
-    out = st.attend_chunk(qd, kd[:, w0:w1], vd[:, w0:w1], top_k, sel_out=sel)
+    if combined:
+        out = st.absorb_and_attend(kd[:, e0:e1], vd[:, e0:e1], qd, kd[:, w0:w1], vd[:, w0:w1],
+                                   top_k, sel_out=sel)
+    else:
+        st.absorb_evicted(kd[:, e0:e1], vd[:, e0:e1])
+        out = st.attend_chunk(qd, kd[:, w0:w1], vd[:, w0:w1], top_k, sel_out=sel)
     torch.cuda.synchronize()
     q64 = oracle.as_f64(inp["q"], "bf16")
     k64 = oracle.as_f64(inp["k"], "bf16")
@@ -167,11 +173,14 @@ def _check_layer(inp, top_k, seed, st=None, sel_expect=None):
     return st, stats, int(differ.sum())
 
 
-def test_wan_layer_bf16():
+@pytest.mark.parametrize("combined", [False, True])
+def test_wan_layer_bf16(combined):
     wl = synth.WORKLOADS["wan_layer_bf16"]
     inp = synth.wan_layer_inputs(2024)
     K = synth.top_k_count(wl.top_k_frac, 220)
-    st, stats, n_diff = _check_layer(inp, K, seed=1)
+    print(f"wan layer, {'one absorb_and_attend call' if combined else 'separate calls'}",
+          flush=True)
+    st, stats, n_diff = _check_layer(inp, K, seed=1, combined=combined)
     print("wan layer", stats, "rows with near-tie differences:", n_diff, flush=True)
 
 

@@ -35,10 +35,21 @@ hipError_t launch_split_state(int heads, int d, const float* S, uint16_t* s_spli
 
 // ---- block pooling, scoring and top-K selection ----------------------------------
 constexpr int kMaxKeyBlocks = 2048;  // key blocks per window (selection LDS budget)
+// Cache of 8-row fp32 sums of K rows for the key-block means, kept across calls:
+// group g (rows 8g .. 8g+7 of the stream, counted from its first token) lives in
+// ring[h][g % cap][0..d). Groups in [lo, hi) are read from the ring; a launch with
+// a ring writes every other group of its window there (windows start on a group and
+// hold whole groups). ring == nullptr: no cache (every group is summed from K).
+struct KeyCache {
+  float* ring = nullptr;
+  int64_t cap = 1;  // groups per head, a power of two
+  int64_t g0 = 0;   // absolute group of window row 0
+  int64_t lo = 0, hi = 0;
+};
 hipError_t launch_block_pool(int dtype, int heads, int d, int block, const void* q, int64_t n_q,
                              int64_t q_hs, const void* k, int64_t n_kv, int64_t kv_hs,
                              float* pooled_q, float* pooled_k, int nqb_cap, int nkb_cap,
-                             hipStream_t stream);
+                             hipStream_t stream, const KeyCache& kc = KeyCache());
 // The partial-state pass of an absorb of n_ev evicted tokens (as in launch_absorb)
 // and launch_block_pool in one launch: the two read and write different buffers
 // and are both bound by memory. The absorb is complete once
@@ -47,7 +58,8 @@ hipError_t launch_absorb_and_pool(int dtype, int heads, int d, int block, const 
                                   const void* v_ev, int64_t n_ev, int64_t ev_hs, float* partials,
                                   const void* q, int64_t n_q, int64_t q_hs, const void* k,
                                   int64_t n_kv, int64_t kv_hs, float* pooled_q, float* pooled_k,
-                                  int nqb_cap, int nkb_cap, hipStream_t stream);
+                                  int nqb_cap, int nkb_cap, hipStream_t stream,
+                                  const KeyCache& kc = KeyCache());
 hipError_t launch_score_select(int heads, int d, int nqb, int nkb, int nqb_cap, int nkb_cap,
                                const float* pooled_q, const float* pooled_k, float scale,
                                int top_k, int32_t* sel, float* scores_out, hipStream_t stream);

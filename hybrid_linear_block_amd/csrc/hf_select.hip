@@ -31,19 +31,23 @@ namespace {
 
 constexpr int POOL_THREADS = 256;  // 4 waves, one (head, block) per wave
 
-// Row mean of one block per wave: lane (rg, cc) accumulates 16-byte column chunk
-// cc over rows rg, rg + RPI, ... (all loads independent), then the row groups are
-// added with lane exchanges in a fixed order.
-// Wave `wid` pools (head wid / (nqb + nkb), block wid % (nqb + nkb)); the Q blocks of
-// a head come first, then its key blocks.
+// Row mean of one block per wave, summed by 8-row groups: lane (rg, cc) owns the
+// 16-byte column chunk cc of the groups rg, rg + RPI, ... of the block (all row
+// loads in flight together), adds each group's 8 rows in row order, adds its groups
+// in order, and the lanes' totals are combined with lane exchanges in a fixed tree
+// (every lane ends with the same sum). A key block's group sums can come from, and
+// go to, a cache of 8-row sums (KeyCache), which gives the same sums bit for bit.
 template <typename T, int D>
 __device__ __forceinline__ void pool_wave(
     int wid, const T* __restrict__ q, int64_t n_q, int64_t q_hs, const T* __restrict__ k,
     int64_t n_kv, int64_t kv_hs, int block, int nqb, int nkb, int heads,
-    float* __restrict__ pooled_q, float* __restrict__ pooled_k, int nqb_cap, int nkb_cap) {
+    float* __restrict__ pooled_q, float* __restrict__ pooled_k, int nqb_cap, int nkb_cap,
+    const KeyCache& kc) {
   constexpr int VEC = 16 / sizeof(T);  // elements per 16-byte chunk
   constexpr int CPR = D / VEC;         // chunks per row
-  constexpr int RPI = 64 / CPR;        // rows per wave-wide load
+  constexpr int RPI = 64 / CPR;        // lane groups (rows per wave-wide load)
+  constexpr int GPL = 8 / RPI;         // 8-row groups per lane (blocks have at most 64 rows)
+  static_assert(RPI >= 1 && RPI <= 8 && 8 % RPI == 0, "lane groups per 8-row group");
   const int lane = threadIdx.x & 63;
   if (wid >= heads * (nqb + nkb)) return;
   const int h = wid / (nqb + nkb), b = wid % (nqb + nkb);
@@ -54,30 +58,66 @@ __device__ __forceinline__ void pool_wave(
   const int64_t r0 = (int64_t)blk * block;
   const int64_t r1 = r0 + block < n ? r0 + block : n;
   const int cc = lane % CPR, rg = lane / CPR;
-  float acc[VEC];
+  // Group i of this lane: rows r0 + 8 (rg + RPI i) + 0..7; cached iff it is a key
+  // group whose absolute index is in the cache's range.
+  const bool use_cache = !is_q && kc.ring != nullptr;  // wave-uniform
+  bool cached[GPL];
+  int64_t gabs[GPL];
 #pragma unroll
-  for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
-  constexpr int MAXIT = 64 / RPI;  // blocks have at most 64 rows
-  uint4 x[MAXIT];
-#pragma unroll
-  for (int u = 0; u < MAXIT; ++u) {
-    const int64_t r = r0 + rg + u * RPI;
-    x[u] = ld16(base + r * D + cc * VEC, r < r1);  // rows past the block read nothing
+  for (int i = 0; i < GPL; ++i) {
+    const int64_t row0 = r0 + 8 * (rg + RPI * i);
+    gabs[i] = kc.g0 + row0 / 8;
+    cached[i] = use_cache && row0 < r1 && gabs[i] >= kc.lo && gabs[i] < kc.hi;
   }
+  uint4 x[GPL][8];
 #pragma unroll
-  for (int u = 0; u < MAXIT; ++u) {
-    if constexpr (sizeof(T) == 2) {
+  for (int i = 0; i < GPL; ++i)
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) acc[e] += bf16_to_f32(half16(x[u], e));
+    for (int r = 0; r < 8; ++r) {
+      const int64_t row = r0 + 8 * (rg + RPI * i) + r;
+      x[i][r] = ld16(base + row * D + cc * VEC, row < r1 && !cached[i]);  // past the block: 0
+    }
+  float tot[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) tot[e] = 0.f;
+#pragma unroll
+  for (int i = 0; i < GPL; ++i) {
+    float g8[VEC];
+    float* slot = nullptr;
+    if (use_cache)
+      slot = kc.ring + ((size_t)h * kc.cap + (size_t)(gabs[i] & (kc.cap - 1))) * D + cc * VEC;
+    if (cached[i]) {
+#pragma unroll
+      for (int e = 0; e < VEC; e += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(slot + e);
+        g8[e] = v.x, g8[e + 1] = v.y, g8[e + 2] = v.z, g8[e + 3] = v.w;
+      }
     } else {
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) acc[e] += __uint_as_float(word(x[u], e));
+      for (int e = 0; e < VEC; ++e) g8[e] = 0.f;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) g8[e] += bf16_to_f32(half16(x[i][r], e));
+        } else {
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) g8[e] += __uint_as_float(word(x[i][r], e));
+        }
+      }
+      if (use_cache && r0 + 8 * (rg + RPI * i) < r1) {  // a key group of the window
+#pragma unroll
+        for (int e = 0; e < VEC; e += 4)
+          *reinterpret_cast<float4*>(slot + e) = make_float4(g8[e], g8[e + 1], g8[e + 2], g8[e + 3]);
+      }
     }
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) tot[e] += g8[e];
   }
 #pragma unroll
   for (int off = CPR; off < 64; off <<= 1)
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) acc[e] += __shfl_xor(acc[e], off);
+    for (int e = 0; e < VEC; ++e) tot[e] += __shfl_xor(tot[e], off);
   if (rg == 0) {
     const float inv = 1.f / (float)(r1 - r0);
     float* dst = is_q ? pooled_q + ((size_t)h * nqb_cap + blk) * D
@@ -85,7 +125,7 @@ __device__ __forceinline__ void pool_wave(
 #pragma unroll
     for (int e = 0; e < VEC; e += 4)
       *reinterpret_cast<float4*>(dst + cc * VEC + e) =
-          make_float4(acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv);
+          make_float4(tot[e] * inv, tot[e + 1] * inv, tot[e + 2] * inv, tot[e + 3] * inv);
   }
 }
 
@@ -93,9 +133,9 @@ template <typename T, int D>
 __global__ __launch_bounds__(POOL_THREADS) void block_pool(
     const T* __restrict__ q, int64_t n_q, int64_t q_hs, const T* __restrict__ k, int64_t n_kv,
     int64_t kv_hs, int block, int nqb, int nkb, int heads, float* __restrict__ pooled_q,
-    float* __restrict__ pooled_k, int nqb_cap, int nkb_cap) {
+    float* __restrict__ pooled_k, int nqb_cap, int nkb_cap, KeyCache kc) {
   pool_wave<T, D>(blockIdx.x * (POOL_THREADS / 64) + (threadIdx.x >> 6), q, n_q, q_hs, k, n_kv,
-                  kv_hs, block, nqb, nkb, heads, pooled_q, pooled_k, nqb_cap, nkb_cap);
+                  kv_hs, block, nqb, nkb, heads, pooled_q, pooled_k, nqb_cap, nkb_cap, kc);
 }
 
 // The absorb's partial states and the block pooling in one launch: workgroups
@@ -110,7 +150,7 @@ __global__ __launch_bounds__((absorb::threads<T, D>())) void absorb_and_pool(
     int n_split, float* __restrict__ partials, int n_abs, const T* __restrict__ q, int64_t n_q,
     int64_t q_hs, const T* __restrict__ k, int64_t n_kv, int64_t kv_hs, int block, int nqb,
     int nkb, int heads, float* __restrict__ pooled_q, float* __restrict__ pooled_k, int nqb_cap,
-    int nkb_cap) {
+    int nkb_cap, KeyCache kc) {
   if ((int)blockIdx.x < n_abs) {
     absorb::item<T, D>(blockIdx.x, n_split, kev, vev, n_ev, ev_hs, tps, partials);
   } else {
@@ -123,7 +163,7 @@ __global__ __launch_bounds__((absorb::threads<T, D>())) void absorb_and_pool(
     for (int wid = ((int)blockIdx.x - n_abs) * WPG + (int)(threadIdx.x >> 6); wid < total;
          wid += n_waves)
       pool_wave<T, D>(wid, q, n_q, q_hs, k, n_kv, kv_hs, block, nqb, nkb, heads, pooled_q,
-                      pooled_k, nqb_cap, nkb_cap);
+                      pooled_k, nqb_cap, nkb_cap, kc);
   }
 }
 
@@ -281,7 +321,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_and_reduce(
 hipError_t launch_block_pool(int dtype, int heads, int d, int block, const void* q, int64_t n_q,
                              int64_t q_hs, const void* k, int64_t n_kv, int64_t kv_hs,
                              float* pooled_q, float* pooled_k, int nqb_cap, int nkb_cap,
-                             hipStream_t stream) {
+                             hipStream_t stream, const KeyCache& kc) {
   const int nqb = (int)((n_q + block - 1) / block);
   const int nkb = (int)((n_kv + block - 1) / block);
   const int waves = heads * (nqb + nkb);
@@ -289,7 +329,7 @@ hipError_t launch_block_pool(int dtype, int heads, int d, int block, const void*
 #define HF_POOL(T, D)                                                                        \
   block_pool<T, D><<<grid, POOL_THREADS, 0, stream>>>(                                       \
       static_cast<const T*>(q), n_q, q_hs, static_cast<const T*>(k), n_kv, kv_hs, block, nqb, \
-      nkb, heads, pooled_q, pooled_k, nqb_cap, nkb_cap)
+      nkb, heads, pooled_q, pooled_k, nqb_cap, nkb_cap, kc)
   if (dtype == 0) {
     if (d == 128) HF_POOL(bf16_t, 128); else HF_POOL(bf16_t, 64);
   } else {
@@ -324,7 +364,8 @@ hipError_t launch_absorb_and_pool(int dtype, int heads, int d, int block, const 
                                   const void* v_ev, int64_t n_ev, int64_t ev_hs, float* partials,
                                   const void* q, int64_t n_q, int64_t q_hs, const void* k,
                                   int64_t n_kv, int64_t kv_hs, float* pooled_q, float* pooled_k,
-                                  int nqb_cap, int nkb_cap, hipStream_t stream) {
+                                  int nqb_cap, int nkb_cap, hipStream_t stream,
+                                  const KeyCache& kc) {
   const int nqb = (int)((n_q + block - 1) / block);
   const int nkb = (int)((n_kv + block - 1) / block);
   const AbsorbPlan p = absorb_plan(dtype, heads, d, n_ev);
@@ -339,7 +380,7 @@ hipError_t launch_absorb_and_pool(int dtype, int heads, int d, int block, const 
         static_cast<const T*>(k_ev), static_cast<const T*>(v_ev), n_ev, ev_hs,                 \
         p.tokens_per_split, p.n_split, partials, n_abs, static_cast<const T*>(q), n_q, q_hs,   \
         static_cast<const T*>(k), n_kv, kv_hs, block, nqb, nkb, heads, pooled_q, pooled_k,     \
-        nqb_cap, nkb_cap);                                                                     \
+        nqb_cap, nkb_cap, kc);                                                                 \
   }
   if (dtype == 0) {
     if (d == 128) HF_ABSPOOL(bf16_t, 128) else HF_ABSPOOL(bf16_t, 64)

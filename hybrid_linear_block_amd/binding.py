@@ -59,6 +59,12 @@ def _load():
                                     c_int64, P, P]),
         "hf_absorb_and_attend": (c_int, [P, P, P, c_int64, c_int64, c_int64, P, c_int64, c_int64,
                                          P, P, c_int64, c_int64, c_int32, P, c_int64, P, P, P]),
+        "hf_attend_chunk_cached": (c_int, [P, P, c_int64, c_int64, P, P, c_int64, c_int64,
+                                           c_int64, c_int32, P, c_int64, P, P]),
+        "hf_absorb_and_attend_cached": (c_int, [P, P, P, c_int64, c_int64, c_int64, P, c_int64,
+                                                c_int64, P, P, c_int64, c_int64, c_int64, c_int32,
+                                                P, c_int64, P, P]),
+        "hf_key_cache_reset": (c_int, [P]),
         "hf_block_scores": (c_int, [P, P, c_int64, c_int64, P, c_int64, c_int64, P, P]),
         "hf_profile_start": (c_int, [P, c_int32]),
         "hf_profile_stop": (c_int, [P, POINTER(ctypes.c_double), POINTER(c_int32)]),
@@ -76,8 +82,9 @@ def _load():
 _lib = _load()
 
 EXPORTED = ("hf_workspace_bytes", "hf_state_init", "hf_absorb_evicted", "hf_attend_chunk",
-            "hf_absorb_and_attend", "hf_block_scores", "hf_profile_start", "hf_profile_stop", "hf_next_ev_index",
-            "hf_state_destroy", "hf_status_string")
+            "hf_absorb_and_attend", "hf_attend_chunk_cached", "hf_absorb_and_attend_cached",
+            "hf_key_cache_reset", "hf_block_scores", "hf_profile_start", "hf_profile_stop",
+            "hf_next_ev_index", "hf_state_destroy", "hf_status_string")
 HF_KERNEL_NAMES = ("absorb", "block_pool", "score_select", "sparse_swa")
 
 
@@ -125,6 +132,29 @@ def hf_absorb_and_attend(state: int, k_ev: int, v_ev: int, n_ev: int, ev_head_st
     return _lib.hf_absorb_and_attend(state, k_ev, v_ev, n_ev, ev_head_stride, ev_index, q, n_q,
                                      q_head_stride, k_win, v_win, n_kv, kv_head_stride, top_k,
                                      out, out_head_stride, sel_out, stream, side_stream)
+
+
+def hf_attend_chunk_cached(state: int, q: int, n_q: int, q_head_stride: int, k_win: int,
+                           v_win: int, n_kv: int, kv_head_stride: int, win_index: int, top_k: int,
+                           out: int, out_head_stride: int, sel_out: int, stream: int) -> int:
+    return _lib.hf_attend_chunk_cached(state, q, n_q, q_head_stride, k_win, v_win, n_kv,
+                                       kv_head_stride, win_index, top_k, out, out_head_stride,
+                                       sel_out, stream)
+
+
+def hf_absorb_and_attend_cached(state: int, k_ev: int, v_ev: int, n_ev: int, ev_head_stride: int,
+                                ev_index: int, q: int, n_q: int, q_head_stride: int, k_win: int,
+                                v_win: int, n_kv: int, kv_head_stride: int, win_index: int,
+                                top_k: int, out: int, out_head_stride: int, sel_out: int,
+                                stream: int) -> int:
+    return _lib.hf_absorb_and_attend_cached(state, k_ev, v_ev, n_ev, ev_head_stride, ev_index, q,
+                                            n_q, q_head_stride, k_win, v_win, n_kv,
+                                            kv_head_stride, win_index, top_k, out,
+                                            out_head_stride, sel_out, stream)
+
+
+def hf_key_cache_reset(state: int) -> int:
+    return _lib.hf_key_cache_reset(state)
 
 
 def hf_block_scores(state: int, q: int, n_q: int, q_head_stride: int, k_win: int, n_kv: int,

@@ -27,6 +27,10 @@ struct hf_state {
   int32_t* sel;
   float* partials;
   uint16_t* s_split;  // bf16 hi/lo split of S (bf16 states), kept in step with S
+  // Cache of 8-token key sums for the cached calls: ring of kc_cap groups per head;
+  // the absolute groups [kc_lo, kc_hi) hold the sums of the last cached window.
+  float* kcache;
+  int64_t kc_cap = 1, kc_lo = 0, kc_hi = 0;
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;  // hf_absorb_and_attend's fork / join
   // Per-kernel timing (hf_profile_start / hf_profile_stop).
   bool prof_on = false;
@@ -67,7 +71,8 @@ hf_status check_config(const hf_config* c) {
 }
 
 struct Layout {
-  size_t pooled_q, pooled_k, sel, partials, s_split, total;
+  size_t pooled_q, pooled_k, sel, partials, s_split, kcache, total;
+  int64_t kc_cap;  // groups per head of the key-sum cache (a power of two)
 };
 
 Layout layout(const hf_config* c) {
@@ -86,6 +91,11 @@ Layout layout(const hf_config* c) {
   off += round_up(hf::absorb_partial_floats((int)H, (int)d) * 4);
   L.s_split = off;
   if (c->dtype == HF_BF16) off += round_up(H * 2 * d * d * 2);
+  // The cache holds every 8-token group of the largest window.
+  L.kc_cap = 1;
+  while (L.kc_cap < ceil_div(c->max_n_kv, 8)) L.kc_cap *= 2;
+  L.kcache = off;
+  off += round_up(H * (size_t)L.kc_cap * d * 4);
   L.total = off;
   return L;
 }
@@ -181,6 +191,8 @@ hf_status hf_state_init(const hf_config* cfg, float* S, float* z, void* workspac
   st->sel = reinterpret_cast<int32_t*>(st->ws + L.sel);
   st->partials = reinterpret_cast<float*>(st->ws + L.partials);
   st->s_split = cfg->dtype == HF_BF16 ? reinterpret_cast<uint16_t*>(st->ws + L.s_split) : nullptr;
+  st->kcache = reinterpret_cast<float*>(st->ws + L.kcache);
+  st->kc_cap = L.kc_cap;
   if (hipGetDevice(&st->device) != hipSuccess) {
     delete st;
     return HF_ERR_HIP;
@@ -269,6 +281,24 @@ static hf_status check_attend_all(const hf_state* st, const void* q, int64_t n_q
   return HF_OK;
 }
 
+// Window of a cached call: it starts on an 8-token group of the stream and holds
+// whole groups (the block size is a multiple of 8 in every configuration).
+static hf_status check_window(int64_t win_index, int64_t n_kv) {
+  if (win_index < 0 || win_index % 8 != 0 || n_kv % 8 != 0) return HF_ERR_INVALID_ARG;
+  return HF_OK;
+}
+
+// The key-sum cache for a call over the window [win_index, win_index + n_kv).
+static hf::KeyCache key_cache(const hf_state* st, int64_t win_index) {
+  hf::KeyCache kc;
+  kc.ring = st->kcache;
+  kc.cap = st->kc_cap;
+  kc.g0 = win_index / 8;
+  kc.lo = st->kc_lo;
+  kc.hi = st->kc_hi;
+  return kc;
+}
+
 // Evicted tokens that an attend call absorbs in its own launches.
 struct FusedAbsorb {
   const void* k_ev;
@@ -286,21 +316,28 @@ static hipError_t enqueue_attend(hf_state* st, const void* q, int64_t n_q, int64
                                  const void* k_win, const void* v_win, int64_t n_kv,
                                  int64_t kv_hs, int32_t top_k, void* out, int64_t out_hs,
                                  int32_t* sel_out, hipStream_t s, hipEvent_t join,
-                                 const FusedAbsorb* fa = nullptr, bool* absorbed = nullptr) {
+                                 const FusedAbsorb* fa = nullptr, bool* absorbed = nullptr,
+                                 const hf::KeyCache* kc = nullptr) {
   const hf_config& c = st->cfg;
   const int nqb = (int)ceil_div(n_q, c.block_size);
   const int nkb = (int)ceil_div(n_kv, c.block_size);
   int32_t* sel = sel_out ? sel_out : st->sel;
   hipError_t r = timed(st, HF_KERNEL_BLOCK_POOL, s, [&]() {
+    const hf::KeyCache none;
+    const hf::KeyCache& kcr = kc ? *kc : none;
     if (fa)
       return hf::launch_absorb_and_pool(c.dtype, c.num_heads, c.head_dim, c.block_size, fa->k_ev,
                                         fa->v_ev, fa->n_ev, fa->head_stride, st->partials, q, n_q,
                                         q_hs, k_win, n_kv, kv_hs, st->pooled_q, st->pooled_k,
-                                        st->nqb_cap, st->nkb_cap, s);
+                                        st->nqb_cap, st->nkb_cap, s, kcr);
     return hf::launch_block_pool(c.dtype, c.num_heads, c.head_dim, c.block_size, q, n_q, q_hs,
                                  k_win, n_kv, kv_hs, st->pooled_q, st->pooled_k, st->nqb_cap,
-                                 st->nkb_cap, s);
+                                 st->nkb_cap, s, kcr);
   });
+  if (r == hipSuccess && kc) {  // the pooling launch sums (or reads) every group of the window
+    st->kc_lo = kc->g0;
+    st->kc_hi = kc->g0 + n_kv / 8;
+  }
   if (r == hipSuccess)
     r = timed(st, HF_KERNEL_SCORE_SELECT, s, [&]() {
       if (fa)
@@ -383,6 +420,65 @@ hf_status hf_absorb_and_attend(hf_state* st, const void* k_ev, const void* v_ev,
   });
   if (absorbed) st->next_ev += n_ev;  // the absorb is enqueued and will run
   return r;
+}
+
+hf_status hf_attend_chunk_cached(hf_state* st, const void* q, int64_t n_q, int64_t q_head_stride,
+                                 const void* k_win, const void* v_win, int64_t n_kv,
+                                 int64_t kv_head_stride, int64_t win_index, int32_t top_k,
+                                 void* out, int64_t out_head_stride, int32_t* sel_out,
+                                 void* stream) {
+  if (!st) return HF_ERR_INVALID_ARG;
+  hf_status e = check_attend_all(st, q, n_q, q_head_stride, k_win, v_win, n_kv, kv_head_stride,
+                                 top_k, out, out_head_stride, sel_out);
+  if (e == HF_OK && n_q > 0) e = check_window(win_index, n_kv);
+  if (e != HF_OK || n_q == 0) return e;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hf::KeyCache kc = key_cache(st, win_index);
+  return on_device(st->device, [&]() {
+    return enqueue_attend(st, q, n_q, q_head_stride, k_win, v_win, n_kv, kv_head_stride, top_k,
+                          out, out_head_stride, sel_out, s, nullptr, nullptr, nullptr, &kc);
+  });
+}
+
+hf_status hf_absorb_and_attend_cached(hf_state* st, const void* k_ev, const void* v_ev,
+                                      int64_t n_ev, int64_t ev_head_stride, int64_t ev_index,
+                                      const void* q, int64_t n_q, int64_t q_head_stride,
+                                      const void* k_win, const void* v_win, int64_t n_kv,
+                                      int64_t kv_head_stride, int64_t win_index, int32_t top_k,
+                                      void* out, int64_t out_head_stride, int32_t* sel_out,
+                                      void* stream) {
+  if (!st) return HF_ERR_INVALID_ARG;
+  hf_status e = check_absorb(st, k_ev, v_ev, n_ev, ev_head_stride, ev_index);
+  if (e == HF_OK)
+    e = check_attend_all(st, q, n_q, q_head_stride, k_win, v_win, n_kv, kv_head_stride, top_k,
+                         out, out_head_stride, sel_out);
+  if (e == HF_OK && n_q > 0) e = check_window(win_index, n_kv);
+  if (e != HF_OK) return e;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hf::KeyCache kc = key_cache(st, win_index);
+  bool absorbed = false;
+  const hf_status r = on_device(st->device, [&]() -> hipError_t {
+    if (n_q == 0) {
+      hipError_t err = hipSuccess;
+      if (n_ev > 0) {
+        err = enqueue_absorb(st, k_ev, v_ev, n_ev, ev_head_stride, s);
+        absorbed = err == hipSuccess;
+      }
+      return err;
+    }
+    const FusedAbsorb fa{k_ev, v_ev, n_ev, ev_head_stride};
+    return enqueue_attend(st, q, n_q, q_head_stride, k_win, v_win, n_kv, kv_head_stride, top_k,
+                          out, out_head_stride, sel_out, s, nullptr, n_ev > 0 ? &fa : nullptr,
+                          &absorbed, &kc);
+  });
+  if (absorbed) st->next_ev += n_ev;  // the absorb is enqueued and will run
+  return r;
+}
+
+hf_status hf_key_cache_reset(hf_state* st) {
+  if (!st) return HF_ERR_INVALID_ARG;
+  st->kc_lo = st->kc_hi = 0;
+  return HF_OK;
 }
 
 hf_status hf_block_scores(hf_state* st, const void* q, int64_t n_q, int64_t q_head_stride,

@@ -130,10 +130,19 @@ class HybridAttentionState:
 
     def attend_chunk(self, q: torch.Tensor, k_win: torch.Tensor, v_win: torch.Tensor,
                      top_k: int, out: Optional[torch.Tensor] = None,
-                     sel_out: Optional[torch.Tensor] = None) -> torch.Tensor:
-        """Hybrid attention of the chunk q over the window (and the state); enqueued."""
+                     sel_out: Optional[torch.Tensor] = None,
+                     win_index: Optional[int] = None) -> torch.Tensor:
+        """Hybrid attention of the chunk q over the window (and the state); enqueued.
+        With win_index (absolute index of the window's first token in the stream), the
+        key pooling uses the state's cache of 8-token key sums (same results)."""
         out, args = self._attend_args(q, k_win, v_win, top_k, out, sel_out)
-        _check(B.hf_attend_chunk(self.handle, *args, _stream(self.device)), "hf_attend_chunk")
+        if win_index is None:
+            _check(B.hf_attend_chunk(self.handle, *args, _stream(self.device)), "hf_attend_chunk")
+        else:
+            a = list(args)
+            a.insert(7, int(win_index))  # after kv_head_stride
+            _check(B.hf_attend_chunk_cached(self.handle, *a, _stream(self.device)),
+                   "hf_attend_chunk_cached")
         return out
 
     def absorb_and_attend(self, k_ev: torch.Tensor, v_ev: torch.Tensor, q: torch.Tensor,
@@ -141,17 +150,32 @@ class HybridAttentionState:
                           out: Optional[torch.Tensor] = None,
                           sel_out: Optional[torch.Tensor] = None,
                           ev_index: Optional[int] = None,
-                          side_stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+                          side_stream: Optional[torch.cuda.Stream] = None,
+                          win_index: Optional[int] = None) -> torch.Tensor:
         """absorb_evicted then attend_chunk in one call (same results); with a side
-        stream the absorb overlaps the block scoring and selection."""
+        stream the absorb overlaps the block scoring and selection. With win_index
+        (one stream only) the key pooling uses the state's cache of 8-token key sums."""
         n_ev, ev_hs = self._evicted_args(k_ev, v_ev)
         out, args = self._attend_args(q, k_win, v_win, top_k, out, sel_out)
         idx = self.next_ev_index if ev_index is None else ev_index
-        side = side_stream.cuda_stream if side_stream is not None else 0
-        _check(B.hf_absorb_and_attend(self.handle, k_ev.data_ptr(), v_ev.data_ptr(), n_ev, ev_hs,
-                                      idx, *args, _stream(self.device), side),
-               "hf_absorb_and_attend")
+        if win_index is None:
+            side = side_stream.cuda_stream if side_stream is not None else 0
+            _check(B.hf_absorb_and_attend(self.handle, k_ev.data_ptr(), v_ev.data_ptr(), n_ev,
+                                          ev_hs, idx, *args, _stream(self.device), side),
+                   "hf_absorb_and_attend")
+        else:
+            if side_stream is not None:
+                raise ValueError("the cached form runs on one stream")
+            a = list(args)
+            a.insert(7, int(win_index))  # after kv_head_stride
+            _check(B.hf_absorb_and_attend_cached(self.handle, k_ev.data_ptr(), v_ev.data_ptr(),
+                                                 n_ev, ev_hs, idx, *a, _stream(self.device)),
+                   "hf_absorb_and_attend_cached")
         return out
+
+    def key_cache_reset(self) -> None:
+        """Forget the cached 8-token key sums (host-side; enqueues nothing)."""
+        _check(B.hf_key_cache_reset(self.handle), "hf_key_cache_reset")
 
     def block_scores(self, q: torch.Tensor, k_win: torch.Tensor) -> torch.Tensor:
         """fp32 pooled block scores [H][ceil(n_q/B)][ceil(n_kv/B)] (enqueued)."""

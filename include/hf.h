@@ -152,6 +152,41 @@ hf_status hf_absorb_and_attend(hf_state* st, const void* k_ev, const void* v_ev,
                                int32_t top_k, void* out, int64_t out_head_stride,
                                int32_t* sel_out, void* stream, void* side_stream);
 
+/* hf_attend_chunk with cached key pooling. win_index is the absolute index, within
+ * the stream, of the window's first token (k_win row 0). The key-block means of the
+ * block scores ([EN] 2.A.2) are formed from fp32 sums of 8-token groups of K that
+ * the state keeps between calls, keyed by absolute token index: the groups that an
+ * earlier cached call of this state summed for its window are read from that cache
+ * instead of k_win. A window that moves by one chunk per call therefore reads only
+ * the chunk's own keys for the pooling; the attention itself still reads k_win and
+ * v_win. Results are bit for bit those of hf_attend_chunk (the pooling always adds
+ * 8-token groups in the same order). Requirements (HF_ERR_INVALID_ARG otherwise):
+ * win_index >= 0, win_index % 8 == 0 and n_kv % 8 == 0. The caller guarantees that
+ * the keys of tokens already cached have not changed (a stream's past keys do not),
+ * and that cached calls of a handle are ordered on the device (one stream, or
+ * synchronised); hf_key_cache_reset forgets the cache. Workspace: the state reserves
+ * H x 2^ceil(log2(ceil(max_n_kv / 8))) x d floats for the cache. */
+hf_status hf_attend_chunk_cached(hf_state* st, const void* q, int64_t n_q, int64_t q_head_stride,
+                                 const void* k_win, const void* v_win, int64_t n_kv,
+                                 int64_t kv_head_stride, int64_t win_index, int32_t top_k,
+                                 void* out, int64_t out_head_stride, int32_t* sel_out,
+                                 void* stream);
+
+/* hf_absorb_and_attend on one stream (its three-launch form) with cached key
+ * pooling as in hf_attend_chunk_cached: bit for bit the results of
+ * hf_absorb_evicted followed by hf_attend_chunk. */
+hf_status hf_absorb_and_attend_cached(hf_state* st, const void* k_ev, const void* v_ev,
+                                      int64_t n_ev, int64_t ev_head_stride, int64_t ev_index,
+                                      const void* q, int64_t n_q, int64_t q_head_stride,
+                                      const void* k_win, const void* v_win, int64_t n_kv,
+                                      int64_t kv_head_stride, int64_t win_index, int32_t top_k,
+                                      void* out, int64_t out_head_stride, int32_t* sel_out,
+                                      void* stream);
+
+/* Forget the cached key sums of hf_attend_chunk_cached (for example before the
+ * handle serves another stream). Host-side only; enqueues nothing. */
+hf_status hf_key_cache_reset(hf_state* st);
+
 /* The pooled block importance scores alone ([EN] 2.A.2), the first stage of
  * hf_attend_chunk: scores_out is fp32 [H][ceil(n_q/B)][ceil(n_kv/B)], dense. The
  * same kernels and arithmetic as hf_attend_chunk produce it. */

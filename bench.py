@@ -64,6 +64,12 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--serial", action="store_true",
                    help="hf_absorb_evicted then hf_attend_chunk (two calls)")
+    p.add_argument("--cached-pooling", action="store_true",
+                   help="hf_absorb_and_attend_cached over streams whose window moves by one "
+                        "chunk per step (the key pooling reads cached 8-token sums)")
+    p.add_argument("--stream-positions", type=int, default=16,
+                   help="window positions per stream buffer in --cached-pooling (the stream "
+                        "wraps after that many steps and its key cache is reset)")
     p.add_argument("--side-stream", action="store_true",
                    help="hf_absorb_and_attend with the absorb on a side stream")
     p.add_argument("--cpu-reps", type=int, default=3)
@@ -137,6 +143,60 @@ class LayerSet:
             sparse_swa=(n_q + 2 * self.n_kv) * d * 2 * H + n_q * d * 2 * H + (d * d + d) * 4 * H)
 
 
+class StreamSet(LayerSet):
+    """One stream of the Wan-like layer for the cached key pooling: device buffers of
+    9 + 3 P latent frames of K, V and Q (seeded normal values on the GPU, not the
+    oracle's generator: this mode is timed, not checked), a state, and a stream step t
+    whose window [3t - 6, 3t + 3) frames moves by one chunk per step; the evicted
+    frames [3t - 9, 3t - 6) are absorbed. After P steps the window goes back to the
+    buffer's start (the absolute indices keep growing) and the key cache is reset,
+    so cached sums always belong to the keys the call passes."""
+
+    T = 1560  # tokens per latent frame
+
+    def __init__(self, hla, torch, seed, top_k, positions):
+        H, d, T = 12, 128, self.T
+        dev = torch.device("cuda:0")
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed)
+        n = (9 + 3 * positions) * T
+        mk = lambda: (torch.randn((H, n, d), generator=g, device=dev) / d ** 0.5).to(  # noqa
+            torch.bfloat16)
+        self.kbuf, self.vbuf, self.qbuf = mk(), mk(), mk()
+        self.H, self.d, self.n_q, self.n_kv, self.n_ev = H, d, 3 * T, 9 * T, 3 * T
+        self.top_k, self.positions, self.t = top_k, positions, 3
+        self.out = torch.empty((H, 3 * T, d), dtype=torch.bfloat16, device=dev)
+        self.st = hla.HybridAttentionState(H, d, 64, torch.bfloat16, max_n_q=self.n_q,
+                                           max_n_kv=self.n_kv, max_n_ev=self.n_ev,
+                                           max_top_k=top_k, device=dev)
+        self.position(0)
+
+    def position(self, p):
+        """Views of the evicted frames, the window and the chunk at buffer position p."""
+        T = self.T
+        self.kev, self.vev = self.kbuf[:, 3 * p * T:(3 * p + 3) * T], self.vbuf[:, 3 * p * T:(3 * p + 3) * T]
+        self.kw, self.vw = self.kbuf[:, (3 * p + 3) * T:(3 * p + 12) * T], self.vbuf[:, (3 * p + 3) * T:(3 * p + 12) * T]
+        self.q = self.qbuf[:, (3 * p + 9) * T:(3 * p + 12) * T]
+
+    def step(self, side=None, serial=False):
+        p = (self.t - 3) % self.positions
+        if p == 0 and self.t > 3:
+            self.st.key_cache_reset()
+        self.position(p)
+        self.st.absorb_and_attend(self.kev, self.vev, self.q, self.kw, self.vw, self.top_k,
+                                  out=self.out, win_index=self.T * (3 * self.t - 6))
+        self.t += 1
+
+    def pool_bytes_cached(self):
+        """Pooling bytes of a step whose window moved by one chunk: Q, the chunk's keys,
+        the cached 8-token sums of the other six frames (read) and the chunk's (written),
+        the block means."""
+        H, d, T, B = self.H, self.d, self.T, 64
+        nqb, nkb = -(-self.n_q // B), -(-self.n_kv // B)
+        return (self.n_q + 3 * T) * d * 2 * H + (6 * T // 8 + 3 * T // 8) * d * 4 * H + \
+            (nqb + nkb) * d * 4 * H
+
+
 def cpu_baseline(layer: LayerSet, reps: int):
     """The float64 oracle on the host cores: the same layer step, median of `reps`."""
     import numpy as np
@@ -191,16 +251,34 @@ def main():
     top_k = synth.top_k_count(wl.top_k_frac, -(-wl.window_tokens // wl.block))
     n_sets = wl.layers if args.workload == "full_depth_bf16" else max(1, args.sets)
     t0 = time.time()
-    sets = [LayerSet(hla, torch, synth, args.seed + i, top_k) for i in range(n_sets)]
+    if args.cached_pooling and args.workload != "wan_layer_bf16":
+        sys.exit("--cached-pooling runs the wan_layer_bf16 shapes")
+    if args.cached_pooling and (args.side_stream or args.serial):
+        sys.exit("--cached-pooling issues hf_absorb_and_attend_cached on one stream")
+    if args.cached_pooling:
+        sets = [StreamSet(hla, torch, args.seed + i, top_k, args.stream_positions)
+                for i in range(n_sets)]
+    else:
+        sets = [LayerSet(hla, torch, synth, args.seed + i, top_k) for i in range(n_sets)]
     log(f"[bench] {n_sets} input sets resident ({time.time() - t0:.1f}s)")
 
     # Selection of every set (for the executed-FLOP count); not timed.
     flops = []
     for s in sets:
         sel = torch.empty((s.H, -(-s.n_q // 64), top_k), dtype=torch.int32, device="cuda")
-        s.st.attend_chunk(s.q, s.kw, s.vw, top_k, out=s.out, sel_out=sel)
-        torch.cuda.synchronize()
-        flops.append(s.flops(torch, sel.cpu().numpy()))
+        if args.cached_pooling:  # every position's selection; their mean stands for a step
+            per = []
+            for p in range(s.positions):
+                s.position(p)
+                s.st.attend_chunk(s.q, s.kw, s.vw, top_k, out=s.out, sel_out=sel)
+                torch.cuda.synchronize()
+                per.append(s.flops(torch, sel.cpu().numpy()))
+            flops.append({k: sum(f[k] for f in per) / len(per) for k in per[0]})
+            s.position(0)
+        else:
+            s.st.attend_chunk(s.q, s.kw, s.vw, top_k, out=s.out, sel_out=sel)
+            torch.cuda.synchronize()
+            flops.append(s.flops(torch, sel.cpu().numpy()))
 
     per_step_layers = n_sets if args.workload == "full_depth_bf16" else 1
     side = torch.cuda.Stream() if args.side_stream else None  # default priority
@@ -297,6 +375,8 @@ def main():
     # and z) runs in the selection launch, so its bytes and FLOPs are counted there.
     fused = not args.side_stream and not args.serial
     kbytes = dict(sets[0].bytes())
+    if args.cached_pooling:  # a step whose window moved by one chunk (all but 1 in P)
+        kbytes["block_pool"] = sets[0].pool_bytes_cached()
     kflops = {name: statistics.mean(fl[name] for fl in flops)
               for name in ("absorb", "block_pool", "score_select", "sparse_swa")}
     names = ("absorb", "block_pool", "score_select", "sparse_swa")
@@ -333,7 +413,7 @@ def main():
         log(f"[bench] calibration copies of {args.calibrate_copy_mib} MiB done")
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.cached_pooling:
         log("[bench] timing the float64 oracle on the host ...")
         cpu = cpu_baseline(sets[0], args.cpu_reps)
         if args.workload == "full_depth_bf16":
@@ -364,7 +444,11 @@ def main():
             "block": 64, "top_k": top_k, "input_sets": n_sets, "layers_per_step": per_step_layers,
             "issue": ("hf_absorb_evicted, then hf_attend_chunk" if args.serial else
                       "hf_absorb_and_attend, absorb on a side stream" if args.side_stream else
-                      "hf_absorb_and_attend, one stream"),
+                      ("hf_absorb_and_attend_cached, one stream; each input set is a stream "
+                       f"whose window moves by one chunk per step ({args.stream_positions} "
+                       "positions per buffer, key cache reset at each wrap)")
+                      if args.cached_pooling else "hf_absorb_and_attend, one stream"),
+            "cached_pooling": bool(args.cached_pooling),
         },
         "pct_of_mfma_peak": round(100 * value / peak, 3),
         "ms_per_step_with_kernel_events": round(ms_step_ev, 5),

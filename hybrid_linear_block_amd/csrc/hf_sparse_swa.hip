@@ -494,6 +494,13 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void s
   };
   static_assert(NET * 2 == LPT * NW, "an S slice is one tile");
 
+  // The first key block's K and V tiles are requested before the Q operands, so that
+  // their latency overlaps the Q loads and the normaliser below (the vector memory
+  // counter completes in order: the waits for Q cover these older loads too).
+  int jb = my_sel[0];
+  issue_tile(kh, jb, lds_k);
+  issue_tile(vh, jb, lds_v);
+
   // Q operands (B of S^T = K Q^T): lane holds Q[16n + c][32s + 8g .. +8].
   bf16x8 qop[NQT][NKS];
 #pragma unroll
@@ -562,9 +569,6 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void s
   }
   constexpr uint32_t kRow16 = 16 * CPR * 16;  // bytes of 16 tile rows
 
-  int jb = my_sel[0];
-  issue_tile(kh, jb, lds_k);
-  issue_tile(vh, jb, lds_v);
 #pragma clang loop unroll(disable)  // no peeled first step (register pressure)
   for (int t = 0; t < top_k; ++t) {
     const bool more = t + 1 < top_k;

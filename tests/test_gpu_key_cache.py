@@ -24,10 +24,13 @@ def _draw(seed, stream, H, n, d, std, dtype):
     return dev_bf16(synth.bf16_bits(x)) if dtype == "bf16" else dev_f32(x)
 
 
-@pytest.mark.parametrize("dt,d,B", [("bf16", 128, 64), ("bf16", 64, 64), ("f32", 64, 16)])
-def test_cached_stream_matches_uncached_bitwise(dt, d, B):
+@pytest.mark.parametrize("dt,d,B,base", [("bf16", 128, 64, 0), ("bf16", 64, 64, 0),
+                                         ("f32", 64, 16, 0), ("bf16", 128, 64, 8 * 1234567)])
+def test_cached_stream_matches_uncached_bitwise(dt, d, B, base):
     """A 6-step stream (window of 9 frames moving by 3) through the cached combined
-    call equals the uncached combined call bit for bit: outputs, selections, S, z."""
+    call equals the uncached combined call bit for bit: outputs, selections, S, z.
+    `base` shifts the absolute token indices (the cache ring then wraps many times
+    over)."""
     H, T, c, W, K = 4, 320, 3, 9, 12
     std = 1.0 / np.sqrt(d)
     nf = c * 6 + c
@@ -47,7 +50,7 @@ def test_cached_stream_matches_uncached_bitwise(dt, d, B):
                 for _ in range(2)]
         o_ref = ref.absorb_and_attend(kev, vev, q, kw, vw, k_t, sel_out=sels[0])
         o_c = cached.absorb_and_attend(kev, vev, q, kw, vw, k_t, sel_out=sels[1],
-                                       win_index=w0 * T)
+                                       win_index=base + w0 * T)
         torch.cuda.synchronize()
         print(f"step {t}: window [{w0}, {w1}) frames, K={k_t}", flush=True)
         assert torch.equal(sels[1], sels[0])

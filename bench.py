@@ -64,9 +64,12 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--serial", action="store_true",
                    help="hf_absorb_evicted then hf_attend_chunk (two calls)")
+    p.add_argument("--streams", action="store_true",
+                   help="each input set is a stream whose window moves by one chunk per step "
+                        "(hf_absorb_and_attend on one stream)")
     p.add_argument("--cached-pooling", action="store_true",
-                   help="hf_absorb_and_attend_cached over streams whose window moves by one "
-                        "chunk per step (the key pooling reads cached 8-token sums)")
+                   help="--streams with hf_absorb_and_attend_cached (the key pooling reads "
+                        "cached 8-token sums)")
     p.add_argument("--stream-positions", type=int, default=16,
                    help="window positions per stream buffer in --cached-pooling (the stream "
                         "wraps after that many steps and its key cache is reset)")
@@ -154,7 +157,7 @@ class StreamSet(LayerSet):
 
     T = 1560  # tokens per latent frame
 
-    def __init__(self, hla, torch, seed, top_k, positions):
+    def __init__(self, hla, torch, seed, top_k, positions, cached):
         H, d, T = 12, 128, self.T
         dev = torch.device("cuda:0")
         g = torch.Generator(device=dev)
@@ -164,7 +167,7 @@ class StreamSet(LayerSet):
             torch.bfloat16)
         self.kbuf, self.vbuf, self.qbuf = mk(), mk(), mk()
         self.H, self.d, self.n_q, self.n_kv, self.n_ev = H, d, 3 * T, 9 * T, 3 * T
-        self.top_k, self.positions, self.t = top_k, positions, 3
+        self.top_k, self.positions, self.t, self.cached = top_k, positions, 3, cached
         self.out = torch.empty((H, 3 * T, d), dtype=torch.bfloat16, device=dev)
         self.st = hla.HybridAttentionState(H, d, 64, torch.bfloat16, max_n_q=self.n_q,
                                            max_n_kv=self.n_kv, max_n_ev=self.n_ev,
@@ -180,11 +183,12 @@ class StreamSet(LayerSet):
 
     def step(self, side=None, serial=False):
         p = (self.t - 3) % self.positions
-        if p == 0 and self.t > 3:
+        if p == 0 and self.t > 3 and self.cached:
             self.st.key_cache_reset()
         self.position(p)
         self.st.absorb_and_attend(self.kev, self.vev, self.q, self.kw, self.vw, self.top_k,
-                                  out=self.out, win_index=self.T * (3 * self.t - 6))
+                                  out=self.out,
+                                  win_index=self.T * (3 * self.t - 6) if self.cached else None)
         self.t += 1
 
     def pool_bytes_cached(self):
@@ -251,13 +255,14 @@ def main():
     top_k = synth.top_k_count(wl.top_k_frac, -(-wl.window_tokens // wl.block))
     n_sets = wl.layers if args.workload == "full_depth_bf16" else max(1, args.sets)
     t0 = time.time()
-    if args.cached_pooling and args.workload != "wan_layer_bf16":
-        sys.exit("--cached-pooling runs the wan_layer_bf16 shapes")
-    if args.cached_pooling and (args.side_stream or args.serial):
-        sys.exit("--cached-pooling issues hf_absorb_and_attend_cached on one stream")
-    if args.cached_pooling:
-        sets = [StreamSet(hla, torch, args.seed + i, top_k, args.stream_positions)
-                for i in range(n_sets)]
+    streams = args.streams or args.cached_pooling
+    if streams and args.workload != "wan_layer_bf16":
+        sys.exit("--streams / --cached-pooling run the wan_layer_bf16 shapes")
+    if streams and (args.side_stream or args.serial):
+        sys.exit("--streams / --cached-pooling issue the combined call on one stream")
+    if streams:
+        sets = [StreamSet(hla, torch, args.seed + i, top_k, args.stream_positions,
+                          args.cached_pooling) for i in range(n_sets)]
     else:
         sets = [LayerSet(hla, torch, synth, args.seed + i, top_k) for i in range(n_sets)]
     log(f"[bench] {n_sets} input sets resident ({time.time() - t0:.1f}s)")
@@ -266,7 +271,7 @@ def main():
     flops = []
     for s in sets:
         sel = torch.empty((s.H, -(-s.n_q // 64), top_k), dtype=torch.int32, device="cuda")
-        if args.cached_pooling:  # every position's selection; their mean stands for a step
+        if streams:  # every position's selection; their mean stands for a step
             per = []
             for p in range(s.positions):
                 s.position(p)
@@ -413,7 +418,7 @@ def main():
         log(f"[bench] calibration copies of {args.calibrate_copy_mib} MiB done")
 
     cpu = None
-    if not args.no_cpu_baseline and not args.cached_pooling:
+    if not args.no_cpu_baseline and not streams:
         log("[bench] timing the float64 oracle on the host ...")
         cpu = cpu_baseline(sets[0], args.cpu_reps)
         if args.workload == "full_depth_bf16":
@@ -444,10 +449,13 @@ def main():
             "block": 64, "top_k": top_k, "input_sets": n_sets, "layers_per_step": per_step_layers,
             "issue": ("hf_absorb_evicted, then hf_attend_chunk" if args.serial else
                       "hf_absorb_and_attend, absorb on a side stream" if args.side_stream else
-                      ("hf_absorb_and_attend_cached, one stream; each input set is a stream "
+                      (("hf_absorb_and_attend_cached" if args.cached_pooling else
+                        "hf_absorb_and_attend") + ", one stream; each input set is a stream "
                        f"whose window moves by one chunk per step ({args.stream_positions} "
-                       "positions per buffer, key cache reset at each wrap)")
-                      if args.cached_pooling else "hf_absorb_and_attend, one stream"),
+                       "positions per buffer" +
+                       (", key cache reset at each wrap)" if args.cached_pooling else ")"))
+                      if streams else "hf_absorb_and_attend, one stream"),
+            "streams": bool(streams),
             "cached_pooling": bool(args.cached_pooling),
         },
         "pct_of_mfma_peak": round(100 * value / peak, 3),

@@ -9,6 +9,7 @@ from .binding import (  # noqa: F401
     HF_BF16, HF_F32, HF_OK, HF_ERR_INVALID_ARG, HF_ERR_UNSUPPORTED, HF_ERR_STATE, HF_ERR_HIP,
     HfError, hf_config, hf_workspace_bytes, hf_state_init, hf_absorb_evicted, hf_attend_chunk,
     hf_absorb_and_attend, hf_attend_chunk_cached, hf_absorb_and_attend_cached, hf_key_cache_reset,
+    hf_window_attach, hf_window_begin_chunk, hf_window_attend, hf_window_range,
     hf_block_scores, hf_profile_start, hf_profile_stop, hf_next_ev_index,
     hf_state_destroy, hf_status_string, library_path)
 from .state import HybridAttentionState, window_frames  # noqa: F401

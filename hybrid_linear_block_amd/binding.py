@@ -65,6 +65,11 @@ def _load():
                                                 c_int64, P, P, c_int64, c_int64, c_int64, c_int32,
                                                 P, c_int64, P, P]),
         "hf_key_cache_reset": (c_int, [P]),
+        "hf_window_attach": (c_int, [P, P, P, c_int64, c_int64]),
+        "hf_window_begin_chunk": (c_int, [P, c_int64, P, POINTER(c_void_p), POINTER(c_void_p),
+                                          POINTER(c_int64)]),
+        "hf_window_attend": (c_int, [P, P, c_int64, c_int64, c_int32, P, c_int64, P, P]),
+        "hf_window_range": (c_int, [P, POINTER(c_int64), POINTER(c_int64)]),
         "hf_block_scores": (c_int, [P, P, c_int64, c_int64, P, c_int64, c_int64, P, P]),
         "hf_profile_start": (c_int, [P, c_int32]),
         "hf_profile_stop": (c_int, [P, POINTER(ctypes.c_double), POINTER(c_int32)]),
@@ -83,8 +88,9 @@ _lib = _load()
 
 EXPORTED = ("hf_workspace_bytes", "hf_state_init", "hf_absorb_evicted", "hf_attend_chunk",
             "hf_absorb_and_attend", "hf_attend_chunk_cached", "hf_absorb_and_attend_cached",
-            "hf_key_cache_reset", "hf_block_scores", "hf_profile_start", "hf_profile_stop",
-            "hf_next_ev_index", "hf_state_destroy", "hf_status_string")
+            "hf_key_cache_reset", "hf_window_attach", "hf_window_begin_chunk",
+            "hf_window_attend", "hf_window_range", "hf_block_scores", "hf_profile_start",
+            "hf_profile_stop", "hf_next_ev_index", "hf_state_destroy", "hf_status_string")
 HF_KERNEL_NAMES = ("absorb", "block_pool", "score_select", "sparse_swa")
 
 
@@ -155,6 +161,32 @@ def hf_absorb_and_attend_cached(state: int, k_ev: int, v_ev: int, n_ev: int, ev_
 
 def hf_key_cache_reset(state: int) -> int:
     return _lib.hf_key_cache_reset(state)
+
+
+def hf_window_attach(state: int, k_ring: int, v_ring: int, ring_tokens: int,
+                     window_tokens: int) -> int:
+    return _lib.hf_window_attach(state, k_ring, v_ring, ring_tokens, window_tokens)
+
+
+def hf_window_begin_chunk(state: int, n: int, stream: int):
+    """Returns (status, k_slot, v_slot, head_stride)."""
+    k, v, hs = c_void_p(), c_void_p(), c_int64()
+    st = _lib.hf_window_begin_chunk(state, n, stream, ctypes.byref(k), ctypes.byref(v),
+                                    ctypes.byref(hs))
+    return st, k.value, v.value, hs.value
+
+
+def hf_window_attend(state: int, q: int, n_q: int, q_head_stride: int, top_k: int, out: int,
+                     out_head_stride: int, sel_out: int, stream: int) -> int:
+    return _lib.hf_window_attend(state, q, n_q, q_head_stride, top_k, out, out_head_stride,
+                                 sel_out, stream)
+
+
+def hf_window_range(state: int):
+    """Returns (status, first token, token count)."""
+    first, count = c_int64(), c_int64()
+    st = _lib.hf_window_range(state, ctypes.byref(first), ctypes.byref(count))
+    return st, first.value, count.value
 
 
 def hf_block_scores(state: int, q: int, n_q: int, q_head_stride: int, k_win: int, n_kv: int,

@@ -11,6 +11,7 @@
 
 #include "../../include/hf.h"
 #include "hf_launch.h"
+#include "hf_window.h"
 
 struct hf_state {
   hf_config cfg;
@@ -32,6 +33,12 @@ struct hf_state {
   float* kcache;
   int64_t kc_cap = 1, kc_lo = 0, kc_hi = 0;
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;  // hf_absorb_and_attend's fork / join
+  // Library-managed window over the caller's K/V ring (hf_window_attach); win_ok turns
+  // false if a slide could not be enqueued whole.
+  hf::Window win;
+  char* k_ring = nullptr;
+  char* v_ring = nullptr;
+  bool win_on = false, win_ok = false;
   // Per-kernel timing (hf_profile_start / hf_profile_stop).
   bool prof_on = false;
   int prof_cap = 0;
@@ -473,6 +480,125 @@ hf_status hf_absorb_and_attend_cached(hf_state* st, const void* k_ev, const void
   });
   if (absorbed) st->next_ev += n_ev;  // the absorb is enqueued and will run
   return r;
+}
+
+hf_status hf_window_attach(hf_state* st, void* k_ring, void* v_ring, int64_t ring_tokens,
+                           int64_t window_tokens) {
+  if (!st || !k_ring || !v_ring || !aligned16(k_ring) || !aligned16(v_ring))
+    return HF_ERR_INVALID_ARG;
+  const hf_config& c = st->cfg;
+  if (window_tokens < 1 || window_tokens > c.max_n_kv) return HF_ERR_INVALID_ARG;
+  if (ring_tokens < 2 * window_tokens) return HF_ERR_INVALID_ARG;
+  if (c.num_heads > 65535) return HF_ERR_UNSUPPORTED;  // the slide's copy grid
+  st->win = hf::Window();
+  st->win.cap = ring_tokens;
+  st->win.win = window_tokens;
+  st->win.base = st->win.hi = st->next_ev;
+  st->k_ring = static_cast<char*>(k_ring);
+  st->v_ring = static_cast<char*>(v_ring);
+  st->win_on = st->win_ok = true;
+  st->kc_lo = st->kc_hi = 0;  // cached key sums may come from other buffers
+  return HF_OK;
+}
+
+hf_status hf_window_begin_chunk(hf_state* st, int64_t n, void* stream, void** k_slot,
+                                void** v_slot, int64_t* head_stride) {
+  if (!st || !k_slot || !v_slot || !head_stride) return HF_ERR_INVALID_ARG;
+  if (!st->win_on || !st->win_ok) return HF_ERR_STATE;
+  const hf_config& c = st->cfg;
+  hf::BeginPlan p;
+  if (n < 1 || n > st->win.win) return HF_ERR_INVALID_ARG;
+  if (!hf::plan_begin(st->win, st->next_ev, n, c.max_n_ev, &p)) {
+    const int64_t new_hi = st->win.hi + st->win.cur;
+    return st->next_ev < st->win.base || st->next_ev > new_hi ? HF_ERR_STATE
+                                                              : HF_ERR_INVALID_ARG;
+  }
+  const size_t row = (size_t)c.head_dim * elem_size(c.dtype);
+  const int64_t hs = st->win.cap * c.head_dim;  // elements
+  if (p.slide) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    bool absorbed = false;
+    const hf_status r = on_device(st->device, [&]() -> hipError_t {
+      hipError_t e = hipSuccess;
+      if (p.absorb_n > 0) {
+        e = enqueue_absorb(st, st->k_ring + p.absorb_row * row, st->v_ring + p.absorb_row * row,
+                           p.absorb_n, hs, s);
+        absorbed = e == hipSuccess;
+      }
+      if (e == hipSuccess)
+        e = hf::launch_copy_rows_kv(st->k_ring + p.copy_src_row * row,
+                                    st->v_ring + p.copy_src_row * row, st->k_ring, st->v_ring,
+                                    c.num_heads, (size_t)p.copy_rows * row,
+                                    (size_t)hs * elem_size(c.dtype), s);
+      return e;
+    });
+    if (absorbed) st->next_ev += p.absorb_n;
+    if (r != HF_OK) {
+      st->win_ok = false;  // the ring no longer matches the bookkeeping
+      return r;
+    }
+  }
+  hf::apply_begin(&st->win, p, n);
+  *k_slot = st->k_ring + p.slot_row * row;
+  *v_slot = st->v_ring + p.slot_row * row;
+  *head_stride = hs;
+  return HF_OK;
+}
+
+hf_status hf_window_attend(hf_state* st, const void* q, int64_t n_q, int64_t q_head_stride,
+                           int32_t top_k, void* out, int64_t out_head_stride, int32_t* sel_out,
+                           void* stream) {
+  if (!st) return HF_ERR_INVALID_ARG;
+  if (!st->win_on || !st->win_ok || st->win.cur == 0) return HF_ERR_STATE;
+  const hf_config& c = st->cfg;
+  if (st->next_ev < st->win.base || st->next_ev > st->win.hi) return HF_ERR_STATE;
+  const hf::AttendView v = hf::attend_view(st->win, st->next_ev);
+  if (v.ev_n > c.max_n_ev) return HF_ERR_INVALID_ARG;
+  const size_t row = (size_t)c.head_dim * elem_size(c.dtype);
+  const int64_t hs = st->win.cap * c.head_dim;
+  const void* k_win = st->k_ring + v.win_row * row;
+  const void* v_win = st->v_ring + v.win_row * row;
+  const hf_status e = check_attend_all(st, q, n_q, q_head_stride, k_win, v_win, v.n_kv, hs,
+                                       top_k, out, out_head_stride, sel_out);
+  if (e != HF_OK) return e;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const void* k_ev = st->k_ring + v.ev_row * row;
+  const void* v_ev = st->v_ring + v.ev_row * row;
+  // Key sums are cached where the window holds whole 8-token groups; only groups
+  // of past chunks stay cached, since the current chunk's keys may still change.
+  const bool cached = check_window(v.ws, v.n_kv) == HF_OK;
+  const hf::KeyCache kc = key_cache(st, v.ws);
+  bool absorbed = false;
+  const hf_status r = on_device(st->device, [&]() -> hipError_t {
+    if (n_q == 0) {
+      hipError_t err = hipSuccess;
+      if (v.ev_n > 0) {
+        err = enqueue_absorb(st, k_ev, v_ev, v.ev_n, hs, s);
+        absorbed = err == hipSuccess;
+      }
+      return err;
+    }
+    const FusedAbsorb fa{k_ev, v_ev, v.ev_n, hs};
+    return enqueue_attend(st, q, n_q, q_head_stride, k_win, v_win, v.n_kv, hs, top_k, out,
+                          out_head_stride, sel_out, s, nullptr, v.ev_n > 0 ? &fa : nullptr,
+                          &absorbed, cached ? &kc : nullptr);
+  });
+  if (cached && n_q > 0) {
+    const int64_t past = st->win.hi / 8;  // whole groups of past chunks
+    if (st->kc_hi > past) st->kc_hi = past;
+    if (st->kc_lo > st->kc_hi) st->kc_lo = st->kc_hi;
+  }
+  if (absorbed) st->next_ev += v.ev_n;
+  return r;
+}
+
+hf_status hf_window_range(const hf_state* st, int64_t* first, int64_t* count) {
+  if (!st || !first || !count) return HF_ERR_INVALID_ARG;
+  if (!st->win_on) return HF_ERR_STATE;
+  const hf::AttendView v = hf::attend_view(st->win, st->next_ev);
+  *first = v.ws;
+  *count = v.n_kv;
+  return HF_OK;
 }
 
 hf_status hf_key_cache_reset(hf_state* st) {

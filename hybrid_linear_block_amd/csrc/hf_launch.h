@@ -80,5 +80,11 @@ hipError_t launch_sparse_swa(int dtype, int heads, int d, int block, const void*
 
 // ---- utilities -------------------------------------------------------------------
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
+// Copy bytes_per_head bytes of each of `heads` heads (head_stride_bytes apart in
+// both source and destination) for a K and a V tensor at once; multiples of 16
+// bytes, 16-byte aligned, source and destination disjoint.
+hipError_t launch_copy_rows_kv(const void* k_src, const void* v_src, void* k_dst, void* v_dst,
+                               int heads, size_t bytes_per_head, size_t head_stride_bytes,
+                               hipStream_t stream);
 
 }  // namespace hf

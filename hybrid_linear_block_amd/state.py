@@ -117,16 +117,19 @@ class HybridAttentionState:
         n_o, o_hs = self._check_input(out, "out")
         if n_o != n_q:
             raise ValueError("out must have as many rows as q")
-        sel_ptr = 0
-        if sel_out is not None:
-            nqb = -(-n_q // self.cfg.block_size)
-            if (sel_out.dtype != torch.int32 or sel_out.device != self.device
-                    or tuple(sel_out.shape) != (self.cfg.num_heads, nqb, top_k)
-                    or not sel_out.is_contiguous()):
-                raise ValueError(f"sel_out must be contiguous int32 [H][{nqb}][{top_k}]")
-            sel_ptr = sel_out.data_ptr()
+        sel_ptr = self._sel_ptr(sel_out, n_q, top_k)
         return out, (q.data_ptr(), n_q, q_hs, k_win.data_ptr(), v_win.data_ptr(), n_kv, kv_hs,
                      int(top_k), out.data_ptr(), o_hs, sel_ptr)
+
+    def _sel_ptr(self, sel_out: Optional[torch.Tensor], n_q: int, top_k: int) -> int:
+        if sel_out is None:
+            return 0
+        nqb = -(-n_q // self.cfg.block_size)
+        if (sel_out.dtype != torch.int32 or sel_out.device != self.device
+                or tuple(sel_out.shape) != (self.cfg.num_heads, nqb, top_k)
+                or not sel_out.is_contiguous()):
+            raise ValueError(f"sel_out must be contiguous int32 [H][{nqb}][{top_k}]")
+        return sel_out.data_ptr()
 
     def attend_chunk(self, q: torch.Tensor, k_win: torch.Tensor, v_win: torch.Tensor,
                      top_k: int, out: Optional[torch.Tensor] = None,
@@ -176,6 +179,53 @@ class HybridAttentionState:
     def key_cache_reset(self) -> None:
         """Forget the cached 8-token key sums (host-side; enqueues nothing)."""
         _check(B.hf_key_cache_reset(self.handle), "hf_key_cache_reset")
+
+    # ------------------------------------------------------- managed window
+
+    def window_attach(self, window_tokens: int, ring_tokens: Optional[int] = None) -> None:
+        """Let the state keep the sliding window of window_tokens tokens in a K/V ring of
+        ring_tokens rows per head (default 2 * window_tokens), allocated here."""
+        ring = 2 * window_tokens if ring_tokens is None else int(ring_tokens)
+        shape = (self.cfg.num_heads, max(ring, 1), self.cfg.head_dim)
+        k_ring = torch.empty(shape, dtype=self.dtype, device=self.device)
+        v_ring = torch.empty(shape, dtype=self.dtype, device=self.device)
+        _check(B.hf_window_attach(self.handle, k_ring.data_ptr(), v_ring.data_ptr(), ring,
+                                  int(window_tokens)), "hf_window_attach")
+        self.k_ring, self.v_ring = k_ring, v_ring
+
+    def begin_chunk(self, n: int) -> Tuple[torch.Tensor, torch.Tensor]:
+        """Start a chunk of n tokens; returns the ring views [H][n][d] that its K and V
+        must be written to (on the current stream) before window_attend."""
+        st, kp, vp, hs = B.hf_window_begin_chunk(self.handle, int(n), _stream(self.device))
+        _check(st, "hf_window_begin_chunk")
+        row_bytes = self.cfg.head_dim * self.k_ring.element_size()
+        row = (kp - self.k_ring.data_ptr()) // row_bytes
+        if (vp - self.v_ring.data_ptr()) // row_bytes != row or hs != self.k_ring.stride(0):
+            raise RuntimeError("hf_window_begin_chunk returned an unexpected slot")
+        return self.k_ring[:, row:row + n], self.v_ring[:, row:row + n]
+
+    def window_attend(self, q: torch.Tensor, top_k: int, out: Optional[torch.Tensor] = None,
+                      sel_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """Hybrid attention of the current chunk's queries against the managed window
+        and the state (absorbing what left the window first); enqueued."""
+        n_q, q_hs = self._check_input(q, "q")
+        if out is None:
+            out = torch.empty((self.cfg.num_heads, n_q, self.cfg.head_dim), dtype=self.dtype,
+                              device=self.device)
+        n_o, o_hs = self._check_input(out, "out")
+        if n_o != n_q:
+            raise ValueError("out must have as many rows as q")
+        sel_ptr = self._sel_ptr(sel_out, n_q, top_k)
+        _check(B.hf_window_attend(self.handle, q.data_ptr(), n_q, q_hs, int(top_k),
+                                  out.data_ptr(), o_hs, sel_ptr, _stream(self.device)),
+               "hf_window_attend")
+        return out
+
+    def window_range(self) -> Tuple[int, int]:
+        """(absolute index of the first token, token count) of the managed window."""
+        st, first, count = B.hf_window_range(self.handle)
+        _check(st, "hf_window_range")
+        return first, count
 
     def block_scores(self, q: torch.Tensor, k_win: torch.Tensor) -> torch.Tensor:
         """fp32 pooled block scores [H][ceil(n_q/B)][ceil(n_kv/B)] (enqueued)."""

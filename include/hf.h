@@ -187,6 +187,56 @@ hf_status hf_absorb_and_attend_cached(hf_state* st, const void* k_ev, const void
  * handle serves another stream). Host-side only; enqueues nothing. */
 hf_status hf_key_cache_reset(hf_state* st);
 
+/* ---- Library-managed window ----------------------------------------------------
+ * The state keeps the sliding window itself ([EN] 2.A.2: attention over the latest
+ * frames only; [EN] 2.A.1 and [ABS]: what leaves the window is absorbed into the
+ * linear state). Its K and V rows live in a caller-owned ring, and each chunk's K
+ * and V are written straight into the ring slot the library names. Tokens keep their
+ * absolute stream index: the first token of the first chunk after hf_window_attach
+ * is hf_next_ev_index(st). The window of a chunk is the last window_tokens tokens up
+ * to and including the chunk. */
+
+/* Attach a window of window_tokens tokens (1 <= window_tokens <= max_n_kv) kept in
+ * k_ring and v_ring: caller-owned [H][ring_tokens][d] buffers of the state's element
+ * type, head stride ring_tokens * d elements, 16-byte aligned, with ring_tokens >=
+ * 2 * window_tokens (a larger ring moves the window less often, see
+ * hf_window_begin_chunk). The window starts empty. Host only (enqueues nothing);
+ * replaces an earlier window and forgets the cached key sums. HF_ERR_UNSUPPORTED for
+ * more than 65535 heads. */
+hf_status hf_window_attach(hf_state* st, void* k_ring, void* v_ring, int64_t ring_tokens,
+                           int64_t window_tokens);
+
+/* Start a chunk of n tokens (1 <= n <= window_tokens). The previous chunk joins the
+ * window's past. *k_slot and *v_slot receive the ring rows for the new chunk's K and
+ * V ([H][n][d], head stride *head_stride elements); the caller writes them, ordered
+ * on the device before hf_window_attend reads them (for example on `stream`). When
+ * the chunk does not fit behind the window in the ring, this call first enqueues on
+ * `stream` the absorb of the tokens that leave the window and a copy of the rest of
+ * the window to the front of the ring (about every (ring_tokens - window_tokens) / n
+ * chunks). HF_ERR_INVALID_ARG if more than max_n_ev tokens would wait for the absorb;
+ * HF_ERR_STATE without a window, if the eviction index was moved outside the window's
+ * tokens (by hf_absorb_evicted), or after a failed copy (HF_ERR_HIP), which leaves the
+ * window unusable until it is attached again. */
+hf_status hf_window_begin_chunk(hf_state* st, int64_t n, void* stream, void** k_slot,
+                                void** v_slot, int64_t* head_stride);
+
+/* Hybrid attention of the current chunk's queries q ([H][n_q][d]) against the window
+ * (the current chunk included) and the state, as hf_absorb_and_attend on one stream:
+ * tokens that left the window and are not yet absorbed are absorbed first, in the
+ * same three launches. The key pooling uses the state's key-sum cache (as
+ * hf_attend_chunk_cached) whenever the window starts on an 8-token group and holds
+ * whole groups, caching only the past chunks' keys. It may be called several times
+ * per chunk (for example once per denoising step, with the slot's K and V rewritten
+ * in between); results are bit for bit those of hf_absorb_and_attend over the same
+ * window. HF_ERR_STATE without a window or before the first hf_window_begin_chunk. */
+hf_status hf_window_attend(hf_state* st, const void* q, int64_t n_q, int64_t q_head_stride,
+                           int32_t top_k, void* out, int64_t out_head_stride, int32_t* sel_out,
+                           void* stream);
+
+/* The window the next hf_window_attend sees: absolute index of its first token and
+ * its length in tokens (HF_ERR_STATE without a window). */
+hf_status hf_window_range(const hf_state* st, int64_t* first, int64_t* count);
+
 /* The pooled block importance scores alone ([EN] 2.A.2), the first stage of
  * hf_attend_chunk: scores_out is fp32 [H][ceil(n_q/B)][ceil(n_kv/B)], dense. The
  * same kernels and arithmetic as hf_attend_chunk produce it. */

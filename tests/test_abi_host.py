@@ -135,6 +135,10 @@ def test_calls_on_null_state_are_rejected():
     assert hla.hf_absorb_and_attend_cached(None, A, A, 10, 1280, 0, A, 10, 1280, A, A, 16, 2048,
                                            0, 1, A, 1280, 0, 0) == B.HF_ERR_INVALID_ARG
     assert hla.hf_key_cache_reset(None) == B.HF_ERR_INVALID_ARG
+    assert hla.hf_window_attach(None, A, A, 20, 10) == B.HF_ERR_INVALID_ARG
+    assert hla.hf_window_begin_chunk(None, 1, 0)[0] == B.HF_ERR_INVALID_ARG
+    assert hla.hf_window_attend(None, A, 10, 1280, 1, A, 1280, 0, 0) == B.HF_ERR_INVALID_ARG
+    assert hla.hf_window_range(None)[0] == B.HF_ERR_INVALID_ARG
     assert hla.hf_profile_start(None, 4) == B.HF_ERR_INVALID_ARG
     assert hla.hf_next_ev_index(None) == -1
     hla.hf_state_destroy(None)  # allowed

@@ -13,6 +13,10 @@ top-K = 55 of 220 key blocks, 4680 evicted tokens. Inputs are resident in HBM
 before timing starts; `--sets` independent input sets (each with its own state)
 are rotated so that consecutive steps do not hit a warm cache.
 
+`--managed-window`: each input set is a stream whose state keeps the window in a
+K/V ring (hf_window_begin_chunk, the chunk's K and V written into the ring slot,
+hf_window_attend); the step time includes those writes and the ring's slides.
+
 Before the warmup steps, untimed steps run for --settle-ms (default 100 ms): the
 GPU needs tens of milliseconds of sustained load before its clocks reach their
 steady state, and a stream of chunks runs at that state.
@@ -73,6 +77,11 @@ def parse():
     p.add_argument("--stream-positions", type=int, default=16,
                    help="window positions per stream buffer in --cached-pooling (the stream "
                         "wraps after that many steps and its key cache is reset)")
+    p.add_argument("--managed-window", action="store_true",
+                   help="the state keeps the window in a K/V ring (hf_window_begin_chunk / "
+                        "hf_window_attend); each step writes the chunk's K and V into its slot")
+    p.add_argument("--ring-windows", type=int, default=4,
+                   help="ring length in windows for --managed-window (>= 2)")
     p.add_argument("--side-stream", action="store_true",
                    help="hf_absorb_and_attend with the absorb on a side stream")
     p.add_argument("--cpu-reps", type=int, default=3)
@@ -191,14 +200,44 @@ class StreamSet(LayerSet):
                                   win_index=self.T * (3 * self.t - 6) if self.cached else None)
         self.t += 1
 
-    def pool_bytes_cached(self):
-        """Pooling bytes of a step whose window moved by one chunk: Q, the chunk's keys,
-        the cached 8-token sums of the other six frames (read) and the chunk's (written),
-        the block means."""
+    def pool_bytes_cached(self, summed_frames=3):
+        """Pooling bytes of a step whose window moved by one chunk: Q, the keys of the
+        `summed_frames` newest frames, the cached 8-token sums of the others (read) and
+        theirs (written), the block means. The managed window sums the previous chunk
+        again (6 frames): its keys may have changed after its last cached call."""
         H, d, T, B = self.H, self.d, self.T, 64
         nqb, nkb = -(-self.n_q // B), -(-self.n_kv // B)
-        return (self.n_q + 3 * T) * d * 2 * H + (6 * T // 8 + 3 * T // 8) * d * 4 * H + \
+        f = summed_frames
+        return (self.n_q + f * T) * d * 2 * H + ((9 - f) * T // 8 + f * T // 8) * d * 4 * H + \
             (nqb + nkb) * d * 4 * H
+
+
+class WindowSet(StreamSet):
+    """One stream of the Wan-like layer through the library-managed window: the state
+    keeps the window in a K/V ring of `ring_windows` windows. A step starts a chunk,
+    writes the chunk's K and V (buffer position p of this stream, standing in for the
+    projection that would write them there) into the ring slot, and attends the chunk
+    (absorbing the frames that left the window). The ring's past chunks never change,
+    so the key cache needs no reset."""
+
+    def __init__(self, hla, torch, seed, top_k, positions, ring_windows):
+        super().__init__(hla, torch, seed, top_k, positions, cached=True)
+        self.st.window_attach(self.n_kv, ring_windows * self.n_kv)
+        self.t, self.slides, self.last_row = 0, 0, -1
+        for _ in range(3):  # fill the window: every later step absorbs one chunk
+            self.step()
+
+    def step(self, side=None, serial=False):
+        T, p = self.T, self.t % self.positions
+        a, b = (3 * p + 9) * T, (3 * p + 12) * T
+        ks, vs = self.st.begin_chunk(b - a)
+        row = (ks.data_ptr() - self.st.k_ring.data_ptr()) // (self.d * 2)
+        self.slides += row < self.last_row
+        self.last_row = row
+        ks.copy_(self.kbuf[:, a:b])
+        vs.copy_(self.vbuf[:, a:b])
+        self.st.window_attend(self.qbuf[:, a:b], self.top_k, out=self.out)
+        self.t += 1
 
 
 def cpu_baseline(layer: LayerSet, reps: int):
@@ -255,12 +294,17 @@ def main():
     top_k = synth.top_k_count(wl.top_k_frac, -(-wl.window_tokens // wl.block))
     n_sets = wl.layers if args.workload == "full_depth_bf16" else max(1, args.sets)
     t0 = time.time()
-    streams = args.streams or args.cached_pooling
+    streams = args.streams or args.cached_pooling or args.managed_window
     if streams and args.workload != "wan_layer_bf16":
-        sys.exit("--streams / --cached-pooling run the wan_layer_bf16 shapes")
+        sys.exit("--streams / --cached-pooling / --managed-window run the wan_layer_bf16 shapes")
     if streams and (args.side_stream or args.serial):
-        sys.exit("--streams / --cached-pooling issue the combined call on one stream")
-    if streams:
+        sys.exit("--streams / --cached-pooling / --managed-window issue one stream's calls")
+    if args.managed_window:
+        if args.ring_windows < 2:
+            sys.exit("--ring-windows must be at least 2")
+        sets = [WindowSet(hla, torch, args.seed + i, top_k, args.stream_positions,
+                          args.ring_windows) for i in range(n_sets)]
+    elif streams:
         sets = [StreamSet(hla, torch, args.seed + i, top_k, args.stream_positions,
                           args.cached_pooling) for i in range(n_sets)]
     else:
@@ -318,11 +362,13 @@ def main():
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
+    slides0 = sum(getattr(s, "slides", 0) for s in sets)
     ev0.record()
     for k in range(args.steps):
         run(k)
     ev1.record()
     host = time.perf_counter() - w0  # host time to enqueue the K steps
+    slides = sum(getattr(s, "slides", 0) for s in sets) - slides0
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     ms_step = ev0.elapsed_time(ev1) / args.steps
@@ -378,10 +424,13 @@ def main():
     # On one stream (the default) the absorb shares the attend call's launches: its
     # partial states are formed in the pooling launch and its reduce (which writes S
     # and z) runs in the selection launch, so its bytes and FLOPs are counted there.
+    absorb_alone_us = kern_us.get("absorb")  # absorbs outside an attend call
     fused = not args.side_stream and not args.serial
     kbytes = dict(sets[0].bytes())
     if args.cached_pooling:  # a step whose window moved by one chunk (all but 1 in P)
         kbytes["block_pool"] = sets[0].pool_bytes_cached()
+    if args.managed_window:
+        kbytes["block_pool"] = sets[0].pool_bytes_cached(6)
     kflops = {name: statistics.mean(fl[name] for fl in flops)
               for name in ("absorb", "block_pool", "score_select", "sparse_swa")}
     names = ("absorb", "block_pool", "score_select", "sparse_swa")
@@ -417,6 +466,26 @@ def main():
         torch.cuda.synchronize()
         log(f"[bench] calibration copies of {args.calibrate_copy_mib} MiB done")
 
+    window = None
+    if args.managed_window:  # cost of the chunk's K and V writes the steps include
+        s0 = sets[0]
+        kt, vt = torch.empty_like(s0.out), torch.empty_like(s0.out)
+        a, b = 9 * s0.T, 12 * s0.T
+        for _ in range(3):
+            kt.copy_(s0.kbuf[:, a:b])
+            vt.copy_(s0.vbuf[:, a:b])
+        ev0.record()
+        for _ in range(20):
+            kt.copy_(s0.kbuf[:, a:b])
+            vt.copy_(s0.vbuf[:, a:b])
+        ev1.record()
+        torch.cuda.synchronize()
+        window = dict(ring_windows=args.ring_windows, slides_in_timed_steps=slides,
+                      chunk_kv_write_us=round(ev0.elapsed_time(ev1) / 20 * 1e3, 2),
+                      absorb_outside_attend_us=None if absorb_alone_us is None
+                      else round(absorb_alone_us, 2))
+        log(f"[bench] managed window: {window}")
+
     cpu = None
     if not args.no_cpu_baseline and not streams:
         log("[bench] timing the float64 oracle on the host ...")
@@ -447,7 +516,9 @@ def main():
                          f"{-(-s0.n_kv // 64)}, {s0.n_ev} evicted tokens absorbed per step"),
             "heads": s0.H, "head_dim": s0.d, "n_q": s0.n_q, "n_kv": s0.n_kv, "n_ev": s0.n_ev,
             "block": 64, "top_k": top_k, "input_sets": n_sets, "layers_per_step": per_step_layers,
-            "issue": ("hf_absorb_evicted, then hf_attend_chunk" if args.serial else
+            "issue": ("hf_window_begin_chunk, K/V chunk copied into the ring slot, "
+                      "hf_window_attend; one stream per input set" if args.managed_window else
+                      "hf_absorb_evicted, then hf_attend_chunk" if args.serial else
                       "hf_absorb_and_attend, absorb on a side stream" if args.side_stream else
                       (("hf_absorb_and_attend_cached" if args.cached_pooling else
                         "hf_absorb_and_attend") + ", one stream; each input set is a stream "
@@ -457,6 +528,7 @@ def main():
                       if streams else "hf_absorb_and_attend, one stream"),
             "streams": bool(streams),
             "cached_pooling": bool(args.cached_pooling),
+            "managed_window": window,
         },
         "pct_of_mfma_peak": round(100 * value / peak, 3),
         "ms_per_step_with_kernel_events": round(ms_step_ev, 5),

@@ -44,6 +44,12 @@
  * NULL = the default stream) and return without synchronising. Device faults
  * surface at the caller's next synchronisation.
  *
+ * Graphs. Every call enqueues kernel launches only (no memset, allocation or
+ * synchronisation), so hf_attend_chunk and hf_block_scores can be captured into a
+ * HIP graph and replayed over the same buffers with new contents. The other calls
+ * capture as well, but their host-side bookkeeping (eviction index, key-sum cache,
+ * managed window) advances once, at capture, not at each replay.
+ *
  * Errors. Status codes only: no abort, no exception across the ABI, no logging.
  * On any error nothing is enqueued and the state is unchanged.
  *   HF_ERR_INVALID_ARG  null pointer; negative size; top_k outside [1, ceil(n_kv/B)]

@@ -73,6 +73,8 @@ def _run_random_case(H, d, B, dtype, n_q, n_kv, n_ev, top_k, seed):
     (1, 128, 64, "f32", 64, 256, 64, 4),
     (1, 128, 64, "bf16", 130, 20000, 64, 80),    # 313 key blocks (8 chunks of 64 per lane)
     (1, 128, 64, "bf16", 70, 70000, 64, 300),    # 1094 key blocks (32 chunks per lane)
+    (1, 128, 64, "bf16", 70, 2048 * 64, 64, 512),  # the maximum of 2048 key blocks
+    (1, 64, 16, "f32", 20, 2048 * 16 - 5, 16, 2048),  # 2048 blocks, all kept, ragged tail
 ])
 def test_random_case_full_compare(H, d, B, dtype, n_q, n_kv, n_ev, top_k):
     print(f"case H={H} d={d} B={B} {dtype} n_q={n_q} n_kv={n_kv} n_ev={n_ev} K={top_k}", flush=True)

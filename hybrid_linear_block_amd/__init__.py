@@ -10,6 +10,7 @@ from .binding import (  # noqa: F401
     HfError, hf_config, hf_workspace_bytes, hf_state_init, hf_absorb_evicted, hf_attend_chunk,
     hf_absorb_and_attend, hf_attend_chunk_cached, hf_absorb_and_attend_cached, hf_key_cache_reset,
     hf_window_attach, hf_window_begin_chunk, hf_window_attend, hf_window_range,
-    hf_block_scores, hf_profile_start, hf_profile_stop, hf_next_ev_index,
+    hf_block_scores, hf_backward_workspace_bytes, hf_attend_backward, hf_absorb_backward,
+    hf_profile_start, hf_profile_stop, hf_next_ev_index,
     hf_state_destroy, hf_status_string, library_path)
 from .state import HybridAttentionState, window_frames  # noqa: F401

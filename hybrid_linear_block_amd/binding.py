@@ -71,6 +71,11 @@ def _load():
         "hf_window_attend": (c_int, [P, P, c_int64, c_int64, c_int32, P, c_int64, P, P]),
         "hf_window_range": (c_int, [P, POINTER(c_int64), POINTER(c_int64)]),
         "hf_block_scores": (c_int, [P, P, c_int64, c_int64, P, c_int64, c_int64, P, P]),
+        "hf_backward_workspace_bytes": (c_size_t, [POINTER(hf_config)]),
+        "hf_attend_backward": (c_int, [P, P, c_int64, c_int64, P, P, c_int64, c_int64, P, c_int32,
+                                       P, c_int64, P, c_int64, P, P, c_int64, P, P, P, c_size_t,
+                                       P]),
+        "hf_absorb_backward": (c_int, [P, P, P, c_int64, c_int64, P, P, P, P, c_int64, P]),
         "hf_profile_start": (c_int, [P, c_int32]),
         "hf_profile_stop": (c_int, [P, POINTER(ctypes.c_double), POINTER(c_int32)]),
         "hf_next_ev_index": (c_int64, [P]),
@@ -89,7 +94,9 @@ _lib = _load()
 EXPORTED = ("hf_workspace_bytes", "hf_state_init", "hf_absorb_evicted", "hf_attend_chunk",
             "hf_absorb_and_attend", "hf_attend_chunk_cached", "hf_absorb_and_attend_cached",
             "hf_key_cache_reset", "hf_window_attach", "hf_window_begin_chunk",
-            "hf_window_attend", "hf_window_range", "hf_block_scores", "hf_profile_start",
+            "hf_window_attend", "hf_window_range", "hf_block_scores",
+            "hf_backward_workspace_bytes", "hf_attend_backward", "hf_absorb_backward",
+            "hf_profile_start",
             "hf_profile_stop", "hf_next_ev_index", "hf_state_destroy", "hf_status_string")
 HF_KERNEL_NAMES = ("absorb", "block_pool", "score_select", "sparse_swa")
 
@@ -193,6 +200,27 @@ def hf_block_scores(state: int, q: int, n_q: int, q_head_stride: int, k_win: int
                     kv_head_stride: int, scores_out: int, stream: int) -> int:
     return _lib.hf_block_scores(state, q, n_q, q_head_stride, k_win, n_kv, kv_head_stride,
                                 scores_out, stream)
+
+
+def hf_backward_workspace_bytes(cfg: hf_config) -> int:
+    return int(_lib.hf_backward_workspace_bytes(ctypes.byref(cfg)))
+
+
+def hf_attend_backward(state: int, q: int, n_q: int, q_head_stride: int, k_win: int, v_win: int,
+                       n_kv: int, kv_head_stride: int, sel: int, top_k: int, dout: int,
+                       dout_head_stride: int, dq: int, dq_head_stride: int, dk_win: int,
+                       dv_win: int, dkv_head_stride: int, dS: int, dz: int, bwd_ws: int,
+                       bwd_ws_bytes: int, stream: int) -> int:
+    return _lib.hf_attend_backward(state, q, n_q, q_head_stride, k_win, v_win, n_kv,
+                                   kv_head_stride, sel, top_k, dout, dout_head_stride, dq,
+                                   dq_head_stride, dk_win, dv_win, dkv_head_stride, dS, dz,
+                                   bwd_ws, bwd_ws_bytes, stream)
+
+
+def hf_absorb_backward(state: int, k_ev: int, v_ev: int, n_ev: int, ev_head_stride: int, dS: int,
+                       dz: int, dk_ev: int, dv_ev: int, dev_head_stride: int, stream: int) -> int:
+    return _lib.hf_absorb_backward(state, k_ev, v_ev, n_ev, ev_head_stride, dS, dz, dk_ev, dv_ev,
+                                   dev_head_stride, stream)
 
 
 def hf_profile_start(state: int, max_launches: int) -> int:

@@ -14,7 +14,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libhf.so")
-SOURCES = ["hf_abi.hip", "hf_absorb.hip", "hf_select.hip", "hf_sparse_swa.hip", "hf_util.hip"]
+SOURCES = ["hf_abi.hip", "hf_absorb.hip", "hf_select.hip", "hf_sparse_swa.hip", "hf_util.hip",
+           "hf_backward.hip"]
 ARCH = os.environ.get("HF_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

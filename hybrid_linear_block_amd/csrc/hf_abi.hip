@@ -631,6 +631,115 @@ hf_status hf_block_scores(hf_state* st, const void* q, int64_t n_q, int64_t q_he
   });
 }
 
+// Backward workspace: per-row statistics, then the inverse selection index.
+struct BwdLayout {
+  size_t rowstats, inv_cnt, inv_list, total;
+};
+
+static BwdLayout bwd_layout(const hf_config* c) {
+  const size_t H = (size_t)c->num_heads;
+  const size_t nqb = (size_t)ceil_div(c->max_n_q, c->block_size);
+  const size_t nkb = (size_t)ceil_div(c->max_n_kv, c->block_size);
+  BwdLayout L;
+  size_t off = 0;
+  L.rowstats = off;
+  off += round_up(H * (size_t)c->max_n_q * 4 * 4);
+  L.inv_cnt = off;
+  off += round_up(H * nkb * 4);
+  L.inv_list = off;
+  off += round_up(H * nkb * nqb * 4);
+  L.total = off;
+  return L;
+}
+
+static hf_status check_f32_out(const float* p, int64_t n, int64_t head_stride, int d) {
+  if (!p || !aligned16(p)) return HF_ERR_INVALID_ARG;
+  if (head_stride < n * d || head_stride % 4 != 0) return HF_ERR_INVALID_ARG;
+  return HF_OK;
+}
+
+size_t hf_backward_workspace_bytes(const hf_config* cfg) {
+  if (check_config(cfg) != HF_OK) return 0;
+  return bwd_layout(cfg).total;
+}
+
+hf_status hf_attend_backward(hf_state* st, const void* q, int64_t n_q, int64_t q_head_stride,
+                             const void* k_win, const void* v_win, int64_t n_kv,
+                             int64_t kv_head_stride, const int32_t* sel, int32_t top_k,
+                             const void* dout, int64_t dout_head_stride, float* dq,
+                             int64_t dq_head_stride, float* dk_win, float* dv_win,
+                             int64_t dkv_head_stride, float* dS, float* dz, void* bwd_ws,
+                             size_t bwd_ws_bytes, void* stream) {
+  if (!st) return HF_ERR_INVALID_ARG;
+  const hf_config& c = st->cfg;
+  if (n_q < 1) return HF_ERR_INVALID_ARG;
+  hf_status e = check_attend_all(st, q, n_q, q_head_stride, k_win, v_win, n_kv, kv_head_stride,
+                                 top_k, dout, dout_head_stride, nullptr);
+  if (e == HF_OK) e = check_f32_out(dq, n_q, dq_head_stride, c.head_dim);
+  if (e == HF_OK) e = check_f32_out(dk_win, n_kv, dkv_head_stride, c.head_dim);
+  if (e == HF_OK) e = check_f32_out(dv_win, n_kv, dkv_head_stride, c.head_dim);
+  if (e == HF_OK) e = check_f32_out(dS, 1, (int64_t)c.head_dim * c.head_dim, c.head_dim);
+  if (e == HF_OK) e = check_f32_out(dz, 1, c.head_dim, c.head_dim);
+  if (e != HF_OK) return e;
+  if (!sel || (reinterpret_cast<uintptr_t>(sel) & 3u)) return HF_ERR_INVALID_ARG;
+  const BwdLayout L = bwd_layout(&c);
+  if (!bwd_ws || !aligned16(bwd_ws) || bwd_ws_bytes < L.total) return HF_ERR_INVALID_ARG;
+  char* w = static_cast<char*>(bwd_ws);
+  hf::BwdArgs a;
+  a.heads = c.num_heads;
+  a.q = q;
+  a.n_q = n_q;
+  a.q_hs = q_head_stride;
+  a.k = k_win;
+  a.v = v_win;
+  a.n_kv = n_kv;
+  a.kv_hs = kv_head_stride;
+  a.sel = sel;
+  a.top_k = top_k;
+  a.S = st->S;
+  a.z = st->z;
+  a.eps = c.eps;
+  a.scale = st->scale;
+  a.dout = dout;
+  a.do_hs = dout_head_stride;
+  a.dq = dq;
+  a.dq_hs = dq_head_stride;
+  a.dk = dk_win;
+  a.dv = dv_win;
+  a.dkv_hs = dkv_head_stride;
+  a.dS = dS;
+  a.dz = dz;
+  a.rowstats = reinterpret_cast<float*>(w + L.rowstats);
+  a.nq_cap = c.max_n_q;
+  a.inv_cnt = reinterpret_cast<int32_t*>(w + L.inv_cnt);
+  a.inv_list = reinterpret_cast<int32_t*>(w + L.inv_list);
+  a.nqb_cap = st->nqb_cap;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return on_device(st->device, [&]() {
+    return hf::launch_attend_backward(c.dtype, c.head_dim, c.block_size, a, s);
+  });
+}
+
+hf_status hf_absorb_backward(hf_state* st, const void* k_ev, const void* v_ev, int64_t n_ev,
+                             int64_t ev_head_stride, const float* dS, const float* dz,
+                             float* dk_ev, float* dv_ev, int64_t dev_head_stride, void* stream) {
+  if (!st) return HF_ERR_INVALID_ARG;
+  const hf_config& c = st->cfg;
+  if (n_ev < 0 || n_ev > c.max_n_ev) return HF_ERR_INVALID_ARG;
+  if (n_ev == 0) return HF_OK;
+  hf_status e = check_tensor(k_ev, n_ev, ev_head_stride, c);
+  if (e == HF_OK) e = check_tensor(v_ev, n_ev, ev_head_stride, c);
+  if (e == HF_OK) e = check_f32_out(dk_ev, n_ev, dev_head_stride, c.head_dim);
+  if (e == HF_OK) e = check_f32_out(dv_ev, n_ev, dev_head_stride, c.head_dim);
+  if (e != HF_OK) return e;
+  if (!dS || !dz || !aligned16(dS) || !aligned16(dz)) return HF_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return on_device(st->device, [&]() {
+    return hf::launch_absorb_backward(c.dtype, c.num_heads, c.head_dim, k_ev, v_ev, n_ev,
+                                      ev_head_stride, dS, dz, dk_ev, dv_ev, dev_head_stride, s);
+  });
+}
+
 hf_status hf_profile_start(hf_state* st, int32_t max_launches) {
   if (!st || max_launches < 1 || max_launches > (1 << 20)) return HF_ERR_INVALID_ARG;
   prof_release(st);

@@ -1,0 +1,485 @@
+// hf_backward.hip -- backward pass of the per-chunk hybrid attention (gfx950).
+//
+// Hybrid Forcing trains through this path ([EN] 2.B-C, decoupled distillation; the
+// state is learnable, [EN] 2.A.1). With the key-block selection of the forward call
+// held fixed and L = sum(dout * out), per head (tau = scale, phi = elu + 1):
+//   softmax path  dv_t += p_rt dout_r, dl_rt = p_rt (dout_r . v_t - D_r),
+//                 D_r = dout_r . o_swa_r, dq_r += tau sum_t dl_rt k_t,
+//                 dk_t += tau dl_rt q_r;
+//   linear read   f = phi(q_r), den = z . f + eps, g = dout_r / den,
+//                 c = -(dout_r . S f) / den^2, dS += g f^T, dz += c f,
+//                 dq_r += phi'(q_r) * (S^T g + c z);
+//   absorb        dv_n = dS phi(k_n), dk_n = phi'(k_n) * (dS^T v_n + dz).
+//
+// Kernels (fp32 arithmetic throughout, no atomics: every sum runs in a fixed order,
+// so the results are bitwise reproducible):
+//   bwd_inv_sel  per (head, key block): the query blocks that selected it, ascending;
+//   bwd_rows     per (head, query block): pass 1 recomputes each row's softmax
+//                (log-sum-exp and o_swa, hence D_r) over its selected blocks, then
+//                the linear read's terms; pass 2 accumulates dq; stores per-row
+//                (lse, D, den, c) for the other kernels;
+//   bwd_kv       per (head, key block): dk and dv over the query blocks that
+//                selected it;
+//   bwd_state    per (head, 8 rows of dS, or z): dS and dz over all query rows;
+//   absorb_bwd   per (head, 64 evicted tokens): dk_ev and dv_ev.
+// A row's dot products are split over TPR adjacent lanes (DS features each) and
+// reduced with xor shuffles; K/V or Q/dout tiles are staged in LDS as fp32.
+#include "hf_device.h"
+#include "hf_launch.h"
+
+namespace hf {
+
+namespace {
+
+constexpr int BT = 256;  // threads per workgroup
+constexpr float kL2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float ldf(const float* p) { return *p; }
+__device__ __forceinline__ float ldf(const bf16_t* p) { return bf16_to_f32(*p); }
+
+__device__ __forceinline__ float phi_prime(float x) { return x > 0.f ? 1.f : __expf(x); }
+
+template <int TPR>
+__device__ __forceinline__ float row_sum(float x) {
+#pragma unroll
+  for (int m = 1; m < TPR; m <<= 1) x += __shfl_xor(x, m, 64);
+  return x;
+}
+
+__device__ __forceinline__ int clamp_block(int j, int n) { return j < 0 ? 0 : (j >= n ? n - 1 : j); }
+
+// rows [row0, row0 + BLK) of a [N][D] head into an fp32 tile; rows >= n read as 0.
+template <typename T, int D, int BLK>
+__device__ __forceinline__ void load_tile(const T* __restrict__ base, int64_t row0, int64_t n,
+                                          float* tile) {
+  for (int e = threadIdx.x; e < BLK * D; e += BT) {
+    const int64_t r = row0 + e / D;
+    tile[e] = r < n ? ldf(base + r * D + (e % D)) : 0.f;
+  }
+}
+
+__global__ void bwd_inv_sel(const int32_t* __restrict__ sel, int heads, int nqb, int nkb,
+                            int top_k, int32_t* __restrict__ cnt, int32_t* __restrict__ list,
+                            int nqb_cap) {
+  const int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (x >= (int64_t)heads * nkb) return;
+  const int h = (int)(x / nkb), j = (int)(x % nkb);
+  int n = 0;
+  for (int i = 0; i < nqb; ++i) {
+    const int32_t* row = sel + ((int64_t)h * nqb + i) * top_k;  // ascending
+    int lo = 0, hi = top_k;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (row[mid] < j) lo = mid + 1;
+      else hi = mid;
+    }
+    if (lo < top_k && row[lo] == j) list[x * nqb_cap + n++] = i;
+  }
+  cnt[x] = n;
+}
+
+template <typename T, int D, int BLK>
+__global__ __launch_bounds__(BT) void bwd_rows(
+    const T* __restrict__ q, int64_t n_q, int64_t q_hs, const T* __restrict__ kg,
+    const T* __restrict__ vg, int64_t n_kv, int64_t kv_hs, const int32_t* __restrict__ sel,
+    int top_k, int nqb, int nkb, const float* __restrict__ S, const float* __restrict__ z,
+    float eps, float scale, const T* __restrict__ dout, int64_t do_hs, float* __restrict__ dq,
+    int64_t dq_hs, float* __restrict__ rs, int64_t nq_cap) {
+  constexpr int TPR = BT / BLK, DS = D / TPR;
+  static_assert(DS % 4 == 0, "float4 slices");
+  __shared__ __align__(16) float tk[BLK * D];
+  __shared__ __align__(16) float tv[BLK * D];
+  const int h = blockIdx.x / nqb, i = blockIdx.x % nqb;
+  const int rl = threadIdx.x / TPR, d0 = (threadIdx.x % TPR) * DS;
+  const int64_t r = (int64_t)i * BLK + rl;
+  const bool live = r < n_q;
+  const int64_t rr = live ? r : n_q - 1;
+  const T* kh = kg + (int64_t)h * kv_hs;
+  const T* vh = vg + (int64_t)h * kv_hs;
+  const float* Sh = S + (int64_t)h * D * D;
+  const float* zh = z + (int64_t)h * D;
+  const int32_t* my_sel = sel + ((int64_t)h * nqb + i) * top_k;
+  float qv[DS], dov[DS], acc[DS];
+#pragma unroll
+  for (int e = 0; e < DS; ++e) {
+    qv[e] = ldf(q + (int64_t)h * q_hs + rr * D + d0 + e);
+    dov[e] = ldf(dout + (int64_t)h * do_hs + rr * D + d0 + e);
+    acc[e] = 0.f;
+  }
+  const float sl2 = scale * kL2e;
+
+  // ---- pass 1: softmax statistics and o_swa (online, base 2) ----
+  float m2 = -INFINITY, l = 0.f;
+  for (int t = 0; t < top_k; ++t) {
+    const int jb = clamp_block(my_sel[t], nkb);
+    __syncthreads();
+    load_tile<T, D, BLK>(kh, (int64_t)jb * BLK, n_kv, tk);
+    load_tile<T, D, BLK>(vh, (int64_t)jb * BLK, n_kv, tv);
+    __syncthreads();
+    const int nvalid = (int)min((int64_t)BLK, n_kv - (int64_t)jb * BLK);
+    for (int u = 0; u < nvalid; ++u) {
+      const float* kr = tk + u * D + d0;
+      float s = 0.f;
+#pragma unroll
+      for (int e = 0; e < DS; ++e) s += qv[e] * kr[e];
+      const float x = row_sum<TPR>(s) * sl2;
+      if (x > m2) {
+        const float a = exp2f(m2 - x);
+        l *= a;
+#pragma unroll
+        for (int e = 0; e < DS; ++e) acc[e] *= a;
+        m2 = x;
+      }
+      const float p = exp2f(x - m2);
+      l += p;
+      const float* vr = tv + u * D + d0;
+#pragma unroll
+      for (int e = 0; e < DS; ++e) acc[e] += p * vr[e];
+    }
+  }
+  const float inv_l = 1.f / l;
+  float dpart = 0.f;
+#pragma unroll
+  for (int e = 0; e < DS; ++e) dpart += dov[e] * (acc[e] * inv_l);
+  const float Dr = row_sum<TPR>(dpart);
+  const float lse2 = m2 + log2f(l);
+
+  // ---- linear read: den, c = -(dout . S f) / den^2, dq_lin ----
+  float fz = 0.f;
+#pragma unroll
+  for (int e = 0; e < DS; ++e) fz += phi(qv[e]) * zh[d0 + e];
+  const float den = row_sum<TPR>(fz) + eps;
+  const float inv_den = 1.f / den;
+  __syncthreads();  // every wave is done with the last tiles
+  float* frow = tk + rl * D;
+  float* grow = tv + rl * D;
+#pragma unroll
+  for (int e = 0; e < DS; ++e) {
+    frow[d0 + e] = phi(qv[e]);
+    grow[d0 + e] = dov[e] * inv_den;
+  }
+  __syncthreads();
+  // (S f)_j for the slice's rows j, column chunk by column chunk
+  float sf[DS];
+#pragma unroll
+  for (int e = 0; e < DS; ++e) sf[e] = 0.f;
+#pragma unroll 2
+  for (int c4 = 0; c4 < D; c4 += 4) {
+    const float4 f4 = *reinterpret_cast<const float4*>(frow + c4);
+#pragma unroll
+    for (int e = 0; e < DS; ++e) {
+      const float4 s4 = *reinterpret_cast<const float4*>(Sh + (int64_t)(d0 + e) * D + c4);
+      sf[e] += s4.x * f4.x + s4.y * f4.y + s4.z * f4.z + s4.w * f4.w;
+    }
+  }
+  float cpart = 0.f;
+#pragma unroll
+  for (int e = 0; e < DS; ++e) cpart += dov[e] * sf[e];
+  const float c = -row_sum<TPR>(cpart) * inv_den * inv_den;
+  float dql[DS];
+#pragma unroll
+  for (int e = 0; e < DS; ++e) dql[e] = 0.f;
+#pragma unroll 2
+  for (int j = 0; j < D; ++j) {
+    const float gj = grow[j];
+    const float* srow = Sh + (int64_t)j * D + d0;
+#pragma unroll
+    for (int e = 0; e < DS; e += 4) {
+      const float4 s4 = *reinterpret_cast<const float4*>(srow + e);
+      dql[e] += gj * s4.x;
+      dql[e + 1] += gj * s4.y;
+      dql[e + 2] += gj * s4.z;
+      dql[e + 3] += gj * s4.w;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < DS; ++e) acc[e] = phi_prime(qv[e]) * (dql[e] + c * zh[d0 + e]);
+
+  // ---- pass 2: dq of the softmax path ----
+  for (int t = 0; t < top_k; ++t) {
+    const int jb = clamp_block(my_sel[t], nkb);
+    __syncthreads();
+    load_tile<T, D, BLK>(kh, (int64_t)jb * BLK, n_kv, tk);
+    load_tile<T, D, BLK>(vh, (int64_t)jb * BLK, n_kv, tv);
+    __syncthreads();
+    const int nvalid = (int)min((int64_t)BLK, n_kv - (int64_t)jb * BLK);
+    for (int u = 0; u < nvalid; ++u) {
+      const float* kr = tk + u * D + d0;
+      const float* vr = tv + u * D + d0;
+      float s = 0.f, dp = 0.f;
+#pragma unroll
+      for (int e = 0; e < DS; ++e) {
+        s += qv[e] * kr[e];
+        dp += dov[e] * vr[e];
+      }
+      s = row_sum<TPR>(s);
+      dp = row_sum<TPR>(dp);
+      const float p = exp2f(s * sl2 - lse2);
+      const float dl = scale * p * (dp - Dr);
+#pragma unroll
+      for (int e = 0; e < DS; ++e) acc[e] += dl * kr[e];
+    }
+  }
+  if (live) {
+    float* o = dq + (int64_t)h * dq_hs + r * D + d0;
+#pragma unroll
+    for (int e = 0; e < DS; ++e) o[e] = acc[e];
+    if (d0 == 0) {
+      float* st = rs + ((int64_t)h * nq_cap + r) * 4;
+      st[0] = lse2;
+      st[1] = Dr;
+      st[2] = den;
+      st[3] = c;
+    }
+  }
+}
+
+template <typename T, int D, int BLK>
+__global__ __launch_bounds__(BT) void bwd_kv(
+    const T* __restrict__ q, int64_t n_q, int64_t q_hs, const T* __restrict__ kg,
+    const T* __restrict__ vg, int64_t n_kv, int64_t kv_hs, int nkb, float scale,
+    const T* __restrict__ dout, int64_t do_hs, const float* __restrict__ rs, int64_t nq_cap,
+    const int32_t* __restrict__ cnt, const int32_t* __restrict__ list, int nqb_cap,
+    float* __restrict__ dk, float* __restrict__ dv, int64_t dkv_hs) {
+  constexpr int TPR = BT / BLK, DS = D / TPR;
+  __shared__ __align__(16) float tq[BLK * D];
+  __shared__ __align__(16) float tdo[BLK * D];
+  __shared__ float tst[BLK * 2];
+  const int h = blockIdx.x / nkb, jb = blockIdx.x % nkb;
+  const int kl = threadIdx.x / TPR, d0 = (threadIdx.x % TPR) * DS;
+  const int64_t t = (int64_t)jb * BLK + kl;
+  const bool live = t < n_kv;
+  const int64_t tt = live ? t : n_kv - 1;
+  const T* qh = q + (int64_t)h * q_hs;
+  const T* doh = dout + (int64_t)h * do_hs;
+  float kv[DS], vv[DS], gk[DS], gv[DS];
+#pragma unroll
+  for (int e = 0; e < DS; ++e) {
+    kv[e] = ldf(kg + (int64_t)h * kv_hs + tt * D + d0 + e);
+    vv[e] = ldf(vg + (int64_t)h * kv_hs + tt * D + d0 + e);
+    gk[e] = gv[e] = 0.f;
+  }
+  const float sl2 = scale * kL2e;
+  const int64_t slot = (int64_t)h * nkb + jb;
+  const int n_sel = cnt[slot];
+  for (int x = 0; x < n_sel; ++x) {
+    const int i = list[slot * nqb_cap + x];
+    __syncthreads();
+    load_tile<T, D, BLK>(qh, (int64_t)i * BLK, n_q, tq);
+    load_tile<T, D, BLK>(doh, (int64_t)i * BLK, n_q, tdo);
+    for (int e = threadIdx.x; e < BLK; e += BT) {
+      const int64_t r = (int64_t)i * BLK + e;
+      const float* st = rs + ((int64_t)h * nq_cap + (r < n_q ? r : n_q - 1)) * 4;
+      tst[2 * e] = st[0];
+      tst[2 * e + 1] = st[1];
+    }
+    __syncthreads();
+    const int nvalid = (int)min((int64_t)BLK, n_q - (int64_t)i * BLK);
+    for (int u = 0; u < nvalid; ++u) {
+      const float* qr = tq + u * D + d0;
+      const float* dr = tdo + u * D + d0;
+      float s = 0.f, dp = 0.f;
+#pragma unroll
+      for (int e = 0; e < DS; ++e) {
+        s += kv[e] * qr[e];
+        dp += vv[e] * dr[e];
+      }
+      s = row_sum<TPR>(s);
+      dp = row_sum<TPR>(dp);
+      const float p = exp2f(s * sl2 - tst[2 * u]);
+      const float dl = scale * p * (dp - tst[2 * u + 1]);
+#pragma unroll
+      for (int e = 0; e < DS; ++e) {
+        gv[e] += p * dr[e];
+        gk[e] += dl * qr[e];
+      }
+    }
+  }
+  if (live) {
+    float* ok = dk + (int64_t)h * dkv_hs + t * D + d0;
+    float* ov = dv + (int64_t)h * dkv_hs + t * D + d0;
+#pragma unroll
+    for (int e = 0; e < DS; ++e) {
+      ok[e] = gk[e];
+      ov[e] = gv[e];
+    }
+  }
+}
+
+// Workgroup (h, jt): jt < D / 8 forms dS rows 8 jt .. 8 jt + 7, jt == D / 8 forms dz.
+template <typename T, int D>
+__global__ __launch_bounds__(BT) void bwd_state(const T* __restrict__ q, int64_t n_q,
+                                                int64_t q_hs, const T* __restrict__ dout,
+                                                int64_t do_hs, const float* __restrict__ rs,
+                                                int64_t nq_cap, float* __restrict__ dS,
+                                                float* __restrict__ dz) {
+  constexpr int RC = 32, NJ = 8, JPT = NJ * D / BT;  // rows per chunk, dS rows, outputs/thread
+  __shared__ float tf[RC * D];
+  __shared__ float tg[RC * NJ];
+  constexpr int NT = D / NJ + 1;
+  const int h = blockIdx.x / NT, jt = blockIdx.x % NT;
+  const bool is_z = jt == D / NJ;
+  const int col = threadIdx.x % D, j0 = threadIdx.x / D;  // rows j0, j0 + BT/D, ...
+  const T* qh = q + (int64_t)h * q_hs;
+  const T* doh = dout + (int64_t)h * do_hs;
+  const float* rsh = rs + (int64_t)h * nq_cap * 4;
+  float a[JPT];
+#pragma unroll
+  for (int e = 0; e < JPT; ++e) a[e] = 0.f;
+  for (int64_t r0 = 0; r0 < n_q; r0 += RC) {
+    __syncthreads();
+    for (int e = threadIdx.x; e < RC * D; e += BT) {
+      const int64_t r = r0 + e / D;
+      tf[e] = r < n_q ? phi(ldf(qh + r * D + (e % D))) : 0.f;
+    }
+    for (int e = threadIdx.x; e < RC * NJ; e += BT) {
+      const int64_t r = r0 + e / NJ;
+      float g = 0.f;
+      if (r < n_q) {
+        const float* st = rsh + r * 4;
+        g = is_z ? (e % NJ == 0 ? st[3] : 0.f)
+                 : ldf(doh + r * D + jt * NJ + (e % NJ)) / st[2];
+      }
+      tg[e] = g;
+    }
+    __syncthreads();
+    const int nr = (int)min((int64_t)RC, n_q - r0);
+    for (int u = 0; u < nr; ++u) {
+      const float f = tf[u * D + col];
+#pragma unroll
+      for (int e = 0; e < JPT; ++e) a[e] += tg[u * NJ + j0 + e * (BT / D)] * f;
+    }
+  }
+  if (is_z) {
+    if (j0 == 0) dz[(int64_t)h * D + col] = a[0];
+  } else {
+#pragma unroll
+    for (int e = 0; e < JPT; ++e)
+      dS[((int64_t)h * D + jt * NJ + j0 + e * (BT / D)) * D + col] = a[e];
+  }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(BT) void absorb_bwd(const T* __restrict__ k, const T* __restrict__ v,
+                                                 int64_t n_ev, int64_t ev_hs,
+                                                 const float* __restrict__ dS,
+                                                 const float* __restrict__ dz,
+                                                 float* __restrict__ dk, float* __restrict__ dv,
+                                                 int64_t dev_hs, int ntile) {
+  constexpr int BLK = 64, TPR = BT / BLK, DS = D / TPR;
+  __shared__ __align__(16) float tf[BLK * D];
+  __shared__ __align__(16) float tv[BLK * D];
+  const int h = blockIdx.x / ntile, tile = blockIdx.x % ntile;
+  const int nl = threadIdx.x / TPR, d0 = (threadIdx.x % TPR) * DS;
+  const int64_t n = (int64_t)tile * BLK + nl;
+  const bool live = n < n_ev;
+  const int64_t nn = live ? n : n_ev - 1;
+  const float* Sh = dS + (int64_t)h * D * D;
+  const float* zh = dz + (int64_t)h * D;
+  float kx[DS];
+#pragma unroll
+  for (int e = 0; e < DS; ++e) {
+    kx[e] = ldf(k + (int64_t)h * ev_hs + nn * D + d0 + e);
+    tf[nl * D + d0 + e] = phi(kx[e]);
+    tv[nl * D + d0 + e] = ldf(v + (int64_t)h * ev_hs + nn * D + d0 + e);
+  }
+  __syncthreads();
+  const float* frow = tf + nl * D;
+  const float* vrow = tv + nl * D;
+  float ov[DS], ok[DS];
+#pragma unroll
+  for (int e = 0; e < DS; ++e) ov[e] = ok[e] = 0.f;
+#pragma unroll 2
+  for (int c4 = 0; c4 < D; c4 += 4) {  // dv[j] = dS[j] . phi(k), column chunk by chunk
+    const float4 f4 = *reinterpret_cast<const float4*>(frow + c4);
+#pragma unroll
+    for (int e = 0; e < DS; ++e) {
+      const float4 s4 = *reinterpret_cast<const float4*>(Sh + (int64_t)(d0 + e) * D + c4);
+      ov[e] += s4.x * f4.x + s4.y * f4.y + s4.z * f4.z + s4.w * f4.w;
+    }
+  }
+#pragma unroll 2
+  for (int j = 0; j < D; ++j) {  // dk[i] = phi'(k_i) (sum_j v_j dS[j][i] + dz[i])
+    const float vj = vrow[j];
+    const float* srow = Sh + (int64_t)j * D + d0;
+#pragma unroll
+    for (int e = 0; e < DS; e += 4) {
+      const float4 s4 = *reinterpret_cast<const float4*>(srow + e);
+      ok[e] += vj * s4.x;
+      ok[e + 1] += vj * s4.y;
+      ok[e + 2] += vj * s4.z;
+      ok[e + 3] += vj * s4.w;
+    }
+  }
+  if (live) {
+    float* pk = dk + (int64_t)h * dev_hs + n * D + d0;
+    float* pv = dv + (int64_t)h * dev_hs + n * D + d0;
+#pragma unroll
+    for (int e = 0; e < DS; ++e) {
+      pk[e] = phi_prime(kx[e]) * (ok[e] + zh[d0 + e]);
+      pv[e] = ov[e];
+    }
+  }
+}
+
+template <typename T, int D, int BLK>
+hipError_t run_attend_bwd(const BwdArgs& a, hipStream_t s) {
+  const int nqb = (int)((a.n_q + BLK - 1) / BLK), nkb = (int)((a.n_kv + BLK - 1) / BLK);
+  const int64_t inv_n = (int64_t)a.heads * nkb;
+  bwd_inv_sel<<<(unsigned)((inv_n + 255) / 256), 256, 0, s>>>(a.sel, a.heads, nqb, nkb, a.top_k,
+                                                              a.inv_cnt, a.inv_list, a.nqb_cap);
+  bwd_rows<T, D, BLK><<<(unsigned)(a.heads * nqb), BT, 0, s>>>(
+      static_cast<const T*>(a.q), a.n_q, a.q_hs, static_cast<const T*>(a.k),
+      static_cast<const T*>(a.v), a.n_kv, a.kv_hs, a.sel, a.top_k, nqb, nkb, a.S, a.z, a.eps,
+      a.scale, static_cast<const T*>(a.dout), a.do_hs, a.dq, a.dq_hs, a.rowstats, a.nq_cap);
+  bwd_kv<T, D, BLK><<<(unsigned)(a.heads * nkb), BT, 0, s>>>(
+      static_cast<const T*>(a.q), a.n_q, a.q_hs, static_cast<const T*>(a.k),
+      static_cast<const T*>(a.v), a.n_kv, a.kv_hs, nkb, a.scale, static_cast<const T*>(a.dout),
+      a.do_hs, a.rowstats, a.nq_cap, a.inv_cnt, a.inv_list, a.nqb_cap, a.dk, a.dv, a.dkv_hs);
+  bwd_state<T, D><<<(unsigned)(a.heads * (D / 8 + 1)), BT, 0, s>>>(
+      static_cast<const T*>(a.q), a.n_q, a.q_hs, static_cast<const T*>(a.dout), a.do_hs,
+      a.rowstats, a.nq_cap, a.dS, a.dz);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t run_absorb_bwd(int heads, const void* k, const void* v, int64_t n_ev, int64_t ev_hs,
+                          const float* dS, const float* dz, float* dk, float* dv, int64_t dev_hs,
+                          hipStream_t s) {
+  const int ntile = (int)((n_ev + 63) / 64);
+  absorb_bwd<T, D><<<(unsigned)(heads * ntile), BT, 0, s>>>(
+      static_cast<const T*>(k), static_cast<const T*>(v), n_ev, ev_hs, dS, dz, dk, dv, dev_hs,
+      ntile);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attend_backward(int dtype, int d, int block, const BwdArgs& a, hipStream_t s) {
+  if (dtype == 0) {
+    if (block == 64 && d == 128) return run_attend_bwd<bf16_t, 128, 64>(a, s);
+    if (block == 64 && d == 64) return run_attend_bwd<bf16_t, 64, 64>(a, s);
+  } else {
+    if (block == 16 && d == 64) return run_attend_bwd<float, 64, 16>(a, s);
+    if (block == 16 && d == 128) return run_attend_bwd<float, 128, 16>(a, s);
+    if (block == 64 && d == 64) return run_attend_bwd<float, 64, 64>(a, s);
+    if (block == 64 && d == 128) return run_attend_bwd<float, 128, 64>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_absorb_backward(int dtype, int heads, int d, const void* k, const void* v,
+                                  int64_t n_ev, int64_t ev_hs, const float* dS, const float* dz,
+                                  float* dk, float* dv, int64_t dev_hs, hipStream_t s) {
+  if (n_ev <= 0) return hipSuccess;
+  if (dtype == 0) {
+    if (d == 128) return run_absorb_bwd<bf16_t, 128>(heads, k, v, n_ev, ev_hs, dS, dz, dk, dv, dev_hs, s);
+    if (d == 64) return run_absorb_bwd<bf16_t, 64>(heads, k, v, n_ev, ev_hs, dS, dz, dk, dv, dev_hs, s);
+  } else {
+    if (d == 128) return run_absorb_bwd<float, 128>(heads, k, v, n_ev, ev_hs, dS, dz, dk, dv, dev_hs, s);
+    if (d == 64) return run_absorb_bwd<float, 64>(heads, k, v, n_ev, ev_hs, dS, dz, dk, dv, dev_hs, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace hf

@@ -78,6 +78,41 @@ hipError_t launch_sparse_swa(int dtype, int heads, int d, int block, const void*
                              const uint16_t* s_split, const float* z, float eps, float scale,
                              void* out, int64_t out_hs, hipStream_t stream);
 
+// ---- backward (fixed selection) ---------------------------------------------------
+struct BwdArgs {
+  int heads;
+  const void* q;
+  int64_t n_q, q_hs;
+  const void* k;
+  const void* v;
+  int64_t n_kv, kv_hs;
+  const int32_t* sel;
+  int top_k;
+  const float* S;
+  const float* z;
+  float eps, scale;
+  const void* dout;
+  int64_t do_hs;
+  float* dq;
+  int64_t dq_hs;
+  float* dk;
+  float* dv;
+  int64_t dkv_hs;
+  float* dS;
+  float* dz;
+  float* rowstats;  // [heads][nq_cap][4]: log2-sum-exp2, D, den, c per query row
+  int64_t nq_cap;
+  int32_t* inv_cnt;   // [heads][nkb]
+  int32_t* inv_list;  // [heads][nkb][nqb_cap]
+  int nqb_cap;
+};
+// dq, dk, dv, dS and dz of the hybrid attention (n_q >= 1): four launches.
+hipError_t launch_attend_backward(int dtype, int d, int block, const BwdArgs& a, hipStream_t s);
+// dk_ev and dv_ev of an absorb from dS and dz (n_ev >= 0).
+hipError_t launch_absorb_backward(int dtype, int heads, int d, const void* k, const void* v,
+                                  int64_t n_ev, int64_t ev_hs, const float* dS, const float* dz,
+                                  float* dk, float* dv, int64_t dev_hs, hipStream_t s);
+
 // ---- utilities -------------------------------------------------------------------
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
 // Copy bytes_per_head bytes of each of `heads` heads (head_stride_bytes apart in

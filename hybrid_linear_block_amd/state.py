@@ -227,6 +227,52 @@ class HybridAttentionState:
         _check(st, "hf_window_range")
         return first, count
 
+    # ------------------------------------------------------------ backward
+
+    def attend_backward(self, q: torch.Tensor, k_win: torch.Tensor, v_win: torch.Tensor,
+                        sel: torch.Tensor, dout: torch.Tensor):
+        """Gradients of an attend_chunk call with its selection `sel` held fixed; the
+        state must be as at that call. Returns fp32 (dq, dk_win, dv_win, dS, dz)."""
+        _, args = self._attend_args(q, k_win, v_win, sel.shape[2], q, None)
+        n_q, q_hs, n_kv, kv_hs = args[1], args[2], args[5], args[6]
+        n_d, d_hs = self._check_input(dout, "dout")
+        if n_d != n_q:
+            raise ValueError("dout must have as many rows as q")
+        nqb = -(-n_q // self.cfg.block_size)
+        if (sel.dtype != torch.int32 or sel.device != self.device or not sel.is_contiguous()
+                or tuple(sel.shape[:2]) != (self.cfg.num_heads, nqb)):
+            raise ValueError(f"sel must be contiguous int32 [H][{nqb}][top_k]")
+        H, d = self.cfg.num_heads, self.cfg.head_dim
+        f32 = dict(dtype=torch.float32, device=self.device)
+        dq = torch.empty((H, n_q, d), **f32)
+        dk, dv = torch.empty((H, n_kv, d), **f32), torch.empty((H, n_kv, d), **f32)
+        dS, dz = torch.empty((H, d, d), **f32), torch.empty((H, d), **f32)
+        if getattr(self, "_bwd_ws", None) is None:
+            self._bwd_ws = torch.empty(B.hf_backward_workspace_bytes(self.cfg), dtype=torch.uint8,
+                                       device=self.device)
+        _check(B.hf_attend_backward(self.handle, q.data_ptr(), n_q, q_hs, k_win.data_ptr(),
+                                    v_win.data_ptr(), n_kv, kv_hs, sel.data_ptr(),
+                                    int(sel.shape[2]), dout.data_ptr(), d_hs, dq.data_ptr(),
+                                    n_q * d, dk.data_ptr(), dv.data_ptr(), n_kv * d, dS.data_ptr(),
+                                    dz.data_ptr(), self._bwd_ws.data_ptr(), self._bwd_ws.numel(),
+                                    _stream(self.device)), "hf_attend_backward")
+        return dq, dk, dv, dS, dz
+
+    def absorb_backward(self, k_ev: torch.Tensor, v_ev: torch.Tensor, dS: torch.Tensor,
+                        dz: torch.Tensor):
+        """fp32 (dk_ev, dv_ev) through an absorb of k_ev, v_ev, from the state's dS, dz."""
+        n, hs = self._evicted_args(k_ev, v_ev)
+        H, d = self.cfg.num_heads, self.cfg.head_dim
+        for t, shape in ((dS, (H, d, d)), (dz, (H, d))):
+            if t.dtype != torch.float32 or tuple(t.shape) != shape or not t.is_contiguous():
+                raise ValueError(f"dS, dz must be contiguous fp32 {shape}")
+        f32 = dict(dtype=torch.float32, device=self.device)
+        dk, dv = torch.empty((H, n, d), **f32), torch.empty((H, n, d), **f32)
+        _check(B.hf_absorb_backward(self.handle, k_ev.data_ptr(), v_ev.data_ptr(), n, hs,
+                                    dS.data_ptr(), dz.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                    max(n, 1) * d, _stream(self.device)), "hf_absorb_backward")
+        return dk, dv
+
     def block_scores(self, q: torch.Tensor, k_win: torch.Tensor) -> torch.Tensor:
         """fp32 pooled block scores [H][ceil(n_q/B)][ceil(n_kv/B)] (enqueued)."""
         n_q, q_hs = self._check_input(q, "q")

@@ -250,6 +250,50 @@ hf_status hf_block_scores(hf_state* st, const void* q, int64_t n_q, int64_t q_he
                           const void* k_win, int64_t n_kv, int64_t kv_head_stride,
                           float* scores_out, void* stream);
 
+/* ---- Backward pass (fixed selection) ------------------------------------------
+ * The method is trained through this path ([EN] 2.B-C, decoupled distillation; the
+ * state is learnable, [EN] 2.A.1). With L = sum(dout * out) for the output of
+ * hf_attend_chunk and the key-block selection of that call held fixed (a discrete
+ * choice, with no gradient), per head: the softmax path gives dv_t = sum_r p_rt
+ * dout_r, dk_t = tau sum_r dl_rt q_r and dq_r = tau sum_t dl_rt k_t with dl_rt =
+ * p_rt (dout_r . v_t - dout_r . o_swa_r); the linear read, with f = phi(q_r), den =
+ * z . f + eps, gives dS = sum_r (dout_r / den) f^T, dz = sum_r c_r f with c_r =
+ * -(dout_r . S f) / den^2, and dq_r += phi'(q_r) * (S^T dout_r / den + c_r z). All
+ * gradients are fp32 and dense per head; every sum runs in a fixed order (bitwise
+ * reproducible on a device type). */
+
+/* Bytes of the backward workspace for this configuration (0 if invalid). */
+size_t hf_backward_workspace_bytes(const hf_config* cfg);
+
+/* Gradients of one hf_attend_chunk call. q, k_win, v_win, n_q, n_kv, strides and
+ * top_k are those of the forward call; sel is its selection (int32
+ * [H][ceil(n_q/B)][top_k], each row ascending, as hf_attend_chunk's sel_out
+ * returns; indices are clamped into the window, so no selection reads out of
+ * bounds). S and z are the state's current ones, i.e. the state must be as at the
+ * forward call. dout ([H][n_q][d], element type of the state, head stride
+ * dout_head_stride) is the incoming gradient. Outputs, all fp32 and written
+ * whole: dq [H][n_q][d] (head stride dq_head_stride), dk_win and dv_win [H][n_kv][d]
+ * (head stride dkv_head_stride; rows of unselected key blocks get 0), dS [H][d][d]
+ * and dz [H][d] (dense). bwd_ws: caller-owned device memory of at least
+ * hf_backward_workspace_bytes bytes, 16-byte aligned. n_q must be >= 1. Four
+ * launches on `stream`. */
+hf_status hf_attend_backward(hf_state* st, const void* q, int64_t n_q, int64_t q_head_stride,
+                             const void* k_win, const void* v_win, int64_t n_kv,
+                             int64_t kv_head_stride, const int32_t* sel, int32_t top_k,
+                             const void* dout, int64_t dout_head_stride, float* dq,
+                             int64_t dq_head_stride, float* dk_win, float* dv_win,
+                             int64_t dkv_head_stride, float* dS, float* dz, void* bwd_ws,
+                             size_t bwd_ws_bytes, void* stream);
+
+/* Gradients through an absorb ([ABS]; [EN] 2.A.1): given dS [H][d][d] and dz [H][d]
+ * (fp32, dense) of the state after absorbing k_ev, v_ev ([H][n_ev][d], head stride
+ * ev_head_stride), writes dv_ev[n] = dS phi(k_n) and dk_ev[n] = phi'(k_n) * (dS^T v_n
+ * + dz) (fp32 [H][n_ev][d], head stride dev_head_stride). The state is only read for
+ * its configuration (the eviction index does not move). n_ev == 0 is a no-op. */
+hf_status hf_absorb_backward(hf_state* st, const void* k_ev, const void* v_ev, int64_t n_ev,
+                             int64_t ev_head_stride, const float* dS, const float* dz,
+                             float* dk_ev, float* dv_ev, int64_t dev_head_stride, void* stream);
+
 /* Kernels a state launches, for per-kernel timing. */
 typedef enum {
   HF_KERNEL_ABSORB = 0,       /* hf_absorb_evicted (both of its launches) */

@@ -139,6 +139,10 @@ def test_calls_on_null_state_are_rejected():
     assert hla.hf_window_begin_chunk(None, 1, 0)[0] == B.HF_ERR_INVALID_ARG
     assert hla.hf_window_attend(None, A, 10, 1280, 1, A, 1280, 0, 0) == B.HF_ERR_INVALID_ARG
     assert hla.hf_window_range(None)[0] == B.HF_ERR_INVALID_ARG
+    assert hla.hf_attend_backward(None, A, 10, 1280, A, A, 10, 1280, A, 1, A, 1280, A, 1280, A, A,
+                                  1280, A, A, A, 1 << 20, 0) == B.HF_ERR_INVALID_ARG
+    assert hla.hf_absorb_backward(None, A, A, 10, 1280, A, A, A, A, 1280, 0) == \
+        B.HF_ERR_INVALID_ARG
     assert hla.hf_profile_start(None, 4) == B.HF_ERR_INVALID_ARG
     assert hla.hf_next_ev_index(None) == -1
     hla.hf_state_destroy(None)  # allowed

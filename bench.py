@@ -77,6 +77,9 @@ def parse():
     p.add_argument("--stream-positions", type=int, default=16,
                    help="window positions per stream buffer in --cached-pooling (the stream "
                         "wraps after that many steps and its key cache is reset)")
+    p.add_argument("--backward", action="store_true",
+                   help="time the backward pass (hf_attend_backward + hf_absorb_backward) of the "
+                        "Wan-like layer instead of the forward step")
     p.add_argument("--managed-window", action="store_true",
                    help="the state keeps the window in a K/V ring (hf_window_begin_chunk / "
                         "hf_window_attend); each step writes the chunk's K and V into its slot")
@@ -240,6 +243,124 @@ class WindowSet(StreamSet):
         self.t += 1
 
 
+class BwdSet(LayerSet):
+    """One input set of the Wan-like layer for the backward pass: the forward call's
+    selection (untimed), a seeded incoming gradient and preallocated fp32 gradients."""
+
+    def __init__(self, hla, torch, synth, seed, top_k):
+        super().__init__(hla, torch, synth, seed, top_k)
+        dev, H, d = self.q.device, self.H, self.d
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed + 7)
+        self.dout = torch.randn(self.q.shape, generator=g, device=dev).to(torch.bfloat16)
+        self.sel = torch.empty((H, -(-self.n_q // 64), top_k), dtype=torch.int32, device=dev)
+        self.st.absorb_evicted(self.kev, self.vev)
+        self.st.attend_chunk(self.q, self.kw, self.vw, top_k, out=self.out, sel_out=self.sel)
+        f32 = dict(dtype=torch.float32, device=dev)
+        self.dq = torch.empty((H, self.n_q, d), **f32)
+        self.dk, self.dv = (torch.empty((H, self.n_kv, d), **f32) for _ in range(2))
+        self.dS, self.dz = torch.empty((H, d, d), **f32), torch.empty((H, d), **f32)
+        self.dkev, self.dvev = (torch.empty((H, self.n_ev, d), **f32) for _ in range(2))
+        self.ws = torch.empty(hla.hf_backward_workspace_bytes(self.st.cfg), dtype=torch.uint8,
+                              device=dev)
+        self.hla, self.torch = hla, torch
+
+    def step(self, side=None, serial=False):
+        hla, st, d = self.hla, self.st, self.d
+        s = self.torch.cuda.current_stream().cuda_stream
+        r = hla.hf_attend_backward(
+            st.handle, self.q.data_ptr(), self.n_q, self.q.stride(0), self.kw.data_ptr(),
+            self.vw.data_ptr(), self.n_kv, self.kw.stride(0), self.sel.data_ptr(), self.top_k,
+            self.dout.data_ptr(), self.dout.stride(0), self.dq.data_ptr(), self.n_q * d,
+            self.dk.data_ptr(), self.dv.data_ptr(), self.n_kv * d, self.dS.data_ptr(),
+            self.dz.data_ptr(), self.ws.data_ptr(), self.ws.numel(), s)
+        if r == hla.HF_OK:
+            r = hla.hf_absorb_backward(st.handle, self.kev.data_ptr(), self.vev.data_ptr(),
+                                       self.n_ev, self.kev.stride(0), self.dS.data_ptr(),
+                                       self.dz.data_ptr(), self.dkev.data_ptr(),
+                                       self.dvev.data_ptr(), self.n_ev * d, s)
+        if r != hla.HF_OK:
+            raise hla.HfError(r, "backward")
+
+    def bwd_flops(self):
+        """FLOPs per kernel. pairs = executed (query row, key row) pairs. Flash-attention
+        convention for the whole pass: 10 d per pair (scores, dp, dq, dk, dv). Executed
+        by each kernel, which is what each must compute without stored statistics:
+        bwd_dq 10 d per pair (pass 1: scores, p v; pass 2: scores, dp, dq) + 6 n_q d^2
+        (S f, S^T g, and their reduction terms counted as the two products), bwd_dkv
+        8 d per pair, bwd_state 2 n_q d^2 + 2 n_q d, absorb_bwd 4 n_ev d^2."""
+        import numpy as np
+        sel = self.sel.cpu().numpy()
+        H, n_q, d, B = self.H, self.n_q, self.d, 64
+        nqb, nkb = -(-n_q // B), -(-self.n_kv // B)
+        qrows = np.minimum(B, n_q - B * np.arange(nqb))
+        krows = np.minimum(B, self.n_kv - B * np.arange(nkb))
+        pairs = int((qrows[None, :, None] * krows[sel]).sum())
+        lin = 4 * n_q * d * d * H
+        return dict(convention=10 * d * pairs + lin + 2 * n_q * d * d * H + 4 * self.n_ev * d * d * H,
+                    bwd_dq=10 * d * pairs + lin, bwd_dkv=8 * d * pairs,
+                    bwd_state=2 * n_q * d * (d + 1) * H, absorb_bwd=4 * self.n_ev * d * d * H,
+                    pairs=pairs)
+
+
+def backward_main(args, torch, hla, synth, wl, top_k):
+    """--backward: K timed backward steps of the Wan-like layer; one JSON line."""
+    n_sets = max(1, args.sets)
+    sets = [BwdSet(hla, torch, synth, args.seed + i, top_k) for i in range(n_sets)]
+    torch.cuda.synchronize()
+    fl = [s.bwd_flops() for s in sets]
+    for k in range(args.warmup):
+        sets[k % n_sets].step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for k in range(args.steps):
+        sets[k % n_sets].step()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    for s in sets:
+        s.st.profile_start(args.steps + 2)
+    for k in range(args.steps):
+        sets[k % n_sets].step()
+    torch.cuda.synchronize()
+    tot = {}
+    for s in sets:
+        for name, (ms, n) in s.st.profile_stop().items():
+            a = tot.setdefault(name, [0.0, 0])
+            a[0] += ms
+            a[1] += n
+    kern_us = {k: v[0] / v[1] * 1e3 for k, v in tot.items() if v[1]}
+    log(f"[bench] backward {ms_step:.4f} ms/step; per-kernel us: {kern_us}")
+    mean = {k: statistics.mean(f[k] for f in fl) for k in fl[0]}
+    peak = 157.3  # MI355X fp32 vector TFLOP/s (the kernels use no MFMA)
+    kernels = {k: dict(avg_us=round(kern_us[k], 2), algo_flop=int(mean[k]),
+                       tflops=round(mean[k] / (kern_us[k] * 1e-6) / 1e12, 2))
+               for k in ("bwd_dq", "bwd_dkv", "bwd_state", "absorb_bwd") if k in kern_us}
+    kernels["bwd_index"] = dict(avg_us=round(kern_us.get("bwd_index", 0.0), 2))
+    dom = max(("bwd_dq", "bwd_dkv"), key=lambda k: kern_us[k])
+    achieved = mean[dom] / (kern_us[dom] * 1e-6) / 1e12
+    value = mean["convention"] / (ms_step * 1e-3) / 1e12
+    s0 = sets[0]
+    print(json.dumps({
+        "metric": "hybrid-attention backward ms/chunk/layer and effective TFLOP/s "
+                  "(flash-attention convention), 1 GPU",
+        "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16 inputs, fp32 arithmetic",
+        "data": "synthetic (seeded N(0,1)/sqrt(d) bf16 Q/K/V, N(0,1) bf16 dout)",
+        "config": {"workload": f"backward of {args.workload}: {s0.H} heads, d={s0.d}, "
+                               f"{s0.n_q} query / {s0.n_kv} window / {s0.n_ev} evicted "
+                               f"tokens, top-K {top_k}, forward selection held fixed",
+                   "input_sets": n_sets, "executed_pairs": int(mean["pairs"])},
+        "kernels": kernels,
+        "roofline": dict(bound="alu", achieved=round(achieved, 2), peak=peak, unit="TFLOP/s",
+                         frac=round(achieved / peak, 4), traffic=None, kernel=dom,
+                         flop_per_launch=int(mean[dom]), avg_launch_us=round(kern_us[dom], 2)),
+        "cpu_baseline": None,
+    }), flush=True)
+
+
 def cpu_baseline(layer: LayerSet, reps: int):
     """The float64 oracle on the host cores: the same layer step, median of `reps`."""
     import numpy as np
@@ -294,6 +415,11 @@ def main():
     top_k = synth.top_k_count(wl.top_k_frac, -(-wl.window_tokens // wl.block))
     n_sets = wl.layers if args.workload == "full_depth_bf16" else max(1, args.sets)
     t0 = time.time()
+    if args.backward:
+        if args.workload != "wan_layer_bf16":
+            sys.exit("--backward runs the wan_layer_bf16 shapes")
+        backward_main(args, torch, hla, synth, wl, top_k)
+        return
     streams = args.streams or args.cached_pooling or args.managed_window
     if streams and args.workload != "wan_layer_bf16":
         sys.exit("--streams / --cached-pooling / --managed-window run the wan_layer_bf16 shapes")

@@ -98,7 +98,8 @@ EXPORTED = ("hf_workspace_bytes", "hf_state_init", "hf_absorb_evicted", "hf_atte
             "hf_backward_workspace_bytes", "hf_attend_backward", "hf_absorb_backward",
             "hf_profile_start",
             "hf_profile_stop", "hf_next_ev_index", "hf_state_destroy", "hf_status_string")
-HF_KERNEL_NAMES = ("absorb", "block_pool", "score_select", "sparse_swa")
+HF_KERNEL_NAMES = ("absorb", "block_pool", "score_select", "sparse_swa", "bwd_index", "bwd_dq",
+                   "bwd_dkv", "bwd_state", "absorb_bwd")
 
 
 def library_path() -> str:

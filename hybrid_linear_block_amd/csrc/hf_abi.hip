@@ -43,7 +43,7 @@ struct hf_state {
   bool prof_on = false;
   int prof_cap = 0;
   std::vector<hipEvent_t> prof_ev[HF_KERNEL_COUNT];  // start/end pairs
-  int prof_n[HF_KERNEL_COUNT] = {0, 0, 0, 0};
+  int prof_n[HF_KERNEL_COUNT] = {};
 };
 
 namespace {
@@ -716,7 +716,12 @@ hf_status hf_attend_backward(hf_state* st, const void* q, int64_t n_q, int64_t q
   a.nqb_cap = st->nqb_cap;
   hipStream_t s = static_cast<hipStream_t>(stream);
   return on_device(st->device, [&]() {
-    return hf::launch_attend_backward(c.dtype, c.head_dim, c.block_size, a, s);
+    hipError_t r = hipSuccess;
+    for (int stage = 0; stage < 4 && r == hipSuccess; ++stage)
+      r = timed(st, HF_KERNEL_BWD_INDEX + stage, s, [&]() {
+        return hf::launch_attend_backward(c.dtype, c.head_dim, c.block_size, a, stage, s);
+      });
+    return r;
   });
 }
 
@@ -735,8 +740,10 @@ hf_status hf_absorb_backward(hf_state* st, const void* k_ev, const void* v_ev, i
   if (!dS || !dz || !aligned16(dS) || !aligned16(dz)) return HF_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
   return on_device(st->device, [&]() {
-    return hf::launch_absorb_backward(c.dtype, c.num_heads, c.head_dim, k_ev, v_ev, n_ev,
-                                      ev_head_stride, dS, dz, dk_ev, dv_ev, dev_head_stride, s);
+    return timed(st, HF_KERNEL_ABSORB_BWD, s, [&]() {
+      return hf::launch_absorb_backward(c.dtype, c.num_heads, c.head_dim, k_ev, v_ev, n_ev,
+                                        ev_head_stride, dS, dz, dk_ev, dv_ev, dev_head_stride, s);
+    });
   });
 }
 

@@ -39,22 +39,90 @@ __device__ __forceinline__ float ldf(const bf16_t* p) { return bf16_to_f32(*p); 
 
 __device__ __forceinline__ float phi_prime(float x) { return x > 0.f ? 1.f : __expf(x); }
 
+// Sum over the TPR adjacent lanes of a row; every lane gets the same bits (xor
+// butterfly, commutative adds). Within a quad the exchanges are DPP quad
+// permutations (no LDS round trip); wider rows use ds_bpermute for the rest.
+__device__ __forceinline__ float dpp_xor1(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+      0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));  // quad_perm [1,0,3,2]
+}
+__device__ __forceinline__ float dpp_xor2(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+      0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));  // quad_perm [2,3,0,1]
+}
+__device__ __forceinline__ float dpp_half_mirror(float x) {  // lane i <- 7 - i in each 8
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+      0, __builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_mirror(float x) {  // lane i <- 15 - i in each 16
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+      0, __builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false));
+}
+// After the quad steps every lane holds its quad's sum; the mirrors pair each lane
+// with one in the other quad (then the other half of 16), so the adds stay
+// commutative pairs and all TPR lanes end with the same bits.
 template <int TPR>
 __device__ __forceinline__ float row_sum(float x) {
-#pragma unroll
-  for (int m = 1; m < TPR; m <<= 1) x += __shfl_xor(x, m, 64);
+  static_assert(TPR >= 1 && TPR <= 16, "rows of up to 16 lanes");
+  if (TPR >= 2) x += dpp_xor1(x);
+  if (TPR >= 4) x += dpp_xor2(x);
+  if (TPR >= 8) x += dpp_half_mirror(x);
+  if (TPR >= 16) x += dpp_mirror(x);
   return x;
 }
 
 __device__ __forceinline__ int clamp_block(int j, int n) { return j < 0 ? 0 : (j >= n ? n - 1 : j); }
 
-// rows [row0, row0 + BLK) of a [N][D] head into an fp32 tile; rows >= n read as 0.
-template <typename T, int D, int BLK>
+__device__ __forceinline__ void widen_store(float* o, uint4 w, const bf16_t*, bool ph) {
+  const uint32_t x[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    float lo = __uint_as_float(x[k] << 16), hi = __uint_as_float(x[k] & 0xffff0000u);
+    if (ph) {
+      lo = phi(lo);
+      hi = phi(hi);
+    }
+    o[2 * k] = lo;
+    o[2 * k + 1] = hi;
+  }
+}
+__device__ __forceinline__ void widen_store(float* o, uint4 w, const float*, bool ph) {
+  float4 f = make_float4(__uint_as_float(w.x), __uint_as_float(w.y), __uint_as_float(w.z),
+                         __uint_as_float(w.w));
+  if (ph) f = make_float4(phi(f.x), phi(f.y), phi(f.z), phi(f.w));
+  *reinterpret_cast<float4*>(o) = f;
+}
+
+// Rows [row0, row0 + R) of a [N][D] head into an fp32 tile (phi applied if PHI);
+// rows >= n read as 0. Every 16-byte load of the workgroup's share is issued before
+// the first LDS store, so the memory latency is paid once per tile.
+template <typename T, int D, int R, bool PHI = false>
 __device__ __forceinline__ void load_tile(const T* __restrict__ base, int64_t row0, int64_t n,
                                           float* tile) {
-  for (int e = threadIdx.x; e < BLK * D; e += BT) {
-    const int64_t r = row0 + e / D;
-    tile[e] = r < n ? ldf(base + r * D + (e % D)) : 0.f;
+  constexpr int EPV = 16 / (int)sizeof(T);  // elements per 16-byte load
+  constexpr int NV = R * D / EPV;
+  constexpr int PER = (NV + BT - 1) / BT;
+  uint4 buf[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int v = threadIdx.x + k * BT;
+    const int64_t r = row0 + (v * EPV) / D;
+    buf[k] = (v < NV && r < n)
+                 ? *reinterpret_cast<const uint4*>(base + r * D + (v * EPV) % D)
+                 : make_uint4(0u, 0u, 0u, 0u);
+  }
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int v = threadIdx.x + k * BT;
+    if (v < NV) {
+      const int64_t r = row0 + (v * EPV) / D;
+      if (PHI && r >= n) {
+#pragma unroll
+        for (int x = 0; x < EPV; ++x) tile[v * EPV + x] = 0.f;
+      } else {
+        widen_store(tile + v * EPV, buf[k], base, PHI);
+      }
+    }
   }
 }
 
@@ -78,20 +146,29 @@ __global__ void bwd_inv_sel(const int32_t* __restrict__ sel, int heads, int nqb,
   cnt[x] = n;
 }
 
+// Query rows per workgroup of bwd_rows and key rows per workgroup of bwd_kv, and
+// the rows of their staged tiles: 32 (16 for 16-row blocks), so that two 32-row
+// fp32 tiles (32 KB at d = 128) and a 16-feature slice per lane leave room for
+// several workgroups per compute unit.
+template <int BLK>
+constexpr int kRows = BLK > 32 ? 32 : BLK;
+
 template <typename T, int D, int BLK>
-__global__ __launch_bounds__(BT) void bwd_rows(
+__global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(4))) void bwd_rows(
     const T* __restrict__ q, int64_t n_q, int64_t q_hs, const T* __restrict__ kg,
     const T* __restrict__ vg, int64_t n_kv, int64_t kv_hs, const int32_t* __restrict__ sel,
     int top_k, int nqb, int nkb, const float* __restrict__ S, const float* __restrict__ z,
     float eps, float scale, const T* __restrict__ dout, int64_t do_hs, float* __restrict__ dq,
     int64_t dq_hs, float* __restrict__ rs, int64_t nq_cap) {
-  constexpr int TPR = BT / BLK, DS = D / TPR;
+  constexpr int RPW = kRows<BLK>, KT = RPW, SPLIT = BLK / RPW;
+  constexpr int TPR = BT / RPW, DS = D / TPR;
   static_assert(DS % 4 == 0, "float4 slices");
-  __shared__ __align__(16) float tk[BLK * D];
-  __shared__ __align__(16) float tv[BLK * D];
-  const int h = blockIdx.x / nqb, i = blockIdx.x % nqb;
+  __shared__ __align__(16) float tk[KT * D];
+  __shared__ __align__(16) float tv[KT * D];
+  const int h = blockIdx.x / (nqb * SPLIT), i = (blockIdx.x / SPLIT) % nqb;
+  const int part = blockIdx.x % SPLIT;
   const int rl = threadIdx.x / TPR, d0 = (threadIdx.x % TPR) * DS;
-  const int64_t r = (int64_t)i * BLK + rl;
+  const int64_t r = (int64_t)i * BLK + part * RPW + rl;
   const bool live = r < n_q;
   const int64_t rr = live ? r : n_q - 1;
   const T* kh = kg + (int64_t)h * kv_hs;
@@ -110,14 +187,47 @@ __global__ __launch_bounds__(BT) void bwd_rows(
 
   // ---- pass 1: softmax statistics and o_swa (online, base 2) ----
   float m2 = -INFINITY, l = 0.f;
-  for (int t = 0; t < top_k; ++t) {
-    const int jb = clamp_block(my_sel[t], nkb);
+  for (int tt = 0; tt < top_k * SPLIT; ++tt) {
+    const int64_t k0 = (int64_t)clamp_block(my_sel[tt / SPLIT], nkb) * BLK + (tt % SPLIT) * KT;
+    if (k0 >= n_kv) continue;  // the ragged last block has no second half
     __syncthreads();
-    load_tile<T, D, BLK>(kh, (int64_t)jb * BLK, n_kv, tk);
-    load_tile<T, D, BLK>(vh, (int64_t)jb * BLK, n_kv, tv);
+    load_tile<T, D, KT>(kh, k0, n_kv, tk);
+    load_tile<T, D, KT>(vh, k0, n_kv, tv);
     __syncthreads();
-    const int nvalid = (int)min((int64_t)BLK, n_kv - (int64_t)jb * BLK);
-    for (int u = 0; u < nvalid; ++u) {
+    const int nvalid = (int)min((int64_t)KT, n_kv - k0);
+    // Keys in groups of 4 (independent dot products, one max update per group),
+    // then the remainder one by one.
+    int u = 0;
+    for (; u + 4 <= nvalid; u += 4) {
+      float x[4];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float* kr = tk + (u + w) * D + d0;
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < DS; ++e) s += qv[e] * kr[e];
+        x[w] = s;
+      }
+#pragma unroll
+      for (int w = 0; w < 4; ++w) x[w] = row_sum<TPR>(x[w]) * sl2;
+      const float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      if (mx > m2) {
+        const float a = exp2f(m2 - mx);
+        l *= a;
+#pragma unroll
+        for (int e = 0; e < DS; ++e) acc[e] *= a;
+        m2 = mx;
+      }
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float p = exp2f(x[w] - m2);
+        l += p;
+        const float* vr = tv + (u + w) * D + d0;
+#pragma unroll
+        for (int e = 0; e < DS; ++e) acc[e] += p * vr[e];
+      }
+    }
+    for (; u < nvalid; ++u) {
       const float* kr = tk + u * D + d0;
       float s = 0.f;
 #pragma unroll
@@ -196,13 +306,15 @@ __global__ __launch_bounds__(BT) void bwd_rows(
   for (int e = 0; e < DS; ++e) acc[e] = phi_prime(qv[e]) * (dql[e] + c * zh[d0 + e]);
 
   // ---- pass 2: dq of the softmax path ----
-  for (int t = 0; t < top_k; ++t) {
-    const int jb = clamp_block(my_sel[t], nkb);
+  for (int tt = 0; tt < top_k * SPLIT; ++tt) {
+    const int64_t k0 = (int64_t)clamp_block(my_sel[tt / SPLIT], nkb) * BLK + (tt % SPLIT) * KT;
+    if (k0 >= n_kv) continue;
     __syncthreads();
-    load_tile<T, D, BLK>(kh, (int64_t)jb * BLK, n_kv, tk);
-    load_tile<T, D, BLK>(vh, (int64_t)jb * BLK, n_kv, tv);
+    load_tile<T, D, KT>(kh, k0, n_kv, tk);
+    load_tile<T, D, KT>(vh, k0, n_kv, tv);
     __syncthreads();
-    const int nvalid = (int)min((int64_t)BLK, n_kv - (int64_t)jb * BLK);
+    const int nvalid = (int)min((int64_t)KT, n_kv - k0);
+#pragma unroll 2
     for (int u = 0; u < nvalid; ++u) {
       const float* kr = tk + u * D + d0;
       const float* vr = tv + u * D + d0;
@@ -241,13 +353,15 @@ __global__ __launch_bounds__(BT) void bwd_kv(
     const T* __restrict__ dout, int64_t do_hs, const float* __restrict__ rs, int64_t nq_cap,
     const int32_t* __restrict__ cnt, const int32_t* __restrict__ list, int nqb_cap,
     float* __restrict__ dk, float* __restrict__ dv, int64_t dkv_hs) {
-  constexpr int TPR = BT / BLK, DS = D / TPR;
-  __shared__ __align__(16) float tq[BLK * D];
-  __shared__ __align__(16) float tdo[BLK * D];
-  __shared__ float tst[BLK * 2];
-  const int h = blockIdx.x / nkb, jb = blockIdx.x % nkb;
+  constexpr int RPW = kRows<BLK>, QT = RPW, SPLIT = BLK / RPW;
+  constexpr int TPR = BT / RPW, DS = D / TPR;
+  __shared__ __align__(16) float tq[QT * D];
+  __shared__ __align__(16) float tdo[QT * D];
+  __shared__ float tst[QT * 2];
+  const int h = blockIdx.x / (nkb * SPLIT), jb = (blockIdx.x / SPLIT) % nkb;
+  const int part = blockIdx.x % SPLIT;
   const int kl = threadIdx.x / TPR, d0 = (threadIdx.x % TPR) * DS;
-  const int64_t t = (int64_t)jb * BLK + kl;
+  const int64_t t = (int64_t)jb * BLK + part * RPW + kl;
   const bool live = t < n_kv;
   const int64_t tt = live ? t : n_kv - 1;
   const T* qh = q + (int64_t)h * q_hs;
@@ -262,19 +376,21 @@ __global__ __launch_bounds__(BT) void bwd_kv(
   const float sl2 = scale * kL2e;
   const int64_t slot = (int64_t)h * nkb + jb;
   const int n_sel = cnt[slot];
-  for (int x = 0; x < n_sel; ++x) {
-    const int i = list[slot * nqb_cap + x];
+  for (int x = 0; x < n_sel * SPLIT; ++x) {
+    const int64_t q0 = (int64_t)list[slot * nqb_cap + x / SPLIT] * BLK + (x % SPLIT) * QT;
+    if (q0 >= n_q) continue;  // the ragged last query block has no second half
     __syncthreads();
-    load_tile<T, D, BLK>(qh, (int64_t)i * BLK, n_q, tq);
-    load_tile<T, D, BLK>(doh, (int64_t)i * BLK, n_q, tdo);
-    for (int e = threadIdx.x; e < BLK; e += BT) {
-      const int64_t r = (int64_t)i * BLK + e;
+    load_tile<T, D, QT>(qh, q0, n_q, tq);
+    load_tile<T, D, QT>(doh, q0, n_q, tdo);
+    for (int e = threadIdx.x; e < QT; e += BT) {
+      const int64_t r = q0 + e;
       const float* st = rs + ((int64_t)h * nq_cap + (r < n_q ? r : n_q - 1)) * 4;
       tst[2 * e] = st[0];
       tst[2 * e + 1] = st[1];
     }
     __syncthreads();
-    const int nvalid = (int)min((int64_t)BLK, n_q - (int64_t)i * BLK);
+    const int nvalid = (int)min((int64_t)QT, n_q - q0);
+#pragma unroll 2
     for (int u = 0; u < nvalid; ++u) {
       const float* qr = tq + u * D + d0;
       const float* dr = tdo + u * D + d0;
@@ -314,7 +430,7 @@ __global__ __launch_bounds__(BT) void bwd_state(const T* __restrict__ q, int64_t
                                                 int64_t nq_cap, float* __restrict__ dS,
                                                 float* __restrict__ dz) {
   constexpr int RC = 32, NJ = 8, JPT = NJ * D / BT;  // rows per chunk, dS rows, outputs/thread
-  __shared__ float tf[RC * D];
+  __shared__ __align__(16) float tf[RC * D];
   __shared__ float tg[RC * NJ];
   constexpr int NT = D / NJ + 1;
   const int h = blockIdx.x / NT, jt = blockIdx.x % NT;
@@ -328,10 +444,7 @@ __global__ __launch_bounds__(BT) void bwd_state(const T* __restrict__ q, int64_t
   for (int e = 0; e < JPT; ++e) a[e] = 0.f;
   for (int64_t r0 = 0; r0 < n_q; r0 += RC) {
     __syncthreads();
-    for (int e = threadIdx.x; e < RC * D; e += BT) {
-      const int64_t r = r0 + e / D;
-      tf[e] = r < n_q ? phi(ldf(qh + r * D + (e % D))) : 0.f;
-    }
+    load_tile<T, D, RC, true>(qh, r0, n_q, tf);
     for (int e = threadIdx.x; e < RC * NJ; e += BT) {
       const int64_t r = r0 + e / NJ;
       float g = 0.f;
@@ -369,13 +482,17 @@ __global__ __launch_bounds__(BT) void absorb_bwd(const T* __restrict__ k, const 
   constexpr int BLK = 64, TPR = BT / BLK, DS = D / TPR;
   __shared__ __align__(16) float tf[BLK * D];
   __shared__ __align__(16) float tv[BLK * D];
+  __shared__ __align__(16) float tS[D * D];  // dS of the head, read by every token
   const int h = blockIdx.x / ntile, tile = blockIdx.x % ntile;
   const int nl = threadIdx.x / TPR, d0 = (threadIdx.x % TPR) * DS;
   const int64_t n = (int64_t)tile * BLK + nl;
   const bool live = n < n_ev;
   const int64_t nn = live ? n : n_ev - 1;
-  const float* Sh = dS + (int64_t)h * D * D;
   const float* zh = dz + (int64_t)h * D;
+  for (int e = threadIdx.x; e < D * D / 4; e += BT)
+    reinterpret_cast<float4*>(tS)[e] =
+        reinterpret_cast<const float4*>(dS + (int64_t)h * D * D)[e];
+  const float* Sh = tS;
   float kx[DS];
 #pragma unroll
   for (int e = 0; e < DS; ++e) {
@@ -423,22 +540,26 @@ __global__ __launch_bounds__(BT) void absorb_bwd(const T* __restrict__ k, const 
 }
 
 template <typename T, int D, int BLK>
-hipError_t run_attend_bwd(const BwdArgs& a, hipStream_t s) {
+hipError_t run_attend_bwd(const BwdArgs& a, int stage, hipStream_t s) {
   const int nqb = (int)((a.n_q + BLK - 1) / BLK), nkb = (int)((a.n_kv + BLK - 1) / BLK);
   const int64_t inv_n = (int64_t)a.heads * nkb;
-  bwd_inv_sel<<<(unsigned)((inv_n + 255) / 256), 256, 0, s>>>(a.sel, a.heads, nqb, nkb, a.top_k,
-                                                              a.inv_cnt, a.inv_list, a.nqb_cap);
-  bwd_rows<T, D, BLK><<<(unsigned)(a.heads * nqb), BT, 0, s>>>(
-      static_cast<const T*>(a.q), a.n_q, a.q_hs, static_cast<const T*>(a.k),
-      static_cast<const T*>(a.v), a.n_kv, a.kv_hs, a.sel, a.top_k, nqb, nkb, a.S, a.z, a.eps,
-      a.scale, static_cast<const T*>(a.dout), a.do_hs, a.dq, a.dq_hs, a.rowstats, a.nq_cap);
-  bwd_kv<T, D, BLK><<<(unsigned)(a.heads * nkb), BT, 0, s>>>(
-      static_cast<const T*>(a.q), a.n_q, a.q_hs, static_cast<const T*>(a.k),
-      static_cast<const T*>(a.v), a.n_kv, a.kv_hs, nkb, a.scale, static_cast<const T*>(a.dout),
-      a.do_hs, a.rowstats, a.nq_cap, a.inv_cnt, a.inv_list, a.nqb_cap, a.dk, a.dv, a.dkv_hs);
-  bwd_state<T, D><<<(unsigned)(a.heads * (D / 8 + 1)), BT, 0, s>>>(
-      static_cast<const T*>(a.q), a.n_q, a.q_hs, static_cast<const T*>(a.dout), a.do_hs,
-      a.rowstats, a.nq_cap, a.dS, a.dz);
+  if (stage == 0)
+    bwd_inv_sel<<<(unsigned)((inv_n + 255) / 256), 256, 0, s>>>(
+        a.sel, a.heads, nqb, nkb, a.top_k, a.inv_cnt, a.inv_list, a.nqb_cap);
+  if (stage == 1)
+    bwd_rows<T, D, BLK><<<(unsigned)(a.heads * nqb * (BLK / kRows<BLK>)), BT, 0, s>>>(
+        static_cast<const T*>(a.q), a.n_q, a.q_hs, static_cast<const T*>(a.k),
+        static_cast<const T*>(a.v), a.n_kv, a.kv_hs, a.sel, a.top_k, nqb, nkb, a.S, a.z, a.eps,
+        a.scale, static_cast<const T*>(a.dout), a.do_hs, a.dq, a.dq_hs, a.rowstats, a.nq_cap);
+  if (stage == 2)
+    bwd_kv<T, D, BLK><<<(unsigned)(a.heads * nkb * (BLK / kRows<BLK>)), BT, 0, s>>>(
+        static_cast<const T*>(a.q), a.n_q, a.q_hs, static_cast<const T*>(a.k),
+        static_cast<const T*>(a.v), a.n_kv, a.kv_hs, nkb, a.scale, static_cast<const T*>(a.dout),
+        a.do_hs, a.rowstats, a.nq_cap, a.inv_cnt, a.inv_list, a.nqb_cap, a.dk, a.dv, a.dkv_hs);
+  if (stage == 3)
+    bwd_state<T, D><<<(unsigned)(a.heads * (D / 8 + 1)), BT, 0, s>>>(
+        static_cast<const T*>(a.q), a.n_q, a.q_hs, static_cast<const T*>(a.dout), a.do_hs,
+        a.rowstats, a.nq_cap, a.dS, a.dz);
   return hipGetLastError();
 }
 
@@ -455,15 +576,16 @@ hipError_t run_absorb_bwd(int heads, const void* k, const void* v, int64_t n_ev,
 
 }  // namespace
 
-hipError_t launch_attend_backward(int dtype, int d, int block, const BwdArgs& a, hipStream_t s) {
+hipError_t launch_attend_backward(int dtype, int d, int block, const BwdArgs& a, int stage,
+                                  hipStream_t s) {
   if (dtype == 0) {
-    if (block == 64 && d == 128) return run_attend_bwd<bf16_t, 128, 64>(a, s);
-    if (block == 64 && d == 64) return run_attend_bwd<bf16_t, 64, 64>(a, s);
+    if (block == 64 && d == 128) return run_attend_bwd<bf16_t, 128, 64>(a, stage, s);
+    if (block == 64 && d == 64) return run_attend_bwd<bf16_t, 64, 64>(a, stage, s);
   } else {
-    if (block == 16 && d == 64) return run_attend_bwd<float, 64, 16>(a, s);
-    if (block == 16 && d == 128) return run_attend_bwd<float, 128, 16>(a, s);
-    if (block == 64 && d == 64) return run_attend_bwd<float, 64, 64>(a, s);
-    if (block == 64 && d == 128) return run_attend_bwd<float, 128, 64>(a, s);
+    if (block == 16 && d == 64) return run_attend_bwd<float, 64, 16>(a, stage, s);
+    if (block == 16 && d == 128) return run_attend_bwd<float, 128, 16>(a, stage, s);
+    if (block == 64 && d == 64) return run_attend_bwd<float, 64, 64>(a, stage, s);
+    if (block == 64 && d == 128) return run_attend_bwd<float, 128, 64>(a, stage, s);
   }
   return hipErrorInvalidValue;
 }

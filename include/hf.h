@@ -303,7 +303,12 @@ typedef enum {
   HF_KERNEL_SCORE_SELECT = 2, /* block scores + top-K selection (in a one-stream
                                  hf_absorb_and_attend also the absorb's reduce) */
   HF_KERNEL_SPARSE_SWA = 3,   /* block-sparse attention + linear read + sum */
-  HF_KERNEL_COUNT = 4
+  HF_KERNEL_BWD_INDEX = 4,    /* hf_attend_backward: inverse selection index */
+  HF_KERNEL_BWD_DQ = 5,       /* hf_attend_backward: dq and per-row statistics */
+  HF_KERNEL_BWD_DKV = 6,      /* hf_attend_backward: dk and dv */
+  HF_KERNEL_BWD_STATE = 7,    /* hf_attend_backward: dS and dz */
+  HF_KERNEL_ABSORB_BWD = 8,   /* hf_absorb_backward */
+  HF_KERNEL_COUNT = 9
 } hf_kernel;
 
 /* Profiling aid (not needed for results). From this call on, every kernel the

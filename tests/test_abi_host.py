@@ -98,6 +98,19 @@ def test_workspace_bytes():
         assert hla.hf_workspace_bytes(cfg(**bad)) == 0, bad
 
 
+def test_backward_workspace_bytes():
+    """Per-row statistics (4 fp32 per query row and head) and the inverse selection
+    index (a count and a list of query blocks per key block and head), 256-byte
+    aligned pieces."""
+    c = cfg()
+    H, B_ = c.num_heads, c.block_size
+    nqb, nkb = -(-c.max_n_q // B_), -(-c.max_n_kv // B_)
+    up = lambda x: -(-x // 256) * 256  # noqa: E731
+    expect = up(H * c.max_n_q * 16) + up(H * nkb * 4) + up(H * nkb * nqb * 4)
+    assert hla.hf_backward_workspace_bytes(c) == expect
+    assert hla.hf_backward_workspace_bytes(cfg(head_dim=96)) == 0
+
+
 def test_state_init_validation():
     c = cfg()
     ws = hla.hf_workspace_bytes(c)

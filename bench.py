@@ -303,6 +303,33 @@ class BwdSet(LayerSet):
                     pairs=pairs)
 
 
+def cpu_baseline_backward(bset: "BwdSet", conv_flop: float):
+    """The float64 backward oracle on the host cores, on a bounded sample: head 0 of
+    the layer (every query block, its selection from the device), scaled by the head
+    count (heads are independent and equally sized)."""
+    import numpy as np
+    import oracle
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        cores = max((i.get("num_threads") or 1) for i in info) if info else 1
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    f64 = lambda t: t[:1].float().cpu().numpy().astype(np.float64)  # noqa: E731
+    q, k, v, do = f64(bset.q), f64(bset.kw), f64(bset.vw), f64(bset.dout)
+    kev, vev = f64(bset.kev), f64(bset.vev)
+    S = bset.st.S[:1].double().cpu().numpy()
+    z = bset.st.z[:1].double().cpu().numpy()
+    sel = bset.sel[:1].cpu().numpy()
+    t0 = time.perf_counter()
+    _, _, _, dS, dz = oracle.attend_with_sel_backward(q, k, v, sel, S, z, do, 64)
+    oracle.absorb_backward(kev, vev, dS, dz)
+    t = (time.perf_counter() - t0) * bset.H
+    return dict(value=conv_flop / t / 1e12, unit="TFLOP/s", cores=int(cores), kind="oracle",
+                sample=f"head 0 of {bset.H} (all query blocks, device selection), float64 "
+                       f"NumPy, scaled x{bset.H}", ms_per_step=t * 1e3)
+
+
 def backward_main(args, torch, hla, synth, wl, top_k):
     """--backward: K timed backward steps of the Wan-like layer; one JSON line."""
     n_sets = max(1, args.sets)
@@ -342,6 +369,10 @@ def backward_main(args, torch, hla, synth, wl, top_k):
     achieved = mean[dom] / (kern_us[dom] * 1e-6) / 1e12
     value = mean["convention"] / (ms_step * 1e-3) / 1e12
     s0 = sets[0]
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the float64 backward oracle on the host (one head) ...")
+        cpu = cpu_baseline_backward(s0, fl[0]["convention"])
     print(json.dumps({
         "metric": "hybrid-attention backward ms/chunk/layer and effective TFLOP/s "
                   "(flash-attention convention), 1 GPU",
@@ -357,7 +388,7 @@ def backward_main(args, torch, hla, synth, wl, top_k):
         "roofline": dict(bound="alu", achieved=round(achieved, 2), peak=peak, unit="TFLOP/s",
                          frac=round(achieved / peak, 4), traffic=None, kernel=dom,
                          flop_per_launch=int(mean[dom]), avg_launch_us=round(kern_us[dom], 2)),
-        "cpu_baseline": None,
+        "cpu_baseline": cpu,
     }), flush=True)
 
 

@@ -24,6 +24,8 @@
 //   absorb_bwd   per (head, 64 evicted tokens): dk_ev and dv_ev.
 // A row's dot products are split over TPR adjacent lanes (DS features each) and
 // reduced with xor shuffles; K/V or Q/dout tiles are staged in LDS as fp32.
+#include <type_traits>
+
 #include "hf_device.h"
 #include "hf_launch.h"
 
@@ -422,6 +424,135 @@ __global__ __launch_bounds__(BT) void bwd_kv(
   }
 }
 
+// bf16 dk and dv on MFMA (v_mfma_f32_16x16x32_bf16), one workgroup per (head, 64-key
+// block), wave w owning keys 16w .. 16w + 15, over the query blocks that selected the
+// block. Per 64-row query block: S = Q K^T and dP = dO V^T (K and V of the wave's keys
+// stay in registers as the B operands), P = exp2(S tau log2e - lse), dL = tau P (dP -
+// D); then dV^T += dO^T P and dK^T += Q^T dL. The contraction over queries takes its
+// k order from the result layout of S (a lane holds queries 4g .. 4g + 3 of two
+// 16-query tiles), so P and dL become B operands in registers, split into bf16 hi and
+// lo parts (Q and dO are exact bf16, so the products keep ~fp32 accuracy), while dO^T
+// and Q^T are read as A operands from transposed copies staged in LDS.
+template <int D>
+__global__ __launch_bounds__(BT) void bwd_kv_mfma(
+    const bf16_t* __restrict__ q, int64_t n_q, int64_t q_hs, const bf16_t* __restrict__ kg,
+    const bf16_t* __restrict__ vg, int64_t n_kv, int64_t kv_hs, int nkb, float scale,
+    const bf16_t* __restrict__ dout, int64_t do_hs, const float* __restrict__ rs, int64_t nq_cap,
+    const int32_t* __restrict__ cnt, const int32_t* __restrict__ list, int nqb_cap,
+    float* __restrict__ dk, float* __restrict__ dv, int64_t dkv_hs) {
+  constexpr int BLK = 64, NKS = D / 32, NE = D / 16;
+  constexpr int RS = D + 8;    // row stride of the row-major copies (bf16)
+  constexpr int TS = BLK + 8;  // row stride of the transposed copies (bf16)
+  typedef Mfma<bf16_t> M;
+  __shared__ __align__(16) bf16_t qs[BLK * RS];
+  __shared__ __align__(16) bf16_t dos[BLK * RS];
+  __shared__ __align__(16) bf16_t qt[D * TS];
+  __shared__ __align__(16) bf16_t dot_[D * TS];
+  __shared__ float tst[BLK * 2];
+  const int h = blockIdx.x / nkb, jb = blockIdx.x % nkb;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const float sl2 = scale * kL2e;
+  const int64_t key = (int64_t)jb * BLK + w * 16 + c;
+  const bool kvalid = key < n_kv;
+  bf16x8 kop[NKS], vop[NKS];
+#pragma unroll
+  for (int s = 0; s < NKS; ++s) {
+    const int64_t off = (int64_t)h * kv_hs + key * D + 32 * s + 8 * g;
+    kop[s] = as_bf16x8(kvalid ? *reinterpret_cast<const uint4*>(kg + off) : zero4());
+    vop[s] = as_bf16x8(kvalid ? *reinterpret_cast<const uint4*>(vg + off) : zero4());
+  }
+  f32x4 dvT[NE], dkT[NE];
+#pragma unroll
+  for (int e = 0; e < NE; ++e) dvT[e] = dkT[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const bf16_t* qh = q + (int64_t)h * q_hs;
+  const bf16_t* doh = dout + (int64_t)h * do_hs;
+  const int64_t slot = (int64_t)h * nkb + jb;
+  const int n_sel = cnt[slot];
+  for (int x = 0; x < n_sel; ++x) {
+    const int64_t q0 = (int64_t)list[slot * nqb_cap + x] * BLK;
+    __syncthreads();  // every wave is done with the previous query block
+    for (int v = threadIdx.x; v < BLK * (D / 8); v += BT) {
+      const int r = v % BLK, ch = v / BLK;  // consecutive lanes take consecutive rows
+      const int64_t row = q0 + r;
+      const uint4 a = row < n_q ? *reinterpret_cast<const uint4*>(qh + row * D + ch * 8) : zero4();
+      const uint4 b =
+          row < n_q ? *reinterpret_cast<const uint4*>(doh + row * D + ch * 8) : zero4();
+      *reinterpret_cast<uint4*>(qs + r * RS + ch * 8) = a;
+      *reinterpret_cast<uint4*>(dos + r * RS + ch * 8) = b;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        qt[(ch * 8 + i) * TS + r] = (bf16_t)half16(a, i);
+        dot_[(ch * 8 + i) * TS + r] = (bf16_t)half16(b, i);
+      }
+    }
+    for (int e = threadIdx.x; e < BLK; e += BT) {
+      const int64_t row = q0 + e;
+      const float* st = rs + ((int64_t)h * nq_cap + (row < n_q ? row : 0)) * 4;
+      tst[2 * e] = row < n_q ? st[0] : INFINITY;  // rows past the chunk: weight 0
+      tst[2 * e + 1] = row < n_q ? st[1] : 0.f;
+    }
+    __syncthreads();
+    float P[4][4], L[4][4];
+#pragma unroll
+    for (int nq = 0; nq < 4; ++nq) {
+      f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f}, pa = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) {
+        const int o = (16 * nq + c) * RS + 32 * s + 8 * g;
+        sa = M::mma(as_bf16x8(*reinterpret_cast<const uint4*>(qs + o)), kop[s], sa);
+        pa = M::mma(as_bf16x8(*reinterpret_cast<const uint4*>(dos + o)), vop[s], pa);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int ql = 16 * nq + 4 * g + r;
+        const float p = exp2f(sa[r] * sl2 - tst[2 * ql]);
+        P[nq][r] = p;
+        L[nq][r] = scale * p * (pa[r] - tst[2 * ql + 1]);
+      }
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      float pv[8], lv[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pv[i] = P[2 * kk][i];
+        pv[4 + i] = P[2 * kk + 1][i];
+        lv[i] = L[2 * kk][i];
+        lv[4 + i] = L[2 * kk + 1][i];
+      }
+      bf16x8 ph, pl, lh, ll;
+      split_bf16x8(pv, ph, pl);
+      split_bf16x8(lv, lh, ll);
+#pragma unroll
+      for (int e = 0; e < NE; ++e) {
+        const int o = (16 * e + c) * TS + 32 * kk + 4 * g;
+        const uint2 d0 = *reinterpret_cast<const uint2*>(dot_ + o);
+        const uint2 d1 = *reinterpret_cast<const uint2*>(dot_ + o + 16);
+        const uint2 q0v = *reinterpret_cast<const uint2*>(qt + o);
+        const uint2 q1v = *reinterpret_cast<const uint2*>(qt + o + 16);
+        const bf16x8 ado = as_bf16x8(make_uint4(d0.x, d0.y, d1.x, d1.y));
+        const bf16x8 aq = as_bf16x8(make_uint4(q0v.x, q0v.y, q1v.x, q1v.y));
+        dvT[e] = M::mma(ado, ph, dvT[e]);
+        dvT[e] = M::mma(ado, pl, dvT[e]);
+        dkT[e] = M::mma(aq, lh, dkT[e]);
+        dkT[e] = M::mma(aq, ll, dkT[e]);
+      }
+    }
+  }
+  if (kvalid) {
+    float* pk = dk + (int64_t)h * dkv_hs + key * D;
+    float* pv = dv + (int64_t)h * dkv_hs + key * D;
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+      *reinterpret_cast<float4*>(pk + 16 * e + 4 * g) =
+          make_float4(dkT[e][0], dkT[e][1], dkT[e][2], dkT[e][3]);
+      *reinterpret_cast<float4*>(pv + 16 * e + 4 * g) =
+          make_float4(dvT[e][0], dvT[e][1], dvT[e][2], dvT[e][3]);
+    }
+  }
+}
+
 // Workgroup (h, jt): jt < D / 8 forms dS rows 8 jt .. 8 jt + 7, jt == D / 8 forms dz.
 template <typename T, int D>
 __global__ __launch_bounds__(BT) void bwd_state(const T* __restrict__ q, int64_t n_q,
@@ -551,7 +682,13 @@ hipError_t run_attend_bwd(const BwdArgs& a, int stage, hipStream_t s) {
         static_cast<const T*>(a.q), a.n_q, a.q_hs, static_cast<const T*>(a.k),
         static_cast<const T*>(a.v), a.n_kv, a.kv_hs, a.sel, a.top_k, nqb, nkb, a.S, a.z, a.eps,
         a.scale, static_cast<const T*>(a.dout), a.do_hs, a.dq, a.dq_hs, a.rowstats, a.nq_cap);
-  if (stage == 2)
+  if (stage == 2 && std::is_same<T, bf16_t>::value && BLK == 64)
+    bwd_kv_mfma<D><<<(unsigned)(a.heads * nkb), BT, 0, s>>>(
+        static_cast<const bf16_t*>(a.q), a.n_q, a.q_hs, static_cast<const bf16_t*>(a.k),
+        static_cast<const bf16_t*>(a.v), a.n_kv, a.kv_hs, nkb, a.scale,
+        static_cast<const bf16_t*>(a.dout), a.do_hs, a.rowstats, a.nq_cap, a.inv_cnt, a.inv_list,
+        a.nqb_cap, a.dk, a.dv, a.dkv_hs);
+  else if (stage == 2)
     bwd_kv<T, D, BLK><<<(unsigned)(a.heads * nkb * (BLK / kRows<BLK>)), BT, 0, s>>>(
         static_cast<const T*>(a.q), a.n_q, a.q_hs, static_cast<const T*>(a.k),
         static_cast<const T*>(a.v), a.n_kv, a.kv_hs, nkb, a.scale, static_cast<const T*>(a.dout),

@@ -155,7 +155,9 @@ __global__ void bwd_inv_sel(const int32_t* __restrict__ sel, int heads, int nqb,
 template <int BLK>
 constexpr int kRows = BLK > 32 ? 32 : BLK;
 
-template <typename T, int D, int BLK>
+// LIN: only the linear read's terms, added to dq (which holds the softmax path's part,
+// written by bwd_dq_mfma together with lse and D); stores den and c only.
+template <typename T, int D, int BLK, bool LIN = false>
 __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(4))) void bwd_rows(
     const T* __restrict__ q, int64_t n_q, int64_t q_hs, const T* __restrict__ kg,
     const T* __restrict__ vg, int64_t n_kv, int64_t kv_hs, const int32_t* __restrict__ sel,
@@ -189,7 +191,7 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(4))) void bw
 
   // ---- pass 1: softmax statistics and o_swa (online, base 2) ----
   float m2 = -INFINITY, l = 0.f;
-  for (int tt = 0; tt < top_k * SPLIT; ++tt) {
+  for (int tt = 0; tt < (LIN ? 0 : top_k * SPLIT); ++tt) {
     const int64_t k0 = (int64_t)clamp_block(my_sel[tt / SPLIT], nkb) * BLK + (tt % SPLIT) * KT;
     if (k0 >= n_kv) continue;  // the ragged last block has no second half
     __syncthreads();
@@ -308,7 +310,7 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(4))) void bw
   for (int e = 0; e < DS; ++e) acc[e] = phi_prime(qv[e]) * (dql[e] + c * zh[d0 + e]);
 
   // ---- pass 2: dq of the softmax path ----
-  for (int tt = 0; tt < top_k * SPLIT; ++tt) {
+  for (int tt = 0; tt < (LIN ? 0 : top_k * SPLIT); ++tt) {
     const int64_t k0 = (int64_t)clamp_block(my_sel[tt / SPLIT], nkb) * BLK + (tt % SPLIT) * KT;
     if (k0 >= n_kv) continue;
     __syncthreads();
@@ -337,11 +339,13 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(4))) void bw
   if (live) {
     float* o = dq + (int64_t)h * dq_hs + r * D + d0;
 #pragma unroll
-    for (int e = 0; e < DS; ++e) o[e] = acc[e];
+    for (int e = 0; e < DS; ++e) o[e] = LIN ? o[e] + acc[e] : acc[e];
     if (d0 == 0) {
       float* st = rs + ((int64_t)h * nq_cap + r) * 4;
-      st[0] = lse2;
-      st[1] = Dr;
+      if (!LIN) {
+        st[0] = lse2;
+        st[1] = Dr;
+      }
       st[2] = den;
       st[3] = c;
     }
@@ -420,6 +424,214 @@ __global__ __launch_bounds__(BT) void bwd_kv(
     for (int e = 0; e < DS; ++e) {
       ok[e] = gk[e];
       ov[e] = gv[e];
+    }
+  }
+}
+
+// bf16 dq of the softmax path on MFMA (v_mfma_f32_16x16x32_bf16), one workgroup per
+// (head, 64-row query block), wave w owning queries 16w .. 16w + 15, whose Q and dO
+// rows stay in registers as B operands. Three passes over the selected key blocks:
+// A the row max of the scores S^T = K Q^T; B the sum l of exp2(S tau log2e - m) and
+// O^T += V^T P^T, giving lse and D = dO . O / l; C dP^T = V dO^T, dL^T = tau P^T (dP^T
+// - D) and dQ^T += K^T dL^T. The key order of the last two products comes from the
+// result layout of S^T (a lane holds keys 4g .. 4g + 3 of two 16-key tiles), so P^T
+// and dL^T are B operands in registers, split into bf16 hi and lo parts, and V^T and
+// K^T are read as A operands from transposed copies staged in LDS. Writes the softmax
+// part of dq and (lse, D) per row; the linear read's part is added by bwd_rows<LIN>.
+template <int D>
+__global__ __launch_bounds__(BT) void bwd_dq_mfma(
+    const bf16_t* __restrict__ q, int64_t n_q, int64_t q_hs, const bf16_t* __restrict__ kg,
+    const bf16_t* __restrict__ vg, int64_t n_kv, int64_t kv_hs, const int32_t* __restrict__ sel,
+    int top_k, int nqb, int nkb, float scale, const bf16_t* __restrict__ dout, int64_t do_hs,
+    float* __restrict__ dq, int64_t dq_hs, float* __restrict__ rs, int64_t nq_cap) {
+  constexpr int BLK = 64, NKS = D / 32, NE = D / 16;
+  constexpr int RS = D + 8, TS = BLK + 8;
+  typedef Mfma<bf16_t> M;
+  __shared__ __align__(16) bf16_t ks[BLK * RS];
+  __shared__ __align__(16) bf16_t vs[BLK * RS];
+  __shared__ __align__(16) bf16_t kt[D * TS];
+  __shared__ __align__(16) bf16_t vt[D * TS];
+  const int h = blockIdx.x / nqb, i = blockIdx.x % nqb;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const float sl2 = scale * kL2e;
+  const int64_t qrow = (int64_t)i * BLK + w * 16 + c;
+  const bool qvalid = qrow < n_q;
+  bf16x8 qop[NKS], dop[NKS];
+#pragma unroll
+  for (int s = 0; s < NKS; ++s) {
+    qop[s] = as_bf16x8(qvalid ? *reinterpret_cast<const uint4*>(q + (int64_t)h * q_hs + qrow * D +
+                                                                 32 * s + 8 * g)
+                              : zero4());
+    dop[s] = as_bf16x8(qvalid ? *reinterpret_cast<const uint4*>(dout + (int64_t)h * do_hs +
+                                                                 qrow * D + 32 * s + 8 * g)
+                              : zero4());
+  }
+  const bf16_t* kh = kg + (int64_t)h * kv_hs;
+  const bf16_t* vh = vg + (int64_t)h * kv_hs;
+  const int32_t* my_sel = sel + ((int64_t)h * nqb + i) * top_k;
+
+  // Stage key block jb: K row-major (always), V row-major, K^T, V^T as asked.
+  auto stage = [&](int jb, bool v_rows, bool k_t, bool v_t) {
+    __syncthreads();  // every wave is done with the previous block's copies
+    for (int v = threadIdx.x; v < BLK * (D / 8); v += BT) {
+      const int r = v % BLK, ch = v / BLK;
+      const int64_t row = (int64_t)jb * BLK + r;
+      const bool ok = row < n_kv;
+      const uint4 a = ok ? *reinterpret_cast<const uint4*>(kh + row * D + ch * 8) : zero4();
+      *reinterpret_cast<uint4*>(ks + r * RS + ch * 8) = a;
+      if (k_t) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) kt[(ch * 8 + e) * TS + r] = (bf16_t)half16(a, e);
+      }
+      if (v_rows || v_t) {
+        const uint4 b = ok ? *reinterpret_cast<const uint4*>(vh + row * D + ch * 8) : zero4();
+        if (v_rows) *reinterpret_cast<uint4*>(vs + r * RS + ch * 8) = b;
+        if (v_t) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) vt[(ch * 8 + e) * TS + r] = (bf16_t)half16(b, e);
+        }
+      }
+    }
+    __syncthreads();
+  };
+  // S^T tiles of the staged block (keys past the window: -inf), in log2 units.
+  auto scores = [&](int jb, f32x4 (&st)[4]) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < NKS; ++s)
+        a = M::mma(as_bf16x8(*reinterpret_cast<const uint4*>(ks + (16 * mt + c) * RS + 32 * s +
+                                                             8 * g)),
+                   qop[s], a);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t key = (int64_t)jb * BLK + 16 * mt + 4 * g + r;
+        st[mt][r] = key < n_kv ? a[r] * sl2 : -INFINITY;
+      }
+    }
+  };
+  // A operand of a transposed copy: row 16e + c, keys 32c2 + 4g + 0..3 and + 16.
+  auto tr_op = [&](const bf16_t* t, int e, int c2) {
+    const int o = (16 * e + c) * TS + 32 * c2 + 4 * g;
+    const uint2 a0 = *reinterpret_cast<const uint2*>(t + o);
+    const uint2 a1 = *reinterpret_cast<const uint2*>(t + o + 16);
+    return as_bf16x8(make_uint4(a0.x, a0.y, a1.x, a1.y));
+  };
+
+  // ---- pass A: row max ----
+  float m = -INFINITY;
+  for (int t = 0; t < top_k; ++t) {
+    const int jb = clamp_block(my_sel[t], nkb);
+    stage(jb, false, false, false);
+    f32x4 st[4];
+    scores(jb, st);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+      m = fmaxf(m, fmaxf(fmaxf(st[mt][0], st[mt][1]), fmaxf(st[mt][2], st[mt][3])));
+  }
+  m = max_over_groups(m);  // finite: every block holds a key of the window
+
+  // ---- pass B: l and O^T = V^T P^T at the fixed max ----
+  float lsum = 0.f;
+  f32x4 oT[NE];
+#pragma unroll
+  for (int e = 0; e < NE; ++e) oT[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < top_k; ++t) {
+    const int jb = clamp_block(my_sel[t], nkb);
+    stage(jb, false, false, true);
+    f32x4 st[4];
+    scores(jb, st);
+    float p[4][4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p[mt][r] = exp2f(st[mt][r] - m);
+        lsum += p[mt][r];
+      }
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) {
+      float pv[8];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        pv[r] = p[2 * c2][r];
+        pv[4 + r] = p[2 * c2 + 1][r];
+      }
+      bf16x8 ph, pl;
+      split_bf16x8(pv, ph, pl);
+#pragma unroll
+      for (int e = 0; e < NE; ++e) {
+        const bf16x8 a = tr_op(vt, e, c2);
+        oT[e] = M::mma(a, ph, oT[e]);
+        oT[e] = M::mma(a, pl, oT[e]);
+      }
+    }
+  }
+  const float l = sum_over_groups(lsum);
+  const float lse2 = m + log2f(l);
+  float dpart = 0.f;
+  if (qvalid) {
+    const bf16_t* dr = dout + (int64_t)h * do_hs + qrow * D;
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+      const uint2 u = *reinterpret_cast<const uint2*>(dr + 16 * e + 4 * g);
+      dpart += bf16_to_f32(u.x & 0xffffu) * oT[e][0] + bf16_to_f32(u.x >> 16) * oT[e][1] +
+               bf16_to_f32(u.y & 0xffffu) * oT[e][2] + bf16_to_f32(u.y >> 16) * oT[e][3];
+    }
+  }
+  const float Dr = sum_over_groups(dpart) / l;
+
+  // ---- pass C: dQ^T += K^T dL^T ----
+  f32x4 gT[NE];
+#pragma unroll
+  for (int e = 0; e < NE; ++e) gT[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < top_k; ++t) {
+    const int jb = clamp_block(my_sel[t], nkb);
+    stage(jb, true, true, false);
+    f32x4 st[4];
+    scores(jb, st);
+    float dl[4][4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < NKS; ++s)
+        a = M::mma(as_bf16x8(*reinterpret_cast<const uint4*>(vs + (16 * mt + c) * RS + 32 * s +
+                                                             8 * g)),
+                   dop[s], a);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dl[mt][r] = scale * exp2f(st[mt][r] - lse2) * (a[r] - Dr);
+    }
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) {
+      float lv[8];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        lv[r] = dl[2 * c2][r];
+        lv[4 + r] = dl[2 * c2 + 1][r];
+      }
+      bf16x8 lh, ll;
+      split_bf16x8(lv, lh, ll);
+#pragma unroll
+      for (int e = 0; e < NE; ++e) {
+        const bf16x8 a = tr_op(kt, e, c2);
+        gT[e] = M::mma(a, lh, gT[e]);
+        gT[e] = M::mma(a, ll, gT[e]);
+      }
+    }
+  }
+  if (qvalid) {
+    float* o = dq + (int64_t)h * dq_hs + qrow * D;
+#pragma unroll
+    for (int e = 0; e < NE; ++e)
+      *reinterpret_cast<float4*>(o + 16 * e + 4 * g) = make_float4(gT[e][0], gT[e][1], gT[e][2],
+                                                                    gT[e][3]);
+    if (g == 0) {
+      float* st = rs + ((int64_t)h * nq_cap + qrow) * 4;
+      st[0] = lse2;
+      st[1] = Dr;
     }
   }
 }
@@ -677,7 +889,16 @@ hipError_t run_attend_bwd(const BwdArgs& a, int stage, hipStream_t s) {
   if (stage == 0)
     bwd_inv_sel<<<(unsigned)((inv_n + 255) / 256), 256, 0, s>>>(
         a.sel, a.heads, nqb, nkb, a.top_k, a.inv_cnt, a.inv_list, a.nqb_cap);
-  if (stage == 1)
+  if (stage == 1 && std::is_same<T, bf16_t>::value && BLK == 64) {
+    bwd_dq_mfma<D><<<(unsigned)(a.heads * nqb), BT, 0, s>>>(
+        static_cast<const bf16_t*>(a.q), a.n_q, a.q_hs, static_cast<const bf16_t*>(a.k),
+        static_cast<const bf16_t*>(a.v), a.n_kv, a.kv_hs, a.sel, a.top_k, nqb, nkb, a.scale,
+        static_cast<const bf16_t*>(a.dout), a.do_hs, a.dq, a.dq_hs, a.rowstats, a.nq_cap);
+    bwd_rows<T, D, BLK, true><<<(unsigned)(a.heads * nqb * (BLK / kRows<BLK>)), BT, 0, s>>>(
+        static_cast<const T*>(a.q), a.n_q, a.q_hs, static_cast<const T*>(a.k),
+        static_cast<const T*>(a.v), a.n_kv, a.kv_hs, a.sel, a.top_k, nqb, nkb, a.S, a.z, a.eps,
+        a.scale, static_cast<const T*>(a.dout), a.do_hs, a.dq, a.dq_hs, a.rowstats, a.nq_cap);
+  } else if (stage == 1)
     bwd_rows<T, D, BLK><<<(unsigned)(a.heads * nqb * (BLK / kRows<BLK>)), BT, 0, s>>>(
         static_cast<const T*>(a.q), a.n_q, a.q_hs, static_cast<const T*>(a.k),
         static_cast<const T*>(a.v), a.n_kv, a.kv_hs, a.sel, a.top_k, nqb, nkb, a.S, a.z, a.eps,

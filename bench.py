@@ -283,12 +283,14 @@ class BwdSet(LayerSet):
             raise hla.HfError(r, "backward")
 
     def bwd_flops(self):
-        """FLOPs per kernel. pairs = executed (query row, key row) pairs. Flash-attention
-        convention for the whole pass: 10 d per pair (scores, dp, dq, dk, dv). Executed
-        by each kernel, which is what each must compute without stored statistics:
-        bwd_dq 10 d per pair (pass 1: scores, p v; pass 2: scores, dp, dq) + 6 n_q d^2
-        (S f, S^T g, and their reduction terms counted as the two products), bwd_dkv
-        8 d per pair, bwd_state 2 n_q d^2 + 2 n_q d, absorb_bwd 4 n_ev d^2."""
+        """Algorithmic FLOPs per kernel. pairs = executed (query row, key row) pairs.
+        Flash-attention convention for the whole pass: 10 d per pair (scores, dp, dq,
+        dk, dv). Per kernel, what each must compute without statistics stored by the
+        forward: bwd_dq 10 d per pair (scores and P V for lse and D; scores, dp, dq) +
+        4 n_q d^2 (the linear read's S f and S^T g), bwd_dkv 8 d per pair (scores, dp,
+        dk, dv), bwd_state 2 n_q d (d + 1), absorb_bwd 4 n_ev d^2. On bf16 states the dq
+        and dk/dv kernels run on MFMA and execute more: a row-max pass and hi/lo parts
+        of P and dL (16 d and 12 d per pair)."""
         import numpy as np
         sel = self.sel.cpu().numpy()
         H, n_q, d, B = self.H, self.n_q, self.d, 64
@@ -360,12 +362,13 @@ def backward_main(args, torch, hla, synth, wl, top_k):
     kern_us = {k: v[0] / v[1] * 1e3 for k, v in tot.items() if v[1]}
     log(f"[bench] backward {ms_step:.4f} ms/step; per-kernel us: {kern_us}")
     mean = {k: statistics.mean(f[k] for f in fl) for k in fl[0]}
-    peak = 157.3  # MI355X fp32 vector TFLOP/s (the kernels use no MFMA)
+    mfma = True  # the Wan-like layer is bf16: its dq and dk/dv kernels run on MFMA
     kernels = {k: dict(avg_us=round(kern_us[k], 2), algo_flop=int(mean[k]),
                        tflops=round(mean[k] / (kern_us[k] * 1e-6) / 1e12, 2))
                for k in ("bwd_dq", "bwd_dkv", "bwd_state", "absorb_bwd") if k in kern_us}
     kernels["bwd_index"] = dict(avg_us=round(kern_us.get("bwd_index", 0.0), 2))
     dom = max(("bwd_dq", "bwd_dkv"), key=lambda k: kern_us[k])
+    peak = PEAK_MFMA_TFLOPS["bf16"] if mfma else PEAK_MFMA_TFLOPS["f32"]
     achieved = mean[dom] / (kern_us[dom] * 1e-6) / 1e12
     value = mean["convention"] / (ms_step * 1e-3) / 1e12
     s0 = sets[0]
@@ -378,14 +381,15 @@ def backward_main(args, torch, hla, synth, wl, top_k):
                   "(flash-attention convention), 1 GPU",
         "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16 inputs, fp32 arithmetic",
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 inputs; bf16 MFMA with fp32 accumulation (hi/lo split weights)",
         "data": "synthetic (seeded N(0,1)/sqrt(d) bf16 Q/K/V, N(0,1) bf16 dout)",
         "config": {"workload": f"backward of {args.workload}: {s0.H} heads, d={s0.d}, "
                                f"{s0.n_q} query / {s0.n_kv} window / {s0.n_ev} evicted "
                                f"tokens, top-K {top_k}, forward selection held fixed",
                    "input_sets": n_sets, "executed_pairs": int(mean["pairs"])},
         "kernels": kernels,
-        "roofline": dict(bound="alu", achieved=round(achieved, 2), peak=peak, unit="TFLOP/s",
+        "roofline": dict(bound="mfma", achieved=round(achieved, 2), peak=peak, unit="TFLOP/s",
                          frac=round(achieved / peak, 4), traffic=None, kernel=dom,
                          flop_per_launch=int(mean[dom]), avg_launch_us=round(kern_us[dom], 2)),
         "cpu_baseline": cpu,

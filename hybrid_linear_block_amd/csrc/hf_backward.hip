@@ -169,6 +169,9 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(4))) void bw
   static_assert(DS % 4 == 0, "float4 slices");
   __shared__ __align__(16) float tk[KT * D];
   __shared__ __align__(16) float tv[KT * D];
+  // S of the head for the linear read, staged in the linear-only form (whose
+  // workgroups do little else); the full form reads it from the cache.
+  __shared__ __align__(16) float tS[LIN ? D * D : 4];
   const int h = blockIdx.x / (nqb * SPLIT), i = (blockIdx.x / SPLIT) % nqb;
   const int part = blockIdx.x % SPLIT;
   const int rl = threadIdx.x / TPR, d0 = (threadIdx.x % TPR) * DS;
@@ -177,7 +180,6 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(4))) void bw
   const int64_t rr = live ? r : n_q - 1;
   const T* kh = kg + (int64_t)h * kv_hs;
   const T* vh = vg + (int64_t)h * kv_hs;
-  const float* Sh = S + (int64_t)h * D * D;
   const float* zh = z + (int64_t)h * D;
   const int32_t* my_sel = sel + ((int64_t)h * nqb + i) * top_k;
   float qv[DS], dov[DS], acc[DS];
@@ -265,6 +267,11 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(4))) void bw
   const float den = row_sum<TPR>(fz) + eps;
   const float inv_den = 1.f / den;
   __syncthreads();  // every wave is done with the last tiles
+  if (LIN)
+    for (int e = threadIdx.x; e < D * D / 4; e += BT)
+      reinterpret_cast<float4*>(tS)[e] =
+          reinterpret_cast<const float4*>(S + (int64_t)h * D * D)[e];
+  const float* Sh = LIN ? tS : S + (int64_t)h * D * D;
   float* frow = tk + rl * D;
   float* grow = tv + rl * D;
 #pragma unroll

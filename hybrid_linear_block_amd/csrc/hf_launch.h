@@ -106,9 +106,10 @@ struct BwdArgs {
   int32_t* inv_list;  // [heads][nkb][nqb_cap]
   int nqb_cap;
 };
-// dq, dk, dv, dS and dz of the hybrid attention (n_q >= 1) in four launches, run in
-// order on one stream: stage 0 the inverse selection index, 1 dq and the per-row
-// statistics, 2 dk and dv, 3 dS and dz.
+// dq, dk, dv, dS and dz of the hybrid attention (n_q >= 1), stage by stage in order on
+// one stream: stage 0 the inverse selection index, 1 dq and the per-row statistics (two
+// launches for bf16 states: the MFMA softmax part, then the linear read's part), 2 dk
+// and dv, 3 dS and dz.
 hipError_t launch_attend_backward(int dtype, int d, int block, const BwdArgs& a, int stage,
                                   hipStream_t s);
 // dk_ev and dv_ev of an absorb from dS and dz (n_ev >= 0).

@@ -275,8 +275,8 @@ size_t hf_backward_workspace_bytes(const hf_config* cfg);
  * whole: dq [H][n_q][d] (head stride dq_head_stride), dk_win and dv_win [H][n_kv][d]
  * (head stride dkv_head_stride; rows of unselected key blocks get 0), dS [H][d][d]
  * and dz [H][d] (dense). bwd_ws: caller-owned device memory of at least
- * hf_backward_workspace_bytes bytes, 16-byte aligned. n_q must be >= 1. Four
- * launches on `stream`. */
+ * hf_backward_workspace_bytes bytes, 16-byte aligned. n_q must be >= 1. Five
+ * launches on `stream` for bf16 states (dq and dk/dv on MFMA), four for fp32. */
 hf_status hf_attend_backward(hf_state* st, const void* q, int64_t n_q, int64_t q_head_stride,
                              const void* k_win, const void* v_win, int64_t n_kv,
                              int64_t kv_head_stride, const int32_t* sel, int32_t top_k,

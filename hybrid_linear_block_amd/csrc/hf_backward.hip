@@ -772,14 +772,17 @@ __global__ __launch_bounds__(BT) void bwd_kv_mfma(
   }
 }
 
-// Workgroup (h, jt): jt < D / 8 forms dS rows 8 jt .. 8 jt + 7, jt == D / 8 forms dz.
+// Workgroup (h, jt): jt < D / NJ forms dS rows NJ jt .. NJ jt + NJ - 1, jt == D / NJ forms
+// dz. Four rows per workgroup: 33 workgroups per head at d = 128, so that the grid
+// covers the compute units.
+constexpr int kStateRows = 4;
 template <typename T, int D>
 __global__ __launch_bounds__(BT) void bwd_state(const T* __restrict__ q, int64_t n_q,
                                                 int64_t q_hs, const T* __restrict__ dout,
                                                 int64_t do_hs, const float* __restrict__ rs,
                                                 int64_t nq_cap, float* __restrict__ dS,
                                                 float* __restrict__ dz) {
-  constexpr int RC = 32, NJ = 8, JPT = NJ * D / BT;  // rows per chunk, dS rows, outputs/thread
+  constexpr int RC = 32, NJ = kStateRows, JPT = NJ * D / BT;  // rows/chunk, dS rows, outs/thread
   __shared__ __align__(16) float tf[RC * D];
   __shared__ float tg[RC * NJ];
   constexpr int NT = D / NJ + 1;
@@ -922,7 +925,7 @@ hipError_t run_attend_bwd(const BwdArgs& a, int stage, hipStream_t s) {
         static_cast<const T*>(a.v), a.n_kv, a.kv_hs, nkb, a.scale, static_cast<const T*>(a.dout),
         a.do_hs, a.rowstats, a.nq_cap, a.inv_cnt, a.inv_list, a.nqb_cap, a.dk, a.dv, a.dkv_hs);
   if (stage == 3)
-    bwd_state<T, D><<<(unsigned)(a.heads * (D / 8 + 1)), BT, 0, s>>>(
+    bwd_state<T, D><<<(unsigned)(a.heads * (D / kStateRows + 1)), BT, 0, s>>>(
         static_cast<const T*>(a.q), a.n_q, a.q_hs, static_cast<const T*>(a.dout), a.do_hs,
         a.rowstats, a.nq_cap, a.dS, a.dz);
   return hipGetLastError();

@@ -164,7 +164,9 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(4))) void bw
     int top_k, int nqb, int nkb, const float* __restrict__ S, const float* __restrict__ z,
     float eps, float scale, const T* __restrict__ dout, int64_t do_hs, float* __restrict__ dq,
     int64_t dq_hs, float* __restrict__ rs, int64_t nq_cap) {
-  constexpr int RPW = kRows<BLK>, KT = RPW, SPLIT = BLK / RPW;
+  // The linear-only form takes a whole query block per workgroup (one staging of S
+  // per 64 rows); the full form splits it into 32-row halves.
+  constexpr int RPW = LIN ? BLK : kRows<BLK>, KT = RPW, SPLIT = BLK / RPW;
   constexpr int TPR = BT / RPW, DS = D / TPR;
   static_assert(DS % 4 == 0, "float4 slices");
   __shared__ __align__(16) float tk[KT * D];
@@ -904,7 +906,7 @@ hipError_t run_attend_bwd(const BwdArgs& a, int stage, hipStream_t s) {
         static_cast<const bf16_t*>(a.q), a.n_q, a.q_hs, static_cast<const bf16_t*>(a.k),
         static_cast<const bf16_t*>(a.v), a.n_kv, a.kv_hs, a.sel, a.top_k, nqb, nkb, a.scale,
         static_cast<const bf16_t*>(a.dout), a.do_hs, a.dq, a.dq_hs, a.rowstats, a.nq_cap);
-    bwd_rows<T, D, BLK, true><<<(unsigned)(a.heads * nqb * (BLK / kRows<BLK>)), BT, 0, s>>>(
+    bwd_rows<T, D, BLK, true><<<(unsigned)(a.heads * nqb), BT, 0, s>>>(
         static_cast<const T*>(a.q), a.n_q, a.q_hs, static_cast<const T*>(a.k),
         static_cast<const T*>(a.v), a.n_kv, a.kv_hs, a.sel, a.top_k, nqb, nkb, a.S, a.z, a.eps,
         a.scale, static_cast<const T*>(a.dout), a.do_hs, a.dq, a.dq_hs, a.rowstats, a.nq_cap);

@@ -128,24 +128,37 @@ __device__ __forceinline__ void load_tile(const T* __restrict__ base, int64_t ro
   }
 }
 
-__global__ void bwd_inv_sel(const int32_t* __restrict__ sel, int heads, int nqb, int nkb,
-                            int top_k, int32_t* __restrict__ cnt, int32_t* __restrict__ list,
-                            int nqb_cap) {
-  const int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (x >= (int64_t)heads * nkb) return;
+// One workgroup per (head, key block): each thread looks for the key block in one
+// query block's ascending selection row (binary search); thread 0 then appends the
+// hits in query-block order.
+__global__ __launch_bounds__(256) void bwd_inv_sel(const int32_t* __restrict__ sel, int nqb,
+                                                   int nkb, int top_k, int32_t* __restrict__ cnt,
+                                                   int32_t* __restrict__ list, int nqb_cap) {
+  __shared__ int hit[256];
+  const int64_t x = blockIdx.x;
   const int h = (int)(x / nkb), j = (int)(x % nkb);
-  int n = 0;
-  for (int i = 0; i < nqb; ++i) {
-    const int32_t* row = sel + ((int64_t)h * nqb + i) * top_k;  // ascending
-    int lo = 0, hi = top_k;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (row[mid] < j) lo = mid + 1;
-      else hi = mid;
+  int n = 0;  // thread 0's running count
+  for (int base = 0; base < nqb; base += 256) {
+    const int i = base + (int)threadIdx.x;
+    bool f = false;
+    if (i < nqb) {
+      const int32_t* row = sel + ((int64_t)h * nqb + i) * top_k;
+      int lo = 0, hi = top_k;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (row[mid] < j) lo = mid + 1;
+        else hi = mid;
+      }
+      f = lo < top_k && row[lo] == j;
     }
-    if (lo < top_k && row[lo] == j) list[x * nqb_cap + n++] = i;
+    hit[threadIdx.x] = f;
+    __syncthreads();
+    if (threadIdx.x == 0)
+      for (int t = 0; t < 256 && base + t < nqb; ++t)
+        if (hit[t]) list[x * nqb_cap + n++] = base + t;
+    __syncthreads();
   }
-  cnt[x] = n;
+  if (threadIdx.x == 0) cnt[x] = n;
 }
 
 // Query rows per workgroup of bwd_rows and key rows per workgroup of bwd_kv, and
@@ -155,10 +168,11 @@ __global__ void bwd_inv_sel(const int32_t* __restrict__ sel, int heads, int nqb,
 template <int BLK>
 constexpr int kRows = BLK > 32 ? 32 : BLK;
 
-// LIN: only the linear read's terms, added to dq (which holds the softmax path's part,
-// written by bwd_dq_mfma together with lse and D); stores den and c only.
-template <typename T, int D, int BLK, bool LIN = false>
-__global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(4))) void bwd_rows(
+// Body of the row kernels. LIN: only the linear read's terms, added to dq (which holds
+// the softmax path's part, written by bwd_dq_mfma together with lse and D); stores den
+// and c only.
+template <typename T, int D, int BLK, bool LIN>
+__device__ __forceinline__ void rows_body(
     const T* __restrict__ q, int64_t n_q, int64_t q_hs, const T* __restrict__ kg,
     const T* __restrict__ vg, int64_t n_kv, int64_t kv_hs, const int32_t* __restrict__ sel,
     int top_k, int nqb, int nkb, const float* __restrict__ S, const float* __restrict__ z,
@@ -195,7 +209,8 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(4))) void bw
 
   // ---- pass 1: softmax statistics and o_swa (online, base 2) ----
   float m2 = -INFINITY, l = 0.f;
-  for (int tt = 0; tt < (LIN ? 0 : top_k * SPLIT); ++tt) {
+  if constexpr (!LIN)
+  for (int tt = 0; tt < top_k * SPLIT; ++tt) {
     const int64_t k0 = (int64_t)clamp_block(my_sel[tt / SPLIT], nkb) * BLK + (tt % SPLIT) * KT;
     if (k0 >= n_kv) continue;  // the ragged last block has no second half
     __syncthreads();
@@ -319,7 +334,8 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(4))) void bw
   for (int e = 0; e < DS; ++e) acc[e] = phi_prime(qv[e]) * (dql[e] + c * zh[d0 + e]);
 
   // ---- pass 2: dq of the softmax path ----
-  for (int tt = 0; tt < (LIN ? 0 : top_k * SPLIT); ++tt) {
+  if constexpr (!LIN)
+  for (int tt = 0; tt < top_k * SPLIT; ++tt) {
     const int64_t k0 = (int64_t)clamp_block(my_sel[tt / SPLIT], nkb) * BLK + (tt % SPLIT) * KT;
     if (k0 >= n_kv) continue;
     __syncthreads();
@@ -327,7 +343,6 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(4))) void bw
     load_tile<T, D, KT>(vh, k0, n_kv, tv);
     __syncthreads();
     const int nvalid = (int)min((int64_t)KT, n_kv - k0);
-#pragma unroll 2
     for (int u = 0; u < nvalid; ++u) {
       const float* kr = tk + u * D + d0;
       const float* vr = tv + u * D + d0;
@@ -360,6 +375,31 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(4))) void bw
     }
   }
 }
+
+#define HF_ROWS_ARGS                                                                       \
+  const T *__restrict__ q, int64_t n_q, int64_t q_hs, const T *__restrict__ kg,            \
+      const T *__restrict__ vg, int64_t n_kv, int64_t kv_hs,                                \
+      const int32_t *__restrict__ sel, int top_k, int nqb, int nkb,                         \
+      const float *__restrict__ S, const float *__restrict__ z, float eps, float scale,     \
+      const T *__restrict__ dout, int64_t do_hs, float *__restrict__ dq, int64_t dq_hs,     \
+      float *__restrict__ rs, int64_t nq_cap
+#define HF_ROWS_PASS \
+  q, n_q, q_hs, kg, vg, n_kv, kv_hs, sel, top_k, nqb, nkb, S, z, eps, scale, dout, do_hs, dq, dq_hs, rs, nq_cap
+
+// Both passes and the linear read (fp32 states), at four waves per SIMD.
+template <typename T, int D, int BLK>
+__global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(4))) void bwd_rows(
+    HF_ROWS_ARGS) {
+  rows_body<T, D, BLK, false>(HF_ROWS_PASS);
+}
+
+// The linear read's terms only (after bwd_dq_mfma); its LDS copy of S sets the occupancy.
+template <typename T, int D, int BLK>
+__global__ __launch_bounds__(BT) void bwd_rows_lin(HF_ROWS_ARGS) {
+  rows_body<T, D, BLK, true>(HF_ROWS_PASS);
+}
+#undef HF_ROWS_ARGS
+#undef HF_ROWS_PASS
 
 template <typename T, int D, int BLK>
 __global__ __launch_bounds__(BT) void bwd_kv(
@@ -405,7 +445,6 @@ __global__ __launch_bounds__(BT) void bwd_kv(
     }
     __syncthreads();
     const int nvalid = (int)min((int64_t)QT, n_q - q0);
-#pragma unroll 2
     for (int u = 0; u < nvalid; ++u) {
       const float* qr = tq + u * D + d0;
       const float* dr = tdo + u * D + d0;
@@ -899,14 +938,14 @@ hipError_t run_attend_bwd(const BwdArgs& a, int stage, hipStream_t s) {
   const int nqb = (int)((a.n_q + BLK - 1) / BLK), nkb = (int)((a.n_kv + BLK - 1) / BLK);
   const int64_t inv_n = (int64_t)a.heads * nkb;
   if (stage == 0)
-    bwd_inv_sel<<<(unsigned)((inv_n + 255) / 256), 256, 0, s>>>(
-        a.sel, a.heads, nqb, nkb, a.top_k, a.inv_cnt, a.inv_list, a.nqb_cap);
+    bwd_inv_sel<<<(unsigned)inv_n, 256, 0, s>>>(a.sel, nqb, nkb, a.top_k, a.inv_cnt,
+                                                 a.inv_list, a.nqb_cap);
   if (stage == 1 && std::is_same<T, bf16_t>::value && BLK == 64) {
     bwd_dq_mfma<D><<<(unsigned)(a.heads * nqb), BT, 0, s>>>(
         static_cast<const bf16_t*>(a.q), a.n_q, a.q_hs, static_cast<const bf16_t*>(a.k),
         static_cast<const bf16_t*>(a.v), a.n_kv, a.kv_hs, a.sel, a.top_k, nqb, nkb, a.scale,
         static_cast<const bf16_t*>(a.dout), a.do_hs, a.dq, a.dq_hs, a.rowstats, a.nq_cap);
-    bwd_rows<T, D, BLK, true><<<(unsigned)(a.heads * nqb), BT, 0, s>>>(
+    bwd_rows_lin<T, D, BLK><<<(unsigned)(a.heads * nqb), BT, 0, s>>>(
         static_cast<const T*>(a.q), a.n_q, a.q_hs, static_cast<const T*>(a.k),
         static_cast<const T*>(a.v), a.n_kv, a.kv_hs, a.sel, a.top_k, nqb, nkb, a.S, a.z, a.eps,
         a.scale, static_cast<const T*>(a.dout), a.do_hs, a.dq, a.dq_hs, a.rowstats, a.nq_cap);

@@ -104,8 +104,8 @@ def swa_source_sha():
 class LayerSet:
     """One input set of the Wan-like layer resident on the GPU, with its own state."""
 
-    def __init__(self, hla, torch, synth, seed, top_k):
-        inp = synth.wan_layer_inputs(seed)
+    def __init__(self, hla, torch, synth, seed, top_k, inp=None):
+        inp = synth.wan_layer_inputs(seed) if inp is None else inp
         dev = torch.device("cuda:0")
         to = lambda b: torch.from_numpy(b.view("int16")).view(torch.bfloat16).to(dev)  # noqa
         self.q = to(inp["q"])
@@ -469,7 +469,11 @@ def main():
         sets = [StreamSet(hla, torch, args.seed + i, top_k, args.stream_positions,
                           args.cached_pooling) for i in range(n_sets)]
     else:
-        sets = [LayerSet(hla, torch, synth, args.seed + i, top_k) for i in range(n_sets)]
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(8) as ex:  # seeded host generation, several layers at once
+            inps = list(ex.map(synth.wan_layer_inputs, [args.seed + i for i in range(n_sets)]))
+        sets = [LayerSet(hla, torch, synth, args.seed + i, top_k, inps[i]) for i in range(n_sets)]
+        del inps
     log(f"[bench] {n_sets} input sets resident ({time.time() - t0:.1f}s)")
 
     # Selection of every set (for the executed-FLOP count); not timed.

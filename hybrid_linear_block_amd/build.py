@@ -18,12 +18,13 @@ SOURCES = ["hf_abi.hip", "hf_absorb.hip", "hf_select.hip", "hf_sparse_swa.hip", 
            "hf_backward.hip"]
 ARCH = os.environ.get("HF_OFFLOAD_ARCH", "gfx950")
 
+OBJ_DIR = os.path.join(PKG, "_build")
+
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}",
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     # Packed fp32 VALU ops stay off: the compiler must not form v_pk_*_f32.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall",
@@ -41,11 +42,7 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found; the HIP toolchain (ROCm) is required to build libhf")
 
 
-def build(verbose: bool = False, extra_flags=None) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *(extra_flags or []), "-I", os.path.join(ROOT, "include"),
-           "-o", tmp, *srcs]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -55,6 +52,21 @@ def build(verbose: bool = False, extra_flags=None) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{msgs}")
     if verbose and msgs.strip():
         print(msgs, flush=True)
+
+
+def build(verbose: bool = False, extra_flags=None) -> str:
+    """Compile every source to an object (in parallel), then link libhf.so."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    flags = [*HIPCC_FLAGS, *(extra_flags or []), "-I", os.path.join(ROOT, "include")]
+    objs = [os.path.join(OBJ_DIR, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+    cmds = [[hipcc(), *flags, "-c", "-o", o, os.path.join(CSRC, s)] for s, o in zip(SOURCES, objs)]
+    jobs = max(1, min(len(cmds), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+    with ThreadPoolExecutor(jobs) as ex:
+        list(ex.map(lambda c: _run(c, verbose), cmds))
+    tmp = LIB + ".tmp"
+    _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -64,7 +64,9 @@ hf_status check_config(const hf_config* c) {
   if (!c) return HF_ERR_INVALID_ARG;
   if (c->num_heads < 1 || c->head_dim < 1 || c->block_size < 1) return HF_ERR_INVALID_ARG;
   if (c->dtype != HF_BF16 && c->dtype != HF_F32) return HF_ERR_UNSUPPORTED;
-  if (!(c->eps >= 0.f) || !std::isfinite(c->eps)) return HF_ERR_INVALID_ARG;
+  // eps > 0: an empty state (z = 0) must read as an exactly zero linear term, and
+  // 0 / (0 + eps) is 0 only for eps > 0.
+  if (!(c->eps > 0.f) || !std::isfinite(c->eps)) return HF_ERR_INVALID_ARG;
   if (!(c->softmax_scale >= 0.f) || !std::isfinite(c->softmax_scale)) return HF_ERR_INVALID_ARG;
   if (c->max_n_q < 1 || c->max_n_kv < 1 || c->max_n_ev < 0 || c->max_top_k < 1)
     return HF_ERR_INVALID_ARG;

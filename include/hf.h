@@ -92,7 +92,9 @@ typedef struct {
   int32_t head_dim;    /* d: 64 or 128 */
   int32_t block_size;  /* B: rows per query/key block (bf16: 64; fp32: 16 or 64) */
   int32_t dtype;       /* hf_dtype of Q, K, V and out; S and z are always fp32 */
-  float eps;           /* added once to the linear normaliser; >= 0 (1e-6 typical) */
+  float eps;           /* added once to the linear normaliser; > 0 and finite (1e-6
+                          typical): with eps > 0 an empty state (z = 0) reads as an
+                          exactly zero linear term */
   float softmax_scale; /* tau; 0 selects 1/sqrt(head_dim) */
   int64_t max_n_q;     /* capacity limits used to size the workspace */
   int64_t max_n_kv;    /* ceil(max_n_kv / B) must be <= 2048 */
@@ -267,9 +269,14 @@ size_t hf_backward_workspace_bytes(const hf_config* cfg);
 
 /* Gradients of one hf_attend_chunk call. q, k_win, v_win, n_q, n_kv, strides and
  * top_k are those of the forward call; sel is its selection (int32
- * [H][ceil(n_q/B)][top_k], each row ascending, as hf_attend_chunk's sel_out
- * returns; indices are clamped into the window, so no selection reads out of
- * bounds). S and z are the state's current ones, i.e. the state must be as at the
+ * [H][ceil(n_q/B)][top_k], as hf_attend_chunk's sel_out returns). Contract: every
+ * row of sel is strictly ascending with indices in [0, ceil(n_kv/B)); any such
+ * selection is differentiated exactly (the top-K property is not needed). For a row
+ * that breaks the contract (unsorted, repeated or out-of-range indices) the
+ * gradients are undefined, but the call stays safe: indices are clamped into the
+ * window and each key block lists a query block at most once, so nothing is read
+ * or written out of bounds. The row contents live in device memory and are not
+ * checked on the host. S and z are the state's current ones, i.e. the state must be as at the
  * forward call. dout ([H][n_q][d], element type of the state, head stride
  * dout_head_stride) is the incoming gradient. Outputs, all fp32 and written
  * whole: dq [H][n_q][d] (head stride dq_head_stride), dk_win and dv_win [H][n_kv][d]

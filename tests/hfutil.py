@@ -6,8 +6,9 @@ of max|oracle| (a bar that stays meaningful where outputs are small); for fp32
 inputs within max-abs 1e-4. Selected block indices must equal the oracle's
 except in rows whose oracle fp32 score gap between the K-th and (K+1)-th block is
 below 1e-3 * max|score| (a near tie), where the device set must still be a valid
-top-K within that gap. Rows whose device set differs (near ties only) are left
-out of the element-wise output comparison and counted.
+top-K within that gap. In such a row the output is compared with the oracle's
+output for the device's (valid) set, so every row of every sampled block is
+compared element by element; the number of such rows is reported.
 """
 
 from __future__ import annotations
@@ -69,13 +70,12 @@ def compare_out(out_dev: np.ndarray, out_ref: np.ndarray, dtype: str, rows_mask=
     return stats
 
 
-def row_mask(shape, differ: np.ndarray, block: int) -> np.ndarray:
-    """Mask [H][N][d] that is False on the rows of query blocks flagged in `differ`."""
-    H, n, d = shape
-    m = np.ones(shape, bool)
-    for h, i in zip(*np.nonzero(differ)):
-        m[h, i * block:(i + 1) * block] = False
-    return m
+def reference_selection(sel_dev: np.ndarray, sel_ref: np.ndarray, differ: np.ndarray):
+    """The selection the oracle's outputs are computed for: the oracle's own, except in
+    the near-tie rows where compare_sel accepted a different valid top-K set of the
+    device; there the oracle attends over the device's set, so those rows' outputs
+    are compared too rather than skipped."""
+    return np.where(differ[..., None], sel_dev, sel_ref).astype(np.int32)
 
 
 def state_close(S_dev, z_dev, S_ref, z_ref, dtype: str):

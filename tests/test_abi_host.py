@@ -93,7 +93,7 @@ def test_workspace_bytes():
     assert hla.hf_workspace_bytes(cfg(dtype=B.HF_F32, block_size=16, head_dim=64)) > 0
     for bad in (dict(head_dim=96), dict(block_size=32), dict(dtype=7), dict(num_heads=0),
                 dict(max_top_k=0), dict(max_n_q=0), dict(max_top_k=300), dict(eps=-1.0),
-                dict(eps=float("nan")), dict(max_n_kv=64 * 2049),
+                dict(eps=0.0), dict(eps=float("inf")), dict(eps=float("nan")), dict(max_n_kv=64 * 2049),
                 dict(dtype=B.HF_BF16, block_size=16)):
         assert hla.hf_workspace_bytes(cfg(**bad)) == 0, bad
 

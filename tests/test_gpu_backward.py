@@ -49,7 +49,7 @@ def _close(name, dev, ref, scale=None):
     assert err <= TOL * scale, name
 
 
-def _run(H, d, B, dt, n_q, n_kv, top_k, n_ev, seed, twice=False):
+def _run(H, d, B, dt, n_q, n_kv, top_k, n_ev, seed, twice=False, own_sel=False):
     print(f"case H={H} d={d} B={B} {dt} n_q={n_q} n_kv={n_kv} K={top_k} n_ev={n_ev}", flush=True)
     std = 1.0 / np.sqrt(d) if dt == "bf16" else 0.5
     q, q64 = _draw(seed, 1, H, n_q, d, std, dt)
@@ -64,6 +64,11 @@ def _run(H, d, B, dt, n_q, n_kv, top_k, n_ev, seed, twice=False):
     st.absorb_evicted(kev, vev)
     sel = torch.empty((H, -(-n_q // B), top_k), dtype=torch.int32, device="cuda")
     st.attend_chunk(q, k, v, top_k, sel_out=sel)
+    if own_sel:  # any strictly ascending in-range selection, not only a top-K one
+        rng = np.random.default_rng(seed)
+        nkb = -(-n_kv // B)
+        rows = [np.sort(rng.choice(nkb, top_k, replace=False)) for _ in range(sel.numel() // top_k)]
+        sel = torch.from_numpy(np.stack(rows).astype(np.int32).reshape(sel.shape)).cuda()
     dq, dk, dv, dS, dz = st.attend_backward(q, k, v, sel, dout)
     dkev, dvev = st.absorb_backward(kev, vev, dS, dz)
     torch.cuda.synchronize()
@@ -96,6 +101,14 @@ def _run(H, d, B, dt, n_q, n_kv, top_k, n_ev, seed, twice=False):
 ])
 def test_backward_matches_oracle(H, d, B, dt, n_q, n_kv, top_k, n_ev):
     _run(H, d, B, dt, n_q, n_kv, top_k, n_ev, seed=300 + n_q, twice=(n_q == 200))
+
+
+@pytest.mark.parametrize("dt,d,B", [("bf16", 128, 64), ("f32", 64, 16)])
+def test_backward_any_ascending_selection(dt, d, B):
+    """The backward differentiates whatever strictly ascending, in-range selection it is
+    given: a random one here, with ragged tails, some key blocks picked by many query
+    blocks and some by none."""
+    _run(2, d, B, dt, 5 * B - 3, 9 * B - 5, 3, 40, seed=77, own_sel=True)
 
 
 def test_backward_wan_layer():

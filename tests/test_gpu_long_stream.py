@@ -20,7 +20,8 @@ pytestmark = pytest.mark.gpu
 
 if torch.cuda.is_available():
     import hybrid_linear_block_amd as hla  # the HIP library must load: no fallback path
-from hfutil import compare_out, compare_sel, dev_bf16, host_f64, row_mask, state_close  # noqa: E402
+from hfutil import (compare_out, compare_sel, dev_bf16, host_f64,  # noqa: E402
+                    reference_selection, state_close)
 
 
 @pytest.mark.timeout(900)
@@ -59,11 +60,13 @@ def test_long_stream_60_steps():
         k64 = oracle.as_f64(kbits[:, w0 * T:w1 * T], "bf16")
         v64 = oracle.as_f64(vbits[:, w0 * T:w1 * T], "bf16")
         sel_ref, s32 = oracle.select(q64, k64, B, K)
-        differ = compare_sel(sel.cpu().numpy(), sel_ref, s32, K)
+        sel_dev = sel.cpu().numpy()
+        differ = compare_sel(sel_dev, sel_ref, s32, K)
         blocks = sorted({(int(rng.integers(H)), int(rng.integers(74))) for _ in range(3)} |
-                        {(t % H, 73)})
-        ref = oracle.attend_with_sel(q64, k64, v64, sel_ref, S, z, B, blocks=blocks)
-        stats = compare_out(host_f64(out), ref, "bf16", row_mask(ref.shape, differ, B))
+                        {(t % H, 73)} | {(int(h), int(i)) for h, i in zip(*np.nonzero(differ))})
+        ref = oracle.attend_with_sel(q64, k64, v64, reference_selection(sel_dev, sel_ref, differ),
+                                     S, z, B, blocks=blocks)
+        stats = compare_out(host_f64(out), ref, "bf16")
         if t % 10 == 0 or t == n_steps - 1:
             print(f"step {t}: window {w0}-{w1} K={K} S fro={fro:.2e} z rel={zrel:.2e} "
                   f"out {stats} ties={int(differ.sum())} ({time.time() - t0:.0f}s)", flush=True)

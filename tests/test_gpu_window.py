@@ -14,7 +14,8 @@ import torch
 
 import oracle
 import synth
-from hfutil import compare_out, compare_sel, dev_bf16, dev_f32, host_f64, row_mask, state_close
+from hfutil import (compare_out, compare_sel, dev_bf16, dev_f32, host_f64, reference_selection,
+                    state_close)
 from synth.inputs import frame_block
 
 pytestmark = pytest.mark.gpu
@@ -95,10 +96,11 @@ def test_window_stream_matches_caller_windows(dt, d, B, T, ring_mult):
     state_close(host_f64(win.S), host_f64(win.z), S, z, dt)
     qa = q64[:, a:b]
     sel_ref, s32 = oracle.select(qa, k64[:, w0 * T:w1 * T], B, k_t)
-    differ = compare_sel(sels[2].cpu().numpy(), sel_ref, s32, k_t)
-    ref_out = oracle.attend_with_sel(qa, k64[:, w0 * T:w1 * T], v64[:, w0 * T:w1 * T], sel_ref,
-                                     S, z, B)
-    compare_out(host_f64(o2), ref_out, dt, row_mask(ref_out.shape, differ, B))
+    sel_dev = sels[2].cpu().numpy()
+    differ = compare_sel(sel_dev, sel_ref, s32, k_t)
+    ref_out = oracle.attend_with_sel(qa, k64[:, w0 * T:w1 * T], v64[:, w0 * T:w1 * T],
+                                     reference_selection(sel_dev, sel_ref, differ), S, z, B)
+    compare_out(host_f64(o2), ref_out, dt)
 
 
 def test_window_errors():

@@ -398,3 +398,37 @@ def test_every_frame_in_exactly_one_path(name, steps):
     else:
         assert oracle.stream_step_frames(3, c, W) == ((0, 3), (3, 12))
         assert max(absorbed) == 170
+
+
+# ------------------------------------------------------------- input decoding
+
+
+def _bf16_by_definition(bits: int) -> float:
+    """bfloat16 is the upper half of an IEEE-754 binary32: 1 sign bit, 8 exponent bits
+    (bias 127) and 7 fraction bits, decoded here from that definition."""
+    sign = -1.0 if bits >> 15 else 1.0
+    e, m = (bits >> 7) & 0xFF, bits & 0x7F
+    if e == 0:  # zero and subnormals: 2^-126 * m / 128
+        return sign * math.ldexp(m, -126 - 7)
+    return sign * math.ldexp(128 + m, e - 127 - 7)
+
+
+def test_as_f64_decodes_bf16_by_definition():
+    """Every finite bf16 pattern decodes to the value its bit fields define, and to
+    what PyTorch's own bf16 -> float64 cast gives (inf/NaN patterns, e = 255, never
+    occur as inputs)."""
+    bits = np.array([b for b in range(1 << 16) if (b >> 7) & 0xFF != 0xFF], np.uint16)
+    got = oracle.as_f64(bits, "bf16")
+    want = np.array([_bf16_by_definition(int(b)) for b in bits])
+    assert np.array_equal(got, want)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).double().numpy()
+    assert np.array_equal(got, ref)
+    # a few values by hand: 1, -2, 1 + 2^-7, the smallest subnormal, the largest finite
+    for b, v in ((0x3F80, 1.0), (0xC000, -2.0), (0x3F81, 1.0 + 2.0 ** -7), (0x0001, 2.0 ** -133),
+                 (0x7F7F, (2.0 - 2.0 ** -7) * 2.0 ** 127)):
+        assert oracle.as_f64(np.array([b], np.uint16), "bf16")[0] == v
+    assert math.copysign(1.0, oracle.as_f64(np.array([0x8000], np.uint16), "bf16")[0]) == -1.0
+    # shape is kept, and fp32 inputs widen exactly
+    x = np.arange(24, dtype=np.float32).reshape(2, 3, 4) / 3
+    assert np.array_equal(oracle.as_f64(x, "f32"), x.astype(np.float64))
+    assert oracle.as_f64(bits[:24].reshape(2, 3, 4), "bf16").shape == (2, 3, 4)

@@ -76,6 +76,8 @@ def _load():
                                        P, c_int64, P, c_int64, P, P, c_int64, P, P, P, c_size_t,
                                        P]),
         "hf_absorb_backward": (c_int, [P, P, P, c_int64, c_int64, P, P, P, P, c_int64, P]),
+        "hf_attend_chunk_noalloc": (c_int, [POINTER(hf_config), P, P, P, c_int64, c_int64, P, P,
+                                            c_int64, c_int64, c_int32, P, c_int64, P, P]),
         "hf_profile_start": (c_int, [P, c_int32]),
         "hf_profile_stop": (c_int, [P, POINTER(ctypes.c_double), POINTER(c_int32)]),
         "hf_next_ev_index": (c_int64, [P]),
@@ -96,7 +98,7 @@ EXPORTED = ("hf_workspace_bytes", "hf_state_init", "hf_absorb_evicted", "hf_atte
             "hf_key_cache_reset", "hf_window_attach", "hf_window_begin_chunk",
             "hf_window_attend", "hf_window_range", "hf_block_scores",
             "hf_backward_workspace_bytes", "hf_attend_backward", "hf_absorb_backward",
-            "hf_profile_start",
+            "hf_attend_chunk_noalloc", "hf_profile_start",
             "hf_profile_stop", "hf_next_ev_index", "hf_state_destroy", "hf_status_string")
 HF_KERNEL_NAMES = ("absorb", "block_pool", "score_select", "sparse_swa", "bwd_index", "bwd_dq",
                    "bwd_dkv", "bwd_state", "absorb_bwd")
@@ -222,6 +224,14 @@ def hf_absorb_backward(state: int, k_ev: int, v_ev: int, n_ev: int, ev_head_stri
                        dz: int, dk_ev: int, dv_ev: int, dev_head_stride: int, stream: int) -> int:
     return _lib.hf_absorb_backward(state, k_ev, v_ev, n_ev, ev_head_stride, dS, dz, dk_ev, dv_ev,
                                    dev_head_stride, stream)
+
+
+def hf_attend_chunk_noalloc(cfg: hf_config, S: int, z: int, q: int, n_q: int, q_head_stride: int,
+                            k_win: int, v_win: int, n_kv: int, kv_head_stride: int, top_k: int,
+                            out: int, out_head_stride: int, sel_out: int, stream: int) -> int:
+    return _lib.hf_attend_chunk_noalloc(ctypes.byref(cfg), S, z, q, n_q, q_head_stride, k_win,
+                                        v_win, n_kv, kv_head_stride, top_k, out, out_head_stride,
+                                        sel_out, stream)
 
 
 def hf_profile_start(state: int, max_launches: int) -> int:

@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -159,6 +160,53 @@ hf_status check_tensor(const void* p, int64_t n, int64_t head_stride, const hf_c
   if (head_stride < n * c.head_dim) return HF_ERR_INVALID_ARG;
   if ((head_stride * (int64_t)elem_size(c.dtype)) % 16 != 0) return HF_ERR_INVALID_ARG;
   return HF_OK;
+}
+
+// ---- Scratch of hf_attend_chunk_noalloc ---------------------------------------------
+// A file-scope device array: every device the library runs on holds its own copy
+// until the process ends. Host code never passes `hf_noalloc_scratch` itself to a
+// kernel (on the host that name is only a stand-in, not a device address): the
+// device address is looked up once per device with hipGetSymbolAddress and kept.
+static __device__ __align__(256) unsigned char hf_noalloc_scratch[HF_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's scratch (the device is current); nullptr on error.
+char* noalloc_scratch(int device) {
+  if (device < 0 || device >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[device]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(hf_noalloc_scratch)) != hipSuccess || !p)
+      return nullptr;
+    g_scratch_ptr[device] = static_cast<char*>(p);
+  }
+  return g_scratch_ptr[device];
+}
+
+// Scratch layout of one call: pooled query and key means, the selection (if the
+// caller passes none) and, for bf16, the hi/lo split of S.
+struct NoallocLayout {
+  size_t pooled_q, pooled_k, sel, s_split, total;
+};
+
+NoallocLayout noalloc_layout(const hf_config& c, int64_t n_q, int64_t n_kv, int32_t top_k) {
+  const size_t H = (size_t)c.num_heads, d = (size_t)c.head_dim;
+  const size_t nqb = (size_t)ceil_div(n_q, c.block_size), nkb = (size_t)ceil_div(n_kv, c.block_size);
+  NoallocLayout L;
+  size_t off = 0;
+  L.pooled_q = off;
+  off += round_up(H * nqb * d * 4);
+  L.pooled_k = off;
+  off += round_up(H * nkb * d * 4);
+  L.sel = off;
+  off += round_up(H * nqb * (size_t)top_k * 4);
+  L.s_split = off;
+  if (c.dtype == HF_BF16) off += round_up(H * 2 * d * d * 2);
+  L.total = off;
+  return L;
 }
 
 }  // namespace
@@ -747,6 +795,62 @@ hf_status hf_absorb_backward(hf_state* st, const void* k_ev, const void* v_ev, i
                                         ev_head_stride, dS, dz, dk_ev, dv_ev, dev_head_stride, s);
     });
   });
+}
+
+hf_status hf_attend_chunk_noalloc(const hf_config* cfg, const float* S, const float* z,
+                                  const void* q, int64_t n_q, int64_t q_head_stride,
+                                  const void* k_win, const void* v_win, int64_t n_kv,
+                                  int64_t kv_head_stride, int32_t top_k, void* out,
+                                  int64_t out_head_stride, int32_t* sel_out, void* stream) {
+  if (!cfg) return HF_ERR_INVALID_ARG;
+  // The call's own sizes stand in for the capacity limits of a state.
+  hf_config c = *cfg;
+  c.max_n_q = n_q > 0 ? n_q : 1;
+  c.max_n_kv = n_kv > 0 ? n_kv : 1;
+  c.max_n_ev = 0;
+  c.max_top_k = top_k > 0 ? top_k : 1;
+  hf_status e = check_config(&c);
+  if (e != HF_OK) return e;
+  if (n_q < 0 || n_kv < 1) return HF_ERR_INVALID_ARG;
+  if (!S || !z || !aligned16(S) || !aligned16(z)) return HF_ERR_INVALID_ARG;
+  e = n_q > 0 ? check_tensor(q, n_q, q_head_stride, c) : HF_OK;
+  if (e == HF_OK) e = check_tensor(k_win, n_kv, kv_head_stride, c);
+  if (e == HF_OK) e = check_tensor(v_win, n_kv, kv_head_stride, c);
+  if (e == HF_OK && n_q > 0) e = check_tensor(out, n_q, out_head_stride, c);
+  if (e != HF_OK) return e;
+  const int64_t nkb = ceil_div(n_kv, c.block_size);
+  if (top_k < 1 || top_k > nkb) return HF_ERR_INVALID_ARG;
+  if (sel_out && (reinterpret_cast<uintptr_t>(sel_out) & 3u)) return HF_ERR_INVALID_ARG;
+  const NoallocLayout L = noalloc_layout(c, n_q, n_kv, top_k);
+  if (L.total > HF_NOALLOC_SCRATCH_BYTES) return HF_ERR_INVALID_ARG;
+  if (n_q == 0) return HF_OK;
+  int device = -1;
+  if (hipGetDevice(&device) != hipSuccess) return HF_ERR_HIP;
+  char* scratch = noalloc_scratch(device);
+  if (!scratch) return HF_ERR_HIP;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const float scale = c.softmax_scale > 0.f ? c.softmax_scale : 1.0f / std::sqrt((float)c.head_dim);
+  const int nqb = (int)ceil_div(n_q, c.block_size);
+  float* pooled_q = reinterpret_cast<float*>(scratch + L.pooled_q);
+  float* pooled_k = reinterpret_cast<float*>(scratch + L.pooled_k);
+  int32_t* sel = sel_out ? sel_out : reinterpret_cast<int32_t*>(scratch + L.sel);
+  uint16_t* s_split = c.dtype == HF_BF16 ? reinterpret_cast<uint16_t*>(scratch + L.s_split) : nullptr;
+  // Every scratch byte a kernel reads is written earlier in the same call, so nothing
+  // needs clearing; the same kernels as hf_attend_chunk give the same bits.
+  hipError_t r = hipSuccess;
+  if (s_split) r = hf::launch_split_state(c.num_heads, c.head_dim, S, s_split, s);
+  if (r == hipSuccess)
+    r = hf::launch_block_pool(c.dtype, c.num_heads, c.head_dim, c.block_size, q, n_q,
+                              q_head_stride, k_win, n_kv, kv_head_stride, pooled_q, pooled_k, nqb,
+                              (int)nkb, s);
+  if (r == hipSuccess)
+    r = hf::launch_score_select(c.num_heads, c.head_dim, nqb, (int)nkb, nqb, (int)nkb, pooled_q,
+                                pooled_k, scale, top_k, sel, nullptr, s);
+  if (r == hipSuccess)
+    r = hf::launch_sparse_swa(c.dtype, c.num_heads, c.head_dim, c.block_size, q, n_q,
+                              q_head_stride, k_win, v_win, n_kv, kv_head_stride, sel, top_k, S,
+                              s_split, z, c.eps, scale, out, out_head_stride, s);
+  return r == hipSuccess ? HF_OK : HF_ERR_HIP;
 }
 
 hf_status hf_profile_start(hf_state* st, int32_t max_launches) {

@@ -301,6 +301,31 @@ hf_status hf_absorb_backward(hf_state* st, const void* k_ev, const void* v_ev, i
                              int64_t ev_head_stride, const float* dS, const float* dz,
                              float* dk_ev, float* dv_ev, int64_t dev_head_stride, void* stream);
 
+/* ---- Allocation-free attention ------------------------------------------------
+ * For callers that cannot allocate device memory or hand the library a workspace:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. hf_attend_chunk_noalloc computes exactly what hf_attend_chunk computes
+ * (same kernels, same bits) for a state holding S and z, without a handle: cfg gives
+ * num_heads, head_dim, block_size, dtype, eps and softmax_scale (its max_* fields are
+ * ignored); S ([H][d][d] fp32) and z ([H][d] fp32) are read only; the other arguments
+ * are those of hf_attend_chunk. The intermediates (pooled block means, the selection
+ * when sel_out is NULL, and for bf16 the hi/lo split of S) live in a scratch array of
+ * HF_NOALLOC_SCRATCH_BYTES that the library keeps in each device's memory for the
+ * life of the process; the call allocates nothing and calls no allocating routine.
+ * A call needs, rounded up to 256 bytes each, H*ceil(n_q/B)*d*4 + H*ceil(n_kv/B)*d*4
+ * + H*ceil(n_q/B)*top_k*4 (+ H*2*d*d*2 for bf16) bytes of it: 2.8 MB at 12 heads,
+ * d = 128, 4680 queries, 14040 window tokens and top_k 55. A larger call fails with
+ * HF_ERR_INVALID_ARG and enqueues nothing. All calls on one device share that device's
+ * scratch and each overwrites it (every byte read is written earlier in the same
+ * call, so nothing needs clearing): calls whose work overlaps on one device race, so
+ * order them on one stream or synchronise between them. */
+#define HF_NOALLOC_SCRATCH_BYTES (8u << 20)
+hf_status hf_attend_chunk_noalloc(const hf_config* cfg, const float* S, const float* z,
+                                  const void* q, int64_t n_q, int64_t q_head_stride,
+                                  const void* k_win, const void* v_win, int64_t n_kv,
+                                  int64_t kv_head_stride, int32_t top_k, void* out,
+                                  int64_t out_head_stride, int32_t* sel_out, void* stream);
+
 /* Kernels a state launches, for per-kernel timing. */
 typedef enum {
   HF_KERNEL_ABSORB = 0,       /* hf_absorb_evicted (both of its launches) */

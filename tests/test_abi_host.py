@@ -166,3 +166,31 @@ def test_window_bookkeeping_matches_the_oracle():
     for c, W in ((2, 2), (3, 9), (1, 4), (4, 3)):
         for t in range(40):
             assert hla.window_frames(t, c, W) == oracle.stream_step_frames(t, c, W)
+
+
+def test_noalloc_validation():
+    """hf_attend_chunk_noalloc rejects bad arguments and calls too large for its static
+    scratch before any HIP call; valid calls reach the runtime (no device here)."""
+    A = 1 << 20
+    c = cfg()
+    H, d = c.num_heads, c.head_dim
+    ok = dict(S=A, z=A, q=A, n_q=4680, qs=4680 * d, k=A, v=A, n_kv=14040, kvs=14040 * d,
+              top_k=55, out=A, outs=4680 * d, sel=0)
+
+    def call(cf=c, **kw):
+        a = dict(ok, **kw)
+        return hla.hf_attend_chunk_noalloc(cf, a["S"], a["z"], a["q"], a["n_q"], a["qs"], a["k"],
+                                           a["v"], a["n_kv"], a["kvs"], a["top_k"], a["out"],
+                                           a["outs"], a["sel"], 0)
+
+    for bad in (dict(S=0), dict(z=A + 4), dict(q=0), dict(out=A + 2), dict(top_k=0),
+                dict(top_k=221), dict(n_kv=0), dict(n_q=-1), dict(qs=10), dict(sel=A + 1)):
+        assert call(**bad) == B.HF_ERR_INVALID_ARG, bad
+    assert call(cf=cfg(head_dim=96)) == B.HF_ERR_UNSUPPORTED
+    assert call(cf=cfg(eps=0.0)) == B.HF_ERR_INVALID_ARG
+    # beyond the scratch: 4x the Wan-like window and chunk (about 11 MB of scratch)
+    assert call(n_q=4 * 4680, qs=4 * 4680 * d, n_kv=4 * 14040, kvs=4 * 14040 * d,
+                top_k=4 * 55, outs=4 * 4680 * d) == B.HF_ERR_INVALID_ARG
+    assert call(n_q=0) == B.HF_OK  # nothing to do, nothing enqueued
+    if NO_GPU:
+        assert call() == B.HF_ERR_HIP

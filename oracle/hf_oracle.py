@@ -178,6 +178,13 @@ def valid_top_k(scores32: np.ndarray, sel: np.ndarray, rel: float = 1e-3) -> boo
 # Sparse path: [EN] 2.A.2; sum of the paths: [ES] 2.A.2; linear read: [EN] 2.A.1.
 
 
+def linear_read(q: np.ndarray, S: np.ndarray, z: np.ndarray, eps: float = DEFAULT_EPS) -> np.ndarray:
+    """Read of one head's linear state for query rows q [n][d] ([EN] 2.A.1):
+    S phi(q_r) / (z . phi(q_r) + eps), float64."""
+    fq = phi(np.asarray(q, np.float64))
+    return (fq @ S.T) / (fq @ z + eps)[:, None]
+
+
 def attend_with_sel(q: np.ndarray, k_win: np.ndarray, v_win: np.ndarray, sel: np.ndarray,
                     S: np.ndarray, z: np.ndarray, block: int, eps: float = DEFAULT_EPS,
                     scale: Optional[float] = None,
@@ -213,8 +220,7 @@ def attend_with_sel(q: np.ndarray, k_win: np.ndarray, v_win: np.ndarray, sel: np
         p = np.exp(logits)
         p /= p.sum(axis=1, keepdims=True)
         o_swa[h, s0:s1] = p @ v_win[h, rows]
-        fq = phi(qi)
-        o_lin[h, s0:s1] = (fq @ S[h].T) / (fq @ z[h] + eps)[:, None]
+        o_lin[h, s0:s1] = linear_read(qi, S[h], z[h], eps)
     out = o_swa + o_lin
     if return_parts:
         return out, o_swa, o_lin
@@ -227,6 +233,65 @@ def attend(q, k_win, v_win, S, z, block: int, top_k: int, eps: float = DEFAULT_E
     sel, s32 = select(q, k_win, block, top_k, scale)
     out = attend_with_sel(q, k_win, v_win, sel, S, z, block, eps, scale, blocks)
     return out, sel, s32
+
+
+# ----------------------------------------------------- relative temporal RoPE
+# [EN] 2.C "Stability Enhancements" (Relative RoPE Constraint) and [ES] 2.C: the
+# temporal rotary position indices are kept below a fixed bound in training and in
+# inference, positions being relative offsets. The pages give neither the rotated
+# features, the frequencies nor the bound; the readings taken here:
+#   * the standard rotary form: the first rot_dims features of a query or key vector
+#     rotate in adjacent pairs (2i, 2i+1), pair i by the angle p * base^(-2i/rot_dims)
+#     for position p; the other features (spatial position, applied upstream) stay;
+#   * the position of a window token is its frame's offset from the window's first
+#     frame, capped: p = min(row // tokens_per_frame, cap); the queries are the
+#     window's last rows (the current chunk);
+#   * the rotation applies to the softmax path (block scores and sparse attention);
+#     the linear state absorbs and reads position-free (unrotated) features.
+
+
+def rope_positions(n_rows: int, tokens_per_frame: int, cap: int, row0: int = 0) -> np.ndarray:
+    """Temporal positions of window rows row0 .. row0 + n_rows - 1: min(frame, cap),
+    frames counted from the window's first row."""
+    rows = np.arange(row0, row0 + n_rows, dtype=np.int64)
+    return np.minimum(rows // tokens_per_frame, cap)
+
+
+def rope_rotate(x: np.ndarray, pos: np.ndarray, rot_dims: int, theta_base: float) -> np.ndarray:
+    """Rotate the first rot_dims features of every row of x [H][n][d] in pairs
+    (2i, 2i+1) by pos[n] * theta_base^(-2i/rot_dims), float64."""
+    x = np.array(x, dtype=np.float64, copy=True)
+    if rot_dims == 0:
+        return x
+    i = np.arange(rot_dims // 2, dtype=np.float64)
+    ang = np.asarray(pos, np.float64)[:, None] * theta_base ** (-2.0 * i / rot_dims)[None, :]
+    c, s = np.cos(ang), np.sin(ang)
+    a = x[..., 0:rot_dims:2].copy()
+    b = x[..., 1:rot_dims:2].copy()
+    x[..., 0:rot_dims:2] = a * c - b * s
+    x[..., 1:rot_dims:2] = a * s + b * c
+    return x
+
+
+def attend_rope(q, k_win, v_win, S, z, block: int, top_k: int, tokens_per_frame: int, cap: int,
+                rot_dims: int, theta_base: float, eps: float = DEFAULT_EPS,
+                scale: Optional[float] = None, blocks=None):
+    """Hybrid attention with the relative temporal rotation on the softmax path.
+    The window [H][n_kv][d] starts on a frame boundary; q holds its last n_q rows.
+    Returns (out, sel, fp32 scores)."""
+    n_q, n_kv = q.shape[1], k_win.shape[1]
+    qr = rope_rotate(q, rope_positions(n_q, tokens_per_frame, cap, n_kv - n_q), rot_dims,
+                     theta_base)
+    kr = rope_rotate(k_win, rope_positions(n_kv, tokens_per_frame, cap), rot_dims, theta_base)
+    sel, s32 = select(qr, kr, block, top_k, scale)
+    _, o_swa, _ = attend_with_sel(qr, kr, v_win, sel, S, z, block, eps, scale, blocks,
+                                  return_parts=True)
+    o_lin = np.full(o_swa.shape, np.nan)
+    rows = np.isfinite(o_swa[..., 0])
+    q = np.asarray(q, np.float64)
+    for h in range(q.shape[0]):
+        o_lin[h, rows[h]] = linear_read(q[h, rows[h]], S[h], z[h], eps)
+    return o_swa + o_lin, sel, s32
 
 
 # --------------------------------------------------------------- stream order

@@ -85,6 +85,9 @@ def parse():
                         "hf_window_attend); each step writes the chunk's K and V into its slot")
     p.add_argument("--ring-windows", type=int, default=4,
                    help="ring length in windows for --managed-window (>= 2)")
+    p.add_argument("--rope-cap", type=int, default=None,
+                   help="turn on the relative temporal rotation (44 of 128 features, base "
+                        "10000, 1560 tokens per frame) with this cap on the position index")
     p.add_argument("--side-stream", action="store_true",
                    help="hf_absorb_and_attend with the absorb on a side stream")
     p.add_argument("--cpu-reps", type=int, default=3)
@@ -117,6 +120,7 @@ class LayerSet:
         self.H, self.n_q, self.d = self.q.shape
         self.n_kv, self.n_ev = w1 - w0, e1 - e0
         self.top_k = top_k
+        self.rope_cap = None
         self.out = torch.empty_like(self.q)
         self.st = hla.HybridAttentionState(self.H, self.d, 64, torch.bfloat16,
                                            max_n_q=self.n_q, max_n_kv=self.n_kv,
@@ -153,7 +157,8 @@ class LayerSet:
         nqb, nkb = -(-n_q // B), -(-self.n_kv // B)
         return dict(
             absorb=2 * self.n_ev * d * 2 * H + self.state_bytes(),
-            block_pool=(n_q + self.n_kv) * d * 2 * H + (nqb + nkb) * d * 4 * H,
+            block_pool=(n_q + self.n_kv) * d * 2 * H + (nqb + nkb) * d * 4 * H
+            + (self.n_kv * d * 2 * H if self.rope_cap is not None else 0),  # rotated keys
             score_select=(nqb + nkb) * d * 4 * H + nqb * self.top_k * 4 * H,
             sparse_swa=(n_q + 2 * self.n_kv) * d * 2 * H + n_q * d * 2 * H + (d * d + d) * 4 * H)
 
@@ -417,7 +422,11 @@ def cpu_baseline(layer: LayerSet, reps: int):
         t0 = time.perf_counter()
         S, z = oracle.state_init(layer.H, layer.d)
         oracle.absorb(S, z, k[:, e0:e1], v[:, e0:e1])
-        _, sel, _ = oracle.attend(q, k[:, w0:w1], v[:, w0:w1], S, z, 64, layer.top_k)
+        if layer.rope_cap is None:
+            _, sel, _ = oracle.attend(q, k[:, w0:w1], v[:, w0:w1], S, z, 64, layer.top_k)
+        else:
+            _, sel, _ = oracle.attend_rope(q, k[:, w0:w1], v[:, w0:w1], S, z, 64, layer.top_k,
+                                           1560, layer.rope_cap, 44, 10000.0)
         times.append(time.perf_counter() - t0)
     t = statistics.median(times)
     fl = layer.flops(None, sel)
@@ -474,6 +483,12 @@ def main():
             inps = list(ex.map(synth.wan_layer_inputs, [args.seed + i for i in range(n_sets)]))
         sets = [LayerSet(hla, torch, synth, args.seed + i, top_k, inps[i]) for i in range(n_sets)]
         del inps
+    if args.rope_cap is not None:
+        if streams:
+            sys.exit("--rope-cap runs with caller-held windows (the default step)")
+        for s in sets:
+            s.rope_cap = args.rope_cap
+            s.st.set_rope(44, 10000.0, 1560, args.rope_cap)
     log(f"[bench] {n_sets} input sets resident ({time.time() - t0:.1f}s)")
 
     # Selection of every set (for the executed-FLOP count); not timed.
@@ -694,6 +709,8 @@ def main():
             "streams": bool(streams),
             "cached_pooling": bool(args.cached_pooling),
             "managed_window": window,
+            "rope": None if args.rope_cap is None else dict(
+                rot_dims=44, theta_base=10000.0, tokens_per_frame=1560, cap=args.rope_cap),
         },
         "pct_of_mfma_peak": round(100 * value / peak, 3),
         "ms_per_step_with_kernel_events": round(ms_step_ev, 5),

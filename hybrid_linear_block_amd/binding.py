@@ -37,6 +37,15 @@ class hf_config(Structure):
     ]
 
 
+class hf_rope(ctypes.Structure):
+    _fields_ = [
+        ("rot_dims", c_int32),
+        ("theta_base", c_float),
+        ("tokens_per_frame", c_int64),
+        ("cap", c_int32),
+    ]
+
+
 class HfError(RuntimeError):
     def __init__(self, status: int, what: str):
         self.status = status
@@ -76,6 +85,8 @@ def _load():
                                        P, c_int64, P, c_int64, P, P, c_int64, P, P, P, c_size_t,
                                        P]),
         "hf_absorb_backward": (c_int, [P, P, P, c_int64, c_int64, P, P, P, P, c_int64, P]),
+        "hf_rope_workspace_bytes": (c_size_t, [POINTER(hf_config), POINTER(hf_rope)]),
+        "hf_set_rope": (c_int, [P, POINTER(hf_rope), P, c_size_t, P]),
         "hf_attend_chunk_noalloc": (c_int, [POINTER(hf_config), P, P, P, c_int64, c_int64, P, P,
                                             c_int64, c_int64, c_int32, P, c_int64, P, P]),
         "hf_profile_start": (c_int, [P, c_int32]),
@@ -98,7 +109,8 @@ EXPORTED = ("hf_workspace_bytes", "hf_state_init", "hf_absorb_evicted", "hf_atte
             "hf_key_cache_reset", "hf_window_attach", "hf_window_begin_chunk",
             "hf_window_attend", "hf_window_range", "hf_block_scores",
             "hf_backward_workspace_bytes", "hf_attend_backward", "hf_absorb_backward",
-            "hf_attend_chunk_noalloc", "hf_profile_start",
+            "hf_rope_workspace_bytes", "hf_set_rope", "hf_attend_chunk_noalloc",
+            "hf_profile_start",
             "hf_profile_stop", "hf_next_ev_index", "hf_state_destroy", "hf_status_string")
 HF_KERNEL_NAMES = ("absorb", "block_pool", "score_select", "sparse_swa", "bwd_index", "bwd_dq",
                    "bwd_dkv", "bwd_state", "absorb_bwd")
@@ -224,6 +236,15 @@ def hf_absorb_backward(state: int, k_ev: int, v_ev: int, n_ev: int, ev_head_stri
                        dz: int, dk_ev: int, dv_ev: int, dev_head_stride: int, stream: int) -> int:
     return _lib.hf_absorb_backward(state, k_ev, v_ev, n_ev, ev_head_stride, dS, dz, dk_ev, dv_ev,
                                    dev_head_stride, stream)
+
+
+def hf_rope_workspace_bytes(cfg: hf_config, rope: hf_rope) -> int:
+    return int(_lib.hf_rope_workspace_bytes(ctypes.byref(cfg), ctypes.byref(rope)))
+
+
+def hf_set_rope(state: int, rope, workspace: int, ws_bytes: int, stream: int) -> int:
+    return _lib.hf_set_rope(state, ctypes.byref(rope) if rope is not None else None, workspace,
+                            ws_bytes, stream)
 
 
 def hf_attend_chunk_noalloc(cfg: hf_config, S: int, z: int, q: int, n_q: int, q_head_stride: int,

@@ -40,6 +40,9 @@ struct hf_state {
   char* k_ring = nullptr;
   char* v_ring = nullptr;
   bool win_on = false, win_ok = false;
+  // Relative temporal rotation of the softmax path (hf_set_rope); rope.cs == nullptr: off.
+  hf_rope rope_cfg = {};
+  hf::Rope rope;
   // Per-kernel timing (hf_profile_start / hf_profile_stop).
   bool prof_on = false;
   int prof_cap = 0;
@@ -159,6 +162,31 @@ hf_status check_tensor(const void* p, int64_t n, int64_t head_stride, const hf_c
   if (!p || !aligned16(p)) return HF_ERR_INVALID_ARG;
   if (head_stride < n * c.head_dim) return HF_ERR_INVALID_ARG;
   if ((head_stride * (int64_t)elem_size(c.dtype)) % 16 != 0) return HF_ERR_INVALID_ARG;
+  return HF_OK;
+}
+
+// ---- Relative temporal rotation -------------------------------------------------------
+struct RopeLayout {
+  size_t table, k_copy, total;
+  int npos;
+};
+
+RopeLayout rope_layout(const hf_config& c, const hf_rope& r) {
+  const int64_t frames = ceil_div(c.max_n_kv, r.tokens_per_frame);
+  RopeLayout L;
+  L.npos = (int)((frames - 1 < r.cap ? frames - 1 : r.cap) + 1);
+  L.table = 0;
+  L.k_copy = round_up((size_t)L.npos * (size_t)(r.rot_dims / 2) * 8);
+  L.total = L.k_copy + round_up((size_t)c.num_heads * (size_t)c.max_n_kv * (size_t)c.head_dim *
+                                elem_size(c.dtype));
+  return L;
+}
+
+hf_status check_rope(const hf_config& c, const hf_rope* r) {
+  if (!r) return HF_ERR_INVALID_ARG;
+  if (r->rot_dims < 0 || r->rot_dims % 2 != 0 || r->rot_dims > c.head_dim) return HF_ERR_INVALID_ARG;
+  if (!(r->theta_base > 0.f) || !std::isfinite(r->theta_base)) return HF_ERR_INVALID_ARG;
+  if (r->tokens_per_frame < 1 || r->cap < 0) return HF_ERR_INVALID_ARG;
   return HF_OK;
 }
 
@@ -338,6 +366,14 @@ static hf_status check_attend_all(const hf_state* st, const void* q, int64_t n_q
   return HF_OK;
 }
 
+// Shapes an attend call needs when the rotation is on: the window holds whole frames
+// and the chunk's queries are its last rows.
+static hf_status check_rope_shapes(const hf_state* st, int64_t n_q, int64_t n_kv) {
+  if (!st->rope.cs) return HF_OK;
+  if (n_kv % st->rope.tpf != 0 || n_q > n_kv) return HF_ERR_INVALID_ARG;
+  return HF_OK;
+}
+
 // Window of a cached call: it starts on an 8-token group of the stream and holds
 // whole groups (the block size is a multiple of 8 in every configuration).
 static hf_status check_window(int64_t win_index, int64_t n_kv) {
@@ -379,6 +415,11 @@ static hipError_t enqueue_attend(hf_state* st, const void* q, int64_t n_q, int64
   const int nqb = (int)ceil_div(n_q, c.block_size);
   const int nkb = (int)ceil_div(n_kv, c.block_size);
   int32_t* sel = sel_out ? sel_out : st->sel;
+  // With the rotation on, the pooling rotates Q and K and writes the rotated window
+  // keys, which the attention kernel reads instead of k_win (the chunk's queries are
+  // the window's last n_q rows).
+  hf::Rope rope = st->rope;
+  if (rope.cs) rope.q_row0 = n_kv - n_q;
   hipError_t r = timed(st, HF_KERNEL_BLOCK_POOL, s, [&]() {
     const hf::KeyCache none;
     const hf::KeyCache& kcr = kc ? *kc : none;
@@ -386,10 +427,10 @@ static hipError_t enqueue_attend(hf_state* st, const void* q, int64_t n_q, int64
       return hf::launch_absorb_and_pool(c.dtype, c.num_heads, c.head_dim, c.block_size, fa->k_ev,
                                         fa->v_ev, fa->n_ev, fa->head_stride, st->partials, q, n_q,
                                         q_hs, k_win, n_kv, kv_hs, st->pooled_q, st->pooled_k,
-                                        st->nqb_cap, st->nkb_cap, s, kcr);
+                                        st->nqb_cap, st->nkb_cap, s, kcr, rope);
     return hf::launch_block_pool(c.dtype, c.num_heads, c.head_dim, c.block_size, q, n_q, q_hs,
                                  k_win, n_kv, kv_hs, st->pooled_q, st->pooled_k, st->nqb_cap,
-                                 st->nkb_cap, s, kcr);
+                                 st->nkb_cap, s, kcr, rope);
   });
   if (r == hipSuccess && kc) {  // the pooling launch sums (or reads) every group of the window
     st->kc_lo = kc->g0;
@@ -412,7 +453,7 @@ static hipError_t enqueue_attend(hf_state* st, const void* q, int64_t n_q, int64
     r = timed(st, HF_KERNEL_SPARSE_SWA, s, [&]() {
       return hf::launch_sparse_swa(c.dtype, c.num_heads, c.head_dim, c.block_size, q, n_q, q_hs,
                                    k_win, v_win, n_kv, kv_hs, sel, top_k, st->S, st->s_split,
-                                   st->z, c.eps, st->scale, out, out_hs, s);
+                                   st->z, c.eps, st->scale, out, out_hs, s, rope);
     });
   return r;
 }
@@ -422,8 +463,9 @@ hf_status hf_attend_chunk(hf_state* st, const void* q, int64_t n_q, int64_t q_he
                           int64_t kv_head_stride, int32_t top_k, void* out,
                           int64_t out_head_stride, int32_t* sel_out, void* stream) {
   if (!st) return HF_ERR_INVALID_ARG;
-  const hf_status e = check_attend_all(st, q, n_q, q_head_stride, k_win, v_win, n_kv,
-                                       kv_head_stride, top_k, out, out_head_stride, sel_out);
+  hf_status e = check_attend_all(st, q, n_q, q_head_stride, k_win, v_win, n_kv,
+                                 kv_head_stride, top_k, out, out_head_stride, sel_out);
+  if (e == HF_OK) e = check_rope_shapes(st, n_q, n_kv);
   if (e != HF_OK || n_q == 0) return e;
   hipStream_t s = static_cast<hipStream_t>(stream);
   return on_device(st->device, [&]() {
@@ -443,6 +485,7 @@ hf_status hf_absorb_and_attend(hf_state* st, const void* k_ev, const void* v_ev,
   if (e == HF_OK)
     e = check_attend_all(st, q, n_q, q_head_stride, k_win, v_win, n_kv, kv_head_stride, top_k,
                          out, out_head_stride, sel_out);
+  if (e == HF_OK && n_q > 0) e = check_rope_shapes(st, n_q, n_kv);
   if (e != HF_OK) return e;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipStream_t side = static_cast<hipStream_t>(side_stream);
@@ -485,6 +528,7 @@ hf_status hf_attend_chunk_cached(hf_state* st, const void* q, int64_t n_q, int64
                                  void* out, int64_t out_head_stride, int32_t* sel_out,
                                  void* stream) {
   if (!st) return HF_ERR_INVALID_ARG;
+  if (st->rope.cs) return HF_ERR_UNSUPPORTED;  // rotated keys are not cached
   hf_status e = check_attend_all(st, q, n_q, q_head_stride, k_win, v_win, n_kv, kv_head_stride,
                                  top_k, out, out_head_stride, sel_out);
   if (e == HF_OK && n_q > 0) e = check_window(win_index, n_kv);
@@ -505,6 +549,7 @@ hf_status hf_absorb_and_attend_cached(hf_state* st, const void* k_ev, const void
                                       void* out, int64_t out_head_stride, int32_t* sel_out,
                                       void* stream) {
   if (!st) return HF_ERR_INVALID_ARG;
+  if (st->rope.cs) return HF_ERR_UNSUPPORTED;  // rotated keys are not cached
   hf_status e = check_absorb(st, k_ev, v_ev, n_ev, ev_head_stride, ev_index);
   if (e == HF_OK)
     e = check_attend_all(st, q, n_q, q_head_stride, k_win, v_win, n_kv, kv_head_stride, top_k,
@@ -599,6 +644,7 @@ hf_status hf_window_attend(hf_state* st, const void* q, int64_t n_q, int64_t q_h
                            int32_t top_k, void* out, int64_t out_head_stride, int32_t* sel_out,
                            void* stream) {
   if (!st) return HF_ERR_INVALID_ARG;
+  if (st->rope.cs) return HF_ERR_UNSUPPORTED;
   if (!st->win_on || !st->win_ok || st->win.cur == 0) return HF_ERR_STATE;
   const hf_config& c = st->cfg;
   if (st->next_ev < st->win.base || st->next_ev > st->win.hi) return HF_ERR_STATE;
@@ -663,6 +709,7 @@ hf_status hf_block_scores(hf_state* st, const void* q, int64_t n_q, int64_t q_he
   if (!st) return HF_ERR_INVALID_ARG;
   const hf_config& c = st->cfg;
   hf_status e = check_attend(st, q, n_q, q_head_stride, k_win, n_kv, kv_head_stride);
+  if (e == HF_OK) e = check_rope_shapes(st, n_q, n_kv);
   if (e != HF_OK) return e;
   if (!scores_out || (reinterpret_cast<uintptr_t>(scores_out) & 3u)) return HF_ERR_INVALID_ARG;
   if (n_q == 0) return HF_OK;
@@ -670,9 +717,12 @@ hf_status hf_block_scores(hf_state* st, const void* q, int64_t n_q, int64_t q_he
   const int nkb = (int)ceil_div(n_kv, c.block_size);
   hipStream_t s = static_cast<hipStream_t>(stream);
   return on_device(st->device, [&]() {
+    hf::Rope rope = st->rope;
+    if (rope.cs) rope.q_row0 = n_kv - n_q;
     hipError_t r = hf::launch_block_pool(c.dtype, c.num_heads, c.head_dim, c.block_size, q, n_q,
                                          q_head_stride, k_win, n_kv, kv_head_stride,
-                                         st->pooled_q, st->pooled_k, st->nqb_cap, st->nkb_cap, s);
+                                         st->pooled_q, st->pooled_k, st->nqb_cap, st->nkb_cap, s,
+                                         hf::KeyCache(), rope);
     if (r == hipSuccess)
       r = hf::launch_score_select(c.num_heads, c.head_dim, nqb, nkb, st->nqb_cap, st->nkb_cap,
                                   st->pooled_q, st->pooled_k, st->scale, 1, nullptr, scores_out,
@@ -721,6 +771,7 @@ hf_status hf_attend_backward(hf_state* st, const void* q, int64_t n_q, int64_t q
                              int64_t dkv_head_stride, float* dS, float* dz, void* bwd_ws,
                              size_t bwd_ws_bytes, void* stream) {
   if (!st) return HF_ERR_INVALID_ARG;
+  if (st->rope.cs) return HF_ERR_UNSUPPORTED;  // the backward has no rotation
   const hf_config& c = st->cfg;
   if (n_q < 1) return HF_ERR_INVALID_ARG;
   hf_status e = check_attend_all(st, q, n_q, q_head_stride, k_win, v_win, n_kv, kv_head_stride,
@@ -795,6 +846,44 @@ hf_status hf_absorb_backward(hf_state* st, const void* k_ev, const void* v_ev, i
                                         ev_head_stride, dS, dz, dk_ev, dv_ev, dev_head_stride, s);
     });
   });
+}
+
+size_t hf_rope_workspace_bytes(const hf_config* cfg, const hf_rope* rope) {
+  if (check_config(cfg) != HF_OK || check_rope(*cfg, rope) != HF_OK || rope->rot_dims == 0)
+    return 0;
+  return rope_layout(*cfg, *rope).total;
+}
+
+hf_status hf_set_rope(hf_state* st, const hf_rope* rope, void* workspace, size_t ws_bytes,
+                      void* stream) {
+  if (!st) return HF_ERR_INVALID_ARG;
+  if (!rope || rope->rot_dims == 0) {
+    st->rope = hf::Rope();
+    st->rope_cfg = hf_rope{};
+    return HF_OK;
+  }
+  const hf_config& c = st->cfg;
+  const hf_status e = check_rope(c, rope);
+  if (e != HF_OK) return e;
+  const RopeLayout L = rope_layout(c, *rope);
+  if (!workspace || !aligned16(workspace) || ws_bytes < L.total) return HF_ERR_INVALID_ARG;
+  char* w = static_cast<char*>(workspace);
+  hf::Rope r;
+  r.cs = reinterpret_cast<const float2*>(w + L.table);
+  r.half = rope->rot_dims / 2;
+  r.tpf = rope->tokens_per_frame;
+  r.cap = rope->cap;
+  r.k_out = w + L.k_copy;
+  r.k_out_hs = c.max_n_kv * c.head_dim;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hf_status rs = on_device(st->device, [&]() {
+    return hf::launch_rope_table(const_cast<float2*>(r.cs), L.npos, r.half,
+                                 (double)rope->theta_base, s);
+  });
+  if (rs != HF_OK) return rs;
+  st->rope = r;
+  st->rope_cfg = *rope;
+  return HF_OK;
 }
 
 hf_status hf_attend_chunk_noalloc(const hf_config* cfg, const float* S, const float* z,

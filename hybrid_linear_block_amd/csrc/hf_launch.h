@@ -46,10 +46,30 @@ struct KeyCache {
   int64_t g0 = 0;   // absolute group of window row 0
   int64_t lo = 0, hi = 0;
 };
+// Relative temporal rotation of the softmax path's queries and keys: the first
+// 2 * half features of a row rotate in pairs (2i, 2i+1) by the angle whose cosine
+// and sine are cs[p * half + i], p = min(window row / tpf, cap) the row's position.
+// Query row n is window row q_row0 + n. The pooling rotates every row it averages
+// and writes the window's rotated keys to k_out ([H][n_kv][d], head stride k_out_hs
+// elements, the element type of K) for the attention kernel. cs == nullptr: none.
+struct Rope {
+  const float2* cs = nullptr;
+  int half = 0;
+  int64_t tpf = 1;
+  int cap = 0;
+  int64_t q_row0 = 0;
+  void* k_out = nullptr;
+  int64_t k_out_hs = 0;
+};
+// cs[p * half + i] = (cos, sin) of p * base^(-2i / (2 half)) for p < npos (computed in
+// double precision).
+hipError_t launch_rope_table(float2* cs, int npos, int half, double theta_base,
+                             hipStream_t stream);
 hipError_t launch_block_pool(int dtype, int heads, int d, int block, const void* q, int64_t n_q,
                              int64_t q_hs, const void* k, int64_t n_kv, int64_t kv_hs,
                              float* pooled_q, float* pooled_k, int nqb_cap, int nkb_cap,
-                             hipStream_t stream, const KeyCache& kc = KeyCache());
+                             hipStream_t stream, const KeyCache& kc = KeyCache(),
+                             const Rope& rope = Rope());
 // The partial-state pass of an absorb of n_ev evicted tokens (as in launch_absorb)
 // and launch_block_pool in one launch: the two read and write different buffers
 // and are both bound by memory. The absorb is complete once
@@ -59,7 +79,7 @@ hipError_t launch_absorb_and_pool(int dtype, int heads, int d, int block, const 
                                   const void* q, int64_t n_q, int64_t q_hs, const void* k,
                                   int64_t n_kv, int64_t kv_hs, float* pooled_q, float* pooled_k,
                                   int nqb_cap, int nkb_cap, hipStream_t stream,
-                                  const KeyCache& kc = KeyCache());
+                                  const KeyCache& kc = KeyCache(), const Rope& rope = Rope());
 hipError_t launch_score_select(int heads, int d, int nqb, int nkb, int nqb_cap, int nkb_cap,
                                const float* pooled_q, const float* pooled_k, float scale,
                                int top_k, int32_t* sel, float* scores_out, hipStream_t stream);
@@ -72,11 +92,15 @@ hipError_t launch_select_and_reduce(int dtype, int heads, int d, int nqb, int nk
                                     hipStream_t stream);
 
 // ---- block-sparse softmax attention + linear read ---------------------------------
+// With rope.cs, the queries are rotated in the kernel and the keys are read from
+// rope.k_out (head stride rope.k_out_hs), the rotated keys the pooling wrote, instead
+// of k; the linear read uses the unrotated queries.
 hipError_t launch_sparse_swa(int dtype, int heads, int d, int block, const void* q, int64_t n_q,
                              int64_t q_hs, const void* k, const void* v, int64_t n_kv,
                              int64_t kv_hs, const int32_t* sel, int top_k, const float* S,
                              const uint16_t* s_split, const float* z, float eps, float scale,
-                             void* out, int64_t out_hs, hipStream_t stream);
+                             void* out, int64_t out_hs, hipStream_t stream,
+                             const Rope& rope = Rope());
 
 // ---- backward (fixed selection) ---------------------------------------------------
 struct BwdArgs {

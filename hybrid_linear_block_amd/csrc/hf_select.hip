@@ -31,6 +31,36 @@ namespace {
 
 constexpr int POOL_THREADS = 256;  // 4 waves, one (head, block) per wave
 
+// Rotate the VEC features of one row chunk (pairs p0 .. p0 + VEC/2 - 1 of the row) by
+// the row's temporal position (window row wrow): pairs below rope.half turn by the
+// tabulated angle, the others stay.
+template <int VEC>
+__device__ __forceinline__ void rope_chunk(float* v, int p0, const Rope& rope, int64_t wrow) {
+  const int64_t f = wrow / rope.tpf;
+  const int pos = f < rope.cap ? (int)f : rope.cap;
+  const float2* cs = rope.cs + (size_t)pos * rope.half;
+#pragma unroll
+  for (int e = 0; e < VEC; e += 2) {
+    if (p0 + e / 2 < rope.half) {
+      const float2 t = cs[p0 + e / 2];
+      const float a = v[e], b = v[e + 1];
+      v[e] = a * t.x - b * t.y;
+      v[e + 1] = a * t.y + b * t.x;
+    }
+  }
+}
+
+// VEC fp32 values as one 16-byte chunk of T (bf16: rounded to nearest even).
+template <typename T>
+__device__ __forceinline__ uint4 narrow16(const float* v) {
+  if constexpr (sizeof(T) == 2)
+    return make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                      pack_bf16x2(v[6], v[7]));
+  else
+    return make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                      __float_as_uint(v[3]));
+}
+
 // Row mean of one block per wave, summed by 8-row groups: lane (rg, cc) owns the
 // 16-byte column chunk cc of the groups rg, rg + RPI, ... of the block (all row
 // loads in flight together), adds each group's 8 rows in row order, adds its groups
@@ -42,7 +72,7 @@ __device__ __forceinline__ void pool_wave(
     int wid, const T* __restrict__ q, int64_t n_q, int64_t q_hs, const T* __restrict__ k,
     int64_t n_kv, int64_t kv_hs, int block, int nqb, int nkb, int heads,
     float* __restrict__ pooled_q, float* __restrict__ pooled_k, int nqb_cap, int nkb_cap,
-    const KeyCache& kc) {
+    const KeyCache& kc, const Rope& rope) {
   constexpr int VEC = 16 / sizeof(T);  // elements per 16-byte chunk
   constexpr int CPR = D / VEC;         // chunks per row
   constexpr int RPI = 64 / CPR;        // lane groups (rows per wave-wide load)
@@ -97,13 +127,25 @@ __device__ __forceinline__ void pool_wave(
       for (int e = 0; e < VEC; ++e) g8[e] = 0.f;
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
+        float v[VEC];
         if constexpr (sizeof(T) == 2) {
 #pragma unroll
-          for (int e = 0; e < VEC; ++e) g8[e] += bf16_to_f32(half16(x[i][r], e));
+          for (int e = 0; e < VEC; ++e) v[e] = bf16_to_f32(half16(x[i][r], e));
         } else {
 #pragma unroll
-          for (int e = 0; e < VEC; ++e) g8[e] += __uint_as_float(word(x[i][r], e));
+          for (int e = 0; e < VEC; ++e) v[e] = __uint_as_float(word(x[i][r], e));
         }
+        if (rope.cs != nullptr) {  // wave-uniform
+          const int64_t row = r0 + 8 * (rg + RPI * i) + r;
+          if (row < r1) {
+            if (cc * VEC < 2 * rope.half) rope_chunk<VEC>(v, cc * VEC / 2, rope, is_q ? rope.q_row0 + row : row);
+            if (!is_q)  // the window's rotated keys for the attention kernel
+              *reinterpret_cast<uint4*>(static_cast<T*>(rope.k_out) + (size_t)h * rope.k_out_hs +
+                                        row * D + cc * VEC) = narrow16<T>(v);
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) g8[e] += v[e];
       }
       if (use_cache && r0 + 8 * (rg + RPI * i) < r1) {  // a key group of the window
 #pragma unroll
@@ -133,9 +175,9 @@ template <typename T, int D>
 __global__ __launch_bounds__(POOL_THREADS) void block_pool(
     const T* __restrict__ q, int64_t n_q, int64_t q_hs, const T* __restrict__ k, int64_t n_kv,
     int64_t kv_hs, int block, int nqb, int nkb, int heads, float* __restrict__ pooled_q,
-    float* __restrict__ pooled_k, int nqb_cap, int nkb_cap, KeyCache kc) {
+    float* __restrict__ pooled_k, int nqb_cap, int nkb_cap, KeyCache kc, Rope rope) {
   pool_wave<T, D>(blockIdx.x * (POOL_THREADS / 64) + (threadIdx.x >> 6), q, n_q, q_hs, k, n_kv,
-                  kv_hs, block, nqb, nkb, heads, pooled_q, pooled_k, nqb_cap, nkb_cap, kc);
+                  kv_hs, block, nqb, nkb, heads, pooled_q, pooled_k, nqb_cap, nkb_cap, kc, rope);
 }
 
 // The absorb's partial states and the block pooling in one launch: workgroups
@@ -150,7 +192,7 @@ __global__ __launch_bounds__((absorb::threads<T, D>())) void absorb_and_pool(
     int n_split, float* __restrict__ partials, int n_abs, const T* __restrict__ q, int64_t n_q,
     int64_t q_hs, const T* __restrict__ k, int64_t n_kv, int64_t kv_hs, int block, int nqb,
     int nkb, int heads, float* __restrict__ pooled_q, float* __restrict__ pooled_k, int nqb_cap,
-    int nkb_cap, KeyCache kc) {
+    int nkb_cap, KeyCache kc, Rope rope) {
   if ((int)blockIdx.x < n_abs) {
     absorb::item<T, D>(blockIdx.x, n_split, kev, vev, n_ev, ev_hs, tps, partials);
   } else {
@@ -163,7 +205,7 @@ __global__ __launch_bounds__((absorb::threads<T, D>())) void absorb_and_pool(
     for (int wid = ((int)blockIdx.x - n_abs) * WPG + (int)(threadIdx.x >> 6); wid < total;
          wid += n_waves)
       pool_wave<T, D>(wid, q, n_q, q_hs, k, n_kv, kv_hs, block, nqb, nkb, heads, pooled_q,
-                      pooled_k, nqb_cap, nkb_cap, kc);
+                      pooled_k, nqb_cap, nkb_cap, kc, rope);
   }
 }
 
@@ -321,7 +363,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_and_reduce(
 hipError_t launch_block_pool(int dtype, int heads, int d, int block, const void* q, int64_t n_q,
                              int64_t q_hs, const void* k, int64_t n_kv, int64_t kv_hs,
                              float* pooled_q, float* pooled_k, int nqb_cap, int nkb_cap,
-                             hipStream_t stream, const KeyCache& kc) {
+                             hipStream_t stream, const KeyCache& kc, const Rope& rope) {
   const int nqb = (int)((n_q + block - 1) / block);
   const int nkb = (int)((n_kv + block - 1) / block);
   const int waves = heads * (nqb + nkb);
@@ -329,7 +371,7 @@ hipError_t launch_block_pool(int dtype, int heads, int d, int block, const void*
 #define HF_POOL(T, D)                                                                        \
   block_pool<T, D><<<grid, POOL_THREADS, 0, stream>>>(                                       \
       static_cast<const T*>(q), n_q, q_hs, static_cast<const T*>(k), n_kv, kv_hs, block, nqb, \
-      nkb, heads, pooled_q, pooled_k, nqb_cap, nkb_cap, kc)
+      nkb, heads, pooled_q, pooled_k, nqb_cap, nkb_cap, kc, rope)
   if (dtype == 0) {
     if (d == 128) HF_POOL(bf16_t, 128); else HF_POOL(bf16_t, 64);
   } else {
@@ -365,7 +407,7 @@ hipError_t launch_absorb_and_pool(int dtype, int heads, int d, int block, const 
                                   const void* q, int64_t n_q, int64_t q_hs, const void* k,
                                   int64_t n_kv, int64_t kv_hs, float* pooled_q, float* pooled_k,
                                   int nqb_cap, int nkb_cap, hipStream_t stream,
-                                  const KeyCache& kc) {
+                                  const KeyCache& kc, const Rope& rope) {
   const int nqb = (int)((n_q + block - 1) / block);
   const int nkb = (int)((n_kv + block - 1) / block);
   const AbsorbPlan p = absorb_plan(dtype, heads, d, n_ev);
@@ -380,7 +422,7 @@ hipError_t launch_absorb_and_pool(int dtype, int heads, int d, int block, const 
         static_cast<const T*>(k_ev), static_cast<const T*>(v_ev), n_ev, ev_hs,                 \
         p.tokens_per_split, p.n_split, partials, n_abs, static_cast<const T*>(q), n_q, q_hs,   \
         static_cast<const T*>(k), n_kv, kv_hs, block, nqb, nkb, heads, pooled_q, pooled_k,     \
-        nqb_cap, nkb_cap, kc);                                                                 \
+        nqb_cap, nkb_cap, kc, rope);                                                           \
   }
   if (dtype == 0) {
     if (d == 128) HF_ABSPOOL(bf16_t, 128) else HF_ABSPOOL(bf16_t, 64)

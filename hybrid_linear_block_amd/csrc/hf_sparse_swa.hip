@@ -35,6 +35,12 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// The angle table row (cos, sin of every rotated pair) of window row wrow's position.
+__device__ __forceinline__ const float2* rope_cs(const Rope& rope, int64_t wrow) {
+  const int64_t f = wrow / rope.tpf;
+  return rope.cs + (size_t)(f < rope.cap ? f : rope.cap) * rope.half;
+}
+
 template <typename T, int D, int BLK>
 struct SwaSmem;
 
@@ -80,12 +86,13 @@ struct SwaCfg {
   static_assert(BLK * CPR % NT == 0, "staging split");
 };
 
-template <typename T, int D, int BLK, int QW>
+template <typename T, int D, int BLK, int QW, bool ROPE>
 __global__ __launch_bounds__((BLK / QW) * 64) void sparse_swa(
     const T* __restrict__ q, int64_t n_q, int64_t q_hs, const T* __restrict__ kg,
     const T* __restrict__ vg, int64_t n_kv, int64_t kv_hs, const int32_t* __restrict__ sel,
     int top_k, int nqb, int n_logical, const float* __restrict__ S,
-    const float* __restrict__ z, float eps, float scale, T* __restrict__ out, int64_t out_hs) {
+    const float* __restrict__ z, float eps, float scale, T* __restrict__ out, int64_t out_hs,
+    Rope rope) {
   using C = SwaCfg<T, D, BLK, QW>;
   using M = Mfma<T>;
   using op_t = typename M::op_t;
@@ -100,7 +107,8 @@ __global__ __launch_bounds__((BLK / QW) * 64) void sparse_swa(
   const int g = lane >> 4, c = lane & 15;
 
   const T* qh = q + (size_t)h * q_hs;
-  const T* kh = kg + (size_t)h * kv_hs;
+  const T* kh = ROPE ? static_cast<const T*>(rope.k_out) + (size_t)h * rope.k_out_hs
+                     : kg + (size_t)h * kv_hs;
   const T* vh = vg + (size_t)h * kv_hs;
   const int32_t* my_sel = sel + ((size_t)h * nqb + i) * top_k;
   const int64_t qrow0 = (int64_t)i * BLK + w * QW;
@@ -116,7 +124,15 @@ __global__ __launch_bounds__((BLK / QW) * 64) void sparse_swa(
       if constexpr (KP == 8) {
         qop[n][s] = as_bf16x8(ld16(qh + r * D + s * KSTEP + g * KP, ok));
       } else {
-        qop[n][s] = ok ? qh[r * D + s * KSTEP + g] : 0.f;
+        const int f = s * KSTEP + g;
+        qop[n][s] = ok ? qh[r * D + f] : 0.f;
+        if constexpr (ROPE) {  // pair (f & ~1, f | 1) turns by the row's position
+          if (ok && (f >> 1) < rope.half) {
+            const float x = qop[n][s], y = qh[r * D + (f ^ 1)];
+            const float2 t = rope_cs(rope, rope.q_row0 + r)[f >> 1];
+            qop[n][s] = (f & 1) ? y * t.y + x * t.x : x * t.x - y * t.y;
+          }
+        }
       }
     }
   }
@@ -352,7 +368,12 @@ __global__ __launch_bounds__((BLK / QW) * 64) void sparse_swa(
       float f[C::NQT];
 #pragma unroll
       for (int n = 0; n < C::NQT; ++n) {
-        f[n] = phi(qop[n][s]);
+        float qv = qop[n][s];
+        if constexpr (ROPE) {  // the linear read takes the unrotated query
+          const int64_t r = qrow0 + n * 16 + c;
+          qv = r < n_q ? qh[r * D + i0] : 0.f;
+        }
+        f[n] = phi(qv);
         den[n] += zz * f[n];
       }
 #pragma unroll
@@ -407,13 +428,13 @@ __global__ __launch_bounds__((BLK / QW) * 64) void sparse_swa(
 // skipped whenever no query of the wave moved (softmax is shift-invariant).
 constexpr float kLazyMaxSlack = 8.f;
 
-template <int D, bool SHORT>
+template <int D, bool SHORT, bool ROPE>
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void sparse_swa_bf16(
     const bf16_t* __restrict__ q, int64_t n_q, int64_t q_hs, const bf16_t* __restrict__ kg,
     const bf16_t* __restrict__ vg, int64_t n_kv, int64_t kv_hs, const int32_t* __restrict__ sel,
     int top_k, int nqb, int n_logical, const uint16_t* __restrict__ s_split,
     const float* __restrict__ z, float eps, float scale, bf16_t* __restrict__ out,
-    int64_t out_hs) {
+    int64_t out_hs, Rope rope) {
   constexpr int BLK = 64, NW = 2, NQT = 2, NMT = 4, NET = D / 16, NKS = D / 32;
   constexpr int CPR = D / 8;            // 16-byte chunks per K/V row
   constexpr int TCH = BLK * CPR;        // chunks per tile
@@ -430,7 +451,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void s
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, c = lane & 15;
   const bf16_t* qh = q + (size_t)h * q_hs;
-  const bf16_t* kh = kg + (size_t)h * kv_hs;
+  const bf16_t* kh = ROPE ? static_cast<const bf16_t*>(rope.k_out) + (size_t)h * rope.k_out_hs
+                          : kg + (size_t)h * kv_hs;
   const bf16_t* vh = vg + (size_t)h * kv_hs;
   const int32_t* my_sel = sel + ((size_t)h * nqb + i) * top_k;
   const int64_t qrow0 = (int64_t)i * BLK + w * 32;
@@ -531,6 +553,33 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void s
     }
 #pragma unroll
     for (int n = 0; n < NQT; ++n) inv_den[n] = 1.f / (sum_over_groups(den[n]) + eps);
+  }
+  if constexpr (ROPE) {  // the QK operands turn by the row's position (rounded to bf16)
+#pragma unroll
+    for (int n = 0; n < NQT; ++n) {
+      const int64_t r = qrow0 + n * 16 + c;
+      const float2* cs = rope_cs(rope, rope.q_row0 + (r < n_q ? r : n_q - 1));
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) {
+        const int p0 = 16 * s + 4 * g;  // this lane's pairs p0 .. p0 + 3
+        if (p0 < rope.half) {
+          const uint4 qb = __builtin_bit_cast(uint4, qop[n][s]);
+          uint32_t w[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float a = bf16_to_f32(half16(qb, 2 * e)), b = bf16_to_f32(half16(qb, 2 * e + 1));
+            if (p0 + e < rope.half) {
+              const float2 t = cs[p0 + e];
+              const float a2 = a * t.x - b * t.y;
+              b = a * t.y + b * t.x;
+              a = a2;
+            }
+            w[e] = pack_bf16x2(a, b);
+          }
+          qop[n][s] = as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
+        }
+      }
+    }
   }
 
   f32x4 acc[NET][NQT];
@@ -738,6 +787,14 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void s
   }
 
   // ---- epilogue ----
+  if constexpr (ROPE) {  // the linear read takes the unrotated queries
+#pragma unroll
+    for (int n = 0; n < NQT; ++n) {
+      const int64_t r = qrow0 + n * 16 + c;
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) qop[n][s] = as_bf16x8(ld16(qh + r * D + s * 32 + g * 8, r < n_q));
+    }
+  }
   // out = O / l + S phi(q) / (z . phi(q) + eps): the accumulators are normalised in
   // place, then the linear read accumulates S (phi(q) / den) into them on MFMA, with
   // S and the scaled phi(q) split into bf16 hi + lo (three products; the split of S
@@ -803,17 +860,21 @@ template <int D>
 hipError_t launch_bf16(const void* q, int64_t n_q, int64_t q_hs, const void* k, const void* v,
                        int64_t n_kv, int64_t kv_hs, const int32_t* sel, int top_k, int heads,
                        const uint16_t* s_split, const float* z, float eps, float scale,
-                       void* out, int64_t out_hs, hipStream_t stream) {
+                       void* out, int64_t out_hs, hipStream_t stream, const Rope& rope) {
   const int nqb = (int)((n_q + 63) / 64);
   const int n_logical = nqb * heads;
   const int n_wg = (n_logical + 7) / 8 * 8;
-#define HF_SWA_BF16(SHORT)                                                                   \
-  sparse_swa_bf16<D, SHORT><<<n_wg, 128, 0, stream>>>(                                       \
+#define HF_SWA_BF16(SHORT, ROPE)                                                             \
+  sparse_swa_bf16<D, SHORT, ROPE><<<n_wg, 128, 0, stream>>>(                                 \
       static_cast<const bf16_t*>(q), n_q, q_hs, static_cast<const bf16_t*>(k),                \
       static_cast<const bf16_t*>(v), n_kv, kv_hs, sel, top_k, nqb, n_logical, s_split, z, eps,  \
       scale,                                                                                  \
-      static_cast<bf16_t*>(out), out_hs)
-  if (n_kv < 64) HF_SWA_BF16(true); else HF_SWA_BF16(false);
+      static_cast<bf16_t*>(out), out_hs, rope)
+  if (rope.cs) {
+    if (n_kv < 64) HF_SWA_BF16(true, true); else HF_SWA_BF16(false, true);
+  } else {
+    if (n_kv < 64) HF_SWA_BF16(true, false); else HF_SWA_BF16(false, false);
+  }
 #undef HF_SWA_BF16
   return hipGetLastError();
 }
@@ -822,14 +883,18 @@ template <typename T, int D, int BLK, int QW>
 hipError_t launch(const void* q, int64_t n_q, int64_t q_hs, const void* k, const void* v,
                   int64_t n_kv, int64_t kv_hs, const int32_t* sel, int top_k, int heads,
                   const float* S, const float* z, float eps, float scale, void* out,
-                  int64_t out_hs, hipStream_t stream) {
+                  int64_t out_hs, hipStream_t stream, const Rope& rope) {
   using Cf = SwaCfg<T, D, BLK, QW>;
   const int nqb = (int)((n_q + BLK - 1) / BLK);
   const int n_logical = nqb * heads;
   const int n_wg = (n_logical + 7) / 8 * 8;
-  sparse_swa<T, D, BLK, QW><<<n_wg, Cf::NT, 0, stream>>>(
-      static_cast<const T*>(q), n_q, q_hs, static_cast<const T*>(k), static_cast<const T*>(v),
-      n_kv, kv_hs, sel, top_k, nqb, n_logical, S, z, eps, scale, static_cast<T*>(out), out_hs);
+#define HF_SWA_GEN(ROPE)                                                                      \
+  sparse_swa<T, D, BLK, QW, ROPE><<<n_wg, Cf::NT, 0, stream>>>(                               \
+      static_cast<const T*>(q), n_q, q_hs, static_cast<const T*>(k), static_cast<const T*>(v), \
+      n_kv, kv_hs, sel, top_k, nqb, n_logical, S, z, eps, scale, static_cast<T*>(out), out_hs, \
+      rope)
+  if (rope.cs) HF_SWA_GEN(true); else HF_SWA_GEN(false);
+#undef HF_SWA_GEN
   return hipGetLastError();
 }
 
@@ -839,17 +904,17 @@ hipError_t launch_sparse_swa(int dtype, int heads, int d, int block, const void*
                              int64_t q_hs, const void* k, const void* v, int64_t n_kv,
                              int64_t kv_hs, const int32_t* sel, int top_k, const float* S,
                              const uint16_t* s_split, const float* z, float eps, float scale,
-                             void* out, int64_t out_hs, hipStream_t stream) {
+                             void* out, int64_t out_hs, hipStream_t stream, const Rope& rope) {
 #define HF_SWA(T, D, BLK, QW)                                                                 \
   return launch<T, D, BLK, QW>(q, n_q, q_hs, k, v, n_kv, kv_hs, sel, top_k, heads, S, z, eps, \
-                               scale, out, out_hs, stream)
+                               scale, out, out_hs, stream, rope)
   if (dtype == 0) {
     if (block == 64 && d == 128)
       return launch_bf16<128>(q, n_q, q_hs, k, v, n_kv, kv_hs, sel, top_k, heads, s_split, z,
-                              eps, scale, out, out_hs, stream);
+                              eps, scale, out, out_hs, stream, rope);
     if (block == 64 && d == 64)
       return launch_bf16<64>(q, n_q, q_hs, k, v, n_kv, kv_hs, sel, top_k, heads, s_split, z,
-                             eps, scale, out, out_hs, stream);
+                             eps, scale, out, out_hs, stream, rope);
   } else {
     if (block == 16 && d == 64) HF_SWA(float, 64, 16, 16);
     if (block == 16 && d == 128) HF_SWA(float, 128, 16, 16);

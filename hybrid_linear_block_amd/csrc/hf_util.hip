@@ -1,4 +1,6 @@
 // hf_util.hip -- small device utilities of libhf.
+#include <math.h>
+
 #include "hf_device.h"
 #include "hf_launch.h"
 
@@ -32,7 +34,29 @@ __global__ void __launch_bounds__(256)
     dst[i] = src[i];
 }
 
+// Angle table of the relative temporal rotation: entry (p, i) = cos and sin of
+// p * base^(-i / half), computed in double precision and rounded once to fp32.
+__global__ void rope_table(float2* cs, int npos, int half, double ln_base) {
+  const int64_t n = (int64_t)npos * half;
+  for (int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; x < n;
+       x += (int64_t)gridDim.x * blockDim.x) {
+    const int pos = (int)(x / half), i = (int)(x % half);
+    const double ang = (double)pos * exp(-ln_base * (double)i / (double)half);
+    cs[x] = make_float2((float)cos(ang), (float)sin(ang));
+  }
+}
+
 }  // namespace
+
+hipError_t launch_rope_table(float2* cs, int npos, int half, double theta_base,
+                             hipStream_t stream) {
+  const int64_t n = (int64_t)npos * half;
+  if (n <= 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 1024) blocks = 1024;
+  rope_table<<<(unsigned)blocks, 256, 0, stream>>>(cs, npos, half, log(theta_base));
+  return hipGetLastError();
+}
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream) {
   if (bytes == 0) return hipSuccess;

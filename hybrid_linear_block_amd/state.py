@@ -90,6 +90,23 @@ class HybridAttentionState:
             raise ValueError(f"{name} must have {self.cfg.num_heads} heads")
         return _rows(t, name, self.cfg.head_dim)
 
+    def set_rope(self, rot_dims: int, theta_base: float = 10000.0, tokens_per_frame: int = 1560,
+                 cap: int = 8) -> None:
+        """Relative temporal rotation of the softmax path (hf_set_rope); rot_dims = 0 turns
+        it off. Allocates the rotation workspace (angle table and rotated keys)."""
+        if rot_dims == 0:
+            _check(B.hf_set_rope(self.handle, None, 0, 0, _stream(self.device)), "hf_set_rope")
+            self.rope_workspace = None
+            return
+        rope = B.hf_rope(rot_dims, theta_base, tokens_per_frame, cap)
+        nbytes = B.hf_rope_workspace_bytes(self.cfg, rope)
+        if nbytes == 0:
+            raise B.HfError(B.HF_ERR_INVALID_ARG, "hf_rope_workspace_bytes")
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        _check(B.hf_set_rope(self.handle, rope, ws.data_ptr(), nbytes, _stream(self.device)),
+               "hf_set_rope")
+        self.rope_workspace = ws
+
     def absorb_evicted(self, k_ev: torch.Tensor, v_ev: torch.Tensor,
                        ev_index: Optional[int] = None) -> None:
         """S += V^T phi(K), z += sum phi(K) over the evicted tokens (enqueued)."""

@@ -252,6 +252,43 @@ hf_status hf_block_scores(hf_state* st, const void* q, int64_t n_q, int64_t q_he
                           const void* k_win, int64_t n_kv, int64_t kv_head_stride,
                           float* scores_out, void* stream);
 
+/* ---- Relative temporal rotation (RoPE) -----------------------------------------
+ * [EN] 2.C "Stability Enhancements" (Relative RoPE Constraint); [ES] 2.C: the temporal
+ * rotary position indices are bounded, the same in training and inference, and
+ * positions are relative offsets. The pages give neither the rotated features, the
+ * frequencies nor the bound, so all three are parameters. Once set on a state, the
+ * softmax path of hf_attend_chunk, hf_absorb_and_attend and hf_block_scores works on
+ * rotated queries and keys: the first rot_dims features of each row turn in adjacent
+ * pairs (2i, 2i+1) by the angle p * theta_base^(-2i / rot_dims), where p is the row's
+ * position: its frame's offset from the window's first frame (frame = window row /
+ * tokens_per_frame), capped at cap; the chunk's queries are the window's last n_q
+ * rows. The linear state absorbs and reads unrotated features. The rotation is fused
+ * into the block pooling launch, which writes the window's rotated keys into the
+ * rotation workspace for the attention kernel; the attention kernel rotates the
+ * queries itself (to bf16 for bf16 states, rounding to nearest even). */
+typedef struct {
+  int32_t rot_dims;         /* rotated features: even, 0 <= rot_dims <= head_dim (0: none) */
+  float theta_base;         /* > 0 (10000 is the usual value) */
+  int64_t tokens_per_frame; /* >= 1 */
+  int32_t cap;              /* >= 0: the largest position index */
+} hf_rope;
+
+/* Bytes of the rotation workspace for this configuration and rotation (0 if either
+ * is invalid): the angle table, min(cap, ceil(max_n_kv / tokens_per_frame) - 1) + 1
+ * positions x rot_dims / 2 pairs x 8 bytes, and the rotated keys, H x max_n_kv x d
+ * elements of the state's type, each rounded up to 256 bytes. */
+size_t hf_rope_workspace_bytes(const hf_config* cfg, const hf_rope* rope);
+
+/* Turn the rotation on (rope != NULL and rope->rot_dims > 0) or off (rope == NULL or
+ * rot_dims == 0; workspace may then be NULL). workspace: caller-owned device memory of
+ * at least hf_rope_workspace_bytes bytes, 16-byte aligned, kept alive while the
+ * rotation is on. Enqueues the angle table's computation (double precision, rounded
+ * to fp32) on stream. While it is on: attend calls need n_kv a multiple of
+ * tokens_per_frame and n_q <= n_kv (HF_ERR_INVALID_ARG otherwise); the cached, managed
+ * window and backward calls return HF_ERR_UNSUPPORTED. */
+hf_status hf_set_rope(hf_state* st, const hf_rope* rope, void* workspace, size_t ws_bytes,
+                      void* stream);
+
 /* ---- Backward pass (fixed selection) ------------------------------------------
  * The method is trained through this path ([EN] 2.B-C, decoupled distillation; the
  * state is learnable, [EN] 2.A.1). With L = sum(dout * out) for the output of

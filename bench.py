@@ -85,6 +85,9 @@ def parse():
                         "hf_window_attend); each step writes the chunk's K and V into its slot")
     p.add_argument("--ring-windows", type=int, default=4,
                    help="ring length in windows for --managed-window (>= 2)")
+    p.add_argument("--ragged", action="store_true",
+                   help="head-aware ragged windows: per-head 9/6/4-frame windows flattened "
+                        "with boundary indices (hf_attend_ragged)")
     p.add_argument("--rope-cap", type=int, default=None,
                    help="turn on the relative temporal rotation (44 of 128 features, base "
                         "10000, 1560 tokens per frame) with this cap on the position index")
@@ -401,6 +404,115 @@ def backward_main(args, torch, hla, synth, wl, top_k):
     }), flush=True)
 
 
+class RaggedSet:
+    """One input set of the Wan-like layer with head-aware ragged windows (a pyramid of
+    9-, 6- and 4-frame windows, flattened with boundary indices) and its own state."""
+
+    def __init__(self, hla, torch, synth, seed):
+        wl = synth.WORKLOADS["ragged_heads_bf16"]
+        inp = synth.ragged_layer_inputs(seed)
+        dev = torch.device("cuda:0")
+        to = lambda b: torch.from_numpy(b.view("int16")).view(torch.bfloat16).to(dev)  # noqa
+        self.q, self.kf, self.vf = to(inp["q"]), to(inp["k_flat"]), to(inp["v_flat"])
+        self.kev, self.vev = to(inp["k_ev"]), to(inp["v_ev"])
+        self.off = [int(x) for x in inp["offsets"]]
+        self.H, self.n_q, self.d = self.q.shape
+        self.lens = [b - a for a, b in zip(self.off, self.off[1:])]
+        self.top_ks = [synth.top_k_count(wl.top_k_frac, -(-n // 64)) for n in self.lens]
+        self.n_ev = self.kev.shape[1]
+        self.out = torch.empty_like(self.q)
+        self.st = hla.HybridAttentionState(self.H, self.d, 64, torch.bfloat16, max_n_q=self.n_q,
+                                           max_n_kv=max(self.lens), max_n_ev=self.n_ev,
+                                           max_top_k=max(self.top_ks), device=dev)
+        self.inp = inp
+
+    def step(self):
+        self.st.absorb_evicted(self.kev, self.vev)
+        self.st.attend_ragged(self.q, self.kf, self.vf, self.off, self.top_ks, out=self.out)
+
+    def flops(self, sel):
+        """Algorithmic FLOPs of the step for this selection (numpy int math)."""
+        import numpy as np
+        H, n_q, d, B = self.H, self.n_q, self.d, 64
+        nqb = -(-n_q // B)
+        qrows = np.minimum(B, n_q - B * np.arange(nqb))
+        swa = 0
+        for h in range(H):
+            n = self.lens[h]
+            krows = np.minimum(B, n - B * np.arange(-(-n // B)))
+            swa += 4 * d * int((qrows[:, None] * krows[sel[h, :, :self.top_ks[h]]]).sum())
+        nkb = sum(-(-n // B) for n in self.lens)
+        return dict(absorb=2 * self.n_ev * d * d * H, score_select=2 * nqb * nkb * d,
+                    sparse_swa=swa + 2 * n_q * d * (d + 1) * H, sparse_swa_softmax_part=swa)
+
+
+def ragged_main(args, torch, hla, synth):
+    """--ragged: K timed steps of the ragged-window layer (absorb + hf_attend_ragged)."""
+    n_sets = max(1, args.sets)
+    sets = [RaggedSet(hla, torch, synth, args.seed + i) for i in range(n_sets)]
+    fl = []
+    for s in sets:
+        sel = torch.empty((s.H, -(-s.n_q // 64), max(s.top_ks)), dtype=torch.int32,
+                          device="cuda")
+        s.st.attend_ragged(s.q, s.kf, s.vf, s.off, s.top_ks, out=s.out, sel_out=sel)
+        torch.cuda.synchronize()
+        fl.append(s.flops(sel.cpu().numpy()))
+    t0 = time.perf_counter()
+    settled = 0
+    while (time.perf_counter() - t0) * 1e3 < args.settle_ms:
+        for _ in range(10):
+            sets[settled % n_sets].step()
+            settled += 1
+        torch.cuda.synchronize()
+    for k in range(args.warmup):
+        sets[k % n_sets].step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for k in range(args.steps):
+        sets[k % n_sets].step()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    for s in sets:
+        s.st.profile_start(args.steps + 2)
+    for k in range(args.steps):
+        sets[k % n_sets].step()
+    torch.cuda.synchronize()
+    tot = {}
+    for s in sets:
+        for name, (ms, n) in s.st.profile_stop().items():
+            a = tot.setdefault(name, [0.0, 0])
+            a[0] += ms
+            a[1] += n
+    kern_us = {k: v[0] / v[1] * 1e3 for k, v in tot.items() if v[1]}
+    log(f"[bench] ragged {ms_step:.4f} ms/step; per-kernel us: {kern_us}")
+    mean = {k: statistics.mean(f[k] for f in fl) for k in fl[0]}
+    step_flop = mean["absorb"] + mean["score_select"] + mean["sparse_swa"]
+    peak = PEAK_MFMA_TFLOPS["bf16"]
+    achieved = mean["sparse_swa"] / (kern_us["sparse_swa"] * 1e-6) / 1e12
+    s0 = sets[0]
+    print(json.dumps({
+        "metric": METRIC, "value": round(step_flop / (ms_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "settle_steps": settled, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1)/sqrt(d) bf16 Q/K/V; no weights or dataset)",
+        "config": {"workload": f"ragged_heads_bf16: {s0.H} heads, d={s0.d}, chunk {s0.n_q} "
+                               f"query tokens, per-head windows {s0.lens} tokens (flattened, "
+                               f"boundary indices), top-K {s0.top_ks}, {s0.n_ev} evicted "
+                               "tokens absorbed per step",
+                   "input_sets": n_sets,
+                   "issue": "hf_absorb_evicted, then hf_attend_ragged, one stream"},
+        "kernels": {k: dict(avg_us=round(v, 2)) for k, v in kern_us.items()},
+        "roofline": dict(bound="mfma", achieved=round(achieved, 2), peak=peak, unit="TFLOP/s",
+                         frac=round(achieved / peak, 4), traffic=None, kernel="sparse_swa",
+                         flop_per_launch=int(mean["sparse_swa"]),
+                         avg_launch_us=round(kern_us["sparse_swa"], 2)),
+        "cpu_baseline": None,
+    }), flush=True)
+
+
 def cpu_baseline(layer: LayerSet, reps: int):
     """The float64 oracle on the host cores: the same layer step, median of `reps`."""
     import numpy as np
@@ -459,6 +571,9 @@ def main():
     top_k = synth.top_k_count(wl.top_k_frac, -(-wl.window_tokens // wl.block))
     n_sets = wl.layers if args.workload == "full_depth_bf16" else max(1, args.sets)
     t0 = time.time()
+    if args.ragged:
+        ragged_main(args, torch, hla, synth)
+        return
     if args.backward:
         if args.workload != "wan_layer_bf16":
             sys.exit("--backward runs the wan_layer_bf16 shapes")

@@ -11,6 +11,6 @@ from .binding import (  # noqa: F401
     hf_absorb_and_attend, hf_attend_chunk_cached, hf_absorb_and_attend_cached, hf_key_cache_reset,
     hf_window_attach, hf_window_begin_chunk, hf_window_attend, hf_window_range,
     hf_block_scores, hf_backward_workspace_bytes, hf_attend_backward, hf_absorb_backward,
-    hf_rope, hf_rope_workspace_bytes, hf_set_rope, hf_attend_chunk_noalloc, hf_profile_start, hf_profile_stop, hf_next_ev_index,
+    hf_attend_ragged, hf_rope, hf_rope_workspace_bytes, hf_set_rope, hf_attend_chunk_noalloc, hf_profile_start, hf_profile_stop, hf_next_ev_index,
     hf_state_destroy, hf_status_string, library_path)
 from .state import HybridAttentionState, window_frames  # noqa: F401

@@ -85,6 +85,8 @@ def _load():
                                        P, c_int64, P, c_int64, P, P, c_int64, P, P, P, c_size_t,
                                        P]),
         "hf_absorb_backward": (c_int, [P, P, P, c_int64, c_int64, P, P, P, P, c_int64, P]),
+        "hf_attend_ragged": (c_int, [P, P, c_int64, c_int64, P, P, POINTER(c_int64),
+                                     POINTER(c_int32), P, c_int64, P, P]),
         "hf_rope_workspace_bytes": (c_size_t, [POINTER(hf_config), POINTER(hf_rope)]),
         "hf_set_rope": (c_int, [P, POINTER(hf_rope), P, c_size_t, P]),
         "hf_attend_chunk_noalloc": (c_int, [POINTER(hf_config), P, P, P, c_int64, c_int64, P, P,
@@ -109,7 +111,8 @@ EXPORTED = ("hf_workspace_bytes", "hf_state_init", "hf_absorb_evicted", "hf_atte
             "hf_key_cache_reset", "hf_window_attach", "hf_window_begin_chunk",
             "hf_window_attend", "hf_window_range", "hf_block_scores",
             "hf_backward_workspace_bytes", "hf_attend_backward", "hf_absorb_backward",
-            "hf_rope_workspace_bytes", "hf_set_rope", "hf_attend_chunk_noalloc",
+            "hf_attend_ragged", "hf_rope_workspace_bytes", "hf_set_rope",
+            "hf_attend_chunk_noalloc",
             "hf_profile_start",
             "hf_profile_stop", "hf_next_ev_index", "hf_state_destroy", "hf_status_string")
 HF_KERNEL_NAMES = ("absorb", "block_pool", "score_select", "sparse_swa", "bwd_index", "bwd_dq",
@@ -236,6 +239,16 @@ def hf_absorb_backward(state: int, k_ev: int, v_ev: int, n_ev: int, ev_head_stri
                        dz: int, dk_ev: int, dv_ev: int, dev_head_stride: int, stream: int) -> int:
     return _lib.hf_absorb_backward(state, k_ev, v_ev, n_ev, ev_head_stride, dS, dz, dk_ev, dv_ev,
                                    dev_head_stride, stream)
+
+
+def hf_attend_ragged(state: int, q: int, n_q: int, q_head_stride: int, k_flat: int, v_flat: int,
+                     kv_offsets, top_k, out: int, out_head_stride: int, sel_out: int,
+                     stream: int) -> int:
+    """kv_offsets (num_heads + 1) and top_k (num_heads): sequences of ints (host)."""
+    off = (c_int64 * len(kv_offsets))(*[int(x) for x in kv_offsets])
+    tk = (c_int32 * len(top_k))(*[int(x) for x in top_k])
+    return _lib.hf_attend_ragged(state, q, n_q, q_head_stride, k_flat, v_flat, off, tk, out,
+                                 out_head_stride, sel_out, stream)
 
 
 def hf_rope_workspace_bytes(cfg: hf_config, rope: hf_rope) -> int:

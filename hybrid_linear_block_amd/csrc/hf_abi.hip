@@ -5,6 +5,7 @@
 // check and the kernel launches on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <climits>
 #include <cmath>
 #include <mutex>
 #include <new>
@@ -845,6 +846,66 @@ hf_status hf_absorb_backward(hf_state* st, const void* k_ev, const void* v_ev, i
       return hf::launch_absorb_backward(c.dtype, c.num_heads, c.head_dim, k_ev, v_ev, n_ev,
                                         ev_head_stride, dS, dz, dk_ev, dv_ev, dev_head_stride, s);
     });
+  });
+}
+
+hf_status hf_attend_ragged(hf_state* st, const void* q, int64_t n_q, int64_t q_head_stride,
+                           const void* k_flat, const void* v_flat, const int64_t* kv_offsets,
+                           const int32_t* top_k, void* out, int64_t out_head_stride,
+                           int32_t* sel_out, void* stream) {
+  if (!st) return HF_ERR_INVALID_ARG;
+  const hf_config& c = st->cfg;
+  if (c.num_heads > hf::kRaggedMaxHeads) return HF_ERR_UNSUPPORTED;
+  if (st->rope.cs) return HF_ERR_UNSUPPORTED;  // positions per head are not modelled
+  if (!kv_offsets || !top_k || n_q < 0 || n_q > c.max_n_q) return HF_ERR_INVALID_ARG;
+  hf::Ragged rg;
+  rg.on = 1;
+  rg.off[0] = 0;
+  rg.kb0[0] = 0;
+  int64_t n_min = INT64_MAX;
+  int32_t k_max = 0, nkb_max = 0;
+  for (int h = 0; h < c.num_heads; ++h) {
+    const int64_t a = kv_offsets[h], b = kv_offsets[h + 1];
+    if (a < 0 || b <= a || b - a > c.max_n_kv || b > INT32_MAX) return HF_ERR_INVALID_ARG;
+    const int32_t nkb = (int32_t)ceil_div(b - a, c.block_size);
+    if (top_k[h] < 1 || top_k[h] > nkb || top_k[h] > c.max_top_k) return HF_ERR_INVALID_ARG;
+    rg.off[h] = (int32_t)a;
+    rg.off[h + 1] = (int32_t)b;
+    rg.top_k[h] = top_k[h];
+    rg.kb0[h + 1] = rg.kb0[h] + nkb;
+    if (b - a < n_min) n_min = b - a;
+    if (top_k[h] > k_max) k_max = top_k[h];
+    if (nkb > nkb_max) nkb_max = nkb;
+  }
+  if (!k_flat || !v_flat || !aligned16(k_flat) || !aligned16(v_flat)) return HF_ERR_INVALID_ARG;
+  hf_status e = n_q > 0 ? check_tensor(q, n_q, q_head_stride, c) : HF_OK;
+  if (e == HF_OK && n_q > 0) e = check_tensor(out, n_q, out_head_stride, c);
+  if (e != HF_OK) return e;
+  if (sel_out && (reinterpret_cast<uintptr_t>(sel_out) & 3u)) return HF_ERR_INVALID_ARG;
+  if (n_q == 0) return HF_OK;
+  const int nqb = (int)ceil_div(n_q, c.block_size);
+  int32_t* sel = sel_out ? sel_out : st->sel;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return on_device(st->device, [&]() {
+    hipError_t r = timed(st, HF_KERNEL_BLOCK_POOL, s, [&]() {
+      return hf::launch_block_pool(c.dtype, c.num_heads, c.head_dim, c.block_size, q, n_q,
+                                   q_head_stride, k_flat, n_min, 0, st->pooled_q, st->pooled_k,
+                                   st->nqb_cap, st->nkb_cap, s, hf::KeyCache(), hf::Rope(), rg);
+    });
+    if (r == hipSuccess)
+      r = timed(st, HF_KERNEL_SCORE_SELECT, s, [&]() {
+        return hf::launch_score_select(c.num_heads, c.head_dim, nqb, nkb_max, st->nqb_cap,
+                                       st->nkb_cap, st->pooled_q, st->pooled_k, st->scale, k_max,
+                                       sel, nullptr, s, rg);
+      });
+    if (r == hipSuccess)
+      r = timed(st, HF_KERNEL_SPARSE_SWA, s, [&]() {
+        return hf::launch_sparse_swa(c.dtype, c.num_heads, c.head_dim, c.block_size, q, n_q,
+                                     q_head_stride, k_flat, v_flat, n_min, 0, sel, k_max, st->S,
+                                     st->s_split, st->z, c.eps, st->scale, out, out_head_stride,
+                                     s, hf::Rope(), rg);
+      });
+    return r;
   });
 }
 

@@ -61,15 +61,27 @@ struct Rope {
   void* k_out = nullptr;
   int64_t k_out_hs = 0;
 };
+// Head-aware ragged windows: head h's window is rows off[h] .. off[h + 1] of K and V
+// flattened one head after the other (row stride d, no head stride), with its own top_k;
+// its key blocks are kb0[h] .. kb0[h + 1] in the order of all heads' blocks. on == false:
+// every head has the call's one window shape.
+constexpr int kRaggedMaxHeads = 64;
+struct Ragged {
+  int32_t on = 0;
+  int32_t off[kRaggedMaxHeads + 1];
+  int32_t top_k[kRaggedMaxHeads];
+  int32_t kb0[kRaggedMaxHeads + 1];
+};
 // cs[p * half + i] = (cos, sin) of p * base^(-2i / (2 half)) for p < npos (computed in
 // double precision).
 hipError_t launch_rope_table(float2* cs, int npos, int half, double theta_base,
                              hipStream_t stream);
+// With rg.on, the key part pools every head's own window (n_kv is then the longest).
 hipError_t launch_block_pool(int dtype, int heads, int d, int block, const void* q, int64_t n_q,
                              int64_t q_hs, const void* k, int64_t n_kv, int64_t kv_hs,
                              float* pooled_q, float* pooled_k, int nqb_cap, int nkb_cap,
                              hipStream_t stream, const KeyCache& kc = KeyCache(),
-                             const Rope& rope = Rope());
+                             const Rope& rope = Rope(), const Ragged& rg = Ragged());
 // The partial-state pass of an absorb of n_ev evicted tokens (as in launch_absorb)
 // and launch_block_pool in one launch: the two read and write different buffers
 // and are both bound by memory. The absorb is complete once
@@ -80,9 +92,12 @@ hipError_t launch_absorb_and_pool(int dtype, int heads, int d, int block, const 
                                   int64_t n_kv, int64_t kv_hs, float* pooled_q, float* pooled_k,
                                   int nqb_cap, int nkb_cap, hipStream_t stream,
                                   const KeyCache& kc = KeyCache(), const Rope& rope = Rope());
+// With rg.on, head h selects rg.top_k[h] of its own rg.kb0[h + 1] - rg.kb0[h] key blocks
+// (nkb is then the largest count and top_k the row stride of sel).
 hipError_t launch_score_select(int heads, int d, int nqb, int nkb, int nqb_cap, int nkb_cap,
                                const float* pooled_q, const float* pooled_k, float scale,
-                               int top_k, int32_t* sel, float* scores_out, hipStream_t stream);
+                               int top_k, int32_t* sel, float* scores_out, hipStream_t stream,
+                               const Ragged& rg = Ragged());
 // launch_score_select and, in the same launch, the reduce of the absorb whose
 // partial states launch_absorb_and_pool has written (dtype and n_ev as given there).
 hipError_t launch_select_and_reduce(int dtype, int heads, int d, int nqb, int nkb, int nqb_cap,
@@ -100,7 +115,7 @@ hipError_t launch_sparse_swa(int dtype, int heads, int d, int block, const void*
                              int64_t kv_hs, const int32_t* sel, int top_k, const float* S,
                              const uint16_t* s_split, const float* z, float eps, float scale,
                              void* out, int64_t out_hs, hipStream_t stream,
-                             const Rope& rope = Rope());
+                             const Rope& rope = Rope(), const Ragged& rg = Ragged());
 
 // ---- backward (fixed selection) ---------------------------------------------------
 struct BwdArgs {

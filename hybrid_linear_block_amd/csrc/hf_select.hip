@@ -72,19 +72,40 @@ __device__ __forceinline__ void pool_wave(
     int wid, const T* __restrict__ q, int64_t n_q, int64_t q_hs, const T* __restrict__ k,
     int64_t n_kv, int64_t kv_hs, int block, int nqb, int nkb, int heads,
     float* __restrict__ pooled_q, float* __restrict__ pooled_k, int nqb_cap, int nkb_cap,
-    const KeyCache& kc, const Rope& rope) {
+    const KeyCache& kc, const Rope& rope, const Ragged& rag) {
   constexpr int VEC = 16 / sizeof(T);  // elements per 16-byte chunk
   constexpr int CPR = D / VEC;         // chunks per row
   constexpr int RPI = 64 / CPR;        // lane groups (rows per wave-wide load)
   constexpr int GPL = 8 / RPI;         // 8-row groups per lane (blocks have at most 64 rows)
   static_assert(RPI >= 1 && RPI <= 8 && 8 % RPI == 0, "lane groups per 8-row group");
   const int lane = threadIdx.x & 63;
-  if (wid >= heads * (nqb + nkb)) return;
-  const int h = wid / (nqb + nkb), b = wid % (nqb + nkb);
-  const bool is_q = b < nqb;
-  const int blk = is_q ? b : b - nqb;
-  const int64_t n = is_q ? n_q : n_kv;
-  const T* base = is_q ? q + (size_t)h * q_hs : k + (size_t)h * kv_hs;
+  int h, blk;
+  bool is_q;
+  int64_t n;
+  const T* base;
+  if (rag.on) {  // query blocks of every head, then each head's own key blocks
+    if (wid >= heads * nqb + rag.kb0[heads]) return;
+    is_q = wid < heads * nqb;
+    if (is_q) {
+      h = wid / nqb;
+      blk = wid % nqb;
+    } else {
+      const int kw = wid - heads * nqb;
+      h = 0;
+      while (rag.kb0[h + 1] <= kw) ++h;
+      blk = kw - rag.kb0[h];
+    }
+    n = is_q ? n_q : (int64_t)(rag.off[h + 1] - rag.off[h]);
+    base = is_q ? q + (size_t)h * q_hs : k + (size_t)rag.off[h] * D;
+  } else {
+    if (wid >= heads * (nqb + nkb)) return;
+    h = wid / (nqb + nkb);
+    const int b = wid % (nqb + nkb);
+    is_q = b < nqb;
+    blk = is_q ? b : b - nqb;
+    n = is_q ? n_q : n_kv;
+    base = is_q ? q + (size_t)h * q_hs : k + (size_t)h * kv_hs;
+  }
   const int64_t r0 = (int64_t)blk * block;
   const int64_t r1 = r0 + block < n ? r0 + block : n;
   const int cc = lane % CPR, rg = lane / CPR;
@@ -175,9 +196,10 @@ template <typename T, int D>
 __global__ __launch_bounds__(POOL_THREADS) void block_pool(
     const T* __restrict__ q, int64_t n_q, int64_t q_hs, const T* __restrict__ k, int64_t n_kv,
     int64_t kv_hs, int block, int nqb, int nkb, int heads, float* __restrict__ pooled_q,
-    float* __restrict__ pooled_k, int nqb_cap, int nkb_cap, KeyCache kc, Rope rope) {
+    float* __restrict__ pooled_k, int nqb_cap, int nkb_cap, KeyCache kc, Rope rope, Ragged rg) {
   pool_wave<T, D>(blockIdx.x * (POOL_THREADS / 64) + (threadIdx.x >> 6), q, n_q, q_hs, k, n_kv,
-                  kv_hs, block, nqb, nkb, heads, pooled_q, pooled_k, nqb_cap, nkb_cap, kc, rope);
+                  kv_hs, block, nqb, nkb, heads, pooled_q, pooled_k, nqb_cap, nkb_cap, kc, rope,
+                  rg);
 }
 
 // The absorb's partial states and the block pooling in one launch: workgroups
@@ -192,7 +214,7 @@ __global__ __launch_bounds__((absorb::threads<T, D>())) void absorb_and_pool(
     int n_split, float* __restrict__ partials, int n_abs, const T* __restrict__ q, int64_t n_q,
     int64_t q_hs, const T* __restrict__ k, int64_t n_kv, int64_t kv_hs, int block, int nqb,
     int nkb, int heads, float* __restrict__ pooled_q, float* __restrict__ pooled_k, int nqb_cap,
-    int nkb_cap, KeyCache kc, Rope rope) {
+    int nkb_cap, KeyCache kc, Rope rope, Ragged rg) {
   if ((int)blockIdx.x < n_abs) {
     absorb::item<T, D>(blockIdx.x, n_split, kev, vev, n_ev, ev_hs, tps, partials);
   } else {
@@ -201,11 +223,11 @@ __global__ __launch_bounds__((absorb::threads<T, D>())) void absorb_and_pool(
     // pooling streams from the start instead of waiting for free slots.
     constexpr int WPG = absorb::threads<T, D>() / 64;  // pooling waves per workgroup
     const int n_waves = ((int)gridDim.x - n_abs) * WPG;
-    const int total = heads * (nqb + nkb);
+    const int total = rg.on ? heads * nqb + rg.kb0[heads] : heads * (nqb + nkb);
     for (int wid = ((int)blockIdx.x - n_abs) * WPG + (int)(threadIdx.x >> 6); wid < total;
          wid += n_waves)
       pool_wave<T, D>(wid, q, n_q, q_hs, k, n_kv, kv_hs, block, nqb, nkb, heads, pooled_q,
-                      pooled_k, nqb_cap, nkb_cap, kc, rope);
+                      pooled_k, nqb_cap, nkb_cap, kc, rope, rg);
   }
 }
 
@@ -231,7 +253,14 @@ template <int D, int NE>
 __device__ __forceinline__ void select_group(
     int qg, int h, const float* __restrict__ pooled_q, const float* __restrict__ pooled_k,
     int nqb, int nkb, int nqb_cap, int nkb_cap, float scale, int top_k,
-    int32_t* __restrict__ sel, float* __restrict__ scores_out) {
+    int32_t* __restrict__ sel, float* __restrict__ scores_out, const Ragged& rg) {
+  // Ragged windows: this head's own block count and top_k; rows of sel keep the stride
+  // top_k (the largest of the heads') passed in.
+  const int sel_stride = top_k;
+  if (rg.on) {
+    nkb = rg.kb0[h + 1] - rg.kb0[h];
+    top_k = rg.top_k[h];
+  }
   __shared__ uint32_t key[SEL_QB][kMaxKeyBlocks];
   __shared__ float4 qs[SEL_QB][D / 4];
   const int i0 = qg * SEL_QB, tid = threadIdx.x;
@@ -309,7 +338,7 @@ __device__ __forceinline__ void select_group(
   }
   const int need = top_k - count_at_least(T + 1u);  // keys equal to T to keep
   const uint64_t lt = (1ull << lane) - 1ull;
-  int32_t* out = sel + ((size_t)h * nqb + i0 + r) * top_k;
+  int32_t* out = sel + ((size_t)h * nqb + i0 + r) * sel_stride;
   int pos = 0, eq_before = 0;
 #pragma unroll
   for (int e = 0; e < NE; ++e) {
@@ -327,9 +356,9 @@ template <int D, int NE>
 __global__ __launch_bounds__(SEL_THREADS) void score_select(
     const float* __restrict__ pooled_q, const float* __restrict__ pooled_k, int nqb, int nkb,
     int nqb_cap, int nkb_cap, float scale, int top_k, int32_t* __restrict__ sel,
-    float* __restrict__ scores_out) {
+    float* __restrict__ scores_out, Ragged rg) {
   select_group<D, NE>(blockIdx.x, blockIdx.y, pooled_q, pooled_k, nqb, nkb, nqb_cap, nkb_cap,
-                      scale, top_k, sel, scores_out);
+                      scale, top_k, sel, scores_out, rg);
 }
 
 // The selection and the absorb's reduce in one launch: workgroups below n_sel
@@ -348,7 +377,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_and_reduce(
     float* __restrict__ z, uint16_t* __restrict__ s_split) {
   if ((int)blockIdx.x < n_sel) {
     select_group<D, NE>((int)blockIdx.x % n_qg, (int)blockIdx.x / n_qg, pooled_q, pooled_k, nqb,
-                        nkb, nqb_cap, nkb_cap, scale, top_k, sel, nullptr);
+                        nkb, nqb_cap, nkb_cap, scale, top_k, sel, nullptr, Ragged());
   } else {
     const int r = (int)blockIdx.x - n_sel;
     const int grp = (r % red_wgs<D>()) * RED_PER_WG + (int)threadIdx.x / RED_THREADS;
@@ -363,15 +392,16 @@ __global__ __launch_bounds__(SEL_THREADS) void select_and_reduce(
 hipError_t launch_block_pool(int dtype, int heads, int d, int block, const void* q, int64_t n_q,
                              int64_t q_hs, const void* k, int64_t n_kv, int64_t kv_hs,
                              float* pooled_q, float* pooled_k, int nqb_cap, int nkb_cap,
-                             hipStream_t stream, const KeyCache& kc, const Rope& rope) {
+                             hipStream_t stream, const KeyCache& kc, const Rope& rope,
+                             const Ragged& rg) {
   const int nqb = (int)((n_q + block - 1) / block);
   const int nkb = (int)((n_kv + block - 1) / block);
-  const int waves = heads * (nqb + nkb);
+  const int waves = rg.on ? heads * nqb + rg.kb0[heads] : heads * (nqb + nkb);
   const int grid = (waves + POOL_THREADS / 64 - 1) / (POOL_THREADS / 64);
 #define HF_POOL(T, D)                                                                        \
   block_pool<T, D><<<grid, POOL_THREADS, 0, stream>>>(                                       \
       static_cast<const T*>(q), n_q, q_hs, static_cast<const T*>(k), n_kv, kv_hs, block, nqb, \
-      nkb, heads, pooled_q, pooled_k, nqb_cap, nkb_cap, kc, rope)
+      nkb, heads, pooled_q, pooled_k, nqb_cap, nkb_cap, kc, rope, rg)
   if (dtype == 0) {
     if (d == 128) HF_POOL(bf16_t, 128); else HF_POOL(bf16_t, 64);
   } else {
@@ -422,7 +452,7 @@ hipError_t launch_absorb_and_pool(int dtype, int heads, int d, int block, const 
         static_cast<const T*>(k_ev), static_cast<const T*>(v_ev), n_ev, ev_hs,                 \
         p.tokens_per_split, p.n_split, partials, n_abs, static_cast<const T*>(q), n_q, q_hs,   \
         static_cast<const T*>(k), n_kv, kv_hs, block, nqb, nkb, heads, pooled_q, pooled_k,     \
-        nqb_cap, nkb_cap, kc, rope);                                                           \
+        nqb_cap, nkb_cap, kc, rope, Ragged());                                                 \
   }
   if (dtype == 0) {
     if (d == 128) HF_ABSPOOL(bf16_t, 128) else HF_ABSPOOL(bf16_t, 64)
@@ -435,11 +465,13 @@ hipError_t launch_absorb_and_pool(int dtype, int heads, int d, int block, const 
 
 hipError_t launch_score_select(int heads, int d, int nqb, int nkb, int nqb_cap, int nkb_cap,
                                const float* pooled_q, const float* pooled_k, float scale,
-                               int top_k, int32_t* sel, float* scores_out, hipStream_t stream) {
+                               int top_k, int32_t* sel, float* scores_out, hipStream_t stream,
+                               const Ragged& rg) {
   dim3 grid((nqb + SEL_QB - 1) / SEL_QB, heads);
 #define HF_SEL(D, NE)                                                                      \
   score_select<D, NE><<<grid, SEL_THREADS, 0, stream>>>(pooled_q, pooled_k, nqb, nkb, nqb_cap, \
-                                                         nkb_cap, scale, top_k, sel, scores_out)
+                                                         nkb_cap, scale, top_k, sel, scores_out, \
+                                                         rg)
   // NE = 64-key chunks held per lane in the selection (the smallest that covers nkb).
   if (d == 128) {
     if (nkb <= 256) HF_SEL(128, 4); else if (nkb <= 512) HF_SEL(128, 8); else HF_SEL(128, 32);

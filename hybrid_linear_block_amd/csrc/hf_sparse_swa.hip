@@ -92,7 +92,7 @@ __global__ __launch_bounds__((BLK / QW) * 64) void sparse_swa(
     const T* __restrict__ vg, int64_t n_kv, int64_t kv_hs, const int32_t* __restrict__ sel,
     int top_k, int nqb, int n_logical, const float* __restrict__ S,
     const float* __restrict__ z, float eps, float scale, T* __restrict__ out, int64_t out_hs,
-    Rope rope) {
+    Rope rope, Ragged rg) {
   using C = SwaCfg<T, D, BLK, QW>;
   using M = Mfma<T>;
   using op_t = typename M::op_t;
@@ -111,6 +111,12 @@ __global__ __launch_bounds__((BLK / QW) * 64) void sparse_swa(
                      : kg + (size_t)h * kv_hs;
   const T* vh = vg + (size_t)h * kv_hs;
   const int32_t* my_sel = sel + ((size_t)h * nqb + i) * top_k;
+  if (rg.on) {  // this head's own window and top_k (sel rows keep the stride top_k)
+    kh = kg + (size_t)rg.off[h] * D;
+    vh = vg + (size_t)rg.off[h] * D;
+    n_kv = rg.off[h + 1] - rg.off[h];
+    top_k = rg.top_k[h];
+  }
   const int64_t qrow0 = (int64_t)i * BLK + w * QW;
 
   // ---- Q operands (B of S^T = K Q^T): lane holds Q[16n + c][s*KSTEP + g*KP ..] ----
@@ -434,7 +440,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void s
     const bf16_t* __restrict__ vg, int64_t n_kv, int64_t kv_hs, const int32_t* __restrict__ sel,
     int top_k, int nqb, int n_logical, const uint16_t* __restrict__ s_split,
     const float* __restrict__ z, float eps, float scale, bf16_t* __restrict__ out,
-    int64_t out_hs, Rope rope) {
+    int64_t out_hs, Rope rope, Ragged rg) {
   constexpr int BLK = 64, NW = 2, NQT = 2, NMT = 4, NET = D / 16, NKS = D / 32;
   constexpr int CPR = D / 8;            // 16-byte chunks per K/V row
   constexpr int TCH = BLK * CPR;        // chunks per tile
@@ -455,6 +461,12 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void s
                           : kg + (size_t)h * kv_hs;
   const bf16_t* vh = vg + (size_t)h * kv_hs;
   const int32_t* my_sel = sel + ((size_t)h * nqb + i) * top_k;
+  if (rg.on) {  // this head's own window and top_k (sel rows keep the stride top_k)
+    kh = kg + (size_t)rg.off[h] * D;
+    vh = vg + (size_t)rg.off[h] * D;
+    n_kv = rg.off[h + 1] - rg.off[h];
+    top_k = rg.top_k[h];
+  }
   const int64_t qrow0 = (int64_t)i * BLK + w * 32;
 
   // Load u of this wave fills LDS chunks (u*NW + w)*64 + lane of a tile with global
@@ -477,7 +489,9 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void s
   // The ragged last block of the window is loaded as the window's last BLK rows
   // (all in bounds; its valid keys are then the tile's last rows and the rows
   // before them are masked), so every load of every tile takes the same address
-  // path. A window shorter than one block (SHORT) repeats its last row instead.
+  // path. The short form (a window shorter than one block, or ragged windows where some
+  // head's is) keeps every tile at its block's first row and repeats the window's last
+  // row past its end instead.
   auto tile_row0 = [&](int jb) {
     const int64_t r0 = (int64_t)jb * BLK;
     return (!SHORT && r0 + BLK > n_kv) ? n_kv - BLK : r0;
@@ -490,9 +504,9 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void s
       const uint32_t off = lpat[u % NPAT];
       if constexpr (!SHORT) {
         lds_dma16(tb + u * RPU * D, off, base + u * NW * 64 * 16);
-      } else {  // rows of the group past the window read the last row
+      } else {  // rows of the tile past the window read the window's last row
         const uint32_t row_bytes = D * 2, row = u * RPU + off / row_bytes;
-        const uint32_t last = (uint32_t)n_kv - 1;
+        const uint32_t last = (uint32_t)(n_kv - 1 - tile_row0(jb));  // tile-relative
         lds_dma16(tb, (row <= last ? row : last) * row_bytes + off % row_bytes,
                   base + u * NW * 64 * 16);
       }
@@ -860,7 +874,8 @@ template <int D>
 hipError_t launch_bf16(const void* q, int64_t n_q, int64_t q_hs, const void* k, const void* v,
                        int64_t n_kv, int64_t kv_hs, const int32_t* sel, int top_k, int heads,
                        const uint16_t* s_split, const float* z, float eps, float scale,
-                       void* out, int64_t out_hs, hipStream_t stream, const Rope& rope) {
+                       void* out, int64_t out_hs, hipStream_t stream, const Rope& rope,
+                       const Ragged& rg) {
   const int nqb = (int)((n_q + 63) / 64);
   const int n_logical = nqb * heads;
   const int n_wg = (n_logical + 7) / 8 * 8;
@@ -869,7 +884,9 @@ hipError_t launch_bf16(const void* q, int64_t n_q, int64_t q_hs, const void* k, 
       static_cast<const bf16_t*>(q), n_q, q_hs, static_cast<const bf16_t*>(k),                \
       static_cast<const bf16_t*>(v), n_kv, kv_hs, sel, top_k, nqb, n_logical, s_split, z, eps,  \
       scale,                                                                                  \
-      static_cast<bf16_t*>(out), out_hs, rope)
+      static_cast<bf16_t*>(out), out_hs, rope, rg)
+  // A window shorter than one block takes the short form (for ragged windows: the
+  // shortest head's window, n_kv the call passes).
   if (rope.cs) {
     if (n_kv < 64) HF_SWA_BF16(true, true); else HF_SWA_BF16(false, true);
   } else {
@@ -883,7 +900,7 @@ template <typename T, int D, int BLK, int QW>
 hipError_t launch(const void* q, int64_t n_q, int64_t q_hs, const void* k, const void* v,
                   int64_t n_kv, int64_t kv_hs, const int32_t* sel, int top_k, int heads,
                   const float* S, const float* z, float eps, float scale, void* out,
-                  int64_t out_hs, hipStream_t stream, const Rope& rope) {
+                  int64_t out_hs, hipStream_t stream, const Rope& rope, const Ragged& rg) {
   using Cf = SwaCfg<T, D, BLK, QW>;
   const int nqb = (int)((n_q + BLK - 1) / BLK);
   const int n_logical = nqb * heads;
@@ -892,7 +909,7 @@ hipError_t launch(const void* q, int64_t n_q, int64_t q_hs, const void* k, const
   sparse_swa<T, D, BLK, QW, ROPE><<<n_wg, Cf::NT, 0, stream>>>(                               \
       static_cast<const T*>(q), n_q, q_hs, static_cast<const T*>(k), static_cast<const T*>(v), \
       n_kv, kv_hs, sel, top_k, nqb, n_logical, S, z, eps, scale, static_cast<T*>(out), out_hs, \
-      rope)
+      rope, rg)
   if (rope.cs) HF_SWA_GEN(true); else HF_SWA_GEN(false);
 #undef HF_SWA_GEN
   return hipGetLastError();
@@ -904,17 +921,18 @@ hipError_t launch_sparse_swa(int dtype, int heads, int d, int block, const void*
                              int64_t q_hs, const void* k, const void* v, int64_t n_kv,
                              int64_t kv_hs, const int32_t* sel, int top_k, const float* S,
                              const uint16_t* s_split, const float* z, float eps, float scale,
-                             void* out, int64_t out_hs, hipStream_t stream, const Rope& rope) {
+                             void* out, int64_t out_hs, hipStream_t stream, const Rope& rope,
+                             const Ragged& rg) {
 #define HF_SWA(T, D, BLK, QW)                                                                 \
   return launch<T, D, BLK, QW>(q, n_q, q_hs, k, v, n_kv, kv_hs, sel, top_k, heads, S, z, eps, \
-                               scale, out, out_hs, stream, rope)
+                               scale, out, out_hs, stream, rope, rg)
   if (dtype == 0) {
     if (block == 64 && d == 128)
       return launch_bf16<128>(q, n_q, q_hs, k, v, n_kv, kv_hs, sel, top_k, heads, s_split, z,
-                              eps, scale, out, out_hs, stream, rope);
+                              eps, scale, out, out_hs, stream, rope, rg);
     if (block == 64 && d == 64)
       return launch_bf16<64>(q, n_q, q_hs, k, v, n_kv, kv_hs, sel, top_k, heads, s_split, z,
-                             eps, scale, out, out_hs, stream, rope);
+                             eps, scale, out, out_hs, stream, rope, rg);
   } else {
     if (block == 16 && d == 64) HF_SWA(float, 64, 16, 16);
     if (block == 16 && d == 128) HF_SWA(float, 128, 16, 16);

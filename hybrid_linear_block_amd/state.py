@@ -193,6 +193,33 @@ class HybridAttentionState:
                    "hf_absorb_and_attend_cached")
         return out
 
+    def attend_ragged(self, q: torch.Tensor, k_flat: torch.Tensor, v_flat: torch.Tensor,
+                      kv_offsets, top_k, out: Optional[torch.Tensor] = None,
+                      sel_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """Head-aware ragged windows (hf_attend_ragged): head h attends rows
+        kv_offsets[h] .. kv_offsets[h + 1] of k_flat / v_flat ([rows][d]) with its own
+        top_k[h]; sel_out, if given, is int32 [H][ceil(n_q / B)][max(top_k)]."""
+        n_q, q_hs = self._check_input(q, "q")
+        d = self.cfg.head_dim
+        for name, t in (("k_flat", k_flat), ("v_flat", v_flat)):
+            if t.dtype != self.dtype or t.device != self.device or t.dim() != 2 or \
+                    t.shape[1] != d or not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous [rows][{d}] {self.dtype}")
+        if out is None:
+            out = torch.empty((self.cfg.num_heads, n_q, d), dtype=self.dtype, device=self.device)
+        _, o_hs = self._check_input(out, "out")
+        sel_ptr = 0
+        if sel_out is not None:
+            nqb = -(-n_q // self.cfg.block_size)
+            if sel_out.dtype != torch.int32 or tuple(sel_out.shape) != \
+                    (self.cfg.num_heads, nqb, max(top_k)) or not sel_out.is_contiguous():
+                raise ValueError("sel_out must be contiguous int32 [H][ceil(n_q/B)][max(top_k)]")
+            sel_ptr = sel_out.data_ptr()
+        _check(B.hf_attend_ragged(self.handle, q.data_ptr(), n_q, q_hs, k_flat.data_ptr(),
+                                  v_flat.data_ptr(), list(kv_offsets), list(top_k), out.data_ptr(),
+                                  o_hs, sel_ptr, _stream(self.device)), "hf_attend_ragged")
+        return out
+
     def key_cache_reset(self) -> None:
         """Forget the cached 8-token key sums (host-side; enqueues nothing)."""
         _check(B.hf_key_cache_reset(self.handle), "hf_key_cache_reset")

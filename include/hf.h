@@ -252,6 +252,27 @@ hf_status hf_block_scores(hf_state* st, const void* q, int64_t n_q, int64_t q_he
                           const void* k_win, int64_t n_kv, int64_t kv_head_stride,
                           float* scores_out, void* stream);
 
+/* ---- Head-aware ragged windows -------------------------------------------------
+ * Related work on the pages ("Resumen Tecnico: Pyramid Forcing", 3 "Optimizacion de
+ * Calculo de Cache KV Heterogenea"): attention heads keep KV caches of different
+ * lengths, stored as flattened sequences with boundary indices, and attention runs
+ * over them with no padding. hf_attend_ragged is hf_attend_chunk where head h attends
+ * its own window: rows kv_offsets[h] .. kv_offsets[h + 1] of k_flat and v_flat (rows of
+ * head_dim elements of the state's type, 16-byte aligned, one flattened sequence:
+ * kv_offsets[h + 1] - kv_offsets[h] >= 1 rows, at most max_n_kv, each head's window right
+ * after the previous one's, kv_offsets[num_heads] < 2^31), keeping top_k[h] of its own
+ * ceil(rows / block_size) key blocks (1 <= top_k[h] <= max_top_k). kv_offsets and top_k
+ * are host arrays of num_heads + 1 and num_heads entries, read during the call. q, out
+ * and the state are as in hf_attend_chunk (the chunk's queries are the same for every
+ * head). sel_out, if not NULL: int32 [H][ceil(n_q / B)][max_h top_k[h]], row (h, i)
+ * holding head h's top_k[h] kept blocks, ascending (the rest of the row is not
+ * written). HF_ERR_UNSUPPORTED for more than 64 heads or with the rotation of
+ * hf_set_rope on. Three launches, as hf_attend_chunk. */
+hf_status hf_attend_ragged(hf_state* st, const void* q, int64_t n_q, int64_t q_head_stride,
+                           const void* k_flat, const void* v_flat, const int64_t* kv_offsets,
+                           const int32_t* top_k, void* out, int64_t out_head_stride,
+                           int32_t* sel_out, void* stream);
+
 /* ---- Relative temporal rotation (RoPE) -----------------------------------------
  * [EN] 2.C "Stability Enhancements" (Relative RoPE Constraint); [ES] 2.C: the temporal
  * rotary position indices are bounded, the same in training and inference, and

@@ -294,6 +294,39 @@ def attend_rope(q, k_win, v_win, S, z, block: int, top_k: int, tokens_per_frame:
     return o_swa + o_lin, sel, s32
 
 
+# --------------------------------------------------- head-aware ragged windows
+# Related work on the pages ("Resumen Tecnico: Pyramid Forcing", 3 "Optimizacion de
+# Calculo de Cache KV Heterogenea"): heads keep KV caches of different lengths,
+# stored as flattened sequences with boundary indices, and attention runs over them
+# without padding. Here each head runs the hybrid attention above over its own
+# window; nothing else changes.
+
+
+def attend_ragged(q, k_flat, v_flat, offsets, S, z, block: int, top_ks,
+                  eps: float = DEFAULT_EPS, scale: Optional[float] = None, blocks=None):
+    """Head h attends the window rows k_flat[offsets[h]:offsets[h+1]] (and v_flat's)
+    with its own top_ks[h]. Returns (out [H][n_q][d], list of per-head selections
+    [Nqb][K_h], list of per-head fp32 scores [Nqb][Nkb_h])."""
+    q = np.asarray(q, np.float64)
+    H = q.shape[0]
+    out = np.full(q.shape, np.nan)
+    sels, scores = [], []
+    for h in range(H):
+        o0, o1 = int(offsets[h]), int(offsets[h + 1])
+        hb = None if blocks is None else [(0, i) for hh, i in blocks if hh == h]
+        if hb == []:
+            sel, s32 = select(q[h:h + 1], np.asarray(k_flat, np.float64)[None, o0:o1], block,
+                              top_ks[h], scale)
+        else:
+            o, sel, s32 = attend(q[h:h + 1], np.asarray(k_flat, np.float64)[None, o0:o1],
+                                 np.asarray(v_flat, np.float64)[None, o0:o1], S[h:h + 1],
+                                 z[h:h + 1], block, top_ks[h], eps, scale, hb)
+            out[h] = o[0]
+        sels.append(sel[0])
+        scores.append(s32[0])
+    return out, sels, scores
+
+
 # --------------------------------------------------------------- stream order
 # [EN] 1 "Problem Statement" and [ES] 1: the window slides and the oldest frames
 # leave the cache; [ABS]: evicted tokens are absorbed into the state.

@@ -17,5 +17,7 @@ from .inputs import (  # noqa: F401
     tiny_f32_frames,
     wan_layer_inputs,
     planted_inputs,
+    ragged_layer_inputs,
+    RAGGED_WINDOW_FRAMES,
     LongStream,
 )

@@ -113,12 +113,22 @@ WORKLOADS = {
     "planted_bf16": Workload(
         "planted_bf16", heads=12, head_dim=128, frame_tokens=1560, chunk_frames=3,
         window_frames=9, block=64, dtype="bf16", top_k_frac=0.25, n_frames=12),
+    # The Wan-1.3B-like layer with per-head window lengths (RAGGED_WINDOW_FRAMES), the
+    # windows stored flattened one after the other with boundary indices.
+    "ragged_heads_bf16": Workload(
+        "ragged_heads_bf16", heads=12, head_dim=128, frame_tokens=1560, chunk_frames=3,
+        window_frames=9, block=64, dtype="bf16", top_k_frac=0.25, n_frames=12),
     # 30 independent layers of the Wan-1.3B-like shapes per 3-frame chunk.
     "full_depth_bf16": Workload(
         "full_depth_bf16", heads=12, head_dim=128, frame_tokens=1560, chunk_frames=3,
         window_frames=9, block=64, dtype="bf16", top_k_frac=0.25, n_frames=12,
         layers=30),
 }
+
+# Head-aware ragged windows: window length of each head in latent frames (the
+# current 3-frame chunk included), a pyramid of three head classes of four heads each
+# standing in for per-head cache policies that keep more or less history.
+RAGGED_WINDOW_FRAMES = (9, 9, 9, 9, 6, 6, 6, 6, 4, 4, 4, 4)
 
 PLANTED_FRACTIONS = (0.125, 0.25, 0.5, 1.0)
 PLANTED_LOGIT_BIAS = 2.0
@@ -189,6 +199,28 @@ def wan_layer_inputs(seed: int, wl: Workload = WORKLOADS["wan_layer_bf16"], *,
     else:
         out.update(q=bf16_bits(q), k=bf16_bits(k), v=bf16_bits(v))
     return out
+
+
+# ------------------------------------------------------------ ragged head windows
+
+
+def ragged_layer_inputs(seed: int, window_frames=RAGGED_WINDOW_FRAMES,
+                        wl: Workload = WORKLOADS["ragged_heads_bf16"]):
+    """The Wan-like layer at stream step 3 where head h keeps the last window_frames[h]
+    frames of frames 0..11 (the chunk, frames 9..11, included): K and V of all heads'
+    windows flattened one after the other ([sum_h n_h][d] bf16 bits, head h's rows at
+    offsets[h] .. offsets[h + 1]), Q of the chunk ([H][3T][d]) and the evicted frames
+    0..2 of every head (for the state; [H][3T][d])."""
+    base = wan_layer_inputs(seed, wl)
+    T, hi = wl.frame_tokens, base["win_hi"]
+    offsets = np.zeros(wl.heads + 1, np.int64)
+    for h, f in enumerate(window_frames):
+        offsets[h + 1] = offsets[h] + f * T
+    parts_k = [base["k"][h, hi - f * T:hi] for h, f in enumerate(window_frames)]
+    parts_v = [base["v"][h, hi - f * T:hi] for h, f in enumerate(window_frames)]
+    return dict(q=base["q"], k_flat=np.concatenate(parts_k), v_flat=np.concatenate(parts_v),
+                offsets=offsets, k_ev=base["k"][:, :base["ev_hi"]],
+                v_ev=base["v"][:, :base["ev_hi"]])
 
 
 # --------------------------------------------------------------- planted structure

@@ -88,20 +88,21 @@ hipError_t launch_split_state(int, int, const float*, uint16_t*, hipStream_t) { 
 hipError_t launch_rope_table(float2*, int, int, double, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_block_pool(int, int, int, int, const void*, int64_t, int64_t, const void*, int64_t,
                              int64_t, float*, float*, int, int, hipStream_t, const KeyCache&,
-                             const Rope&) { return hipErrorNoDevice; }
+                             const Rope&, const Ragged&) { return hipErrorNoDevice; }
 hipError_t launch_absorb_and_pool(int, int, int, int, const void*, const void*, int64_t, int64_t,
                                   float*, const void*, int64_t, int64_t, const void*, int64_t,
                                   int64_t, float*, float*, int, int, hipStream_t, const KeyCache&,
                                   const Rope&) { return hipErrorNoDevice; }
 hipError_t launch_score_select(int, int, int, int, int, int, const float*, const float*, float, int,
-                               int32_t*, float*, hipStream_t) { return hipErrorNoDevice; }
+                               int32_t*, float*, hipStream_t, const Ragged&) {
+  return hipErrorNoDevice; }
 hipError_t launch_select_and_reduce(int, int, int, int, int, int, int, const float*, const float*,
                                     float, int, int32_t*, const float*, int64_t, float*, float*,
                                     uint16_t*, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_sparse_swa(int, int, int, int, const void*, int64_t, int64_t, const void*,
                              const void*, int64_t, int64_t, const int32_t*, int, const float*,
                              const uint16_t*, const float*, float, float, void*, int64_t,
-                             hipStream_t, const Rope&) { return hipErrorNoDevice; }
+                             hipStream_t, const Rope&, const Ragged&) { return hipErrorNoDevice; }
 hipError_t launch_attend_backward(int, int, int, const BwdArgs&, int, hipStream_t) {
   return hipErrorNoDevice; }
 hipError_t launch_absorb_backward(int, int, int, const void*, const void*, int64_t, int64_t,
@@ -171,6 +172,13 @@ int main() {
   const int rn = hf_attend_chunk_noalloc(&c, (float*)A, (float*)A, A, 4680, 4680 * 128, A, A,
                                          14040, 14040 * 128, 55, A, 4680 * 128, nullptr, nullptr);
   if (rn != HF_ERR_HIP && rn != HF_OK) return 1;
+  {  // ragged windows: validation only (no handle)
+    int64_t off[13] = {0};
+    int32_t tk[12];
+    for (int h = 0; h < 12; ++h) { off[h + 1] = off[h] + 1000; tk[h] = 4; }
+    EXPECT(hf_attend_ragged(nullptr, A, 10, 1280, A, A, off, tk, A, 1280, nullptr, nullptr),
+           HF_ERR_INVALID_ARG);
+  }
   hf_rope rp = {44, 10000.f, 1560, 8};
   if (hf_rope_workspace_bytes(&c, &rp) == 0) return 1;
   hf_rope bad_rope = rp; bad_rope.rot_dims = 43;

@@ -432,3 +432,45 @@ def test_as_f64_decodes_bf16_by_definition():
     x = np.arange(24, dtype=np.float32).reshape(2, 3, 4) / 3
     assert np.array_equal(oracle.as_f64(x, "f32"), x.astype(np.float64))
     assert oracle.as_f64(bits[:24].reshape(2, 3, 4), "bf16").shape == (2, 3, 4)
+
+
+# ------------------------------------------------------ head-aware ragged windows
+
+
+def test_ragged_with_equal_windows_is_the_dense_layout():
+    """Equal per-head windows stored flattened give the dense [H][n][d] results."""
+    rng = _rng(41)
+    H, n_q, n_kv, d, B, K = 3, 40, 96, 16, 16, 2
+    q = rng.standard_normal((H, n_q, d))
+    k = rng.standard_normal((H, n_kv, d))
+    v = rng.standard_normal((H, n_kv, d))
+    S, z = oracle.state_init(H, d)
+    oracle.absorb(S, z, rng.standard_normal((H, 20, d)), rng.standard_normal((H, 20, d)))
+    ref, sel, _ = oracle.attend(q, k, v, S, z, B, K)
+    off = np.arange(H + 1) * n_kv
+    out, sels, _ = oracle.attend_ragged(q, k.reshape(-1, d), v.reshape(-1, d), off, S, z, B, [K] * H)
+    assert np.array_equal(out, ref)
+    assert all(np.array_equal(sels[h], sel[h]) for h in range(H))
+
+
+def test_ragged_heads_are_independent_single_head_windows():
+    """Head h's result is that of a one-head call over its own window, whatever the other
+    heads' windows are (lengths 96, 40 and 17 rows, ragged last blocks)."""
+    rng = _rng(42)
+    H, n_q, d, B = 3, 33, 16, 16
+    lens, ks = [96, 40, 17], [3, 1, 2]
+    off = np.concatenate([[0], np.cumsum(lens)])
+    q = rng.standard_normal((H, n_q, d))
+    kf = rng.standard_normal((off[-1], d))
+    vf = rng.standard_normal((off[-1], d))
+    S, z = oracle.state_init(H, d)
+    oracle.absorb(S, z, rng.standard_normal((H, 9, d)), rng.standard_normal((H, 9, d)))
+    out, sels, _ = oracle.attend_ragged(q, kf, vf, off, S, z, B, ks)
+    kf2 = kf.copy()
+    kf2[off[0]:off[1]] = rng.standard_normal((lens[0], d))  # another window for head 0
+    out2, _, _ = oracle.attend_ragged(q, kf2, vf, off, S, z, B, ks)
+    assert np.array_equal(out[1:], out2[1:]) and not np.allclose(out[0], out2[0])
+    for h in range(H):
+        o, sel, _ = oracle.attend(q[h:h + 1], kf[None, off[h]:off[h + 1]], vf[None, off[h]:off[h + 1]],
+                                  S[h:h + 1], z[h:h + 1], B, ks[h])
+        assert np.array_equal(out[h], o[0]) and np.array_equal(sels[h], sel[0])

@@ -187,7 +187,8 @@ hf_status check_rope(const hf_config& c, const hf_rope* r) {
   if (!r) return HF_ERR_INVALID_ARG;
   if (r->rot_dims < 0 || r->rot_dims % 2 != 0 || r->rot_dims > c.head_dim) return HF_ERR_INVALID_ARG;
   if (!(r->theta_base > 0.f) || !std::isfinite(r->theta_base)) return HF_ERR_INVALID_ARG;
-  if (r->tokens_per_frame < 1 || r->cap < 0) return HF_ERR_INVALID_ARG;
+  if (r->tokens_per_frame < 8 || r->tokens_per_frame > INT32_MAX || r->cap < 0)
+    return HF_ERR_INVALID_ARG;
   return HF_OK;
 }
 
@@ -885,6 +886,21 @@ hf_status hf_attend_ragged(hf_state* st, const void* q, int64_t n_q, int64_t q_h
   if (n_q == 0) return HF_OK;
   const int nqb = (int)ceil_div(n_q, c.block_size);
   int32_t* sel = sel_out ? sel_out : st->sel;
+  // The attention's items (head-major) cut into 8 ranges of equal selected-block work,
+  // one per XCD: range x ends at the first item whose work prefix reaches (x + 1) / 8.
+  {
+    int64_t total = 0;
+    for (int h = 0; h < c.num_heads; ++h) total += (int64_t)nqb * top_k[h];
+    int64_t acc = 0;
+    int item = 0, x = 1;
+    rg.xcd0[0] = 0;
+    for (int h = 0; h < c.num_heads; ++h)
+      for (int i = 0; i < nqb; ++i, ++item) {
+        acc += top_k[h];
+        while (x < 8 && acc * 8 >= total * x) rg.xcd0[x++] = item + 1;
+      }
+    while (x <= 8) rg.xcd0[x++] = item;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   return on_device(st->device, [&]() {
     hipError_t r = timed(st, HF_KERNEL_BLOCK_POOL, s, [&]() {

@@ -66,11 +66,16 @@ struct Rope {
 // its key blocks are kb0[h] .. kb0[h + 1] in the order of all heads' blocks. on == false:
 // every head has the call's one window shape.
 constexpr int kRaggedMaxHeads = 64;
+// The attention launch gives XCD x the (head, query block) items xcd0[x] .. xcd0[x + 1]
+// of the head-major order, ranges cut so that every XCD gets the same number of
+// selected key blocks (a head's items stay together, which keeps its window in that
+// XCD's L2).
 struct Ragged {
   int32_t on = 0;
   int32_t off[kRaggedMaxHeads + 1];
   int32_t top_k[kRaggedMaxHeads];
   int32_t kb0[kRaggedMaxHeads + 1];
+  int32_t xcd0[9];
 };
 // cs[p * half + i] = (cos, sin) of p * base^(-2i / (2 half)) for p < npos (computed in
 // double precision).

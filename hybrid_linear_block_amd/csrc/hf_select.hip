@@ -31,22 +31,43 @@ namespace {
 
 constexpr int POOL_THREADS = 256;  // 4 waves, one (head, block) per wave
 
-// Rotate the VEC features of one row chunk (pairs p0 .. p0 + VEC/2 - 1 of the row) by
-// the row's temporal position (window row wrow): pairs below rope.half turn by the
-// tabulated angle, the others stay.
+// The angles of one 8-row group's chunk (pairs p0 .. p0 + VEC/2 - 1) for the temporal
+// rotation: with at least 8 tokens per frame a group spans at most two frames, so the
+// (cos, sin) of both are loaded once (t0 for rows in the group's first frame, t1 for
+// the next) and row r of the group is in the first frame iff r < split.
 template <int VEC>
-__device__ __forceinline__ void rope_chunk(float* v, int p0, const Rope& rope, int64_t wrow) {
-  const int64_t f = wrow / rope.tpf;
-  const int pos = f < rope.cap ? (int)f : rope.cap;
-  const float2* cs = rope.cs + (size_t)pos * rope.half;
+struct GroupAngles {
+  float2 t0[VEC / 2], t1[VEC / 2];
+  int split;
+};
+template <int VEC>
+__device__ __forceinline__ GroupAngles<VEC> group_angles(const Rope& rope, int p0,
+                                                         int64_t wrow0) {
+  GroupAngles<VEC> a;
+  const uint32_t tpf = (uint32_t)rope.tpf, f0 = (uint32_t)wrow0 / tpf;
+  a.split = (int)(tpf - ((uint32_t)wrow0 - f0 * tpf));  // rows left in the first frame
+  const uint32_t cap = (uint32_t)rope.cap;
+  const float2* c0 = rope.cs + (size_t)(f0 < cap ? f0 : cap) * rope.half;
+  const float2* c1 = rope.cs + (size_t)(f0 + 1 < cap ? f0 + 1 : cap) * rope.half;
+#pragma unroll
+  for (int e = 0; e < VEC / 2; ++e) {
+    const bool on = p0 + e < rope.half;
+    a.t0[e] = on ? c0[p0 + e] : make_float2(1.f, 0.f);
+    a.t1[e] = on ? c1[p0 + e] : make_float2(1.f, 0.f);
+  }
+  return a;
+}
+
+// Rotate the VEC features of row r of the group (pairs below rope.half turn by the
+// row's position; the others keep cos 1, sin 0, which leaves them exactly as they are).
+template <int VEC>
+__device__ __forceinline__ void rope_row(float* v, const GroupAngles<VEC>& a, int r) {
 #pragma unroll
   for (int e = 0; e < VEC; e += 2) {
-    if (p0 + e / 2 < rope.half) {
-      const float2 t = cs[p0 + e / 2];
-      const float a = v[e], b = v[e + 1];
-      v[e] = a * t.x - b * t.y;
-      v[e + 1] = a * t.y + b * t.x;
-    }
+    const float2 t = r < a.split ? a.t0[e / 2] : a.t1[e / 2];
+    const float x = v[e], y = v[e + 1];
+    v[e] = x * t.x - y * t.y;
+    v[e + 1] = x * t.y + y * t.x;
   }
 }
 
@@ -146,6 +167,10 @@ __device__ __forceinline__ void pool_wave(
     } else {
 #pragma unroll
       for (int e = 0; e < VEC; ++e) g8[e] = 0.f;
+      const int64_t grow0 = r0 + 8 * (rg + RPI * i);  // the group's first row
+      const bool rot = rope.cs != nullptr && cc * VEC < 2 * rope.half && grow0 < r1;
+      GroupAngles<VEC> ang;
+      if (rot) ang = group_angles<VEC>(rope, cc * VEC / 2, is_q ? rope.q_row0 + grow0 : grow0);
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
         float v[VEC];
@@ -157,9 +182,9 @@ __device__ __forceinline__ void pool_wave(
           for (int e = 0; e < VEC; ++e) v[e] = __uint_as_float(word(x[i][r], e));
         }
         if (rope.cs != nullptr) {  // wave-uniform
-          const int64_t row = r0 + 8 * (rg + RPI * i) + r;
+          const int64_t row = grow0 + r;
           if (row < r1) {
-            if (cc * VEC < 2 * rope.half) rope_chunk<VEC>(v, cc * VEC / 2, rope, is_q ? rope.q_row0 + row : row);
+            if (rot) rope_row<VEC>(v, ang, r);
             if (!is_q)  // the window's rotated keys for the attention kernel
               *reinterpret_cast<uint4*>(static_cast<T*>(rope.k_out) + (size_t)h * rope.k_out_hs +
                                         row * D + cc * VEC) = narrow16<T>(v);

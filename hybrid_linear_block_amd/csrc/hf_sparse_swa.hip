@@ -35,10 +35,17 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Item of workgroup wg in a ragged launch: the hardware hands consecutive workgroups to
+// the 8 XCDs in turn; XCD wg % 8 takes the (wg / 8)-th item of its range (-1: none).
+__device__ __forceinline__ int ragged_item(const Ragged& rg, int wg) {
+  const int x = wg & 7, k = wg >> 3;
+  return rg.xcd0[x] + k < rg.xcd0[x + 1] ? rg.xcd0[x] + k : -1;
+}
+
 // The angle table row (cos, sin of every rotated pair) of window row wrow's position.
 __device__ __forceinline__ const float2* rope_cs(const Rope& rope, int64_t wrow) {
-  const int64_t f = wrow / rope.tpf;
-  return rope.cs + (size_t)(f < rope.cap ? f : rope.cap) * rope.half;
+  const uint32_t f = (uint32_t)wrow / (uint32_t)rope.tpf;
+  return rope.cs + (size_t)(f < (uint32_t)rope.cap ? f : (uint32_t)rope.cap) * rope.half;
 }
 
 template <typename T, int D, int BLK>
@@ -100,7 +107,8 @@ __global__ __launch_bounds__((BLK / QW) * 64) void sparse_swa(
   constexpr int NKS = D / KSTEP;  // k-steps over features
   __shared__ SwaSmem<T, D, BLK> sm;
 
-  const int logical = xcd_remap(blockIdx.x, gridDim.x, n_logical);
+  // Ragged windows: XCD x takes its work-balanced range of the head-major items.
+  const int logical = rg.on ? ragged_item(rg, blockIdx.x) : xcd_remap(blockIdx.x, gridDim.x, n_logical);
   if (logical < 0) return;
   const int h = logical / nqb, i = logical % nqb;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -450,7 +458,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void s
   __shared__ uint4 lds_k[TCH];
   __shared__ uint4 lds_v[TCH];
 
-  const int logical = xcd_remap(blockIdx.x, gridDim.x, n_logical);
+  // Ragged windows: XCD x takes its work-balanced range of the head-major items.
+  const int logical = rg.on ? ragged_item(rg, blockIdx.x) : xcd_remap(blockIdx.x, gridDim.x, n_logical);
   if (logical < 0) return;
   const int h = logical / nqb, i = logical % nqb;
   const int lane = threadIdx.x & 63;
@@ -870,6 +879,13 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void s
   }
 }
 
+// Workgroups per XCD of a ragged launch: the longest XCD range.
+int ragged_width(const Ragged& rg) {
+  int w = 0;
+  for (int x = 0; x < 8; ++x) w = rg.xcd0[x + 1] - rg.xcd0[x] > w ? rg.xcd0[x + 1] - rg.xcd0[x] : w;
+  return w > 0 ? w : 1;
+}
+
 template <int D>
 hipError_t launch_bf16(const void* q, int64_t n_q, int64_t q_hs, const void* k, const void* v,
                        int64_t n_kv, int64_t kv_hs, const int32_t* sel, int top_k, int heads,
@@ -878,7 +894,7 @@ hipError_t launch_bf16(const void* q, int64_t n_q, int64_t q_hs, const void* k, 
                        const Ragged& rg) {
   const int nqb = (int)((n_q + 63) / 64);
   const int n_logical = nqb * heads;
-  const int n_wg = (n_logical + 7) / 8 * 8;
+  const int n_wg = rg.on ? 8 * ragged_width(rg) : (n_logical + 7) / 8 * 8;
 #define HF_SWA_BF16(SHORT, ROPE)                                                             \
   sparse_swa_bf16<D, SHORT, ROPE><<<n_wg, 128, 0, stream>>>(                                 \
       static_cast<const bf16_t*>(q), n_q, q_hs, static_cast<const bf16_t*>(k),                \
@@ -904,7 +920,7 @@ hipError_t launch(const void* q, int64_t n_q, int64_t q_hs, const void* k, const
   using Cf = SwaCfg<T, D, BLK, QW>;
   const int nqb = (int)((n_q + BLK - 1) / BLK);
   const int n_logical = nqb * heads;
-  const int n_wg = (n_logical + 7) / 8 * 8;
+  const int n_wg = rg.on ? 8 * ragged_width(rg) : (n_logical + 7) / 8 * 8;
 #define HF_SWA_GEN(ROPE)                                                                      \
   sparse_swa<T, D, BLK, QW, ROPE><<<n_wg, Cf::NT, 0, stream>>>(                               \
       static_cast<const T*>(q), n_q, q_hs, static_cast<const T*>(k), static_cast<const T*>(v), \

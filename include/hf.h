@@ -290,7 +290,7 @@ hf_status hf_attend_ragged(hf_state* st, const void* q, int64_t n_q, int64_t q_h
 typedef struct {
   int32_t rot_dims;         /* rotated features: even, 0 <= rot_dims <= head_dim (0: none) */
   float theta_base;         /* > 0 (10000 is the usual value) */
-  int64_t tokens_per_frame; /* >= 1 */
+  int64_t tokens_per_frame; /* >= 8 (an 8-row group then spans at most two frames) */
   int32_t cap;              /* >= 0: the largest position index */
 } hf_rope;
 

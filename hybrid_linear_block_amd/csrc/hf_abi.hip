@@ -735,7 +735,7 @@ hf_status hf_block_scores(hf_state* st, const void* q, int64_t n_q, int64_t q_he
 
 // Backward workspace: per-row statistics, then the inverse selection index.
 struct BwdLayout {
-  size_t rowstats, inv_cnt, inv_list, total;
+  size_t rowstats, inv_cnt, inv_list, state_part, total;
 };
 
 static BwdLayout bwd_layout(const hf_config* c) {
@@ -750,6 +750,10 @@ static BwdLayout bwd_layout(const hf_config* c) {
   off += round_up(H * nkb * 4);
   L.inv_list = off;
   off += round_up(H * nkb * nqb * 4);
+  L.state_part = off;  // bf16 states: partial dS and dz per 256-row chunk
+  if (c->dtype == HF_BF16)
+    off += round_up(H * (size_t)ceil_div(c->max_n_q, hf::kBwdStateChunk) *
+                    ((size_t)c->head_dim * c->head_dim + c->head_dim) * 4);
   L.total = off;
   return L;
 }
@@ -816,6 +820,8 @@ hf_status hf_attend_backward(hf_state* st, const void* q, int64_t n_q, int64_t q
   a.nq_cap = c.max_n_q;
   a.inv_cnt = reinterpret_cast<int32_t*>(w + L.inv_cnt);
   a.inv_list = reinterpret_cast<int32_t*>(w + L.inv_list);
+  a.state_part = reinterpret_cast<float*>(w + L.state_part);
+  a.s_split = st->s_split;
   a.nqb_cap = st->nqb_cap;
   hipStream_t s = static_cast<hipStream_t>(stream);
   return on_device(st->device, [&]() {

@@ -933,6 +933,365 @@ __global__ __launch_bounds__(BT) void absorb_bwd(const T* __restrict__ k, const 
   }
 }
 
+// bf16 absorb backward on MFMA (v_mfma_f32_16x16x32_bf16), one workgroup per (head,
+// 64 evicted tokens), wave w owning the output feature tiles 2w, 2w + 1 of both
+// gradients for all 64 tokens:
+//   dv^T = dS Phi^T        (A = rows of dS, B = phi(k) of the tokens)
+//   dk^T = dS^T V^T        (A = columns of dS, B = v of the tokens), then
+//   dk   = phi'(k) (dk + dz).
+// The fp32 operands (dS, phi(k)) are split into bf16 hi + lo and multiplied in three
+// products (hi hi, lo hi, hi lo); v is exact bf16, so dk takes two. A lane's B
+// operand is 8 consecutive features of one token (one 16-byte load of its row); its
+// A operand is 8 consecutive entries of a row (dv) or a column (dk) of dS, read from
+// global memory (dS is 64 KB per head and stays in cache). Results leave straight
+// from the MFMA layout: 4 consecutive features of one token per lane.
+template <int D>
+__global__ __launch_bounds__(BT) void absorb_bwd_mfma(const bf16_t* __restrict__ k,
+                                                      const bf16_t* __restrict__ v, int64_t n_ev,
+                                                      int64_t ev_hs, const float* __restrict__ dS,
+                                                      const float* __restrict__ dz,
+                                                      float* __restrict__ dk, float* __restrict__ dv,
+                                                      int64_t dev_hs, int ntile) {
+  constexpr int NKS = D / 32, NT = 4, FT = D / 16 / 4;  // k-steps, token tiles, tiles per wave
+  typedef Mfma<bf16_t> M;
+  const int h = blockIdx.x / ntile, tile = blockIdx.x % ntile;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const bf16_t* kh = k + (int64_t)h * ev_hs;
+  const bf16_t* vh = v + (int64_t)h * ev_hs;
+  const float* Sh = dS + (int64_t)h * D * D;
+  const int64_t n0 = (int64_t)tile * 64;
+  f32x4 av[FT][NT], ak[FT][NT];
+#pragma unroll
+  for (int f = 0; f < FT; ++f)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) av[f][t] = ak[f][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < NKS; ++s) {
+    // B operands of the 4 token tiles: phi(k) split, v exact
+    bf16x8 fh[NT], fl[NT], vb[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int64_t n = n0 + 16 * t + c;
+      const bool ok = n < n_ev;
+      const uint4 kr = ok ? *reinterpret_cast<const uint4*>(kh + n * D + 32 * s + 8 * g) : zero4();
+      const uint4 vr = ok ? *reinterpret_cast<const uint4*>(vh + n * D + 32 * s + 8 * g) : zero4();
+      float f[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = ok ? phi(bf16_to_f32(half16(kr, e))) : 0.f;
+      split_bf16x8(f, fh[t], fl[t]);
+      vb[t] = as_bf16x8(vr);
+    }
+#pragma unroll
+    for (int f = 0; f < FT; ++f) {
+      const int ft = FT * w + f;  // output feature tile
+      // A for dv: dS[16 ft + c][32 s + 8 g .. + 8]; for dk: dS[32 s + 8 g + e][16 ft + c]
+      float ra[8], rc[8];
+      const float4 r0 = *reinterpret_cast<const float4*>(Sh + (16 * ft + c) * D + 32 * s + 8 * g);
+      const float4 r1 = *reinterpret_cast<const float4*>(Sh + (16 * ft + c) * D + 32 * s + 8 * g + 4);
+      ra[0] = r0.x, ra[1] = r0.y, ra[2] = r0.z, ra[3] = r0.w;
+      ra[4] = r1.x, ra[5] = r1.y, ra[6] = r1.z, ra[7] = r1.w;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) rc[e] = Sh[(32 * s + 8 * g + e) * D + 16 * ft + c];
+      bf16x8 rh, rl, ch, cl;
+      split_bf16x8(ra, rh, rl);
+      split_bf16x8(rc, ch, cl);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        av[f][t] = M::mma(rh, fh[t], av[f][t]);
+        av[f][t] = M::mma(rl, fh[t], av[f][t]);
+        av[f][t] = M::mma(rh, fl[t], av[f][t]);
+        ak[f][t] = M::mma(ch, vb[t], ak[f][t]);
+        ak[f][t] = M::mma(cl, vb[t], ak[f][t]);
+      }
+    }
+  }
+  // lane holds features 16 ft + 4 g .. + 3 of token 16 t + c
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int64_t n = n0 + 16 * t + c;
+    if (n >= n_ev) continue;
+#pragma unroll
+    for (int f = 0; f < FT; ++f) {
+      const int i0 = 16 * (FT * w + f) + 4 * g;
+      *reinterpret_cast<float4*>(dv + (int64_t)h * dev_hs + n * D + i0) =
+          make_float4(av[f][t][0], av[f][t][1], av[f][t][2], av[f][t][3]);
+      const uint2 kq = *reinterpret_cast<const uint2*>(kh + n * D + i0);
+      const float4 z4 = *reinterpret_cast<const float4*>(dz + (int64_t)h * D + i0);
+      const float kx[4] = {bf16_to_f32(kq.x & 0xFFFFu), bf16_to_f32(kq.x >> 16),
+                           bf16_to_f32(kq.y & 0xFFFFu), bf16_to_f32(kq.y >> 16)};
+      *reinterpret_cast<float4*>(dk + (int64_t)h * dev_hs + n * D + i0) =
+          make_float4(phi_prime(kx[0]) * (ak[f][t][0] + z4.x), phi_prime(kx[1]) * (ak[f][t][1] + z4.y),
+                      phi_prime(kx[2]) * (ak[f][t][2] + z4.z), phi_prime(kx[3]) * (ak[f][t][3] + z4.w));
+    }
+  }
+}
+
+// bf16 linear-read part of dq on MFMA, one workgroup per (head, 64-row query block),
+// wave w owning rows 16w .. 16w + 15 (one per lane c). With f = phi(q_r), den = z . f
+// + eps and g = dout_r / den:
+//   (S f)^T = S F^T           A = rows of S, B = f of the wave's rows,
+//   c_r     = -(dout_r . S f) / den^2,
+//   (S^T g)^T = S^T G^T       A = columns of S, B = g of the wave's rows,
+//   dq_r   += phi'(q_r) (S^T g + c_r z),
+// and den, c go to the per-row statistics for the dS / dz kernel. The bf16 hi/lo split
+// of S (kept by the state for the forward epilogue) is staged in LDS; its rows are read
+// with ds_read_b128, its columns with the transposing read (rows 4g .. 4g + 3 and
+// 4g + 16 .. 4g + 19 of a 32-row step for lane group g, so g takes that order of the
+// contracted index); f and g are split into hi + lo in registers; three products each.
+template <int D>
+__global__ __launch_bounds__(BT) void bwd_rows_lin_mfma(
+    const bf16_t* __restrict__ q, int64_t n_q, int64_t q_hs, const uint16_t* __restrict__ s_split,
+    const float* __restrict__ z, float eps, const bf16_t* __restrict__ dout, int64_t do_hs,
+    float* __restrict__ dq, int64_t dq_hs, float* __restrict__ rs, int64_t nq_cap, int nqb) {
+  constexpr int NKS = D / 32, NT = D / 16, RSB = D + 16;
+  typedef Mfma<bf16_t> M;
+  __shared__ __align__(16) bf16_t sS[2 * D * RSB];  // hi rows, then lo rows
+  const int h = blockIdx.x / nqb, i = blockIdx.x % nqb;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const int64_t r = (int64_t)i * 64 + 16 * w + c;
+  const bool live = r < n_q;
+  const int64_t rr = live ? r : n_q - 1;
+  const bf16_t* qr = q + (int64_t)h * q_hs + rr * D;
+  const bf16_t* dr = dout + (int64_t)h * do_hs + rr * D;
+  const float* zh = z + (int64_t)h * D;
+  // stage the split of S
+  const uint16_t* Ssp = s_split + (int64_t)h * 2 * D * D;
+  for (int x = threadIdx.x; x < 2 * D * (D / 8); x += BT) {
+    const int row = x / (D / 8), ch = x % (D / 8);  // row of [hi; lo]
+    *reinterpret_cast<uint4*>(sS + row * RSB + ch * 8) =
+        *reinterpret_cast<const uint4*>(Ssp + (int64_t)row * D + ch * 8);
+  }
+  // f of this lane's row in k-step order (B operand of S F^T) and den
+  bf16x8 fhi[NKS], flo[NKS];
+  float qv[NKS][8];
+  float den = 0.f;
+#pragma unroll
+  for (int s2 = 0; s2 < NKS; ++s2) {
+    const uint4 qb = *reinterpret_cast<const uint4*>(qr + 32 * s2 + 8 * g);
+    const float4 z0 = *reinterpret_cast<const float4*>(zh + 32 * s2 + 8 * g);
+    const float4 z1 = *reinterpret_cast<const float4*>(zh + 32 * s2 + 8 * g + 4);
+    const float zz[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
+    float f[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      qv[s2][e] = bf16_to_f32(half16(qb, e));
+      f[e] = phi(qv[s2][e]);
+      den += zz[e] * f[e];
+    }
+    split_bf16x8(f, fhi[s2], flo[s2]);
+  }
+  den = sum_over_groups(den) + eps;
+  const float inv_den = 1.f / den;
+  // g of this lane's row in the transposing read's order of the contracted index
+  bf16x8 ghi[NKS], glo[NKS];
+#pragma unroll
+  for (int s2 = 0; s2 < NKS; ++s2) {
+    const uint2 a = *reinterpret_cast<const uint2*>(dr + 32 * s2 + 4 * g);
+    const uint2 b = *reinterpret_cast<const uint2*>(dr + 32 * s2 + 4 * g + 16);
+    const uint32_t wv[4] = {a.x, a.y, b.x, b.y};
+    float gv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) gv[e] = bf16_to_f32((wv[e >> 1] >> (16 * (e & 1))) & 0xFFFFu) * inv_den;
+    split_bf16x8(gv, ghi[s2], glo[s2]);
+  }
+  __syncthreads();
+  const uint32_t sb = lds_offset(sS);
+  // (S f)^T tiles and c_r
+  float cpart = 0.f;
+#pragma unroll
+  for (int jt = 0; jt < NT; ++jt) {
+    f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s2 = 0; s2 < NKS; ++s2) {
+      const uint32_t o = (uint32_t)((16 * jt + c) * RSB + 32 * s2 + 8 * g) * 2u;
+      const bf16x8 sh = as_bf16x8(lds_ld16(sb + o));
+      const bf16x8 sl = as_bf16x8(lds_ld16(sb + o + (uint32_t)D * RSB * 2u));
+      a = M::mma(sh, fhi[s2], a);
+      a = M::mma(sl, fhi[s2], a);
+      a = M::mma(sh, flo[s2], a);
+    }
+    // lane holds (S f)[16 jt + 4 g + 0..3] of its row
+    const uint2 dv2 = *reinterpret_cast<const uint2*>(dr + 16 * jt + 4 * g);
+    cpart += bf16_to_f32(dv2.x & 0xFFFFu) * a[0] + bf16_to_f32(dv2.x >> 16) * a[1] +
+             bf16_to_f32(dv2.y & 0xFFFFu) * a[2] + bf16_to_f32(dv2.y >> 16) * a[3];
+  }
+  const float cr = -sum_over_groups(cpart) * inv_den * inv_den;
+  // (S^T g)^T tiles and the update of dq
+  const int jj = (lane & 15) >> 2, pp = lane & 3;
+  const uint32_t row_lo = (uint32_t)(4 * g + jj) * RSB * 2u + pp * 8u;
+  const uint32_t row_hi = row_lo + 16u * RSB * 2u;
+#pragma unroll
+  for (int it = 0; it < NT; ++it) {
+    f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s2 = 0; s2 < NKS; ++s2) {
+      const uint32_t b = sb + (uint32_t)(32 * s2 * RSB) * 2u + it * 32u;
+      const v4i16 h0 = lds_tr8(b + row_lo), h1 = lds_tr8(b + row_hi);
+      const v4i16 l0 = lds_tr8(b + row_lo + (uint32_t)D * RSB * 2u);
+      const v4i16 l1 = lds_tr8(b + row_hi + (uint32_t)D * RSB * 2u);
+      const bf16x8 th = __builtin_bit_cast(bf16x8, __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7));
+      const bf16x8 tl = __builtin_bit_cast(bf16x8, __builtin_shufflevector(l0, l1, 0, 1, 2, 3, 4, 5, 6, 7));
+      a = M::mma(th, ghi[s2], a);
+      a = M::mma(tl, ghi[s2], a);
+      a = M::mma(th, glo[s2], a);
+    }
+    if (live) {  // lane holds (S^T g)[16 it + 4 g + 0..3] of its row
+      const int i0 = 16 * it + 4 * g;
+      const uint2 qq = *reinterpret_cast<const uint2*>(qr + i0);
+      const float4 z4 = *reinterpret_cast<const float4*>(zh + i0);
+      float* o = dq + (int64_t)h * dq_hs + r * D + i0;
+      const float4 prev = *reinterpret_cast<const float4*>(o);
+      *reinterpret_cast<float4*>(o) = make_float4(
+          prev.x + phi_prime(bf16_to_f32(qq.x & 0xFFFFu)) * (a[0] + cr * z4.x),
+          prev.y + phi_prime(bf16_to_f32(qq.x >> 16)) * (a[1] + cr * z4.y),
+          prev.z + phi_prime(bf16_to_f32(qq.y & 0xFFFFu)) * (a[2] + cr * z4.z),
+          prev.w + phi_prime(bf16_to_f32(qq.y >> 16)) * (a[3] + cr * z4.w));
+    }
+  }
+  if (live && g == 0) {
+    float* st = rs + ((int64_t)h * nq_cap + r) * 4;
+    st[2] = den;
+    st[3] = cr;
+  }
+}
+
+// bf16 dS and dz on MFMA: dS = G^T F and dz = F^T c over the query rows, where
+// g_r = dout_r / den_r, f_r = phi(q_r) and c_r come from the per-row statistics of
+// the linear read. One workgroup per (head, chunk of kStateChunk rows) writes the
+// chunk's partial dS and dz; bwd_state_reduce adds the chunks in order (no atomics).
+// Per 32-row k-step the workgroup forms g and f once (fp32, split into bf16 hi + lo)
+// into LDS row-major; both MFMA operands are then 8 rows of one column, read with the
+// transposing LDS read (rows 4g .. 4g + 3 and 4g + 16 .. 4g + 19 of the step for lane
+// group g, the same row order for both operands), and each dS tile takes three
+// products (hi hi, lo hi, hi lo). Wave w owns dS rows 32w .. 32w + 31 (two 16-row
+// tiles at d = 128) against all columns.
+constexpr int kStateChunk = kBwdStateChunk;
+template <int D>
+__global__ __launch_bounds__(BT) void bwd_state_mfma(const bf16_t* __restrict__ q, int64_t n_q,
+                                                     int64_t q_hs, const bf16_t* __restrict__ dout,
+                                                     int64_t do_hs, const float* __restrict__ rs,
+                                                     int64_t nq_cap, float* __restrict__ part,
+                                                     int n_chunk) {
+  constexpr int NT = D / 16, JT = NT / 4;  // column tiles; row tiles per wave
+  constexpr int RSB = D + 16;               // LDS row stride (bf16): conflict-free transposing reads
+  constexpr int CPT = 32 * (D / 8) / BT;    // 16-byte chunks per thread per step
+  typedef Mfma<bf16_t> M;
+  __shared__ __align__(16) bf16_t gh[32 * RSB], gl[32 * RSB], fh[32 * RSB], fl[32 * RSB];
+  __shared__ float zred[BT / (D / 8)][D];
+  const int h = blockIdx.x / n_chunk, p = blockIdx.x % n_chunk;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int g = lane >> 4;
+  const bf16_t* qh = q + (int64_t)h * q_hs;
+  const bf16_t* doh = dout + (int64_t)h * do_hs;
+  const float* rsh = rs + (int64_t)h * nq_cap * 4;
+  // staging: thread's chunk ch (8 features) of rows rr, rr + BT / (D / 8), ...
+  const int ch = threadIdx.x % (D / 8), rr = threadIdx.x / (D / 8);
+  float zacc[8] = {};
+  f32x4 acc[JT][NT];
+#pragma unroll
+  for (int j = 0; j < JT; ++j)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // transposing-read addresses: lane (4jj + pp) of group g -> row 4g + jj, columns 4pp ..
+  const int jj = (lane & 15) >> 2, pp = lane & 3;
+  const uint32_t row_lo = (uint32_t)(4 * g + jj) * RSB * 2u + pp * 8u;
+  const uint32_t row_hi = row_lo + 16u * RSB * 2u;
+  auto tr_op = [&](const bf16_t* base, int col_tile) {
+    const uint32_t b = lds_offset(base) + col_tile * 32u;
+    const v4i16 lo = lds_tr8(b + row_lo), hi = lds_tr8(b + row_hi);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  const int64_t r_begin = (int64_t)p * kStateChunk;
+  const int64_t r_end = r_begin + kStateChunk < n_q ? r_begin + kStateChunk : n_q;
+  for (int64_t r0 = r_begin; r0 < r_end; r0 += 32) {
+    __syncthreads();  // every wave is done with the previous step's operands
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int row = rr + u * (BT / (D / 8));
+      const int64_t r = r0 + row;
+      float f[8], gv[8];
+      if (r < r_end) {
+        const uint4 qb = *reinterpret_cast<const uint4*>(qh + r * D + ch * 8);
+        const uint4 db = *reinterpret_cast<const uint4*>(doh + r * D + ch * 8);
+        const float inv_den = 1.f / rsh[r * 4 + 2], cr = rsh[r * 4 + 3];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          f[e] = phi(bf16_to_f32(half16(qb, e)));
+          gv[e] = bf16_to_f32(half16(db, e)) * inv_den;
+          zacc[e] += cr * f[e];
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = gv[e] = 0.f;
+      }
+      bf16x8 a, b, x, y;
+      split_bf16x8(gv, a, b);
+      split_bf16x8(f, x, y);
+      *reinterpret_cast<bf16x8*>(gh + row * RSB + ch * 8) = a;
+      *reinterpret_cast<bf16x8*>(gl + row * RSB + ch * 8) = b;
+      *reinterpret_cast<bf16x8*>(fh + row * RSB + ch * 8) = x;
+      *reinterpret_cast<bf16x8*>(fl + row * RSB + ch * 8) = y;
+    }
+    __syncthreads();
+    bf16x8 ah[JT], al[JT];
+#pragma unroll
+    for (int j = 0; j < JT; ++j) {
+      ah[j] = tr_op(gh, JT * w + j);
+      al[j] = tr_op(gl, JT * w + j);
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const bf16x8 bh = tr_op(fh, t), bl = tr_op(fl, t);
+#pragma unroll
+      for (int j = 0; j < JT; ++j) {
+        acc[j][t] = M::mma(ah[j], bh, acc[j][t]);
+        acc[j][t] = M::mma(al[j], bh, acc[j][t]);
+        acc[j][t] = M::mma(ah[j], bl, acc[j][t]);
+      }
+    }
+  }
+  // partial dS of the chunk in MFMA order: [tile (row tile, column tile)][lane][4]
+  float* ph = part + ((int64_t)h * n_chunk + p) * (D * D + D);
+#pragma unroll
+  for (int j = 0; j < JT; ++j)
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      *reinterpret_cast<float4*>(ph + ((JT * w + j) * NT + t) * 256 + lane * 4) =
+          make_float4(acc[j][t][0], acc[j][t][1], acc[j][t][2], acc[j][t][3]);
+  // partial dz: the staging threads' column sums, added in thread order
+#pragma unroll
+  for (int e = 0; e < 8; ++e) zred[rr][ch * 8 + e] = zacc[e];
+  __syncthreads();
+  if (threadIdx.x < D) {
+    float z = 0.f;
+    for (int k = 0; k < BT / (D / 8); ++k) z += zred[k][threadIdx.x];
+    ph[D * D + threadIdx.x] = z;
+  }
+}
+
+// dS and dz from the chunks' partials, added in chunk order.
+template <int D>
+__global__ __launch_bounds__(BT) void bwd_state_reduce(const float* __restrict__ part,
+                                                       int n_chunk, float* __restrict__ dS,
+                                                       float* __restrict__ dz) {
+  constexpr int NT = D / 16, PER = D * D + D;
+  const int h = blockIdx.y;
+  const int x = blockIdx.x * BT + threadIdx.x;  // element of a partial
+  if (x >= PER) return;
+  const float* ph = part + (int64_t)h * n_chunk * PER + x;
+  float a = 0.f;
+  for (int p = 0; p < n_chunk; ++p) a += ph[(int64_t)p * PER];
+  if (x >= D * D) {
+    dz[(int64_t)h * D + (x - D * D)] = a;
+  } else {  // MFMA order -> dS[16 jt + 4 g + r][16 t + c]
+    const int tile = x / 256, l = (x % 256) / 4, r = x % 4;
+    const int jt = tile / NT, t = tile % NT;
+    dS[(int64_t)h * D * D + (16 * jt + 4 * (l >> 4) + r) * D + 16 * t + (l & 15)] = a;
+  }
+}
+
 template <typename T, int D, int BLK>
 hipError_t run_attend_bwd(const BwdArgs& a, int stage, hipStream_t s) {
   const int nqb = (int)((a.n_q + BLK - 1) / BLK), nkb = (int)((a.n_kv + BLK - 1) / BLK);
@@ -945,10 +1304,9 @@ hipError_t run_attend_bwd(const BwdArgs& a, int stage, hipStream_t s) {
         static_cast<const bf16_t*>(a.q), a.n_q, a.q_hs, static_cast<const bf16_t*>(a.k),
         static_cast<const bf16_t*>(a.v), a.n_kv, a.kv_hs, a.sel, a.top_k, nqb, nkb, a.scale,
         static_cast<const bf16_t*>(a.dout), a.do_hs, a.dq, a.dq_hs, a.rowstats, a.nq_cap);
-    bwd_rows_lin<T, D, BLK><<<(unsigned)(a.heads * nqb), BT, 0, s>>>(
-        static_cast<const T*>(a.q), a.n_q, a.q_hs, static_cast<const T*>(a.k),
-        static_cast<const T*>(a.v), a.n_kv, a.kv_hs, a.sel, a.top_k, nqb, nkb, a.S, a.z, a.eps,
-        a.scale, static_cast<const T*>(a.dout), a.do_hs, a.dq, a.dq_hs, a.rowstats, a.nq_cap);
+    bwd_rows_lin_mfma<D><<<(unsigned)(a.heads * nqb), BT, 0, s>>>(
+        static_cast<const bf16_t*>(a.q), a.n_q, a.q_hs, a.s_split, a.z, a.eps,
+        static_cast<const bf16_t*>(a.dout), a.do_hs, a.dq, a.dq_hs, a.rowstats, a.nq_cap, nqb);
   } else if (stage == 1)
     bwd_rows<T, D, BLK><<<(unsigned)(a.heads * nqb * (BLK / kRows<BLK>)), BT, 0, s>>>(
         static_cast<const T*>(a.q), a.n_q, a.q_hs, static_cast<const T*>(a.k),
@@ -965,7 +1323,14 @@ hipError_t run_attend_bwd(const BwdArgs& a, int stage, hipStream_t s) {
         static_cast<const T*>(a.q), a.n_q, a.q_hs, static_cast<const T*>(a.k),
         static_cast<const T*>(a.v), a.n_kv, a.kv_hs, nkb, a.scale, static_cast<const T*>(a.dout),
         a.do_hs, a.rowstats, a.nq_cap, a.inv_cnt, a.inv_list, a.nqb_cap, a.dk, a.dv, a.dkv_hs);
-  if (stage == 3)
+  if (stage == 3 && std::is_same<T, bf16_t>::value) {
+    const int n_chunk = (int)((a.n_q + kStateChunk - 1) / kStateChunk);
+    bwd_state_mfma<D><<<(unsigned)(a.heads * n_chunk), BT, 0, s>>>(
+        static_cast<const bf16_t*>(a.q), a.n_q, a.q_hs, static_cast<const bf16_t*>(a.dout),
+        a.do_hs, a.rowstats, a.nq_cap, a.state_part, n_chunk);
+    bwd_state_reduce<D><<<dim3((D * D + D + BT - 1) / BT, a.heads), BT, 0, s>>>(
+        a.state_part, n_chunk, a.dS, a.dz);
+  } else if (stage == 3)
     bwd_state<T, D><<<(unsigned)(a.heads * (D / kStateRows + 1)), BT, 0, s>>>(
         static_cast<const T*>(a.q), a.n_q, a.q_hs, static_cast<const T*>(a.dout), a.do_hs,
         a.rowstats, a.nq_cap, a.dS, a.dz);
@@ -977,9 +1342,14 @@ hipError_t run_absorb_bwd(int heads, const void* k, const void* v, int64_t n_ev,
                           const float* dS, const float* dz, float* dk, float* dv, int64_t dev_hs,
                           hipStream_t s) {
   const int ntile = (int)((n_ev + 63) / 64);
-  absorb_bwd<T, D><<<(unsigned)(heads * ntile), BT, 0, s>>>(
-      static_cast<const T*>(k), static_cast<const T*>(v), n_ev, ev_hs, dS, dz, dk, dv, dev_hs,
-      ntile);
+  if constexpr (std::is_same<T, bf16_t>::value)
+    absorb_bwd_mfma<D><<<(unsigned)(heads * ntile), BT, 0, s>>>(
+        static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v), n_ev, ev_hs, dS, dz, dk, dv,
+        dev_hs, ntile);
+  else
+    absorb_bwd<T, D><<<(unsigned)(heads * ntile), BT, 0, s>>>(
+        static_cast<const T*>(k), static_cast<const T*>(v), n_ev, ev_hs, dS, dz, dk, dv, dev_hs,
+        ntile);
   return hipGetLastError();
 }
 

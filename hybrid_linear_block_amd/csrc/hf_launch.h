@@ -149,7 +149,11 @@ struct BwdArgs {
   int32_t* inv_cnt;   // [heads][nkb]
   int32_t* inv_list;  // [heads][nkb][nqb_cap]
   int nqb_cap;
+  float* state_part;  // bf16 states: [heads][ceil(n_q / 256)][d * d + d], partial dS and dz
+  const uint16_t* s_split;  // bf16 states: the state's hi/lo split of S ([heads][2][d][d])
 };
+// Query rows per partial of the bf16 dS / dz kernel (sizes the backward workspace).
+constexpr int kBwdStateChunk = 256;
 // dq, dk, dv, dS and dz of the hybrid attention (n_q >= 1), stage by stage in order on
 // one stream: stage 0 the inverse selection index, 1 dq and the per-row statistics (two
 // launches for bf16 states: the MFMA softmax part, then the linear read's part), 2 dk

@@ -99,15 +99,21 @@ def test_workspace_bytes():
 
 
 def test_backward_workspace_bytes():
-    """Per-row statistics (4 fp32 per query row and head) and the inverse selection
-    index (a count and a list of query blocks per key block and head), 256-byte
-    aligned pieces."""
+    """Per-row statistics (4 fp32 per query row and head), the inverse selection
+    index (a count and a list of query blocks per key block and head) and, for bf16
+    states, the partial dS and dz of every 256-query-row chunk, 256-byte aligned
+    pieces."""
     c = cfg()
-    H, B_ = c.num_heads, c.block_size
+    H, B_, d = c.num_heads, c.block_size, c.head_dim
     nqb, nkb = -(-c.max_n_q // B_), -(-c.max_n_kv // B_)
     up = lambda x: -(-x // 256) * 256  # noqa: E731
     expect = up(H * c.max_n_q * 16) + up(H * nkb * 4) + up(H * nkb * nqb * 4)
-    assert hla.hf_backward_workspace_bytes(c) == expect
+    parts = up(H * -(-c.max_n_q // 256) * (d * d + d) * 4)
+    assert hla.hf_backward_workspace_bytes(c) == expect + parts
+    f32 = cfg(dtype=B.HF_F32, block_size=16, head_dim=64)
+    nqb, nkb = -(-f32.max_n_q // 16), -(-f32.max_n_kv // 16)
+    assert hla.hf_backward_workspace_bytes(f32) == (up(H * f32.max_n_q * 16) + up(H * nkb * 4) +
+                                                     up(H * nkb * nqb * 4))
     assert hla.hf_backward_workspace_bytes(cfg(head_dim=96)) == 0
 
 

@@ -11,19 +11,28 @@
 //                 dq_r += phi'(q_r) * (S^T g + c z);
 //   absorb        dv_n = dS phi(k_n), dk_n = phi'(k_n) * (dS^T v_n + dz).
 //
-// Kernels (fp32 arithmetic throughout, no atomics: every sum runs in a fixed order,
-// so the results are bitwise reproducible):
-//   bwd_inv_sel  per (head, key block): the query blocks that selected it, ascending;
-//   bwd_rows     per (head, query block): pass 1 recomputes each row's softmax
-//                (log-sum-exp and o_swa, hence D_r) over its selected blocks, then
-//                the linear read's terms; pass 2 accumulates dq; stores per-row
-//                (lse, D, den, c) for the other kernels;
-//   bwd_kv       per (head, key block): dk and dv over the query blocks that
-//                selected it;
-//   bwd_state    per (head, 8 rows of dS, or z): dS and dz over all query rows;
-//   absorb_bwd   per (head, 64 evicted tokens): dk_ev and dv_ev.
-// A row's dot products are split over TPR adjacent lanes (DS features each) and
-// reduced with xor shuffles; K/V or Q/dout tiles are staged in LDS as fp32.
+// No atomics: every sum runs in a fixed order, so the results are bitwise
+// reproducible. Kernels:
+//   bwd_inv_sel        per (head, key block): the query blocks that selected it,
+//                      ascending.
+// fp32 states (fp32 arithmetic on the vector units; a row's dot products are split
+// over TPR adjacent lanes and reduced with xor shuffles, tiles staged in LDS as fp32):
+//   bwd_rows           per (head, query block): pass 1 recomputes each row's softmax
+//                      (log-sum-exp and o_swa, hence D_r) over its selected blocks, then
+//                      the linear read's terms; pass 2 accumulates dq; stores per-row
+//                      (lse, D, den, c) for the other kernels;
+//   bwd_kv             per (head, key block): dk and dv over the query blocks that
+//                      selected it;
+//   bwd_state          per (head, 4 rows of dS, or z): dS and dz over all query rows;
+//   absorb_bwd         per (head, 64 evicted tokens): dk_ev and dv_ev.
+// bf16 states (v_mfma_f32_16x16x32_bf16; fp32 operands split into bf16 hi + lo, so the
+// products keep ~fp32 accuracy, fp32 accumulation):
+//   bwd_dq2            the softmax part of dq, lse and D (tiles staged like the forward);
+//   bwd_rows_lin_mfma  the linear read's part of dq, den and c;
+//   bwd_kv2            dk and dv (tiles staged like the forward);
+//   bwd_state_mfma     partial dS and dz per 256 query rows, bwd_state_reduce sums them
+//                      in order;
+//   absorb_bwd_mfma    dk_ev and dv_ev.
 #include <type_traits>
 
 #include "hf_device.h"
@@ -168,26 +177,20 @@ __global__ __launch_bounds__(256) void bwd_inv_sel(const int32_t* __restrict__ s
 template <int BLK>
 constexpr int kRows = BLK > 32 ? 32 : BLK;
 
-// Body of the row kernels. LIN: only the linear read's terms, added to dq (which holds
-// the softmax path's part, written by bwd_dq_mfma together with lse and D); stores den
-// and c only.
-template <typename T, int D, int BLK, bool LIN>
+// Body of the fp32 row kernel.
+template <typename T, int D, int BLK>
 __device__ __forceinline__ void rows_body(
     const T* __restrict__ q, int64_t n_q, int64_t q_hs, const T* __restrict__ kg,
     const T* __restrict__ vg, int64_t n_kv, int64_t kv_hs, const int32_t* __restrict__ sel,
     int top_k, int nqb, int nkb, const float* __restrict__ S, const float* __restrict__ z,
     float eps, float scale, const T* __restrict__ dout, int64_t do_hs, float* __restrict__ dq,
     int64_t dq_hs, float* __restrict__ rs, int64_t nq_cap) {
-  // The linear-only form takes a whole query block per workgroup (one staging of S
-  // per 64 rows); the full form splits it into 32-row halves.
-  constexpr int RPW = LIN ? BLK : kRows<BLK>, KT = RPW, SPLIT = BLK / RPW;
+  // A query block is split into 32-row parts.
+  constexpr int RPW = kRows<BLK>, KT = RPW, SPLIT = BLK / RPW;
   constexpr int TPR = BT / RPW, DS = D / TPR;
   static_assert(DS % 4 == 0, "float4 slices");
   __shared__ __align__(16) float tk[KT * D];
   __shared__ __align__(16) float tv[KT * D];
-  // S of the head for the linear read, staged in the linear-only form (whose
-  // workgroups do little else); the full form reads it from the cache.
-  __shared__ __align__(16) float tS[LIN ? D * D : 4];
   const int h = blockIdx.x / (nqb * SPLIT), i = (blockIdx.x / SPLIT) % nqb;
   const int part = blockIdx.x % SPLIT;
   const int rl = threadIdx.x / TPR, d0 = (threadIdx.x % TPR) * DS;
@@ -209,7 +212,6 @@ __device__ __forceinline__ void rows_body(
 
   // ---- pass 1: softmax statistics and o_swa (online, base 2) ----
   float m2 = -INFINITY, l = 0.f;
-  if constexpr (!LIN)
   for (int tt = 0; tt < top_k * SPLIT; ++tt) {
     const int64_t k0 = (int64_t)clamp_block(my_sel[tt / SPLIT], nkb) * BLK + (tt % SPLIT) * KT;
     if (k0 >= n_kv) continue;  // the ragged last block has no second half
@@ -284,11 +286,7 @@ __device__ __forceinline__ void rows_body(
   const float den = row_sum<TPR>(fz) + eps;
   const float inv_den = 1.f / den;
   __syncthreads();  // every wave is done with the last tiles
-  if (LIN)
-    for (int e = threadIdx.x; e < D * D / 4; e += BT)
-      reinterpret_cast<float4*>(tS)[e] =
-          reinterpret_cast<const float4*>(S + (int64_t)h * D * D)[e];
-  const float* Sh = LIN ? tS : S + (int64_t)h * D * D;
+  const float* Sh = S + (int64_t)h * D * D;
   float* frow = tk + rl * D;
   float* grow = tv + rl * D;
 #pragma unroll
@@ -334,7 +332,6 @@ __device__ __forceinline__ void rows_body(
   for (int e = 0; e < DS; ++e) acc[e] = phi_prime(qv[e]) * (dql[e] + c * zh[d0 + e]);
 
   // ---- pass 2: dq of the softmax path ----
-  if constexpr (!LIN)
   for (int tt = 0; tt < top_k * SPLIT; ++tt) {
     const int64_t k0 = (int64_t)clamp_block(my_sel[tt / SPLIT], nkb) * BLK + (tt % SPLIT) * KT;
     if (k0 >= n_kv) continue;
@@ -363,13 +360,11 @@ __device__ __forceinline__ void rows_body(
   if (live) {
     float* o = dq + (int64_t)h * dq_hs + r * D + d0;
 #pragma unroll
-    for (int e = 0; e < DS; ++e) o[e] = LIN ? o[e] + acc[e] : acc[e];
+    for (int e = 0; e < DS; ++e) o[e] = acc[e];
     if (d0 == 0) {
       float* st = rs + ((int64_t)h * nq_cap + r) * 4;
-      if (!LIN) {
-        st[0] = lse2;
-        st[1] = Dr;
-      }
+      st[0] = lse2;
+      st[1] = Dr;
       st[2] = den;
       st[3] = c;
     }
@@ -390,14 +385,9 @@ __device__ __forceinline__ void rows_body(
 template <typename T, int D, int BLK>
 __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(4))) void bwd_rows(
     HF_ROWS_ARGS) {
-  rows_body<T, D, BLK, false>(HF_ROWS_PASS);
+  rows_body<T, D, BLK>(HF_ROWS_PASS);
 }
 
-// The linear read's terms only (after bwd_dq_mfma); its LDS copy of S sets the occupancy.
-template <typename T, int D, int BLK>
-__global__ __launch_bounds__(BT) void bwd_rows_lin(HF_ROWS_ARGS) {
-  rows_body<T, D, BLK, true>(HF_ROWS_PASS);
-}
 #undef HF_ROWS_ARGS
 #undef HF_ROWS_PASS
 
@@ -476,335 +466,464 @@ __global__ __launch_bounds__(BT) void bwd_kv(
   }
 }
 
-// bf16 dq of the softmax path on MFMA (v_mfma_f32_16x16x32_bf16), one workgroup per
-// (head, 64-row query block), wave w owning queries 16w .. 16w + 15, whose Q and dO
-// rows stay in registers as B operands. Three passes over the selected key blocks:
-// A the row max of the scores S^T = K Q^T; B the sum l of exp2(S tau log2e - m) and
-// O^T += V^T P^T, giving lse and D = dO . O / l; C dP^T = V dO^T, dL^T = tau P^T (dP^T
-// - D) and dQ^T += K^T dL^T. The key order of the last two products comes from the
-// result layout of S^T (a lane holds keys 4g .. 4g + 3 of two 16-key tiles), so P^T
-// and dL^T are B operands in registers, split into bf16 hi and lo parts, and V^T and
-// K^T are read as A operands from transposed copies staged in LDS. Writes the softmax
-// part of dq and (lse, D) per row; the linear read's part is added by bwd_rows<LIN>.
-template <int D>
-__global__ __launch_bounds__(BT) void bwd_dq_mfma(
+// bf16 dq of the softmax path, staged as the forward attention kernel stages its tiles:
+// one workgroup per (head, 64-row query block), 2 waves x 32 query rows, the selected
+// blocks' K and V tiles loaded straight from global memory into LDS (16-byte global->LDS
+// loads, swizzled rows), XCD-remapped like the forward launch. The Q and dO rows of a
+// wave stay in registers as B operands. Two passes over the selected blocks:
+//   1. S^T = K Q^T and dP^T = V dO^T (K and V rows by ds_read_b128), then, online per
+//      query with a lazily moved reference max, l = sum exp2(s - m) and
+//      D' = sum exp2(s - m) dP: lse = m + log2 l and D = D' / l (= dO . o_swa);
+//   2. dP^T first (V rows; V(t+1) is then requested while K(t) is read), S^T, P =
+//      exp2(s tau log2e - lse), dL^T = tau P^T (dP^T - D) split into bf16 hi + lo as B
+//      operands in the key order of the S^T result layout, and dQ^T += K^T dL^T with K^T
+//      by the transposing LDS read (the forward's V^T addressing on the K tile).
+// Writes the softmax part of dq and (lse, D) per row; the linear read's part is added by
+// bwd_rows_lin_mfma.
+template <int D, bool SHORT>
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dq2(
     const bf16_t* __restrict__ q, int64_t n_q, int64_t q_hs, const bf16_t* __restrict__ kg,
     const bf16_t* __restrict__ vg, int64_t n_kv, int64_t kv_hs, const int32_t* __restrict__ sel,
-    int top_k, int nqb, int nkb, float scale, const bf16_t* __restrict__ dout, int64_t do_hs,
-    float* __restrict__ dq, int64_t dq_hs, float* __restrict__ rs, int64_t nq_cap) {
-  constexpr int BLK = 64, NKS = D / 32, NE = D / 16;
-  constexpr int RS = D + 8, TS = BLK + 8;
+    int top_k, int nqb, int nkb, int n_logical, float scale, const bf16_t* __restrict__ dout,
+    int64_t do_hs, float* __restrict__ dq, int64_t dq_hs, float* __restrict__ rs,
+    int64_t nq_cap) {
+  constexpr int BLK = 64, NW = 2, NQT = 2, NMT = 4, NET = D / 16, NKS = D / 32;
+  constexpr int CPR = D / 8, TCH = BLK * CPR, LPT = TCH / (NW * 64);
+  constexpr float kSlack = 8.f;  // the reference max moves when a score exceeds it by more
   typedef Mfma<bf16_t> M;
-  __shared__ __align__(16) bf16_t ks[BLK * RS];
-  __shared__ __align__(16) bf16_t vs[BLK * RS];
-  __shared__ __align__(16) bf16_t kt[D * TS];
-  __shared__ __align__(16) bf16_t vt[D * TS];
-  const int h = blockIdx.x / nqb, i = blockIdx.x % nqb;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  __shared__ uint4 lds_k[TCH];
+  __shared__ uint4 lds_v[TCH];
+  const int logical = xcd_remap(blockIdx.x, gridDim.x, n_logical);
+  if (logical < 0) return;
+  const int h = logical / nqb, i = logical % nqb;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, c = lane & 15;
-  const float sl2 = scale * kL2e;
-  const int64_t qrow = (int64_t)i * BLK + w * 16 + c;
-  const bool qvalid = qrow < n_q;
-  bf16x8 qop[NKS], dop[NKS];
-#pragma unroll
-  for (int s = 0; s < NKS; ++s) {
-    qop[s] = as_bf16x8(qvalid ? *reinterpret_cast<const uint4*>(q + (int64_t)h * q_hs + qrow * D +
-                                                                 32 * s + 8 * g)
-                              : zero4());
-    dop[s] = as_bf16x8(qvalid ? *reinterpret_cast<const uint4*>(dout + (int64_t)h * do_hs +
-                                                                 qrow * D + 32 * s + 8 * g)
-                              : zero4());
-  }
+  const bf16_t* qh = q + (int64_t)h * q_hs;
   const bf16_t* kh = kg + (int64_t)h * kv_hs;
   const bf16_t* vh = vg + (int64_t)h * kv_hs;
+  const bf16_t* doh = dout + (int64_t)h * do_hs;
   const int32_t* my_sel = sel + ((int64_t)h * nqb + i) * top_k;
+  const int64_t qrow0 = (int64_t)i * BLK + w * 32;
+  const float sl2 = scale * kL2e;
 
-  // Stage key block jb: K row-major (always), V row-major, K^T, V^T as asked.
-  auto stage = [&](int jb, bool v_rows, bool k_t, bool v_t) {
-    __syncthreads();  // every wave is done with the previous block's copies
-    for (int v = threadIdx.x; v < BLK * (D / 8); v += BT) {
-      const int r = v % BLK, ch = v / BLK;
-      const int64_t row = (int64_t)jb * BLK + r;
-      const bool ok = row < n_kv;
-      const uint4 a = ok ? *reinterpret_cast<const uint4*>(kh + row * D + ch * 8) : zero4();
-      *reinterpret_cast<uint4*>(ks + r * RS + ch * 8) = a;
-      if (k_t) {
+  // ---- tile staging (as the forward kernel) ----
+  constexpr int RPU = NW * 64 / CPR;
+  constexpr int NPAT = RPU % 16 == 0 ? 1 : 2;
+  uint32_t lpat[NPAT];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) kt[(ch * 8 + e) * TS + r] = (bf16_t)half16(a, e);
+  for (int u = 0; u < NPAT; ++u) {
+    const int P = (u * NW + w) * 64 + lane;
+    const int row = P / CPR, cc = (P % CPR) ^ swz<CPR>(row);
+    lpat[u] = (uint32_t)((row - u * RPU) * D + cc * 8) * 2u;
+  }
+  auto tile_row0 = [&](int jb) {
+    const int64_t r0 = (int64_t)jb * BLK;
+    return (!SHORT && r0 + BLK > n_kv) ? n_kv - BLK : r0;
+  };
+  auto issue_tile = [&](const bf16_t* src, int jb, const uint4* tile) {
+    const bf16_t* tb = src + (size_t)tile_row0(jb) * D;
+    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_offset(tile) + w * 64 * 16);
+#pragma unroll
+    for (int u = 0; u < LPT; ++u) {
+      const uint32_t off = lpat[u % NPAT];
+      if constexpr (!SHORT) {
+        lds_dma16(tb + u * RPU * D, off, base + u * NW * 64 * 16);
+      } else {
+        const uint32_t row_bytes = D * 2, row = u * RPU + off / row_bytes;
+        const uint32_t last = (uint32_t)(n_kv - 1 - tile_row0(jb));
+        lds_dma16(tb, (row <= last ? row : last) * row_bytes + off % row_bytes,
+                  base + u * NW * 64 * 16);
       }
-      if (v_rows || v_t) {
-        const uint4 b = ok ? *reinterpret_cast<const uint4*>(vh + row * D + ch * 8) : zero4();
-        if (v_rows) *reinterpret_cast<uint4*>(vs + r * RS + ch * 8) = b;
-        if (v_t) {
+    }
+  };
+  // keys of the tile that lie outside block jb (ragged last block): -inf
+  auto mask = [&](int jb, f32x4 (&st)[NMT][NQT]) {
+    const int64_t key0 = (int64_t)jb * BLK;
+    if (key0 + BLK > n_kv) {
+      const int valid = (int)(n_kv - key0);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) vt[(ch * 8 + e) * TS + r] = (bf16_t)half16(b, e);
+      for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int tr = mt * 16 + g * 4 + r;
+          const bool out = SHORT ? tr >= valid : tr < BLK - valid;
+#pragma unroll
+          for (int n = 0; n < NQT; ++n) st[mt][n][r] = out ? -INFINITY : st[mt][n][r];
         }
-      }
     }
-    __syncthreads();
-  };
-  // S^T tiles of the staged block (keys past the window: -inf), in log2 units.
-  auto scores = [&](int jb, f32x4 (&st)[4]) {
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < NKS; ++s)
-        a = M::mma(as_bf16x8(*reinterpret_cast<const uint4*>(ks + (16 * mt + c) * RS + 32 * s +
-                                                             8 * g)),
-                   qop[s], a);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t key = (int64_t)jb * BLK + 16 * mt + 4 * g + r;
-        st[mt][r] = key < n_kv ? a[r] * sl2 : -INFINITY;
-      }
-    }
-  };
-  // A operand of a transposed copy: row 16e + c, keys 32c2 + 4g + 0..3 and + 16.
-  auto tr_op = [&](const bf16_t* t, int e, int c2) {
-    const int o = (16 * e + c) * TS + 32 * c2 + 4 * g;
-    const uint2 a0 = *reinterpret_cast<const uint2*>(t + o);
-    const uint2 a1 = *reinterpret_cast<const uint2*>(t + o + 16);
-    return as_bf16x8(make_uint4(a0.x, a0.y, a1.x, a1.y));
   };
 
-  // ---- pass A: row max ----
-  float m = -INFINITY;
-  for (int t = 0; t < top_k; ++t) {
-    const int jb = clamp_block(my_sel[t], nkb);
-    stage(jb, false, false, false);
-    f32x4 st[4];
-    scores(jb, st);
+  int jb = clamp_block(my_sel[0], nkb);
+  issue_tile(vh, jb, lds_v);
+  issue_tile(kh, jb, lds_k);
+
+  // Q and dO operands: lane holds row 16n + c, features 32s + 8g .. + 8
+  bf16x8 qop[NQT][NKS], dop[NQT][NKS];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-      m = fmaxf(m, fmaxf(fmaxf(st[mt][0], st[mt][1]), fmaxf(st[mt][2], st[mt][3])));
+  for (int n = 0; n < NQT; ++n) {
+    const int64_t r = qrow0 + n * 16 + c;
+#pragma unroll
+    for (int s2 = 0; s2 < NKS; ++s2) {
+      qop[n][s2] = as_bf16x8(ld16(qh + r * D + s2 * 32 + g * 8, r < n_q));
+      dop[n][s2] = as_bf16x8(ld16(doh + r * D + s2 * 32 + g * 8, r < n_q));
+    }
   }
-  m = max_over_groups(m);  // finite: every block holds a key of the window
+  // LDS byte addresses: K / V rows (key tile mt adds mt * kRow16), K^T (chunk c2 adds
+  // 2 c2 kRow16, its second half one more kRow16)
+  constexpr uint32_t kRow16 = 16 * CPR * 16;
+  uint32_t kaddr[NKS], vaddr[NKS], taddr[NET];
+#pragma unroll
+  for (int s2 = 0; s2 < NKS; ++s2) {
+    const uint32_t o = (uint32_t)(c * CPR + ((s2 * 4 + g) ^ swz<CPR>(c))) * 16u;
+    kaddr[s2] = lds_offset(lds_k) + o;
+    vaddr[s2] = lds_offset(lds_v) + o;
+  }
+  {
+    const int rv = 4 * g + ((lane & 15) >> 2), pp = lane & 3;
+#pragma unroll
+    for (int et = 0; et < NET; ++et)
+      taddr[et] = lds_offset(lds_k) +
+                  (uint32_t)(rv * CPR + ((2 * et + (pp >> 1)) ^ swz<CPR>(rv))) * 16u + (pp & 1) * 8u;
+  }
+  // products of one tile: st (K rows x Q) or dp (V rows x dO)
+  auto rows_x = [&](const uint32_t (&addr)[NKS], const bf16x8 (&op)[NQT][NKS],
+                    f32x4 (&out)[NMT][NQT]) {
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+      for (int n = 0; n < NQT; ++n) out[mt][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s2 = 0; s2 < NKS; ++s2) {
+      bf16x8 a[NMT];
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt) a[mt] = as_bf16x8(lds_ld16(addr[s2] + mt * kRow16));
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+        for (int n = 0; n < NQT; ++n) out[mt][n] = M::mma(a[mt], op[n][s2], out[mt][n]);
+    }
+  };
 
-  // ---- pass B: l and O^T = V^T P^T at the fixed max ----
-  float lsum = 0.f;
-  f32x4 oT[NE];
+  // ---- pass 1: lse and D ----
+  float m_run[NQT], l_part[NQT], d_part[NQT];
 #pragma unroll
-  for (int e = 0; e < NE; ++e) oT[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int n = 0; n < NQT; ++n) m_run[n] = l_part[n] = d_part[n] = 0.f;
   for (int t = 0; t < top_k; ++t) {
-    const int jb = clamp_block(my_sel[t], nkb);
-    stage(jb, false, false, true);
-    f32x4 st[4];
-    scores(jb, st);
-    float p[4][4];
+    const bool more = t + 1 < top_k;
+    // the next block, or pass 2's first block after the last one
+    const int jb_next = clamp_block(my_sel[more ? t + 1 : 0], nkb);
+    wait_vmem<0>();
+    lds_barrier();
+    f32x4 st[NMT][NQT], dp[NMT][NQT];
+    rows_x(kaddr, qop, st);
+    rows_x(vaddr, dop, dp);
+    lds_barrier();  // every wave has read both tiles
+    issue_tile(vh, jb_next, lds_v);
+    issue_tile(kh, jb_next, lds_k);
+    mask(jb, st);
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int n = 0; n < NQT; ++n) {
+      float mx = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        p[mt][r] = exp2f(st[mt][r] - m);
-        lsum += p[mt][r];
+      for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          st[mt][n][r] *= sl2;
+          mx = fmaxf(mx, st[mt][n][r]);
+        }
+      if (t == 0) m_run[n] = max_over_groups(mx);  // finite: a block holds a window key
+      if (__builtin_amdgcn_ballot_w64(mx - m_run[n] > kSlack)) {  // wave-uniform
+        const float d_blk = max_over_groups(mx) - m_run[n];
+        const float shift = d_blk > kSlack ? d_blk : 0.f;
+        const float a = exp2f(-shift);
+        m_run[n] += shift;
+        l_part[n] *= a;
+        d_part[n] *= a;
+      }
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float e = exp2f(st[mt][n][r] - m_run[n]);
+          l_part[n] += e;
+          d_part[n] += e * dp[mt][n][r];
+        }
+    }
+    jb = jb_next;
+  }
+  float lse2[NQT], Dr[NQT];
+#pragma unroll
+  for (int n = 0; n < NQT; ++n) {
+    const float l = sum_over_groups(l_part[n]);
+    lse2[n] = m_run[n] + log2f(l);
+    Dr[n] = sum_over_groups(d_part[n]) / l;
+  }
+
+  // ---- pass 2: dQ^T += K^T dL^T ----
+  f32x4 gT[NET][NQT];
+#pragma unroll
+  for (int e = 0; e < NET; ++e)
+#pragma unroll
+    for (int n = 0; n < NQT; ++n) gT[e][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < top_k; ++t) {
+    const bool more = t + 1 < top_k;
+    const int jb_next = more ? clamp_block(my_sel[t + 1], nkb) : 0;
+    wait_vmem<LPT>();  // V(t) has landed (K(t) may be in flight)
+    lds_barrier();
+    f32x4 dp[NMT][NQT];
+    rows_x(vaddr, dop, dp);
+    lds_barrier();  // every wave has read V(t)
+    if (more) {
+      issue_tile(vh, jb_next, lds_v);
+      wait_vmem<LPT>();  // K(t) has landed (V(t+1) may be in flight)
+    } else {
+      wait_vmem<0>();
+    }
+    lds_barrier();
+    f32x4 st[NMT][NQT];
+    rows_x(kaddr, qop, st);
+    mask(jb, st);
+    // dL in the key order of the result layout, split into bf16 hi + lo
+    bf16x8 lh[2][NQT], ll[2][NQT];
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+      for (int n = 0; n < NQT; ++n) {
+        float lv[8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          lv[r] = scale * exp2f(st[2 * c2][n][r] * sl2 - lse2[n]) * (dp[2 * c2][n][r] - Dr[n]);
+          lv[4 + r] =
+              scale * exp2f(st[2 * c2 + 1][n][r] * sl2 - lse2[n]) * (dp[2 * c2 + 1][n][r] - Dr[n]);
+        }
+        split_bf16x8(lv, lh[c2][n], ll[c2][n]);
       }
 #pragma unroll
     for (int c2 = 0; c2 < 2; ++c2) {
-      float pv[8];
+      bf16x8 kt[NET];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        pv[r] = p[2 * c2][r];
-        pv[4 + r] = p[2 * c2 + 1][r];
+      for (int et = 0; et < NET; ++et) {
+        const v4i16 lo = lds_tr8(taddr[et] + 2 * c2 * kRow16);
+        const v4i16 hi = lds_tr8(taddr[et] + (2 * c2 + 1) * kRow16);
+        kt[et] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
-      bf16x8 ph, pl;
-      split_bf16x8(pv, ph, pl);
 #pragma unroll
-      for (int e = 0; e < NE; ++e) {
-        const bf16x8 a = tr_op(vt, e, c2);
-        oT[e] = M::mma(a, ph, oT[e]);
-        oT[e] = M::mma(a, pl, oT[e]);
-      }
+      for (int et = 0; et < NET; ++et)
+#pragma unroll
+        for (int n = 0; n < NQT; ++n) {
+          gT[et][n] = M::mma(kt[et], lh[c2][n], gT[et][n]);
+          gT[et][n] = M::mma(kt[et], ll[c2][n], gT[et][n]);
+        }
     }
+    lds_barrier();  // every wave has read K(t)
+    if (more) issue_tile(kh, jb_next, lds_k);
+    jb = jb_next;
   }
-  const float l = sum_over_groups(lsum);
-  const float lse2 = m + log2f(l);
-  float dpart = 0.f;
-  if (qvalid) {
-    const bf16_t* dr = dout + (int64_t)h * do_hs + qrow * D;
+  // lane holds dq[row 16n + c][16 et + 4g .. + 3]
 #pragma unroll
-    for (int e = 0; e < NE; ++e) {
-      const uint2 u = *reinterpret_cast<const uint2*>(dr + 16 * e + 4 * g);
-      dpart += bf16_to_f32(u.x & 0xffffu) * oT[e][0] + bf16_to_f32(u.x >> 16) * oT[e][1] +
-               bf16_to_f32(u.y & 0xffffu) * oT[e][2] + bf16_to_f32(u.y >> 16) * oT[e][3];
-    }
-  }
-  const float Dr = sum_over_groups(dpart) / l;
-
-  // ---- pass C: dQ^T += K^T dL^T ----
-  f32x4 gT[NE];
+  for (int n = 0; n < NQT; ++n) {
+    const int64_t r = qrow0 + n * 16 + c;
+    if (r >= n_q) continue;
+    float* o = dq + (int64_t)h * dq_hs + r * D;
 #pragma unroll
-  for (int e = 0; e < NE; ++e) gT[e] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int t = 0; t < top_k; ++t) {
-    const int jb = clamp_block(my_sel[t], nkb);
-    stage(jb, true, true, false);
-    f32x4 st[4];
-    scores(jb, st);
-    float dl[4][4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < NKS; ++s)
-        a = M::mma(as_bf16x8(*reinterpret_cast<const uint4*>(vs + (16 * mt + c) * RS + 32 * s +
-                                                             8 * g)),
-                   dop[s], a);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) dl[mt][r] = scale * exp2f(st[mt][r] - lse2) * (a[r] - Dr);
-    }
-#pragma unroll
-    for (int c2 = 0; c2 < 2; ++c2) {
-      float lv[8];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        lv[r] = dl[2 * c2][r];
-        lv[4 + r] = dl[2 * c2 + 1][r];
-      }
-      bf16x8 lh, ll;
-      split_bf16x8(lv, lh, ll);
-#pragma unroll
-      for (int e = 0; e < NE; ++e) {
-        const bf16x8 a = tr_op(kt, e, c2);
-        gT[e] = M::mma(a, lh, gT[e]);
-        gT[e] = M::mma(a, ll, gT[e]);
-      }
-    }
-  }
-  if (qvalid) {
-    float* o = dq + (int64_t)h * dq_hs + qrow * D;
-#pragma unroll
-    for (int e = 0; e < NE; ++e)
-      *reinterpret_cast<float4*>(o + 16 * e + 4 * g) = make_float4(gT[e][0], gT[e][1], gT[e][2],
-                                                                    gT[e][3]);
+    for (int et = 0; et < NET; ++et)
+      *reinterpret_cast<float4*>(o + 16 * et + 4 * g) =
+          make_float4(gT[et][n][0], gT[et][n][1], gT[et][n][2], gT[et][n][3]);
     if (g == 0) {
-      float* st = rs + ((int64_t)h * nq_cap + qrow) * 4;
-      st[0] = lse2;
-      st[1] = Dr;
+      float* st = rs + ((int64_t)h * nq_cap + r) * 4;
+      st[0] = lse2[n];
+      st[1] = Dr[n];
     }
   }
 }
 
-// bf16 dk and dv on MFMA (v_mfma_f32_16x16x32_bf16), one workgroup per (head, 64-key
-// block), wave w owning keys 16w .. 16w + 15, over the query blocks that selected the
-// block. Per 64-row query block: S = Q K^T and dP = dO V^T (K and V of the wave's keys
-// stay in registers as the B operands), P = exp2(S tau log2e - lse), dL = tau P (dP -
-// D); then dV^T += dO^T P and dK^T += Q^T dL. The contraction over queries takes its
-// k order from the result layout of S (a lane holds queries 4g .. 4g + 3 of two
-// 16-query tiles), so P and dL become B operands in registers, split into bf16 hi and
-// lo parts (Q and dO are exact bf16, so the products keep ~fp32 accuracy), while dO^T
-// and Q^T are read as A operands from transposed copies staged in LDS.
+// bf16 dk and dv with the forward kernel's tile staging: one workgroup per (head, 64-key
+// block), 4 waves x 16 keys (K and V of the wave's keys stay in registers as B
+// operands), over the query blocks that selected the block. Per query block its Q and
+// dO tiles are loaded straight from global memory into LDS (16-byte global->LDS loads,
+// swizzled rows; rows past the chunk repeat its last row and get weight 0). dP = dO V^T
+// (dO rows by ds_read_b128) comes first, then S = Q K^T (Q rows), P = exp2(s tau log2e
+// - lse), dL = tau P (dP - D); P and dL become B operands (bf16 hi + lo) in the query
+// order of the result layout; dV^T += dO^T P and dK^T += Q^T dL with dO^T and Q^T by the
+// transposing LDS read. The dO tile is released (and the next one requested) before the
+// dK products, the Q tile after them.
 template <int D>
-__global__ __launch_bounds__(BT) void bwd_kv_mfma(
+__global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2))) void bwd_kv2(
     const bf16_t* __restrict__ q, int64_t n_q, int64_t q_hs, const bf16_t* __restrict__ kg,
     const bf16_t* __restrict__ vg, int64_t n_kv, int64_t kv_hs, int nkb, float scale,
     const bf16_t* __restrict__ dout, int64_t do_hs, const float* __restrict__ rs, int64_t nq_cap,
     const int32_t* __restrict__ cnt, const int32_t* __restrict__ list, int nqb_cap,
     float* __restrict__ dk, float* __restrict__ dv, int64_t dkv_hs) {
-  constexpr int BLK = 64, NKS = D / 32, NE = D / 16;
-  constexpr int RS = D + 8;    // row stride of the row-major copies (bf16)
-  constexpr int TS = BLK + 8;  // row stride of the transposed copies (bf16)
+  constexpr int BLK = 64, NW = 4, NMQ = 4, NET = D / 16, NKS = D / 32;
+  constexpr int CPR = D / 8, TCH = BLK * CPR, LPT = TCH / (NW * 64);
   typedef Mfma<bf16_t> M;
-  __shared__ __align__(16) bf16_t qs[BLK * RS];
-  __shared__ __align__(16) bf16_t dos[BLK * RS];
-  __shared__ __align__(16) bf16_t qt[D * TS];
-  __shared__ __align__(16) bf16_t dot_[D * TS];
-  __shared__ float tst[BLK * 2];
+  __shared__ uint4 lds_q[TCH];
+  __shared__ uint4 lds_o[TCH];
+  __shared__ uint4 lds_st[NW][BLK];  // per wave: the block's rows of the statistics
   const int h = blockIdx.x / nkb, jb = blockIdx.x % nkb;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, c = lane & 15;
   const float sl2 = scale * kL2e;
   const int64_t key = (int64_t)jb * BLK + w * 16 + c;
   const bool kvalid = key < n_kv;
   bf16x8 kop[NKS], vop[NKS];
 #pragma unroll
-  for (int s = 0; s < NKS; ++s) {
-    const int64_t off = (int64_t)h * kv_hs + key * D + 32 * s + 8 * g;
-    kop[s] = as_bf16x8(kvalid ? *reinterpret_cast<const uint4*>(kg + off) : zero4());
-    vop[s] = as_bf16x8(kvalid ? *reinterpret_cast<const uint4*>(vg + off) : zero4());
+  for (int s2 = 0; s2 < NKS; ++s2) {
+    const int64_t off = (int64_t)h * kv_hs + key * D + 32 * s2 + 8 * g;
+    kop[s2] = as_bf16x8(ld16(kg + off, kvalid));
+    vop[s2] = as_bf16x8(ld16(vg + off, kvalid));
   }
-  f32x4 dvT[NE], dkT[NE];
-#pragma unroll
-  for (int e = 0; e < NE; ++e) dvT[e] = dkT[e] = f32x4{0.f, 0.f, 0.f, 0.f};
   const bf16_t* qh = q + (int64_t)h * q_hs;
   const bf16_t* doh = dout + (int64_t)h * do_hs;
   const int64_t slot = (int64_t)h * nkb + jb;
   const int n_sel = cnt[slot];
-  for (int x = 0; x < n_sel; ++x) {
-    const int64_t q0 = (int64_t)list[slot * nqb_cap + x] * BLK;
-    __syncthreads();  // every wave is done with the previous query block
-    for (int v = threadIdx.x; v < BLK * (D / 8); v += BT) {
-      const int r = v % BLK, ch = v / BLK;  // consecutive lanes take consecutive rows
-      const int64_t row = q0 + r;
-      const uint4 a = row < n_q ? *reinterpret_cast<const uint4*>(qh + row * D + ch * 8) : zero4();
-      const uint4 b =
-          row < n_q ? *reinterpret_cast<const uint4*>(doh + row * D + ch * 8) : zero4();
-      *reinterpret_cast<uint4*>(qs + r * RS + ch * 8) = a;
-      *reinterpret_cast<uint4*>(dos + r * RS + ch * 8) = b;
+  const int32_t* my_list = list + slot * nqb_cap;
+
+  // tile loads: load u of this wave fills LDS chunks (u NW + w) 64 + lane with chunk
+  // (row, slot ^ swz(row)); rows past the chunk read its last row
+  constexpr int RPU = NW * 64 / CPR;
+  uint32_t lrow[LPT], lcol[LPT];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        qt[(ch * 8 + i) * TS + r] = (bf16_t)half16(a, i);
-        dot_[(ch * 8 + i) * TS + r] = (bf16_t)half16(b, i);
-      }
+  for (int u = 0; u < LPT; ++u) {
+    const int P = (u * NW + w) * 64 + lane;
+    const int row = P / CPR, cc = (P % CPR) ^ swz<CPR>(row);
+    lrow[u] = (uint32_t)row;
+    lcol[u] = (uint32_t)cc * 16u;
+  }
+  static_assert(RPU >= 1, "rows per load");
+  auto issue = [&](const bf16_t* src, int64_t q0, const uint4* tile) {
+    const uint32_t last = (uint32_t)(n_q - 1 - q0);
+    const bf16_t* tb = src + (size_t)q0 * D;
+    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_offset(tile) + w * 64 * 16);
+#pragma unroll
+    for (int u = 0; u < LPT; ++u) {
+      const uint32_t row = lrow[u] <= last ? lrow[u] : last;
+      lds_dma16(tb, row * (uint32_t)(D * 2) + lcol[u], base + u * NW * 64 * 16);
     }
-    for (int e = threadIdx.x; e < BLK; e += BT) {
-      const int64_t row = q0 + e;
-      const float* st = rs + ((int64_t)h * nq_cap + (row < n_q ? row : 0)) * 4;
-      tst[2 * e] = row < n_q ? st[0] : INFINITY;  // rows past the chunk: weight 0
-      tst[2 * e + 1] = row < n_q ? st[1] : 0.f;
+  };
+  constexpr uint32_t kRow16 = 16 * CPR * 16;
+  uint32_t qaddr[NKS], oaddr[NKS], tq[NET], to[NET];
+#pragma unroll
+  for (int s2 = 0; s2 < NKS; ++s2) {
+    const uint32_t o = (uint32_t)(c * CPR + ((s2 * 4 + g) ^ swz<CPR>(c))) * 16u;
+    qaddr[s2] = lds_offset(lds_q) + o;
+    oaddr[s2] = lds_offset(lds_o) + o;
+  }
+  {
+    const int rv = 4 * g + ((lane & 15) >> 2), pp = lane & 3;
+#pragma unroll
+    for (int et = 0; et < NET; ++et) {
+      const uint32_t o = (uint32_t)(rv * CPR + ((2 * et + (pp >> 1)) ^ swz<CPR>(rv))) * 16u +
+                         (pp & 1) * 8u;
+      tq[et] = lds_offset(lds_q) + o;
+      to[et] = lds_offset(lds_o) + o;
     }
-    __syncthreads();
-    float P[4][4], L[4][4];
+  }
+  auto rows_x = [&](const uint32_t (&addr)[NKS], const bf16x8 (&op)[NKS], f32x4 (&out)[NMQ]) {
 #pragma unroll
-    for (int nq = 0; nq < 4; ++nq) {
-      f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f}, pa = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int m = 0; m < NMQ; ++m) out[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < NKS; ++s) {
-        const int o = (16 * nq + c) * RS + 32 * s + 8 * g;
-        sa = M::mma(as_bf16x8(*reinterpret_cast<const uint4*>(qs + o)), kop[s], sa);
-        pa = M::mma(as_bf16x8(*reinterpret_cast<const uint4*>(dos + o)), vop[s], pa);
-      }
+    for (int s2 = 0; s2 < NKS; ++s2) {
+      bf16x8 a[NMQ];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int ql = 16 * nq + 4 * g + r;
-        const float p = exp2f(sa[r] * sl2 - tst[2 * ql]);
-        P[nq][r] = p;
-        L[nq][r] = scale * p * (pa[r] - tst[2 * ql + 1]);
-      }
+      for (int m = 0; m < NMQ; ++m) a[m] = as_bf16x8(lds_ld16(addr[s2] + m * kRow16));
+#pragma unroll
+      for (int m = 0; m < NMQ; ++m) out[m] = M::mma(a[m], op[s2], out[m]);
     }
+  };
+  // statistics rows (16 bytes each) of query rows q0 .. q0 + 63 into this wave's copy
+  const float* rsh = rs + (int64_t)h * nq_cap * 4;
+  const uint32_t st_base = __builtin_amdgcn_readfirstlane(lds_offset(&lds_st[w][0]));
+  auto issue_st = [&](int64_t q0) {
+    const uint32_t last = (uint32_t)(n_q - 1 - q0);
+    const uint32_t row = (uint32_t)lane <= last ? (uint32_t)lane : last;
+    lds_dma16(rsh + q0 * 4, row * 16u, st_base);
+  };
+  auto tr_ops = [&](const uint32_t (&addr)[NET], int c2, bf16x8 (&out)[NET]) {
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      float pv[8], lv[8];
+    for (int et = 0; et < NET; ++et) {
+      const v4i16 lo = lds_tr8(addr[et] + 2 * c2 * kRow16);
+      const v4i16 hi = lds_tr8(addr[et] + (2 * c2 + 1) * kRow16);
+      out[et] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  };
+
+  f32x4 dvT[NET], dkT[NET];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pv[i] = P[2 * kk][i];
-        pv[4 + i] = P[2 * kk + 1][i];
-        lv[i] = L[2 * kk][i];
-        lv[4 + i] = L[2 * kk + 1][i];
+  for (int e = 0; e < NET; ++e) dvT[e] = dkT[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (n_sel > 0) {
+    int64_t q0 = (int64_t)my_list[0] * BLK;
+    issue(doh, q0, lds_o);
+    issue_st(q0);
+    issue(qh, q0, lds_q);
+    for (int x = 0; x < n_sel; ++x) {
+      const bool more = x + 1 < n_sel;
+      const int64_t q0n = more ? (int64_t)my_list[x + 1] * BLK : 0;
+      const int n_valid = n_q - q0 < BLK ? (int)(n_q - q0) : BLK;  // rows past: weight 0
+      wait_vmem<LPT>();  // dO(x) and the statistics have landed (Q(x) may be in flight)
+      lds_barrier();
+      f32x4 dp[NMQ];
+      rows_x(oaddr, vop, dp);
+      wait_vmem<0>();  // Q(x)
+      lds_barrier();
+      f32x4 sc[NMQ];
+      rows_x(qaddr, kop, sc);
+      // P and dL in the query order of the result layout (lane: queries 4g .. 4g + 3 of
+      // tiles 2c2 and 2c2 + 1, key c), split into bf16 hi + lo
+      bf16x8 ph[2], pl[2], lh[2], ll[2];
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        float pv[8], lv[8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf) {
+            const int m = 2 * c2 + hf, ql = 16 * m + 4 * g + r;
+            const float2 st = lds_ld8f(st_base + ql * 16u);
+            const float p = ql < n_valid ? exp2f(sc[m][r] * sl2 - st.x) : 0.f;
+            pv[4 * hf + r] = p;
+            lv[4 * hf + r] = scale * p * (dp[m][r] - st.y);
+          }
+        split_bf16x8(pv, ph[c2], pl[c2]);
+        split_bf16x8(lv, lh[c2], ll[c2]);
       }
-      bf16x8 ph, pl, lh, ll;
-      split_bf16x8(pv, ph, pl);
-      split_bf16x8(lv, lh, ll);
 #pragma unroll
-      for (int e = 0; e < NE; ++e) {
-        const int o = (16 * e + c) * TS + 32 * kk + 4 * g;
-        const uint2 d0 = *reinterpret_cast<const uint2*>(dot_ + o);
-        const uint2 d1 = *reinterpret_cast<const uint2*>(dot_ + o + 16);
-        const uint2 q0v = *reinterpret_cast<const uint2*>(qt + o);
-        const uint2 q1v = *reinterpret_cast<const uint2*>(qt + o + 16);
-        const bf16x8 ado = as_bf16x8(make_uint4(d0.x, d0.y, d1.x, d1.y));
-        const bf16x8 aq = as_bf16x8(make_uint4(q0v.x, q0v.y, q1v.x, q1v.y));
-        dvT[e] = M::mma(ado, ph, dvT[e]);
-        dvT[e] = M::mma(ado, pl, dvT[e]);
-        dkT[e] = M::mma(aq, lh, dkT[e]);
-        dkT[e] = M::mma(aq, ll, dkT[e]);
+      for (int c2 = 0; c2 < 2; ++c2) {
+        bf16x8 a[NET];
+        tr_ops(to, c2, a);
+#pragma unroll
+        for (int et = 0; et < NET; ++et) {
+          dvT[et] = M::mma(a[et], ph[c2], dvT[et]);
+          dvT[et] = M::mma(a[et], pl[c2], dvT[et]);
+        }
       }
+      lds_barrier();  // every wave has read dO(x)
+      if (more) {
+        issue(doh, q0n, lds_o);
+        issue_st(q0n);
+      }
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        bf16x8 a[NET];
+        tr_ops(tq, c2, a);
+#pragma unroll
+        for (int et = 0; et < NET; ++et) {
+          dkT[et] = M::mma(a[et], lh[c2], dkT[et]);
+          dkT[et] = M::mma(a[et], ll[c2], dkT[et]);
+        }
+      }
+      lds_barrier();  // every wave has read Q(x)
+      if (more) issue(qh, q0n, lds_q);
+      q0 = q0n;
     }
   }
   if (kvalid) {
     float* pk = dk + (int64_t)h * dkv_hs + key * D;
     float* pv = dv + (int64_t)h * dkv_hs + key * D;
 #pragma unroll
-    for (int e = 0; e < NE; ++e) {
+    for (int e = 0; e < NET; ++e) {
       *reinterpret_cast<float4*>(pk + 16 * e + 4 * g) =
           make_float4(dkT[e][0], dkT[e][1], dkT[e][2], dkT[e][3]);
       *reinterpret_cast<float4*>(pv + 16 * e + 4 * g) =
@@ -1300,10 +1419,14 @@ hipError_t run_attend_bwd(const BwdArgs& a, int stage, hipStream_t s) {
     bwd_inv_sel<<<(unsigned)inv_n, 256, 0, s>>>(a.sel, nqb, nkb, a.top_k, a.inv_cnt,
                                                  a.inv_list, a.nqb_cap);
   if (stage == 1 && std::is_same<T, bf16_t>::value && BLK == 64) {
-    bwd_dq_mfma<D><<<(unsigned)(a.heads * nqb), BT, 0, s>>>(
-        static_cast<const bf16_t*>(a.q), a.n_q, a.q_hs, static_cast<const bf16_t*>(a.k),
-        static_cast<const bf16_t*>(a.v), a.n_kv, a.kv_hs, a.sel, a.top_k, nqb, nkb, a.scale,
-        static_cast<const bf16_t*>(a.dout), a.do_hs, a.dq, a.dq_hs, a.rowstats, a.nq_cap);
+    const int n_logical = a.heads * nqb;
+#define HF_DQ2(SHORT)                                                                          \
+  bwd_dq2<D, SHORT><<<(unsigned)((n_logical + 7) / 8 * 8), 128, 0, s>>>(                       \
+      static_cast<const bf16_t*>(a.q), a.n_q, a.q_hs, static_cast<const bf16_t*>(a.k),         \
+      static_cast<const bf16_t*>(a.v), a.n_kv, a.kv_hs, a.sel, a.top_k, nqb, nkb, n_logical,     \
+      a.scale, static_cast<const bf16_t*>(a.dout), a.do_hs, a.dq, a.dq_hs, a.rowstats, a.nq_cap)
+    if (a.n_kv < 64) HF_DQ2(true); else HF_DQ2(false);
+#undef HF_DQ2
     bwd_rows_lin_mfma<D><<<(unsigned)(a.heads * nqb), BT, 0, s>>>(
         static_cast<const bf16_t*>(a.q), a.n_q, a.q_hs, a.s_split, a.z, a.eps,
         static_cast<const bf16_t*>(a.dout), a.do_hs, a.dq, a.dq_hs, a.rowstats, a.nq_cap, nqb);
@@ -1313,7 +1436,7 @@ hipError_t run_attend_bwd(const BwdArgs& a, int stage, hipStream_t s) {
         static_cast<const T*>(a.v), a.n_kv, a.kv_hs, a.sel, a.top_k, nqb, nkb, a.S, a.z, a.eps,
         a.scale, static_cast<const T*>(a.dout), a.do_hs, a.dq, a.dq_hs, a.rowstats, a.nq_cap);
   if (stage == 2 && std::is_same<T, bf16_t>::value && BLK == 64)
-    bwd_kv_mfma<D><<<(unsigned)(a.heads * nkb), BT, 0, s>>>(
+    bwd_kv2<D><<<(unsigned)(a.heads * nkb), BT, 0, s>>>(
         static_cast<const bf16_t*>(a.q), a.n_q, a.q_hs, static_cast<const bf16_t*>(a.k),
         static_cast<const bf16_t*>(a.v), a.n_kv, a.kv_hs, nkb, a.scale,
         static_cast<const bf16_t*>(a.dout), a.do_hs, a.rowstats, a.nq_cap, a.inv_cnt, a.inv_list,

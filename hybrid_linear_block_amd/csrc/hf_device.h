@@ -159,10 +159,28 @@ __device__ __forceinline__ uint4 lds_ld16(uint32_t byte_off) {
       *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>((size_t)byte_off);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float2 lds_ld8f(uint32_t byte_off) {
+  const f32x2_t v =
+      *reinterpret_cast<const __attribute__((address_space(3))) f32x2_t*>((size_t)byte_off);
+  return make_float2(v.x, v.y);
+}
 __device__ __forceinline__ v4i16 lds_tr8(uint32_t byte_off) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)((size_t)byte_off));
 }
 
+
+// Swizzle of the 16-byte chunks of a tile row in LDS (64-row K/V tiles, rows of
+// CPR chunks): chunk cc of row r lives in slot cc ^ swz(r). Chosen (as a linear map
+// over GF(2) of row bits 0..3) so that both ds_read_b128 operand reads (lane (g, c)
+// reads chunk 4s + g of row c) and the transposing reads (8 rows x one aligned chunk
+// pair per half-wave) are free of bank conflicts; with 128-byte rows (CPR = 8) two
+// rows share the 64 banks, so swz has 3 bits.
+template <int CPR>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (CPR == 16) return ((r & 1) << 3) ^ (r & 6) ^ (((r >> 3) & 1) * 5);
+  else return (r & 6) ^ (((r >> 3) & 1) * 5);
+}
 
 // Wait until at most N vector-memory operations of this wave are in flight.
 template <int N>

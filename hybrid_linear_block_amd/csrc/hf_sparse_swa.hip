@@ -62,11 +62,7 @@ struct SwaSmem;
 // (over GF(2)) swizzles below were chosen so that both reads are conflict-free, as
 // measured with the LDS bank-conflict counter on patterns of exactly these reads.
 // With 128-byte rows (CPR = 8) two rows share the 64 banks, so swz has 3 bits.
-template <int CPR>
-__device__ __forceinline__ int swz(int r) {
-  if constexpr (CPR == 16) return ((r & 1) << 3) ^ (r & 6) ^ (((r >> 3) & 1) * 5);
-  else return (r & 6) ^ (((r >> 3) & 1) * 5);
-}
+// (swz<CPR>, in hf_device.h, is that swizzle.)
 template <int D, int BLK>
 struct SwaSmem<bf16_t, D, BLK> {
   uint4 k[BLK * D / 8];

@@ -88,7 +88,7 @@ __device__ __forceinline__ uint4 narrow16(const float* v) {
 // in order, and the lanes' totals are combined with lane exchanges in a fixed tree
 // (every lane ends with the same sum). A key block's group sums can come from, and
 // go to, a cache of 8-row sums (KeyCache), which gives the same sums bit for bit.
-template <typename T, int D>
+template <typename T, int D, bool ROPE>
 __device__ __forceinline__ void pool_wave(
     int wid, const T* __restrict__ q, int64_t n_q, int64_t q_hs, const T* __restrict__ k,
     int64_t n_kv, int64_t kv_hs, int block, int nqb, int nkb, int heads,
@@ -168,9 +168,10 @@ __device__ __forceinline__ void pool_wave(
 #pragma unroll
       for (int e = 0; e < VEC; ++e) g8[e] = 0.f;
       const int64_t grow0 = r0 + 8 * (rg + RPI * i);  // the group's first row
-      const bool rot = rope.cs != nullptr && cc * VEC < 2 * rope.half && grow0 < r1;
+      const bool rot = ROPE && cc * VEC < 2 * rope.half && grow0 < r1;
       GroupAngles<VEC> ang;
-      if (rot) ang = group_angles<VEC>(rope, cc * VEC / 2, is_q ? rope.q_row0 + grow0 : grow0);
+      if constexpr (ROPE)
+        if (rot) ang = group_angles<VEC>(rope, cc * VEC / 2, is_q ? rope.q_row0 + grow0 : grow0);
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
         float v[VEC];
@@ -181,7 +182,7 @@ __device__ __forceinline__ void pool_wave(
 #pragma unroll
           for (int e = 0; e < VEC; ++e) v[e] = __uint_as_float(word(x[i][r], e));
         }
-        if (rope.cs != nullptr) {  // wave-uniform
+        if constexpr (ROPE) {
           const int64_t row = grow0 + r;
           if (row < r1) {
             if (rot) rope_row<VEC>(v, ang, r);
@@ -217,12 +218,12 @@ __device__ __forceinline__ void pool_wave(
   }
 }
 
-template <typename T, int D>
+template <typename T, int D, bool ROPE>
 __global__ __launch_bounds__(POOL_THREADS) void block_pool(
     const T* __restrict__ q, int64_t n_q, int64_t q_hs, const T* __restrict__ k, int64_t n_kv,
     int64_t kv_hs, int block, int nqb, int nkb, int heads, float* __restrict__ pooled_q,
     float* __restrict__ pooled_k, int nqb_cap, int nkb_cap, KeyCache kc, Rope rope, Ragged rg) {
-  pool_wave<T, D>(blockIdx.x * (POOL_THREADS / 64) + (threadIdx.x >> 6), q, n_q, q_hs, k, n_kv,
+  pool_wave<T, D, ROPE>(blockIdx.x * (POOL_THREADS / 64) + (threadIdx.x >> 6), q, n_q, q_hs, k, n_kv,
                   kv_hs, block, nqb, nkb, heads, pooled_q, pooled_k, nqb_cap, nkb_cap, kc, rope,
                   rg);
 }
@@ -233,7 +234,7 @@ __global__ __launch_bounds__(POOL_THREADS) void block_pool(
 // memory, so they share the launch (and its ramp) instead of running one after
 // the other. The absorb workgroups come first, so that they are spread over the
 // compute units before the pooling fills the rest.
-template <typename T, int D>
+template <typename T, int D, bool ROPE>
 __global__ __launch_bounds__((absorb::threads<T, D>())) void absorb_and_pool(
     const T* __restrict__ kev, const T* __restrict__ vev, int64_t n_ev, int64_t ev_hs, int tps,
     int n_split, float* __restrict__ partials, int n_abs, const T* __restrict__ q, int64_t n_q,
@@ -251,7 +252,7 @@ __global__ __launch_bounds__((absorb::threads<T, D>())) void absorb_and_pool(
     const int total = rg.on ? heads * nqb + rg.kb0[heads] : heads * (nqb + nkb);
     for (int wid = ((int)blockIdx.x - n_abs) * WPG + (int)(threadIdx.x >> 6); wid < total;
          wid += n_waves)
-      pool_wave<T, D>(wid, q, n_q, q_hs, k, n_kv, kv_hs, block, nqb, nkb, heads, pooled_q,
+      pool_wave<T, D, ROPE>(wid, q, n_q, q_hs, k, n_kv, kv_hs, block, nqb, nkb, heads, pooled_q,
                       pooled_k, nqb_cap, nkb_cap, kc, rope, rg);
   }
 }
@@ -423,16 +424,19 @@ hipError_t launch_block_pool(int dtype, int heads, int d, int block, const void*
   const int nkb = (int)((n_kv + block - 1) / block);
   const int waves = rg.on ? heads * nqb + rg.kb0[heads] : heads * (nqb + nkb);
   const int grid = (waves + POOL_THREADS / 64 - 1) / (POOL_THREADS / 64);
-#define HF_POOL(T, D)                                                                        \
-  block_pool<T, D><<<grid, POOL_THREADS, 0, stream>>>(                                       \
+#define HF_POOL_R(T, D, R)                                                                    \
+  block_pool<T, D, R><<<grid, POOL_THREADS, 0, stream>>>(                                    \
       static_cast<const T*>(q), n_q, q_hs, static_cast<const T*>(k), n_kv, kv_hs, block, nqb, \
       nkb, heads, pooled_q, pooled_k, nqb_cap, nkb_cap, kc, rope, rg)
+#define HF_POOL(T, D) \
+  do { if (rope.cs) HF_POOL_R(T, D, true); else HF_POOL_R(T, D, false); } while (0)
   if (dtype == 0) {
     if (d == 128) HF_POOL(bf16_t, 128); else HF_POOL(bf16_t, 64);
   } else {
     if (d == 128) HF_POOL(float, 128); else HF_POOL(float, 64);
   }
 #undef HF_POOL
+#undef HF_POOL_R
   return hipGetLastError();
 }
 
@@ -467,24 +471,27 @@ hipError_t launch_absorb_and_pool(int dtype, int heads, int d, int block, const 
   const int nkb = (int)((n_kv + block - 1) / block);
   const AbsorbPlan p = absorb_plan(dtype, heads, d, n_ev);
   const int n_abs = absorb_items(dtype, heads, d, p);
-#define HF_ABSPOOL(T, D)                                                                       \
+#define HF_ABSPOOL_R(T, D, R)                                                                  \
   {                                                                                            \
     constexpr int wpg = absorb::threads<T, D>() / 64;                                          \
     static std::atomic<int> occ_cache[64];                                                     \
-    const int n_pool = pool_workgroups(absorb_and_pool<T, D>, absorb::threads<T, D>(), n_abs, \
+    const int n_pool = pool_workgroups(absorb_and_pool<T, D, R>, absorb::threads<T, D>(), n_abs, \
                                        (heads * (nqb + nkb) + wpg - 1) / wpg, occ_cache);      \
-    absorb_and_pool<T, D><<<n_abs + n_pool, absorb::threads<T, D>(), 0, stream>>>(             \
+    absorb_and_pool<T, D, R><<<n_abs + n_pool, absorb::threads<T, D>(), 0, stream>>>(          \
         static_cast<const T*>(k_ev), static_cast<const T*>(v_ev), n_ev, ev_hs,                 \
         p.tokens_per_split, p.n_split, partials, n_abs, static_cast<const T*>(q), n_q, q_hs,   \
         static_cast<const T*>(k), n_kv, kv_hs, block, nqb, nkb, heads, pooled_q, pooled_k,     \
         nqb_cap, nkb_cap, kc, rope, Ragged());                                                 \
   }
+#define HF_ABSPOOL(T, D) \
+  { if (rope.cs) HF_ABSPOOL_R(T, D, true) else HF_ABSPOOL_R(T, D, false) }
   if (dtype == 0) {
     if (d == 128) HF_ABSPOOL(bf16_t, 128) else HF_ABSPOOL(bf16_t, 64)
   } else {
     if (d == 128) HF_ABSPOOL(float, 128) else HF_ABSPOOL(float, 64)
   }
 #undef HF_ABSPOOL
+#undef HF_ABSPOOL_R
   return hipGetLastError();
 }
 

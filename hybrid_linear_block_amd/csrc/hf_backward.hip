@@ -13,7 +13,7 @@
 //
 // No atomics: every sum runs in a fixed order, so the results are bitwise
 // reproducible. Kernels:
-//   bwd_inv_sel        per (head, key block): the query blocks that selected it,
+//   bwd_inv_sel        per (head, 64 key blocks): the query blocks that selected each,
 //                      ascending.
 // fp32 states (fp32 arithmetic on the vector units; a row's dot products are split
 // over TPR adjacent lanes and reduced with xor shuffles, tiles staged in LDS as fp32):
@@ -137,37 +137,63 @@ __device__ __forceinline__ void load_tile(const T* __restrict__ base, int64_t ro
   }
 }
 
-// One workgroup per (head, key block): each thread looks for the key block in one
-// query block's ascending selection row (binary search); thread 0 then appends the
-// hits in query-block order.
+// One workgroup per (head, 64 key blocks j0 .. j0 + 63). The head's selection rows are
+// read once, flat and coalesced, a chunk of up to kInvChunk query blocks at a time; each
+// entry in the workgroup's range sets bit (j, i) of a bitmap in LDS; then thread j - j0
+// appends the query blocks of its row of bits in ascending order. Entries outside
+// [0, nkb) set no bit and a repeated entry sets its bit once (the rows are strictly
+// ascending and in range by the backward's contract).
+constexpr int kInvKeys = 64;                // key blocks per workgroup
+constexpr int kInvWords = 32;               // bitmap words per key block and chunk
+constexpr int kInvChunk = 32 * kInvWords;   // query blocks per chunk
 __global__ __launch_bounds__(256) void bwd_inv_sel(const int32_t* __restrict__ sel, int nqb,
                                                    int nkb, int top_k, int32_t* __restrict__ cnt,
                                                    int32_t* __restrict__ list, int nqb_cap) {
-  __shared__ int hit[256];
-  const int64_t x = blockIdx.x;
-  const int h = (int)(x / nkb), j = (int)(x % nkb);
-  int n = 0;  // thread 0's running count
-  for (int base = 0; base < nqb; base += 256) {
-    const int i = base + (int)threadIdx.x;
-    bool f = false;
-    if (i < nqb) {
-      const int32_t* row = sel + ((int64_t)h * nqb + i) * top_k;
-      int lo = 0, hi = top_k;
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (row[mid] < j) lo = mid + 1;
-        else hi = mid;
-      }
-      f = lo < top_k && row[lo] == j;
-    }
-    hit[threadIdx.x] = f;
+  __shared__ uint32_t bits[kInvKeys][kInvWords];
+  const int groups = (nkb + kInvKeys - 1) / kInvKeys;
+  const int h = (int)blockIdx.x / groups, j0 = ((int)blockIdx.x % groups) * kInvKeys;
+  const int tid = (int)threadIdx.x;
+  const int32_t* sh = sel + (int64_t)h * nqb * top_k;
+  const int jl = tid;  // threads 0 .. 63 own key block j0 + jl
+  int n = 0;
+  for (int i0 = 0; i0 < nqb; i0 += kInvChunk) {
+    const int rows = nqb - i0 < kInvChunk ? nqb - i0 : kInvChunk;
+    for (int e = tid; e < kInvKeys * kInvWords; e += 256) (&bits[0][0])[e] = 0u;
     __syncthreads();
-    if (threadIdx.x == 0)
-      for (int t = 0; t < 256 && base + t < nqb; ++t)
-        if (hit[t]) list[x * nqb_cap + n++] = base + t;
+    const int n_ent = rows * top_k;  // <= kInvChunk * kMaxKeyBlocks
+    const int32_t* base = sh + (int64_t)i0 * top_k;
+    constexpr int U = 8;  // loads in flight per thread
+    for (int f0 = 0; f0 < n_ent; f0 += U * 256) {
+      int32_t jv[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int f = f0 + u * 256 + tid;
+        jv[u] = f < n_ent ? base[f] : -1;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int f = f0 + u * 256 + tid;
+        const int jj = jv[u] - j0;
+        if (jj >= 0 && jj < kInvKeys && jv[u] < nkb) {
+          const int i = f / top_k;
+          atomicOr(&bits[jj][i >> 5], 1u << (i & 31));
+        }
+      }
+    }
+    __syncthreads();
+    if (jl < kInvKeys && j0 + jl < nkb) {
+      int32_t* out = list + ((int64_t)h * nkb + j0 + jl) * nqb_cap;
+      for (int w = 0; w * 32 < rows; ++w) {
+        uint32_t m = bits[jl][w];
+        while (m) {
+          out[n++] = i0 + 32 * w + __builtin_ctz(m);
+          m &= m - 1u;
+        }
+      }
+    }
     __syncthreads();
   }
-  if (threadIdx.x == 0) cnt[x] = n;
+  if (jl < kInvKeys && j0 + jl < nkb) cnt[(int64_t)h * nkb + j0 + jl] = n;
 }
 
 // Query rows per workgroup of bwd_rows and key rows per workgroup of bwd_kv, and
@@ -1414,7 +1440,7 @@ __global__ __launch_bounds__(BT) void bwd_state_reduce(const float* __restrict__
 template <typename T, int D, int BLK>
 hipError_t run_attend_bwd(const BwdArgs& a, int stage, hipStream_t s) {
   const int nqb = (int)((a.n_q + BLK - 1) / BLK), nkb = (int)((a.n_kv + BLK - 1) / BLK);
-  const int64_t inv_n = (int64_t)a.heads * nkb;
+  const int64_t inv_n = (int64_t)a.heads * ((nkb + kInvKeys - 1) / kInvKeys);
   if (stage == 0)
     bwd_inv_sel<<<(unsigned)inv_n, 256, 0, s>>>(a.sel, nqb, nkb, a.top_k, a.inv_cnt,
                                                  a.inv_list, a.nqb_cap);

@@ -98,6 +98,8 @@ def _run(H, d, B, dt, n_q, n_kv, top_k, n_ev, seed, twice=False, own_sel=False):
     (1, 128, 16, "f32", 48, 80, 5, 33),
     (1, 64, 64, "f32", 64, 200, 4, 10),      # every key block kept
     (1, 128, 64, "bf16", 1, 70, 1, 1),       # one query row, one key block
+    (2, 128, 64, "bf16", 37, 50, 1, 9),      # a window shorter than one key block
+    (1, 64, 64, "bf16", 64, 63, 1, 3),       # d = 64, one full query block, 63 keys
 ])
 def test_backward_matches_oracle(H, d, B, dt, n_q, n_kv, top_k, n_ev):
     _run(H, d, B, dt, n_q, n_kv, top_k, n_ev, seed=300 + n_q, twice=(n_q == 200))

@@ -110,6 +110,8 @@ def swa_source_sha():
 class LayerSet:
     """One input set of the Wan-like layer resident on the GPU, with its own state."""
 
+    rope_cap = None  # set per instance by --rope-cap (subclasses without it keep None)
+
     def __init__(self, hla, torch, synth, seed, top_k, inp=None):
         inp = synth.wan_layer_inputs(seed) if inp is None else inp
         dev = torch.device("cuda:0")

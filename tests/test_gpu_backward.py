@@ -105,6 +105,22 @@ def test_backward_matches_oracle(H, d, B, dt, n_q, n_kv, top_k, n_ev):
     _run(H, d, B, dt, n_q, n_kv, top_k, n_ev, seed=300 + n_q, twice=(n_q == 200))
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_backward_random_shapes(seed):
+    """A seeded draw over the supported shapes (bf16 with 64-row blocks, fp32 with 16-
+    or 64-row blocks, d 64 or 128, ragged lengths, any valid top-K)."""
+    r = np.random.default_rng(3000 + seed)
+    dt = ["bf16", "f32"][int(r.integers(2))]
+    d = [64, 128][int(r.integers(2))]
+    B = 64 if dt == "bf16" else [16, 64][int(r.integers(2))]
+    H = int(r.integers(1, 3))
+    n_q = int(r.integers(1, 300))
+    n_kv = int(r.integers(1, 1000))
+    n_ev = int(r.integers(1, 200))
+    top_k = int(r.integers(1, -(-n_kv // B) + 1))
+    _run(H, d, B, dt, n_q, n_kv, top_k, n_ev, seed=4000 + seed)
+
+
 @pytest.mark.parametrize("dt,d,B", [("bf16", 128, 64), ("f32", 64, 16)])
 def test_backward_any_ascending_selection(dt, d, B):
     """The backward differentiates whatever strictly ascending, in-range selection it is

@@ -99,6 +99,30 @@ def test_edge_cases(dtype, d, B, n_q, n_kv, top_k, n_ev):
     _run_random_case(1, d, B, dtype, n_q, n_kv, n_ev, K, seed=7)
 
 
+def _random_shape(seed):
+    """A seeded draw over the supported shapes: bf16 with 64-row blocks, fp32 with 16- or
+    64-row blocks, d 64 or 128, ragged lengths, any valid top-K, empty or filled state."""
+    r = np.random.default_rng(seed)
+    dtype = ["bf16", "f32"][int(r.integers(2))]
+    d = [64, 128][int(r.integers(2))]
+    B = 64 if dtype == "bf16" else [16, 64][int(r.integers(2))]
+    H = int(r.integers(1, 4))
+    n_q = int(r.integers(1, 400))
+    n_kv = int(r.integers(1, 1500))
+    n_ev = int(r.integers(0, 300))
+    nkb = -(-n_kv // B)
+    top_k = int(r.integers(1, nkb + 1))
+    return H, d, B, dtype, n_q, n_kv, n_ev, top_k
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_shapes(seed):
+    shape = _random_shape(1000 + seed)
+    print("random shape H,d,B,dtype,n_q,n_kv,n_ev,K =", shape, flush=True)
+    stats = _run_random_case(*shape, seed=2000 + seed)
+    print(stats, flush=True)
+
+
 # --------------------------------------------------------------- tiny fp32 stream
 
 

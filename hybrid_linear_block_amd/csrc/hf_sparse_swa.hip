@@ -663,6 +663,9 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void s
     };
     read_k(0);
     if (NKS > 1) read_k(1);
+    // The product phases and the tile requests run at a raised issue priority: the
+    // SIMD's other waves (of other workgroups) then fill the gaps between them.
+    __builtin_amdgcn_s_setprio(2);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
@@ -681,9 +684,12 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void s
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_s_setprio(0);
     lds_barrier();  // every wave is done with K(t)
+    __builtin_amdgcn_s_setprio(2);
     if (more) issue_tile(kh, jb_next, lds_k);
     else issue_s(0, lds_k);  // last block: the first S slice takes the K buffer
+    __builtin_amdgcn_s_setprio(0);
 
     // ---- online softmax (base 2) with a lazily moved reference max ----
     const int64_t key0 = (int64_t)jb * BLK;
@@ -789,6 +795,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void s
           acc[et][n] = Mfma<bf16_t>::mma(vop[c2][et], pop[n], acc[et][n]);
     };
     read_v(0);
+    __builtin_amdgcn_s_setprio(2);
     __builtin_amdgcn_sched_barrier(0);
     read_v(1);
     mma_v(0);
@@ -799,9 +806,12 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void s
     }
     __builtin_amdgcn_sched_barrier(0);
     mma_v(1);
+    __builtin_amdgcn_s_setprio(0);
     lds_barrier();  // every wave is done with V(t)
+    __builtin_amdgcn_s_setprio(2);
     if (more) issue_tile(vh, jb_next, lds_v);
     else if (NKS > 1) issue_s(1, lds_v);
+    __builtin_amdgcn_s_setprio(0);
     jb = jb_next;
   }
 

@@ -641,12 +641,16 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void b
     const int jb_next = clamp_block(my_sel[more ? t + 1 : 0], nkb);
     wait_vmem<0>();
     lds_barrier();
+    // products and tile requests at a raised issue priority, the VALU work at the
+    // normal one (as in the forward kernel: the SIMD's waves drift into different phases)
+    __builtin_amdgcn_s_setprio(2);
     f32x4 st[NMT][NQT], dp[NMT][NQT];
     rows_x(kaddr, qop, st);
     rows_x(vaddr, dop, dp);
     lds_barrier();  // every wave has read both tiles
     issue_tile(vh, jb_next, lds_v);
     issue_tile(kh, jb_next, lds_k);
+    __builtin_amdgcn_s_setprio(0);
     mask(jb, st);
 #pragma unroll
     for (int n = 0; n < NQT; ++n) {
@@ -697,6 +701,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void b
     const int jb_next = more ? clamp_block(my_sel[t + 1], nkb) : 0;
     wait_vmem<LPT>();  // V(t) has landed (K(t) may be in flight)
     lds_barrier();
+    __builtin_amdgcn_s_setprio(2);  // dP and S products, tile requests (dQ products: normal)
     f32x4 dp[NMT][NQT];
     rows_x(vaddr, dop, dp);
     lds_barrier();  // every wave has read V(t)
@@ -709,6 +714,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void b
     lds_barrier();
     f32x4 st[NMT][NQT];
     rows_x(kaddr, qop, st);
+    __builtin_amdgcn_s_setprio(0);
     mask(jb, st);
     // dL in the key order of the result layout, split into bf16 hi + lo
     bf16x8 lh[2][NQT], ll[2][NQT];
@@ -743,7 +749,9 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void b
         }
     }
     lds_barrier();  // every wave has read K(t)
+    __builtin_amdgcn_s_setprio(2);
     if (more) issue_tile(kh, jb_next, lds_k);
+    __builtin_amdgcn_s_setprio(0);
     jb = jb_next;
   }
   // lane holds dq[row 16n + c][16 et + 4g .. + 3]

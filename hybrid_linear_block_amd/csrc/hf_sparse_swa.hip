@@ -428,7 +428,9 @@ __global__ __launch_bounds__((BLK / QW) * 64) void sparse_swa(
 // global_load_lds, no staging registers) in the swizzled row-major layout above.
 // The two tiles are single-buffered and their loads are staggered so each one
 // overlaps compute: K(t+1) streams in during the softmax and O^T += V^T P^T of
-// block t, V(t+1) during S^T = K Q^T and the softmax of block t+1. The V operand
+// block t, V(t) during S^T = K Q^T and the softmax of block t. Three barriers per
+// block: K(t) has landed (which also frees the V tile of block t - 1, so V(t) is
+// requested right after it), every wave is done with K(t), V(t) has landed. The V operand
 // is read with the transposing LDS read, so V needs no transposed copy. The
 // epilogue normalises the accumulators in place, adds the linear read on MFMA
 // into them and stores the rows from registers.
@@ -535,12 +537,11 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void s
   };
   static_assert(NET * 2 == LPT * NW, "an S slice is one tile");
 
-  // The first key block's K and V tiles are requested before the Q operands, so that
-  // their latency overlaps the Q loads and the normaliser below (the vector memory
-  // counter completes in order: the waits for Q cover these older loads too).
+  // The first key block's K tile is requested before the Q operands, so that its
+  // latency overlaps the Q loads and the normaliser below (the vector memory counter
+  // completes in order: the waits for Q cover this older load too).
   int jb = my_sel[0];
   issue_tile(kh, jb, lds_k);
-  issue_tile(vh, jb, lds_v);
 
   // Q operands (B of S^T = K Q^T): lane holds Q[16n + c][32s + 8g .. +8].
   bf16x8 qop[NQT][NKS];
@@ -641,8 +642,10 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void s
   for (int t = 0; t < top_k; ++t) {
     const bool more = t + 1 < top_k;
     const int jb_next = more ? my_sel[t + 1] : 0;
-    wait_vmem<LPT>();  // K(t) has landed (V(t) may still be in flight)
-    lds_barrier();
+    wait_vmem<0>();  // K(t) has landed
+    lds_barrier();  // ... for every wave; every wave is also done with V(t-1)
+    __builtin_amdgcn_s_setprio(2);  // (priorities: see the S products below)
+    issue_tile(vh, jb, lds_v);
     // The next block index is taken here, where the barrier has already waited for
     // the scalar load, so no scalar load is pending once the operand reads start
     // (it would make every wait for them a full wait).
@@ -808,11 +811,10 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void s
     }
     __builtin_amdgcn_sched_barrier(0);
     mma_v(1);
-    lds_barrier();  // every wave is done with V(t)
-    __builtin_amdgcn_s_setprio(2);
-    if (more) issue_tile(vh, jb_next, lds_v);
-    else if (NKS > 1) issue_s(1, lds_v);
-    __builtin_amdgcn_s_setprio(0);
+    if (!more && NKS > 1) {  // last block: the second S slice takes the V buffer
+      lds_barrier();         // every wave is done with V(t)
+      issue_s(1, lds_v);
+    }
     jb = jb_next;
   }
 

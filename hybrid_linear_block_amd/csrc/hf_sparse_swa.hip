@@ -430,7 +430,8 @@ __global__ __launch_bounds__((BLK / QW) * 64) void sparse_swa(
 // overlaps compute: K(t+1) streams in during the softmax and O^T += V^T P^T of
 // block t, V(t) during S^T = K Q^T and the softmax of block t. Three barriers per
 // block: K(t) has landed (which also frees the V tile of block t - 1, so V(t) is
-// requested right after it), every wave is done with K(t), V(t) has landed. The V operand
+// requested from then on, in pieces between the k-steps of S^T), every wave is done
+// with K(t), V(t) has landed. The V operand
 // is read with the transposing LDS read, so V needs no transposed copy. The
 // epilogue normalises the accumulators in place, adds the linear read on MFMA
 // into them and stores the rows from registers.
@@ -451,6 +452,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void s
   constexpr int CPR = D / 8;            // 16-byte chunks per K/V row
   constexpr int TCH = BLK * CPR;        // chunks per tile
   constexpr int LPT = TCH / (NW * 64);  // global->LDS loads per lane per tile
+  static_assert(LPT % NKS == 0, "the V tile's loads spread evenly over the k-steps");
   // Separate objects, so that the compiler can tell an in-flight load into one
   // tile from reads of the other; after the loop they stage the slices of S.
   __shared__ uint4 lds_k[TCH];
@@ -502,6 +504,19 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void s
   auto tile_row0 = [&](int jb) {
     const int64_t r0 = (int64_t)jb * BLK;
     return (!SHORT && r0 + BLK > n_kv) ? n_kv - BLK : r0;
+  };
+  auto issue_part = [&](const bf16_t* src, int jb, const uint4* tile, int u) {  // load u only
+    const bf16_t* tb = src + (size_t)tile_row0(jb) * D;
+    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_offset(tile) + w * 64 * 16);
+    const uint32_t off = lpat[u % NPAT];
+    if constexpr (!SHORT) {
+      lds_dma16(tb + u * RPU * D, off, base + u * NW * 64 * 16);
+    } else {
+      const uint32_t row_bytes = D * 2, row = u * RPU + off / row_bytes;
+      const uint32_t last = (uint32_t)(n_kv - 1 - tile_row0(jb));
+      lds_dma16(tb, (row <= last ? row : last) * row_bytes + off % row_bytes,
+                base + u * NW * 64 * 16);
+    }
   };
   auto issue_tile = [&](const bf16_t* src, int jb, const uint4* tile) {
     const bf16_t* tb = src + (size_t)tile_row0(jb) * D;
@@ -645,7 +660,6 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void s
     wait_vmem<0>();  // K(t) has landed
     lds_barrier();  // ... for every wave; every wave is also done with V(t-1)
     __builtin_amdgcn_s_setprio(2);  // (priorities: see the S products below)
-    issue_tile(vh, jb, lds_v);
     // The next block index is taken here, where the barrier has already waited for
     // the scalar load, so no scalar load is pending once the operand reads start
     // (it would make every wait for them a full wait).
@@ -687,6 +701,10 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void s
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
+      // V(t) is requested in pieces between the k-steps, behind queued products.
+#pragma unroll
+      for (int u = s * (LPT / NKS); u < (s + 1) * (LPT / NKS); ++u) issue_part(vh, jb, lds_v, u);
       __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_setprio(0);

@@ -505,34 +505,22 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void s
     const int64_t r0 = (int64_t)jb * BLK;
     return (!SHORT && r0 + BLK > n_kv) ? n_kv - BLK : r0;
   };
-  auto issue_part = [&](const bf16_t* src, int jb, const uint4* tile, int u) {  // load u only
+  auto issue_part = [&](const bf16_t* src, int jb, const uint4* tile, int u) {  // load u
     const bf16_t* tb = src + (size_t)tile_row0(jb) * D;
     const uint32_t base = __builtin_amdgcn_readfirstlane(lds_offset(tile) + w * 64 * 16);
     const uint32_t off = lpat[u % NPAT];
     if constexpr (!SHORT) {
       lds_dma16(tb + u * RPU * D, off, base + u * NW * 64 * 16);
-    } else {
+    } else {  // rows of the tile past the window read the window's last row
       const uint32_t row_bytes = D * 2, row = u * RPU + off / row_bytes;
-      const uint32_t last = (uint32_t)(n_kv - 1 - tile_row0(jb));
+      const uint32_t last = (uint32_t)(n_kv - 1 - tile_row0(jb));  // tile-relative
       lds_dma16(tb, (row <= last ? row : last) * row_bytes + off % row_bytes,
                 base + u * NW * 64 * 16);
     }
   };
   auto issue_tile = [&](const bf16_t* src, int jb, const uint4* tile) {
-    const bf16_t* tb = src + (size_t)tile_row0(jb) * D;
-    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_offset(tile) + w * 64 * 16);
 #pragma unroll
-    for (int u = 0; u < LPT; ++u) {
-      const uint32_t off = lpat[u % NPAT];
-      if constexpr (!SHORT) {
-        lds_dma16(tb + u * RPU * D, off, base + u * NW * 64 * 16);
-      } else {  // rows of the tile past the window read the window's last row
-        const uint32_t row_bytes = D * 2, row = u * RPU + off / row_bytes;
-        const uint32_t last = (uint32_t)(n_kv - 1 - tile_row0(jb));  // tile-relative
-        lds_dma16(tb, (row <= last ? row : last) * row_bytes + off % row_bytes,
-                  base + u * NW * 64 * 16);
-      }
-    }
+    for (int u = 0; u < LPT; ++u) issue_part(src, jb, tile, u);
   };
 
   // The linear read's S operands are staged through the same two buffers, one k-step
@@ -659,7 +647,6 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void s
     const int jb_next = more ? my_sel[t + 1] : 0;
     wait_vmem<0>();  // K(t) has landed
     lds_barrier();  // ... for every wave; every wave is also done with V(t-1)
-    __builtin_amdgcn_s_setprio(2);  // (priorities: see the S products below)
     // The next block index is taken here, where the barrier has already waited for
     // the scalar load, so no scalar load is pending once the operand reads start
     // (it would make every wait for them a full wait).

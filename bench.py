@@ -93,6 +93,10 @@ def parse():
                         "10000, 1560 tokens per frame) with this cap on the position index")
     p.add_argument("--side-stream", action="store_true",
                    help="hf_absorb_and_attend with the absorb on a side stream")
+    p.add_argument("--ahead", action="store_true",
+                   help="hf_absorb_and_attend_ahead: each step attends with the absorb its "
+                        "previous step formed (reduced in the selection launch) and forms the "
+                        "next chunk's absorb inside the attention launch")
     p.add_argument("--cpu-reps", type=int, default=3)
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="also run device copies of this size (HBM counter calibration)")
@@ -111,6 +115,7 @@ class LayerSet:
     """One input set of the Wan-like layer resident on the GPU, with its own state."""
 
     rope_cap = None  # set per instance by --rope-cap (subclasses without it keep None)
+    ahead = False  # set by --ahead
 
     def __init__(self, hla, torch, synth, seed, top_k, inp=None):
         inp = synth.wan_layer_inputs(seed) if inp is None else inp
@@ -133,7 +138,10 @@ class LayerSet:
         self.inp = inp
 
     def step(self, side=None, serial=False):
-        if serial:
+        if self.ahead:  # this set's stream: the same evicted frames every chunk
+            self.st.absorb_and_attend_ahead(self.q, self.kw, self.vw, self.top_k,
+                                            k_next=self.kev, v_next=self.vev, out=self.out)
+        elif serial:
             self.st.absorb_evicted(self.kev, self.vev)
             self.st.attend_chunk(self.q, self.kw, self.vw, self.top_k, out=self.out)
         else:  # one call; with a side stream the absorb overlaps the block selection
@@ -584,8 +592,10 @@ def main():
     streams = args.streams or args.cached_pooling or args.managed_window
     if streams and args.workload != "wan_layer_bf16":
         sys.exit("--streams / --cached-pooling / --managed-window run the wan_layer_bf16 shapes")
-    if streams and (args.side_stream or args.serial):
+    if streams and (args.side_stream or args.serial or args.ahead):
         sys.exit("--streams / --cached-pooling / --managed-window issue one stream's calls")
+    if args.ahead and (args.side_stream or args.serial):
+        sys.exit("--ahead issues one call per step on one stream")
     if args.managed_window:
         if args.ring_windows < 2:
             sys.exit("--ring-windows must be at least 2")
@@ -606,6 +616,8 @@ def main():
         for s in sets:
             s.rope_cap = args.rope_cap
             s.st.set_rope(44, 10000.0, 1560, args.rope_cap)
+    for s in sets:
+        s.ahead = bool(args.ahead)
     log(f"[bench] {n_sets} input sets resident ({time.time() - t0:.1f}s)")
 
     # Selection of every set (for the executed-FLOP count); not timed.
@@ -705,7 +717,7 @@ def main():
 
     # Roofline of the dominant kernel (sparse_swa): executed algorithmic FLOPs per launch
     # over its average event-timed duration.
-    swa_flop = statistics.mean(f["sparse_swa"] for f in flops)
+    swa_flop = statistics.mean(f["sparse_swa"] + (f["absorb"] if args.ahead else 0) for f in flops)
     swa_us = kern_us["sparse_swa"]
     achieved = swa_flop / (swa_us * 1e-6) / 1e12
     peak = PEAK_MFMA_TFLOPS[wl.dtype]
@@ -715,14 +727,16 @@ def main():
         if tr.get("source_sha256") == swa_source_sha():
             traffic = tr.get("hbm_bytes_per_launch")
     roofline = dict(bound="mfma", achieved=round(achieved, 2), peak=peak, unit="TFLOP/s",
-                    frac=round(achieved / peak, 4), traffic=traffic, kernel="sparse_swa",
+                    frac=round(achieved / peak, 4), traffic=traffic if not args.ahead else None,
+                    kernel="sparse_swa" + (" (with the next absorb's partial states)"
+                                           if args.ahead else ""),
                     flop_per_launch=int(swa_flop), avg_launch_us=round(swa_us, 2))
 
     # On one stream (the default) the absorb shares the attend call's launches: its
     # partial states are formed in the pooling launch and its reduce (which writes S
     # and z) runs in the selection launch, so its bytes and FLOPs are counted there.
     absorb_alone_us = kern_us.get("absorb")  # absorbs outside an attend call
-    fused = not args.side_stream and not args.serial
+    fused = not args.side_stream and not args.serial and not args.ahead
     kbytes = dict(sets[0].bytes())
     if args.cached_pooling:  # a step whose window moved by one chunk (all but 1 in P)
         kbytes["block_pool"] = sets[0].pool_bytes_cached()
@@ -742,6 +756,17 @@ def main():
                        select_and_reduce=kern_us.get("score_select"),
                        sparse_swa=kern_us.get("sparse_swa"))
         names = ("absorb_and_pool", "select_and_reduce", "sparse_swa")
+    if args.ahead:  # partial states in the attention launch, their reduce in the selection's
+        sz = sets[0].state_bytes()
+        kbytes = dict(block_pool=kbytes["block_pool"],
+                      select_and_reduce=kbytes["score_select"] + sz,
+                      attend_and_absorb=kbytes["sparse_swa"] + kbytes["absorb"] - sz)
+        kflops = dict(block_pool=kflops["block_pool"], select_and_reduce=kflops["score_select"],
+                      attend_and_absorb=kflops["sparse_swa"] + kflops["absorb"])
+        kern_us = dict(block_pool=kern_us.get("block_pool"),
+                       select_and_reduce=kern_us.get("score_select"),
+                       attend_and_absorb=kern_us.get("sparse_swa"))
+        names = ("block_pool", "select_and_reduce", "attend_and_absorb")
     kernels = {}
     for name in names:
         us = kern_us.get(name)
@@ -817,6 +842,9 @@ def main():
                       "hf_window_attend; one stream per input set" if args.managed_window else
                       "hf_absorb_evicted, then hf_attend_chunk" if args.serial else
                       "hf_absorb_and_attend, absorb on a side stream" if args.side_stream else
+                      "hf_absorb_and_attend_ahead, one stream: each step reduces the absorb the "
+                      "previous step of its input set formed and forms the next one inside its "
+                      "attention launch" if args.ahead else
                       (("hf_absorb_and_attend_cached" if args.cached_pooling else
                         "hf_absorb_and_attend") + ", one stream; each input set is a stream "
                        f"whose window moves by one chunk per step ({args.stream_positions} "

@@ -73,6 +73,11 @@ def _load():
         "hf_absorb_and_attend_cached": (c_int, [P, P, P, c_int64, c_int64, c_int64, P, c_int64,
                                                 c_int64, P, P, c_int64, c_int64, c_int64, c_int32,
                                                 P, c_int64, P, P]),
+        "hf_absorb_and_attend_ahead": (c_int, [P, P, c_int64, c_int64, P, P, c_int64, c_int64,
+                                               c_int64, c_int32, P, c_int64, P, P, P, c_int64,
+                                               c_int64, c_int64, P]),
+        "hf_absorb_flush": (c_int, [P, P]),
+        "hf_pending_ev": (c_int64, [P]),
         "hf_key_cache_reset": (c_int, [P]),
         "hf_window_attach": (c_int, [P, P, P, c_int64, c_int64]),
         "hf_window_begin_chunk": (c_int, [P, c_int64, P, POINTER(c_void_p), POINTER(c_void_p),
@@ -108,6 +113,7 @@ _lib = _load()
 
 EXPORTED = ("hf_workspace_bytes", "hf_state_init", "hf_absorb_evicted", "hf_attend_chunk",
             "hf_absorb_and_attend", "hf_attend_chunk_cached", "hf_absorb_and_attend_cached",
+            "hf_absorb_and_attend_ahead", "hf_absorb_flush", "hf_pending_ev",
             "hf_key_cache_reset", "hf_window_attach", "hf_window_begin_chunk",
             "hf_window_attend", "hf_window_range", "hf_block_scores",
             "hf_backward_workspace_bytes", "hf_attend_backward", "hf_absorb_backward",
@@ -182,6 +188,25 @@ def hf_absorb_and_attend_cached(state: int, k_ev: int, v_ev: int, n_ev: int, ev_
                                             n_q, q_head_stride, k_win, v_win, n_kv,
                                             kv_head_stride, win_index, top_k, out,
                                             out_head_stride, sel_out, stream)
+
+
+def hf_absorb_and_attend_ahead(state: int, q: int, n_q: int, q_head_stride: int, k_win: int,
+                               v_win: int, n_kv: int, kv_head_stride: int, win_index: int,
+                               top_k: int, out: int, out_head_stride: int, sel_out: int,
+                               k_next: int, v_next: int, n_next: int, next_head_stride: int,
+                               next_index: int, stream: int) -> int:
+    return _lib.hf_absorb_and_attend_ahead(state, q, n_q, q_head_stride, k_win, v_win, n_kv,
+                                           kv_head_stride, win_index, top_k, out,
+                                           out_head_stride, sel_out, k_next, v_next, n_next,
+                                           next_head_stride, next_index, stream)
+
+
+def hf_absorb_flush(state: int, stream: int) -> int:
+    return _lib.hf_absorb_flush(state, stream)
+
+
+def hf_pending_ev(state: int) -> int:
+    return _lib.hf_pending_ev(state)
 
 
 def hf_key_cache_reset(state: int) -> int:

@@ -29,6 +29,9 @@ struct hf_state {
   float* pooled_k;
   int32_t* sel;
   float* partials;
+  // Tokens whose partial states an ahead call left in `partials` for the next call to
+  // reduce into S and z (0: none pending).
+  int64_t pend_n = 0;
   uint16_t* s_split;  // bf16 hi/lo split of S (bf16 states), kept in step with S
   // Cache of 8-token key sums for the cached calls: ring of kc_cap groups per head;
   // the absolute groups [kc_lo, kc_hi) hold the sums of the last cached window.
@@ -321,10 +324,26 @@ static hf_status check_absorb(const hf_state* st, const void* k_ev, const void* 
   return ev_index != st->next_ev ? HF_ERR_STATE : HF_OK;
 }
 
+// The reduce of the partial states that hf_absorb_and_attend_ahead left in the
+// workspace, if any, on stream s. Every call that reads or writes S, z or the
+// workspace's partial states completes a pending absorb first.
+static hipError_t flush_pending(hf_state* st, hipStream_t s) {
+  if (st->pend_n == 0) return hipSuccess;
+  const hf_config& c = st->cfg;
+  const hipError_t e = timed(st, HF_KERNEL_ABSORB, s, [&]() {
+    return hf::launch_absorb_reduce(c.dtype, c.num_heads, c.head_dim, st->pend_n, st->partials,
+                                    st->S, st->z, st->s_split, s);
+  });
+  if (e == hipSuccess) st->pend_n = 0;
+  return e;
+}
+
 // The absorb kernels on stream s (n_ev > 0); the caller has validated everything.
 static hipError_t enqueue_absorb(hf_state* st, const void* k_ev, const void* v_ev, int64_t n_ev,
                                  int64_t ev_head_stride, hipStream_t s) {
   const hf_config& c = st->cfg;
+  const hipError_t e = flush_pending(st, s);
+  if (e != hipSuccess) return e;
   return timed(st, HF_KERNEL_ABSORB, s, [&]() {
     return hf::launch_absorb(c.dtype, c.num_heads, c.head_dim, k_ev, v_ev, n_ev, ev_head_stride,
                              st->S, st->z, st->partials, st->s_split, s);
@@ -406,14 +425,26 @@ struct FusedAbsorb {
 // caller; with `join`, the attention waits for that event. With `fa`, the absorb of
 // its tokens runs inside the first two launches: the partial states next to the
 // pooling, the reduce next to the selection, so S and z hold the new tokens before
-// the attention reads them; *absorbed tells whether the reduce was enqueued.
+// the attention reads them; *absorbed tells whether the reduce was enqueued. A pending
+// absorb (an ahead call's) is reduced in the selection launch (before the pooling
+// launch if `fa` needs the partial-state buffer). With `next`, the partial states of
+// those tokens are formed in the attention launch (bf16; fp32: a launch after it) and
+// left pending; *formed tells whether they were enqueued.
 static hipError_t enqueue_attend(hf_state* st, const void* q, int64_t n_q, int64_t q_hs,
                                  const void* k_win, const void* v_win, int64_t n_kv,
                                  int64_t kv_hs, int32_t top_k, void* out, int64_t out_hs,
                                  int32_t* sel_out, hipStream_t s, hipEvent_t join,
                                  const FusedAbsorb* fa = nullptr, bool* absorbed = nullptr,
-                                 const hf::KeyCache* kc = nullptr) {
+                                 const hf::KeyCache* kc = nullptr,
+                                 const FusedAbsorb* next = nullptr, bool* formed = nullptr) {
   const hf_config& c = st->cfg;
+  if (absorbed) *absorbed = false;
+  if (formed) *formed = false;
+  if (fa && st->pend_n > 0) {
+    const hipError_t e = flush_pending(st, s);
+    if (e != hipSuccess) return e;
+  }
+  const int64_t reduce_n = fa ? 0 : st->pend_n;
   const int nqb = (int)ceil_div(n_q, c.block_size);
   const int nkb = (int)ceil_div(n_kv, c.block_size);
   int32_t* sel = sel_out ? sel_out : st->sel;
@@ -440,23 +471,46 @@ static hipError_t enqueue_attend(hf_state* st, const void* q, int64_t n_q, int64
   }
   if (r == hipSuccess)
     r = timed(st, HF_KERNEL_SCORE_SELECT, s, [&]() {
-      if (fa)
+      const int64_t red = fa ? fa->n_ev : reduce_n;
+      if (red > 0)
         return hf::launch_select_and_reduce(c.dtype, c.num_heads, c.head_dim, nqb, nkb,
                                             st->nqb_cap, st->nkb_cap, st->pooled_q, st->pooled_k,
-                                            st->scale, top_k, sel, st->partials, fa->n_ev, st->S,
+                                            st->scale, top_k, sel, st->partials, red, st->S,
                                             st->z, st->s_split, s);
       return hf::launch_score_select(c.num_heads, c.head_dim, nqb, nkb, st->nqb_cap, st->nkb_cap,
                                      st->pooled_q, st->pooled_k, st->scale, top_k, sel, nullptr,
                                      s);
     });
   if (absorbed) *absorbed = fa && r == hipSuccess;
+  if (r == hipSuccess && reduce_n > 0) st->pend_n = 0;
   if (r == hipSuccess && join) r = hipStreamWaitEvent(s, join, 0);
+  // bf16: the next absorb's partial states are formed by workgroups appended to the
+  // attention launch, in the slots its own workgroups leave free.
+  hf::AbsorbAhead ab;
+  const bool in_launch = next && c.dtype == HF_BF16;
+  if (in_launch) {
+    const hf::AbsorbPlan p = hf::absorb_plan(c.dtype, c.num_heads, c.head_dim, next->n_ev);
+    ab.k = next->k_ev;
+    ab.v = next->v_ev;
+    ab.n_ev = next->n_ev;
+    ab.hs = next->head_stride;
+    ab.tps = p.tokens_per_split;
+    ab.n_split = p.n_split;
+    ab.partials = st->partials;
+  }
   if (r == hipSuccess)
     r = timed(st, HF_KERNEL_SPARSE_SWA, s, [&]() {
       return hf::launch_sparse_swa(c.dtype, c.num_heads, c.head_dim, c.block_size, q, n_q, q_hs,
                                    k_win, v_win, n_kv, kv_hs, sel, top_k, st->S, st->s_split,
-                                   st->z, c.eps, st->scale, out, out_hs, s, rope);
+                                   st->z, c.eps, st->scale, out, out_hs, s, rope, hf::Ragged(),
+                                   ab);
     });
+  if (r == hipSuccess && next && !in_launch)
+    r = timed(st, HF_KERNEL_ABSORB, s, [&]() {
+      return hf::launch_absorb_parts(c.dtype, c.num_heads, c.head_dim, next->k_ev, next->v_ev,
+                                     next->n_ev, next->head_stride, st->partials, s);
+    });
+  if (formed) *formed = next && r == hipSuccess;
   return r;
 }
 
@@ -578,6 +632,59 @@ hf_status hf_absorb_and_attend_cached(hf_state* st, const void* k_ev, const void
   if (absorbed) st->next_ev += n_ev;  // the absorb is enqueued and will run
   return r;
 }
+
+hf_status hf_absorb_and_attend_ahead(hf_state* st, const void* q, int64_t n_q,
+                                     int64_t q_head_stride, const void* k_win, const void* v_win,
+                                     int64_t n_kv, int64_t kv_head_stride, int64_t win_index,
+                                     int32_t top_k, void* out, int64_t out_head_stride,
+                                     int32_t* sel_out, const void* k_next, const void* v_next,
+                                     int64_t n_next, int64_t next_head_stride,
+                                     int64_t next_index, void* stream) {
+  if (!st) return HF_ERR_INVALID_ARG;
+  const hf_config& c = st->cfg;
+  hf_status e = check_absorb(st, k_next, v_next, n_next, next_head_stride, next_index);
+  if (e == HF_OK)
+    e = check_attend_all(st, q, n_q, q_head_stride, k_win, v_win, n_kv, kv_head_stride, top_k,
+                         out, out_head_stride, sel_out);
+  if (e == HF_OK && n_q > 0) e = check_rope_shapes(st, n_q, n_kv);
+  if (e == HF_OK && n_q > 0 && win_index >= 0)
+    e = st->rope.cs ? HF_ERR_UNSUPPORTED : check_window(win_index, n_kv);  // rotated keys are not cached
+  if (e != HF_OK) return e;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hf::KeyCache kc = key_cache(st, win_index >= 0 ? win_index : 0);
+  bool formed = false;
+  const hf_status r = on_device(st->device, [&]() -> hipError_t {
+    const FusedAbsorb nx{k_next, v_next, n_next, next_head_stride};
+    if (n_q == 0) {  // no attention launch to carry the partial states: a launch of their own
+      hipError_t err = flush_pending(st, s);
+      if (err == hipSuccess && n_next > 0) {
+        err = timed(st, HF_KERNEL_ABSORB, s, [&]() {
+          return hf::launch_absorb_parts(c.dtype, c.num_heads, c.head_dim, k_next, v_next, n_next,
+                                         next_head_stride, st->partials, s);
+        });
+        formed = err == hipSuccess;
+      }
+      return err;
+    }
+    return enqueue_attend(st, q, n_q, q_head_stride, k_win, v_win, n_kv, kv_head_stride, top_k,
+                          out, out_head_stride, sel_out, s, nullptr, nullptr, nullptr,
+                          win_index >= 0 ? &kc : nullptr, n_next > 0 ? &nx : nullptr, &formed);
+  });
+  if (formed) {  // the partial states are enqueued: the tokens count as absorbed
+    st->pend_n = n_next;
+    st->next_ev += n_next;
+  }
+  return r;
+}
+
+hf_status hf_absorb_flush(hf_state* st, void* stream) {
+  if (!st) return HF_ERR_INVALID_ARG;
+  if (st->pend_n == 0) return HF_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return on_device(st->device, [&]() { return flush_pending(st, s); });
+}
+
+int64_t hf_pending_ev(const hf_state* st) { return st ? st->pend_n : -1; }
 
 hf_status hf_window_attach(hf_state* st, void* k_ring, void* v_ring, int64_t ring_tokens,
                            int64_t window_tokens) {
@@ -825,7 +932,7 @@ hf_status hf_attend_backward(hf_state* st, const void* q, int64_t n_q, int64_t q
   a.nqb_cap = st->nqb_cap;
   hipStream_t s = static_cast<hipStream_t>(stream);
   return on_device(st->device, [&]() {
-    hipError_t r = hipSuccess;
+    hipError_t r = flush_pending(st, s);  // the backward reads S and z
     for (int stage = 0; stage < 4 && r == hipSuccess; ++stage)
       r = timed(st, HF_KERNEL_BWD_INDEX + stage, s, [&]() {
         return hf::launch_attend_backward(c.dtype, c.head_dim, c.block_size, a, stage, s);
@@ -909,7 +1016,9 @@ hf_status hf_attend_ragged(hf_state* st, const void* q, int64_t n_q, int64_t q_h
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   return on_device(st->device, [&]() {
-    hipError_t r = timed(st, HF_KERNEL_BLOCK_POOL, s, [&]() {
+    hipError_t r = flush_pending(st, s);  // the attention reads S and z
+    if (r == hipSuccess)
+      r = timed(st, HF_KERNEL_BLOCK_POOL, s, [&]() {
       return hf::launch_block_pool(c.dtype, c.num_heads, c.head_dim, c.block_size, q, n_q,
                                    q_head_stride, k_flat, n_min, 0, st->pooled_q, st->pooled_k,
                                    st->nqb_cap, st->nkb_cap, s, hf::KeyCache(), hf::Rope(), rg);

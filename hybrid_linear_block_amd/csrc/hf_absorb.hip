@@ -97,9 +97,9 @@ int absorb_items(int dtype, int heads, int d, const AbsorbPlan& p) {
   return p.n_split * per * heads;
 }
 
-hipError_t launch_absorb(int dtype, int heads, int d, const void* k, const void* v, int64_t n_ev,
-                         int64_t head_stride, float* S, float* z, float* partials,
-                         uint16_t* s_split, hipStream_t stream) {
+hipError_t launch_absorb_parts(int dtype, int heads, int d, const void* k, const void* v,
+                               int64_t n_ev, int64_t head_stride, float* partials,
+                               hipStream_t stream) {
   const AbsorbPlan p = absorb_plan(dtype, heads, d, n_ev);
   const int items = absorb_items(dtype, heads, d, p);
 #define HF_ABS(T, D)                                                                        \
@@ -112,14 +112,26 @@ hipError_t launch_absorb(int dtype, int heads, int d, const void* k, const void*
     if (d == 128) HF_ABS(float, 128); else HF_ABS(float, 64);
   }
 #undef HF_ABS
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+hipError_t launch_absorb_reduce(int dtype, int heads, int d, int64_t n_ev, const float* partials,
+                                float* S, float* z, uint16_t* s_split, hipStream_t stream) {
+  const AbsorbPlan p = absorb_plan(dtype, heads, d, n_ev);
 #define HF_RED(D)                                                                   \
   absorb_reduce<D><<<dim3((part_floats<D>() / 4 + RED_THREADS - 1) / RED_THREADS, heads), \
                      RED_THREADS, 0, stream>>>(partials, p.n_split, S, z, s_split)
   if (d == 128) HF_RED(128); else HF_RED(64);
 #undef HF_RED
   return hipGetLastError();
+}
+
+hipError_t launch_absorb(int dtype, int heads, int d, const void* k, const void* v, int64_t n_ev,
+                         int64_t head_stride, float* S, float* z, float* partials,
+                         uint16_t* s_split, hipStream_t stream) {
+  hipError_t e = launch_absorb_parts(dtype, heads, d, k, v, n_ev, head_stride, partials, stream);
+  if (e != hipSuccess) return e;
+  return launch_absorb_reduce(dtype, heads, d, n_ev, partials, S, z, s_split, stream);
 }
 
 hipError_t launch_split_state(int heads, int d, const float* S, uint16_t* s_split,

@@ -190,6 +190,157 @@ __device__ __forceinline__ void absorb_part_bf16(int split, int h, const bf16_t*
   if (g == 0) part[D * D + w * 16 + c] = zs;
 }
 
+// The partial state of absorb_part_bf16, bit for bit, formed by a workgroup of two
+// waves (128 threads) inside the LDS of another kernel: wave w owns the key-feature
+// tiles w * NIT .. w * NIT + NIT - 1 against every value-feature tile, and the token
+// tiles pass through two stages, st0 and st1 (each a K tile followed by a V tile,
+// BT * D * 4 bytes), one tile ahead. Every accumulator takes the products of
+// absorb_part_bf16 in the same order (per token tile the hi product, then the lo
+// product) and every z the same additions, so the partials are identical.
+template <int D>
+__device__ __forceinline__ void absorb_part_bf16_w2(int split, int h,
+                                                    const bf16_t* __restrict__ kev,
+                                                    const bf16_t* __restrict__ vev, int64_t n_ev,
+                                                    int64_t hs, int tps, int n_split,
+                                                    float* __restrict__ partials,
+                                                    const void* st0, const void* st1) {
+  constexpr int NTH = 128;
+  constexpr int CPR = D / 8;            // 16-byte chunks per row
+  constexpr int LPT = BT * CPR / NTH;   // loads per thread per tile
+  constexpr int NJT = D / 16;           // value-feature tiles
+  constexpr int NIT = D / 32;           // key-feature tiles per wave
+  constexpr uint32_t kTile = BT * D * 2;  // bytes of one token tile
+  static_assert(LPT * NTH == BT * CPR, "whole loads per tile");
+  // Workgroup-uniform by construction; said so for the compiler, since the tile
+  // addresses must be scalar operands of the loads.
+  split = __builtin_amdgcn_readfirstlane(split);
+  h = __builtin_amdgcn_readfirstlane(h);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, c = lane & 15;
+  const int64_t n0 = (int64_t)split * tps;
+  const int64_t n1 = n0 + tps < n_ev ? n0 + tps : n_ev;
+  const int niter = (int)((n1 - n0 + BT - 1) / BT);
+  const bf16_t* kb = kev + (size_t)h * hs;
+  const bf16_t* vb = vev + (size_t)h * hs;
+
+  // Load u of thread tid fills LDS chunk u * NTH + tid of a tile (row P / CPR, slot
+  // P % CPR) with global chunk slot ^ 2 swz(row) of that row, as in absorb_part_bf16.
+  int lrow[LPT];
+  uint32_t loff[LPT];
+#pragma unroll
+  for (int u = 0; u < LPT; ++u) {
+    const int P = u * NTH + tid;
+    lrow[u] = P / CPR;
+    loff[u] = (uint32_t)(lrow[u] * D + (((P % CPR) ^ (2 * swz<D>(lrow[u]))) * 8)) * 2u;
+  }
+  auto issue = [&](int t, uint32_t sbase) {
+    const int64_t r0 = n0 + (int64_t)t * BT;
+    const bf16_t* kt = kb + (size_t)r0 * D;
+    const bf16_t* vt = vb + (size_t)r0 * D;
+    const int64_t left = n1 - r0;
+#pragma unroll
+    for (int u = 0; u < LPT; ++u) {
+      uint32_t off = loff[u];
+      if (left < BT) {  // partial last tile: rows past the end repeat the last row (masked)
+        const uint32_t last = (uint32_t)left - 1;
+        if ((uint32_t)lrow[u] > last) off = last * (D * 2) + loff[u] % (D * 2);
+      }
+      const uint32_t base = __builtin_amdgcn_readfirstlane(sbase + u * NTH * 16 + w * 1024);
+      lds_dma16(kt, off, base);
+      lds_dma16(vt, off, base + kTile);
+    }
+  };
+
+  // Transposing-read source role, as in absorb_part_bf16.
+  const int e_row = (lane & 15) >> 2, q = lane & 3;
+  auto tr_off = [&](int row, int col0) {
+    const int cc = (col0 >> 3) + (q >> 1);
+    return (uint32_t)((row * CPR + (cc ^ (2 * swz<D>(row)))) * 16 + (q & 1) * 8);
+  };
+  const int ra = 8 * g + e_row, rb = ra + 4;
+  uint32_t koff_a[NIT], koff_b[NIT], voff_a[NJT], voff_b[NJT];
+#pragma unroll
+  for (int i = 0; i < NIT; ++i) {
+    koff_a[i] = tr_off(ra, (w * NIT + i) * 16);
+    koff_b[i] = tr_off(rb, (w * NIT + i) * 16);
+  }
+#pragma unroll
+  for (int j = 0; j < NJT; ++j) {
+    voff_a[j] = kTile + tr_off(ra, j * 16);
+    voff_b[j] = kTile + tr_off(rb, j * 16);
+  }
+
+  f32x4 acc[NJT][NIT];
+#pragma unroll
+  for (int j = 0; j < NJT; ++j)
+#pragma unroll
+    for (int i = 0; i < NIT; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float zacc[NIT];
+#pragma unroll
+  for (int i = 0; i < NIT; ++i) zacc[i] = 0.f;
+
+  const uint32_t sb0 = lds_offset(st0), sb1 = lds_offset(st1);
+  if (niter > 0) issue(0, sb0);
+  for (int t = 0; t < niter; ++t) {
+    const uint32_t sb = (t & 1) ? sb1 : sb0;
+    wait_vmem<0>();  // tile t has landed
+    lds_barrier();   // ... for both waves, which are also done with tile t - 1
+    if (t + 1 < niter) issue(t + 1, (t & 1) ? sb0 : sb1);
+    const int valid = (int)(n1 - (n0 + (int64_t)t * BT));
+    bf16x8 a[NJT];
+#pragma unroll
+    for (int j = 0; j < NJT; ++j) {
+      const v4i16 v0 = lds_tr8(sb + voff_a[j]), v1 = lds_tr8(sb + voff_b[j]);
+      a[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NIT; ++i) {
+      const v4i16 k0 = lds_tr8(sb + koff_a[i]), k1 = lds_tr8(sb + koff_b[i]);
+      float f[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = bf16_to_f32((uint32_t)(uint16_t)(e < 4 ? k0[e] : k1[e - 4]));
+        f[e] = __builtin_amdgcn_exp2f(fminf(x * kLog2eAbs, 0.f)) + fmaxf(x, 0.f);
+      }
+      if (valid < BT) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = 8 * g + e < valid ? f[e] : 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) zacc[i] += f[e];
+      uint32_t hw[4], lw[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        hw[e] = pack_bf16x2(f[2 * e], f[2 * e + 1]);
+        lw[e] = pack_bf16x2(f[2 * e] - __uint_as_float(hw[e] << 16),
+                            f[2 * e + 1] - __uint_as_float(hw[e] & 0xFFFF0000u));
+      }
+      const bf16x8 bh = as_bf16x8(make_uint4(hw[0], hw[1], hw[2], hw[3]));
+      const bf16x8 bl = as_bf16x8(make_uint4(lw[0], lw[1], lw[2], lw[3]));
+#pragma unroll
+      for (int j = 0; j < NJT; ++j) acc[j][i] = Mfma<bf16_t>::mma(a[j], bh, acc[j][i]);
+#pragma unroll
+      for (int j = 0; j < NJT; ++j) acc[j][i] = Mfma<bf16_t>::mma(a[j], bl, acc[j][i]);
+    }
+  }
+
+  float* part = partials + ((size_t)h * n_split + split) * part_floats<D>();
+#pragma unroll
+  for (int j = 0; j < NJT; ++j)
+#pragma unroll
+    for (int i = 0; i < NIT; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        part[(j * 16 + g * 4 + r) * D + (w * NIT + i) * 16 + c] = acc[j][i][r];
+#pragma unroll
+  for (int i = 0; i < NIT; ++i) {
+    const float zs = sum_over_groups(zacc[i]);
+    if (g == 0) part[D * D + (w * NIT + i) * 16 + c] = zs;
+  }
+}
+
 // Workgroup (token split, 64x64 state tile, head h) of the fp32 absorb: NTHR threads.
 template <int D>
 __device__ __forceinline__ void absorb_part_f32(int split, int tile, int h,

@@ -27,6 +27,13 @@ size_t absorb_partial_floats(int heads, int d);
 hipError_t launch_absorb(int dtype, int heads, int d, const void* k, const void* v, int64_t n_ev,
                          int64_t head_stride, float* S, float* z, float* partials,
                          uint16_t* s_split, hipStream_t stream);
+// The two passes of launch_absorb as separate launches: the partial states of n_ev
+// tokens, and their reduce into S, z (and s_split) by a later launch.
+hipError_t launch_absorb_parts(int dtype, int heads, int d, const void* k, const void* v,
+                               int64_t n_ev, int64_t head_stride, float* partials,
+                               hipStream_t stream);
+hipError_t launch_absorb_reduce(int dtype, int heads, int d, int64_t n_ev, const float* partials,
+                                float* S, float* z, uint16_t* s_split, hipStream_t stream);
 // s_split[h] = the bf16 hi and lo parts of S[h] ([H][2][d][d]): x ~= hi + lo, hi =
 // bf16(x), lo = bf16(x - hi), both rounded to nearest even. The bf16 attention
 // epilogue reads S in this form.
@@ -112,6 +119,17 @@ hipError_t launch_select_and_reduce(int dtype, int heads, int d, int nqb, int nk
                                     hipStream_t stream);
 
 // ---- block-sparse softmax attention + linear read ---------------------------------
+// Partial states of an absorb (launch_absorb's plan for n_ev tokens) formed by extra
+// workgroups appended to the bf16 attention launch, so that they run in the compute
+// units' free slots beside it (n_split == 0: none). The reduce is a later launch's.
+struct AbsorbAhead {
+  const void* k = nullptr;
+  const void* v = nullptr;
+  int64_t n_ev = 0, hs = 0;
+  int tps = 0, n_split = 0;
+  float* partials = nullptr;
+  int n_attn_wg = 0;  // set by the launcher: workgroups of the attention part
+};
 // With rope.cs, the queries are rotated in the kernel and the keys are read from
 // rope.k_out (head stride rope.k_out_hs), the rotated keys the pooling wrote, instead
 // of k; the linear read uses the unrotated queries.
@@ -120,7 +138,8 @@ hipError_t launch_sparse_swa(int dtype, int heads, int d, int block, const void*
                              int64_t kv_hs, const int32_t* sel, int top_k, const float* S,
                              const uint16_t* s_split, const float* z, float eps, float scale,
                              void* out, int64_t out_hs, hipStream_t stream,
-                             const Rope& rope = Rope(), const Ragged& rg = Ragged());
+                             const Rope& rope = Rope(), const Ragged& rg = Ragged(),
+                             const AbsorbAhead& ab = AbsorbAhead());
 
 // ---- backward (fixed selection) ---------------------------------------------------
 struct BwdArgs {

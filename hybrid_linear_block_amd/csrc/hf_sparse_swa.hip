@@ -27,6 +27,7 @@
 // window and sweep it in the same ascending order, which keeps the gathered K/V
 // blocks in that XCD's L2.
 #include "hf_device.h"
+#include "hf_absorb_parts.h"
 #include "hf_launch.h"
 
 namespace hf {
@@ -447,7 +448,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void s
     const bf16_t* __restrict__ vg, int64_t n_kv, int64_t kv_hs, const int32_t* __restrict__ sel,
     int top_k, int nqb, int n_logical, const uint16_t* __restrict__ s_split,
     const float* __restrict__ z, float eps, float scale, bf16_t* __restrict__ out,
-    int64_t out_hs, Rope rope, Ragged rg) {
+    int64_t out_hs, Rope rope, Ragged rg, AbsorbAhead ab) {
   constexpr int BLK = 64, NW = 2, NQT = 2, NMT = 4, NET = D / 16, NKS = D / 32;
   constexpr int CPR = D / 8;            // 16-byte chunks per K/V row
   constexpr int TCH = BLK * CPR;        // chunks per tile
@@ -458,8 +459,19 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void s
   __shared__ uint4 lds_k[TCH];
   __shared__ uint4 lds_v[TCH];
 
+  // Workgroups past the attention part form the partial states of an absorb in the
+  // same LDS (the two tile buffers are its two stages).
+  if (ab.n_split > 0 && (int)blockIdx.x >= ab.n_attn_wg) {
+    const int it = (int)blockIdx.x - ab.n_attn_wg;
+    absorb::absorb_part_bf16_w2<D>(it % ab.n_split, it / ab.n_split,
+                                   static_cast<const bf16_t*>(ab.k),
+                                   static_cast<const bf16_t*>(ab.v), ab.n_ev, ab.hs, ab.tps,
+                                   ab.n_split, ab.partials, lds_k, lds_v);
+    return;
+  }
   // Ragged windows: XCD x takes its work-balanced range of the head-major items.
-  const int logical = rg.on ? ragged_item(rg, blockIdx.x) : xcd_remap(blockIdx.x, gridDim.x, n_logical);
+  const int logical =
+      rg.on ? ragged_item(rg, blockIdx.x) : xcd_remap(blockIdx.x, ab.n_attn_wg, n_logical);
   if (logical < 0) return;
   const int h = logical / nqb, i = logical % nqb;
   const int lane = threadIdx.x & 63;
@@ -904,16 +916,22 @@ hipError_t launch_bf16(const void* q, int64_t n_q, int64_t q_hs, const void* k, 
                        int64_t n_kv, int64_t kv_hs, const int32_t* sel, int top_k, int heads,
                        const uint16_t* s_split, const float* z, float eps, float scale,
                        void* out, int64_t out_hs, hipStream_t stream, const Rope& rope,
-                       const Ragged& rg) {
+                       const Ragged& rg, const AbsorbAhead& ab_in) {
   const int nqb = (int)((n_q + 63) / 64);
   const int n_logical = nqb * heads;
   const int n_wg = rg.on ? 8 * ragged_width(rg) : (n_logical + 7) / 8 * 8;
+  // The absorb's workgroups come after the attention's: the dispatcher hands them the
+  // slots the attention leaves free, and they never delay an attention workgroup.
+  AbsorbAhead ab = ab_in;
+  ab.n_attn_wg = n_wg;
+  if (ab.n_ev <= 0) ab.n_split = 0;
+  const int grid = n_wg + heads * ab.n_split;
 #define HF_SWA_BF16(SHORT, ROPE)                                                             \
-  sparse_swa_bf16<D, SHORT, ROPE><<<n_wg, 128, 0, stream>>>(                                 \
+  sparse_swa_bf16<D, SHORT, ROPE><<<grid, 128, 0, stream>>>(                                 \
       static_cast<const bf16_t*>(q), n_q, q_hs, static_cast<const bf16_t*>(k),                \
       static_cast<const bf16_t*>(v), n_kv, kv_hs, sel, top_k, nqb, n_logical, s_split, z, eps,  \
       scale,                                                                                  \
-      static_cast<bf16_t*>(out), out_hs, rope, rg)
+      static_cast<bf16_t*>(out), out_hs, rope, rg, ab)
   // A window shorter than one block takes the short form (for ragged windows: the
   // shortest head's window, n_kv the call passes).
   if (rope.cs) {
@@ -951,17 +969,17 @@ hipError_t launch_sparse_swa(int dtype, int heads, int d, int block, const void*
                              int64_t kv_hs, const int32_t* sel, int top_k, const float* S,
                              const uint16_t* s_split, const float* z, float eps, float scale,
                              void* out, int64_t out_hs, hipStream_t stream, const Rope& rope,
-                             const Ragged& rg) {
+                             const Ragged& rg, const AbsorbAhead& ab) {
 #define HF_SWA(T, D, BLK, QW)                                                                 \
   return launch<T, D, BLK, QW>(q, n_q, q_hs, k, v, n_kv, kv_hs, sel, top_k, heads, S, z, eps, \
                                scale, out, out_hs, stream, rope, rg)
   if (dtype == 0) {
     if (block == 64 && d == 128)
       return launch_bf16<128>(q, n_q, q_hs, k, v, n_kv, kv_hs, sel, top_k, heads, s_split, z,
-                              eps, scale, out, out_hs, stream, rope, rg);
+                              eps, scale, out, out_hs, stream, rope, rg, ab);
     if (block == 64 && d == 64)
       return launch_bf16<64>(q, n_q, q_hs, k, v, n_kv, kv_hs, sel, top_k, heads, s_split, z,
-                             eps, scale, out, out_hs, stream, rope, rg);
+                             eps, scale, out, out_hs, stream, rope, rg, ab);
   } else {
     if (block == 16 && d == 64) HF_SWA(float, 64, 16, 16);
     if (block == 16 && d == 128) HF_SWA(float, 128, 16, 16);

@@ -193,6 +193,40 @@ class HybridAttentionState:
                    "hf_absorb_and_attend_cached")
         return out
 
+    def absorb_and_attend_ahead(self, q: torch.Tensor, k_win: torch.Tensor, v_win: torch.Tensor,
+                                top_k: int, k_next: Optional[torch.Tensor] = None,
+                                v_next: Optional[torch.Tensor] = None,
+                                out: Optional[torch.Tensor] = None,
+                                sel_out: Optional[torch.Tensor] = None,
+                                next_index: Optional[int] = None,
+                                win_index: Optional[int] = None) -> torch.Tensor:
+        """Attend the chunk with the state as of the previous call's pending absorb
+        (reduced first), and form the partial states of the next chunk's evicted tokens
+        (k_next, v_next) inside the attention launch as the new pending absorb
+        (hf_absorb_and_attend_ahead). absorb_flush() completes a pending absorb."""
+        out, args = self._attend_args(q, k_win, v_win, top_k, out, sel_out)
+        if k_next is None:
+            n_next, nx_hs, kp, vp = 0, 0, 0, 0
+        else:
+            n_next, nx_hs = self._evicted_args(k_next, v_next)
+            kp, vp = k_next.data_ptr(), v_next.data_ptr()
+        idx = self.next_ev_index if next_index is None else next_index
+        a = list(args)
+        a.insert(7, -1 if win_index is None else int(win_index))  # after kv_head_stride
+        _check(B.hf_absorb_and_attend_ahead(self.handle, *a, kp, vp, n_next, nx_hs, idx,
+                                            _stream(self.device)),
+               "hf_absorb_and_attend_ahead")
+        return out
+
+    def absorb_flush(self) -> None:
+        """Reduce the pending absorb of absorb_and_attend_ahead into S and z."""
+        _check(B.hf_absorb_flush(self.handle, _stream(self.device)), "hf_absorb_flush")
+
+    @property
+    def pending_ev(self) -> int:
+        """Tokens whose partial states wait for the next call to reduce them."""
+        return B.hf_pending_ev(self.handle)
+
     def attend_ragged(self, q: torch.Tensor, k_flat: torch.Tensor, v_flat: torch.Tensor,
                       kv_offsets, top_k, out: Optional[torch.Tensor] = None,
                       sel_out: Optional[torch.Tensor] = None) -> torch.Tensor:

@@ -191,6 +191,47 @@ hf_status hf_absorb_and_attend_cached(hf_state* st, const void* k_ev, const void
                                       void* out, int64_t out_head_stride, int32_t* sel_out,
                                       void* stream);
 
+/* One chunk of a stream with its absorb one call ahead ([EN] 2.A.1 and 2.A.2; [ABS]):
+ * the tokens that leave the window at the NEXT chunk (k_next, v_next: [H][n_next][d],
+ * head stride next_head_stride, first absolute index next_index) are known a chunk
+ * early, so their partial states are formed inside this call's attention launch, by
+ * workgroups appended to it that run in the compute-unit slots the attention leaves
+ * free (bf16; fp32 states take a launch after the attention), and kept in the
+ * workspace as the handle's pending absorb. The next call of this function reduces the
+ * pending absorb into S and z in its selection launch, before its attention reads them.
+ * So the sequence
+ *     hf_absorb_evicted(E0); ahead(chunk 0, E1); ahead(chunk 1, E2); ...
+ *     ahead(chunk c, E(c+1)); hf_absorb_flush()
+ * gives the outputs, selections, S and z of
+ *     hf_absorb_and_attend(E0, chunk 0); hf_absorb_and_attend(E1, chunk 1); ...
+ *     hf_absorb_and_attend(E(c+1), empty chunk)
+ * bit for bit (the partial states and their reduce are the same kernels' arithmetic in
+ * the same order), with one launch of work fewer per chunk on the critical path. The
+ * chunk arguments are those of hf_attend_chunk; win_index >= 0 selects the cached key
+ * pooling of hf_attend_chunk_cached (same requirements), win_index < 0 none.
+ * next_index must equal the state's next eviction index, which advances by n_next
+ * once the partial states are enqueued (n_next == 0: nothing becomes pending). Until
+ * it is reduced, S and z lack the pending tokens: every other call of the handle that
+ * reads or writes S and z (the absorb and attend calls, the managed window, the ragged
+ * attention, hf_attend_backward) first enqueues the pending reduce on its own stream,
+ * and hf_absorb_flush does only that; a caller that reads S or z itself flushes first.
+ * Calls of one handle stay ordered on one stream (the pending partial states live in
+ * its workspace). n_q == 0 forms the partial states in a launch of their own. */
+hf_status hf_absorb_and_attend_ahead(hf_state* st, const void* q, int64_t n_q,
+                                     int64_t q_head_stride, const void* k_win, const void* v_win,
+                                     int64_t n_kv, int64_t kv_head_stride, int64_t win_index,
+                                     int32_t top_k, void* out, int64_t out_head_stride,
+                                     int32_t* sel_out, const void* k_next, const void* v_next,
+                                     int64_t n_next, int64_t next_head_stride,
+                                     int64_t next_index, void* stream);
+
+/* Reduce the pending absorb of hf_absorb_and_attend_ahead into S and z on `stream`
+ * (a no-op when none is pending). */
+hf_status hf_absorb_flush(hf_state* st, void* stream);
+
+/* Tokens of the pending absorb (0: none; -1 for a NULL handle). */
+int64_t hf_pending_ev(const hf_state* st);
+
 /* Forget the cached key sums of hf_attend_chunk_cached (for example before the
  * handle serves another stream). Host-side only; enqueues nothing. */
 hf_status hf_key_cache_reset(hf_state* st);

@@ -153,6 +153,10 @@ def test_calls_on_null_state_are_rejected():
         B.HF_ERR_INVALID_ARG
     assert hla.hf_absorb_and_attend_cached(None, A, A, 10, 1280, 0, A, 10, 1280, A, A, 16, 2048,
                                            0, 1, A, 1280, 0, 0) == B.HF_ERR_INVALID_ARG
+    assert hla.hf_absorb_and_attend_ahead(None, A, 10, 1280, A, A, 16, 2048, -1, 1, A, 1280, 0,
+                                          A, A, 10, 1280, 0, 0) == B.HF_ERR_INVALID_ARG
+    assert hla.hf_absorb_flush(None, 0) == B.HF_ERR_INVALID_ARG
+    assert hla.hf_pending_ev(None) == -1
     assert hla.hf_key_cache_reset(None) == B.HF_ERR_INVALID_ARG
     assert hla.hf_window_attach(None, A, A, 20, 10) == B.HF_ERR_INVALID_ARG
     assert hla.hf_window_begin_chunk(None, 1, 0)[0] == B.HF_ERR_INVALID_ARG

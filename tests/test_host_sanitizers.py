@@ -84,6 +84,10 @@ int absorb_items(int, int heads, int, const AbsorbPlan& p) { return heads * p.n_
 size_t absorb_partial_floats(int heads, int d) { return (size_t)heads * 24 * (d * d + d); }
 hipError_t launch_absorb(int, int, int, const void*, const void*, int64_t, int64_t, float*, float*,
                          float*, uint16_t*, hipStream_t) { return hipErrorNoDevice; }
+hipError_t launch_absorb_parts(int, int, int, const void*, const void*, int64_t, int64_t, float*,
+                               hipStream_t) { return hipErrorNoDevice; }
+hipError_t launch_absorb_reduce(int, int, int, int64_t, const float*, float*, float*, uint16_t*,
+                                hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_split_state(int, int, const float*, uint16_t*, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_rope_table(float2*, int, int, double, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_block_pool(int, int, int, int, const void*, int64_t, int64_t, const void*, int64_t,
@@ -102,7 +106,8 @@ hipError_t launch_select_and_reduce(int, int, int, int, int, int, int, const flo
 hipError_t launch_sparse_swa(int, int, int, int, const void*, int64_t, int64_t, const void*,
                              const void*, int64_t, int64_t, const int32_t*, int, const float*,
                              const uint16_t*, const float*, float, float, void*, int64_t,
-                             hipStream_t, const Rope&, const Ragged&) { return hipErrorNoDevice; }
+                             hipStream_t, const Rope&, const Ragged&, const AbsorbAhead&) {
+  return hipErrorNoDevice; }
 hipError_t launch_attend_backward(int, int, int, const BwdArgs&, int, hipStream_t) {
   return hipErrorNoDevice; }
 hipError_t launch_absorb_backward(int, int, int, const void*, const void*, int64_t, int64_t,
@@ -143,6 +148,9 @@ int main() {
   const int r = hf_state_init(&c, (float*)A, (float*)A, A, ws, 1, 0, nullptr, &st);
   if (r == HF_OK) {  // a device is present: exercise the handle's host paths too
     EXPECT(hf_absorb_evicted(st, A, A, 10, 10 * 128, 5, nullptr), HF_ERR_STATE);
+    EXPECT(hf_absorb_and_attend_ahead(st, A, 10, 1280, A, A, 100, 12800, -1, 1, A, 1280, nullptr,
+                                      A, A, 10, 1280, 5, nullptr), HF_ERR_STATE);
+    EXPECT(hf_pending_ev(st), 0);
     EXPECT(hf_attend_chunk(st, A, 10, 1280, A, A, 100, 12800, 3, A, 1280, nullptr, nullptr),
            HF_ERR_INVALID_ARG);
     hf_state_destroy(st);
@@ -151,6 +159,10 @@ int main() {
     EXPECT(st == nullptr, 1);
   }
   // null handles and null arguments
+  EXPECT(hf_absorb_and_attend_ahead(nullptr, A, 10, 1280, A, A, 10, 1280, -1, 1, A, 1280, nullptr,
+                                    A, A, 10, 1280, 0, nullptr), HF_ERR_INVALID_ARG);
+  EXPECT(hf_absorb_flush(nullptr, nullptr), HF_ERR_INVALID_ARG);
+  EXPECT(hf_pending_ev(nullptr), -1);
   EXPECT(hf_absorb_evicted(nullptr, A, A, 10, 1280, 0, nullptr), HF_ERR_INVALID_ARG);
   EXPECT(hf_attend_chunk(nullptr, A, 10, 1280, A, A, 10, 1280, 1, A, 1280, nullptr, nullptr),
          HF_ERR_INVALID_ARG);

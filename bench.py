@@ -4,9 +4,14 @@
 A step is one pass of the whole hot path over one batch of synthetic input: the
 absorb of the evicted tokens into the linear state and the hybrid attention of
 the chunk (block pooling, block scores and top-K selection, block-sparse
-attention with the fused linear read), issued as one hf_absorb_and_attend call
-on one stream (`--side-stream`: its absorb on a second stream next to the block
-selection; `--serial`: hf_absorb_evicted then hf_attend_chunk). The default
+attention with the fused linear read), issued as one hf_absorb_and_attend_ahead
+call on one stream: each input set is a stream of chunks whose evicted tokens are
+known a chunk early, so a step reduces the absorb that the set's previous step
+formed (in its selection launch) and forms the next one inside its attention
+launch; every step still absorbs n_ev tokens and attends one chunk (`--no-ahead`:
+one hf_absorb_and_attend call, the absorb's partial states in the pooling launch;
+`--side-stream`: that call's absorb on a second stream next to the block selection;
+`--serial`: hf_absorb_evicted then hf_attend_chunk). The default
 workload is one Wan-1.3B-like layer: 12 heads, d = 128, a 3-frame chunk (4680
 query tokens) over a 9-frame window (14040 key/value tokens), 64-token blocks,
 top-K = 55 of 220 key blocks, 4680 evicted tokens. Inputs are resident in HBM
@@ -43,6 +48,7 @@ METRIC = "hybrid-attention ms/chunk/layer and effective TFLOP/s (% of MFMA peak)
 PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # MI355X dense MFMA peaks
 PEAK_HBM_GBS = 8000.0
 SWA_SOURCES = ("hybrid_linear_block_amd/csrc/hf_sparse_swa.hip",
+               "hybrid_linear_block_amd/csrc/hf_absorb_parts.h",
                "hybrid_linear_block_amd/csrc/hf_device.h")
 PEAK_HBM_BPS = 8.0e12  # MI355X HBM3E, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_sparse_swa_wan_layer.json")
@@ -93,10 +99,9 @@ def parse():
                         "10000, 1560 tokens per frame) with this cap on the position index")
     p.add_argument("--side-stream", action="store_true",
                    help="hf_absorb_and_attend with the absorb on a side stream")
-    p.add_argument("--ahead", action="store_true",
-                   help="hf_absorb_and_attend_ahead: each step attends with the absorb its "
-                        "previous step formed (reduced in the selection launch) and forms the "
-                        "next chunk's absorb inside the attention launch")
+    p.add_argument("--no-ahead", action="store_true",
+                   help="one hf_absorb_and_attend call per step instead of "
+                        "hf_absorb_and_attend_ahead (the absorb formed next to the pooling)")
     p.add_argument("--cpu-reps", type=int, default=3)
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="also run device copies of this size (HBM counter calibration)")
@@ -592,10 +597,10 @@ def main():
     streams = args.streams or args.cached_pooling or args.managed_window
     if streams and args.workload != "wan_layer_bf16":
         sys.exit("--streams / --cached-pooling / --managed-window run the wan_layer_bf16 shapes")
-    if streams and (args.side_stream or args.serial or args.ahead):
+    if streams and (args.side_stream or args.serial):
         sys.exit("--streams / --cached-pooling / --managed-window issue one stream's calls")
-    if args.ahead and (args.side_stream or args.serial):
-        sys.exit("--ahead issues one call per step on one stream")
+    # The ahead call is the step of caller-held windows on one stream (the default).
+    args.ahead = not (args.no_ahead or args.serial or args.side_stream or streams)
     if args.managed_window:
         if args.ring_windows < 2:
             sys.exit("--ring-windows must be at least 2")
@@ -724,10 +729,11 @@ def main():
     traffic = None
     if os.path.exists(TRAFFIC_FILE) and args.workload == "wan_layer_bf16":
         tr = json.load(open(TRAFFIC_FILE))
-        if tr.get("source_sha256") == swa_source_sha():
+        if tr.get("source_sha256") == swa_source_sha() and \
+                tr.get("ahead", False) == bool(args.ahead):
             traffic = tr.get("hbm_bytes_per_launch")
     roofline = dict(bound="mfma", achieved=round(achieved, 2), peak=peak, unit="TFLOP/s",
-                    frac=round(achieved / peak, 4), traffic=traffic if not args.ahead else None,
+                    frac=round(achieved / peak, 4), traffic=traffic,
                     kernel="sparse_swa" + (" (with the next absorb's partial states)"
                                            if args.ahead else ""),
                     flop_per_launch=int(swa_flop), avg_launch_us=round(swa_us, 2))

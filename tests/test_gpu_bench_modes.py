@@ -20,7 +20,7 @@ KEYS = {"metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
 @pytest.mark.gpu
 @pytest.mark.parametrize("mode", [
     [], ["--streams"], ["--cached-pooling"], ["--managed-window"], ["--ragged"],
-    ["--rope-cap", "8"], ["--backward"], ["--serial"], ["--side-stream"], ["--ahead"],
+    ["--rope-cap", "8"], ["--backward"], ["--serial"], ["--side-stream"], ["--no-ahead"],
 ])
 def test_bench_mode_prints_contract_line(mode):
     print("bench mode", mode, flush=True)

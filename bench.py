@@ -220,10 +220,20 @@ class StreamSet(LayerSet):
         p = (self.t - 3) % self.positions
         if p == 0 and self.t > 3 and self.cached:
             self.st.key_cache_reset()
-        self.position(p)
-        self.st.absorb_and_attend(self.kev, self.vev, self.q, self.kw, self.vw, self.top_k,
-                                  out=self.out,
-                                  win_index=self.T * (3 * self.t - 6) if self.cached else None)
+        win = self.T * (3 * self.t - 6) if self.cached else None
+        if self.ahead:  # the next step's evicted frames are known now
+            if self.t == 3:  # the stream's first step: its own evicted frames up front
+                self.position(p)
+                self.st.absorb_evicted(self.kev, self.vev)
+            self.position((p + 1) % self.positions)
+            k_next, v_next = self.kev, self.vev
+            self.position(p)
+            self.st.absorb_and_attend_ahead(self.q, self.kw, self.vw, self.top_k, k_next=k_next,
+                                            v_next=v_next, out=self.out, win_index=win)
+        else:
+            self.position(p)
+            self.st.absorb_and_attend(self.kev, self.vev, self.q, self.kw, self.vw, self.top_k,
+                                      out=self.out, win_index=win)
         self.t += 1
 
     def pool_bytes_cached(self, summed_frames=3):
@@ -528,6 +538,29 @@ def ragged_main(args, torch, hla, synth):
     }), flush=True)
 
 
+def issue_text(args, streams) -> str:
+    """How the bench issues a step (the JSON line's config.issue)."""
+    if args.managed_window:
+        return ("hf_window_begin_chunk, K/V chunk copied into the ring slot, hf_window_attend; "
+                "one stream per input set")
+    if args.serial:
+        return "hf_absorb_evicted, then hf_attend_chunk"
+    if args.side_stream:
+        return "hf_absorb_and_attend, absorb on a side stream"
+    call = ("hf_absorb_and_attend_ahead" if args.ahead else
+            "hf_absorb_and_attend_cached" if args.cached_pooling else "hf_absorb_and_attend")
+    text = call + ", one stream"
+    if args.ahead:
+        text += (": each step reduces the absorb that the previous step of its input set formed "
+                 "and forms the next one inside its attention launch")
+    if streams:
+        text += (f"; each input set is a stream whose window moves by one chunk per step "
+                 f"({args.stream_positions} positions per buffer" +
+                 (", key pooling from the 8-token key-sum cache, reset at each wrap)"
+                  if args.cached_pooling else ")"))
+    return text
+
+
 def cpu_baseline(layer: LayerSet, reps: int):
     """The float64 oracle on the host cores: the same layer step, median of `reps`."""
     import numpy as np
@@ -599,8 +632,9 @@ def main():
         sys.exit("--streams / --cached-pooling / --managed-window run the wan_layer_bf16 shapes")
     if streams and (args.side_stream or args.serial):
         sys.exit("--streams / --cached-pooling / --managed-window issue one stream's calls")
-    # The ahead call is the step of caller-held windows on one stream (the default).
-    args.ahead = not (args.no_ahead or args.serial or args.side_stream or streams)
+    # The ahead call is the step of one stream's calls (the default), with caller-held
+    # windows (not the managed window, which absorbs at its own calls).
+    args.ahead = not (args.no_ahead or args.serial or args.side_stream or args.managed_window)
     if args.managed_window:
         if args.ring_windows < 2:
             sys.exit("--ring-windows must be at least 2")
@@ -844,19 +878,7 @@ def main():
                          f"{-(-s0.n_kv // 64)}, {s0.n_ev} evicted tokens absorbed per step"),
             "heads": s0.H, "head_dim": s0.d, "n_q": s0.n_q, "n_kv": s0.n_kv, "n_ev": s0.n_ev,
             "block": 64, "top_k": top_k, "input_sets": n_sets, "layers_per_step": per_step_layers,
-            "issue": ("hf_window_begin_chunk, K/V chunk copied into the ring slot, "
-                      "hf_window_attend; one stream per input set" if args.managed_window else
-                      "hf_absorb_evicted, then hf_attend_chunk" if args.serial else
-                      "hf_absorb_and_attend, absorb on a side stream" if args.side_stream else
-                      "hf_absorb_and_attend_ahead, one stream: each step reduces the absorb the "
-                      "previous step of its input set formed and forms the next one inside its "
-                      "attention launch" if args.ahead else
-                      (("hf_absorb_and_attend_cached" if args.cached_pooling else
-                        "hf_absorb_and_attend") + ", one stream; each input set is a stream "
-                       f"whose window moves by one chunk per step ({args.stream_positions} "
-                       "positions per buffer" +
-                       (", key cache reset at each wrap)" if args.cached_pooling else ")"))
-                      if streams else "hf_absorb_and_attend, one stream"),
+            "issue": issue_text(args, streams),
             "streams": bool(streams),
             "cached_pooling": bool(args.cached_pooling),
             "managed_window": window,

@@ -4,7 +4,10 @@ Each step absorbs the frames that left the 9-frame window (from step 3 on) and
 attends the new 3-frame chunk. At every step the device state (S, z) is compared
 with the float64 state of all tokens evicted so far, the selection with the
 oracle's, and sampled output blocks with the oracle's outputs. K drifts slowly
-(random-walk mean per frame) so the state stays non-trivial.
+(random-walk mean per frame) so the state stays non-trivial. A second state runs the
+same stream through the absorb-ahead call (each step forms the next step's absorb in
+its attention launch): its outputs, selections, S and z equal the first state's bit
+for bit at every step.
 """
 
 import time
@@ -37,6 +40,8 @@ def test_long_stream_60_steps():
     print(f"generated {F} frames in {time.time() - t0:.1f}s", flush=True)
     st = hla.HybridAttentionState(H, d, B, torch.bfloat16, max_n_q=c * T, max_n_kv=W * T,
                                   max_n_ev=c * T, max_top_k=synth.top_k_count(wl.top_k_frac, 220))
+    ah = hla.HybridAttentionState(H, d, B, torch.bfloat16, max_n_q=c * T, max_n_kv=W * T,
+                                  max_n_ev=c * T, max_top_k=synth.top_k_count(wl.top_k_frac, 220))
     S, z = oracle.state_init(H, d)
     rng = np.random.default_rng(5)
     n_steps = F // c
@@ -52,9 +57,17 @@ def test_long_stream_60_steps():
         nkb = -(-n_kv // B)
         K = synth.top_k_count(wl.top_k_frac, nkb)
         sel = torch.empty((H, c * T // B + 1, K), dtype=torch.int32, device="cuda")
-        out = st.attend_chunk(dev_bf16(qbits), kd[:, w0 * T:w1 * T], vd[:, w0 * T:w1 * T], K,
-                              sel_out=sel)
+        qd = dev_bf16(qbits)
+        out = st.attend_chunk(qd, kd[:, w0 * T:w1 * T], vd[:, w0 * T:w1 * T], K, sel_out=sel)
+        (n0, n1), _ = hla.window_frames(t + 1, c, W)  # the next step's evicted frames
+        sel_ah = torch.empty_like(sel)
+        out_ah = ah.absorb_and_attend_ahead(qd, kd[:, w0 * T:w1 * T], vd[:, w0 * T:w1 * T], K,
+                                            k_next=kd[:, n0 * T:n1 * T], v_next=vd[:, n0 * T:n1 * T],
+                                            sel_out=sel_ah)
         torch.cuda.synchronize()
+        assert torch.equal(sel_ah, sel) and torch.equal(out_ah.view(torch.int16), out.view(torch.int16))
+        assert torch.equal(ah.S, st.S) and torch.equal(ah.z, st.z)
+        assert ah.pending_ev == (n1 - n0) * T
         fro, zrel = state_close(host_f64(st.S), host_f64(st.z), S, z, "bf16")
         q64 = oracle.as_f64(qbits, "bf16")
         k64 = oracle.as_f64(kbits[:, w0 * T:w1 * T], "bf16")

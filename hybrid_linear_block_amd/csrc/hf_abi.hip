@@ -32,6 +32,11 @@ struct hf_state {
   // Tokens whose partial states an ahead call left in `partials` for the next call to
   // reduce into S and z (0: none pending).
   int64_t pend_n = 0;
+  // Managed window: partial states formed ahead, in an attention launch, for the tokens
+  // [spec_lo, spec_lo + spec_n) that leave the window at the next chunk if it has the
+  // current chunk's size. They are not absorbed yet: the next absorb of exactly those
+  // tokens reduces them, anything else that writes `partials` drops them.
+  int64_t spec_lo = 0, spec_n = 0;
   uint16_t* s_split;  // bf16 hi/lo split of S (bf16 states), kept in step with S
   // Cache of 8-token key sums for the cached calls: ring of kc_cap groups per head;
   // the absolute groups [kc_lo, kc_hi) hold the sums of the last cached window.
@@ -344,6 +349,7 @@ static hipError_t enqueue_absorb(hf_state* st, const void* k_ev, const void* v_e
   const hf_config& c = st->cfg;
   const hipError_t e = flush_pending(st, s);
   if (e != hipSuccess) return e;
+  st->spec_n = 0;  // its partial states take the buffer
   return timed(st, HF_KERNEL_ABSORB, s, [&]() {
     return hf::launch_absorb(c.dtype, c.num_heads, c.head_dim, k_ev, v_ev, n_ev, ev_head_stride,
                              st->S, st->z, st->partials, st->s_split, s);
@@ -444,6 +450,7 @@ static hipError_t enqueue_attend(hf_state* st, const void* q, int64_t n_q, int64
     const hipError_t e = flush_pending(st, s);
     if (e != hipSuccess) return e;
   }
+  if (fa || next) st->spec_n = 0;  // partial states of this call take the buffer
   const int64_t reduce_n = fa ? 0 : st->pend_n;
   const int nqb = (int)ceil_div(n_q, c.block_size);
   const int nkb = (int)ceil_div(n_kv, c.block_size);
@@ -658,6 +665,7 @@ hf_status hf_absorb_and_attend_ahead(hf_state* st, const void* q, int64_t n_q,
     if (n_q == 0) {  // no attention launch to carry the partial states: a launch of their own
       hipError_t err = flush_pending(st, s);
       if (err == hipSuccess && n_next > 0) {
+        st->spec_n = 0;
         err = timed(st, HF_KERNEL_ABSORB, s, [&]() {
           return hf::launch_absorb_parts(c.dtype, c.num_heads, c.head_dim, k_next, v_next, n_next,
                                          next_head_stride, st->partials, s);
@@ -702,6 +710,7 @@ hf_status hf_window_attach(hf_state* st, void* k_ring, void* v_ring, int64_t rin
   st->v_ring = static_cast<char*>(v_ring);
   st->win_on = st->win_ok = true;
   st->kc_lo = st->kc_hi = 0;  // cached key sums may come from other buffers
+  st->spec_n = 0;
   return HF_OK;
 }
 
@@ -725,8 +734,16 @@ hf_status hf_window_begin_chunk(hf_state* st, int64_t n, void* stream, void** k_
     const hf_status r = on_device(st->device, [&]() -> hipError_t {
       hipError_t e = hipSuccess;
       if (p.absorb_n > 0) {
-        e = enqueue_absorb(st, st->k_ring + p.absorb_row * row, st->v_ring + p.absorb_row * row,
-                           p.absorb_n, hs, s);
+        if (st->spec_n == p.absorb_n && st->spec_lo == st->next_ev) {
+          // the previous attend formed these tokens' partial states: reduce them
+          st->pend_n = st->spec_n;
+          st->spec_n = 0;
+          e = flush_pending(st, s);
+          if (e != hipSuccess) st->pend_n = 0;
+        } else {
+          e = enqueue_absorb(st, st->k_ring + p.absorb_row * row,
+                             st->v_ring + p.absorb_row * row, p.absorb_n, hs, s);
+        }
         absorbed = e == hipSuccess;
       }
       if (e == hipSuccess)
@@ -773,27 +790,54 @@ hf_status hf_window_attend(hf_state* st, const void* q, int64_t n_q, int64_t q_h
   // of past chunks stay cached, since the current chunk's keys may still change.
   const bool cached = check_window(v.ws, v.n_kv) == HF_OK;
   const hf::KeyCache kc = key_cache(st, v.ws);
-  bool absorbed = false;
+  // The tokens that leave the window at the next chunk if it has this chunk's size. If
+  // they all belong to past chunks (whose K and V no longer change), their partial
+  // states are formed in this call's attention launch; the next absorb uses them if it
+  // absorbs exactly these tokens.
+  const int64_t end = st->win.hi + st->win.cur;
+  const int64_t nx_lo = v.ws;
+  const int64_t nx_hi = hf::window_start(end + st->win.cur, st->win.win, v.ws);
+  const int64_t nx_n = nx_hi - nx_lo;
+  const bool spec_have = nx_n > 0 && st->spec_n == nx_n && st->spec_lo == nx_lo;
+  const bool form = n_q > 0 && nx_n > 0 && nx_n <= c.max_n_ev && nx_hi <= st->win.hi &&
+                    !spec_have;
+  const bool spec_hit = v.ev_n > 0 && st->spec_n == v.ev_n && st->spec_lo == st->next_ev;
+  bool absorbed = false, formed = false;
   const hf_status r = on_device(st->device, [&]() -> hipError_t {
+    if (spec_hit) {  // reduced as the pending absorb: in the selection launch, or alone
+      st->pend_n = st->spec_n;
+      st->spec_n = 0;
+    }
     if (n_q == 0) {
       hipError_t err = hipSuccess;
       if (v.ev_n > 0) {
-        err = enqueue_absorb(st, k_ev, v_ev, v.ev_n, hs, s);
+        err = spec_hit ? flush_pending(st, s) : enqueue_absorb(st, k_ev, v_ev, v.ev_n, hs, s);
         absorbed = err == hipSuccess;
       }
       return err;
     }
     const FusedAbsorb fa{k_ev, v_ev, v.ev_n, hs};
-    return enqueue_attend(st, q, n_q, q_head_stride, k_win, v_win, v.n_kv, hs, top_k, out,
-                          out_head_stride, sel_out, s, nullptr, v.ev_n > 0 ? &fa : nullptr,
-                          &absorbed, cached ? &kc : nullptr);
+    const FusedAbsorb nx{st->k_ring + (nx_lo - st->win.base) * row,
+                         st->v_ring + (nx_lo - st->win.base) * row, nx_n, hs};
+    const hipError_t err =
+        enqueue_attend(st, q, n_q, q_head_stride, k_win, v_win, v.n_kv, hs, top_k, out,
+                       out_head_stride, sel_out, s, nullptr,
+                       v.ev_n > 0 && !spec_hit ? &fa : nullptr, &absorbed,
+                       cached ? &kc : nullptr, form ? &nx : nullptr, &formed);
+    if (spec_hit) absorbed = st->pend_n == 0;  // the selection launch reduced them
+    return err;
   });
+  if (spec_hit && st->pend_n != 0) st->pend_n = 0;  // not enqueued: dropped
   if (cached && n_q > 0) {
     const int64_t past = st->win.hi / 8;  // whole groups of past chunks
     if (st->kc_hi > past) st->kc_hi = past;
     if (st->kc_lo > st->kc_hi) st->kc_lo = st->kc_hi;
   }
   if (absorbed) st->next_ev += v.ev_n;
+  if (formed) {
+    st->spec_lo = nx_lo;
+    st->spec_n = nx_n;
+  }
   return r;
 }
 

@@ -277,7 +277,14 @@ hf_status hf_window_begin_chunk(hf_state* st, int64_t n, void* stream, void** k_
  * whole groups, caching only the past chunks' keys. It may be called several times
  * per chunk (for example once per denoising step, with the slot's K and V rewritten
  * in between); results are bit for bit those of hf_absorb_and_attend over the same
- * window. HF_ERR_STATE without a window or before the first hf_window_begin_chunk. */
+ * window. The tokens that would leave the window at the next chunk if it had this
+ * chunk's size are known now; when they all belong to past chunks, their partial
+ * states are formed inside this call's attention launch (as hf_absorb_and_attend_ahead
+ * does). They are not absorbed yet: the next absorb of exactly those tokens (at the
+ * next chunk's hf_window_begin_chunk slide or hf_window_attend) reduces them instead of
+ * forming them again, and any call that forms other partial states drops them, so the
+ * results never depend on whether the next chunk had that size. HF_ERR_STATE without
+ * a window or before the first hf_window_begin_chunk. */
 hf_status hf_window_attend(hf_state* st, const void* q, int64_t n_q, int64_t q_head_stride,
                            int32_t top_k, void* out, int64_t out_head_stride, int32_t* sel_out,
                            void* stream);

@@ -103,6 +103,48 @@ def test_window_stream_matches_caller_windows(dt, d, B, T, ring_mult):
     compare_out(host_f64(o2), ref_out, dt)
 
 
+@pytest.mark.parametrize("dt,d,B,T", [("bf16", 128, 64, 320), ("f32", 64, 16, 100)])
+def test_window_chunk_sizes_vary(dt, d, B, T):
+    """Chunks of 3, 2, 3, 1, 3, 3, 2, 3, 3, 3 frames over a 9-frame window: the partial
+    states an attend forms for the next chunk's evicted tokens are used when the next
+    chunk has the same size and dropped otherwise. Every output, selection and state
+    equals bit for bit that of hf_absorb_and_attend over caller-held windows."""
+    H, W, K = 2, 9, 12
+    sizes = [3, 2, 3, 1, 3, 3, 2, 3, 3, 3]
+    std = 1.0 / np.sqrt(d)
+    nf = sum(sizes)
+    kd, _ = _draw(72, 41, H, nf * T, d, std, dt)
+    vd, _ = _draw(72, 42, H, nf * T, d, std, dt)
+    qd, _ = _draw(72, 43, H, nf * T, d, std, dt)
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    mk = dict(max_n_q=3 * T, max_n_kv=W * T, max_n_ev=3 * T, max_top_k=K)
+    ref = hla.HybridAttentionState(H, d, B, tdt, **mk)
+    win = hla.HybridAttentionState(H, d, B, tdt, **mk)
+    win.window_attach(W * T, 2 * W * T)
+    a = 0
+    for t, f in enumerate(sizes):
+        b = a + f * T
+        ks, vs = win.begin_chunk(b - a)
+        ks.copy_(kd[:, a:b])
+        vs.copy_(vd[:, a:b])
+        first, count = win.window_range()
+        assert first + count == b
+        k_t = min(K, -(-count // B))
+        nqb = -(-(b - a) // B)
+        sels = [torch.empty((H, nqb, k_t), dtype=torch.int32, device="cuda") for _ in range(2)]
+        o = win.window_attend(qd[:, a:b], k_t, sel_out=sels[0])
+        e0 = ref.next_ev_index
+        r = ref.absorb_and_attend(kd[:, e0:first], vd[:, e0:first], qd[:, a:b],
+                                  kd[:, first:b], vd[:, first:b], k_t, sel_out=sels[1])
+        torch.cuda.synchronize()
+        print(f"chunk {t}: {f} frames, window [{first}, {b}), absorbed up to {first}", flush=True)
+        assert win.next_ev_index == ref.next_ev_index == first
+        assert torch.equal(sels[0], sels[1])
+        assert torch.equal(_bits(o), _bits(r))
+        assert torch.equal(win.S, ref.S) and torch.equal(win.z, ref.z)
+        a = b
+
+
 def test_window_errors():
     H, d, B, T = 2, 128, 64, 320
     st = hla.HybridAttentionState(H, d, B, torch.bfloat16, max_n_q=T, max_n_kv=4 * T,

@@ -756,7 +756,10 @@ def main():
 
     # Roofline of the dominant kernel (sparse_swa): executed algorithmic FLOPs per launch
     # over its average event-timed duration.
-    swa_flop = statistics.mean(f["sparse_swa"] + (f["absorb"] if args.ahead else 0) for f in flops)
+    # The attention launch also forms an absorb's partial states in the ahead step and in
+    # the managed window (whose attend forms the next chunk's ahead).
+    ahead_like = bool(args.ahead or args.managed_window)
+    swa_flop = statistics.mean(f["sparse_swa"] + (f["absorb"] if ahead_like else 0) for f in flops)
     swa_us = kern_us["sparse_swa"]
     achieved = swa_flop / (swa_us * 1e-6) / 1e12
     peak = PEAK_MFMA_TFLOPS[wl.dtype]
@@ -769,14 +772,14 @@ def main():
     roofline = dict(bound="mfma", achieved=round(achieved, 2), peak=peak, unit="TFLOP/s",
                     frac=round(achieved / peak, 4), traffic=traffic,
                     kernel="sparse_swa" + (" (with the next absorb's partial states)"
-                                           if args.ahead else ""),
+                                           if ahead_like else ""),
                     flop_per_launch=int(swa_flop), avg_launch_us=round(swa_us, 2))
 
     # On one stream (the default) the absorb shares the attend call's launches: its
     # partial states are formed in the pooling launch and its reduce (which writes S
     # and z) runs in the selection launch, so its bytes and FLOPs are counted there.
     absorb_alone_us = kern_us.get("absorb")  # absorbs outside an attend call
-    fused = not args.side_stream and not args.serial and not args.ahead
+    fused = not args.side_stream and not args.serial and not ahead_like
     kbytes = dict(sets[0].bytes())
     if args.cached_pooling:  # a step whose window moved by one chunk (all but 1 in P)
         kbytes["block_pool"] = sets[0].pool_bytes_cached()
@@ -796,7 +799,7 @@ def main():
                        select_and_reduce=kern_us.get("score_select"),
                        sparse_swa=kern_us.get("sparse_swa"))
         names = ("absorb_and_pool", "select_and_reduce", "sparse_swa")
-    if args.ahead:  # partial states in the attention launch, their reduce in the selection's
+    if ahead_like:  # partial states in the attention launch, their reduce in the selection's
         sz = sets[0].state_bytes()
         kbytes = dict(block_pool=kbytes["block_pool"],
                       select_and_reduce=kbytes["score_select"] + sz,

@@ -50,6 +50,11 @@ __device__ __forceinline__ float ldf(const bf16_t* p) { return bf16_to_f32(*p); 
 
 __device__ __forceinline__ float phi_prime(float x) { return x > 0.f ? 1.f : __expf(x); }
 
+// 2^x on the transcendental unit (one v_exp_f32). Results below 2^-126 may flush to
+// zero; the weights and rescale factors this serves are then negligible next to the
+// row's largest term, which is at least 1/n.
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Sum over the TPR adjacent lanes of a row; every lane gets the same bits (xor
 // butterfly, commutative adds). Within a quad the exchanges are DPP quad
 // permutations (no LDS round trip); wider rows use ds_bpermute for the rest.
@@ -263,7 +268,7 @@ __device__ __forceinline__ void rows_body(
       for (int w = 0; w < 4; ++w) x[w] = row_sum<TPR>(x[w]) * sl2;
       const float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
       if (mx > m2) {
-        const float a = exp2f(m2 - mx);
+        const float a = exp2_hw(m2 - mx);
         l *= a;
 #pragma unroll
         for (int e = 0; e < DS; ++e) acc[e] *= a;
@@ -271,7 +276,7 @@ __device__ __forceinline__ void rows_body(
       }
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const float p = exp2f(x[w] - m2);
+        const float p = exp2_hw(x[w] - m2);
         l += p;
         const float* vr = tv + (u + w) * D + d0;
 #pragma unroll
@@ -285,13 +290,13 @@ __device__ __forceinline__ void rows_body(
       for (int e = 0; e < DS; ++e) s += qv[e] * kr[e];
       const float x = row_sum<TPR>(s) * sl2;
       if (x > m2) {
-        const float a = exp2f(m2 - x);
+        const float a = exp2_hw(m2 - x);
         l *= a;
 #pragma unroll
         for (int e = 0; e < DS; ++e) acc[e] *= a;
         m2 = x;
       }
-      const float p = exp2f(x - m2);
+      const float p = exp2_hw(x - m2);
       l += p;
       const float* vr = tv + u * D + d0;
 #pragma unroll
@@ -377,7 +382,7 @@ __device__ __forceinline__ void rows_body(
       }
       s = row_sum<TPR>(s);
       dp = row_sum<TPR>(dp);
-      const float p = exp2f(s * sl2 - lse2);
+      const float p = exp2_hw(s * sl2 - lse2);
       const float dl = scale * p * (dp - Dr);
 #pragma unroll
       for (int e = 0; e < DS; ++e) acc[e] += dl * kr[e];
@@ -472,7 +477,7 @@ __global__ __launch_bounds__(BT) void bwd_kv(
       }
       s = row_sum<TPR>(s);
       dp = row_sum<TPR>(dp);
-      const float p = exp2f(s * sl2 - tst[2 * u]);
+      const float p = exp2_hw(s * sl2 - tst[2 * u]);
       const float dl = scale * p * (dp - tst[2 * u + 1]);
 #pragma unroll
       for (int e = 0; e < DS; ++e) {
@@ -666,7 +671,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void b
       if (__builtin_amdgcn_ballot_w64(mx - m_run[n] > kSlack)) {  // wave-uniform
         const float d_blk = max_over_groups(mx) - m_run[n];
         const float shift = d_blk > kSlack ? d_blk : 0.f;
-        const float a = exp2f(-shift);
+        const float a = exp2_hw(-shift);
         m_run[n] += shift;
         l_part[n] *= a;
         d_part[n] *= a;
@@ -675,7 +680,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void b
       for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float e = exp2f(st[mt][n][r] - m_run[n]);
+          const float e = exp2_hw(st[mt][n][r] - m_run[n]);
           l_part[n] += e;
           d_part[n] += e * dp[mt][n][r];
         }
@@ -725,9 +730,9 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void b
         float lv[8];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          lv[r] = scale * exp2f(st[2 * c2][n][r] * sl2 - lse2[n]) * (dp[2 * c2][n][r] - Dr[n]);
+          lv[r] = scale * exp2_hw(st[2 * c2][n][r] * sl2 - lse2[n]) * (dp[2 * c2][n][r] - Dr[n]);
           lv[4 + r] =
-              scale * exp2f(st[2 * c2 + 1][n][r] * sl2 - lse2[n]) * (dp[2 * c2 + 1][n][r] - Dr[n]);
+              scale * exp2_hw(st[2 * c2 + 1][n][r] * sl2 - lse2[n]) * (dp[2 * c2 + 1][n][r] - Dr[n]);
         }
         split_bf16x8(lv, lh[c2][n], ll[c2][n]);
       }
@@ -916,7 +921,7 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2))) void bw
           for (int hf = 0; hf < 2; ++hf) {
             const int m = 2 * c2 + hf, ql = 16 * m + 4 * g + r;
             const float2 st = lds_ld8f(st_base + ql * 16u);
-            const float p = ql < n_valid ? exp2f(sc[m][r] * sl2 - st.x) : 0.f;
+            const float p = ql < n_valid ? exp2_hw(sc[m][r] * sl2 - st.x) : 0.f;
             pv[4 * hf + r] = p;
             lv[4 * hf + r] = scale * p * (dp[m][r] - st.y);
           }

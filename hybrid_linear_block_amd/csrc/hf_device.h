@@ -61,20 +61,18 @@ template <> struct Mfma<float> {
 // Pack 8 bf16 patterns (as 4 uint32 words, low half first) into an MFMA operand.
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 w) { return __builtin_bit_cast(bf16x8, w); }
 
-// Split 8 fp32 values into bf16 hi + lo operands (x ~= hi + lo to ~2^-17 relative).
+// Split 8 fp32 values into bf16 hi + lo operands (x ~= hi + lo to ~2^-17 relative):
+// hi = bf16(x), lo = bf16(x - hi), both rounded to nearest even by the hardware pack.
 __device__ __forceinline__ void split_bf16x8(const float* x, bf16x8& hi, bf16x8& lo) {
-  uint32_t h[8], l[8];
+  uint32_t h[4], l[4];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    h[e] = f32_to_bf16_bits(x[e]);
-    l[e] = f32_to_bf16_bits(x[e] - bf16_to_f32(h[e]));
+  for (int e = 0; e < 4; ++e) {
+    h[e] = pack_bf16x2(x[2 * e], x[2 * e + 1]);
+    l[e] = pack_bf16x2(x[2 * e] - __uint_as_float(h[e] << 16),
+                       x[2 * e + 1] - __uint_as_float(h[e] & 0xFFFF0000u));
   }
-  uint4 hw = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
-                        h[6] | (h[7] << 16));
-  uint4 lw = make_uint4(l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16),
-                        l[6] | (l[7] << 16));
-  hi = as_bf16x8(hw);
-  lo = as_bf16x8(lw);
+  hi = as_bf16x8(make_uint4(h[0], h[1], h[2], h[3]));
+  lo = as_bf16x8(make_uint4(l[0], l[1], l[2], l[3]));
 }
 
 // Word k / 16-bit half e of a 16-byte register value (indices are compile-time

@@ -659,14 +659,12 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void b
     mask(jb, st);
 #pragma unroll
     for (int n = 0; n < NQT; ++n) {
-      float mx = -INFINITY;
+      float mxr = -INFINITY;  // on the unscaled scores (sl2 > 0 keeps the order)
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          st[mt][n][r] *= sl2;
-          mx = fmaxf(mx, st[mt][n][r]);
-        }
+        for (int r = 0; r < 4; ++r) mxr = fmaxf(mxr, st[mt][n][r]);
+      const float mx = mxr * sl2;
       if (t == 0) m_run[n] = max_over_groups(mx);  // finite: a block holds a window key
       if (__builtin_amdgcn_ballot_w64(mx - m_run[n] > kSlack)) {  // wave-uniform
         const float d_blk = max_over_groups(mx) - m_run[n];
@@ -680,7 +678,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void b
       for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float e = exp2_hw(st[mt][n][r] - m_run[n]);
+          const float e = exp2_hw(__builtin_fmaf(st[mt][n][r], sl2, -m_run[n]));
           l_part[n] += e;
           d_part[n] += e * dp[mt][n][r];
         }
@@ -730,9 +728,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void b
         float lv[8];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          lv[r] = scale * exp2_hw(st[2 * c2][n][r] * sl2 - lse2[n]) * (dp[2 * c2][n][r] - Dr[n]);
-          lv[4 + r] =
-              scale * exp2_hw(st[2 * c2 + 1][n][r] * sl2 - lse2[n]) * (dp[2 * c2 + 1][n][r] - Dr[n]);
+          lv[r] = exp2_hw(st[2 * c2][n][r] * sl2 - lse2[n]) * (dp[2 * c2][n][r] - Dr[n]);
+          lv[4 + r] = exp2_hw(st[2 * c2 + 1][n][r] * sl2 - lse2[n]) * (dp[2 * c2 + 1][n][r] - Dr[n]);
         }
         split_bf16x8(lv, lh[c2][n], ll[c2][n]);
       }
@@ -759,7 +756,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void b
     __builtin_amdgcn_s_setprio(0);
     jb = jb_next;
   }
-  // lane holds dq[row 16n + c][16 et + 4g .. + 3]
+  // lane holds dq[row 16n + c][16 et + 4g .. + 3] / tau (dL went in without tau)
 #pragma unroll
   for (int n = 0; n < NQT; ++n) {
     const int64_t r = qrow0 + n * 16 + c;
@@ -768,7 +765,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void b
 #pragma unroll
     for (int et = 0; et < NET; ++et)
       *reinterpret_cast<float4*>(o + 16 * et + 4 * g) =
-          make_float4(gT[et][n][0], gT[et][n][1], gT[et][n][2], gT[et][n][3]);
+          make_float4(scale * gT[et][n][0], scale * gT[et][n][1], scale * gT[et][n][2],
+                      scale * gT[et][n][3]);
     if (g == 0) {
       float* st = rs + ((int64_t)h * nq_cap + r) * 4;
       st[0] = lse2[n];
@@ -911,23 +909,30 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2))) void bw
       rows_x(qaddr, kop, sc);
       // P and dL in the query order of the result layout (lane: queries 4g .. 4g + 3 of
       // tiles 2c2 and 2c2 + 1, key c), split into bf16 hi + lo
+      // (dL without tau, which the result takes once; rows past the chunk, in its last
+      // query block only, get weight 0)
       bf16x8 ph[2], pl[2], lh[2], ll[2];
+      auto weights = [&](auto masked) {
 #pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
-        float pv[8], lv[8];
+        for (int c2 = 0; c2 < 2; ++c2) {
+          float pv[8], lv[8];
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
+          for (int r = 0; r < 4; ++r)
 #pragma unroll
-          for (int hf = 0; hf < 2; ++hf) {
-            const int m = 2 * c2 + hf, ql = 16 * m + 4 * g + r;
-            const float2 st = lds_ld8f(st_base + ql * 16u);
-            const float p = ql < n_valid ? exp2_hw(sc[m][r] * sl2 - st.x) : 0.f;
-            pv[4 * hf + r] = p;
-            lv[4 * hf + r] = scale * p * (dp[m][r] - st.y);
-          }
-        split_bf16x8(pv, ph[c2], pl[c2]);
-        split_bf16x8(lv, lh[c2], ll[c2]);
-      }
+            for (int hf = 0; hf < 2; ++hf) {
+              const int m = 2 * c2 + hf, ql = 16 * m + 4 * g + r;
+              const float2 st = lds_ld8f(st_base + ql * 16u);
+              float p = exp2_hw(sc[m][r] * sl2 - st.x);
+              if constexpr (decltype(masked)::value) p = ql < n_valid ? p : 0.f;
+              pv[4 * hf + r] = p;
+              lv[4 * hf + r] = p * (dp[m][r] - st.y);
+            }
+          split_bf16x8(pv, ph[c2], pl[c2]);
+          split_bf16x8(lv, lh[c2], ll[c2]);
+        }
+      };
+      if (n_valid < BLK) weights(std::true_type{});
+      else weights(std::false_type{});
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2) {
         bf16x8 a[NET];
@@ -963,8 +968,8 @@ __global__ __launch_bounds__(BT) __attribute__((amdgpu_waves_per_eu(2))) void bw
     float* pv = dv + (int64_t)h * dkv_hs + key * D;
 #pragma unroll
     for (int e = 0; e < NET; ++e) {
-      *reinterpret_cast<float4*>(pk + 16 * e + 4 * g) =
-          make_float4(dkT[e][0], dkT[e][1], dkT[e][2], dkT[e][3]);
+      *reinterpret_cast<float4*>(pk + 16 * e + 4 * g) =  // dL went in without tau
+          make_float4(scale * dkT[e][0], scale * dkT[e][1], scale * dkT[e][2], scale * dkT[e][3]);
       *reinterpret_cast<float4*>(pv + 16 * e + 4 * g) =
           make_float4(dvT[e][0], dvT[e][1], dvT[e][2], dvT[e][3]);
     }

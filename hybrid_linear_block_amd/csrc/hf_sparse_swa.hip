@@ -749,14 +749,16 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void s
     bool move_any = false;
 #pragma unroll
     for (int n = 0; n < NQT; ++n) {
-      float m4[NMT];
 #pragma unroll
-      for (int mt = 0; mt < NMT; ++mt) {
+      for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) tx[mt][n][r] = __builtin_fmaf(st[mt][n][r], sl2, -m_run[n]);
-        m4[mt] = fmaxf(fmaxf(tx[mt][n][0], tx[mt][n][1]), fmaxf(tx[mt][n][2], tx[mt][n][3]));
-      }
-      mx[n] = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+      // a running max taking two new values per step (v_max3_f32)
+      float m = fmaxf(tx[0][n][0], tx[0][n][1]);
+#pragma unroll
+      for (int k = 2; k < 4 * NMT; k += 2)
+        m = fmaxf(fmaxf(m, tx[k / 4][n][k % 4]), tx[(k + 1) / 4][n][(k + 1) % 4]);
+      mx[n] = m;
       move_any |= mx[n] > kLazyMaxSlack;
     }
     if (__builtin_amdgcn_ballot_w64(move_any)) {  // wave-uniform

@@ -39,13 +39,16 @@ def _stream(seed, H, T, c, W, d, dt, steps):
 
 @pytest.mark.parametrize("dt,d,B,mode", [("bf16", 128, 64, "plain"), ("bf16", 64, 64, "plain"),
                                          ("f32", 64, 16, "plain"), ("bf16", 128, 64, "cached"),
-                                         ("bf16", 128, 64, "rope")])
+                                         ("bf16", 128, 64, "rope"), ("bf16", 128, 64, "ragged"),
+                                         ("f32", 64, 16, "ragged")])
 def test_ahead_stream_matches_fused_bitwise(dt, d, B, mode):
     """Seven chunks (window of 9 frames moving by 3 after the first steps; the tokens
     that leave it absorbed). Reference: hf_absorb_and_attend per chunk. Ahead: the
     first chunk's evicted tokens absorbed up front, then one ahead call per chunk
-    carrying the next chunk's evicted tokens, and a flush at the end."""
-    H, T, c, W, K, steps = 3, 320, 3, 9, 12, 7
+    carrying the next chunk's evicted tokens, and a flush at the end. "ragged": 100
+    tokens per frame, so every absorb ends in a partial 32-token tile and every chunk
+    and window in a partial block."""
+    H, T, c, W, K, steps = 3, 100 if mode == "ragged" else 320, 3, 9, 12, 7
     kd, vd, qd = _stream(71, H, T, c, W, d, dt, steps)
     mk = dict(max_n_q=c * T, max_n_kv=W * T, max_n_ev=c * T, max_top_k=K)
     tdt = torch.bfloat16 if dt == "bf16" else torch.float32

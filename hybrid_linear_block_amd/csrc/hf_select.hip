@@ -287,23 +287,25 @@ __device__ __forceinline__ void select_group(
     nkb = rg.kb0[h + 1] - rg.kb0[h];
     top_k = rg.top_k[h];
   }
-  __shared__ uint32_t key[SEL_QB][kMaxKeyBlocks];
-  __shared__ float4 qs[SEL_QB][D / 4];
-  const int i0 = qg * SEL_QB, tid = threadIdx.x;
-  const int nq = nqb - i0 < SEL_QB ? nqb - i0 : SEL_QB;
-  for (int x = tid; x < SEL_QB * (D / 4); x += SEL_THREADS) {
-    const int r = x / (D / 4), e = x % (D / 4);
-    qs[r][e] = r < nq ? reinterpret_cast<const float4*>(
-                            pooled_q + ((size_t)h * nqb_cap + i0 + r) * D)[e]
-                      : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-  __syncthreads();
   // Four adjacent lanes per key block, each over a quarter of the features (the
   // block's row is read as four contiguous segments); the quarters are added with
   // two lane exchanges, which give every lane of the four the same sum. One pass
   // covers SEL_THREADS / 4 key blocks (256), so the pooled key rows' load latency is
   // paid once.
   constexpr int PARTS = 4, EV = D / 4 / PARTS;  // float4s per quarter
+  __shared__ uint32_t key[SEL_QB][kMaxKeyBlocks];
+  // The pooled query rows by quarter, each quarter padded by one float4: the four
+  // quarters a wave reads at once then start 4 banks apart instead of on the same bank.
+  __shared__ float4 qs[SEL_QB][PARTS][EV + 1];
+  const int i0 = qg * SEL_QB, tid = threadIdx.x;
+  const int nq = nqb - i0 < SEL_QB ? nqb - i0 : SEL_QB;
+  for (int x = tid; x < SEL_QB * (D / 4); x += SEL_THREADS) {
+    const int r = x / (D / 4), e = x % (D / 4);
+    qs[r][e / EV][e % EV] = r < nq ? reinterpret_cast<const float4*>(
+                                         pooled_q + ((size_t)h * nqb_cap + i0 + r) * D)[e]
+                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  __syncthreads();
   static_assert(SEL_THREADS % PARTS == 0, "a key block's lanes stay in one pass");
   for (int x = tid; x < nkb * PARTS; x += SEL_THREADS) {
     const int j = x / PARTS, part = x % PARTS;
@@ -321,7 +323,7 @@ __device__ __forceinline__ void select_group(
       float s = 0.f;
 #pragma unroll
       for (int e = 0; e < EV; ++e) {
-        const float4 qv = qs[r][part * EV + e];
+        const float4 qv = qs[r][part][e];
         s += qv.x * kv[e].x;
         s += qv.y * kv[e].y;
         s += qv.z * kv[e].z;

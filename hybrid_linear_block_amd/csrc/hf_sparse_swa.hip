@@ -560,16 +560,12 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void s
 
   // Q operands (B of S^T = K Q^T): lane holds Q[16n + c][32s + 8g .. +8].
   bf16x8 qop[NQT][NKS];
-  auto load_q = [&]() {
 #pragma unroll
-    for (int n = 0; n < NQT; ++n) {
-      const int64_t r = qrow0 + n * 16 + c;
+  for (int n = 0; n < NQT; ++n) {
+    const int64_t r = qrow0 + n * 16 + c;
 #pragma unroll
-      for (int s = 0; s < NKS; ++s)
-        qop[n][s] = as_bf16x8(ld16(qh + r * D + s * 32 + g * 8, r < n_q));
-    }
-  };
-  load_q();
+    for (int s = 0; s < NKS; ++s) qop[n][s] = as_bf16x8(ld16(qh + r * D + s * 32 + g * 8, r < n_q));
+  }
 
   // Normaliser of the linear read, 1 / (z . phi(q) + eps), formed here (fp32) so that
   // it is ready when the epilogue folds the linear read into the accumulators.
@@ -593,38 +589,31 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void s
 #pragma unroll
     for (int n = 0; n < NQT; ++n) inv_den[n] = 1.f / (sum_over_groups(den[n]) + eps);
   }
-  // The QK operands carry the score scale: Q (turned by the row's position first, with
-  // the rotation) times tau log2(e), rounded to bf16 once. The products of a block then
-  // come out in log2 units, and the first k-step starts from minus the reference max
-  // (the MFMA's C operand), so the exponents need no per-score arithmetic. The linear
-  // read takes phi of the plain queries, loaded again for the epilogue.
-  const float sl2 = scale * kLog2e;
+  if constexpr (ROPE) {  // the QK operands turn by the row's position (rounded to bf16)
 #pragma unroll
-  for (int n = 0; n < NQT; ++n) {
-    const float2* cs = nullptr;
-    if constexpr (ROPE) {
+    for (int n = 0; n < NQT; ++n) {
       const int64_t r = qrow0 + n * 16 + c;
-      cs = rope_cs(rope, rope.q_row0 + (r < n_q ? r : n_q - 1));
-    }
+      const float2* cs = rope_cs(rope, rope.q_row0 + (r < n_q ? r : n_q - 1));
 #pragma unroll
-    for (int s = 0; s < NKS; ++s) {
-      const int p0 = 16 * s + 4 * g;  // this lane's pairs p0 .. p0 + 3
-      const uint4 qb = __builtin_bit_cast(uint4, qop[n][s]);
-      uint32_t wd[4];
+      for (int s = 0; s < NKS; ++s) {
+        const int p0 = 16 * s + 4 * g;  // this lane's pairs p0 .. p0 + 3
+        if (p0 < rope.half) {
+          const uint4 qb = __builtin_bit_cast(uint4, qop[n][s]);
+          uint32_t w[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float a = bf16_to_f32(half16(qb, 2 * e)), b = bf16_to_f32(half16(qb, 2 * e + 1));
-        if constexpr (ROPE) {
-          if (p0 + e < rope.half) {
-            const float2 t = cs[p0 + e];
-            const float a2 = a * t.x - b * t.y;
-            b = a * t.y + b * t.x;
-            a = a2;
+          for (int e = 0; e < 4; ++e) {
+            float a = bf16_to_f32(half16(qb, 2 * e)), b = bf16_to_f32(half16(qb, 2 * e + 1));
+            if (p0 + e < rope.half) {
+              const float2 t = cs[p0 + e];
+              const float a2 = a * t.x - b * t.y;
+              b = a * t.y + b * t.x;
+              a = a2;
+            }
+            w[e] = pack_bf16x2(a, b);
           }
+          qop[n][s] = as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
         }
-        wd[e] = pack_bf16x2(a * sl2, b * sl2);
       }
-      qop[n][s] = as_bf16x8(make_uint4(wd[0], wd[1], wd[2], wd[3]));
     }
   }
 
@@ -638,14 +627,13 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void s
   // the bf16 weights that go into O.
   f32x4 acc_l[NQT];
   float m_run[NQT];  // reference max of each query (log2 units), set by the first block
-  f32x4 negm[NQT];   // minus the reference, in all four places (k-step 0's C operand)
 #pragma unroll
   for (int n = 0; n < NQT; ++n) {
     m_run[n] = 0.f;
-    negm[n] = f32x4{0.f, 0.f, 0.f, 0.f};
     acc_l[n] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const bf16x8 ones = as_bf16x8(make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
+  const float sl2 = scale * kLog2e;
   // LDS byte addresses of this lane's operand reads. The swizzle reads row bits 0..3
   // only, so the key tile (16 rows), the 32-key chunk and the second half of a chunk
   // (16 rows) are constant offsets from these.
@@ -677,9 +665,11 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void s
     asm volatile("" ::"s"(jb_next));
 
     // ---- S^T = K Q^T: st[mt][n][r] = score(key 16mt + 4g + r, query 16n + c) ----
-    // st[mt][n] = (score - reference) in log2 units: k-step 0 adds its products to the
-    // query's minus-reference tuple.
     f32x4 st[NMT][NQT];
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+      for (int n = 0; n < NQT; ++n) st[mt][n] = f32x4{0.f, 0.f, 0.f, 0.f};
     // The operands of k-step 0 are read up front, those of step s + 1 while the
     // products of step s run (two steps ahead measured the same and held 16 more VGPRs).
     bf16x8 kop[NKS][NMT];
@@ -702,7 +692,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void s
       for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
         for (int n = 0; n < NQT; ++n)
-          st[mt][n] = Mfma<bf16_t>::mma(kop[s][mt], qop[n][s], s == 0 ? negm[n] : st[mt][n]);
+          st[mt][n] = Mfma<bf16_t>::mma(kop[s][mt], qop[n][s], st[mt][n]);
       if (s + 1 < NKS) {
 #pragma unroll
         for (int mt = 0; mt < NMT; ++mt) {  // one read of step s + 1 after every 2 products
@@ -737,53 +727,52 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void s
           for (int n = 0; n < NQT; ++n) st[mt][n][r] = out ? -INFINITY : st[mt][n][r];
         }
     }
-    // The exponent of every weight relative to the query's reference max is st itself.
-    // The reference moves only when some key of the block exceeds it by more than the
+    // Exponent of every weight relative to the query's reference max, t = s tau log2 e
+    // - m (the FMA output needs no canonicalisation for the max below). The
+    // reference moves only when some key of the block exceeds it by more than the
     // slack: each lane checks its own 16 keys of the query, and only if any lane of
     // the wave sees that (rare after the first block) is the block max formed
-    // across the lane groups, st shifted and the output rescaled. The first block
-    // sets the reference to its max (finite: every block has a key in the window);
-    // nothing is accumulated yet, so nothing is rescaled.
-    const bool first = t == 0;
-    // The check takes the maximum of the exponents' bit patterns as signed integers:
-    // every float at or below the slack (negative values and -inf included) has a
-    // pattern at or below the slack's, and among positive floats the order is the
-    // same, so "some exponent exceeds the slack" is decided exactly, without the
-    // quieting that a float max of the MFMA results would need.
-    int mxb[NQT];
-#pragma unroll
-    for (int n = 0; n < NQT; ++n) {
-      auto bits = [&](int k) { return __float_as_int(st[k / 4][n][k % 4]); };
-      int m = max(bits(0), bits(1));  // then two new values per step (v_max3_i32)
-#pragma unroll
-      for (int k = 2; k < 4 * NMT; k += 2) m = max(max(m, bits(k)), bits(k + 1));
-      mxb[n] = m;
-    }
-    const bool move_any = max(mxb[0], mxb[NQT - 1]) > __float_as_int(kLazyMaxSlack);
-    if (first || __builtin_amdgcn_ballot_w64(move_any)) {  // wave-uniform
+    // across the lane groups, t shifted and the output rescaled.
+    if (t == 0) {  // the reference starts at the first block's max (finite: every
+                   // block has a key in the window)
 #pragma unroll
       for (int n = 0; n < NQT; ++n) {
-        // The lane's float max: from the patterns when some exponent of the wave
-        // exceeds the slack (then any lane's value that matters is positive), from
-        // the values for the first block, whose max can be negative.
-        float ml = __int_as_float(mxb[n]);
-        if (first) {
-          ml = st[0][n][0];
+        float m4[NMT];
 #pragma unroll
-          for (int k = 1; k < 4 * NMT; ++k) ml = fmaxf(ml, st[k / 4][n][k % 4]);
-        }
-        const float d_blk = max_over_groups(ml);  // block max - reference
-        const float shift = (first || d_blk > kLazyMaxSlack) ? d_blk : 0.f;
+        for (int mt = 0; mt < NMT; ++mt)
+          m4[mt] = fmaxf(fmaxf(st[mt][n][0], st[mt][n][1]), fmaxf(st[mt][n][2], st[mt][n][3]));
+        m_run[n] = max_over_groups(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]))) * sl2;
+      }
+    }
+    f32x4 tx[NMT][NQT];
+    float mx[NQT];
+    bool move_any = false;
+#pragma unroll
+    for (int n = 0; n < NQT; ++n) {
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) tx[mt][n][r] = __builtin_fmaf(st[mt][n][r], sl2, -m_run[n]);
+      // a running max taking two new values per step (v_max3_f32)
+      float m = fmaxf(tx[0][n][0], tx[0][n][1]);
+#pragma unroll
+      for (int k = 2; k < 4 * NMT; k += 2)
+        m = fmaxf(fmaxf(m, tx[k / 4][n][k % 4]), tx[(k + 1) / 4][n][(k + 1) % 4]);
+      mx[n] = m;
+      move_any |= mx[n] > kLazyMaxSlack;
+    }
+    if (__builtin_amdgcn_ballot_w64(move_any)) {  // wave-uniform
+#pragma unroll
+      for (int n = 0; n < NQT; ++n) {
+        const float d_blk = max_over_groups(mx[n]);  // block max - reference
+        const float shift = d_blk > kLazyMaxSlack ? d_blk : 0.f;
+        const float alpha = __builtin_amdgcn_exp2f(-shift);
         m_run[n] += shift;
-        negm[n] = f32x4{-m_run[n], -m_run[n], -m_run[n], -m_run[n]};
-        if (!first) {
-          const float alpha = __builtin_amdgcn_exp2f(-shift);
-          acc_l[n] *= alpha;
+        acc_l[n] *= alpha;
 #pragma unroll
-          for (int e = 0; e < NET; ++e) acc[e][n] *= alpha;
-        }
+        for (int e = 0; e < NET; ++e) acc[e][n] *= alpha;
 #pragma unroll
-        for (int mt = 0; mt < NMT; ++mt) st[mt][n] -= shift;
+        for (int mt = 0; mt < NMT; ++mt) tx[mt][n] -= shift;
       }
     }
     uint32_t pk[NMT][NQT][2];  // bf16 weights, packed in pairs (the B operand of PV)
@@ -793,7 +782,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void s
       for (int mt = 0; mt < NMT; ++mt) {
         float e4[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) e4[r] = __builtin_amdgcn_exp2f(st[mt][n][r]);
+        for (int r = 0; r < 4; ++r) e4[r] = __builtin_amdgcn_exp2f(tx[mt][n][r]);
         pk[mt][n][0] = pack_bf16x2(e4[0], e4[1]);
         pk[mt][n][1] = pack_bf16x2(e4[2], e4[3]);
       }
@@ -848,7 +837,14 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void s
   }
 
   // ---- epilogue ----
-  load_q();  // the linear read takes phi of the plain queries
+  if constexpr (ROPE) {  // the linear read takes the unrotated queries
+#pragma unroll
+    for (int n = 0; n < NQT; ++n) {
+      const int64_t r = qrow0 + n * 16 + c;
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) qop[n][s] = as_bf16x8(ld16(qh + r * D + s * 32 + g * 8, r < n_q));
+    }
+  }
   // out = O / l + S phi(q) / (z . phi(q) + eps): the accumulators are normalised in
   // place, then the linear read accumulates S (phi(q) / den) into them on MFMA, with
   // S and the scaled phi(q) split into bf16 hi + lo (three products; the split of S

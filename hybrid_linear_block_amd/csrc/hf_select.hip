@@ -299,6 +299,19 @@ __device__ __forceinline__ void select_group(
   __shared__ float4 qs[SEL_QB][PARTS][EV + 1];
   const int i0 = qg * SEL_QB, tid = threadIdx.x;
   const int nq = nqb - i0 < SEL_QB ? nqb - i0 : SEL_QB;
+  static_assert(SEL_THREADS % PARTS == 0, "a key block's lanes stay in one pass");
+  // The first pass's key rows are requested before the query rows are staged, so that
+  // the two loads' latencies overlap instead of following one another.
+  auto key_part = [&](int x) {
+    return reinterpret_cast<const float4*>(pooled_k + ((size_t)h * nkb_cap + x / PARTS) * D) +
+           (x % PARTS) * EV;
+  };
+  float4 kv[EV];
+  if (tid < nkb * PARTS) {
+    const float4* km = key_part(tid);
+#pragma unroll
+    for (int e = 0; e < EV; ++e) kv[e] = km[e];
+  }
   for (int x = tid; x < SEL_QB * (D / 4); x += SEL_THREADS) {
     const int r = x / (D / 4), e = x % (D / 4);
     qs[r][e / EV][e % EV] = r < nq ? reinterpret_cast<const float4*>(
@@ -306,14 +319,13 @@ __device__ __forceinline__ void select_group(
                                    : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   __syncthreads();
-  static_assert(SEL_THREADS % PARTS == 0, "a key block's lanes stay in one pass");
   for (int x = tid; x < nkb * PARTS; x += SEL_THREADS) {
     const int j = x / PARTS, part = x % PARTS;
-    const float4* km =
-        reinterpret_cast<const float4*>(pooled_k + ((size_t)h * nkb_cap + j) * D) + part * EV;
-    float4 kv[EV];
+    if (x != tid) {  // later passes (more than SEL_THREADS / PARTS key blocks)
+      const float4* km = key_part(x);
 #pragma unroll
-    for (int e = 0; e < EV; ++e) kv[e] = km[e];
+      for (int e = 0; e < EV; ++e) kv[e] = km[e];
+    }
     float sq[SEL_QB];
 #pragma unroll
     for (int r = 0; r < SEL_QB; ++r) {

@@ -88,6 +88,13 @@ hf_status check_config(const hf_config* c) {
   if (c->dtype == HF_F32 && c->block_size != 16 && c->block_size != 64) return HF_ERR_UNSUPPORTED;
   if (ceil_div(c->max_n_kv, c->block_size) > hf::kMaxKeyBlocks) return HF_ERR_UNSUPPORTED;
   if (ceil_div(c->max_n_q, c->block_size) > (int64_t)1 << 24) return HF_ERR_UNSUPPORTED;
+  // Launch sizes are 32-bit products of the head count and the block counts (a
+  // workgroup or wave per (head, block), up to a few per block in the backward), so
+  // their sum per head times the heads stays below 2^26.
+  if ((int64_t)c->num_heads *
+          (ceil_div(c->max_n_q, c->block_size) + ceil_div(c->max_n_kv, c->block_size)) >
+      (int64_t)1 << 26)
+    return HF_ERR_UNSUPPORTED;
   if (c->max_top_k > ceil_div(c->max_n_kv, c->block_size)) return HF_ERR_INVALID_ARG;
   return HF_OK;
 }

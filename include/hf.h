@@ -58,7 +58,9 @@
  *                       max_* limits of the state.
  *   HF_ERR_UNSUPPORTED  head_dim, block_size or dtype outside the instantiated set:
  *                       head_dim in {64, 128}; bf16 with block_size 64; fp32 with
- *                       block_size 16 or 64.
+ *                       block_size 16 or 64. Also a configuration whose
+ *                       num_heads * (ceil(max_n_q/B) + ceil(max_n_kv/B)) exceeds 2^26
+ *                       (the kernels' launch sizes are 32-bit).
  *   HF_ERR_STATE        ev_index differs from the next expected eviction index
  *                       (a gap or a duplicate in the eviction sequence).
  *   HF_ERR_HIP          a HIP runtime call or kernel launch failed.

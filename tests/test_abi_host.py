@@ -96,6 +96,11 @@ def test_workspace_bytes():
                 dict(eps=0.0), dict(eps=float("inf")), dict(eps=float("nan")), dict(max_n_kv=64 * 2049),
                 dict(dtype=B.HF_BF16, block_size=16)):
         assert hla.hf_workspace_bytes(cfg(**bad)) == 0, bad
+    # Launch sizes are 32-bit: heads x (query + key blocks) is capped at 2^26.
+    nb = lambda n: -(-n // 64)  # noqa: E731
+    heads_ok = (1 << 26) // (nb(4680) + nb(14040))
+    assert hla.hf_workspace_bytes(cfg(num_heads=heads_ok)) > 0
+    assert hla.hf_workspace_bytes(cfg(num_heads=heads_ok + 1)) == 0
 
 
 def test_backward_workspace_bytes():

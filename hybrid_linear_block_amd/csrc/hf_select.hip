@@ -404,8 +404,11 @@ __global__ __launch_bounds__(SEL_THREADS) void score_select(
 // The selection and the absorb's reduce in one launch: workgroups below n_sel
 // select (n_qg groups of query blocks per head), the others reduce (red_wgs per
 // head, RED_PER_WG reduce groups each). They read and write different buffers.
-// A workgroup of the reduce part runs SEL_THREADS / RED_THREADS reduce groups.
-constexpr int RED_PER_WG = SEL_THREADS / RED_THREADS;
+// The reduce is bound by what each of its compute units pulls from memory, so a
+// reduce workgroup runs one group fewer than it could hold (at 12 heads and 74 query
+// blocks: 72 reduce workgroups beside the 180 selecting ones, one per compute unit),
+// and its fourth group of threads idles.
+constexpr int RED_PER_WG = SEL_THREADS / RED_THREADS - 1;
 static_assert(SEL_THREADS % RED_THREADS == 0, "whole reduce groups per workgroup");
 template <int D>
 constexpr int red_wgs() { return (red_groups<D>() + RED_PER_WG - 1) / RED_PER_WG; }
@@ -421,7 +424,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_and_reduce(
   } else {
     const int r = (int)blockIdx.x - n_sel;
     const int grp = (r % red_wgs<D>()) * RED_PER_WG + (int)threadIdx.x / RED_THREADS;
-    if (grp < red_groups<D>())
+    if ((int)threadIdx.x / RED_THREADS < RED_PER_WG && grp < red_groups<D>())
       absorb_reduce_group<D>(grp, r / red_wgs<D>(), partials, n_split, S, z, s_split,
                              (int)threadIdx.x % RED_THREADS);
   }
